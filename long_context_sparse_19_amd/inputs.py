@@ -1,0 +1,199 @@
+"""Seeded synthetic inputs for every workload.
+
+This module only draws random numbers and lays them out; it holds none of the
+pooling, scoring, selection or attention arithmetic.  Both the device path (tests,
+bench) and the CPU oracle consume the arrays it returns, so both see the same
+bytes.
+
+Recipe (numpy PCG64; every array has its own seed stream derived from the
+workload seed and a fixed tag, and large arrays are drawn in fixed-size row
+chunks, so the values do not depend on how much memory is free):
+
+* all values are N(0,1) float32, except the per-head indexer gates, N(0,1)/2;
+* one pooling logit per cached token, N(0,1);
+* bf16 tensors are the float32 draws rounded to nearest even (torch's cast);
+* fp8 index keys: each token row x is stored as codes = e4m3fn(x / s) with the
+  per-token scale s = max|x| / 448 (torch's cast, after clamping to +-448);
+* salient rows: in each sequence, round(salient_frac * L) token rows drawn
+  uniformly without replacement get their index-key scale multiplied by 8
+  (their codes are unchanged), which makes the blocks holding them stand out;
+* ragged lengths: L_b = 4 * U{min_blocks .. seq_len/4}; the paged cache uses
+  64-token pages and one seeded permutation of all pages of all sequences, shared
+  by the token-level and the pooled caches.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from .configs import Workload, INDEX_KPOOL
+
+_CHUNK_ROWS = 1 << 16
+
+_TAGS = {
+    "lens": 1, "perm": 2, "idx_keys": 3, "logits": 4, "latent": 5, "k": 6, "v": 7,
+    "q": 8, "q_idx": 9, "gates": 10, "salient": 11,
+}
+
+
+def _rng(seed: int, tag: str, chunk: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([seed, _TAGS[tag], chunk]))
+
+
+def _normal_rows(seed: int, tag: str, rows: int, cols: int) -> np.ndarray:
+    out = np.empty((rows, cols), dtype=np.float32)
+    for c, r0 in enumerate(range(0, rows, _CHUNK_ROWS)):
+        r1 = min(rows, r0 + _CHUNK_ROWS)
+        out[r0:r1] = _rng(seed, tag, c).standard_normal((r1 - r0, cols), dtype=np.float32)
+    return out
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest even (torch's cast)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def _fp8_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row fp8 e4m3fn storage of float32 rows (codes, scale) using torch's cast."""
+    import torch
+    amax = np.abs(x).max(axis=1)
+    s = (amax / np.float32(448.0)).astype(np.float32)
+    s_safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    codes = np.empty(x.shape, dtype=np.uint8)
+    for r0 in range(0, x.shape[0], _CHUNK_ROWS):
+        r1 = min(x.shape[0], r0 + _CHUNK_ROWS)
+        y = torch.from_numpy(x[r0:r1] / s_safe[r0:r1, None]).clamp_(-448.0, 448.0)
+        codes[r0:r1] = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, s
+
+
+@dataclass
+class Inputs:
+    w: Workload
+    seq_lens: np.ndarray            # int32 [B] tokens
+    page_table: Optional[np.ndarray]  # int32 [B, max_pages] or None
+    page_tokens: int                # tokens per page (0 if contiguous)
+    seq_stride: int                 # tokens between sequences (contiguous layout)
+    n_rows_tok: int                 # physical token rows
+    idx_keys: np.ndarray            # uint8 fp8 codes [R, D_I] or float32 [R, D_I]
+    idx_scale: Optional[np.ndarray]  # float32 [R] (fp8 keys) or None
+    pool_logits: np.ndarray         # float32 [R]
+    latent: Optional[np.ndarray]    # uint16 bf16 bits [R, dk] (bf16 workloads)
+    k_cache: Optional[np.ndarray]   # float32 [R, dk] (f32 workload)
+    v_cache: Optional[np.ndarray]   # float32 [R, dv] (f32 workload)
+    q: np.ndarray                   # uint16 bf16 bits or float32 [n_q, H, dk]
+    q_idx: np.ndarray               # uint16 bf16 bits or float32 [n_q, H_I, D_I]
+    gates: np.ndarray               # float32 [n_q, H_I]
+    q_seq: np.ndarray               # int32 [n_q]
+    q_pos: np.ndarray               # int32 [n_q]
+    salient_rows: np.ndarray        # int64 physical token rows whose scale was x8
+
+    @property
+    def max_pages(self) -> int:
+        return 0 if self.page_table is None else int(self.page_table.shape[1])
+
+    @property
+    def n_rows_pooled(self) -> int:
+        return self.n_rows_tok // INDEX_KPOOL
+
+
+def make_inputs(w: Workload, with_attention: bool = True) -> Inputs:
+    """Draw every input of workload ``w`` (host numpy arrays)."""
+    B = w.batch
+    seed = w.seed
+    if w.ragged:
+        nb = _rng(seed, "lens").integers(w.min_blocks, w.seq_len // INDEX_KPOOL + 1, size=B)
+        seq_lens = (nb * INDEX_KPOOL).astype(np.int32)
+    else:
+        seq_lens = np.full(B, w.seq_len, dtype=np.int32)
+
+    page_table = None
+    if w.page_tokens:
+        pt = w.page_tokens
+        assert pt % INDEX_KPOOL == 0
+        n_pages = (seq_lens.astype(np.int64) + pt - 1) // pt
+        total = int(n_pages.sum())
+        perm = _rng(seed, "perm").permutation(total).astype(np.int32)
+        max_pages = int(n_pages.max())
+        page_table = np.zeros((B, max_pages), dtype=np.int32)
+        off = 0
+        for b in range(B):
+            page_table[b, : n_pages[b]] = perm[off: off + n_pages[b]]
+            off += int(n_pages[b])
+        n_rows = total * pt
+        seq_stride = 0
+    else:
+        seq_stride = int(w.seq_len)
+        n_rows = B * seq_stride
+
+    # token rows of every (sequence, token) in the physical cache, for salient rows
+    def phys_rows(b: int, t: np.ndarray) -> np.ndarray:
+        if page_table is None:
+            return b * seq_stride + t
+        return page_table[b, t // w.page_tokens].astype(np.int64) * w.page_tokens + t % w.page_tokens
+
+    # indexer keys
+    x = _normal_rows(seed, "idx_keys", n_rows, w.idx_dim)
+    if w.idx_key_dtype == "fp8":
+        idx_keys, idx_scale = _fp8_rows(x)
+    else:
+        idx_keys, idx_scale = x, None
+    del x
+    salient = np.zeros(0, dtype=np.int64)
+    if w.salient_frac > 0 and idx_scale is not None:
+        rs = _rng(seed, "salient")
+        picks = []
+        for b in range(B):
+            L = int(seq_lens[b])
+            n = int(round(w.salient_frac * L))
+            t = rs.choice(L, size=n, replace=False)
+            picks.append(phys_rows(b, np.sort(t)))
+        salient = np.concatenate(picks)
+        idx_scale[salient] *= np.float32(w.salient_mult)
+    logits = _normal_rows(seed, "logits", n_rows, 1)[:, 0].copy()
+
+    # attention caches
+    latent = k_cache = v_cache = None
+    if with_attention:
+        if w.attn_dtype == "bf16":
+            latent = np.empty((n_rows, w.dk), dtype=np.uint16)
+            for c, r0 in enumerate(range(0, n_rows, _CHUNK_ROWS)):
+                r1 = min(n_rows, r0 + _CHUNK_ROWS)
+                latent[r0:r1] = to_bf16_bits(
+                    _rng(seed, "latent", c).standard_normal((r1 - r0, w.dk), dtype=np.float32))
+        else:
+            k_cache = _normal_rows(seed, "k", n_rows, w.dk)
+            v_cache = _normal_rows(seed, "v", n_rows, w.dv)
+
+    # queries
+    n_q = w.n_rows
+    if w.mode == "decode":
+        q_seq = np.arange(B, dtype=np.int32)
+        q_pos = (seq_lens - 1).astype(np.int32)
+    else:
+        assert B == 1
+        q_seq = np.zeros(n_q, dtype=np.int32)
+        q_pos = (int(seq_lens[0]) - n_q + np.arange(n_q)).astype(np.int32)
+    qf = _normal_rows(seed, "q", n_q, w.n_heads * w.dk).reshape(n_q, w.n_heads, w.dk)
+    qif = _normal_rows(seed, "q_idx", n_q, w.idx_heads * w.idx_dim).reshape(n_q, w.idx_heads, w.idx_dim)
+    gates = (_normal_rows(seed, "gates", n_q, w.idx_heads) * np.float32(0.5)).astype(np.float32)
+    if w.attn_dtype == "bf16":
+        q = to_bf16_bits(qf)
+        q_idx = to_bf16_bits(qif)
+    else:
+        q, q_idx = qf, qif
+
+    return Inputs(
+        w=w, seq_lens=seq_lens, page_table=page_table, page_tokens=w.page_tokens,
+        seq_stride=seq_stride, n_rows_tok=n_rows, idx_keys=idx_keys, idx_scale=idx_scale,
+        pool_logits=logits, latent=latent, k_cache=k_cache, v_cache=v_cache, q=q,
+        q_idx=q_idx, gates=gates, q_seq=q_seq, q_pos=q_pos, salient_rows=salient,
+    )

@@ -1,0 +1,325 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test checks the oracle against a library routine, a closed form, a worked
+example derived by hand, an invariant the pages state, or brute force on tiny
+inputs, so that a dropped term, a wrong sign or index, or a transposed operand
+anywhere in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------- fp8 codec
+def test_fp8_decode_exhaustive_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.fp8_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.isnan(ours[0x7F]) and np.isnan(ours[0xFF])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def test_fp8_encode_roundtrips_every_finite_code():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.fp8_decode(codes)
+    fin = ~np.isnan(vals)
+    assert np.array_equal(O.fp8_encode(vals[fin]), codes[fin])
+
+
+@pytest.mark.parametrize("scale", [448.0, 1.0, 2.0 ** -6, 2.0 ** -9])
+def test_fp8_encode_matches_torch_rne(scale):
+    # float32-exact inputs: torch narrows float64 to float32 before the fp8 cast,
+    # which would round twice
+    x = (np.random.default_rng(7).uniform(-1, 1, 200000) * scale).astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.fp8_encode(x), ref)
+
+
+def test_fp8_encode_midpoints_round_to_even():
+    vals = O.fp8_decode(np.arange(0, 0x7E, dtype=np.uint8))   # 0 .. 416 ascending
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    got = O.fp8_encode(mids)
+    ref = torch.from_numpy(mids).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+    assert np.all(got % 2 == 0)            # even mantissa wins every tie
+
+
+def test_fp8_encode_saturates_and_flushes():
+    assert O.fp8_encode(np.array([464.0, 500.0, 1e9, -1e9])).tolist() == [0x7E, 0x7E, 0x7E, 0xFE]
+    assert O.fp8_encode(np.array([2.0 ** -10, 3 * 2.0 ** -11, -2.0 ** -11])).tolist() == [0, 1, 0x80]
+
+
+# --------------------------------------------------------------------------- IndexPool
+def test_pool_worked_example():
+    g = _golden("pool_worked_example.json")
+    keys = np.array(g["keys"])[None]
+    logits = np.array(g["logits"])[None]
+    np.testing.assert_allclose(O.pool_f32(keys, logits)[0], g["pooled"], rtol=1e-15)
+    # fp8 version: store each key as codes with scale 1 (all values are exact in fp8)
+    codes = O.fp8_encode(keys)
+    c, sigma, v, _ = O.pool_fp8(codes, np.ones((1, 4)), logits)
+    assert c[0].tolist() == g["codes"]
+    assert sigma[0] == pytest.approx(g["sigma"], rel=1e-15)
+
+
+def test_pool_equal_logits_is_plain_mean():
+    """QSA's r=4 average-pooled key block is IndexPool with equal weights."""
+    rng = np.random.default_rng(1)
+    keys = rng.standard_normal((50, 4, 32))
+    logits = np.repeat(rng.standard_normal((50, 1)), 4, axis=1)
+    np.testing.assert_allclose(O.pool_f32(keys, logits), keys.mean(axis=1), rtol=1e-13, atol=1e-15)
+    codes = O.fp8_encode(keys * 100)
+    scale = rng.uniform(0.5, 2.0, (50, 4))
+    _, sigma, v, _ = O.pool_fp8(codes, scale, logits)
+    mean = (scale[:, :, None] * O.fp8_decode(codes)).mean(axis=1)
+    np.testing.assert_allclose(v * sigma[:, None], mean, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("hot", [0, 1, 2, 3])
+def test_pool_one_hot_logit_copies_that_key(hot):
+    """A dominant logit makes the pooled key an exact copy of that token's key;
+    for an fp8 row whose max element is coded 448, the requantised codes and
+    scale equal the source codes and scale."""
+    rng = np.random.default_rng(hot)
+    x = rng.standard_normal((20, 4, 64))
+    s = np.abs(x).max(axis=2) / 448.0
+    codes = O.fp8_encode(x / s[:, :, None])
+    logits = np.zeros((20, 4))
+    logits[:, hot] = 60.0
+    c, sigma, _, _ = O.pool_fp8(codes, s, logits)
+    assert np.array_equal(c, codes[:, hot])
+    np.testing.assert_allclose(sigma, s[:, hot], rtol=1e-15)
+    kf = O.pool_f32(x, logits)
+    np.testing.assert_allclose(kf, x[:, hot], rtol=1e-12, atol=1e-12)
+
+
+def test_pool_identical_keys_give_that_key():
+    """Weights sum to one, whatever the logits."""
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((30, 1, 16))
+    keys = np.repeat(k, 4, axis=1)
+    logits = rng.standard_normal((30, 4)) * 5
+    np.testing.assert_allclose(O.pool_f32(keys, logits), k[:, 0], rtol=1e-13, atol=1e-14)
+
+
+def test_pool_max_element_codes_448_and_zero_block():
+    rng = np.random.default_rng(4)
+    codes = rng.integers(0, 0x7E, (40, 4, 128), dtype=np.uint8)
+    codes[0] = 0                                   # an all-zero block
+    scale = rng.uniform(0.01, 1.0, (40, 4))
+    c, sigma, v, _ = O.pool_fp8(codes, scale, rng.standard_normal((40, 4)))
+    assert sigma[0] == 0 and not c[0].any()
+    dec = O.fp8_decode(c[1:])
+    assert np.all(np.abs(dec).max(axis=1) == 448.0)
+
+
+def test_pooled_cache_is_four_times_smaller():
+    """The resident indexer state drops 4x: T/4 pooled rows of the same width."""
+    from long_context_sparse_19_amd.configs import TINY, DECODE, scaled_down
+    from long_context_sparse_19_amd.inputs import make_inputs
+    for w in (TINY, scaled_down(DECODE, 4096, batch=2)):
+        inp = make_inputs(w, with_attention=False)
+        pooled, sigma, *_ , rows = O.compress(inp)
+        T = int(inp.seq_lens.sum())
+        assert len(rows) == T // 4
+        tok_bytes = inp.idx_keys[:T].nbytes + (0 if inp.idx_scale is None else inp.idx_scale[:T].nbytes)
+        item = pooled.dtype.itemsize if sigma is not None else 4   # f32 keys stay f32
+        pool_bytes = len(rows) * pooled.shape[1] * item + (0 if sigma is None else 4 * len(rows))
+        assert tok_bytes == 4 * pool_bytes
+
+
+# --------------------------------------------------------------------------- scoring
+def test_score_select_worked_example():
+    g = _golden("score_select_worked_example.json")
+    S = O.score(np.array(g["q_idx"]), np.array(g["gates"]), np.array(g["keys"][:5]))
+    assert S.tolist() == g["scores"]
+    b_q = g["pos"] // 4
+    assert O.select(S, b_q, 3).tolist() == g["select_k3"]
+    assert O.select(S, b_q, 8).tolist() == g["select_k8"]
+
+
+def test_score_unit_query_is_relu_of_one_coordinate():
+    rng = np.random.default_rng(5)
+    keys = rng.standard_normal((100, 24))
+    for d in (0, 7, 23):
+        q = np.zeros((1, 24))
+        q[0, d] = 1.0
+        np.testing.assert_array_equal(O.score(q, [1.0], keys), np.maximum(keys[:, d], 0))
+
+
+def test_score_gates_pick_heads_and_sign():
+    rng = np.random.default_rng(6)
+    keys = rng.standard_normal((64, 8))
+    q = rng.standard_normal((2, 8))
+    h0 = np.maximum(keys @ q[0], 0)
+    h1 = np.maximum(keys @ q[1], 0)
+    np.testing.assert_allclose(O.score(q, [1.0, 0.0], keys), h0, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(O.score(q, [0.0, 1.0], keys), h1, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(O.score(q, [-2.0, 0.5], keys), -2 * h0 + 0.5 * h1, rtol=1e-13, atol=1e-13)
+
+
+def test_score_fp8_pooled_includes_sigma():
+    codes = np.array([[0x7E, 0xFE, 0x38]], dtype=np.uint8)   # 448, -448, 1.0
+    sigma = np.array([0.25])
+    vals = O.pooled_values(codes, sigma)
+    assert vals.tolist() == [[112.0, -112.0, 0.25]]
+    q = np.eye(3)
+    assert O.score(q[[0]], [1.0], vals).tolist() == [112.0]
+    assert O.score(q[[1]], [1.0], vals).tolist() == [0.0]
+    assert O.score(q[[2]], [1.0], vals).tolist() == [0.25]
+
+
+# --------------------------------------------------------------------------- selection
+def _brute_select(S, b_q, k):
+    """j is kept iff fewer than k'-1 blocks beat it under (higher score, lower index)."""
+    kp = min(k, b_q + 1)
+    keep = []
+    for j in range(b_q):
+        better = sum(1 for i in range(b_q) if S[i] > S[j] or (S[i] == S[j] and i < j))
+        if better < kp - 1:
+            keep.append(j)
+    return keep + [b_q] + [-1] * (k - kp)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_select_matches_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    b_q = int(rng.integers(0, 40))
+    k = int(rng.integers(1, 50))
+    S = np.round(rng.standard_normal(b_q) * 2) / 2      # many exact ties
+    assert O.select(S, b_q, k).tolist() == _brute_select(S, b_q, k)
+
+
+def test_select_all_when_k_exceeds_blocks_and_own_block_only():
+    assert O.select(np.zeros(5), 5, 9).tolist() == [0, 1, 2, 3, 4, 5, -1, -1, -1]
+    assert O.select(np.zeros(0), 0, 4).tolist() == [0, -1, -1, -1]
+    assert O.select(np.arange(10.0), 10, 1).tolist() == [10]
+    # all-equal scores: lowest indices win
+    assert O.select(np.zeros(10), 10, 4).tolist() == [0, 1, 2, 10]
+
+
+# --------------------------------------------------------------------------- attention
+def _sdpa_causal(q, K, V, scale, pos):
+    """torch scaled_dot_product_attention in float64 with an explicit causal mask."""
+    qt = torch.from_numpy(q)[None]                   # [1, n, H, d] -> [1, H, n, d]
+    qt = qt.permute(0, 2, 1, 3)
+    Kt = torch.from_numpy(K)[None, None].expand(1, q.shape[1], -1, -1)
+    Vt = torch.from_numpy(V)[None, None].expand(1, q.shape[1], -1, -1)
+    t = torch.arange(K.shape[0])
+    mask = t[None, :] <= torch.from_numpy(pos)[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, Kt, Vt, attn_mask=mask[None, None], scale=scale)
+    return o.permute(0, 2, 1, 3)[0].numpy()
+
+
+def test_attend_selecting_every_block_is_dense_causal_attention():
+    """With k >= b_q + 1 every earlier block is selected, and the masked own block
+    completes the causal prefix: sparse attention equals dense causal attention."""
+    rng = np.random.default_rng(8)
+    T, H, dk, dv = 64, 3, 16, 8
+    K = rng.standard_normal((T, dk))
+    V = rng.standard_normal((T, dv))
+    pos = np.arange(40, 64)                          # positions inside blocks too
+    q = rng.standard_normal((len(pos), H, dk))
+    ref = _sdpa_causal(q, K, V, 0.3, pos)
+    for n, p in enumerate(pos):
+        ids = O.select(np.zeros(p // 4), p // 4, 100)
+        t = O.selected_tokens(ids, int(p))
+        assert t.tolist() == list(range(p + 1))
+        Ot, _ = O.attend(q[n], K[t], V[t], 0.3)
+        np.testing.assert_allclose(Ot, ref[n], rtol=1e-12, atol=1e-12)
+
+
+def test_attend_special_cases():
+    rng = np.random.default_rng(9)
+    K = rng.standard_normal((12, 6))
+    V = rng.standard_normal((12, 5))
+    q = rng.standard_normal((4, 6))
+    O1, lse1 = O.attend(q, K[3:4], V[3:4], 0.7)          # a single token
+    np.testing.assert_array_equal(O1, np.repeat(V[3:4], 4, axis=0))
+    np.testing.assert_allclose(lse1, 0.7 * q @ K[3], rtol=1e-14)
+    O0, lse0 = O.attend(np.zeros((2, 6)), K, V, 0.7)      # q = 0: plain mean
+    np.testing.assert_allclose(O0, np.repeat(V.mean(0, keepdims=True), 2, 0), rtol=1e-13)
+    np.testing.assert_allclose(lse0, math.log(12), rtol=1e-14)
+    Oa, lse = O.attend(q, K, V, 0.7)
+    assert np.all(Oa >= V.min(0) - 1e-12) and np.all(Oa <= V.max(0) + 1e-12)
+    ref = np.log(np.exp(0.7 * q @ K.T).sum(1))
+    np.testing.assert_allclose(lse, ref, rtol=1e-13)
+
+
+def test_selected_tokens_causal_inside_own_block():
+    ids = np.array([1, 3, 7, -1])
+    assert O.selected_tokens(ids, 29).tolist() == [4, 5, 6, 7, 12, 13, 14, 15, 28, 29]
+
+
+# --------------------------------------------------------------------------- layout
+def test_paged_and_contiguous_layouts_agree():
+    """A shuffled page table changes only where rows live, never the result."""
+    from long_context_sparse_19_amd.configs import RAGGED, scaled_down
+    from long_context_sparse_19_amd.inputs import make_inputs
+    w = scaled_down(RAGGED, 2048, batch=3, min_blocks=100, top_k=32)
+    inp = make_inputs(w)
+
+    class Flat:
+        pass
+    flat = Flat()
+    L = int(inp.seq_lens.max())
+    flat.page_table, flat.page_tokens, flat.seq_stride = None, 0, L
+    flat.seq_lens, flat.q_seq, flat.q_pos = inp.seq_lens, inp.q_seq, inp.q_pos
+    flat.q, flat.q_idx, flat.gates = inp.q, inp.q_idx, inp.gates
+    n = len(inp.seq_lens) * L
+    flat.idx_keys = np.zeros((n, inp.idx_keys.shape[1]), inp.idx_keys.dtype)
+    flat.idx_scale = np.ones(n, np.float32)
+    flat.pool_logits = np.zeros(n, np.float32)
+    flat.latent = np.zeros((n, inp.latent.shape[1]), np.uint16)
+    flat.k_cache = flat.v_cache = None
+    for b in range(len(inp.seq_lens)):
+        t = np.arange(int(inp.seq_lens[b]))
+        src = O.token_rows(inp, b, t)
+        dst = b * L + t
+        flat.idx_keys[dst] = inp.idx_keys[src]
+        flat.idx_scale[dst] = inp.idx_scale[src]
+        flat.pool_logits[dst] = inp.pool_logits[src]
+        flat.latent[dst] = inp.latent[src]
+    outs = []
+    for x in (inp, flat):
+        pooled, sigma, *_ = O.compress(x)
+        vals = O.pooled_values(pooled, sigma)
+        ids, _ = O.score_select(x, vals, w.top_k)
+        Ox, lse = O.attention_rows(x, ids, w.scale, w.dv)
+        outs.append((ids, Ox, lse))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+    assert np.array_equal(outs[0][2], outs[1][2])
+
+
+def test_end_to_end_all_blocks_equals_dense_causal():
+    """pool -> score -> select (k covering every block) -> attend reproduces dense
+    causal attention over the whole history, for a prefill chunk."""
+    from long_context_sparse_19_amd.configs import PREFILL, scaled_down
+    from long_context_sparse_19_amd.inputs import make_inputs, bf16_bits_to_f32
+    w = scaled_down(PREFILL, 256, n_query=24, top_k=64)
+    inp = make_inputs(w)
+    pooled, sigma, *_ = O.compress(inp)
+    ids, _ = O.score_select(inp, O.pooled_values(pooled, sigma), w.top_k)
+    Os, _ = O.attention_rows(inp, ids, w.scale, w.dv)
+    KV = bf16_bits_to_f32(inp.latent).astype(np.float64)
+    q = bf16_bits_to_f32(inp.q).astype(np.float64)
+    ref = _sdpa_causal(q, KV, KV[:, : w.dv].copy(), w.scale, inp.q_pos.astype(np.int64))
+    np.testing.assert_allclose(Os, ref, rtol=1e-11, atol=1e-11)
