@@ -1,0 +1,202 @@
+/*
+ * indexpool.h -- C ABI of libindexpool.so: the global-retrieval half of a hybrid
+ * attention layer (IndexPool-compressed indexer, block top-k, sparse attention)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The four calls are the four stages of the pipeline that the G2C Brief
+ * "GLM-5.3-Flash: hybrid attention becomes the product" draws in its section
+ * "DSA keeps selected global access in eleven layers": the latent cache of the
+ * full token history, IndexPool (four indexer keys -> one pooled key), learned
+ * sparse selection (top 2048 tokens = 512 blocks of 4) and attention over the
+ * selected history.  Decode and prefill are separate calls because the two phases
+ * have very different arithmetic intensity (reading notes "GLM-5.3-Flash: Hybrid
+ * Attention, IndexPool, and Vision-in-the-Loop", section 4, "EPD disaggregation").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Memory: every pointer named "device" is device memory owned by the caller.
+ *    The library allocates nothing and keeps no state between calls.
+ *  - Streams: every call only enqueues work on `stream` (0 = the null stream) and
+ *    never synchronises the host.  Outputs are ready when the stream reaches them.
+ *  - Errors: arguments the host can check (null pointers, unsupported dtypes or
+ *    sizes, a workspace that is too small) make a call return a non-zero
+ *    ip_status before anything is enqueued; ip_last_error() then describes it.
+ *    A failed launch returns IP_EDEVICE.  Contents of device arrays (lengths,
+ *    page ids, positions, selected ids) are not checked: they are the caller's
+ *    contract, stated per call below.
+ *  - Caches: token t of sequence b lives at physical row
+ *        page_table[b * max_pages + t / page_tokens] * page_tokens + t % page_tokens
+ *    when a page table is given, else at row  b * seq_stride + t.  Pooled block j
+ *    (tokens 4j..4j+3) of sequence b lives at the same formula with
+ *    page_tokens / 4 and seq_stride / 4, so pooled row r always covers token rows
+ *    4r .. 4r+3.
+ */
+#ifndef INDEXPOOL_H
+#define INDEXPOOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IP_OK = 0,
+  IP_EINVAL = 1,        /* a null pointer or an inconsistent size */
+  IP_EUNSUPPORTED = 2,  /* a dtype / geometry / size outside the supported set */
+  IP_EWORKSPACE = 3,    /* workspace missing or smaller than *_workspace_bytes() */
+  IP_EDEVICE = 4        /* a HIP launch failed */
+} ip_status;
+
+typedef enum {
+  IP_F32 = 0,
+  IP_BF16 = 1,
+  IP_FP8_E4M3FN = 2     /* OCP e4m3fn: bias 7, max 448, no infinities */
+} ip_dtype;
+
+/* One cache: `rows` rows of `row_dim` elements; row r starts at
+ * (char*)data + r * row_stride.  FP8 rows carry one fp32 scale each
+ * (value = scale[r] * decode(code)). */
+typedef struct ip_cache {
+  void*   data;        /* device */
+  float*  scale;       /* device [rows] fp32; required iff dtype == IP_FP8_E4M3FN, else NULL */
+  int32_t dtype;       /* ip_dtype of the elements */
+  int32_t row_dim;     /* elements per row */
+  int64_t row_stride;  /* bytes between rows; a multiple of 16 */
+} ip_cache;
+
+/* The batch of sequences and how their caches are laid out. */
+typedef struct ip_seqs {
+  int32_t        batch;        /* number of sequences, >= 1 */
+  int32_t        max_seq_len;  /* host-side upper bound on every seq_lens[b] (sizes grids) */
+  const int32_t* seq_lens;     /* device [batch]: tokens cached for each sequence */
+  const int32_t* page_table;   /* device [batch, max_pages] physical page ids, or NULL */
+  int32_t        max_pages;    /* row length of page_table (ignored when NULL) */
+  int32_t        page_tokens;  /* tokens per page, a multiple of 4 (ignored when NULL) */
+  int64_t        seq_stride;   /* tokens between sequence starts, a multiple of 4 (page_table NULL) */
+} ip_seqs;
+
+/* ---------------------------------------------------------------------------------
+ * indexpool_compress -- IndexPool.
+ * Reading notes, section 2, sub-section "IndexPool": four indexer key vectors are
+ * merged into one by weighted pooling with learned weights (QSA's r = 4 block
+ * pooling with a plain mean is the equal-weight case), so the resident indexer
+ * state shrinks 4x; the FP8 cache tier is from section 4, "The serving stack".
+ *
+ * For each sequence b and each complete block j in
+ *     [begin_b, min(begin_b + max_blocks, seq_lens[b] / 4))      (begin_b = block_begin[b] or 0)
+ * with token keys k_i, scales s_i and logits l_i (i = 0..3, tokens 4j+i):
+ *     w = softmax(l_0..l_3);   K_j = sum_i w_i * s_i * k_i
+ * FP8 output: sigma_j = max_d |K_j[d]| / 448, code_j = e4m3fn(K_j / sigma_j) rounded
+ *             to nearest even and saturated at +-448; sigma_j = 0 gives zero codes.
+ * F32 output: K_j as is (keys F32, no scales).
+ *
+ *  keys     token-level index keys, dtype FP8 (with scale) or F32; row_dim D = 128
+ *           for FP8, D <= 256 and a multiple of 4 for F32
+ *  logits   device [token rows] fp32, one pooling logit per cached token, indexed
+ *           like the key rows
+ *  pooled   output, same dtype and row_dim as keys; FP8 also writes pooled->scale
+ *  block_begin  device [batch] first block to pool per sequence, or NULL (= 0)
+ *  max_blocks   host bound on blocks pooled per sequence (grid size); <= 0 means
+ *               max_seq_len / 4
+ * Only the rows of the pooled blocks are written.
+ * ------------------------------------------------------------------------------- */
+ip_status indexpool_compress(const ip_seqs* seqs, const int32_t* block_begin, int32_t max_blocks,
+                             const ip_cache* keys, const float* logits, const ip_cache* pooled,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * index_score_topk -- the lightweight indexer and the learned top-k selection.
+ * Reading notes, section 2 "Hybrid Attention: Linear State + Sparse Retrieval"
+ * (sparse attention as the global retriever, via a lightweight indexer, in the
+ * lineage of DeepSeek-V3.2's DSA indexer); G2C Brief, "DSA keeps selected global
+ * access in eleven layers" (learned sparse selection, index_topk = 2048 tokens).
+ *
+ * Query row r belongs to sequence b = q_seq[r] (NULL: b = r) at position
+ * p = q_pos[r] (NULL: seq_lens[b] - 1); its own block is b_q = p / 4.  For every
+ * block j < b_q:
+ *     S_j = sum_h gates[r, h] * relu(q_idx[r, h, :] . K_j)        (K_j dequantised)
+ * The selection keeps b_q plus the k'-1 best blocks j < b_q, k' = min(top_k, b_q+1),
+ * ordered by higher S_j then lower j.  out_idx[r, :] lists the kept ids ascending
+ * (b_q last), then -1 up to top_k.
+ *
+ *  q_idx    device [n_q, n_heads, head_dim]; BF16 with FP8 pooled keys (n_heads 32,
+ *           head_dim 128), or F32 with F32 pooled keys (n_heads <= 64,
+ *           n_heads * head_dim <= 4096)
+ *  gates    device [n_q, n_heads] fp32
+ *  pooled   pooled keys written by indexpool_compress for blocks j < b_q
+ *  top_k    1 .. 2048
+ *  out_idx  device [n_q, top_k] int32
+ *  scores   device [n_q, ld] fp32 or NULL, ld = index_scores_ld(max_seq_len); when
+ *           given, S_j is written at [r, j] for j < b_q (other entries untouched)
+ *           and no score workspace is used
+ *  ws       device workspace of ws_bytes >= index_score_topk_workspace_bytes(...)
+ * Contract: 0 <= p < seq_lens[b]; blocks j < b_q were pooled.
+ * ------------------------------------------------------------------------------- */
+int64_t index_scores_ld(int32_t max_seq_len);   /* max_seq_len/4 rounded up to 64 */
+size_t index_score_topk_workspace_bytes(const ip_seqs* seqs, int32_t n_q, int32_t top_k,
+                                        int32_t scores_given);
+ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
+                           const int32_t* q_pos, const void* q_idx, int32_t q_dtype,
+                           int32_t n_heads, int32_t head_dim, const float* gates,
+                           const ip_cache* pooled, int32_t top_k, int32_t* out_idx,
+                           float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * sparse_attn_decode / sparse_attn_prefill -- attention over the selected history.
+ * G2C Brief, "DSA keeps selected global access in eleven layers": the layer keeps
+ * a token-addressable MLA latent history of rank 512 and attends over the
+ * selected subset of it.
+ *
+ * For query row r (sequence b, position p as in index_score_topk), the tokens are
+ * U = { 4j + i : j in sel_idx[r, :], j >= 0, 0 <= i < 4, 4j + i <= p } and, per head h,
+ *     l_t = scale * q[r, h, :] . K_t,   O[r, h, :] = sum_t softmax(l)_t V_t,
+ *     lse[r, h] = log sum_t exp(l_t).
+ * Geometries:
+ *   BF16 latent (MQA): q BF16 [n_q, 64, 576]; k is the 576-dim BF16 latent cache,
+ *     v must be NULL: V is the first 512 dims of the same rows (dk 576, dv 512);
+ *     out BF16 [n_q, 64, 512] (round to nearest even).
+ *   F32: q F32 [n_q, n_heads, dk]; separate F32 k [rows, dk] and v [rows, dv]
+ *     caches; n_heads <= 16, dk, dv <= 128 and multiples of 4; out F32.
+ *  sel_idx  device [n_q, top_k] ascending block ids, -1 entries ignored
+ *           (index_score_topk's output)
+ *  lse      device [n_q, n_heads] fp32 or NULL
+ *  ws       device workspace of ws_bytes >= sparse_attn_workspace_bytes(...) (may be
+ *           0 bytes, then ws may be NULL)
+ * Contract: every non-negative id j satisfies 4j <= p, and the own block of each
+ * row is among them (so U is never empty).
+ * decode:  row r is sequence r at p = seq_lens[r] - 1 (n_q = batch).
+ * prefill: rows given by q_seq (NULL: row r is sequence r) and q_pos.
+ * ------------------------------------------------------------------------------- */
+size_t sparse_attn_workspace_bytes(int32_t n_q, int32_t n_heads, int32_t dv, int32_t top_k,
+                                   int32_t q_dtype);
+ip_status sparse_attn_decode(const ip_seqs* seqs, const void* q, int32_t q_dtype,
+                             int32_t n_heads, int32_t dk, int32_t dv, float scale,
+                             const ip_cache* k, const ip_cache* v, const int32_t* sel_idx,
+                             int32_t top_k, void* out, float* lse, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+ip_status sparse_attn_prefill(const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
+                              const int32_t* q_pos, const void* q, int32_t q_dtype,
+                              int32_t n_heads, int32_t dk, int32_t dv, float scale,
+                              const ip_cache* k, const ip_cache* v, const int32_t* sel_idx,
+                              int32_t top_k, void* out, float* lse, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+const char* ip_last_error(void);
+
+/* Timing hook for benchmarks: the next launch (on this thread) of kernel `kernel_id`
+ * is bracketed by hipEventRecord(start) / hipEventRecord(stop) on its stream.
+ * kernel_id: 1 compress, 2 score, 3 top-k (first stage), 4 attention, 5 combine.
+ * Pass NULL events to clear.  Not needed for normal use. */
+ip_status ip_time_next_launch(int32_t kernel_id, hipEvent_t start, hipEvent_t stop);
+
+/* Library version, e.g. "0.1.0". */
+const char* ip_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* INDEXPOOL_H */

@@ -1,0 +1,372 @@
+// C ABI of libindexpool: argument checks, workspace carving and kernel dispatch.
+// Every check that the host can make happens before anything is enqueued.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/indexpool.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+ip_status fail(ip_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ip_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return IP_OK;
+  return fail(IP_EDEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+struct Hook {
+  int id = 0;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local Hook g_hook;
+
+constexpr int64_t kMaxTokens = int64_t(1) << 31;   // int32 token positions
+constexpr size_t kScoreBudget = size_t(256) << 20;  // score workspace per row chunk
+constexpr int kTargetWorkgroups = 256;              // MI355X compute units
+
+ip_status check_seqs(const ip_seqs* s, const char* fn) {
+  if (!s) return fail(IP_EINVAL, "%s: seqs is NULL", fn);
+  if (s->batch < 1) return fail(IP_EINVAL, "%s: batch must be >= 1 (got %d)", fn, s->batch);
+  if (!s->seq_lens) return fail(IP_EINVAL, "%s: seqs->seq_lens is NULL", fn);
+  if (s->max_seq_len < 1 || s->max_seq_len >= kMaxTokens)
+    return fail(IP_EINVAL, "%s: max_seq_len out of range (got %d)", fn, s->max_seq_len);
+  if (s->page_table) {
+    if (s->page_tokens < 4 || s->page_tokens % 4)
+      return fail(IP_EINVAL, "%s: page_tokens must be a positive multiple of 4 (got %d)", fn, s->page_tokens);
+    if (s->max_pages < 1) return fail(IP_EINVAL, "%s: max_pages must be >= 1", fn);
+    if ((int64_t)s->max_pages * s->page_tokens < s->max_seq_len)
+      return fail(IP_EINVAL, "%s: max_pages * page_tokens < max_seq_len", fn);
+  } else {
+    if (s->seq_stride < s->max_seq_len || s->seq_stride % 4)
+      return fail(IP_EINVAL, "%s: seq_stride must be a multiple of 4 and >= max_seq_len (got %lld)", fn,
+                  (long long)s->seq_stride);
+  }
+  return IP_OK;
+}
+
+ip::Layout layout_of(const ip_seqs* s) {
+  ip::Layout L;
+  L.seq_lens = s->seq_lens;
+  L.page_table = s->page_table;
+  L.max_pages = s->max_pages;
+  L.page_tokens = s->page_tokens;
+  L.seq_stride = s->seq_stride;
+  return L;
+}
+
+int elem_bytes(int dt) { return dt == IP_F32 ? 4 : dt == IP_BF16 ? 2 : 1; }
+
+ip_status check_cache(const ip_cache* c, const char* fn, const char* name) {
+  if (!c) return fail(IP_EINVAL, "%s: %s is NULL", fn, name);
+  if (!c->data) return fail(IP_EINVAL, "%s: %s->data is NULL", fn, name);
+  if (c->dtype < IP_F32 || c->dtype > IP_FP8_E4M3FN) return fail(IP_EUNSUPPORTED, "%s: %s has an unknown dtype", fn, name);
+  if (c->row_dim < 1) return fail(IP_EINVAL, "%s: %s->row_dim must be >= 1", fn, name);
+  if (c->row_stride % 16 || c->row_stride < (int64_t)c->row_dim * elem_bytes(c->dtype))
+    return fail(IP_EINVAL, "%s: %s->row_stride must be a multiple of 16 covering a row", fn, name);
+  if ((reinterpret_cast<uintptr_t>(c->data) & 15) != 0) return fail(IP_EINVAL, "%s: %s->data must be 16-byte aligned", fn, name);
+  if (c->dtype == IP_FP8_E4M3FN && !c->scale) return fail(IP_EINVAL, "%s: %s->scale is required for FP8", fn, name);
+  return IP_OK;
+}
+
+// Score workspace plan shared by the size query and the call.
+struct ScorePlan {
+  int64_t ld;          // floats per score row
+  int max_blocks;      // eligible blocks bound
+  int n_chunks;        // stage-1 chunks per row
+  int rows_per_chunk;  // query rows per pass
+  size_t score_bytes, cand_bytes, total;
+};
+
+ScorePlan score_plan(const ip_seqs* s, int n_q, int top_k, bool scores_given) {
+  ScorePlan p;
+  p.max_blocks = (s->max_seq_len - 1) / 4;          // j < b_q <= (max_seq_len - 1) / 4
+  p.ld = index_scores_ld(s->max_seq_len);
+  p.n_chunks = p.max_blocks <= 0 ? 1 : (p.max_blocks + ip::TOPK_CHUNK - 1) / ip::TOPK_CHUNK;
+  if (scores_given) {
+    p.rows_per_chunk = n_q;
+  } else {
+    const size_t per_row = (size_t)p.ld * 4;
+    p.rows_per_chunk = (int)std::max<size_t>(1, std::min<size_t>(n_q, kScoreBudget / per_row));
+  }
+  p.score_bytes = scores_given ? 0 : (size_t)p.rows_per_chunk * p.ld * 4;
+  p.cand_bytes = p.n_chunks > 1 ? (size_t)p.rows_per_chunk * p.n_chunks * (size_t)(top_k - 1) * 8 : 0;
+  p.score_bytes = (p.score_bytes + 255) & ~size_t(255);
+  p.total = p.score_bytes + p.cand_bytes;
+  return p;
+}
+
+struct AttnPlan {
+  int n_split, blocks_per_split;
+  size_t bytes;
+};
+
+AttnPlan attn_plan(int n_q, int n_heads, int dv, int top_k, int q_dtype) {
+  AttnPlan p;
+  p.n_split = 1;
+  p.blocks_per_split = top_k;
+  if (q_dtype == IP_BF16) {
+    const int nsub = (top_k + 15) / 16;                 // 64-token sub-tiles
+    const int want = (kTargetWorkgroups + n_q - 1) / std::max(1, n_q);
+    const int max_split = std::max(1, nsub / 2);        // >= 2 sub-tiles per split
+    const int ns = std::max(1, std::min(want, max_split));
+    const int sub_per = (nsub + ns - 1) / ns;
+    p.blocks_per_split = sub_per * 16;
+    p.n_split = (top_k + p.blocks_per_split - 1) / p.blocks_per_split;
+  }
+  p.bytes = p.n_split > 1 ? (size_t)n_q * p.n_split * n_heads * ((size_t)dv + 2) * 4 : 0;
+  return p;
+}
+
+}  // namespace
+
+namespace ip {
+void hook_before(int id, hipStream_t s) {
+  if (g_hook.id == id && g_hook.start) hipEventRecord(g_hook.start, s);
+}
+void hook_after(int id, hipStream_t s) {
+  if (g_hook.id == id && g_hook.stop) {
+    hipEventRecord(g_hook.stop, s);
+    g_hook = Hook{};
+  }
+}
+}  // namespace ip
+
+extern "C" {
+
+const char* ip_last_error(void) { return g_err.c_str(); }
+const char* ip_version(void) { return "0.1.0"; }
+
+ip_status ip_time_next_launch(int32_t kernel_id, hipEvent_t start, hipEvent_t stop) {
+  if (!start || !stop) { g_hook = Hook{}; return IP_OK; }
+  if (kernel_id < ip::K_COMPRESS || kernel_id > ip::K_COMBINE)
+    return fail(IP_EINVAL, "ip_time_next_launch: unknown kernel id %d", kernel_id);
+  g_hook.id = kernel_id;
+  g_hook.start = start;
+  g_hook.stop = stop;
+  return IP_OK;
+}
+
+int64_t index_scores_ld(int32_t max_seq_len) {
+  const int64_t n = std::max<int64_t>(1, max_seq_len / 4);
+  return (n + 63) & ~int64_t(63);
+}
+
+// ------------------------------------------------------------------ IndexPool
+ip_status indexpool_compress(const ip_seqs* seqs, const int32_t* block_begin, int32_t max_blocks,
+                             const ip_cache* keys, const float* logits, const ip_cache* pooled,
+                             hipStream_t stream) {
+  const char* fn = "indexpool_compress";
+  if (ip_status st = check_seqs(seqs, fn)) return st;
+  if (ip_status st = check_cache(keys, fn, "keys")) return st;
+  if (ip_status st = check_cache(pooled, fn, "pooled")) return st;
+  if (!logits) return fail(IP_EINVAL, "%s: logits is NULL", fn);
+  if (keys->dtype != pooled->dtype || keys->row_dim != pooled->row_dim)
+    return fail(IP_EINVAL, "%s: keys and pooled must share dtype and row_dim", fn);
+  ip::CompressArgs a;
+  a.L = layout_of(seqs);
+  a.batch = seqs->batch;
+  a.block_begin = block_begin;
+  a.max_blocks = max_blocks > 0 ? max_blocks : seqs->max_seq_len / 4;
+  a.keys = (const uint8_t*)keys->data;
+  a.key_stride = keys->row_stride;
+  a.key_scale = keys->scale;
+  a.logits = logits;
+  a.out = (uint8_t*)pooled->data;
+  a.out_stride = pooled->row_stride;
+  a.out_scale = pooled->scale;
+  a.dim = keys->row_dim;
+  if (seqs->batch > 65535) return fail(IP_EUNSUPPORTED, "%s: batch > 65535", fn);
+  if (keys->dtype == IP_FP8_E4M3FN) {
+    if (keys->row_dim != 128) return fail(IP_EUNSUPPORTED, "%s: FP8 keys need row_dim 128 (got %d)", fn, keys->row_dim);
+    return device_status(ip::launch_compress_fp8(a, stream), fn);
+  }
+  if (keys->dtype == IP_F32) {
+    if (keys->row_dim > 256 || keys->row_dim % 4)
+      return fail(IP_EUNSUPPORTED, "%s: F32 keys need row_dim <= 256 and a multiple of 4", fn);
+    return device_status(ip::launch_compress_f32(a, stream), fn);
+  }
+  return fail(IP_EUNSUPPORTED, "%s: keys must be FP8 or F32", fn);
+}
+
+// ------------------------------------------------------------------ indexer + top-k
+size_t index_score_topk_workspace_bytes(const ip_seqs* seqs, int32_t n_q, int32_t top_k,
+                                        int32_t scores_given) {
+  if (!seqs || n_q < 1 || top_k < 1 || seqs->max_seq_len < 1) return 0;
+  return score_plan(seqs, n_q, top_k, scores_given != 0).total;
+}
+
+ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
+                           const int32_t* q_pos, const void* q_idx, int32_t q_dtype,
+                           int32_t n_heads, int32_t head_dim, const float* gates,
+                           const ip_cache* pooled, int32_t top_k, int32_t* out_idx,
+                           float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "index_score_topk";
+  if (ip_status st = check_seqs(seqs, fn)) return st;
+  if (ip_status st = check_cache(pooled, fn, "pooled")) return st;
+  if (n_q < 1) return fail(IP_EINVAL, "%s: n_q must be >= 1", fn);
+  if (!q_idx || !gates || !out_idx) return fail(IP_EINVAL, "%s: q_idx, gates and out_idx are required", fn);
+  if (top_k < 1 || top_k > 2048) return fail(IP_EUNSUPPORTED, "%s: top_k must be in 1..2048 (got %d)", fn, top_k);
+  if (!q_seq && n_q > seqs->batch) return fail(IP_EINVAL, "%s: q_seq is NULL but n_q > batch", fn);
+  if (pooled->row_dim != head_dim) return fail(IP_EINVAL, "%s: head_dim %d != pooled row_dim %d", fn, head_dim, pooled->row_dim);
+  const bool fp8 = pooled->dtype == IP_FP8_E4M3FN;
+  if (fp8) {
+    if (q_dtype != IP_BF16 || n_heads != 32 || head_dim != 128)
+      return fail(IP_EUNSUPPORTED, "%s: FP8 keys need BF16 queries with 32 heads x 128 dims", fn);
+  } else if (pooled->dtype == IP_F32) {
+    if (q_dtype != IP_F32 || n_heads < 1 || n_heads > 64 || head_dim < 1 || n_heads * head_dim > 4096)
+      return fail(IP_EUNSUPPORTED, "%s: F32 keys need F32 queries with n_heads <= 64 and n_heads*head_dim <= 4096", fn);
+  } else {
+    return fail(IP_EUNSUPPORTED, "%s: pooled keys must be FP8 or F32", fn);
+  }
+  const ScorePlan plan = score_plan(seqs, n_q, top_k, scores != nullptr);
+  if ((int64_t)plan.n_chunks * (top_k - 1) > ip::TOPK_MERGE_CAP)
+    return fail(IP_EUNSUPPORTED, "%s: %d score chunks x (top_k-1) exceeds the merge capacity %d; lower max_seq_len or top_k",
+                fn, plan.n_chunks, ip::TOPK_MERGE_CAP);
+  if (plan.total > 0 && (!ws || ws_bytes < plan.total))
+    return fail(IP_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.total, ws ? ws_bytes : 0);
+  if (((uintptr_t)ws & 255) != 0) return fail(IP_EINVAL, "%s: ws must be 256-byte aligned", fn);
+
+  float* score_buf = scores ? scores : (float*)ws;
+  uint32_t* cand_key = (uint32_t*)((char*)ws + plan.score_bytes);
+  int32_t* cand_idx = (int32_t*)(cand_key + (plan.cand_bytes / 8));
+
+  for (int row0 = 0; row0 < n_q; row0 += plan.rows_per_chunk) {
+    const int nr = std::min(plan.rows_per_chunk, n_q - row0);
+    ip::ScoreArgs sa;
+    sa.L = layout_of(seqs);
+    sa.row0 = row0;
+    sa.n_rows = nr;
+    sa.q_seq = q_seq;
+    sa.q_pos = q_pos;
+    sa.q = q_idx;
+    sa.gates = gates;
+    sa.keys = (const uint8_t*)pooled->data;
+    sa.key_stride = pooled->row_stride;
+    sa.key_scale = pooled->scale;
+    sa.scores = scores ? score_buf + (int64_t)row0 * plan.ld : score_buf;
+    sa.ld = plan.ld;
+    sa.heads = n_heads;
+    sa.dim = head_dim;
+    sa.max_blocks = plan.max_blocks;
+    // the kernels index scores by (r - row0)
+    ip_status st = device_status(fp8 ? ip::launch_score_fp8_bf16(sa, stream) : ip::launch_score_f32(sa, stream), fn);
+    if (st) return st;
+    ip::TopkArgs ta;
+    ta.L = sa.L;
+    ta.row0 = row0;
+    ta.n_rows = nr;
+    ta.q_seq = q_seq;
+    ta.q_pos = q_pos;
+    ta.scores = sa.scores;
+    ta.ld = plan.ld;
+    ta.top_k = top_k;
+    ta.out = out_idx;
+    ta.cand_key = cand_key;
+    ta.cand_idx = cand_idx;
+    ta.n_chunks = plan.n_chunks;
+    st = device_status(ip::launch_topk(ta, stream), fn);
+    if (st) return st;
+  }
+  return IP_OK;
+}
+
+// ------------------------------------------------------------------ sparse attention
+size_t sparse_attn_workspace_bytes(int32_t n_q, int32_t n_heads, int32_t dv, int32_t top_k,
+                                   int32_t q_dtype) {
+  if (n_q < 1 || n_heads < 1 || dv < 1 || top_k < 1) return 0;
+  return attn_plan(n_q, n_heads, dv, top_k, q_dtype).bytes;
+}
+
+static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
+                             const int32_t* q_pos, const void* q, int32_t q_dtype, int32_t n_heads,
+                             int32_t dk, int32_t dv, float scale, const ip_cache* k, const ip_cache* v,
+                             const int32_t* sel_idx, int32_t top_k, void* out, float* lse, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  if (ip_status st = check_seqs(seqs, fn)) return st;
+  if (ip_status st = check_cache(k, fn, "k")) return st;
+  if (n_q < 1) return fail(IP_EINVAL, "%s: n_q must be >= 1", fn);
+  if (!q || !sel_idx || !out) return fail(IP_EINVAL, "%s: q, sel_idx and out are required", fn);
+  if (top_k < 1 || top_k > 2048) return fail(IP_EUNSUPPORTED, "%s: top_k must be in 1..2048 (got %d)", fn, top_k);
+  if (!q_seq && n_q > seqs->batch) return fail(IP_EINVAL, "%s: q_seq is NULL but n_q > batch", fn);
+  if (!(scale > 0.f)) return fail(IP_EINVAL, "%s: scale must be positive", fn);
+  ip::AttnArgs a;
+  a.L = layout_of(seqs);
+  a.row0 = 0;
+  a.n_rows = n_q;
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.q = q;
+  a.k = (const uint8_t*)k->data;
+  a.k_stride = k->row_stride;
+  a.sel = sel_idx;
+  a.top_k = top_k;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  a.heads = n_heads;
+  a.dk = dk;
+  a.dv = dv;
+  if (q_dtype == IP_BF16) {
+    if (k->dtype != IP_BF16 || n_heads != ip::LAT_H || dk != ip::LAT_DK || dv != ip::LAT_DV || k->row_dim < ip::LAT_DK)
+      return fail(IP_EUNSUPPORTED, "%s: BF16 attention needs 64 heads, dk 576, dv 512 over a BF16 latent cache", fn);
+    if (v) return fail(IP_EUNSUPPORTED, "%s: BF16 latent attention takes V from the latent rows; pass v = NULL", fn);
+    if (n_q > 65535) return fail(IP_EUNSUPPORTED, "%s: n_q > 65535", fn);
+    const AttnPlan p = attn_plan(n_q, n_heads, dv, top_k, q_dtype);
+    if (p.bytes > 0 && (!ws || ws_bytes < p.bytes))
+      return fail(IP_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, p.bytes, ws ? ws_bytes : 0);
+    if (((uintptr_t)ws & 15) != 0) return fail(IP_EINVAL, "%s: ws must be 16-byte aligned", fn);
+    a.v = nullptr;
+    a.v_stride = 0;
+    a.n_split = p.n_split;
+    a.blocks_per_split = p.blocks_per_split;
+    a.part_o = (float*)ws;
+    a.part_ml = p.n_split > 1 ? (float*)ws + (size_t)n_q * p.n_split * n_heads * dv : nullptr;
+    return device_status(ip::launch_attn_bf16(a, stream), fn);
+  }
+  if (q_dtype == IP_F32) {
+    if (ip_status st = check_cache(v, fn, "v")) return st;
+    if (k->dtype != IP_F32 || v->dtype != IP_F32 || n_heads < 1 || n_heads > 16 || dk < 1 || dk > 128 ||
+        dv < 1 || dv > 128 || k->row_dim < dk || v->row_dim < dv)
+      return fail(IP_EUNSUPPORTED, "%s: F32 attention needs F32 k/v caches, n_heads <= 16, dk and dv <= 128", fn);
+    a.v = (const uint8_t*)v->data;
+    a.v_stride = v->row_stride;
+    a.n_split = 1;
+    a.blocks_per_split = top_k;
+    a.part_o = a.part_ml = nullptr;
+    return device_status(ip::launch_attn_f32(a, stream), fn);
+  }
+  return fail(IP_EUNSUPPORTED, "%s: q must be BF16 or F32", fn);
+}
+
+ip_status sparse_attn_decode(const ip_seqs* seqs, const void* q, int32_t q_dtype, int32_t n_heads,
+                             int32_t dk, int32_t dv, float scale, const ip_cache* k, const ip_cache* v,
+                             const int32_t* sel_idx, int32_t top_k, void* out, float* lse, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  if (!seqs) return fail(IP_EINVAL, "sparse_attn_decode: seqs is NULL");
+  return attn_common("sparse_attn_decode", seqs, seqs->batch, nullptr, nullptr, q, q_dtype, n_heads, dk, dv,
+                     scale, k, v, sel_idx, top_k, out, lse, ws, ws_bytes, stream);
+}
+
+ip_status sparse_attn_prefill(const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq, const int32_t* q_pos,
+                              const void* q, int32_t q_dtype, int32_t n_heads, int32_t dk, int32_t dv,
+                              float scale, const ip_cache* k, const ip_cache* v, const int32_t* sel_idx,
+                              int32_t top_k, void* out, float* lse, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (!q_pos) return fail(IP_EINVAL, "sparse_attn_prefill: q_pos is required");
+  return attn_common("sparse_attn_prefill", seqs, n_q, q_seq, q_pos, q, q_dtype, n_heads, dk, dv, scale, k, v,
+                     sel_idx, top_k, out, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Shared device helpers for the gfx950 kernels of libindexpool.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ip {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- cache layout
+// Token t of sequence b: paged -> page_table[b][t / page_tokens] * page_tokens + t % page_tokens,
+// contiguous -> b * seq_stride + t.  Pooled block j uses page_tokens / 4 and seq_stride / 4.
+struct Layout {
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int32_t max_pages;
+  int32_t page_tokens;
+  int64_t seq_stride;
+
+  __device__ __forceinline__ int64_t tok_row(int b, int64_t t) const {
+    if (page_table) {
+      const int64_t pg = page_table[(int64_t)b * max_pages + t / page_tokens];
+      return pg * page_tokens + t % page_tokens;
+    }
+    return (int64_t)b * seq_stride + t;
+  }
+  __device__ __forceinline__ int64_t pool_row(int b, int64_t j) const {
+    if (page_table) {
+      const int pr = page_tokens >> 2;
+      const int64_t pg = page_table[(int64_t)b * max_pages + j / pr];
+      return pg * pr + j % pr;
+    }
+    return (int64_t)b * (seq_stride >> 2) + j;
+  }
+};
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// round to nearest even; inputs here are finite
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- fp8 e4m3fn
+// Four codes (one dword, byte 0 first) -> four floats, by the hardware converter
+// (gfx950 decodes the OCP e4m3fn format: bias 7, max 448).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+  f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = hi[0]; f[3] = hi[1];
+}
+
+// Eight codes -> eight bf16 (exact: every e4m3fn value is a bf16 value, so the
+// top half of the float is the bf16 pattern).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  float f[8];
+  fp8x4_to_f32(w0, f);
+  fp8x4_to_f32(w1, f + 4);
+  u32x4_t p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    p[i] = (__float_as_uint(f[2 * i]) >> 16) | (__float_as_uint(f[2 * i + 1]) & 0xFFFF0000u);
+  return __builtin_bit_cast(bf16x8_t, p);
+}
+
+// float -> e4m3fn code, round to nearest even.  |x| must already be <= 448.
+// Normal range (|x| >= 2^-6): round the float's mantissa to 3 bits, then rebias the
+// exponent from 127 to 7.  Below 2^-6 the code is the nearest multiple of 2^-9
+// (8 * 2^-9 = 2^-6 is code 0x08, so the two branches meet).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a < 0x3C800000u) {                       // < 2^-6
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;   // 8-bit exp + 3-bit mantissa
+    code = r - (120u << 3);
+  }
+  return code | sign;
+}
+
+// ---------------------------------------------------------------- order-preserving keys
+// float -> uint32 whose unsigned order is the float order (-0 folded into +0).
+// Key 0 is never produced for a non-NaN float and marks "no element".
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- block scans
+// Exclusive prefix sum of one int per thread over a block of NT threads (wave64).
+// tmp: >= NT/64 + 1 ints of LDS.  Returns the exclusive prefix; *total = block sum.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wv] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int s = 0;
+    for (int i = 0; i < NT / 64; ++i) { int t = tmp[i]; tmp[i] = s; s += t; }
+    tmp[NT / 64] = s;
+  }
+  __syncthreads();
+  const int r = tmp[wv] + x - v;
+  *total = tmp[NT / 64];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace ip

@@ -1,0 +1,96 @@
+// Host-side launch interface of the gfx950 kernels (internal to libindexpool).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "common.hpp"
+
+namespace ip {
+
+enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3, K_ATTN = 4, K_COMBINE = 5 };
+
+// Records the timing hook's events around one launch if it targets `id`.
+void hook_before(int id, hipStream_t s);
+void hook_after(int id, hipStream_t s);
+
+// ------------------------------------------------------------ IndexPool
+struct CompressArgs {
+  Layout L;
+  int batch;
+  const int32_t* block_begin;  // [batch] or null
+  int max_blocks;              // blocks per sequence covered by the grid
+  const uint8_t* keys;         // token key rows
+  int64_t key_stride;          // bytes
+  const float* key_scale;      // [token rows] (fp8) or null
+  const float* logits;         // [token rows]
+  uint8_t* out;                // pooled rows
+  int64_t out_stride;          // bytes
+  float* out_scale;            // [pooled rows] (fp8) or null
+  int dim;                     // elements per key row
+};
+hipError_t launch_compress_fp8(const CompressArgs& a, hipStream_t s);
+hipError_t launch_compress_f32(const CompressArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------ indexer scoring
+struct ScoreArgs {
+  Layout L;
+  int row0, n_rows;            // query rows [row0, row0 + n_rows)
+  const int32_t* q_seq;        // [n_q] or null
+  const int32_t* q_pos;        // [n_q] or null
+  const void* q;               // [n_q, heads, dim]
+  const float* gates;          // [n_q, heads]
+  const uint8_t* keys;         // pooled rows
+  int64_t key_stride;
+  const float* key_scale;      // [pooled rows] (fp8) or null
+  float* scores;               // [n_rows, ld], row r - row0
+  int64_t ld;
+  int heads, dim;
+  int max_blocks;              // key range covered by the grid
+};
+hipError_t launch_score_fp8_bf16(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------ top-k selection
+struct TopkArgs {
+  Layout L;
+  int row0, n_rows;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  const float* scores;         // [n_rows, ld]
+  int64_t ld;
+  int top_k;
+  int32_t* out;                // [n_q, top_k], row r
+  uint32_t* cand_key;          // [n_rows, n_chunks, top_k - 1]
+  int32_t* cand_idx;           // same
+  int n_chunks;                // chunks per row covered by the grid
+};
+constexpr int TOPK_CHUNK = 8192;        // stage-1 elements per workgroup
+constexpr int TOPK_MERGE_CAP = 32768;   // stage-2 candidate slots per row
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------ sparse attention
+struct AttnArgs {
+  Layout L;
+  int row0, n_rows;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  const void* q;               // [n_q, H, dk]
+  const uint8_t* k;            // K rows (bf16 latent or f32)
+  int64_t k_stride;
+  const uint8_t* v;            // V rows (f32 path)
+  int64_t v_stride;
+  const int32_t* sel;          // [n_q, top_k]
+  int top_k;
+  float scale;
+  void* out;                   // [n_q, H, dv]
+  float* lse;                  // [n_q, H] or null
+  float* part_o;               // [n_rows, n_split, H, dv] (split > 1)
+  float* part_ml;              // [n_rows, n_split, H, 2]
+  int n_split, blocks_per_split;
+  int heads, dk, dv;
+};
+// bf16 latent MQA: 64 heads, dk 576, dv 512
+constexpr int LAT_H = 64, LAT_DK = 576, LAT_DV = 512;
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+
+}  // namespace ip

@@ -1,0 +1,142 @@
+// Lightweight indexer: S_j = sum_h g_h * relu(q_h . K_j) for every pooled block j
+// before the query's own block.  Reading notes "GLM-5.3-Flash: Hybrid Attention,
+// IndexPool, and Vision-in-the-Loop", section 2 "Hybrid Attention: Linear State +
+// Sparse Retrieval" (sparse attention as the global retriever through a lightweight
+// indexer; DeepSeek-V3.2's DSA indexer as its lineage).
+//
+// fp8 keys x bf16 queries: the heads x keys product is a dense contraction
+// (32 heads x 128 dims x keys), so it runs on bf16 MFMA (v_mfma_f32_32x32x16_bf16)
+// with the 32 heads as M and 32 keys per tile as N.  The fp8 codes are widened to
+// bf16 exactly, so every product is exact in the fp32 accumulator.  The per-block
+// scale sigma_j > 0 is applied after the ReLU (relu(sigma x) = sigma relu(x)).
+// The output layout puts one key per lane and 16 heads per lane, so the gated
+// head-sum is 16 local FMAs plus one cross-half exchange.
+#include "kernels.hpp"
+
+namespace ip {
+
+namespace {
+
+constexpr int NT = 256;
+constexpr int KEYS_PER_WG = 256;   // 4 waves x 2 tiles x 32 keys
+constexpr int HI = 32, DI = 128;
+
+// rows_per_wg query rows share one key chunk held in registers
+template <int RPW>
+__global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int kl = lane & 31, hh = lane >> 5;
+  const int kc0 = blockIdx.x * KEYS_PER_WG;
+  const int rbeg = a.row0 + blockIdx.y * RPW;
+  const int rend = min(rbeg + RPW, a.row0 + a.n_rows);
+
+  bf16x8_t kf[2][8];
+  float ksig[2] = {0.f, 0.f};
+  int cur_b = -1;
+
+  for (int r = rbeg; r < rend; ++r) {
+    const int b = a.q_seq ? a.q_seq[r] : r;
+    const int p = a.q_pos ? a.q_pos[r] : a.L.seq_lens[b] - 1;
+    const int nel = p >> 2;                    // eligible blocks j < b_q
+    if (kc0 >= nel) continue;                  // uniform over the workgroup
+    if (b != cur_b) {
+      cur_b = b;
+      const int nrows = (a.L.seq_lens[b] + 3) >> 2;   // pooled rows that exist
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int j = kc0 + wv * 64 + t * 32 + kl;
+        if (j < nrows) {
+          const int64_t row = a.L.pool_row(b, j);
+          const u32x4_t* src = (const u32x4_t*)(a.keys + row * a.key_stride + hh * 64);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const u32x4_t w = src[c];
+            kf[t][2 * c] = fp8x8_to_bf16x8(w[0], w[1]);
+            kf[t][2 * c + 1] = fp8x8_to_bf16x8(w[2], w[3]);
+          }
+          ksig[t] = a.key_scale[row];
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) kf[t][c] = bf16x8_t{};
+          ksig[t] = 0.f;
+        }
+      }
+    }
+    // query fragment: head kl, dims hh*64 .. hh*64+63 (the same dims as the key half)
+    bf16x8_t qf[8];
+    const u32x4_t* qsrc = (const u32x4_t*)((const uint16_t*)a.q + ((int64_t)r * HI + kl) * DI + hh * 64);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qf[c] = __builtin_bit_cast(bf16x8_t, qsrc[c]);
+    // gates of the 16 heads this lane accumulates: rows (i/4)*8 + hh*4 + i%4
+    float g[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) g[i] = a.gates[(int64_t)r * HI + (i >> 2) * 8 + hh * 4 + (i & 3)];
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x16_t acc = {};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[c], kf[t][c], acc, 0, 0, 0);
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part = fmaf(g[i], fmaxf(acc[i], 0.f), part);
+      part += __shfl_xor(part, 32);
+      const int j = kc0 + wv * 64 + t * 32 + kl;
+      if (hh == 0 && j < nel) a.scores[(int64_t)(r - a.row0) * a.ld + j] = part * ksig[t];
+    }
+  }
+}
+
+// float keys and queries (small geometries): one thread per key, queries in LDS.
+constexpr int F32_MAX_Q = 64 * 256;
+__global__ __launch_bounds__(NT) void score_f32_kernel(ScoreArgs a) {
+  __shared__ float qs[F32_MAX_Q / 4];          // heads * dim <= 4096 floats
+  __shared__ float gs[64];
+  const int r = a.row0 + blockIdx.y;
+  const int b = a.q_seq ? a.q_seq[r] : r;
+  const int p = a.q_pos ? a.q_pos[r] : a.L.seq_lens[b] - 1;
+  const int nel = p >> 2;
+  const int j = blockIdx.x * NT + threadIdx.x;
+  if ((int)(blockIdx.x * NT) >= nel) return;
+  const int HD = a.heads * a.dim;
+  const float* q = (const float*)a.q + (int64_t)r * HD;
+  for (int i = threadIdx.x; i < HD; i += NT) qs[i] = q[i];
+  for (int i = threadIdx.x; i < a.heads; i += NT) gs[i] = a.gates[(int64_t)r * a.heads + i];
+  __syncthreads();
+  if (j >= nel) return;
+  const float* k = (const float*)(a.keys + a.L.pool_row(b, j) * a.key_stride);
+  float s = 0.f;
+  for (int h = 0; h < a.heads; ++h) {
+    float d = 0.f;
+    for (int e = 0; e < a.dim; ++e) d = fmaf(qs[h * a.dim + e], k[e], d);
+    s = fmaf(gs[h], fmaxf(d, 0.f), s);
+  }
+  a.scores[(int64_t)(r - a.row0) * a.ld + j] = s;
+}
+
+}  // namespace
+
+hipError_t launch_score_fp8_bf16(const ScoreArgs& a, hipStream_t s) {
+  if (a.n_rows <= 0 || a.max_blocks <= 0) return hipSuccess;
+  const unsigned gx = (a.max_blocks + KEYS_PER_WG - 1) / KEYS_PER_WG;
+  hook_before(K_SCORE, s);
+  if (a.n_rows >= 64) {
+    constexpr int R = 16;
+    hipLaunchKernelGGL(score_fp8_bf16_kernel<R>, dim3(gx, (a.n_rows + R - 1) / R), dim3(NT), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(score_fp8_bf16_kernel<1>, dim3(gx, a.n_rows), dim3(NT), 0, s, a);
+  }
+  hook_after(K_SCORE, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s) {
+  if (a.n_rows <= 0 || a.max_blocks <= 0) return hipSuccess;
+  dim3 grid((a.max_blocks + NT - 1) / NT, a.n_rows);
+  hook_before(K_SCORE, s);
+  hipLaunchKernelGGL(score_f32_kernel, grid, dim3(NT), 0, s, a);
+  hook_after(K_SCORE, s);
+  return hipGetLastError();
+}
+
+}  // namespace ip

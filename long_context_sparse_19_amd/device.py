@@ -1,0 +1,123 @@
+"""Device-resident copies of a workload's inputs and the three-stage pipeline.
+
+Thin glue over the C ABI (``_lib``): it uploads the seeded host arrays once,
+allocates outputs and workspaces with torch, and calls indexpool_compress,
+index_score_topk and sparse_attn_decode / sparse_attn_prefill.  All arithmetic
+runs in the HIP kernels behind those calls.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+from .inputs import Inputs
+
+
+def _dev(x: np.ndarray, device, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(device)
+
+
+@dataclass
+class DeviceInputs:
+    inp: Inputs
+    seqs: _lib.Seqs
+    keys: _lib.Cache          # token-level index keys
+    logits: torch.Tensor
+    pooled: _lib.Cache        # pooled keys (output of compress)
+    kv: _lib.Cache            # latent (bf16) or K (f32)
+    v: Optional[_lib.Cache]   # V (f32 only)
+    q: torch.Tensor
+    q_idx: torch.Tensor
+    gates: torch.Tensor
+    q_seq: torch.Tensor
+    q_pos: torch.Tensor
+    top_k: int
+    scale: float
+    dv: int
+
+    @property
+    def n_q(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def is_decode(self) -> bool:
+        return self.inp.w.mode == "decode"
+
+
+def upload(inp: Inputs, device="cuda") -> DeviceInputs:
+    w = inp.w
+    seq_lens = _dev(inp.seq_lens, device)
+    pt = None if inp.page_table is None else _dev(inp.page_table, device)
+    seqs = _lib.Seqs(seq_lens, int(inp.seq_lens.max()), pt, inp.page_tokens, inp.seq_stride)
+    R = inp.n_rows_tok
+    if inp.idx_scale is not None:
+        keys = _lib.Cache(_dev(inp.idx_keys, device), _dev(inp.idx_scale, device))
+        pooled = _lib.Cache(torch.zeros((R // 4, inp.idx_keys.shape[1]), dtype=torch.uint8, device=device),
+                            torch.zeros(R // 4, dtype=torch.float32, device=device))
+    else:
+        keys = _lib.Cache(_dev(inp.idx_keys, device))
+        pooled = _lib.Cache(torch.zeros((R // 4, inp.idx_keys.shape[1]), dtype=torch.float32, device=device))
+    logits = _dev(inp.pool_logits, device)
+    kv = v = None
+    if w.attn_dtype == "bf16":
+        if inp.latent is not None:
+            kv = _lib.Cache(_dev(inp.latent, device, torch.bfloat16))
+        q = _dev(inp.q, device, torch.bfloat16)
+        q_idx = _dev(inp.q_idx, device, torch.bfloat16)
+    else:
+        if inp.k_cache is not None:
+            kv = _lib.Cache(_dev(inp.k_cache, device))
+            v = _lib.Cache(_dev(inp.v_cache, device))
+        q = _dev(inp.q, device)
+        q_idx = _dev(inp.q_idx, device)
+    return DeviceInputs(inp=inp, seqs=seqs, keys=keys, logits=logits, pooled=pooled, kv=kv, v=v, q=q,
+                        q_idx=q_idx, gates=_dev(inp.gates, device), q_seq=_dev(inp.q_seq, device),
+                        q_pos=_dev(inp.q_pos, device), top_k=w.top_k, scale=w.scale, dv=w.dv)
+
+
+def compress(d: DeviceInputs, block_begin: Optional[torch.Tensor] = None, max_blocks: int = 0,
+             stream=None) -> None:
+    _lib.indexpool_compress(d.seqs, d.keys, d.logits, d.pooled, block_begin, max_blocks, stream)
+
+
+class Workspaces:
+    """Outputs and workspaces of one pipeline pass, allocated once."""
+
+    def __init__(self, d: DeviceInputs, keep_scores: bool = False):
+        dev = d.q.device
+        self.sel = torch.empty((d.n_q, d.top_k), dtype=torch.int32, device=dev)
+        self.scores = None
+        if keep_scores:
+            ld = _lib.index_scores_ld(d.seqs.max_seq_len)
+            self.scores = torch.zeros((d.n_q, ld), dtype=torch.float32, device=dev)
+        nb = _lib.index_score_topk_workspace_bytes(d.seqs, d.n_q, d.top_k, keep_scores)
+        self.ws_idx = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        qdt = _lib.IP_BF16 if d.q.dtype == torch.bfloat16 else _lib.IP_F32
+        na = _lib.sparse_attn_workspace_bytes(d.n_q, d.q.shape[1], d.dv, d.top_k, qdt)
+        self.ws_attn = torch.empty(max(na, 16), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((d.n_q, d.q.shape[1], d.dv), dtype=d.q.dtype, device=dev)
+        self.lse = torch.empty((d.n_q, d.q.shape[1]), dtype=torch.float32, device=dev)
+
+
+def score_topk(d: DeviceInputs, ws: Workspaces, stream=None) -> None:
+    q_seq = None if d.is_decode else d.q_seq
+    q_pos = None if d.is_decode else d.q_pos
+    _lib.index_score_topk(d.seqs, d.q_idx, d.gates, d.pooled, d.top_k, ws.sel, q_seq=q_seq, q_pos=q_pos,
+                          scores=ws.scores, ws=ws.ws_idx, stream=stream)
+
+
+def attention(d: DeviceInputs, ws: Workspaces, sel: Optional[torch.Tensor] = None, stream=None) -> None:
+    sel = ws.sel if sel is None else sel
+    if d.is_decode:
+        _lib.sparse_attn_decode(d.seqs, d.q, d.kv, d.v, sel, ws.out, d.scale, d.dv, lse=ws.lse,
+                                ws=ws.ws_attn, stream=stream)
+    else:
+        _lib.sparse_attn_prefill(d.seqs, d.q, d.kv, d.v, sel, ws.out, d.scale, d.dv, d.q_seq, d.q_pos,
+                                 lse=ws.lse, ws=ws.ws_attn, stream=stream)

@@ -1,0 +1,154 @@
+"""The C ABI on the host: every declared symbol is exported, and arguments the host
+can check are rejected before anything is launched (no GPU needed: these calls
+return before touching the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "indexpool.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    lib_path = os.path.join(ROOT, "long_context_sparse_19_amd", "libindexpool.so")
+    if not os.path.exists(lib_path):
+        from long_context_sparse_19_amd.build import build
+        build()
+    from long_context_sparse_19_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined", "sizeof"})
+
+
+def test_header_declares_the_pipeline_calls():
+    names = declared_functions()
+    for fn in ("indexpool_compress", "index_score_topk", "sparse_attn_decode", "sparse_attn_prefill",
+               "ip_last_error"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for fn in declared_functions():
+        assert hasattr(lib, fn), fn
+    assert set(L.EXPORTED) == set(declared_functions())
+
+
+FAKE = 1 << 20   # a non-null, 256-aligned address; never dereferenced by these calls
+
+
+def seqs(**kw):
+    from long_context_sparse_19_amd._lib import IpSeqs
+    base = dict(batch=2, max_seq_len=1024, seq_lens=FAKE, page_table=None, max_pages=0, page_tokens=0,
+                seq_stride=1024)
+    base.update(kw)
+    return IpSeqs(**base)
+
+
+def cache(L, dtype=None, row_dim=128, stride=128, scale=FAKE, data=FAKE):
+    dtype = L.IP_FP8_E4M3FN if dtype is None else dtype
+    return L.IpCache(data, scale, dtype, row_dim, stride)
+
+
+def compress(L, s, keys, logits=FAKE, pooled=None):
+    pooled = keys if pooled is None else pooled
+    return L.LIB.indexpool_compress(ctypes.byref(s), None, 0, ctypes.byref(keys), logits, ctypes.byref(pooled),
+                                    None)
+
+
+def test_compress_rejects_bad_arguments(L):
+    good = cache(L)
+    assert compress(L, seqs(batch=0), good) == L.IP_EINVAL
+    assert "batch" in L.LIB.ip_last_error().decode()
+    assert compress(L, seqs(seq_lens=None), good) == L.IP_EINVAL
+    assert compress(L, seqs(seq_stride=1022), good) == L.IP_EINVAL
+    assert compress(L, seqs(page_table=FAKE, max_pages=4, page_tokens=62), good) == L.IP_EINVAL
+    assert compress(L, seqs(page_table=FAKE, max_pages=4, page_tokens=64), good) == L.IP_EINVAL  # 4*64 < 1024
+    assert compress(L, seqs(), good, logits=None) == L.IP_EINVAL
+    assert compress(L, seqs(), cache(L, scale=None)) == L.IP_EINVAL
+    assert compress(L, seqs(), cache(L, row_dim=64, stride=64)) == L.IP_EUNSUPPORTED
+    assert compress(L, seqs(), cache(L, stride=120)) == L.IP_EINVAL
+    assert compress(L, seqs(), cache(L, dtype=L.IP_BF16, stride=256)) == L.IP_EUNSUPPORTED
+    assert compress(L, seqs(), good, pooled=cache(L, dtype=L.IP_F32, stride=512)) == L.IP_EINVAL
+    assert compress(L, seqs(), cache(L, dtype=L.IP_F32, row_dim=512, stride=2048, scale=None)) == L.IP_EUNSUPPORTED
+
+
+def score(L, s, n_q=2, q_dtype=None, H=32, D=128, pooled=None, top_k=512, ws=FAKE, ws_bytes=1 << 30,
+          q_seq=None):
+    q_dtype = L.IP_BF16 if q_dtype is None else q_dtype
+    pooled = cache(L) if pooled is None else pooled
+    return L.LIB.index_score_topk(ctypes.byref(s), n_q, q_seq, None, FAKE, q_dtype, H, D, FAKE,
+                                  ctypes.byref(pooled), top_k, FAKE, None, ws, ws_bytes, None)
+
+
+def test_score_topk_rejects_bad_arguments(L):
+    s = seqs()
+    assert score(L, s, top_k=0) == L.IP_EUNSUPPORTED
+    assert score(L, s, top_k=4096) == L.IP_EUNSUPPORTED
+    assert score(L, s, n_q=0) == L.IP_EINVAL
+    assert score(L, s, n_q=3) == L.IP_EINVAL            # more rows than sequences, no q_seq
+    assert score(L, s, H=16) == L.IP_EUNSUPPORTED
+    assert score(L, s, D=64) == L.IP_EINVAL             # head_dim != pooled row_dim
+    assert score(L, s, q_dtype=L.IP_F32) == L.IP_EUNSUPPORTED
+    assert score(L, s, ws=None) == L.IP_EWORKSPACE
+    need = L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 2, 512, 0)
+    assert need > 0
+    assert score(L, s, ws_bytes=need - 1) == L.IP_EWORKSPACE
+    assert "workspace" in L.LIB.ip_last_error().decode()
+    big = seqs(max_seq_len=1 << 30, seq_stride=1 << 30)
+    assert score(L, big) == L.IP_EUNSUPPORTED            # beyond the top-k merge capacity
+    f32 = cache(L, dtype=L.IP_F32, row_dim=32, stride=128, scale=None)
+    assert score(L, s, q_dtype=L.IP_F32, H=4, D=32, pooled=f32, top_k=64, ws_bytes=0) == L.IP_EWORKSPACE
+
+
+def attn(L, s, q_dtype=None, H=64, dk=576, dv=512, k=None, v=None, top_k=512, ws=FAKE, ws_bytes=1 << 30,
+         scale=0.1):
+    q_dtype = L.IP_BF16 if q_dtype is None else q_dtype
+    k = cache(L, dtype=L.IP_BF16, row_dim=576, stride=1152, scale=None) if k is None else k
+    return L.LIB.sparse_attn_decode(ctypes.byref(s), FAKE, q_dtype, H, dk, dv, scale, ctypes.byref(k),
+                                    None if v is None else ctypes.byref(v), FAKE, top_k, FAKE, None, ws,
+                                    ws_bytes, None)
+
+
+def test_attention_rejects_bad_arguments(L):
+    s = seqs()
+    assert attn(L, s, H=32) == L.IP_EUNSUPPORTED
+    assert attn(L, s, dk=512) == L.IP_EUNSUPPORTED
+    assert attn(L, s, scale=0.0) == L.IP_EINVAL
+    assert attn(L, s, top_k=0) == L.IP_EUNSUPPORTED
+    assert attn(L, s, v=cache(L, dtype=L.IP_BF16, row_dim=512, stride=1024, scale=None)) == L.IP_EUNSUPPORTED
+    need = L.LIB.sparse_attn_workspace_bytes(2, 64, 512, 512, L.IP_BF16)
+    assert need > 0
+    assert attn(L, s, ws=None) == L.IP_EWORKSPACE
+    assert attn(L, s, ws_bytes=need - 1) == L.IP_EWORKSPACE
+    f = cache(L, dtype=L.IP_F32, row_dim=64, stride=256, scale=None)
+    assert attn(L, s, q_dtype=L.IP_F32, H=16, dk=64, dv=64, k=f, v=None) == L.IP_EINVAL   # v required
+    assert attn(L, s, q_dtype=L.IP_F32, H=32, dk=64, dv=64, k=f, v=f) == L.IP_EUNSUPPORTED
+    assert L.LIB.sparse_attn_prefill(ctypes.byref(s), 2, None, None, FAKE, L.IP_BF16, 64, 576, 512, 0.1,
+                                     ctypes.byref(cache(L, dtype=L.IP_BF16, row_dim=576, stride=1152, scale=None)),
+                                     None, FAKE, 512, FAKE, None, None, 0, None) == L.IP_EINVAL  # q_pos
+
+
+def test_workspace_sizes_are_consistent(L):
+    s = seqs(batch=8, max_seq_len=131072, seq_stride=131072)
+    n = L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 0)
+    # scores for 8 rows + 4 chunks of 511 candidates (key + id) per row
+    ld = L.LIB.index_scores_ld(131072)
+    assert ld == 32768
+    assert n == 8 * ld * 4 + 8 * 4 * 511 * 8
+    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 1) == 8 * 4 * 511 * 8
+    assert L.LIB.sparse_attn_workspace_bytes(8192, 64, 512, 512, L.IP_BF16) == 0      # prefill: no split
+    assert L.LIB.sparse_attn_workspace_bytes(1, 16, 64, 64, L.IP_F32) == 0
+    assert L.version() == "0.1.0"
+
+
+def test_timing_hook_arguments(L):
+    assert L.LIB.ip_time_next_launch(99, FAKE, FAKE) == L.IP_EINVAL
+    assert L.LIB.ip_time_next_launch(0, None, None) == L.IP_OK
