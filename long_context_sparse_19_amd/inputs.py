@@ -23,6 +23,8 @@ chunks, so the values do not depend on how much memory is free):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Optional
 
@@ -42,11 +44,25 @@ def _rng(seed: int, tag: str, chunk: int = 0) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([seed, _TAGS[tag], chunk]))
 
 
+def _threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _chunked(rows: int, fn) -> None:
+    """Run fn(chunk_index, r0, r1) over fixed row chunks on a thread pool (numpy's
+    generators and torch's casts release the GIL); results do not depend on the
+    thread count because every chunk has its own seed stream."""
+    spans = [(c, r0, min(rows, r0 + _CHUNK_ROWS)) for c, r0 in enumerate(range(0, rows, _CHUNK_ROWS))]
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(lambda a: fn(*a), spans))
+
+
 def _normal_rows(seed: int, tag: str, rows: int, cols: int) -> np.ndarray:
     out = np.empty((rows, cols), dtype=np.float32)
-    for c, r0 in enumerate(range(0, rows, _CHUNK_ROWS)):
-        r1 = min(rows, r0 + _CHUNK_ROWS)
-        out[r0:r1] = _rng(seed, tag, c).standard_normal((r1 - r0, cols), dtype=np.float32)
+
+    def fill(c, r0, r1):
+        _rng(seed, tag, c).standard_normal((r1 - r0, cols), dtype=np.float32, out=out[r0:r1])
+    _chunked(rows, fill)
     return out
 
 
@@ -68,10 +84,11 @@ def _fp8_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     s = (amax / np.float32(448.0)).astype(np.float32)
     s_safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
     codes = np.empty(x.shape, dtype=np.uint8)
-    for r0 in range(0, x.shape[0], _CHUNK_ROWS):
-        r1 = min(x.shape[0], r0 + _CHUNK_ROWS)
-        y = torch.from_numpy(x[r0:r1] / s_safe[r0:r1, None]).clamp_(-448.0, 448.0)
-        codes[r0:r1] = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+    def conv(c, r0, r1):
+        y = torch.from_numpy(x[r0:r1]) / torch.from_numpy(s_safe[r0:r1, None])
+        codes[r0:r1] = y.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    _chunked(x.shape[0], conv)
     return codes, s
 
 
@@ -165,10 +182,11 @@ def make_inputs(w: Workload, with_attention: bool = True) -> Inputs:
     if with_attention:
         if w.attn_dtype == "bf16":
             latent = np.empty((n_rows, w.dk), dtype=np.uint16)
-            for c, r0 in enumerate(range(0, n_rows, _CHUNK_ROWS)):
-                r1 = min(n_rows, r0 + _CHUNK_ROWS)
+
+            def fill(c, r0, r1):
                 latent[r0:r1] = to_bf16_bits(
                     _rng(seed, "latent", c).standard_normal((r1 - r0, w.dk), dtype=np.float32))
+            _chunked(n_rows, fill)
         else:
             k_cache = _normal_rows(seed, "k", n_rows, w.dk)
             v_cache = _normal_rows(seed, "v", n_rows, w.dv)
