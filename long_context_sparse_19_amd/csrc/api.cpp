@@ -84,7 +84,8 @@ ip_status check_cache(const ip_cache* c, const char* fn, const char* name) {
 struct ScorePlan {
   int64_t ld;          // floats per score row
   int max_blocks;      // eligible blocks bound
-  int n_chunks;        // stage-1 chunks per row
+  int chunk;           // scores per top-k chunk
+  int n_chunks;        // top-k chunks per row
   int rows_per_chunk;  // query rows per pass
   size_t score_bytes, cand_bytes, total;
 };
@@ -93,7 +94,8 @@ ScorePlan score_plan(const ip_seqs* s, int n_q, int top_k, bool scores_given) {
   ScorePlan p;
   p.max_blocks = (s->max_seq_len - 1) / 4;          // j < b_q <= (max_seq_len - 1) / 4
   p.ld = index_scores_ld(s->max_seq_len);
-  p.n_chunks = p.max_blocks <= 0 ? 1 : (p.max_blocks + ip::TOPK_CHUNK - 1) / ip::TOPK_CHUNK;
+  p.chunk = ip::topk_chunk_size(std::max(1, p.max_blocks));
+  p.n_chunks = p.max_blocks <= 0 ? 1 : (p.max_blocks + p.chunk - 1) / p.chunk;
   if (scores_given) {
     p.rows_per_chunk = n_q;
   } else {
@@ -117,11 +119,11 @@ AttnPlan attn_plan(int n_q, int n_heads, int dv, int top_k, int q_dtype) {
   p.n_split = 1;
   p.blocks_per_split = top_k;
   if (q_dtype == IP_BF16) {
+    // one workgroup per (row, split, 16-head group): aim at one per compute unit
     const int nsub = (top_k + 15) / 16;                 // 64-token sub-tiles
-    const int want = (kTargetWorkgroups + n_q - 1) / std::max(1, n_q);
-    const int max_split = std::max(1, nsub / 2);        // >= 2 sub-tiles per split
-    const int ns = std::max(1, std::min(want, max_split));
-    const int sub_per = (nsub + ns - 1) / ns;
+    const int want = (kTargetWorkgroups / (ip::LAT_H / 16) + n_q - 1) / std::max(1, n_q);
+    const int ns = std::max(1, std::min(want, std::min(nsub, 64)));
+    const int sub_per = std::min((nsub + ns - 1) / ns, 32);   // <= 512 blocks per split
     p.blocks_per_split = sub_per * 16;
     p.n_split = (top_k + p.blocks_per_split - 1) / p.blocks_per_split;
   }
@@ -276,6 +278,7 @@ ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_se
     ta.cand_key = cand_key;
     ta.cand_idx = cand_idx;
     ta.n_chunks = plan.n_chunks;
+    ta.chunk = plan.chunk;
     st = device_status(ip::launch_topk(ta, stream), fn);
     if (st) return st;
   }

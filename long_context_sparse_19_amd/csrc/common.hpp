@@ -96,30 +96,11 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// ---------------------------------------------------------------- block scans
-// Exclusive prefix sum of one int per thread over a block of NT threads (wave64).
-// tmp: >= NT/64 + 1 ints of LDS.  Returns the exclusive prefix; *total = block sum.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) tmp[wv] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int s = 0;
-    for (int i = 0; i < NT / 64; ++i) { int t = tmp[i]; tmp[i] = s; s += t; }
-    tmp[NT / 64] = s;
-  }
-  __syncthreads();
-  const int r = tmp[wv] + x - v;
-  *total = tmp[NT / 64];
-  __syncthreads();
-  return r;
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
+// then s_barrier.  Unlike __syncthreads() it does not wait for outstanding global
+// loads (on gfx9 vmcnt counts loads too), so prefetches stay in flight across it.
+// The "memory" clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-
 }  // namespace ip

@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <algorithm>
 #include "common.hpp"
 
 namespace ip {
@@ -62,9 +63,11 @@ struct TopkArgs {
   uint32_t* cand_key;          // [n_rows, n_chunks, top_k - 1]
   int32_t* cand_idx;           // same
   int n_chunks;                // chunks per row covered by the grid
+  int chunk;                   // scores per chunk (topk_chunk_size)
 };
-constexpr int TOPK_CHUNK = 8192;        // stage-1 elements per workgroup
-constexpr int TOPK_MERGE_CAP = 32768;   // stage-2 candidate slots per row
+constexpr int TOPK_MAX_CHUNK = 32768;   // scores per chunk workgroup (1024 threads x 32)
+constexpr int TOPK_MERGE_CAP = 32768;   // candidate slots per row in the merge
+int topk_chunk_size(int max_blocks);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------ sparse attention

@@ -18,20 +18,26 @@ namespace ip {
 namespace {
 
 constexpr int NT = 256;
-constexpr int KEYS_PER_WG = 256;   // 4 waves x 2 tiles x 32 keys
+constexpr int TILES = 4;                        // 32-key tiles per wave
+constexpr int KEYS_PER_WG = 4 * TILES * 32;     // 512
 constexpr int HI = 32, DI = 128;
 
-// rows_per_wg query rows share one key chunk held in registers
+// RPW query rows share one key chunk held in registers (prefill); decode uses 1.
+// All key loads of a wave are issued before the first MFMA, so each compute unit
+// keeps ~128 KB of the pooled cache in flight.
 template <int RPW>
 __global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
+  constexpr int QROW = DI + 8;                  // padded LDS row (272 bytes): conflict-free reads
+  __shared__ __align__(16) uint16_t qs[HI * QROW];
+  __shared__ float gs[HI];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int kl = lane & 31, hh = lane >> 5;
   const int kc0 = blockIdx.x * KEYS_PER_WG;
   const int rbeg = a.row0 + blockIdx.y * RPW;
   const int rend = min(rbeg + RPW, a.row0 + a.n_rows);
 
-  bf16x8_t kf[2][8];
-  float ksig[2] = {0.f, 0.f};
+  bf16x8_t kf[TILES][8];
+  float ksig[TILES];
   int cur_b = -1;
 
   for (int r = rbeg; r < rend; ++r) {
@@ -39,41 +45,60 @@ __global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
     const int p = a.q_pos ? a.q_pos[r] : a.L.seq_lens[b] - 1;
     const int nel = p >> 2;                    // eligible blocks j < b_q
     if (kc0 >= nel) continue;                  // uniform over the workgroup
+    // the row's query (8 KB) and gates: issued first, staged through LDS
+    u32x4_t qv0, qv1;
+    float gv = 0.f;
+    {
+      const u32x4_t* qg = (const u32x4_t*)((const uint16_t*)a.q + (int64_t)r * HI * DI);
+      qv0 = qg[2 * threadIdx.x];
+      qv1 = qg[2 * threadIdx.x + 1];
+      if (threadIdx.x < HI) gv = a.gates[(int64_t)r * HI + threadIdx.x];
+    }
     if (b != cur_b) {
       cur_b = b;
-      const int nrows = (a.L.seq_lens[b] + 3) >> 2;   // pooled rows that exist
+      // pooled rows that exist; keys past them are clamped to the last one (their
+      // scores are never written), so every load is unconditional and all of a
+      // wave's loads are in flight together
+      const int nrows = (a.L.seq_lens[b] + 3) >> 2;
+      u32x4_t raw[TILES][4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int j = kc0 + wv * 64 + t * 32 + kl;
-        if (j < nrows) {
-          const int64_t row = a.L.pool_row(b, j);
-          const u32x4_t* src = (const u32x4_t*)(a.keys + row * a.key_stride + hh * 64);
+      for (int t = 0; t < TILES; ++t) {
+        const int j = min(kc0 + (wv * TILES + t) * 32 + kl, nrows - 1);
+        const int64_t row = a.L.pool_row(b, j);
+        const u32x4_t* src = (const u32x4_t*)(a.keys + row * a.key_stride + hh * 64);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const u32x4_t w = src[c];
-            kf[t][2 * c] = fp8x8_to_bf16x8(w[0], w[1]);
-            kf[t][2 * c + 1] = fp8x8_to_bf16x8(w[2], w[3]);
-          }
-          ksig[t] = a.key_scale[row];
-        } else {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) kf[t][c] = bf16x8_t{};
-          ksig[t] = 0.f;
-        }
+        for (int c = 0; c < 4; ++c) raw[t][c] = src[c];
+        ksig[t] = a.key_scale[row];
       }
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          kf[t][2 * c] = fp8x8_to_bf16x8(raw[t][c][0], raw[t][c][1]);
+          kf[t][2 * c + 1] = fp8x8_to_bf16x8(raw[t][c][2], raw[t][c][3]);
+        }
     }
+    // LDS-only barriers: loads still in flight are not waited for
+    block_sync_lds();
+    {
+      // thread t holds elements 16t .. 16t+15 = head t/8, dims (t%8)*16 ..
+      const int h = threadIdx.x >> 3, d = (threadIdx.x & 7) * 16;
+      *(u32x4_t*)(qs + h * QROW + d) = qv0;
+      *(u32x4_t*)(qs + h * QROW + d + 8) = qv1;
+      if (threadIdx.x < HI) gs[threadIdx.x] = gv;
+    }
+    block_sync_lds();
     // query fragment: head kl, dims hh*64 .. hh*64+63 (the same dims as the key half)
     bf16x8_t qf[8];
-    const u32x4_t* qsrc = (const u32x4_t*)((const uint16_t*)a.q + ((int64_t)r * HI + kl) * DI + hh * 64);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qf[c] = __builtin_bit_cast(bf16x8_t, qsrc[c]);
+    for (int c = 0; c < 8; ++c) qf[c] = *(const bf16x8_t*)(qs + kl * QROW + hh * 64 + c * 8);
     // gates of the 16 heads this lane accumulates: rows (i/4)*8 + hh*4 + i%4
     float g[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) g[i] = a.gates[(int64_t)r * HI + (i >> 2) * 8 + hh * 4 + (i & 3)];
+    for (int i = 0; i < 16; ++i) g[i] = gs[(i >> 2) * 8 + hh * 4 + (i & 3)];
 
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < TILES; ++t) {
       f32x16_t acc = {};
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[c], kf[t][c], acc, 0, 0, 0);
@@ -81,7 +106,7 @@ __global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) part = fmaf(g[i], fmaxf(acc[i], 0.f), part);
       part += __shfl_xor(part, 32);
-      const int j = kc0 + wv * 64 + t * 32 + kl;
+      const int j = kc0 + (wv * TILES + t) * 32 + kl;
       if (hh == 0 && j < nel) a.scores[(int64_t)(r - a.row0) * a.ld + j] = part * ksig[t];
     }
   }
