@@ -10,7 +10,9 @@ One step = one pass of the whole path over one batch:
 The default workload is decode of 8 sequences x 131072 tokens with top-512
 blocks (2048 tokens).  Inputs are seeded synthetic data of the workload's shape,
 resident in HBM before timing; R replicas of every device buffer are rotated so
-that successive steps do not hit in the 256 MB last-level cache.
+that successive steps do not hit in the 256 MB last-level cache.  Each replica's
+step is captured once into a HIP graph and replayed (--eager launches every call
+from Python instead).
 
 Prints one JSON line.  `value` is query tokens per second; `hbm_gbps` the
 algorithmic bytes of a step over the step time; `roofline` describes the
@@ -133,6 +135,7 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "max_ctx", "ragged", "prefill", "tiny"])
     ap.add_argument("--replicas", type=int, default=0, help="rotated input copies (0 = auto, >= 1 GiB touched)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of HIP graphs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (got --gpus {args.gpus}); "
@@ -174,8 +177,6 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {R} replicas resident, {step_bytes / 1e6:.2f} MB algorithmic per step", file=sys.stderr, flush=True)
 
-    stream = torch.cuda.current_stream()
-
     def step(i, ev=None):
         d, ws = reps[i % R], wss[i % R]
         D.compress(d, block_begin=begin, max_blocks=max_new)
@@ -186,22 +187,50 @@ def main():
             _lib.time_next_launch(_lib.K_ATTN, ev[2], ev[3])
         D.attention(d, ws)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    # per-replica events around the score and attention kernels
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(R)]
     for e in evs:
         for x in e:
-            x.record(stream)       # materialise the events before handing them to the library
+            x.record()             # materialise the events before handing them to the library
     torch.cuda.synchronize()
+
+    graphs = None
+    if not args.eager:
+        # one HIP graph per replica holding one whole step (the library only
+        # enqueues kernels and event records on the capturing stream)
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(R):
+                step(i)            # warm once outside capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for i in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i, evs[i])
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i, timed):
+        if graphs is not None:
+            graphs[i % R].replay()
+        else:
+            step(i, evs[i % R] if timed else None)
+
+    for i in range(args.warmup):
+        run(i, False)
+    torch.cuda.synchronize()
+    K = args.steps
     t0 = time.perf_counter()
     for i in range(K):
-        step(args.warmup + i, evs[i])
+        run(args.warmup + i, True)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    score_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    used = sorted({(args.warmup + i) % R for i in range(K)})
+    score_ms = float(np.mean([evs[j][0].elapsed_time(evs[j][1]) for j in used]))
+    attn_ms = float(np.mean([evs[j][2].elapsed_time(evs[j][3]) for j in used]))
     ms = dt * 1e3 / K
     value = w.n_rows / (ms / 1e3)
 
@@ -236,7 +265,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "context": w.seq_len, "query_rows": w.n_rows,
                    "top_k_blocks": w.top_k, "index_keys": w.idx_key_dtype, "latent": w.attn_dtype,
-                   "replicas": R, "parallelism": "single GPU"},
+                   "replicas": R, "launch": "eager" if args.eager else "hip-graph",
+                   "parallelism": "single GPU"},
         "hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "algorithmic_bytes_per_step": step_bytes,
         "roofline": roof,

@@ -135,7 +135,7 @@ ip_status indexpool_compress(const ip_seqs* seqs, const int32_t* block_begin, in
  *  ws       device workspace of ws_bytes >= index_score_topk_workspace_bytes(...)
  * Contract: 0 <= p < seq_lens[b]; blocks j < b_q were pooled.
  * ------------------------------------------------------------------------------- */
-int64_t index_scores_ld(int32_t max_seq_len);   /* max_seq_len/4 rounded up to 64 */
+int64_t index_scores_ld(int32_t max_seq_len);   /* >= max_seq_len/4, rounded up to whole top-k chunks */
 size_t index_score_topk_workspace_bytes(const ip_seqs* seqs, int32_t n_q, int32_t top_k,
                                         int32_t scores_given);
 ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,

@@ -161,8 +161,11 @@ ip_status ip_time_next_launch(int32_t kernel_id, hipEvent_t start, hipEvent_t st
 }
 
 int64_t index_scores_ld(int32_t max_seq_len) {
+  // whole top-k chunks, so every chunk workgroup reads inside its row
+  const int max_blocks = std::max(1, (max_seq_len - 1) / 4);
+  const int64_t chunk = ip::topk_chunk_size(max_blocks);
   const int64_t n = std::max<int64_t>(1, max_seq_len / 4);
-  return (n + 63) & ~int64_t(63);
+  return (n + chunk - 1) / chunk * chunk;
 }
 
 // ------------------------------------------------------------------ IndexPool

@@ -104,3 +104,67 @@ __device__ __forceinline__ void block_sync_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 }  // namespace ip
+
+namespace ip {
+// ---------------------------------------------------------------- wave-level DPP
+// Cross-lane steps on the VALU (DPP) instead of ds_bpermute: a reduction or scan
+// over 64 lanes is six dependent VALU ops rather than six LDS round trips.
+// DPP controls (GFX9): quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_shr:n =
+// 0x110+n, row_mirror = 0x140, row_half_mirror = 0x141, row_bcast:15 = 0x142,
+// row_bcast:31 = 0x143.  Lanes whose source is masked off get `old`.
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ int dpp_i(int old, int x) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ float dpp_f(float old, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL, ROW_MASK, 0xF,
+                                                    BOUND_ZERO));
+}
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i<0x111, 0xF, true>(0, x);
+  x += dpp_i<0x112, 0xF, true>(0, x);
+  x += dpp_i<0x114, 0xF, true>(0, x);
+  x += dpp_i<0x118, 0xF, true>(0, x);
+  x += dpp_i<0x142, 0xA>(0, x);
+  x += dpp_i<0x143, 0xC>(0, x);
+  return x;
+}
+
+// value of lane 63 (wave-uniform)
+__device__ __forceinline__ int lane63(int x) { return __builtin_amdgcn_readlane(x, 63); }
+__device__ __forceinline__ float lane63f(float x) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// sum / max / min over the 64 lanes of a wave, returned to every lane
+__device__ __forceinline__ int wave_sum(int x) {
+  x += dpp_i<0xB1>(0, x);
+  x += dpp_i<0x4E>(0, x);
+  x += dpp_i<0x141>(0, x);
+  x += dpp_i<0x140>(0, x);
+  x += dpp_i<0x142, 0xA>(0, x);
+  x += dpp_i<0x143, 0xC>(0, x);
+  return lane63(x);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<0x4E>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<0x141>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<0x140>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<0x142, 0xA>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<0x143, 0xC>(-INFINITY, x));
+  return lane63f(x);
+}
+__device__ __forceinline__ float wave_min(float x) {
+  x = fminf(x, dpp_f<0xB1>(INFINITY, x));
+  x = fminf(x, dpp_f<0x4E>(INFINITY, x));
+  x = fminf(x, dpp_f<0x141>(INFINITY, x));
+  x = fminf(x, dpp_f<0x140>(INFINITY, x));
+  x = fminf(x, dpp_f<0x142, 0xA>(INFINITY, x));
+  x = fminf(x, dpp_f<0x143, 0xC>(INFINITY, x));
+  return lane63f(x);
+}
+}  // namespace ip

@@ -65,8 +65,8 @@ struct TopkArgs {
   int n_chunks;                // chunks per row covered by the grid
   int chunk;                   // scores per chunk (topk_chunk_size)
 };
-constexpr int TOPK_MAX_CHUNK = 32768;   // scores per chunk workgroup (1024 threads x 32)
-constexpr int TOPK_MERGE_CAP = 32768;   // candidate slots per row in the merge
+constexpr int TOPK_MAX_CHUNK = 16384;   // scores per chunk workgroup (512 threads x 32)
+constexpr int TOPK_MERGE_CAP = 16384;   // candidate slots per row in the merge (512 x 32)
 int topk_chunk_size(int max_blocks);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 

@@ -139,15 +139,19 @@ def test_attention_rejects_bad_arguments(L):
 def test_workspace_sizes_are_consistent(L):
     s = seqs(batch=8, max_seq_len=131072, seq_stride=131072)
     n = L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 0)
-    # scores for 8 rows; 32767 eligible blocks fit one top-k chunk
+    # scores for 8 rows; 32767 eligible blocks -> 2 top-k chunks of 16384 with
+    # 511 candidates (key + id) each
     ld = L.LIB.index_scores_ld(131072)
     assert ld == 32768
-    assert n == 8 * ld * 4
-    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 1) == 0
-    # 1M tokens: 262143 blocks -> 8 chunks of 32768, 511 candidates (key + id) each
+    assert n == 8 * ld * 4 + 8 * 2 * 511 * 8
+    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 1) == 8 * 2 * 511 * 8
+    # 1M tokens: 262143 blocks -> 16 chunks
     s1 = seqs(batch=1, max_seq_len=1 << 20, seq_stride=1 << 20)
     ld1 = L.LIB.index_scores_ld(1 << 20)
-    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s1), 1, 512, 0) == ld1 * 4 + 8 * 511 * 8
+    assert ld1 == 262144
+    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s1), 1, 512, 0) == ld1 * 4 + 16 * 511 * 8
+    # rows are padded to whole chunks: 1025 blocks -> chunk 2048
+    assert L.LIB.index_scores_ld(4 * 1026) == 2048
     assert L.LIB.sparse_attn_workspace_bytes(8192, 64, 512, 512, L.IP_BF16) == 0      # prefill: no split
     assert L.LIB.sparse_attn_workspace_bytes(1, 16, 64, 64, L.IP_F32) == 0
     assert L.version() == "0.1.0"
