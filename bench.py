@@ -14,11 +14,19 @@ that successive steps do not hit in the 256 MB last-level cache.  Each replica's
 step is captured once into a HIP graph and replayed (--eager launches every call
 from Python instead).
 
-Prints one JSON line.  `value` is query tokens per second; `hbm_gbps` the
-algorithmic bytes of a step over the step time; `roofline` describes the
-dominant kernel with its average duration from HIP events recorded around its
-launches inside the timed region; `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload.
+Two timed regions of K steps each:
+  1. the graph replays -> `value` (query tokens per second) and `ms_per_step`;
+  2. the same K steps launched call by call, every kernel launch carrying a pair
+     of HIP events that receive its dispatch start and end times
+     (hipExtLaunchKernelGGL, on the stream the kernel runs on) -> the per-kernel
+     averages in `kernels`, `kernel_sum_ms` and `roofline` (the kernel with the
+     longest average).  These are the same timestamps rocprofv3's kernel trace
+     reports, so the two agree.
+`hbm_gbps` is the step's algorithmic bytes over the step time, and
+`hbm_frac_kernel_sum` the same bytes over the summed kernel times of the path
+(scoring, both top-k stages, attention and its split combine) against 8 TB/s.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -66,6 +74,36 @@ def algorithmic_bytes(inp, w):
     return dict(score=int(score_b.sum()), select=int(sel_b * len(n)), attention=int(attn_b.sum()),
                 pool=int(pool_b), total=int(score_b.sum() + sel_b * len(n) + attn_b.sum() + pool_b),
                 U=U)
+
+
+def kernel_bytes(inp, w, ab):
+    """Bytes each kernel must move given the path's stages (for the per-kernel
+    rates; the step's algorithmic total above excludes the score and candidate
+    intermediates counted here)."""
+    import numpy as np
+    n = inp.q_pos.astype(np.int64) // 4
+    k = w.top_k
+    chunk = _chunk_size(int(inp.seq_lens.max()))
+    n_chunks = np.maximum(1, (n + chunk - 1) // chunk)
+    multi = n_chunks > 1
+    topk = n * 4 + np.where(multi, n_chunks * (k - 1) * 8, k * 4)
+    merge = np.where(multi, n_chunks * (k - 1) * 8 + k * 4, 0)
+    # split-softmax partials: read once by the combine, which writes the bf16 output and lse
+    from long_context_sparse_19_amd import _lib
+    nq = len(n)
+    part = _lib.LIB.sparse_attn_workspace_bytes(nq, w.n_heads, w.dv, k, _lib.IP_BF16 if w.attn_dtype == "bf16" else _lib.IP_F32)
+    comb = part + nq * w.n_heads * (w.dv * 2 + 4) if part else None
+    return {"compress": ab["pool"], "score": ab["score"], "topk": int(topk.sum()),
+            "topk_merge": int(merge.sum()) or None, "attention": ab["attention"], "combine": comb}
+
+
+def _chunk_size(max_seq_len):
+    nb = max(1, (max_seq_len - 1) // 4)
+    # the library pads score rows to whole chunks; the chunk is the row padding unit
+    c = 512
+    while c < min(nb, 16384):
+        c *= 2
+    return c
 
 
 def attention_flops(U, w):
@@ -177,83 +215,97 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {R} replicas resident, {step_bytes / 1e6:.2f} MB algorithmic per step", file=sys.stderr, flush=True)
 
-    def step(i, ev=None):
+    def step(i):
         d, ws = reps[i % R], wss[i % R]
         D.compress(d, block_begin=begin, max_blocks=max_new)
-        if ev is not None:
-            _lib.time_next_launch(_lib.K_SCORE, ev[0], ev[1])
         D.score_topk(d, ws)
-        if ev is not None:
-            _lib.time_next_launch(_lib.K_ATTN, ev[2], ev[3])
         D.attention(d, ws)
-
-    # per-replica events around the score and attention kernels
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(R)]
-    for e in evs:
-        for x in e:
-            x.record()             # materialise the events before handing them to the library
-    torch.cuda.synchronize()
 
     graphs = None
     if not args.eager:
-        # one HIP graph per replica holding one whole step (the library only
-        # enqueues kernels and event records on the capturing stream)
+        # one HIP graph per replica holding one whole step (a forked branch for the
+        # decode pooling, which the rest of the step does not read, measured slower)
         graphs = []
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
             for i in range(R):
                 step(i)            # warm once outside capture
-        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
         for i in range(R):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(i, evs[i])
+                step(i)
             graphs.append(g)
         torch.cuda.synchronize()
 
-    def run(i, timed):
+    def run(i):
         if graphs is not None:
             graphs[i % R].replay()
         else:
-            step(i, evs[i % R] if timed else None)
+            step(i)
 
+    # --- timed region 1: K whole steps -> value
     for i in range(args.warmup):
-        run(i, False)
+        run(i)
     torch.cuda.synchronize()
     K = args.steps
     t0 = time.perf_counter()
     for i in range(K):
-        run(args.warmup + i, True)
+        run(args.warmup + i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    used = sorted({(args.warmup + i) % R for i in range(K)})
-    score_ms = float(np.mean([evs[j][0].elapsed_time(evs[j][1]) for j in used]))
-    attn_ms = float(np.mean([evs[j][2].elapsed_time(evs[j][3]) for j in used]))
     ms = dt * 1e3 / K
     value = w.n_rows / (ms / 1e3)
 
+    # --- timed region 2: the same K steps launched one call at a time, every kernel
+    # launch carrying HIP events that receive its dispatch start / end times (the
+    # timestamps a kernel trace reports), on the stream the kernel runs on
+    ids = {"compress": _lib.K_COMPRESS, "score": _lib.K_SCORE, "topk": _lib.K_TOPK,
+           "topk_merge": _lib.K_TOPK_MERGE, "attention": _lib.K_ATTN, "combine": _lib.K_COMBINE}
+    evk = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+           for n in ids}
+    for n in ids:
+        for e0, e1 in evk[n]:
+            e0.record()
+            e1.record()            # materialise the events before handing them to the library
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(K):
+        for n, kid in ids.items():
+            _lib.time_next_launch(kid, *evk[n][i])
+        step(args.warmup + i)
+        _lib.time_next_launch(0, None, None)      # kernels this workload does not launch
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t1) * 1e3 / K
+    kern_ms = {}
+    for n in ids:
+        ts = [e0.elapsed_time(e1) for e0, e1 in evk[n]]
+        ts = [t for t in ts if t > 0]
+        if len(ts) == K:
+            kern_ms[n] = float(np.mean(ts))
+
     U = ab["U"]
-    score_bytes = ab["score"]
-    attn_bytes = ab["attention"]
-    kernels = {
-        "score": {"avg_ms": score_ms, "algorithmic_bytes": score_bytes,
-                  "GBps": score_bytes / (score_ms * 1e-3) / 1e9},
-        "attention": {"avg_ms": attn_ms, "algorithmic_bytes": attn_bytes,
-                      "GBps": attn_bytes / (attn_ms * 1e-3) / 1e9,
-                      "flops": attention_flops(U, w),
-                      "TFLOPs": attention_flops(U, w) / (attn_ms * 1e-3) / 1e12},
-    }
-    if w.mode == "prefill":
+    kbytes = kernel_bytes(inp, w, ab)
+    kernels = {}
+    for n, t in kern_ms.items():
+        kernels[n] = {"avg_ms": t, "bytes": kbytes.get(n), "GBps": (kbytes[n] / (t * 1e-3) / 1e9) if kbytes.get(n) else None}
+    if "attention" in kernels:
+        fl = attention_flops(U, w)
+        kernels["attention"].update(flops=fl, TFLOPs=fl / (kern_ms["attention"] * 1e-3) / 1e12)
+    path_ms = sum(kern_ms.get(n, 0.0) for n in ("score", "topk", "topk_merge", "attention", "combine"))
+    dom = max(kern_ms, key=kern_ms.get)
+    if w.mode == "prefill" and dom == "attention":
         ach = kernels["attention"]["TFLOPs"]
-        roof = {"bound": "mfma", "kernel": "attn_bf16 (sparse_attn_prefill)", "achieved": ach,
+        roof = {"bound": "mfma", "kernel": "attention (sparse_attn_prefill)", "achieved": ach,
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None}
     else:
-        name, kk = max(kernels.items(), key=lambda kv: kv[1]["avg_ms"])
-        ach = kk["GBps"]
-        roof = {"bound": "hbm", "kernel": name, "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        ach = kernels[dom]["GBps"]
+        roof = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBPS, "traffic": None}
+    roof["avg_ms"] = kern_ms[dom]
+    roof["launches"] = K
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -269,6 +321,9 @@ def main():
                    "parallelism": "single GPU"},
         "hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "algorithmic_bytes_per_step": step_bytes,
+        "kernel_sum_ms": path_ms,
+        "hbm_frac_kernel_sum": step_bytes / (path_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS if path_ms else None,
+        "eager_ms_per_step": eager_ms,
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,

@@ -188,9 +188,13 @@ ip_status sparse_attn_prefill(const ip_seqs* seqs, int32_t n_q, const int32_t* q
 const char* ip_last_error(void);
 
 /* Timing hook for benchmarks: the next launch (on this thread) of kernel `kernel_id`
- * is bracketed by hipEventRecord(start) / hipEventRecord(stop) on its stream.
- * kernel_id: 1 compress, 2 score, 3 top-k (first stage), 4 attention, 5 combine.
- * Pass NULL events to clear.  Not needed for normal use. */
+ * goes through hipExtLaunchKernelGGL with `start` / `stop`, so the two events
+ * receive that dispatch's own start and end times (the timestamps a kernel trace
+ * reports).  kernel_id: 1 compress, 2 score, 3 top-k (per-chunk stage),
+ * 4 attention, 5 split combine, 6 top-k merge.  Hooks for different ids may be
+ * armed together; each is consumed by one launch.  Passing NULL for one event
+ * only is IP_EINVAL; kernel_id 0 with both NULL disarms every hook.  Use it
+ * outside stream capture.  Not needed for normal use. */
 ip_status ip_time_next_launch(int32_t kernel_id, hipEvent_t start, hipEvent_t stop);
 
 /* Library version, e.g. "0.1.0". */

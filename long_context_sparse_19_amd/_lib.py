@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libindexpool.so")
 
 IP_OK, IP_EINVAL, IP_EUNSUPPORTED, IP_EWORKSPACE, IP_EDEVICE = range(5)
 IP_F32, IP_BF16, IP_FP8_E4M3FN = range(3)
-K_COMPRESS, K_SCORE, K_TOPK, K_ATTN, K_COMBINE = 1, 2, 3, 4, 5
+K_COMPRESS, K_SCORE, K_TOPK, K_ATTN, K_COMBINE, K_TOPK_MERGE = 1, 2, 3, 4, 5, 6
 
 _c_void_p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -189,7 +189,8 @@ def sparse_attn_prefill(seqs: Seqs, q: torch.Tensor, k: Cache, v: Optional[Cache
 
 
 def time_next_launch(kernel_id: int, start, stop) -> None:
-    """Bracket the next launch of ``kernel_id`` with two torch.cuda.Event records."""
+    """The next launch of ``kernel_id`` stores its dispatch start / end times in two
+    torch.cuda.Event objects (kernel_id 0 with both None disarms every hook)."""
     a = None if start is None else start.cuda_event
     b = None if stop is None else stop.cuda_event
     _check("ip_time_next_launch", LIB.ip_time_next_launch(kernel_id, a, b))

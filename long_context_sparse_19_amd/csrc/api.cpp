@@ -27,10 +27,9 @@ ip_status device_status(hipError_t e, const char* what) {
 }
 
 struct Hook {
-  int id = 0;
   hipEvent_t start = nullptr, stop = nullptr;
 };
-thread_local Hook g_hook;
+thread_local Hook g_hook[ip::K_LAST + 1];   // armed events per kernel id
 
 constexpr int64_t kMaxTokens = int64_t(1) << 31;   // int32 token positions
 constexpr size_t kScoreBudget = size_t(256) << 20;  // score workspace per row chunk
@@ -134,14 +133,12 @@ AttnPlan attn_plan(int n_q, int n_heads, int dv, int top_k, int q_dtype) {
 }  // namespace
 
 namespace ip {
-void hook_before(int id, hipStream_t s) {
-  if (g_hook.id == id && g_hook.start) hipEventRecord(g_hook.start, s);
-}
-void hook_after(int id, hipStream_t s) {
-  if (g_hook.id == id && g_hook.stop) {
-    hipEventRecord(g_hook.stop, s);
-    g_hook = Hook{};
-  }
+bool hook_take(int id, hipEvent_t* start, hipEvent_t* stop) {
+  if (id < 1 || id > K_LAST || !g_hook[id].start) return false;
+  *start = g_hook[id].start;
+  *stop = g_hook[id].stop;
+  g_hook[id] = Hook{};
+  return true;
 }
 }  // namespace ip
 
@@ -151,12 +148,15 @@ const char* ip_last_error(void) { return g_err.c_str(); }
 const char* ip_version(void) { return "0.1.0"; }
 
 ip_status ip_time_next_launch(int32_t kernel_id, hipEvent_t start, hipEvent_t stop) {
-  if (!start || !stop) { g_hook = Hook{}; return IP_OK; }
-  if (kernel_id < ip::K_COMPRESS || kernel_id > ip::K_COMBINE)
+  if (kernel_id == 0 && !start && !stop) {
+    for (auto& h : g_hook) h = Hook{};
+    return IP_OK;
+  }
+  if (kernel_id < ip::K_COMPRESS || kernel_id > ip::K_LAST)
     return fail(IP_EINVAL, "ip_time_next_launch: unknown kernel id %d", kernel_id);
-  g_hook.id = kernel_id;
-  g_hook.start = start;
-  g_hook.stop = stop;
+  if (!start != !stop) return fail(IP_EINVAL, "ip_time_next_launch: pass both events or neither");
+  g_hook[kernel_id].start = start;
+  g_hook[kernel_id].stop = stop;
   return IP_OK;
 }
 

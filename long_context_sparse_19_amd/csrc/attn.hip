@@ -423,22 +423,16 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   const int64_t groups = (int64_t)a.n_rows * a.n_split;
   const unsigned grid = (unsigned)((groups + 7) / 8 * 8 * HGRP);
-  hook_before(K_ATTN, s);
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(grid), dim3(NT), 0, s, a);
-  hook_after(K_ATTN, s);
+  launch(K_ATTN, attn_bf16_kernel, dim3(grid), dim3(NT), s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  hook_before(K_COMBINE, s);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(LAT_H / 2, a.n_rows), dim3(256), 0, s, a);
-  hook_after(K_COMBINE, s);
+  launch(K_COMBINE, attn_combine_kernel, dim3(LAT_H / 2, a.n_rows), dim3(256), s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  hook_before(K_ATTN, s);
-  hipLaunchKernelGGL(attn_f32_kernel, dim3(a.n_rows), dim3(NT), 0, s, a);
-  hook_after(K_ATTN, s);
+  launch(K_ATTN, attn_f32_kernel, dim3(a.n_rows), dim3(NT), s, a);
   return hipGetLastError();
 }
 

@@ -118,9 +118,7 @@ __global__ __launch_bounds__(NT) void compress_f32_kernel(CompressArgs a) {
 hipError_t launch_compress_fp8(const CompressArgs& a, hipStream_t s) {
   if (a.max_blocks <= 0) return hipSuccess;
   dim3 grid((a.max_blocks + 15) / 16, a.batch);
-  hook_before(K_COMPRESS, s);
-  hipLaunchKernelGGL(compress_fp8_kernel, grid, dim3(NT), 0, s, a);
-  hook_after(K_COMPRESS, s);
+  launch(K_COMPRESS, compress_fp8_kernel, grid, dim3(NT), s, a);
   return hipGetLastError();
 }
 
@@ -128,9 +126,7 @@ hipError_t launch_compress_f32(const CompressArgs& a, hipStream_t s) {
   if (a.max_blocks <= 0) return hipSuccess;
   const int64_t threads = (int64_t)a.max_blocks * (a.dim / 4);
   dim3 grid((unsigned)((threads + NT - 1) / NT), a.batch);
-  hook_before(K_COMPRESS, s);
-  hipLaunchKernelGGL(compress_f32_kernel, grid, dim3(NT), 0, s, a);
-  hook_after(K_COMPRESS, s);
+  launch(K_COMPRESS, compress_f32_kernel, grid, dim3(NT), s, a);
   return hipGetLastError();
 }
 

@@ -1,17 +1,29 @@
 // Host-side launch interface of the gfx950 kernels (internal to libindexpool).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 #include <algorithm>
 #include "common.hpp"
 
 namespace ip {
 
-enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3, K_ATTN = 4, K_COMBINE = 5 };
+enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3, K_ATTN = 4, K_COMBINE = 5, K_TOPK_MERGE = 6, K_LAST = 6 };
 
-// Records the timing hook's events around one launch if it targets `id`.
-void hook_before(int id, hipStream_t s);
-void hook_after(int id, hipStream_t s);
+// Takes (and disarms) the timing hook's events if one is armed for kernel `id`.
+bool hook_take(int id, hipEvent_t* start, hipEvent_t* stop);
+
+// Launches kernel `id`.  When the timing hook is armed for it, the launch goes
+// through hipExtLaunchKernelGGL, which stores the dispatch's own start and end
+// times in the two events (the same timestamps a kernel trace reports).
+template <typename K, typename... Args>
+void launch(int id, K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  hipEvent_t e0, e1;
+  if (hook_take(id, &e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
 
 // ------------------------------------------------------------ IndexPool
 struct CompressArgs {

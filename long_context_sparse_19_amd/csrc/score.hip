@@ -144,23 +144,19 @@ __global__ __launch_bounds__(NT) void score_f32_kernel(ScoreArgs a) {
 hipError_t launch_score_fp8_bf16(const ScoreArgs& a, hipStream_t s) {
   if (a.n_rows <= 0 || a.max_blocks <= 0) return hipSuccess;
   const unsigned gx = (a.max_blocks + KEYS_PER_WG - 1) / KEYS_PER_WG;
-  hook_before(K_SCORE, s);
   if (a.n_rows >= 64) {
     constexpr int R = 16;
-    hipLaunchKernelGGL(score_fp8_bf16_kernel<R>, dim3(gx, (a.n_rows + R - 1) / R), dim3(NT), 0, s, a);
+    launch(K_SCORE, score_fp8_bf16_kernel<R>, dim3(gx, (a.n_rows + R - 1) / R), dim3(NT), s, a);
   } else {
-    hipLaunchKernelGGL(score_fp8_bf16_kernel<1>, dim3(gx, a.n_rows), dim3(NT), 0, s, a);
+    launch(K_SCORE, score_fp8_bf16_kernel<1>, dim3(gx, a.n_rows), dim3(NT), s, a);
   }
-  hook_after(K_SCORE, s);
   return hipGetLastError();
 }
 
 hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s) {
   if (a.n_rows <= 0 || a.max_blocks <= 0) return hipSuccess;
   dim3 grid((a.max_blocks + NT - 1) / NT, a.n_rows);
-  hook_before(K_SCORE, s);
-  hipLaunchKernelGGL(score_f32_kernel, grid, dim3(NT), 0, s, a);
-  hook_after(K_SCORE, s);
+  launch(K_SCORE, score_f32_kernel, grid, dim3(NT), s, a);
   return hipGetLastError();
 }
 

@@ -6,15 +6,21 @@
 //
 // One 512-thread workgroup selects the kk best of a chunk of up to 16384 scores
 // held in registers.  Thread t owns the contiguous slots [t*E, t*E+E), so "lower
-// slot first" is a per-thread count plus one workgroup prefix sum.
+// slot first" is a per-thread count plus one workgroup prefix sum.  Cross-lane
+// steps use DPP; a cross-wave step is one LDS exchange and one barrier (the
+// exchange slots alternate between two sets, so no second barrier is needed
+// before they are rewritten).  A typical row costs about a dozen barriers.
 //   1. Threshold: with m the kk-th largest maximum of 8-score groups, at least kk
 //      scores are >= m, so the answer lies in {v >= m}.  A 2048-bucket histogram
 //      of the group maxima (linear between their min and max) gives T <= m.
 //   2. If fewer than kk scores are > T, T itself is the kk-th largest value: keep
 //      every v > T and the first kk - #(v > T) ties in slot order.
 //   3. Else if at most 4096 scores are >= T, compact them in slot order into LDS
-//      and run an exact radix select (2048 linear buckets, then 11/11/10-bit
-//      digits of the order-preserving keys) on those few.
+//      and bucket them linearly over [T, max].  Candidates above the boundary
+//      bucket are kept; the few in the boundary bucket are ranked by direct
+//      comparison (value, then position).  A boundary bucket holding more than 64
+//      candidates is resolved by radix passes over the 11/11/10-bit digits of the
+//      order-preserving keys instead.
 //   4. Else raise T with a histogram of the scores >= T and repeat (T strictly
 //      increases, so this ends; typical rows never get here).
 // Rows longer than one chunk are split: every chunk keeps its own best
@@ -32,75 +38,89 @@ constexpr int NBINS = 2048;
 constexpr int BPT = NBINS / NT;          // histogram bins scanned per thread
 constexpr int CAND_CAP = 4096;           // candidates compacted into LDS
 constexpr int EC = CAND_CAP / NT;        // candidates per thread in the exact select
+constexpr int BND_CAP = 64;              // boundary candidates ranked directly
 
 struct SelShared {
   int hist[NBINS];
-  int wsum[NW], wsum2[NW];
-  int woff[NW + 1];
-  float fa[NW], fb[NW];
+  int xi[2][NW], xj[2][NW];              // per-wave exchange slots, two sets
+  float xf[2][NW], xg[2][NW], xh[2][NW];
   int digit, above;
-  uint32_t ckey[CAND_CAP + 1];           // last entry: sink for non-candidates
+  uint32_t ckey[CAND_CAP + 1];           // candidates; the last entry is a sink
   int32_t cid[CAND_CAP + 1];
+  __attribute__((aligned(16))) uint32_t bkey[BND_CAP + 4];   // boundary candidates
 };
-
-__device__ __forceinline__ uint64_t lanemask_lt() {
-  const int lane = threadIdx.x & 63;
-  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
-}
-
-// exclusive scan of one value per wave through LDS: returns this wave's offset
-// and *total the sum over the workgroup
-__device__ __forceinline__ int wave_offsets(int v, SelShared& sh, int* total) {
-  const int wv = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) sh.wsum[wv] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int s = 0;
-    for (int i = 0; i < NW; ++i) { sh.woff[i] = s; s += sh.wsum[i]; }
-    sh.woff[NW] = s;
-  }
-  __syncthreads();
-  *total = sh.woff[NW];
-  return sh.woff[wv];
-}
-
-// workgroup sums of two per-wave counts
-__device__ __forceinline__ void wave_sum2(int x, int y, SelShared& sh, int* sx, int* sy) {
-  const int wv = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) { sh.wsum[wv] = x; sh.wsum2[wv] = y; }
-  __syncthreads();
-  int a = 0, b = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) { a += sh.wsum[i]; b += sh.wsum2[i]; }
-  *sx = a;
-  *sy = b;
-  __syncthreads();
-}
-
-// workgroup min of lo and max of hi
-__device__ __forceinline__ void minmax(float lo, float hi, SelShared& sh, float* mn, float* mx) {
-  const int wv = threadIdx.x >> 6;
-  lo = wave_min(lo);
-  hi = wave_max(hi);
-  if ((threadIdx.x & 63) == 0) { sh.fa[wv] = lo; sh.fb[wv] = hi; }
-  __syncthreads();
-  lo = sh.fa[0];
-  hi = sh.fb[0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) { lo = fminf(lo, sh.fa[i]); hi = fmaxf(hi, sh.fb[i]); }
-  *mn = lo;
-  *mx = hi;
-  __syncthreads();
-}
 
 __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Histogram scan: thread t holds the BPT bins below 2048 - BPT*t (descending);
+// Workgroup exchanges: each holds exactly one barrier.  Two consecutive calls
+// must use different sets p (a call's slots may still be read by slower waves
+// until the next barrier has passed).
+
+// sum of an int; min of a, max of b, min of c
+__device__ __forceinline__ void x_stats(int n, float a, float b, float c, SelShared& sh, int p, int* sn,
+                                        float* ma, float* mb, float* mc) {
+  const int wv = threadIdx.x >> 6;
+  n = wave_sum(n);
+  a = wave_min(a);
+  b = wave_max(b);
+  c = wave_min(c);
+  if ((threadIdx.x & 63) == 0) { sh.xi[p][wv] = n; sh.xf[p][wv] = a; sh.xg[p][wv] = b; sh.xh[p][wv] = c; }
+  __syncthreads();
+  int s = 0;
+  float x = INFINITY, y = -INFINITY, z = INFINITY;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    s += sh.xi[p][i];
+    x = fminf(x, sh.xf[p][i]);
+    y = fmaxf(y, sh.xg[p][i]);
+    z = fminf(z, sh.xh[p][i]);
+  }
+  *sn = s;
+  *ma = x;
+  *mb = y;
+  *mc = z;
+}
+
+// min of a and of b
+__device__ __forceinline__ void x_min2(float a, float b, SelShared& sh, int p, float* ma, float* mb) {
+  const int wv = threadIdx.x >> 6;
+  a = wave_min(a);
+  b = wave_min(b);
+  if ((threadIdx.x & 63) == 0) { sh.xf[p][wv] = a; sh.xh[p][wv] = b; }
+  __syncthreads();
+  float x = INFINITY, y = INFINITY;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) { x = fminf(x, sh.xf[p][i]); y = fminf(y, sh.xh[p][i]); }
+  *ma = x;
+  *mb = y;
+}
+
+// exclusive prefix of x over the threads, its total, and the sum of y
+__device__ __forceinline__ int x_scan(int x, int y, SelShared& sh, int p, int* total, int* ysum) {
+  const int wv = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(x);
+  y = wave_sum(y);
+  if ((threadIdx.x & 63) == 0) { sh.xi[p][wv] = lane63(incl); sh.xj[p][wv] = y; }
+  __syncthreads();
+  int before = 0, tot = 0, ys = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int c = sh.xi[p][i];
+    before += i < wv ? c : 0;
+    tot += c;
+    ys += sh.xj[p][i];
+  }
+  *total = tot;
+  *ysum = ys;
+  return before + incl - x;
+}
+
+// Histogram scan: thread t holds the BPT bins below NBINS - BPT*t (descending);
 // finds the bin d with count(bins > d) < remaining <= count(bins >= d) into
-// sh.digit / sh.above, and clears the histogram for the next pass.
-__device__ __forceinline__ void find_bin(SelShared& sh, int remaining) {
+// sh.digit / sh.above and clears the histogram for the next pass.  Two barriers.
+__device__ __forceinline__ void find_bin(SelShared& sh, int remaining, int p) {
   const int top = NBINS - 1 - BPT * (int)threadIdx.x;
   int h[BPT];
   int sum = 0;
@@ -110,10 +130,8 @@ __device__ __forceinline__ void find_bin(SelShared& sh, int remaining) {
     sh.hist[top - i] = 0;
     sum += h[i];
   }
-  const int x = wave_incl_scan(sum);
-  int tot;
-  const int base = wave_offsets(lane63(x), sh, &tot);
-  int before = base + x - sum;               // values in bins > top
+  int tot, unused;
+  int before = x_scan(sum, 0, sh, p, &tot, &unused);   // values in bins > top
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
     if (before < remaining && before + h[i] >= remaining) {
@@ -125,7 +143,7 @@ __device__ __forceinline__ void find_bin(SelShared& sh, int remaining) {
   __syncthreads();
 }
 
-// monotone map of a float range onto the 2048 histogram bins
+// monotone map of a float range onto the histogram bins
 struct Buckets {
   float lo, inv;
   __device__ __forceinline__ int operator()(float f) const {
@@ -142,126 +160,163 @@ __device__ __forceinline__ Buckets make_buckets(float lo, float hi) {
   return bk;
 }
 
-// exclusive prefix sum of one int per thread over the workgroup
-__device__ __forceinline__ int block_scan(int x, SelShared& sh, int* total) {
-  const int incl = wave_incl_scan(x);
-  const int base = wave_offsets(lane63(incl), sh, total);
-  return base + incl - x;
-}
-
-// Exact select over the compacted candidates (sh.ckey / sh.cid [0..M)), 1 <= kk <= M:
-// emit(rank, id, key) for the kk best, ties to the lower candidate position.
+// Exact select over the compacted candidates (sh.ckey / sh.cid [0..M)), all in
+// [lo, hi], 1 <= kk <= M: emit(rank, id, key) for the kk best, ties to the lower
+// candidate position.  Enters right after a barrier; its first exchange uses set 0.
 template <class Emit>
-__device__ void select_candidates(int M, int kk, SelShared& sh, Emit emit) {
+__device__ void select_candidates(int M, int kk, float lo, float hi, SelShared& sh, Emit emit) {
   const int cb = threadIdx.x * EC;
   uint32_t key[EC];
-#pragma unroll
-  for (int e = 0; e < EC; ++e) key[e] = cb + e < M ? sh.ckey[cb + e] : 0u;
-  uint32_t prefix = 0;
-  int remaining = kk;
-  if (kk < M) {
-    // pass 0: linear buckets over the candidates' value range
-    float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < EC; ++e)
-      if (key[e]) { lo = fminf(lo, key_float(key[e])); hi = fmaxf(hi, key_float(key[e])); }
-    minmax(lo, hi, sh, &lo, &hi);
-    const Buckets bk = make_buckets(lo, hi);
-#pragma unroll
-    for (int e = 0; e < EC; ++e)
-      if (key[e]) atomicAdd(&sh.hist[bk(key_float(key[e]))], 1);
-    __syncthreads();
-    find_bin(sh, remaining);
-    const int B = sh.digit;
-    remaining -= sh.above;
-    uint32_t inb = 0;
-#pragma unroll
-    for (int e = 0; e < EC; ++e)
-      if (key[e] && bk(key_float(key[e])) == B) inb |= 1u << e;
-    // passes 1-3: exact digits of the keys in the boundary bucket
-    uint32_t pmask = 0;
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
-#pragma unroll
-      for (int e = 0; e < EC; ++e)
-        if (((inb >> e) & 1u) && (key[e] & pmask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & dmask], 1);
-      __syncthreads();
-      find_bin(sh, remaining);
-      remaining -= sh.above;
-      prefix |= (uint32_t)sh.digit << shift;
-      pmask |= dmask << shift;
-    }
-  }
-  // ordered output: keys > prefix, then the first `remaining` keys == prefix
-  int nt = 0;
-#pragma unroll
-  for (int e = 0; e < EC; ++e) nt += (key[e] != 0u && key[e] == prefix);
-  int tot;
-  int tie = block_scan(nt, sh, &tot);
-  uint32_t smask = 0;
-  int ns = 0;
+  int32_t cid[EC];
 #pragma unroll
   for (int e = 0; e < EC; ++e) {
-    const bool eq = key[e] != 0u && key[e] == prefix;
-    const bool sl = (key[e] != 0u && key[e] > prefix) || (eq && tie < remaining);
-    tie += eq;
-    smask |= (uint32_t)sl << e;
-    ns += sl;
+    key[e] = cb + e < M ? sh.ckey[cb + e] : 0u;
+    cid[e] = sh.cid[cb + e];
   }
-  int off = block_scan(ns, sh, &tot);
+  uint32_t sel = 0;                       // bit e: candidate e is kept
+  if (kk >= M) {
+#pragma unroll
+    for (int e = 0; e < EC; ++e) sel |= (uint32_t)(key[e] != 0u) << e;
+  } else {
+    const Buckets bk = make_buckets(lo, hi);
+    int bin[EC];
+#pragma unroll
+    for (int e = 0; e < EC; ++e) {
+      bin[e] = key[e] ? bk(key_float(key[e])) : -1;
+      if (key[e]) atomicAdd(&sh.hist[bin[e]], 1);
+    }
+    __syncthreads();
+    find_bin(sh, kk, 0);
+    const int B = sh.digit;
+    const int remaining = kk - sh.above;  // boundary candidates still to keep
+    int nb = 0;
+#pragma unroll
+    for (int e = 0; e < EC; ++e) {
+      sel |= (uint32_t)(bin[e] > B) << e;
+      nb += bin[e] == B;
+    }
+    int NB, unused;
+    int bpos = x_scan(nb, 0, sh, 1, &NB, &unused);
+    if (NB <= BND_CAP) {
+      // rank each boundary candidate among them: a higher key, or an equal key at
+      // a lower position, ranks before it.  Entries NB .. NB+3 are zero keys,
+      // which never rank before a candidate.
+#pragma unroll
+      for (int e = 0; e < EC; ++e)
+        if (bin[e] == B) sh.bkey[bpos++] = key[e];
+      if ((int)threadIdx.x < 4) sh.bkey[NB + threadIdx.x] = 0u;
+      __syncthreads();
+      bpos -= nb;
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        if (bin[e] == B) {
+          int rank = 0;
+#pragma unroll 1
+          for (int j = 0; j < NB; j += 4) {
+            const u32x4_t k4 = *(const u32x4_t*)&sh.bkey[j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rank += k4[i] > key[e] || (k4[i] == key[e] && j + i < bpos);
+          }
+          sel |= (uint32_t)(rank < remaining) << e;
+          ++bpos;
+        }
+      }
+    } else {
+      // a crowded boundary bucket: exact digits of its keys
+      uint32_t prefix = 0, pmask = 0;
+      int rem = remaining;
+#pragma unroll 1
+      for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+#pragma unroll
+        for (int e = 0; e < EC; ++e)
+          if (bin[e] == B && (key[e] & pmask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & dmask], 1);
+        __syncthreads();
+        find_bin(sh, rem, pass & 1);
+        rem -= sh.above;
+        prefix |= (uint32_t)sh.digit << shift;
+        pmask |= dmask << shift;
+      }
+      // keys > prefix, then the first rem keys == prefix in candidate order
+      int nt = 0;
+#pragma unroll
+      for (int e = 0; e < EC; ++e) nt += bin[e] == B && key[e] == prefix;
+      int tot;
+      int tie = x_scan(nt, 0, sh, 1, &tot, &unused);
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        if (bin[e] == B) {
+          const bool eq = key[e] == prefix;
+          sel |= (uint32_t)(key[e] > prefix || (eq && tie < rem)) << e;
+          tie += eq;
+        }
+      }
+    }
+  }
+  int ns = 0;
+#pragma unroll
+  for (int e = 0; e < EC; ++e) ns += (sel >> e) & 1u;
+  int tot, unused;
+  int off = x_scan(ns, 0, sh, 0, &tot, &unused);
 #pragma unroll
   for (int e = 0; e < EC; ++e)
-    if ((smask >> e) & 1u) emit(off++, sh.cid[cb + e], key[e]);
+    if ((sel >> e) & 1u) emit(off++, cid[e], key[e]);
 }
 
 // The kk best of v (NaN = empty), ties to the lower slot, 1 <= kk <= #values;
-// emit(rank, id, key) once per kept value (id[] carried along, key = float_key(v)),
-// ranks in slot order.  Nothing is loaded from memory at emit time: a load inside
-// the per-element branches would serialise one round trip per element.
+// emit(rank, id[e], key) once per kept value, ranks in slot order.  Nothing is
+// loaded from memory at emit time: a load inside the per-element branches would
+// serialise one round trip per element.
 template <int E, class Emit>
 __device__ void select_top(const float (&v)[E], const int32_t (&id)[E], int kk, SelShared& sh, Emit emit) {
   constexpr int GS = E >= 8 ? 8 : E;          // scores per group maximum
   constexpr int NG = E / GS;
-  // every histogram pass below starts from zeroed bins (find_bin re-zeroes them)
+  // zeroed before the first exchange's barrier; find_bin re-zeroes what it reads
   for (int i = threadIdx.x; i < NBINS; i += NT) sh.hist[i] = 0;
-  __syncthreads();
 
-  // 1. T <= the kk-th largest group maximum (or -inf if there are fewer groups)
+  // 1. T <= the kk-th largest group maximum (or the smallest value if there are
+  //    fewer than kk groups)
   float gm[NG];
   int ngv = 0;
+  float glo = INFINITY, vhi = -INFINITY, vlo = INFINITY;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    float m = v[g * GS];
+    float m = v[g * GS], mn = v[g * GS];
 #pragma unroll
-    for (int i = 1; i < GS; ++i) m = fmaxf(m, v[g * GS + i]);    // NaN-ignoring
+    for (int i = 1; i < GS; ++i) {
+      m = fmaxf(m, v[g * GS + i]);               // NaN-ignoring
+      mn = fminf(mn, v[g * GS + i]);
+    }
     gm[g] = m;
-    ngv += !__builtin_isnan(m);
+    if (!__builtin_isnan(m)) {
+      ++ngv;
+      glo = fminf(glo, m);
+      vhi = fmaxf(vhi, m);
+      vlo = fminf(vlo, mn);
+    }
   }
-  int nval, unused;
-  wave_sum2(wave_sum(ngv), 0, sh, &nval, &unused);
-  float T = -INFINITY;
+  int nval;
+  x_stats(ngv, glo, vhi, vlo, sh, 0, &nval, &glo, &vhi, &vlo);
+  float T = vlo;
+  int par = 1;
   if (kk <= nval) {
-    float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-      if (!__builtin_isnan(gm[g])) { lo = fminf(lo, gm[g]); hi = fmaxf(hi, gm[g]); }
-    minmax(lo, hi, sh, &lo, &hi);
-    const Buckets bk = make_buckets(lo, hi);
+    const Buckets bk = make_buckets(glo, vhi);
 #pragma unroll
     for (int g = 0; g < NG; ++g)
       if (!__builtin_isnan(gm[g])) atomicAdd(&sh.hist[bk(gm[g])], 1);
     __syncthreads();
-    find_bin(sh, kk);
+    find_bin(sh, kk, 1);
     const int B = sh.digit;
     float m = INFINITY;
 #pragma unroll
     for (int g = 0; g < NG; ++g)
       if (!__builtin_isnan(gm[g]) && bk(gm[g]) >= B) m = fminf(m, gm[g]);
-    minmax(m, m, sh, &T, &hi);
+    float unusedf;
+    x_min2(m, INFINITY, sh, 0, &T, &unusedf);
   }
 
+  // T is always one of the values, so every candidate lies in [T, vhi]
 #pragma unroll 1
   for (;;) {
     int g = 0, q = 0;
@@ -270,16 +325,16 @@ __device__ void select_top(const float (&v)[E], const int32_t (&id)[E], int kk, 
       g += v[e] > T;
       q += v[e] >= T;
     }
-    int G, Q;
-    const int qoff = block_scan(q, sh, &Q);
-    wave_sum2(wave_sum(g), 0, sh, &G, &unused);
+    int Q, G;
+    const int qoff = x_scan(q, g, sh, par, &Q, &G);
+    par ^= 1;
     if (G < kk) {
       // 2. T is the kk-th largest value: every v > T, then the first kk - G ties
       int nt = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) nt += v[e] == T;
-      int tot;
-      int tie = block_scan(nt, sh, &tot);
+      int tot, unused;
+      int tie = x_scan(nt, 0, sh, par, &tot, &unused);
       uint64_t smask = 0;
       int ns = 0;
 #pragma unroll
@@ -290,7 +345,7 @@ __device__ void select_top(const float (&v)[E], const int32_t (&id)[E], int kk, 
         smask |= (uint64_t)sl << e;
         ns += sl;
       }
-      int off = block_scan(ns, sh, &tot);
+      int off = x_scan(ns, 0, sh, par ^ 1, &tot, &unused);
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if ((smask >> e) & 1ull) emit(off++, id[e], float_key(v[e]));
@@ -309,23 +364,17 @@ __device__ void select_top(const float (&v)[E], const int32_t (&id)[E], int kk, 
         off += c;
       }
       __syncthreads();
-      select_candidates(Q, kk, sh, emit);
+      select_candidates(Q, kk, T, vhi, sh, emit);
       return;
     }
-    // 4. raise T: histogram of {v >= T} over [T, max]; the new T stays <= the
+    // 4. raise T: histogram of {v >= T} over [T, vhi]; the new T stays <= the
     //    kk-th largest value and strictly increases
-    float hi = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (v[e] >= T) hi = fmaxf(hi, v[e]);
-    float lo;
-    minmax(INFINITY, hi, sh, &lo, &hi);
-    const Buckets bk = make_buckets(T, hi);
+    const Buckets bk = make_buckets(T, vhi);
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (v[e] >= T) atomicAdd(&sh.hist[bk(v[e])], 1);
     __syncthreads();
-    find_bin(sh, kk);
+    find_bin(sh, kk, par);
     const int B = sh.digit;
     float m = INFINITY, above = INFINITY;
 #pragma unroll
@@ -334,9 +383,9 @@ __device__ void select_top(const float (&v)[E], const int32_t (&id)[E], int kk, 
       if (v[e] > T) above = fminf(above, v[e]);
     }
     float Tn, An;
-    minmax(m, -above, sh, &Tn, &An);
+    x_min2(m, above, sh, par ^ 1, &Tn, &An);
     // more than kk values exceed T here, so the smallest of them is also safe
-    T = Tn > T ? Tn : -An;
+    T = Tn > T ? Tn : An;
   }
 }
 
@@ -453,12 +502,12 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(TopkArgs a) {
 
 template <int E>
 void launch_chunks(const TopkArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((topk_chunk_kernel<E>), dim3(a.n_chunks, a.n_rows), dim3(NT), 0, s, a);
+  launch(K_TOPK, topk_chunk_kernel<E>, dim3(a.n_chunks, a.n_rows), dim3(NT), s, a);
 }
 
 template <int E>
 void launch_merge(const TopkArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((topk_merge_kernel<E>), dim3(a.n_rows), dim3(NT), 0, s, a);
+  launch(K_TOPK_MERGE, topk_merge_kernel<E>, dim3(a.n_rows), dim3(NT), s, a);
 }
 
 int per_thread(int n) {
@@ -474,7 +523,6 @@ int topk_chunk_size(int max_blocks) {
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  hook_before(K_TOPK, s);
   switch (a.chunk / NT) {
     case 1: launch_chunks<1>(a, s); break;
     case 2: launch_chunks<2>(a, s); break;
@@ -483,7 +531,6 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     case 16: launch_chunks<16>(a, s); break;
     default: launch_chunks<32>(a, s); break;
   }
-  hook_after(K_TOPK, s);
   if (a.n_chunks > 1) {
     switch (per_thread(a.n_chunks * (a.top_k - 1))) {
       case 1: launch_merge<1>(a, s); break;

@@ -159,4 +159,7 @@ def test_workspace_sizes_are_consistent(L):
 
 def test_timing_hook_arguments(L):
     assert L.LIB.ip_time_next_launch(99, FAKE, FAKE) == L.IP_EINVAL
-    assert L.LIB.ip_time_next_launch(0, None, None) == L.IP_OK
+    assert L.LIB.ip_time_next_launch(7, FAKE, FAKE) == L.IP_EINVAL
+    assert L.LIB.ip_time_next_launch(2, FAKE, None) == L.IP_EINVAL      # one event only
+    assert L.LIB.ip_time_next_launch(6, FAKE, FAKE) == L.IP_OK          # top-k merge is hookable
+    assert L.LIB.ip_time_next_launch(0, None, None) == L.IP_OK          # disarms all
