@@ -33,7 +33,7 @@ thread_local Hook g_hook[ip::K_LAST + 1];   // armed events per kernel id
 
 constexpr int64_t kMaxTokens = int64_t(1) << 31;   // int32 token positions
 constexpr size_t kScoreBudget = size_t(256) << 20;  // score workspace per row chunk
-constexpr int kTargetWorkgroups = 256;              // MI355X compute units
+constexpr int kAttnWorkgroups = 128;                // split decode attention up to this many workgroups
 
 ip_status check_seqs(const ip_seqs* s, const char* fn) {
   if (!s) return fail(IP_EINVAL, "%s: seqs is NULL", fn);
@@ -118,9 +118,10 @@ AttnPlan attn_plan(int n_q, int n_heads, int dv, int top_k, int q_dtype) {
   p.n_split = 1;
   p.blocks_per_split = top_k;
   if (q_dtype == IP_BF16) {
-    // one workgroup per (row, split, 16-head group): aim at one per compute unit
+    // one workgroup per (row, split) covering all 64 heads; splits add workgroups
+    // for small batches at the price of (O, m, l) partials (128 KB per split)
     const int nsub = (top_k + 15) / 16;                 // 64-token sub-tiles
-    const int want = (kTargetWorkgroups / (ip::LAT_H / 16) + n_q - 1) / std::max(1, n_q);
+    const int want = (kAttnWorkgroups + n_q - 1) / std::max(1, n_q);
     const int ns = std::max(1, std::min(want, std::min(nsub, 64)));
     const int sub_per = std::min((nsub + ns - 1) / ns, 32);   // <= 512 blocks per split
     p.blocks_per_split = sub_per * 16;
@@ -343,9 +344,9 @@ static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, c
   }
   if (q_dtype == IP_F32) {
     if (ip_status st = check_cache(v, fn, "v")) return st;
-    if (k->dtype != IP_F32 || v->dtype != IP_F32 || n_heads < 1 || n_heads > 16 || dk < 1 || dk > 128 ||
-        dv < 1 || dv > 128 || k->row_dim < dk || v->row_dim < dv)
-      return fail(IP_EUNSUPPORTED, "%s: F32 attention needs F32 k/v caches, n_heads <= 16, dk and dv <= 128", fn);
+    if (k->dtype != IP_F32 || v->dtype != IP_F32 || n_heads < 1 || n_heads > 16 || dk < 4 || dk > 128 ||
+        dv < 1 || dv > 128 || dk % 4 || dv % 4 || k->row_dim < dk || v->row_dim < dv)
+      return fail(IP_EUNSUPPORTED, "%s: F32 attention needs F32 k/v caches, n_heads <= 16, dk and dv <= 128 and multiples of 4", fn);
     a.v = (const uint8_t*)v->data;
     a.v_stride = v->row_stride;
     a.n_split = 1;

@@ -149,6 +149,15 @@ __device__ __forceinline__ int wave_sum(int x) {
   x += dpp_i<0x143, 0xC>(0, x);
   return lane63(x);
 }
+__device__ __forceinline__ float wave_sum_f(float x) {
+  x += dpp_f<0xB1>(0.f, x);
+  x += dpp_f<0x4E>(0.f, x);
+  x += dpp_f<0x141>(0.f, x);
+  x += dpp_f<0x140>(0.f, x);
+  x += dpp_f<0x142, 0xA>(0.f, x);
+  x += dpp_f<0x143, 0xC>(0.f, x);
+  return lane63f(x);
+}
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp_f<0xB1>(-INFINITY, x));
   x = fmaxf(x, dpp_f<0x4E>(-INFINITY, x));

@@ -22,7 +22,8 @@ constexpr int TILES = 4;                        // 32-key tiles per wave
 constexpr int KEYS_PER_WG = 4 * TILES * 32;     // 512
 constexpr int HI = 32, DI = 128;
 
-// RPW query rows share one key chunk held in registers (prefill); decode uses 1.
+// RPW query rows share one key chunk held in registers (prefill, where consecutive
+// rows are tokens of one sequence); decode rows are separate sequences and use 1.
 // All key loads of a wave are issued before the first MFMA, so each compute unit
 // keeps ~128 KB of the pooled cache in flight.
 template <int RPW>
@@ -144,7 +145,8 @@ __global__ __launch_bounds__(NT) void score_f32_kernel(ScoreArgs a) {
 hipError_t launch_score_fp8_bf16(const ScoreArgs& a, hipStream_t s) {
   if (a.n_rows <= 0 || a.max_blocks <= 0) return hipSuccess;
   const unsigned gx = (a.max_blocks + KEYS_PER_WG - 1) / KEYS_PER_WG;
-  if (a.n_rows >= 64) {
+  if (a.q_seq && a.n_rows >= 64) {
+    // prefill: consecutive rows are query tokens of one sequence and share its keys
     constexpr int R = 16;
     launch(K_SCORE, score_fp8_bf16_kernel<R>, dim3(gx, (a.n_rows + R - 1) / R), dim3(NT), s, a);
   } else {
