@@ -21,6 +21,10 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops stay off (hand-off to the scalar forms)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs where they fit: the attention kernel
+    # rescales its O accumulators with VALU ops, which otherwise costs a copy of
+    # all of them between register files on every sub-tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
 ]

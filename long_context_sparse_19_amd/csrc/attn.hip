@@ -7,15 +7,19 @@
 //   one workgroup (4 waves) per (query row, split of the selected blocks) covers all
 //   64 heads, so every gathered latent row is read from memory once and feeds 64
 //   heads.  The selected rows are staged 64 tokens (16 blocks of 4 contiguous rows)
-//   at a time into LDS, double buffered through registers.
-//   - S^T = K . q^T on v_mfma_f32_32x32x16_bf16: wave w takes tokens 32*(w&1) .. +31
-//     against heads 32*(w>>1) .. +31; its 32 heads of q (576 dims) stay in
-//     registers for the whole row, K comes from LDS.
-//   - Online softmax in base 2; the two waves that share a head block exchange their
-//     per-head maxima and sums through LDS; P goes to LDS as bf16.
-//   - O[64 heads, 128 dims of wave w] += P . V on the same MFMA, V read with the
-//     transposing LDS read (ds_read_b64_tr_b16) from the rows K came from.
-//   With more than one split the unnormalised partials (O, m, l) are merged by a
+//   at a time into LDS by LDS DMA, double buffered.  The kernel is bound by LDS
+//   reads, so both products use v_mfma_f32_32x32x16_bf16, whose operand fragments
+//   each feed 32 heads:
+//   - S^T = K . q^T: wave w takes heads 32(w&1) .. +31 against tokens 32(w>>1) .. +31
+//     (its 32 heads of q, 576 dims, stay in accumulation registers);
+//   - online softmax in base 2 against a per-head reference maximum shared by the
+//     two waves of a head block; it moves (and O and l with it) only when a tile
+//     maximum passes it by more than 2^8, which after the first sub-tile is rare, so
+//     the common path needs no exchange of maxima; P goes to LDS as bf16;
+//   - O^T[dims, heads] += V^T . P^T: wave w takes dims 128w .. +127 for all 64 heads,
+//     V read with the transposing LDS read (ds_read_b64_tr_b16).
+//   Two barriers per sub-tile: P complete, and next sub-tile landed / buffer free.
+//   With more than one split the partials (O, reference maximum, l) are merged by a
 //   combine kernel.
 // f32 path (small geometries): plain VALU, one workgroup per row.
 #include "kernels.hpp"
@@ -25,16 +29,17 @@ namespace ip {
 namespace {
 
 constexpr int NT = 256;                        // f32 path
-constexpr int NTA = 512;                       // bf16 path: 8 waves
+constexpr int NTA = 256;                       // bf16 path: 4 waves
 constexpr int NWA = NTA / 64;
 constexpr int SUBT = 64;                       // tokens per sub-tile (16 blocks)
-constexpr int ROWB = LAT_DK * 2 + 16;          // padded LDS row: 1168 bytes
-constexpr int KVBUF = SUBT * ROWB;             // 74752 bytes
-constexpr int PROW = SUBT * 2 + 16;            // P row of one head: 64 bf16 + pad = 144 bytes
+constexpr int COLB = SUBT * 64;                // one 64-byte column (32 dims) of all 64 rows
+constexpr int NCOL = LAT_DK * 2 / 64;          // 18 columns per latent row
+constexpr int KVBUF = NCOL * COLB;             // 73728 bytes
 constexpr int CHUNKS = LAT_DK * 2 / 16;        // 72 16-byte chunks per latent row
-constexpr int QSTEPS = LAT_DK / 32;            // 18 MFMA k-steps over the 576 dims
+constexpr int KSTEPS = LAT_DK / 16;            // 36 MFMA k-steps over the 576 dims
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float LOG2E = 1.44269504088896341f;
+constexpr float RESCALE_LOG2 = 8.f;            // reference maximum moves when passed by more
 
 constexpr int MAX_BLOCKS_PER_SPLIT = 512;      // host keeps splits within this
 constexpr int VIS_SHIFT = 29;                  // block table: first row | visible tokens << 29
@@ -43,19 +48,20 @@ constexpr uint32_t ROW_BITS = (1u << VIS_SHIFT) - 1;
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-// The latent sub-tiles live in their own LDS object (filled by LDS DMA); keeping the
-// other shared data in a separate object lets the compiler see that stores to it
-// cannot alias the DMA, so it does not make them wait for outstanding loads.
-struct __align__(16) AttnKV {
-  uint8_t kv[2][KVBUF];
-};
+// The two latent sub-tile buffers are LDS objects of their own (filled by LDS DMA),
+// apart from the rest of the shared data.  The compiler tags accesses with the LDS
+// object they touch, so it can see that reading one buffer (or the other shared
+// data) does not alias the DMA into the other buffer, and does not make those
+// accesses wait for the outstanding sub-tile loads.  For that every access must
+// name its buffer statically: the main loop is unrolled by two.
+constexpr int PROW = SUBT * 2 + 16;            // P row of one head: 64 bf16 + pad = 144 bytes
+
 struct __align__(16) AttnShared {
-  uint8_t p[LAT_H * PROW];
+  uint8_t p[LAT_H * PROW];                     // P[head][token] bf16
   uint32_t brow[MAX_BLOCKS_PER_SPLIT];
-  float m_part[2][LAT_H];
-  float l_part[2][LAT_H];
-  float alpha[LAT_H];
-  float lfin[LAT_H];
+  float tmax[2][LAT_H];                        // tile maxima of the two token halves
+  float lpart[2][LAT_H];                       // l of the two token halves (end)
+  int need[4];                                 // a wave's tile maximum passed the reference
 };
 
 // LDS accesses that never touch the latent sub-tile buffers go through these.  The
@@ -80,6 +86,17 @@ __device__ __forceinline__ RowCtx row_ctx(const AttnArgs& a, int r) {
   return c;
 }
 
+// Lanes l and l ^ 32 combined (v_permlane32_swap with the same register as both
+// operands gives every lane its own value and that of lane l ^ 32).
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Combine over the four lanes l % 16 + 16q (q < 4).  v_permlane16_swap /
 // v_permlane32_swap with the same register as both operands give every lane, in
 // the two results, its own value and that of lane l ^ 16 (resp. l ^ 32).
@@ -100,243 +117,309 @@ __device__ __forceinline__ float quad_sum16(float x) {
 // sel[sb0 + i] with the number of its tokens at or before the query (0..4) in the
 // top bits.  Entries that are -1, past the split or entirely after the query
 // point at the query's own block (whose 4 rows exist) with 0 visible tokens, so
-// every load stays inside the cache.
-__device__ __forceinline__ void build_block_table(const AttnArgs& a, const RowCtx& c, int sb0, int send,
-                                                  AttnShared& sh) {
+// every load stays inside the cache.  Thread t handles entries t and t + NTA: the
+// selection ids are fetched first (fetch_blocks) and turned into entries later
+// (build_block_table), so other loads can be issued in between.
+struct BlockIds {
+  int blk[MAX_BLOCKS_PER_SPLIT / NTA];
+};
+
+__device__ __forceinline__ BlockIds fetch_blocks(const RowCtx& c, int sb0, int send) {
+  BlockIds ids;
+#pragma unroll
+  for (int k = 0; k < MAX_BLOCKS_PER_SPLIT / NTA; ++k) {
+    const int bi = sb0 + (int)threadIdx.x + k * NTA;
+    ids.blk[k] = bi < send ? c.sel[bi] : -1;
+  }
+  return ids;
+}
+
+__device__ __forceinline__ void build_block_table(const AttnArgs& a, const RowCtx& c, const BlockIds& ids, int sb0,
+                                                  int send, AttnShared& sh) {
   const int nb = ((send - sb0 + 15) >> 4) << 4;
   const uint32_t own = (uint32_t)a.L.tok_row(c.b, (int64_t)(c.p >> 2) * 4);
-  for (int i = threadIdx.x; i < nb; i += NTA) {
-    const int bi = sb0 + i;
-    const int blk = bi < send ? c.sel[bi] : -1;
-    uint32_t e = own;
-    if (blk >= 0 && blk * 4 <= c.p) {
-      const uint32_t row = (uint32_t)a.L.tok_row(c.b, (int64_t)blk * 4);
-      e = row | ((uint32_t)min(4, c.p - blk * 4 + 1) << VIS_SHIFT);
+#pragma unroll
+  for (int k = 0; k < MAX_BLOCKS_PER_SPLIT / NTA; ++k) {
+    const int i = (int)threadIdx.x + k * NTA;
+    if (i < nb) {
+      const int blk = ids.blk[k];
+      uint32_t e = own;
+      if (blk >= 0 && blk * 4 <= c.p) {
+        const uint32_t row = (uint32_t)a.L.tok_row(c.b, (int64_t)blk * 4);
+        e = row | ((uint32_t)min(4, c.p - blk * 4 + 1) << VIS_SHIFT);
+      }
+      lds_st(&sh.brow[i], e);
     }
-    sh.brow[i] = e;
   }
 }
 
-// Sub-tile n (64 tokens = 16 blocks) straight from global memory into LDS
-// (global_load_lds_dwordx4: lane l of one instruction fills bytes 16l .. 16l+15 of
-// a 1 KB LDS span).  The buffer holds 64 rows of 73 16-byte chunks (72 data + 1 pad);
-// linear chunk c = 64k + lane of instruction k is chunk c % 73 of row c / 73, and a
-// pad chunk loads chunk 0 of its row again.  73 instructions; wave w issues
-// k = w, w+8, .. (10 for wave 0, 9 for the others).
-constexpr int KV_INSTR = SUBT * (CHUNKS + 1) / 64;    // 73
+// Sub-tile layout in LDS: 18 columns of 4 KB, column c holding bytes 64c .. 64c+63
+// (dims 32c .. 32c+31) of all 64 rows, row t at 64t, with the four 16-byte chunks of
+// each 64-byte segment stored in slots chunk ^ ((t >> 2) & 3).  The swizzle spreads
+// the same chunk of 16 consecutive rows (a K fragment read) over all 64 banks; the
+// 4-row groups of the transposing V reads share one swizzle and stay conflict-free.
+//
+// Sub-tile n goes straight from global memory into that layout with
+// global_load_lds_dwordx4 (lane l of one instruction fills bytes 16l .. 16l+15 of a
+// 1 KB span): instruction (c, g) fills rows 16g .. 16g+15 of column c, lane l taking
+// bytes 16(l%4) of the column from row 16g + l/4.  Wave w issues the 9 instructions
+// g = w and c = 0 .. 17, so each lane reads one row per sub-tile.
+constexpr int KV_LOADS = NCOL * 4 / NWA;       // 18 per wave
 
-__device__ __forceinline__ int subtile_loads(int wv) { return (KV_INSTR - wv + NWA - 1) / NWA; }
+// This lane's source row segment for sub-tile n (see above); column c then comes
+// from src + 64c and goes to buf + wv*1024 + c*COLB.
+__device__ __forceinline__ const uint8_t* subtile_src(const AttnArgs& a, const AttnShared& sh, int n) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = 16 * wv + (lane >> 2);
+  const uint32_t grow = (lds_ld(&sh.brow[n * 16 + (row >> 2)]) & ROW_BITS) + (row & 3);
+  // 16-byte slot j of a row's 64-byte segment holds chunk j ^ ((row >> 2) & 3)
+  return a.k + (uint64_t)grow * a.k_stride + 16 * ((lane & 3) ^ ((row >> 2) & 3));
+}
+
+__device__ __forceinline__ void load_column(const uint8_t* src, uint8_t* buf, int c) {
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src + 64 * c),
+                                   (void __attribute__((address_space(3)))*)(buf + wv * 1024 + c * COLB), 16, 0, 0);
+}
 
 __device__ __forceinline__ void load_subtile(const AttnArgs& a, const AttnShared& sh, int n, uint8_t* buf) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint8_t* src = subtile_src(a, sh, n);
 #pragma unroll
-  for (int i = 0; i < (KV_INSTR + NWA - 1) / NWA; ++i) {
-    const int k = wv + NWA * i;
-    if (k < KV_INSTR) {
-      const int cl = 64 * k + lane;
-      const int row = cl / (CHUNKS + 1);
-      const int chunk = cl - (CHUNKS + 1) * row;
-      const uint32_t grow = (lds_ld(&sh.brow[n * 16 + (row >> 2)]) & ROW_BITS) + (row & 3);
-      const uint8_t* src = a.k + (uint64_t)grow * a.k_stride + (chunk < CHUNKS ? chunk : 0) * 16;
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                       (void __attribute__((address_space(3)))*)(buf + 1024 * k), 16, 0, 0);
-    }
-  }
+  for (int c = 0; c < KV_LOADS; ++c) load_column(src, buf, c);
 }
 
-// Waits until at most `pending` (0, 9 or 10) of this wave's global loads are
+// Waits until at most `pending` (0 or 18) of this wave's global loads are
 // outstanding.  The vmcnt field of the s_waitcnt immediate is bits 0..3 and 14..15;
 // expcnt (bits 4..6) and lgkmcnt (bits 8..11) stay at their maxima (no wait).
 __device__ __forceinline__ void wait_loads(int pending) {
   constexpr int NOWAIT = (0x7 << 4) | (0xF << 8);
-  if (pending >= 10) __builtin_amdgcn_s_waitcnt(10 | NOWAIT);
-  else if (pending == 9) __builtin_amdgcn_s_waitcnt(9 | NOWAIT);
+  if (pending >= KV_LOADS) __builtin_amdgcn_s_waitcnt(KV_LOADS | NOWAIT);
   else __builtin_amdgcn_s_waitcnt(NOWAIT);
+}
+
+// byte offset in a sub-tile buffer of 16-byte chunk `ch` (0..71) of row `t`
+__device__ __forceinline__ int kv_off(int t, int ch) {
+  return (ch >> 2) * COLB + t * 64 + 16 * ((ch & 3) ^ ((t >> 2) & 3));
 }
 
 __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
   __shared__ AttnShared sh;
-  __shared__ AttnKV kvs;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int l16 = lane & 15, q4 = lane >> 4;
-  const int lr = lane & 31, lh = lane >> 5;
-  const int tb = wv & 1, hg = wv >> 1;           // S^T tile: tokens 32tb .. +31, heads 16hg .. +15
-  const int g = blockIdx.x;
-  if (g >= a.n_rows * a.n_split) return;
-  const int split = g % a.n_split;
-  const int rl = g / a.n_split;
+  __shared__ __align__(16) uint8_t kv0[KVBUF];
+  __shared__ __align__(16) uint8_t kv1[KVBUF];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int hb = wv & 1, th = wv >> 1;           // S^T tile: heads 32hb .., tokens 32th ..
+  const int bid = blockIdx.x;
+  if (bid >= a.n_rows * a.n_split) return;
+  const int split = bid % a.n_split;
+  const int rl = bid / a.n_split;
   const int r = a.row0 + rl;
   const RowCtx c = row_ctx(a, r);
   const int sb0 = split * a.blocks_per_split;
   const int send = min(a.top_k, sb0 + a.blocks_per_split);
   const int nsub = (send - sb0 + 15) >> 4;
-  const int hq = 16 * hg + l16;                  // head of this lane in the S^T layout
+  const int hs = 32 * hb + l32;                  // head of this lane in the S^T layout
 
-  // q fragments of head hq: dims 32s + 8q4 .. +8 for k-step s
-  bf16x8_t qf[QSTEPS];
+  // prologue loads, in this order: selection ids, q fragments (head hs, dims
+  // 16s + 8lh .. +8 for k-step s), then the first sub-tiles; building the block
+  // table waits only for the ids, and the q fragments land while the first
+  // sub-tile is fetched
+  const BlockIds ids = fetch_blocks(c, sb0, send);
+  bf16x8_t qf[KSTEPS];
   {
-    const u32x4_t* qs = (const u32x4_t*)((const uint16_t*)a.q + ((int64_t)r * LAT_H + hq) * LAT_DK + 8 * q4);
+    const u32x4_t* qs = (const u32x4_t*)((const uint16_t*)a.q + ((int64_t)r * LAT_H + hs) * LAT_DK + 8 * lh);
 #pragma unroll
-    for (int s = 0; s < QSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, qs[4 * s]);
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, qs[2 * s]);
   }
   const float cs = a.scale * LOG2E;
 
-  f32x16_t o[2][2];                              // [32-head block][32-dim block of this wave]
+  // O^T tiles [32 dims, 32 heads]: o[i][db][k] = head 32i + l32, dim 128wv + 32db +
+  // 8(k/4) + 4lh + k%4
+  f32x16_t o[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) o[i][j] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int d = 0; d < 4; ++d) o[i][d] = f32x16_t{};
+  // reference maxima: ms for head hs (S^T layout), mo[i] for head 32i + l32 (O layout)
+  float ms = -INFINITY, mo[2] = {-INFINITY, -INFINITY};
+  float l_half = 0.f;                            // l of head hs over this wave's token half
 
-  build_block_table(a, c, sb0, send, sh);
-  // the q fragments (issued first) are in registers before the sub-tile loads
-  // start, so the loop never waits on them behind the latent loads
-  wait_loads(0);
+  build_block_table(a, c, ids, sb0, send, sh);
+  if (threadIdx.x < 4) lds_st(&sh.need[threadIdx.x], 0);
   block_sync_lds();
-  if (nsub > 0) load_subtile(a, sh, 0, kvs.kv[0]);
+  if (nsub > 0) load_subtile(a, sh, 0, kv0);
   if (nsub > 1) {
-    load_subtile(a, sh, 1, kvs.kv[1]);
-    wait_loads(subtile_loads(wv));               // sub-tile 0 landed (this wave's part)
+    load_subtile(a, sh, 1, kv1);
+    wait_loads(KV_LOADS);                        // q and sub-tile 0 landed (this wave's part)
   } else {
     wait_loads(0);
   }
+  // q only feeds MFMA B operands, which may sit in accumulation registers: keep it
+  // there, leaving the ordinary VGPRs to the O accumulators
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+a"(qf[s]));
   block_sync_lds();
 
-  // transposed V reads: in 16-lane group G, source lane s points at token
-  // 8*(G>>1) + s/4 (+4 for the second read) and dims 16*(G&1) + 4*(s%4) of the
-  // 32-dim block, so lane l receives V[8*lh + j][32-dim block + lr], j = 0..3 (4..7)
-  const int vtok = 8 * (q4 >> 1) + (l16 >> 2), vdim = 16 * (q4 & 1) + 4 * (l16 & 3);
-
-  for (int n = 0; n < nsub; ++n) {
-    const uint8_t* buf = kvs.kv[n & 1];
-    // ---- S^T[token, head]: lane holds head hq and tokens 32tb + 16u + 4q4 + i
-    //      (block 8tb + 4u + q4 of the sub-tile, offset i)
-    f32x4v sacc[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      sacc[u] = f32x4v{0.f, 0.f, 0.f, 0.f};
-      const uint8_t* kr = buf + (32 * tb + 16 * u + l16) * ROWB + q4 * 16;
-#pragma unroll
-      for (int s = 0; s < QSTEPS; ++s) {
-        const bf16x8_t kf = *(const bf16x8_t*)(kr + s * 64);
-        sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sacc[u], 0, 0, 0);
-      }
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int vis = (int)(lds_ld(&sh.brow[n * 16 + 8 * tb + 4 * u + q4]) >> VIS_SHIFT);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sacc[u][i] = i < vis ? sacc[u][i] * cs : -INFINITY;
-        mloc = fmaxf(mloc, sacc[u][i]);
-      }
-    }
-    mloc = quad_max16(mloc);                     // over the 4 lanes of head hq
-    if (q4 == 0) lds_st(&sh.m_part[tb][hq], mloc);
-    block_sync_lds();
-    const float m_new = fmaxf(m_run, fmaxf(lds_ld(&sh.m_part[0][hq]), lds_ld(&sh.m_part[1][hq])));
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    m_run = m_new;
-    float lsum = 0.f;
+  // one sub-tile: compute on `buf`, while sub-tile n+1 streams into `nxt`
+  auto step = [&](const int n, const uint8_t* buf, uint8_t* nxt) {
+    // sub-tile n+1 is in flight since the previous step (or the prologue); `nxt`
+    // was last read in step n-1, which every wave has left.  Sub-tile n+1 is
+    // fetched one column per two k-steps of the S^T product below: each DMA
+    // instruction takes long to issue, and between MFMAs that time is hidden.
+    const bool fetch = n >= 1 && n + 1 < nsub;
+    const uint8_t* fsrc = fetch ? subtile_src(a, sh, n + 1) : nullptr;
+    // ---- S^T[token, head]: lane holds head hs, tokens 32th + 8q + 4lh + u (q, u < 4)
+    //      Two accumulation chains (even and odd k-steps) keep back-to-back MFMAs
+    //      independent; K fragments are read KPF k-steps ahead.
+    f32x16_t sacc;
     {
-      uint8_t* pr = sh.p + hq * PROW + (32 * tb + 4 * q4) * 2;
+      f32x16_t sa[2] = {f32x16_t{}, f32x16_t{}};
+      const int t = 32 * th + l32;
+      constexpr int KPF = 4;
+      bf16x8_t kb[KPF];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int p = 0; p < KPF; ++p) kb[p] = *(const bf16x8_t*)(buf + kv_off(t, 2 * p + lh));
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        sa[s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[s % KPF], qf[s], sa[s & 1], 0, 0, 0);
+        if (s + KPF < KSTEPS) kb[s % KPF] = *(const bf16x8_t*)(buf + kv_off(t, 2 * (s + KPF) + lh));
+        if ((s & 1) && fetch) load_column(fsrc, nxt, s >> 1);
+      }
+      sacc = sa[0] + sa[1];
+    }
+    // ---- masking, scale, this half's tile maximum of head hs
+    float tm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int vis = (int)(lds_ld(&sh.brow[n * 16 + 8 * th + 2 * q + lh]) >> VIS_SHIFT);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sacc[4 * q + u] = u < vis ? sacc[4 * q + u] * cs : -INFINITY;
+        tm = fmaxf(tm, sacc[4 * q + u]);
+      }
+    }
+    tm = pair_max32(tm);
+    if (lh == 0) lds_st(&sh.tmax[th][hs], tm);
+    const bool need = __ballot(tm > ms + RESCALE_LOG2) != 0ull;
+    if (need && lane == 0) lds_st(&sh.need[wv], 1);
+    // P against the current reference (recomputed below in the rare case)
+    auto write_p = [&](float m) {
+      const float mu = m == -INFINITY ? 0.f : m;
+      float ls = 0.f;
+      uint8_t* pr = sh.p + hs * PROW + (32 * th + 4 * lh) * 2;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
         float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { pv[i] = exp2f(sacc[u][i] - m_use); lsum += pv[i]; }
-        lds_st((uint2*)(pr + 32 * u), make_uint2((uint32_t)f32_to_bf16(pv[0]) | ((uint32_t)f32_to_bf16(pv[1]) << 16),
-                                                 (uint32_t)f32_to_bf16(pv[2]) | ((uint32_t)f32_to_bf16(pv[3]) << 16)));
+        for (int u = 0; u < 4; ++u) { pv[u] = exp2f(sacc[4 * q + u] - mu); ls += pv[u]; }
+        lds_st((uint2*)(pr + 16 * q), make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])));
       }
-    }
-    lsum = quad_sum16(lsum);
-    if (q4 == 0) {
-      lds_st(&sh.l_part[tb][hq], lsum);
-      if (tb == 0) lds_st(&sh.alpha[hq], alpha);
-    }
+      return ls;
+    };
+    float ls = write_p(ms);
     block_sync_lds();
-    l_run = alpha * l_run + lds_ld(&sh.l_part[0][hq]) + lds_ld(&sh.l_part[1][hq]);
-
-    // ---- O[head, dim] for dims 64wv .. +63: lane holds dim 64wv + 32j + lr and
-    //      heads 32i + 8q + 4lh + u; rescale by the heads' alpha, then += P . V
+    // ---- rare: some head maximum passed its reference by more than 2^8.  Every
+    //      wave moves the references to the new maxima, rescales what it holds,
+    //      and P is rewritten.
+    bool moved = false;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int w = 0; w < 4; ++w) moved |= lds_ld(&sh.need[w]) != 0;
+    if (moved) {
+      const float msn = fmaxf(ms, fmaxf(lds_ld(&sh.tmax[0][hs]), lds_ld(&sh.tmax[1][hs])));
+      l_half *= ms == -INFINITY ? 0.f : exp2f(ms - msn);
+      ms = msn;
+      ls = write_p(ms);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4v al = lds_ld((const f32x4v*)&sh.alpha[32 * i + 8 * q + 4 * lh]);
+      for (int i = 0; i < 2; ++i) {
+        const int h = 32 * i + l32;
+        const float mon = fmaxf(mo[i], fmaxf(lds_ld(&sh.tmax[0][h]), lds_ld(&sh.tmax[1][h])));
+        const float al = mo[i] == -INFINITY ? 0.f : exp2f(mo[i] - mon);
+        mo[i] = mon;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) o[i][j][4 * q + u] *= al[u];
+        for (int d = 0; d < 4; ++d) o[i][d] *= al;
       }
+      block_sync_lds();                          // new P complete; flags read by all
+      if (threadIdx.x < 4) lds_st(&sh.need[threadIdx.x], 0);
+    }
+    l_half += pair_sum32(ls);
+    // ---- O^T += V^T . P^T: dims 128wv + 32db, heads 32i, tokens 16ks .. +15
+    {
+      typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+      // transposed V reads: in 16-lane group G, source lane s points at token
+      // 16ks + 8(G>>1) + s/4 (+4 for the second read) and dims 16(G&1) + 4(s%4) of
+      // the 32-dim block, so lane l receives dim l32 of tokens 16ks + 8lh + j
+      const int g4 = lane >> 4, s16 = lane & 15;
+      const int vt = 8 * (g4 >> 1) + (s16 >> 2);
+      const int vd = 16 * (g4 & 1) + 4 * (s16 & 3);           // dim within the 32-dim block
+      const int vch = vd >> 3, vin = (vd & 7) * 2;             // chunk of the block, byte in chunk
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t pa[2];
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8_t pb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) pa[i] = lds_ld((const bf16x8_t*)(sh.p + (32 * i + lr) * PROW + (16 * ks + 8 * lh) * 2));
-      const uint8_t* vr = buf + (16 * ks + vtok) * ROWB + (64 * wv + vdim) * 2;
+        for (int i = 0; i < 2; ++i) pb[i] = lds_ld((const bf16x8_t*)(sh.p + (32 * i + l32) * PROW + (16 * ks + 8 * lh) * 2));
+        // ks-step operands: 2 P reads and 8 V reads for 8 MFMAs
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr + j * 64));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr + 4 * ROWB + j * 64));
-        const s16x4_t v8[2] = {lo, hi};
-        const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, v8);
+        for (int db = 0; db < 4; ++db) {
+          const int ch = 4 * (4 * wv + db) + vch;             // chunk of the row: dims 128wv + 32db + vd
+          const int t0 = 16 * ks + vt;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + kv_off(t0, ch) + vin));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + kv_off(t0 + 4, ch) + vin));
+          const s16x4_t v8[2] = {lo, hi};
+          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, v8);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) o[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i], vb, o[i][j], 0, 0, 0);
+          for (int i = 0; i < 2; ++i) o[i][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[i], o[i][db], 0, 0, 0);
+        }
       }
     }
-    // ---- every wave is done with buffer n&1 past this barrier: fetch sub-tile n+2
-    //      into it, then make sure sub-tile n+1 (fetched an iteration ago) landed
-    block_sync_lds();
+    // ---- sub-tile n+1 has landed for every wave, and every wave is done with
+    //      `buf` and with P, past this barrier
     if (n + 1 < nsub) {
-      if (n + 2 < nsub) {
-        load_subtile(a, sh, n + 2, kvs.kv[n & 1]);
-        wait_loads(subtile_loads(wv));
-      } else {
-        wait_loads(0);
-      }
+      wait_loads(0);
       block_sync_lds();
     }
+  };
+  for (int n = 0; n < nsub; n += 2) {
+    step(n, kv0, kv1);
+    if (n + 1 < nsub) step(n + 1, kv1, kv0);
   }
 
-  // ---- epilogue: per-head l to the O layout
-  if (tb == 0 && q4 == 0) lds_st(&sh.lfin[hq], l_run);
+  // ---- epilogue: l of each head = sum of its two token halves
+  if (lh == 0) lds_st(&sh.lpart[th][hs], l_half);
+  block_sync_lds();
   if (a.n_split == 1) {
-    if (tb == 0 && q4 == 0 && a.lse) a.lse[(int64_t)r * LAT_H + hq] = (m_run + log2f(l_run)) * LN2;
-    block_sync_lds();
-    uint16_t* out = (uint16_t*)a.out + (int64_t)r * LAT_H * LAT_DV + 64 * wv + lr;
+    if (th == 0 && lh == 0 && a.lse) {
+      const float lt = lds_ld(&sh.lpart[0][hs]) + lds_ld(&sh.lpart[1][hs]);
+      a.lse[(int64_t)r * LAT_H + hs] = ((ms == -INFINITY ? 0.f : ms) + log2f(lt)) * LN2;
+    }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+      const int h = 32 * i + l32;
+      const float inv = 1.f / (lds_ld(&sh.lpart[0][h]) + lds_ld(&sh.lpart[1][h]));
+      uint16_t* out = (uint16_t*)a.out + ((int64_t)r * LAT_H + h) * LAT_DV + 128 * wv + 4 * lh;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4v lf = lds_ld((const f32x4v*)&sh.lfin[32 * i + 8 * q + 4 * lh]);
+      for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int h = 32 * i + 8 * q + 4 * lh + u;
-          const float inv = 1.f / lf[u];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) out[h * LAT_DV + 32 * j] = f32_to_bf16(o[i][j][4 * q + u] * inv);
-        }
-      }
+        for (int q = 0; q < 4; ++q)
+          *(uint2*)(out + 32 * d + 8 * q) = make_uint2(pack_bf16x2(o[i][d][4 * q] * inv, o[i][d][4 * q + 1] * inv),
+                                                       pack_bf16x2(o[i][d][4 * q + 2] * inv, o[i][d][4 * q + 3] * inv));
+    }
   } else {
     const int64_t pi = (int64_t)rl * a.n_split + split;
-    float* po = a.part_o + pi * LAT_H * LAT_DV + 64 * wv + lr;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+      const int h = 32 * i + l32;
+      float* po = a.part_o + (pi * LAT_H + h) * LAT_DV + 128 * wv + 4 * lh;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int h = 32 * i + 8 * q + 4 * lh + u;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) po[h * LAT_DV + 32 * j] = o[i][j][4 * q + u];
-        }
-    if (tb == 0 && q4 == 0) {
-      a.part_ml[(pi * LAT_H + hq) * 2] = m_run;
-      a.part_ml[(pi * LAT_H + hq) * 2 + 1] = l_run;
+        for (int q = 0; q < 4; ++q)
+          *(f32x4v*)(po + 32 * d + 8 * q) = f32x4v{o[i][d][4 * q], o[i][d][4 * q + 1], o[i][d][4 * q + 2], o[i][d][4 * q + 3]};
+    }
+    if (th == 0 && lh == 0) {
+      a.part_ml[(pi * LAT_H + hs) * 2] = ms == -INFINITY ? 0.f : ms;
+      a.part_ml[(pi * LAT_H + hs) * 2 + 1] = lds_ld(&sh.lpart[0][hs]) + lds_ld(&sh.lpart[1][hs]);
     }
   }
 }
@@ -390,9 +473,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   }
   const float inv = 1.f / L;
   uint16_t* out = (uint16_t*)a.out + ((int64_t)r * LAT_H + head) * LAT_DV + t * 4;
-  const uint32_t lo = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
-  const uint32_t hi = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
-  *(uint2*)out = make_uint2(lo, hi);
+  *(uint2*)out = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
   if (a.lse && t == 0) a.lse[(int64_t)r * LAT_H + head] = (m + log2f(L)) * LN2;
 }
 

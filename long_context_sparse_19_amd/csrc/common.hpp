@@ -48,6 +48,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// two floats -> packed bf16 pair (lo in the low half), round to nearest even, by
+// gfx950's v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // ---------------------------------------------------------------- fp8 e4m3fn
 // Four codes (one dword, byte 0 first) -> four floats, by the hardware converter
 // (gfx950 decodes the OCP e4m3fn format: bias 7, max 448).
