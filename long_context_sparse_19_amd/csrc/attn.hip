@@ -32,9 +32,9 @@ constexpr int NT = 256;                        // f32 path
 constexpr int NTA = 256;                       // bf16 path: 4 waves
 constexpr int NWA = NTA / 64;
 constexpr int SUBT = 64;                       // tokens per sub-tile (16 blocks)
-constexpr int COLB = SUBT * 64;                // one 64-byte column (32 dims) of all 64 rows
-constexpr int NCOL = LAT_DK * 2 / 64;          // 18 columns per latent row
-constexpr int KVBUF = NCOL * COLB;             // 73728 bytes
+constexpr int SEGB = SUBT * 128;               // one 128-byte segment (64 dims) of all 64 rows
+constexpr int NSEG = LAT_DK * 2 / 128;         // 9 segments per latent row
+constexpr int KVBUF = NSEG * SEGB;             // 73728 bytes
 constexpr int CHUNKS = LAT_DK * 2 / 16;        // 72 16-byte chunks per latent row
 constexpr int KSTEPS = LAT_DK / 16;            // 36 MFMA k-steps over the 576 dims
 constexpr float LN2 = 0.69314718055994531f;
@@ -153,38 +153,58 @@ __device__ __forceinline__ void build_block_table(const AttnArgs& a, const RowCt
   }
 }
 
-// Sub-tile layout in LDS: 18 columns of 4 KB, column c holding bytes 64c .. 64c+63
-// (dims 32c .. 32c+31) of all 64 rows, row t at 64t, with the four 16-byte chunks of
-// each 64-byte segment stored in slots chunk ^ ((t >> 2) & 3).  The swizzle spreads
-// the same chunk of 16 consecutive rows (a K fragment read) over all 64 banks; the
-// 4-row groups of the transposing V reads share one swizzle and stay conflict-free.
+// Sub-tile layout in LDS: 9 segments of 8 KB, segment g holding bytes 128g ..
+// 128g+127 (dims 64g .. 64g+63) of all 64 rows, row t at 128t, with the eight
+// 16-byte chunks of each 128-byte piece stored in slots chunk ^ x(t),
+// x(t) = 2(t % 4) + (t / 4) % 2.  Within 8 consecutive rows x takes all 8 values,
+// so a K fragment read (the same chunk of 8 rows per LDS cycle) hits every bank
+// once; within 4 consecutive rows x keeps the chunk pairs (2i, 2i+1) of the
+// transposing V reads apart.
 //
 // Sub-tile n goes straight from global memory into that layout with
 // global_load_lds_dwordx4 (lane l of one instruction fills bytes 16l .. 16l+15 of a
-// 1 KB span): instruction (c, g) fills rows 16g .. 16g+15 of column c, lane l taking
-// bytes 16(l%4) of the column from row 16g + l/4.  Wave w issues the 9 instructions
-// g = w and c = 0 .. 17, so each lane reads one row per sub-tile.
-constexpr int KV_LOADS = NCOL * 4 / NWA;       // 18 per wave
+// 1 KB span): instruction (g, q) fills rows 8q .. 8q+7 of segment g, lane l taking
+// slot l%8 of row 8q + l/8, i.e. chunk (l%8) ^ x of that row.  Each instruction
+// touches 8 whole 128-byte lines.  Wave w issues the 18 instructions q = 2w, 2w+1
+// and g = 0 .. 8, so each lane reads two rows per sub-tile.
+constexpr int KV_LOADS = NSEG * 8 / NWA;       // 18 per wave
 
-// This lane's source row segment for sub-tile n (see above); column c then comes
-// from src + 64c and goes to buf + wv*1024 + c*COLB.
-__device__ __forceinline__ const uint8_t* subtile_src(const AttnArgs& a, const AttnShared& sh, int n) {
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row = 16 * wv + (lane >> 2);
-  const uint32_t grow = (lds_ld(&sh.brow[n * 16 + (row >> 2)]) & ROW_BITS) + (row & 3);
-  // 16-byte slot j of a row's 64-byte segment holds chunk j ^ ((row >> 2) & 3)
-  return a.k + (uint64_t)grow * a.k_stride + 16 * ((lane & 3) ^ ((row >> 2) & 3));
+__device__ __forceinline__ int kv_swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+// byte offset in a sub-tile buffer of 16-byte chunk `ch` (0..71) of row `t`
+__device__ __forceinline__ int kv_off(int t, int ch) {
+  return (ch >> 3) * SEGB + t * 128 + 16 * ((ch & 7) ^ kv_swz(t));
 }
 
-__device__ __forceinline__ void load_column(const uint8_t* src, uint8_t* buf, int c) {
+// This lane's two source rows for sub-tile n; load k (0..17) is segment k/2 of
+// row half k%2.
+struct SubtileSrc {
+  const uint8_t* row[2];
+};
+
+__device__ __forceinline__ SubtileSrc subtile_src(const AttnArgs& a, const AttnShared& sh, int n) {
+  const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src + 64 * c),
-                                   (void __attribute__((address_space(3)))*)(buf + wv * 1024 + c * COLB), 16, 0, 0);
+  SubtileSrc src;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = 8 * (2 * wv + h) + (lane >> 3);
+    const uint32_t grow = (lds_ld(&sh.brow[n * 16 + (t >> 2)]) & ROW_BITS) + (t & 3);
+    src.row[h] = a.k + (uint64_t)grow * a.k_stride + 16 * ((lane & 7) ^ kv_swz(t));
+  }
+  return src;
+}
+
+__device__ __forceinline__ void load_column(const SubtileSrc& src, uint8_t* buf, int k) {
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = k >> 1, h = k & 1;
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src.row[h] + 128 * g),
+                                   (void __attribute__((address_space(3)))*)(buf + g * SEGB + (2 * wv + h) * 1024),
+                                   16, 0, 0);
 }
 
 __device__ __forceinline__ void load_subtile(const AttnArgs& a, const AttnShared& sh, int n, uint8_t* buf) {
-  const uint8_t* src = subtile_src(a, sh, n);
+  const SubtileSrc src = subtile_src(a, sh, n);
 #pragma unroll
   for (int c = 0; c < KV_LOADS; ++c) load_column(src, buf, c);
 }
@@ -196,11 +216,6 @@ __device__ __forceinline__ void wait_loads(int pending) {
   constexpr int NOWAIT = (0x7 << 4) | (0xF << 8);
   if (pending >= KV_LOADS) __builtin_amdgcn_s_waitcnt(KV_LOADS | NOWAIT);
   else __builtin_amdgcn_s_waitcnt(NOWAIT);
-}
-
-// byte offset in a sub-tile buffer of 16-byte chunk `ch` (0..71) of row `t`
-__device__ __forceinline__ int kv_off(int t, int ch) {
-  return (ch >> 2) * COLB + t * 64 + 16 * ((ch & 3) ^ ((t >> 2) & 3));
 }
 
 __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
@@ -269,7 +284,10 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
     // fetched one column per two k-steps of the S^T product below: each DMA
     // instruction takes long to issue, and between MFMAs that time is hidden.
     const bool fetch = n >= 1 && n + 1 < nsub;
-    const uint8_t* fsrc = fetch ? subtile_src(a, sh, n + 1) : nullptr;
+    const SubtileSrc fsrc = subtile_src(a, sh, fetch ? n + 1 : n);
+    // visible-token counts of this wave's 8 blocks, read before any fetch is in flight
+    const u32x4_t bv0 = lds_ld((const u32x4_t*)&sh.brow[n * 16 + 8 * th]);
+    const u32x4_t bv1 = lds_ld((const u32x4_t*)&sh.brow[n * 16 + 8 * th + 4]);
     // ---- S^T[token, head]: lane holds head hs, tokens 32th + 8q + 4lh + u (q, u < 4)
     //      Two accumulation chains (even and odd k-steps) keep back-to-back MFMAs
     //      independent; K fragments are read KPF k-steps ahead.
@@ -293,7 +311,8 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
     float tm = -INFINITY;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int vis = (int)(lds_ld(&sh.brow[n * 16 + 8 * th + 2 * q + lh]) >> VIS_SHIFT);
+      const uint32_t e = q < 2 ? (lh ? bv0[2 * q + 1] : bv0[2 * q]) : (lh ? bv1[2 * q - 3] : bv1[2 * q - 4]);
+      const int vis = (int)(e >> VIS_SHIFT);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         sacc[4 * q + u] = u < vis ? sacc[4 * q + u] * cs : -INFINITY;
