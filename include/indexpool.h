@@ -190,8 +190,8 @@ const char* ip_last_error(void);
 /* Timing hook for benchmarks: the next launch (on this thread) of kernel `kernel_id`
  * goes through hipExtLaunchKernelGGL with `start` / `stop`, so the two events
  * receive that dispatch's own start and end times (the timestamps a kernel trace
- * reports).  kernel_id: 1 compress, 2 score, 3 top-k (per-chunk stage),
- * 4 attention, 5 split combine, 6 top-k merge.  Hooks for different ids may be
+ * reports).  kernel_id: 1 compress, 2 score, 3 top-k, 4 attention, 5 split
+ * combine.  Hooks for different ids may be
  * armed together; each is consumed by one launch.  Passing NULL for one event
  * only is IP_EINVAL; kernel_id 0 with both NULL disarms every hook.  Use it
  * outside stream capture.  Not needed for normal use. */

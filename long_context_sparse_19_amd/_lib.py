@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libindexpool.so")
 
 IP_OK, IP_EINVAL, IP_EUNSUPPORTED, IP_EWORKSPACE, IP_EDEVICE = range(5)
 IP_F32, IP_BF16, IP_FP8_E4M3FN = range(3)
-K_COMPRESS, K_SCORE, K_TOPK, K_ATTN, K_COMBINE, K_TOPK_MERGE = 1, 2, 3, 4, 5, 6
+K_COMPRESS, K_SCORE, K_TOPK, K_ATTN, K_COMBINE = 1, 2, 3, 4, 5
 
 _c_void_p = ctypes.c_void_p
 _i32 = ctypes.c_int32

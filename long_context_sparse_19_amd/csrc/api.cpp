@@ -86,7 +86,7 @@ struct ScorePlan {
   int chunk;           // scores per top-k chunk
   int n_chunks;        // top-k chunks per row
   int rows_per_chunk;  // query rows per pass
-  size_t score_bytes, cand_bytes, total;
+  size_t score_bytes, cand_bytes, count_bytes, total;
 };
 
 ScorePlan score_plan(const ip_seqs* s, int n_q, int top_k, bool scores_given) {
@@ -103,8 +103,9 @@ ScorePlan score_plan(const ip_seqs* s, int n_q, int top_k, bool scores_given) {
   }
   p.score_bytes = scores_given ? 0 : (size_t)p.rows_per_chunk * p.ld * 4;
   p.cand_bytes = p.n_chunks > 1 ? (size_t)p.rows_per_chunk * p.n_chunks * (size_t)(top_k - 1) * 8 : 0;
+  p.count_bytes = p.n_chunks > 1 ? (size_t)p.rows_per_chunk * 4 : 0;
   p.score_bytes = (p.score_bytes + 255) & ~size_t(255);
-  p.total = p.score_bytes + p.cand_bytes;
+  p.total = p.score_bytes + p.cand_bytes + p.count_bytes;
   return p;
 }
 
@@ -247,6 +248,7 @@ ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_se
   float* score_buf = scores ? scores : (float*)ws;
   uint32_t* cand_key = (uint32_t*)((char*)ws + plan.score_bytes);
   int32_t* cand_idx = (int32_t*)(cand_key + (plan.cand_bytes / 8));
+  int32_t* topk_count = plan.count_bytes ? (int32_t*)((char*)ws + plan.score_bytes + plan.cand_bytes) : nullptr;
 
   for (int row0 = 0; row0 < n_q; row0 += plan.rows_per_chunk) {
     const int nr = std::min(plan.rows_per_chunk, n_q - row0);
@@ -266,6 +268,7 @@ ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_se
     sa.heads = n_heads;
     sa.dim = head_dim;
     sa.max_blocks = plan.max_blocks;
+    sa.topk_count = topk_count;
     // the kernels index scores by (r - row0)
     ip_status st = device_status(fp8 ? ip::launch_score_fp8_bf16(sa, stream) : ip::launch_score_f32(sa, stream), fn);
     if (st) return st;
@@ -283,6 +286,7 @@ ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_se
     ta.cand_idx = cand_idx;
     ta.n_chunks = plan.n_chunks;
     ta.chunk = plan.chunk;
+    ta.count = topk_count;
     st = device_status(ip::launch_topk(ta, stream), fn);
     if (st) return st;
   }

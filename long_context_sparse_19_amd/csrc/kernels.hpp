@@ -8,7 +8,7 @@
 
 namespace ip {
 
-enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3, K_ATTN = 4, K_COMBINE = 5, K_TOPK_MERGE = 6, K_LAST = 6 };
+enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3, K_ATTN = 4, K_COMBINE = 5, K_LAST = 5 };
 
 // Takes (and disarms) the timing hook's events if one is armed for kernel `id`.
 bool hook_take(int id, hipEvent_t* start, hipEvent_t* stop);
@@ -58,6 +58,7 @@ struct ScoreArgs {
   int64_t ld;
   int heads, dim;
   int max_blocks;              // key range covered by the grid
+  int32_t* topk_count;         // [n_rows] or null: zeroed here for the top-k that follows
 };
 hipError_t launch_score_fp8_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s);
@@ -76,9 +77,10 @@ struct TopkArgs {
   int32_t* cand_idx;           // same
   int n_chunks;                // chunks per row covered by the grid
   int chunk;                   // scores per chunk (topk_chunk_size)
+  int32_t* count;              // [n_rows] chunks done per row, zero on entry (n_chunks > 1)
 };
 constexpr int TOPK_MAX_CHUNK = 16384;   // scores per chunk workgroup (512 threads x 32)
-constexpr int TOPK_MERGE_CAP = 16384;   // candidate slots per row in the merge (512 x 32)
+constexpr int TOPK_MERGE_CAP = 16384;   // candidate slots per row in the in-kernel merge (512 x 32)
 int topk_chunk_size(int max_blocks);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 

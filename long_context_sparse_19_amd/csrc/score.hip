@@ -36,6 +36,8 @@ __global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
   const int kc0 = blockIdx.x * KEYS_PER_WG;
   const int rbeg = a.row0 + blockIdx.y * RPW;
   const int rend = min(rbeg + RPW, a.row0 + a.n_rows);
+  if (a.topk_count && blockIdx.x == 0 && (int)threadIdx.x < rend - rbeg)
+    a.topk_count[rbeg + threadIdx.x - a.row0] = 0;
 
   bf16x8_t kf[TILES][8];
   float ksig[TILES];
@@ -123,6 +125,7 @@ __global__ __launch_bounds__(NT) void score_f32_kernel(ScoreArgs a) {
   const int p = a.q_pos ? a.q_pos[r] : a.L.seq_lens[b] - 1;
   const int nel = p >> 2;
   const int j = blockIdx.x * NT + threadIdx.x;
+  if (a.topk_count && blockIdx.x == 0 && threadIdx.x == 0) a.topk_count[blockIdx.y] = 0;
   if ((int)(blockIdx.x * NT) >= nel) return;
   const int HD = a.heads * a.dim;
   const float* q = (const float*)a.q + (int64_t)r * HD;

@@ -24,8 +24,9 @@
 //   4. Else raise T with a histogram of the scores >= T and repeat (T strictly
 //      increases, so this ends; typical rows never get here).
 // Rows longer than one chunk are split: every chunk keeps its own best
-// min(k'-1, chunk) and a merge launch selects among the concatenated winners,
-// which are already in ascending index order.
+// min(k'-1, chunk), and the last chunk workgroup of the row to finish (a per-row
+// counter, zeroed by the scoring kernel of the same call) selects among the
+// concatenated winners, which are already in ascending index order.
 #include "kernels.hpp"
 
 namespace ip {
@@ -36,17 +37,17 @@ constexpr int NT = 512;
 constexpr int NW = NT / 64;
 constexpr int NBINS = 2048;
 constexpr int BPT = NBINS / NT;          // histogram bins scanned per thread
-constexpr int CAND_CAP = 4096;           // candidates compacted into LDS
-constexpr int EC = CAND_CAP / NT;        // candidates per thread in the exact select
+constexpr int CAND_CAP = 8192;           // candidates compacted into LDS (>= top_k - 1)
+constexpr int EC = CAND_CAP / NT;        // candidates per thread in the exact select (at most)
 constexpr int BND_CAP = 64;              // boundary candidates ranked directly
 
 struct SelShared {
-  int hist[NBINS];
+  int hist[NBINS + 64];                  // + one spare bin per lane (never read)
   int xi[2][NW], xj[2][NW];              // per-wave exchange slots, two sets
   float xf[2][NW], xg[2][NW], xh[2][NW];
   int digit, above;
-  uint32_t ckey[CAND_CAP + 1];           // candidates; the last entry is a sink
-  int32_t cid[CAND_CAP + 1];
+  uint32_t ckey[CAND_CAP + 64];          // candidates, then the kept pairs; + one
+  int32_t cid[CAND_CAP + 64];            // spare entry per lane (never read)
   __attribute__((aligned(16))) uint32_t bkey[BND_CAP + 4];   // boundary candidates
 };
 
@@ -160,12 +161,15 @@ __device__ __forceinline__ Buckets make_buckets(float lo, float hi) {
   return bk;
 }
 
-// Exact select over the compacted candidates (sh.ckey / sh.cid [0..M)), all in
-// [lo, hi], 1 <= kk <= M: emit(rank, id, key) for the kk best, ties to the lower
-// candidate position.  Enters right after a barrier; its first exchange uses set 0.
-template <class Emit>
-__device__ void select_candidates(int M, int kk, float lo, float hi, SelShared& sh, Emit emit) {
+// Exact select over the compacted candidates (sh.ckey / sh.cid [0..M), key 0 =
+// empty slot), all in [lo, hi], 1 <= kk <= #non-empty: the kk best, ties to the
+// lower candidate position, are left in sh.ckey / sh.cid [0..kk) in candidate
+// order once the caller's next barrier has passed.  Enters right after a barrier;
+// its first exchange uses set 0.
+template <int EC>
+__device__ __forceinline__ void select_candidates_ec(int M, int kk, float lo, float hi, SelShared& sh) {
   const int cb = threadIdx.x * EC;
+  const int lane = threadIdx.x & 63;
   uint32_t key[EC];
   int32_t cid[EC];
 #pragma unroll
@@ -183,7 +187,7 @@ __device__ void select_candidates(int M, int kk, float lo, float hi, SelShared& 
 #pragma unroll
     for (int e = 0; e < EC; ++e) {
       bin[e] = key[e] ? bk(key_float(key[e])) : -1;
-      if (key[e]) atomicAdd(&sh.hist[bin[e]], 1);
+      atomicAdd(&sh.hist[key[e] ? bin[e] : NBINS + lane], 1);   // empty slots: this lane's spare bin
     }
     __syncthreads();
     find_bin(sh, kk, 0);
@@ -259,19 +263,34 @@ __device__ void select_candidates(int M, int kk, float lo, float hi, SelShared& 
   for (int e = 0; e < EC; ++e) ns += (sel >> e) & 1u;
   int tot, unused;
   int off = x_scan(ns, 0, sh, 0, &tot, &unused);
+  // every candidate was read before the barrier above, so the store is free;
+  // dropped ones go to this lane's spare entry (no branch, no shared address)
 #pragma unroll
-  for (int e = 0; e < EC; ++e)
-    if ((sel >> e) & 1u) emit(off++, cid[e], key[e]);
+  for (int e = 0; e < EC; ++e) {
+    const bool k = (sel >> e) & 1u;
+    const int at = k ? off : CAND_CAP + lane;
+    sh.ckey[at] = key[e];
+    sh.cid[at] = cid[e];
+    off += k;
+  }
 }
 
-// The kk best of v (NaN = empty), ties to the lower slot, 1 <= kk <= #values;
-// emit(rank, id[e], key) once per kept value, ranks in slot order.  Nothing is
-// loaded from memory at emit time: a load inside the per-element branches would
-// serialise one round trip per element.
-template <int E, class Emit>
-__device__ void select_top(const float (&v)[E], const int32_t (&id)[E], int kk, SelShared& sh, Emit emit) {
+// the exact select with 8 candidate slots per thread while they suffice (MAXM:
+// a bound on M known at compile time)
+template <int MAXM>
+__device__ __forceinline__ void select_candidates(int M, int kk, float lo, float hi, SelShared& sh) {
+  if (MAXM <= NT * 8 || M <= NT * 8) select_candidates_ec<8>(M, kk, lo, hi, sh);
+  else select_candidates_ec<EC>(M, kk, lo, hi, sh);
+}
+
+// The kk best of v (NaN = empty), ties to the lower slot, 1 <= kk <= #values:
+// their (order-preserving key, id) pairs are left in sh.ckey / sh.cid [0..kk) in
+// slot order once the caller's next barrier has passed.
+template <int E>
+__device__ __forceinline__ void select_top(const float (&v)[E], const int32_t (&id)[E], int kk, SelShared& sh) {
   constexpr int GS = E >= 8 ? 8 : E;          // scores per group maximum
   constexpr int NG = E / GS;
+  const int lane = threadIdx.x & 63;
   // zeroed before the first exchange's barrier; find_bin re-zeroes what it reads
   for (int i = threadIdx.x; i < NBINS; i += NT) sh.hist[i] = 0;
 
@@ -304,7 +323,7 @@ __device__ void select_top(const float (&v)[E], const int32_t (&id)[E], int kk, 
     const Buckets bk = make_buckets(glo, vhi);
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-      if (!__builtin_isnan(gm[g])) atomicAdd(&sh.hist[bk(gm[g])], 1);
+      atomicAdd(&sh.hist[__builtin_isnan(gm[g]) ? NBINS + lane : bk(gm[g])], 1);
     __syncthreads();
     find_bin(sh, kk, 1);
     const int B = sh.digit;
@@ -347,32 +366,36 @@ __device__ void select_top(const float (&v)[E], const int32_t (&id)[E], int kk, 
       }
       int off = x_scan(ns, 0, sh, par ^ 1, &tot, &unused);
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if ((smask >> e) & 1ull) emit(off++, id[e], float_key(v[e]));
+      for (int e = 0; e < E; ++e) {
+        const bool k = (smask >> e) & 1ull;
+        const int at = k ? off : CAND_CAP + lane;
+        sh.ckey[at] = float_key(v[e]);
+        sh.cid[at] = id[e];
+        off += k;
+      }
       return;
     }
     if (Q <= CAND_CAP) {
-      // 3. compact {v >= T} in slot order (non-candidates write the sink entry),
-      //    then the exact select on the candidates
+      // 3. compact {v >= T} in slot order (the others write this lane's spare
+      //    entry: no branch, no shared address), then the exact select on them
       int off = qoff;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const bool c = v[e] >= T;
-        const int at = c ? off : CAND_CAP;
+        const int at = c ? off : CAND_CAP + lane;
         sh.ckey[at] = float_key(v[e]);
         sh.cid[at] = id[e];
         off += c;
       }
       __syncthreads();
-      select_candidates(Q, kk, T, vhi, sh, emit);
+      select_candidates<E * NT>(Q, kk, T, vhi, sh);
       return;
     }
     // 4. raise T: histogram of {v >= T} over [T, vhi]; the new T stays <= the
     //    kk-th largest value and strictly increases
     const Buckets bk = make_buckets(T, vhi);
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (v[e] >= T) atomicAdd(&sh.hist[bk(v[e])], 1);
+    for (int e = 0; e < E; ++e) atomicAdd(&sh.hist[v[e] >= T ? bk(v[e]) : NBINS + lane], 1);
     __syncthreads();
     find_bin(sh, kk, par);
     const int B = sh.digit;
@@ -404,23 +427,102 @@ __device__ __forceinline__ RowInfo row_info(const TopkArgs& a, int r) {
   return ri;
 }
 
-// own block after the kept ids, then -1 padding
-__device__ __forceinline__ void write_tail(const TopkArgs& a, int r, const RowInfo& ri) {
+// The row's output from the staged pairs (sh.cid [0..kept), kept = need):
+// the kept ids, the own block, then -1 padding; coalesced.
+__device__ __forceinline__ void write_row(const TopkArgs& a, int r, const RowInfo& ri, const SelShared& sh) {
   int32_t* out = a.out + (int64_t)r * a.top_k;
-  for (int i = ri.need + threadIdx.x; i < a.top_k; i += NT) out[i] = (i == ri.need) ? ri.bq : -1;
+  for (int i = threadIdx.x; i < a.top_k; i += NT)
+    out[i] = i < ri.need ? sh.cid[i] : (i == ri.need ? ri.bq : -1);
 }
 
-template <int E>
+// Device-scope relaxed accesses: coherent across the dies' separate L2 caches.
+template <typename T>
+__device__ __forceinline__ void store_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T load_agent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Select the row's k'-1 among the winners of its chunks (nchunks * (top_k-1) slots,
+// unused slots hold key 0) and write the row.  When every slot fits the candidate
+// store they all go there as they are (slot order is ascending id order; zero keys
+// are skipped), and only the exact select runs.
+template <int EM>
+__device__ __forceinline__ void merge_row(const TopkArgs& a, int rl, int r, const RowInfo& ri, SelShared& sh) {
+  const int km1 = a.top_k - 1;
+  const int64_t base = (int64_t)rl * a.n_chunks * km1;
+  const int nslots = ri.nchunks * km1;
+  if (ri.need == 0) {        // top_k == 1: the own block only
+    write_row(a, r, ri, sh);
+    return;
+  }
+  if (nslots <= CAND_CAP) {
+    for (int i = threadIdx.x; i < NBINS; i += NT) sh.hist[i] = 0;
+    // all loads in flight at once: one round trip
+    uint32_t k[EC];
+    int32_t id[EC];
+#pragma unroll
+    for (int e = 0; e < EC; ++e) {
+      const int i = min((int)threadIdx.x + e * NT, nslots - 1);
+      k[e] = load_agent(a.cand_key + base + i);
+      id[e] = load_agent(a.cand_idx + base + i);
+    }
+    int nv = 0;
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EC; ++e) {
+      const int i = threadIdx.x + e * NT;
+      if (i < nslots) {
+        sh.ckey[i] = k[e];
+        sh.cid[i] = id[e];
+        if (k[e]) {
+          const float f = key_float(k[e]);
+          lo = fminf(lo, f);
+          hi = fmaxf(hi, f);
+          ++nv;
+        }
+      }
+    }
+    float unusedf;
+    x_stats(nv, lo, hi, INFINITY, sh, 1, &nv, &lo, &hi, &unusedf);
+    select_candidates<CAND_CAP>(nslots, ri.need, lo, hi, sh);
+  } else {
+    const int s0 = threadIdx.x * EM;
+    float v[EM];
+    int32_t id[EM];
+    {
+      uint32_t k[EM];
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+        const int64_t at = base + min(s0 + e, nslots - 1);
+        k[e] = load_agent(a.cand_key + at);
+        id[e] = load_agent(a.cand_idx + at);
+      }
+#pragma unroll
+      for (int e = 0; e < EM; ++e) v[e] = (s0 + e < nslots && k[e] != 0u) ? key_float(k[e]) : __builtin_nanf("");
+    }
+    select_top<EM>(v, id, ri.need, sh);
+  }
+  __syncthreads();
+  write_row(a, r, ri, sh);
+}
+
+// E scores per thread; EM > 0: rows may span several chunks, merged in-kernel by
+// the row's last chunk workgroup (EM candidate slots per thread where the winners
+// overflow the candidate store).  EM == 0: one chunk per row.
+template <int E, int EM>
 __global__ __launch_bounds__(NT) void topk_chunk_kernel(TopkArgs a) {
   __shared__ SelShared sh;
+  __shared__ int merge_here;
   const int rl = blockIdx.y, r = a.row0 + rl, c = blockIdx.x;
   const RowInfo ri = row_info(a, r);
   if (c >= ri.nchunks) return;
   const int c0 = c * a.chunk;
   const int clen = max(0, min(a.chunk, ri.nel - c0));
   const int kk = min(ri.need, clen);
-  const bool final_out = ri.nchunks == 1;
-  int32_t* out = a.out + (int64_t)r * a.top_k;
+  const bool final_out = EM == 0 || ri.nchunks == 1;
   const int km1 = a.top_k - 1;
   const int64_t cbase = ((int64_t)rl * a.n_chunks + c) * km1;
   const float* src = a.scores + (int64_t)rl * a.ld + c0;
@@ -447,99 +549,80 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(TopkArgs a) {
     int32_t id[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) id[e] = c0 + s0 + e;
-    // ranks are < kk by construction; the guard keeps a logic error from ever
-    // writing outside this row's output
-    if (final_out) {
-      select_top<E>(v, id, kk, sh, [&](int pos, int32_t i, uint32_t) {
-        if (pos < kk) out[pos] = i;
-      });
-    } else {
-      select_top<E>(v, id, kk, sh, [&](int pos, int32_t i, uint32_t key) {
-        if (pos < kk) {
-          a.cand_key[cbase + pos] = key;
-          a.cand_idx[cbase + pos] = i;
-        }
-      });
-    }
+    select_top<E>(v, id, kk, sh);
   }
-  if (final_out) {
-    write_tail(a, r, ri);
-  } else {
-    for (int i = kk + threadIdx.x; i < km1; i += NT) a.cand_key[cbase + i] = 0u;   // unused slots
+  __syncthreads();
+  if (final_out) {           // kk == need here
+    write_row(a, r, ri, sh);
+    return;
+  }
+  if constexpr (EM > 0) {
+    // this chunk's winners, then key 0 in the unused slots; coalesced
+    for (int i = threadIdx.x; i < km1; i += NT) {
+      store_agent(a.cand_key + cbase + i, i < kk ? sh.ckey[i] : 0u);
+      store_agent(a.cand_idx + cbase + i, i < kk ? sh.cid[i] : 0);
+    }
+    // Count this chunk in once its winners are stored; the workgroup that completes
+    // the count merges.  The winners go through device-coherent stores and loads
+    // (write-through past this die's L2, re-read past the reader's), so no
+    // whole-cache write-back or invalidate (a device-scope fence) is needed: only
+    // that every store has completed before the count moves.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (threadIdx.x == 0) merge_here = atomicAdd(&a.count[rl], 1) == ri.nchunks - 1;
+    __syncthreads();
+    if (!merge_here) return;
+    merge_row<EM>(a, rl, r, ri, sh);
   }
 }
 
-template <int E>
-__global__ __launch_bounds__(NT) void topk_merge_kernel(TopkArgs a) {
-  __shared__ SelShared sh;
-  const int rl = blockIdx.x, r = a.row0 + rl;
-  const RowInfo ri = row_info(a, r);
-  if (ri.nchunks <= 1) return;
-  const int km1 = a.top_k - 1;
-  const int64_t base = (int64_t)rl * a.n_chunks * km1;
-  const int nslots = ri.nchunks * km1;
-  const int s0 = threadIdx.x * E;
-  float v[E];
-  int32_t id[E];
-  {
-    uint32_t k[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int64_t at = base + min(s0 + e, nslots - 1);
-      k[e] = a.cand_key[at];
-      id[e] = a.cand_idx[at];
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = (s0 + e < nslots && k[e] != 0u) ? key_float(k[e]) : __builtin_nanf("");
-  }
-  int32_t* out = a.out + (int64_t)r * a.top_k;
-  if (ri.need > 0)
-    select_top<E>(v, id, ri.need, sh, [&](int pos, int32_t i, uint32_t) {
-      if (pos < ri.need) out[pos] = i;
-    });
-  write_tail(a, r, ri);
-}
-
-template <int E>
+template <int E, int EM>
 void launch_chunks(const TopkArgs& a, hipStream_t s) {
-  launch(K_TOPK, topk_chunk_kernel<E>, dim3(a.n_chunks, a.n_rows), dim3(NT), s, a);
-}
-
-template <int E>
-void launch_merge(const TopkArgs& a, hipStream_t s) {
-  launch(K_TOPK_MERGE, topk_merge_kernel<E>, dim3(a.n_rows), dim3(NT), s, a);
+  launch(K_TOPK, topk_chunk_kernel<E, EM>, dim3(a.n_chunks, a.n_rows), dim3(NT), s, a);
 }
 
 int per_thread(int n) {
-  const int e = (n + NT - 1) / NT;
-  return e <= 1 ? 1 : e <= 2 ? 2 : e <= 4 ? 4 : e <= 8 ? 8 : e <= 16 ? 16 : 32;
+  int e = 1;
+  while (e < 32 && e * NT < n) e *= 2;
+  return e;
 }
 
 }  // namespace
 
+// Scores per chunk workgroup for rows of up to max_blocks eligible blocks: one
+// chunk of 512 x E (E a power of two up to 32, else 36, 40 or 48) while a row
+// fits 48 per thread; beyond that 8192-score chunks (at most 8 per row, so their
+// winners fit the candidate store of the merge), then 16384-score chunks.
 int topk_chunk_size(int max_blocks) {
-  return NT * per_thread(std::min(max_blocks, TOPK_MAX_CHUNK));
+  if (max_blocks <= TOPK_MAX_CHUNK) return NT * per_thread(max_blocks);
+  for (int e : {36, 40, 48})
+    if (max_blocks <= NT * e) return NT * e;
+  return max_blocks <= 8 * 8192 ? 8192 : TOPK_MAX_CHUNK;
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  switch (a.chunk / NT) {
-    case 1: launch_chunks<1>(a, s); break;
-    case 2: launch_chunks<2>(a, s); break;
-    case 4: launch_chunks<4>(a, s); break;
-    case 8: launch_chunks<8>(a, s); break;
-    case 16: launch_chunks<16>(a, s); break;
-    default: launch_chunks<32>(a, s); break;
-  }
   if (a.n_chunks > 1) {
-    switch (per_thread(a.n_chunks * (a.top_k - 1))) {
-      case 1: launch_merge<1>(a, s); break;
-      case 2: launch_merge<2>(a, s); break;
-      case 4: launch_merge<4>(a, s); break;
-      case 8: launch_merge<8>(a, s); break;
-      case 16: launch_merge<16>(a, s); break;
-      default: launch_merge<32>(a, s); break;
-    }
+    // rows of several chunks: 8192- or 16384-score chunks.  Winners that fit the
+    // candidate store (8192 slots) are merged directly; more (up to 16384) take
+    // the 32-slot-per-thread select first.
+    if ((a.chunk != 8192 && a.chunk != TOPK_MAX_CHUNK) || !a.count) return hipErrorInvalidValue;
+    if (a.chunk == 8192) launch_chunks<16, 32>(a, s);
+    else launch_chunks<32, 32>(a, s);
+    return hipGetLastError();
+  }
+  switch (a.chunk / NT) {
+    case 48: launch_chunks<48, 0>(a, s); break;
+    case 40: launch_chunks<40, 0>(a, s); break;
+    case 36: launch_chunks<36, 0>(a, s); break;
+    case 1: launch_chunks<1, 0>(a, s); break;
+    case 2: launch_chunks<2, 0>(a, s); break;
+    case 4: launch_chunks<4, 0>(a, s); break;
+    case 8: launch_chunks<8, 0>(a, s); break;
+    case 16: launch_chunks<16, 0>(a, s); break;
+    default: launch_chunks<32, 0>(a, s); break;
   }
   return hipGetLastError();
 }

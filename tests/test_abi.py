@@ -139,17 +139,21 @@ def test_attention_rejects_bad_arguments(L):
 def test_workspace_sizes_are_consistent(L):
     s = seqs(batch=8, max_seq_len=131072, seq_stride=131072)
     n = L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 0)
-    # scores for 8 rows; 32767 eligible blocks -> 2 top-k chunks of 16384 with
-    # 511 candidates (key + id) each
+    # scores for 8 rows; 32767 eligible blocks -> 4 top-k chunks of 8192 with
+    # 511 candidates (key + id) each, and one chunk counter per row
     ld = L.LIB.index_scores_ld(131072)
     assert ld == 32768
-    assert n == 8 * ld * 4 + 8 * 2 * 511 * 8
-    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 1) == 8 * 2 * 511 * 8
+    assert n == 8 * ld * 4 + 8 * 4 * 511 * 8 + 8 * 4
+    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 1) == 8 * 4 * 511 * 8 + 8 * 4
+    # a row of up to 48 x 512 blocks is one chunk: 73728 tokens -> 18431 blocks -> 18432
+    assert L.LIB.index_scores_ld(73728) == 18432
+    s2 = seqs(batch=1, max_seq_len=73728, seq_stride=73728)
+    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s2), 8192, 512, 1) == 0
     # 1M tokens: 262143 blocks -> 16 chunks
     s1 = seqs(batch=1, max_seq_len=1 << 20, seq_stride=1 << 20)
     ld1 = L.LIB.index_scores_ld(1 << 20)
     assert ld1 == 262144
-    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s1), 1, 512, 0) == ld1 * 4 + 16 * 511 * 8
+    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s1), 1, 512, 0) == ld1 * 4 + 16 * 511 * 8 + 4
     # rows are padded to whole chunks: 1025 blocks -> chunk 2048
     assert L.LIB.index_scores_ld(4 * 1026) == 2048
     assert L.LIB.sparse_attn_workspace_bytes(8192, 64, 512, 512, L.IP_BF16) == 0      # prefill: no split
@@ -159,7 +163,7 @@ def test_workspace_sizes_are_consistent(L):
 
 def test_timing_hook_arguments(L):
     assert L.LIB.ip_time_next_launch(99, FAKE, FAKE) == L.IP_EINVAL
-    assert L.LIB.ip_time_next_launch(7, FAKE, FAKE) == L.IP_EINVAL
+    assert L.LIB.ip_time_next_launch(6, FAKE, FAKE) == L.IP_EINVAL
     assert L.LIB.ip_time_next_launch(2, FAKE, None) == L.IP_EINVAL      # one event only
-    assert L.LIB.ip_time_next_launch(6, FAKE, FAKE) == L.IP_OK          # top-k merge is hookable
+    assert L.LIB.ip_time_next_launch(5, FAKE, FAKE) == L.IP_OK          # split combine is hookable
     assert L.LIB.ip_time_next_launch(0, None, None) == L.IP_OK          # disarms all

@@ -142,7 +142,15 @@ def full_case(w, rows=None, keep_scores=True):
 # ---------------------------------------------------------------- small cases
 SMALL = {
     "tiny": TINY,
-    "decode_multichunk": scaled_down(DECODE, 4 * 20000 + 36, batch=2),
+    # one top-k chunk of 512 x 40 and of 512 x 48 scores per row
+    "decode_chunk40": scaled_down(DECODE, 4 * 20000 + 36, batch=2),
+    "decode_chunk48": scaled_down(DECODE, 4 * 24000 + 8, batch=2),
+    # four 8192-score chunks with a ragged last one, merged in the top-k kernel
+    "decode_multichunk": scaled_down(DECODE, 4 * 30000 + 36, batch=2),
+    # five 16384-score chunks whose 5 x 2047 winners overflow the direct merge
+    "merge_overflow": scaled_down(DECODE, 4 * 70000, batch=1, top_k=2048),
+    # rows of one to five chunks in the same launch
+    "ragged_multichunk": scaled_down(RAGGED, 4 * 40000, batch=4, min_blocks=100),
     "decode_short": scaled_down(DECODE, 300, batch=3),
     "prefill_tail": scaled_down(PREFILL, 3000, n_query=130),
     "prefill_from_zero": scaled_down(PREFILL, 64, n_query=64, top_k=6),
