@@ -36,19 +36,20 @@ namespace {
 constexpr int NT = 512;
 constexpr int NW = NT / 64;
 constexpr int NBINS = 2048;
-constexpr int BPT = NBINS / NT;          // histogram bins scanned per thread
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 constexpr int CAND_CAP = 8192;           // candidates compacted into LDS (>= top_k - 1)
 constexpr int EC = CAND_CAP / NT;        // candidates per thread in the exact select (at most)
 constexpr int BND_CAP = 64;              // boundary candidates ranked directly
 
 struct SelShared {
-  int hist[NBINS + 64];                  // + one spare bin per lane (never read)
+  __attribute__((aligned(16))) int hist[NBINS + 64];   // + one spare bin per lane (never read)
   int xi[2][NW], xj[2][NW];              // per-wave exchange slots, two sets
   float xf[2][NW], xg[2][NW], xh[2][NW];
   int digit, above;
-  uint32_t ckey[CAND_CAP + 64];          // candidates, then the kept pairs; + one
-  int32_t cid[CAND_CAP + 64];            // spare entry per lane (never read)
+  __attribute__((aligned(16))) uint32_t ckey[CAND_CAP + 64];   // candidates, then the kept
+  __attribute__((aligned(16))) int32_t cid[CAND_CAP + 64];      // pairs; + one spare entry per lane
   __attribute__((aligned(16))) uint32_t bkey[BND_CAP + 4];   // boundary candidates
+  int bkeep[BND_CAP];                    // boundary candidate i is kept
 };
 
 __device__ __forceinline__ float key_float(uint32_t k) {
@@ -118,28 +119,39 @@ __device__ __forceinline__ int x_scan(int x, int y, SelShared& sh, int p, int* t
   return before + incl - x;
 }
 
-// Histogram scan: thread t holds the BPT bins below NBINS - BPT*t (descending);
-// finds the bin d with count(bins > d) < remaining <= count(bins >= d) into
-// sh.digit / sh.above and clears the histogram for the next pass.  Two barriers.
-__device__ __forceinline__ void find_bin(SelShared& sh, int remaining, int p) {
-  const int top = NBINS - 1 - BPT * (int)threadIdx.x;
-  int h[BPT];
-  int sum = 0;
+// Histogram scan by the first wave, in two levels: lane i sums the 32 bins below
+// NBINS - 32 i (descending) and a wave scan finds the lane c whose range holds
+// the bin d with count(bins > d) < remaining <= count(bins >= d); then lane t
+// takes bin (c's top) - t and a second wave scan finds d.  Writes sh.digit /
+// sh.above and clears the histogram for the next pass.  Enters after the barrier
+// that completed the histogram; one barrier.  Needs 1 <= remaining <= total.
+__device__ __forceinline__ void find_bin(SelShared& sh, int remaining) {
+  if (threadIdx.x < 64) {
+    constexpr int BW = NBINS / 64;
+    const int lane = threadIdx.x;
+    const int lo = NBINS - BW * (lane + 1);    // this lane's bins [lo, lo + BW)
+    int sum = 0;
 #pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    h[i] = sh.hist[top - i];
-    sh.hist[top - i] = 0;
-    sum += h[i];
-  }
-  int tot, unused;
-  int before = x_scan(sum, 0, sh, p, &tot, &unused);   // values in bins > top
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    if (before < remaining && before + h[i] >= remaining) {
-      sh.digit = top - i;
-      sh.above = before;
+    for (int i = 0; i < BW; i += 4) {
+      const i32x4_t x = *(const i32x4_t*)&sh.hist[lo + i];
+      sum += x[0] + x[1] + x[2] + x[3];
     }
-    before += h[i];
+    const int incl = wave_incl_scan(sum);
+    const int before = incl - sum;             // values in bins >= lo + BW
+    const uint64_t m = __ballot(before < remaining && incl >= remaining);
+    const int c = m ? __ffsll((unsigned long long)m) - 1 : 0;
+    const int ctop = NBINS - 1 - BW * c;       // lane c's highest bin
+    const int h = lane < BW ? sh.hist[ctop - lane] : 0;
+    const int incl2 = wave_incl_scan(h);
+    const int before2 = __shfl(before, c) + incl2 - h;
+    const uint64_t m2 = __ballot(lane < BW && before2 < remaining && before2 + h >= remaining);
+    if (m2 && lane == __ffsll((unsigned long long)m2) - 1) {
+      sh.digit = ctop - lane;
+      sh.above = before2;
+    }
+    // in issue order after the reads above (one wave's LDS accesses stay ordered)
+#pragma unroll
+    for (int i = 0; i < BW; i += 4) *(i32x4_t*)&sh.hist[lo + i] = i32x4_t{0, 0, 0, 0};
   }
   __syncthreads();
 }
@@ -172,10 +184,17 @@ __device__ __forceinline__ void select_candidates_ec(int M, int kk, float lo, fl
   const int lane = threadIdx.x & 63;
   uint32_t key[EC];
   int32_t cid[EC];
+  // 16-byte LDS reads (a lane's slots are contiguous; the arrays end past
+  // NT * EC), then the slots past M are emptied
 #pragma unroll
-  for (int e = 0; e < EC; ++e) {
-    key[e] = cb + e < M ? sh.ckey[cb + e] : 0u;
-    cid[e] = sh.cid[cb + e];
+  for (int e = 0; e < EC; e += 4) {
+    const u32x4_t k4 = *(const u32x4_t*)&sh.ckey[cb + e];
+    const u32x4_t i4 = *(const u32x4_t*)&sh.cid[cb + e];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      key[e + i] = cb + e + i < M ? k4[i] : 0u;
+      cid[e + i] = (int32_t)i4[i];
+    }
   }
   uint32_t sel = 0;                       // bit e: candidate e is kept
   if (kk >= M) {
@@ -190,7 +209,7 @@ __device__ __forceinline__ void select_candidates_ec(int M, int kk, float lo, fl
       atomicAdd(&sh.hist[key[e] ? bin[e] : NBINS + lane], 1);   // empty slots: this lane's spare bin
     }
     __syncthreads();
-    find_bin(sh, kk, 0);
+    find_bin(sh, kk);
     const int B = sh.digit;
     const int remaining = kk - sh.above;  // boundary candidates still to keep
     int nb = 0;
@@ -202,26 +221,31 @@ __device__ __forceinline__ void select_candidates_ec(int M, int kk, float lo, fl
     int NB, unused;
     int bpos = x_scan(nb, 0, sh, 1, &NB, &unused);
     if (NB <= BND_CAP) {
-      // rank each boundary candidate among them: a higher key, or an equal key at
-      // a lower position, ranks before it.  Entries NB .. NB+3 are zero keys,
-      // which never rank before a candidate.
+      // one wave ranks the boundary candidates (lane i holds the i-th in candidate
+      // order): a higher key, or an equal key at a lower position, ranks before
+      // it.  Entries NB .. 63 are zero keys, which never rank before one.
 #pragma unroll
       for (int e = 0; e < EC; ++e)
         if (bin[e] == B) sh.bkey[bpos++] = key[e];
-      if ((int)threadIdx.x < 4) sh.bkey[NB + threadIdx.x] = 0u;
+      if ((int)threadIdx.x >= NB && threadIdx.x < 64) sh.bkey[threadIdx.x] = 0u;
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        const uint32_t ki = sh.bkey[lane];
+        int rank = 0;
+#pragma unroll 1
+        for (int j = 0; j < NB; j += 4) {
+          const u32x4_t k4 = *(const u32x4_t*)&sh.bkey[j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rank += k4[i] > ki || (k4[i] == ki && j + i < lane);
+        }
+        sh.bkeep[lane] = rank < remaining;
+      }
       __syncthreads();
       bpos -= nb;
 #pragma unroll
       for (int e = 0; e < EC; ++e) {
         if (bin[e] == B) {
-          int rank = 0;
-#pragma unroll 1
-          for (int j = 0; j < NB; j += 4) {
-            const u32x4_t k4 = *(const u32x4_t*)&sh.bkey[j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rank += k4[i] > key[e] || (k4[i] == key[e] && j + i < bpos);
-          }
-          sel |= (uint32_t)(rank < remaining) << e;
+          sel |= (uint32_t)sh.bkeep[bpos] << e;
           ++bpos;
         }
       }
@@ -237,7 +261,7 @@ __device__ __forceinline__ void select_candidates_ec(int M, int kk, float lo, fl
         for (int e = 0; e < EC; ++e)
           if (bin[e] == B && (key[e] & pmask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & dmask], 1);
         __syncthreads();
-        find_bin(sh, rem, pass & 1);
+        find_bin(sh, rem);
         rem -= sh.above;
         prefix |= (uint32_t)sh.digit << shift;
         pmask |= dmask << shift;
@@ -286,8 +310,8 @@ __device__ __forceinline__ void select_candidates(int M, int kk, float lo, float
 // The kk best of v (NaN = empty), ties to the lower slot, 1 <= kk <= #values:
 // their (order-preserving key, id) pairs are left in sh.ckey / sh.cid [0..kk) in
 // slot order once the caller's next barrier has passed.
-template <int E>
-__device__ __forceinline__ void select_top(const float (&v)[E], const int32_t (&id)[E], int kk, SelShared& sh) {
+template <int E, class IdOf>
+__device__ __forceinline__ void select_top(const float (&v)[E], IdOf id, int kk, SelShared& sh) {
   constexpr int GS = E >= 8 ? 8 : E;          // scores per group maximum
   constexpr int NG = E / GS;
   const int lane = threadIdx.x & 63;
@@ -325,7 +349,7 @@ __device__ __forceinline__ void select_top(const float (&v)[E], const int32_t (&
     for (int g = 0; g < NG; ++g)
       atomicAdd(&sh.hist[__builtin_isnan(gm[g]) ? NBINS + lane : bk(gm[g])], 1);
     __syncthreads();
-    find_bin(sh, kk, 1);
+    find_bin(sh, kk);
     const int B = sh.digit;
     float m = INFINITY;
 #pragma unroll
@@ -370,7 +394,7 @@ __device__ __forceinline__ void select_top(const float (&v)[E], const int32_t (&
         const bool k = (smask >> e) & 1ull;
         const int at = k ? off : CAND_CAP + lane;
         sh.ckey[at] = float_key(v[e]);
-        sh.cid[at] = id[e];
+        sh.cid[at] = id(e);
         off += k;
       }
       return;
@@ -384,7 +408,7 @@ __device__ __forceinline__ void select_top(const float (&v)[E], const int32_t (&
         const bool c = v[e] >= T;
         const int at = c ? off : CAND_CAP + lane;
         sh.ckey[at] = float_key(v[e]);
-        sh.cid[at] = id[e];
+        sh.cid[at] = id(e);
         off += c;
       }
       __syncthreads();
@@ -397,7 +421,7 @@ __device__ __forceinline__ void select_top(const float (&v)[E], const int32_t (&
 #pragma unroll
     for (int e = 0; e < E; ++e) atomicAdd(&sh.hist[v[e] >= T ? bk(v[e]) : NBINS + lane], 1);
     __syncthreads();
-    find_bin(sh, kk, par);
+    find_bin(sh, kk);
     const int B = sh.digit;
     float m = INFINITY, above = INFINITY;
 #pragma unroll
@@ -503,7 +527,7 @@ __device__ __forceinline__ void merge_row(const TopkArgs& a, int rl, int r, cons
 #pragma unroll
       for (int e = 0; e < EM; ++e) v[e] = (s0 + e < nslots && k[e] != 0u) ? key_float(k[e]) : __builtin_nanf("");
     }
-    select_top<EM>(v, id, ri.need, sh);
+    select_top<EM>(v, [&](int e) { return id[e]; }, ri.need, sh);
   }
   __syncthreads();
   write_row(a, r, ri, sh);
@@ -546,10 +570,8 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(TopkArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (s0 + e >= clen) v[e] = __builtin_nanf("");
-    int32_t id[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) id[e] = c0 + s0 + e;
-    select_top<E>(v, id, kk, sh);
+    const int id0 = c0 + s0;
+    select_top<E>(v, [=](int e) { return id0 + e; }, kk, sh);
   }
   __syncthreads();
   if (final_out) {           // kk == need here
