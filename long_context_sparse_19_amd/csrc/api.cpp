@@ -120,7 +120,7 @@ AttnPlan attn_plan(int n_q, int n_heads, int dv, int top_k, int q_dtype) {
   p.blocks_per_split = top_k;
   if (q_dtype == IP_BF16) {
     // one workgroup per (row, split) covering all 64 heads; splits add workgroups
-    // for small batches at the price of (O, m, l) partials (128 KB per split)
+    // for small batches at the price of (O, m, l) partials (64 KB per split)
     const int nsub = (top_k + 15) / 16;                 // 64-token sub-tiles
     const int want = (kAttnWorkgroups + n_q - 1) / std::max(1, n_q);
     const int ns = std::max(1, std::min(want, std::min(nsub, 64)));
@@ -128,7 +128,8 @@ AttnPlan attn_plan(int n_q, int n_heads, int dv, int top_k, int q_dtype) {
     p.blocks_per_split = sub_per * 16;
     p.n_split = (top_k + p.blocks_per_split - 1) / p.blocks_per_split;
   }
-  p.bytes = p.n_split > 1 ? (size_t)n_q * p.n_split * n_heads * ((size_t)dv + 2) * 4 : 0;
+  // bf16 partial O, then fp32 (m, l) pairs
+  p.bytes = p.n_split > 1 ? (size_t)n_q * p.n_split * n_heads * ((size_t)dv * 2 + 8) : 0;
   return p;
 }
 
@@ -342,8 +343,8 @@ static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, c
     a.v_stride = 0;
     a.n_split = p.n_split;
     a.blocks_per_split = p.blocks_per_split;
-    a.part_o = (float*)ws;
-    a.part_ml = p.n_split > 1 ? (float*)ws + (size_t)n_q * p.n_split * n_heads * dv : nullptr;
+    a.part_o = (uint16_t*)ws;
+    a.part_ml = p.n_split > 1 ? (float*)(a.part_o + (size_t)n_q * p.n_split * n_heads * dv) : nullptr;
     return device_status(ip::launch_attn_bf16(a, stream), fn);
   }
   if (q_dtype == IP_F32) {
@@ -355,7 +356,8 @@ static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, c
     a.v_stride = v->row_stride;
     a.n_split = 1;
     a.blocks_per_split = top_k;
-    a.part_o = a.part_ml = nullptr;
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
     return device_status(ip::launch_attn_f32(a, stream), fn);
   }
   return fail(IP_EUNSUPPORTED, "%s: q must be BF16 or F32", fn);

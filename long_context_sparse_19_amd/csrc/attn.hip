@@ -429,12 +429,13 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int h = 32 * i + l32;
-      float* po = a.part_o + (pi * LAT_H + h) * LAT_DV + 128 * wv + 4 * lh;
+      uint16_t* po = a.part_o + (pi * LAT_H + h) * LAT_DV + 128 * wv + 4 * lh;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *(f32x4v*)(po + 32 * d + 8 * q) = f32x4v{o[i][d][4 * q], o[i][d][4 * q + 1], o[i][d][4 * q + 2], o[i][d][4 * q + 3]};
+          *(uint2*)(po + 32 * d + 8 * q) = make_uint2(pack_bf16x2(o[i][d][4 * q], o[i][d][4 * q + 1]),
+                                                      pack_bf16x2(o[i][d][4 * q + 2], o[i][d][4 * q + 3]));
     }
     if (th == 0 && lh == 0) {
       a.part_ml[(pi * LAT_H + hs) * 2] = ms == -INFINITY ? 0.f : ms;
@@ -467,29 +468,22 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* base = a.part_o + (pi0 * LAT_H + head) * LAT_DV + t * 4;
+  const uint16_t* base = a.part_o + (pi0 * LAT_H + head) * LAT_DV + t * 4;
+  auto add = [&](float wu, uint2 v) {
+    acc.x = fmaf(wu, __uint_as_float(v.x << 16), acc.x);
+    acc.y = fmaf(wu, __uint_as_float(v.x & 0xFFFF0000u), acc.y);
+    acc.z = fmaf(wu, __uint_as_float(v.y << 16), acc.z);
+    acc.w = fmaf(wu, __uint_as_float(v.y & 0xFFFF0000u), acc.w);
+  };
   int s = 0;
   for (; s + 4 <= S; s += 4) {
-    float4 v[4];
+    uint2 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *(const float4*)(base + (int64_t)(s + u) * LAT_H * LAT_DV);
+    for (int u = 0; u < 4; ++u) v[u] = *(const uint2*)(base + (int64_t)(s + u) * LAT_H * LAT_DV);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wu = __shfl(wgt, s + u);
-      acc.x = fmaf(wu, v[u].x, acc.x);
-      acc.y = fmaf(wu, v[u].y, acc.y);
-      acc.z = fmaf(wu, v[u].z, acc.z);
-      acc.w = fmaf(wu, v[u].w, acc.w);
-    }
+    for (int u = 0; u < 4; ++u) add(__shfl(wgt, s + u), v[u]);
   }
-  for (; s < S; ++s) {
-    const float4 v = *(const float4*)(base + (int64_t)s * LAT_H * LAT_DV);
-    const float wu = __shfl(wgt, s);
-    acc.x = fmaf(wu, v.x, acc.x);
-    acc.y = fmaf(wu, v.y, acc.y);
-    acc.z = fmaf(wu, v.z, acc.z);
-    acc.w = fmaf(wu, v.w, acc.w);
-  }
+  for (; s < S; ++s) add(__shfl(wgt, s), *(const uint2*)(base + (int64_t)s * LAT_H * LAT_DV));
   const float inv = 1.f / L;
   uint16_t* out = (uint16_t*)a.out + ((int64_t)r * LAT_H + head) * LAT_DV + t * 4;
   *(uint2*)out = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));

@@ -100,7 +100,7 @@ struct AttnArgs {
   float scale;
   void* out;                   // [n_q, H, dv]
   float* lse;                  // [n_q, H] or null
-  float* part_o;               // [n_rows, n_split, H, dv] (split > 1)
+  uint16_t* part_o;            // [n_rows, n_split, H, dv] bf16, unnormalised (split > 1)
   float* part_ml;              // [n_rows, n_split, H, 2]
   int n_split, blocks_per_split;
   int heads, dk, dv;
