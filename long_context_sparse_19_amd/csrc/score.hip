@@ -29,8 +29,8 @@ constexpr int HI = 32, DI = 128;
 template <int RPW>
 __global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
   constexpr int QROW = DI + 8;                  // padded LDS row (272 bytes): conflict-free reads
-  __shared__ __align__(16) uint16_t qs[HI * QROW];
-  __shared__ float gs[HI];
+  __shared__ __align__(16) uint16_t qs[2][HI * QROW];   // double-buffered query rows
+  __shared__ float gs[2][HI];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int kl = lane & 31, hh = lane >> 5;
   const int kc0 = blockIdx.x * KEYS_PER_WG;
@@ -39,30 +39,56 @@ __global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
   if (a.topk_count && blockIdx.x == 0 && (int)threadIdx.x < rend - rbeg)
     a.topk_count[rbeg + threadIdx.x - a.row0] = 0;
 
+  // query rows (8 KB) and gates go through LDS; row r+1's are loaded while row r
+  // is computed, and staged in the other buffer, so one barrier per row suffices
+  // and the load latency of a row is hidden behind the previous one.  Thread t
+  // holds elements 16t .. 16t+15 = head t/8, dims (t%8)*16 ..
+  u32x4_t qv0, qv1;
+  float gv = 0.f;
+  auto load_q = [&](int r) {
+    const u32x4_t* qg = (const u32x4_t*)((const uint16_t*)a.q + (int64_t)r * HI * DI);
+    qv0 = qg[2 * threadIdx.x];
+    qv1 = qg[2 * threadIdx.x + 1];
+    if (threadIdx.x < HI) gv = a.gates[(int64_t)r * HI + threadIdx.x];
+  };
+  auto stage_q = [&](int buf) {
+    const int h = threadIdx.x >> 3, d = (threadIdx.x & 7) * 16;
+    *(u32x4_t*)(qs[buf] + h * QROW + d) = qv0;
+    *(u32x4_t*)(qs[buf] + h * QROW + d + 8) = qv1;
+    if (threadIdx.x < HI) gs[buf][threadIdx.x] = gv;
+  };
+  // per-row sequence, position and pooled-row count, one row per lane, read once
+  // (per-row loads inside the loop would each wait for every load in flight)
+  int rb = 0, rp = 0, rn = 1;
+  if (lane < rend - rbeg) {
+    const int rr = rbeg + lane;
+    rb = a.q_seq ? a.q_seq[rr] : rr;
+    const int len = a.L.seq_lens[rb];
+    rp = a.q_pos ? a.q_pos[rr] : len - 1;
+    rn = (len + 3) >> 2;
+  }
+  load_q(rbeg);
+  stage_q(0);
+  if (rbeg + 1 < rend) load_q(rbeg + 1);
+
   bf16x8_t kf[TILES][8];
   float ksig[TILES];
   int cur_b = -1;
 
-  for (int r = rbeg; r < rend; ++r) {
-    const int b = a.q_seq ? a.q_seq[r] : r;
-    const int p = a.q_pos ? a.q_pos[r] : a.L.seq_lens[b] - 1;
+  for (int r = rbeg, i = 0; r < rend; ++r, ++i) {
+    // row r's query is visible in buffer i&1, and every wave is done with buffer
+    // (i+1)&1 (read in row r-1); LDS-only barrier: loads in flight are not waited for
+    block_sync_lds();
+    const int b = __builtin_amdgcn_readlane(rb, i);
+    const int p = __builtin_amdgcn_readlane(rp, i);
     const int nel = p >> 2;                    // eligible blocks j < b_q
-    if (kc0 >= nel) continue;                  // uniform over the workgroup
-    // the row's query (8 KB) and gates: issued first, staged through LDS
-    u32x4_t qv0, qv1;
-    float gv = 0.f;
-    {
-      const u32x4_t* qg = (const u32x4_t*)((const uint16_t*)a.q + (int64_t)r * HI * DI);
-      qv0 = qg[2 * threadIdx.x];
-      qv1 = qg[2 * threadIdx.x + 1];
-      if (threadIdx.x < HI) gv = a.gates[(int64_t)r * HI + threadIdx.x];
-    }
-    if (b != cur_b) {
+    const bool run = kc0 < nel;                // uniform over the workgroup
+    if (run && b != cur_b) {
       cur_b = b;
       // pooled rows that exist; keys past them are clamped to the last one (their
       // scores are never written), so every load is unconditional and all of a
       // wave's loads are in flight together
-      const int nrows = (a.L.seq_lens[b] + 3) >> 2;
+      const int nrows = __builtin_amdgcn_readlane(rn, i);
       u32x4_t raw[TILES][4];
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
@@ -80,25 +106,31 @@ __global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
           kf[t][2 * c] = fp8x8_to_bf16x8(raw[t][c][0], raw[t][c][1]);
           kf[t][2 * c + 1] = fp8x8_to_bf16x8(raw[t][c][2], raw[t][c][3]);
         }
+      // the scales land here too, so that no later use of them waits for the
+      // query prefetch issued after this point
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) asm volatile("" ::"v"(ksig[t]));
     }
-    // LDS-only barriers: loads still in flight are not waited for
-    block_sync_lds();
-    {
-      // thread t holds elements 16t .. 16t+15 = head t/8, dims (t%8)*16 ..
-      const int h = threadIdx.x >> 3, d = (threadIdx.x & 7) * 16;
-      *(u32x4_t*)(qs + h * QROW + d) = qv0;
-      *(u32x4_t*)(qs + h * QROW + d + 8) = qv1;
-      if (threadIdx.x < HI) gs[threadIdx.x] = gv;
-    }
-    block_sync_lds();
+    const uint16_t* qb = qs[i & 1];
+    const float* gb = gs[i & 1];
     // query fragment: head kl, dims hh*64 .. hh*64+63 (the same dims as the key half)
     bf16x8_t qf[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qf[c] = *(const bf16x8_t*)(qs + kl * QROW + hh * 64 + c * 8);
     // gates of the 16 heads this lane accumulates: rows (i/4)*8 + hh*4 + i%4
     float g[16];
+    if (run) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) g[i] = gs[(i >> 2) * 8 + hh * 4 + (i & 3)];
+      for (int c = 0; c < 8; ++c) qf[c] = *(const bf16x8_t*)(qb + kl * QROW + hh * 64 + c * 8);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) g[e] = gb[(e >> 2) * 8 + hh * 4 + (e & 3)];
+    }
+    // stage row r+1 and fetch row r+2.  Staging waits for row r+1's loads, issued
+    // one row ago, and for whatever followed them (row r-1's score stores): both
+    // have had a row's time to finish.
+    if (r + 1 < rend) {
+      stage_q((i + 1) & 1);
+      if (r + 2 < rend) load_q(r + 2);
+    }
+    if (!run) continue;
 
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
@@ -107,7 +139,7 @@ __global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
       for (int c = 0; c < 8; ++c) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[c], kf[t][c], acc, 0, 0, 0);
       float part = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) part = fmaf(g[i], fmaxf(acc[i], 0.f), part);
+      for (int e = 0; e < 16; ++e) part = fmaf(g[e], fmaxf(acc[e], 0.f), part);
       part += __shfl_xor(part, 32);
       const int j = kc0 + (wv * TILES + t) * 32 + kl;
       if (hh == 0 && j < nel) a.scores[(int64_t)(r - a.row0) * a.ld + j] = part * ksig[t];
