@@ -406,41 +406,41 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
 
   // ---- epilogue: l of each head = sum of its two token halves
   if (lh == 0) lds_st(&sh.lpart[th][hs], l_half);
-  block_sync_lds();
-  if (a.n_split == 1) {
-    if (th == 0 && lh == 0 && a.lse) {
-      const float lt = lds_ld(&sh.lpart[0][hs]) + lds_ld(&sh.lpart[1][hs]);
-      a.lse[(int64_t)r * LAT_H + hs] = ((ms == -INFINITY ? 0.f : ms) + log2f(lt)) * LN2;
-    }
+  block_sync_lds();                              // also: every wave is done with kv0 / kv1
+  const bool final_out = a.n_split == 1;
+  const int64_t pi = (int64_t)rl * a.n_split + split;
+  // O in bf16 (normalised when final) goes through kv0 as rows of one head's 512
+  // dims, OPITCH bytes apart (2-way bank conflicts at most on the writes), and
+  // leaves in whole 1 KB rows; straight from the MFMA layout every store would
+  // scatter 8-byte pieces over 64 rows
+  constexpr int OPITCH = LAT_DV * 2 + 16;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int h = 32 * i + l32;
-      const float inv = 1.f / (lds_ld(&sh.lpart[0][h]) + lds_ld(&sh.lpart[1][h]));
-      uint16_t* out = (uint16_t*)a.out + ((int64_t)r * LAT_H + h) * LAT_DV + 128 * wv + 4 * lh;
+  for (int i = 0; i < 2; ++i) {
+    const int h = 32 * i + l32;
+    const float sc = final_out ? 1.f / (lds_ld(&sh.lpart[0][h]) + lds_ld(&sh.lpart[1][h])) : 1.f;
+    uint8_t* row = kv0 + h * OPITCH + (128 * wv + 4 * lh) * 2;
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
+    for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *(uint2*)(out + 32 * d + 8 * q) = make_uint2(pack_bf16x2(o[i][d][4 * q] * inv, o[i][d][4 * q + 1] * inv),
-                                                       pack_bf16x2(o[i][d][4 * q + 2] * inv, o[i][d][4 * q + 3] * inv));
-    }
-  } else {
-    const int64_t pi = (int64_t)rl * a.n_split + split;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int h = 32 * i + l32;
-      uint16_t* po = a.part_o + (pi * LAT_H + h) * LAT_DV + 128 * wv + 4 * lh;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *(uint2*)(po + 32 * d + 8 * q) = make_uint2(pack_bf16x2(o[i][d][4 * q], o[i][d][4 * q + 1]),
-                                                      pack_bf16x2(o[i][d][4 * q + 2], o[i][d][4 * q + 3]));
-    }
-    if (th == 0 && lh == 0) {
+      for (int q = 0; q < 4; ++q)
+        *(uint2*)(row + (32 * d + 8 * q) * 2) = make_uint2(pack_bf16x2(o[i][d][4 * q] * sc, o[i][d][4 * q + 1] * sc),
+                                                           pack_bf16x2(o[i][d][4 * q + 2] * sc, o[i][d][4 * q + 3] * sc));
+  }
+  if (th == 0 && lh == 0) {
+    const float lt = lds_ld(&sh.lpart[0][hs]) + lds_ld(&sh.lpart[1][hs]);
+    if (final_out) {
+      if (a.lse) a.lse[(int64_t)r * LAT_H + hs] = ((ms == -INFINITY ? 0.f : ms) + log2f(lt)) * LN2;
+    } else {
       a.part_ml[(pi * LAT_H + hs) * 2] = ms == -INFINITY ? 0.f : ms;
-      a.part_ml[(pi * LAT_H + hs) * 2 + 1] = lds_ld(&sh.lpart[0][hs]) + lds_ld(&sh.lpart[1][hs]);
+      a.part_ml[(pi * LAT_H + hs) * 2 + 1] = lt;
     }
+  }
+  block_sync_lds();
+  uint16_t* dst = final_out ? (uint16_t*)a.out + (int64_t)r * LAT_H * LAT_DV : a.part_o + pi * LAT_H * LAT_DV;
+#pragma unroll
+  for (int k = 0; k < LAT_H / NWA; ++k) {
+    const int h = wv + NWA * k;
+    *(u32x4_t*)(dst + h * LAT_DV + lane * 8) = *(const u32x4_t*)(kv0 + h * OPITCH + lane * 16);
   }
 }
 
