@@ -134,22 +134,19 @@ __device__ __forceinline__ BlockIds fetch_blocks(const RowCtx& c, int sb0, int s
   return ids;
 }
 
+__device__ __forceinline__ uint32_t block_entry(const AttnArgs& a, const RowCtx& c, int blk) {
+  if (blk >= 0 && blk * 4 <= c.p)
+    return (uint32_t)a.L.tok_row(c.b, (int64_t)blk * 4) | ((uint32_t)min(4, c.p - blk * 4 + 1) << VIS_SHIFT);
+  return (uint32_t)a.L.tok_row(c.b, (int64_t)(c.p >> 2) * 4);
+}
+
 __device__ __forceinline__ void build_block_table(const AttnArgs& a, const RowCtx& c, const BlockIds& ids, int sb0,
                                                   int send, AttnShared& sh) {
   const int nb = ((send - sb0 + 15) >> 4) << 4;
-  const uint32_t own = (uint32_t)a.L.tok_row(c.b, (int64_t)(c.p >> 2) * 4);
 #pragma unroll
   for (int k = 0; k < MAX_BLOCKS_PER_SPLIT / NTA; ++k) {
     const int i = (int)threadIdx.x + k * NTA;
-    if (i < nb) {
-      const int blk = ids.blk[k];
-      uint32_t e = own;
-      if (blk >= 0 && blk * 4 <= c.p) {
-        const uint32_t row = (uint32_t)a.L.tok_row(c.b, (int64_t)blk * 4);
-        e = row | ((uint32_t)min(4, c.p - blk * 4 + 1) << VIS_SHIFT);
-      }
-      lds_st(&sh.brow[i], e);
-    }
+    if (i < nb) lds_st(&sh.brow[i], block_entry(a, c, ids.blk[k]));
   }
 }
 
@@ -195,6 +192,22 @@ __device__ __forceinline__ SubtileSrc subtile_src(const AttnArgs& a, const AttnS
   return src;
 }
 
+// The same rows for sub-tile n straight from the selection ids (blk[h]: the block
+// of row half h, -1 past the split), for the prologue: the block table is not
+// built yet, and reading it while LDS DMA is in flight would wait for the DMA.
+__device__ __forceinline__ SubtileSrc subtile_src_ids(const AttnArgs& a, const RowCtx& c, const int (&blk)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  SubtileSrc src;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = 8 * (2 * wv + h) + (lane >> 3);
+    const uint32_t grow = (block_entry(a, c, blk[h]) & ROW_BITS) + (t & 3);
+    src.row[h] = a.k + (uint64_t)grow * a.k_stride + 16 * ((lane & 7) ^ kv_swz(t));
+  }
+  return src;
+}
+
 __device__ __forceinline__ void load_column(const SubtileSrc& src, uint8_t* buf, int k) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = k >> 1, h = k & 1;
@@ -210,11 +223,13 @@ __device__ __forceinline__ void load_subtile(const AttnArgs& a, const AttnShared
 }
 
 // Waits until at most `pending` (0 or 18) of this wave's global loads are
-// outstanding.  The vmcnt field of the s_waitcnt immediate is bits 0..3 and 14..15;
-// expcnt (bits 4..6) and lgkmcnt (bits 8..11) stay at their maxima (no wait).
+// outstanding.  The vmcnt field of the s_waitcnt immediate is bits 0..3 (low) and
+// 14..15 (high); expcnt (bits 4..6) and lgkmcnt (bits 8..11) stay at their maxima
+// (no wait).
 __device__ __forceinline__ void wait_loads(int pending) {
   constexpr int NOWAIT = (0x7 << 4) | (0xF << 8);
-  if (pending >= KV_LOADS) __builtin_amdgcn_s_waitcnt(KV_LOADS | NOWAIT);
+  constexpr int VM18 = (KV_LOADS & 0xF) | ((KV_LOADS >> 4) << 14);
+  if (pending >= KV_LOADS) __builtin_amdgcn_s_waitcnt(VM18 | NOWAIT);
   else __builtin_amdgcn_s_waitcnt(NOWAIT);
 }
 
@@ -237,17 +252,35 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
   const int nsub = (send - sb0 + 15) >> 4;
   const int hs = 32 * hb + l32;                  // head of this lane in the S^T layout
 
-  // prologue loads, in this order: selection ids, q fragments (head hs, dims
-  // 16s + 8lh .. +8 for k-step s), then the first sub-tiles; building the block
-  // table waits only for the ids, and the q fragments land while the first
-  // sub-tile is fetched
+  // prologue loads, in this order: selection ids, the query row (into kv1), then
+  // sub-tile 0; building the block table waits only for the ids, and q is read
+  // into registers while sub-tile 0 is fetched
   const BlockIds ids = fetch_blocks(c, sb0, send);
-  bf16x8_t qf[KSTEPS];
-  {
-    const u32x4_t* qs = (const u32x4_t*)((const uint16_t*)a.q + ((int64_t)r * LAT_H + hs) * LAT_DK + 8 * lh);
+  // ids of this lane's source blocks for sub-tiles 0 and 1 (rows 8(2w + h) + l/8)
+  int pid[2][2];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, qs[2 * s]);
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int bi = sb0 + 16 * n + ((8 * (2 * wv + h) + (lane >> 3)) >> 2);
+      pid[n][h] = bi < send ? c.sel[bi] : -1;
+    }
+  {
+    // the query row (64 heads x 576 dims = one sub-tile's bytes) goes to kv1 by LDS
+    // DMA in the sub-tile layout, head h as row h: whole 128-byte lines, and the
+    // fragment reads below are the conflict-free K-fragment pattern
+    SubtileSrc qsrc;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = 8 * (2 * wv + h) + (lane >> 3);
+      qsrc.row[h] = (const uint8_t*)a.q + ((int64_t)r * LAT_H + t) * (LAT_DK * 2) + 16 * ((lane & 7) ^ kv_swz(t));
+    }
+#pragma unroll
+    for (int k = 0; k < KV_LOADS; ++k) load_column(qsrc, kv1, k);
   }
+  // every query DMA is issued before anything consumes the ids: a use of a loaded
+  // register while LDS DMA is in flight makes the compiler wait for all loads
+  __builtin_amdgcn_sched_barrier(0);
   const float cs = a.scale * LOG2E;
 
   // O^T tiles [32 dims, 32 heads]: o[i][db][k] = head 32i + l32, dim 128wv + 32db +
@@ -261,20 +294,33 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
   float ms = -INFINITY, mo[2] = {-INFINITY, -INFINITY};
   float l_half = 0.f;                            // l of head hs over this wave's token half
 
+  const SubtileSrc src0 = subtile_src_ids(a, c, pid[0]);
+  const SubtileSrc src1 = subtile_src_ids(a, c, pid[1]);
+  if (nsub > 0) {
+#pragma unroll
+    for (int k = 0; k < KV_LOADS; ++k) load_column(src0, kv0, k);
+  }
   build_block_table(a, c, ids, sb0, send, sh);
   if (threadIdx.x < 4) lds_st(&sh.need[threadIdx.x], 0);
+  if (nsub > 0) wait_loads(KV_LOADS);            // this wave's part of q landed
+  else wait_loads(0);
   block_sync_lds();
-  if (nsub > 0) load_subtile(a, sh, 0, kv0);
+  // q fragments: head hs, dims 16s + 8lh .. +8 for k-step s.  q only feeds MFMA B
+  // operands, which may sit in accumulation registers: keep it there, leaving the
+  // ordinary VGPRs to the O accumulators
+  bf16x8_t qf[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const bf16x8_t*)(kv1 + kv_off(hs, 2 * s + lh));
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+a"(qf[s]));
+  block_sync_lds();                              // every wave has its q: kv1 is free
   if (nsub > 1) {
-    load_subtile(a, sh, 1, kv1);
-    wait_loads(KV_LOADS);                        // q and sub-tile 0 landed (this wave's part)
+#pragma unroll
+    for (int k = 0; k < KV_LOADS; ++k) load_column(src1, kv1, k);
+    wait_loads(KV_LOADS);                        // sub-tile 0 landed (this wave's part)
   } else {
     wait_loads(0);
   }
-  // q only feeds MFMA B operands, which may sit in accumulation registers: keep it
-  // there, leaving the ordinary VGPRs to the O accumulators
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+a"(qf[s]));
   block_sync_lds();
 
   // one sub-tile: compute on `buf`, while sub-tile n+1 streams into `nxt`
