@@ -108,6 +108,39 @@ ip_status indexpool_compress(const ip_seqs* seqs, const int32_t* block_begin, in
                              hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * indexpool_append -- one decode step's cache growth.
+ * G2C Brief, "DSA keeps selected global access in eleven layers": the DSA layers
+ * keep a token-addressable history that grows with the sequence (the MLA latent
+ * rows, and the indexer keys that IndexPool pools four at a time); reading notes,
+ * section 4 "The serving stack": the FP8 cache tier; reading notes, section 2,
+ * sub-section "IndexPool" for the pooling.
+ *
+ * seq_lens[b] already counts the new token, which goes to position
+ * t = seq_lens[b] - 1 of sequence b (sequences with seq_lens[b] < 1 are skipped):
+ *     kv[t]     = kv_new[b]       row copy (BF16 or F32 cache, same dtype as kv_new)
+ *     v[t]      = v_new[b]        only when v is not NULL (separate V cache)
+ *     keys[t]   = key_new[b]      FP8 keys: sigma_t = max_d |x_d| / 448 and codes
+ *                                 e4m3fn(x / sigma_t), rounded to nearest even and
+ *                                 saturated at +-448 (sigma_t = 0: zero codes);
+ *                                 F32 keys: copied
+ *     logits[t] = logit_new[b]
+ * and when seq_lens[b] % 4 == 0 the block t / 4 that the token completes is pooled
+ * into `pooled` exactly as indexpool_compress pools it.
+ *
+ *  kv_new   device [batch, kv->row_dim], kv->dtype; kv->row_dim * element size a
+ *           multiple of 16 bytes (the same for v_new / v)
+ *  key_new  device [batch, keys->row_dim], key_dtype BF16 or F32 (F32 for F32 keys)
+ *  logit_new  device [batch] fp32;  logits  device [token rows] fp32
+ *  keys, pooled  as in indexpool_compress (FP8 with scales, row_dim 128; or F32)
+ * Errors: NULL pointers, dtype or shape mismatches -> IP_EINVAL / IP_EUNSUPPORTED
+ * before any launch.  Writes only the new token's rows and the pooled row.
+ * ------------------------------------------------------------------------------- */
+ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cache* kv,
+                           const void* v_new, const ip_cache* v, const void* key_new,
+                           int32_t key_dtype, const ip_cache* keys, const float* logit_new,
+                           float* logits, const ip_cache* pooled, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * index_score_topk -- the lightweight indexer and the learned top-k selection.
  * Reading notes, section 2 "Hybrid Attention: Linear State + Sparse Retrieval"
  * (sparse attention as the global retriever, via a lightweight indexer, in the
@@ -191,7 +224,7 @@ const char* ip_last_error(void);
  * goes through hipExtLaunchKernelGGL with `start` / `stop`, so the two events
  * receive that dispatch's own start and end times (the timestamps a kernel trace
  * reports).  kernel_id: 1 compress, 2 score, 3 top-k, 4 attention, 5 split
- * combine.  Hooks for different ids may be
+ * combine, 6 append.  Hooks for different ids may be
  * armed together; each is consumed by one launch.  Passing NULL for one event
  * only is IP_EINVAL; kernel_id 0 with both NULL disarms every hook.  Use it
  * outside stream capture.  Not needed for normal use. */

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libindexpool.so")
 
 IP_OK, IP_EINVAL, IP_EUNSUPPORTED, IP_EWORKSPACE, IP_EDEVICE = range(5)
 IP_F32, IP_BF16, IP_FP8_E4M3FN = range(3)
-K_COMPRESS, K_SCORE, K_TOPK, K_ATTN, K_COMBINE = 1, 2, 3, 4, 5
+K_COMPRESS, K_SCORE, K_TOPK, K_ATTN, K_COMBINE, K_APPEND = 1, 2, 3, 4, 5, 6
 
 _c_void_p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -51,6 +51,8 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     lib.indexpool_compress.argtypes = [P(IpSeqs), _c_void_p, _i32, P(IpCache), _c_void_p, P(IpCache), _c_void_p]
+    lib.indexpool_append.argtypes = [P(IpSeqs), _c_void_p, P(IpCache), _c_void_p, P(IpCache), _c_void_p, _i32,
+                                     P(IpCache), _c_void_p, _c_void_p, P(IpCache), _c_void_p]
     lib.index_scores_ld.argtypes = [_i32]
     lib.index_scores_ld.restype = _i64
     lib.index_score_topk_workspace_bytes.argtypes = [P(IpSeqs), _i32, _i32, _i32]
@@ -69,15 +71,15 @@ def _load() -> ctypes.CDLL:
     lib.ip_last_error.restype = ctypes.c_char_p
     lib.ip_version.restype = ctypes.c_char_p
     lib.ip_time_next_launch.argtypes = [_i32, _c_void_p, _c_void_p]
-    for fn in ("indexpool_compress", "index_score_topk", "sparse_attn_decode", "sparse_attn_prefill",
-               "ip_time_next_launch"):
+    for fn in ("indexpool_compress", "indexpool_append", "index_score_topk", "sparse_attn_decode",
+               "sparse_attn_prefill", "ip_time_next_launch"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
 
 LIB = _load()
 
-EXPORTED = ("indexpool_compress", "index_scores_ld", "index_score_topk_workspace_bytes", "index_score_topk",
+EXPORTED = ("indexpool_compress", "indexpool_append", "index_scores_ld", "index_score_topk_workspace_bytes", "index_score_topk",
             "sparse_attn_workspace_bytes", "sparse_attn_decode", "sparse_attn_prefill", "ip_last_error",
             "ip_time_next_launch", "ip_version")
 
@@ -133,6 +135,17 @@ def indexpool_compress(seqs: Seqs, keys: Cache, logits: torch.Tensor, pooled: Ca
     _check("indexpool_compress", LIB.indexpool_compress(
         ctypes.byref(s), _ptr(block_begin), max_blocks, ctypes.byref(k), logits.data_ptr(), ctypes.byref(p),
         _stream(stream)))
+
+
+def indexpool_append(seqs: Seqs, kv_new: torch.Tensor, kv: Cache, key_new: torch.Tensor, keys: Cache,
+                     logit_new: torch.Tensor, logits: torch.Tensor, pooled: Cache,
+                     v_new: Optional[torch.Tensor] = None, v: Optional[Cache] = None, stream=None) -> None:
+    s, kc, k, p = seqs.c(), kv.c(), keys.c(), pooled.c()
+    vc = None if v is None else v.c()
+    _check("indexpool_append", LIB.indexpool_append(
+        ctypes.byref(s), kv_new.data_ptr(), ctypes.byref(kc), _ptr(v_new),
+        None if vc is None else ctypes.byref(vc), key_new.data_ptr(), _DT[key_new.dtype], ctypes.byref(k),
+        logit_new.data_ptr(), logits.data_ptr(), ctypes.byref(p), _stream(stream)))
 
 
 def index_scores_ld(max_seq_len: int) -> int:

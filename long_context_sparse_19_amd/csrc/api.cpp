@@ -208,6 +208,63 @@ ip_status indexpool_compress(const ip_seqs* seqs, const int32_t* block_begin, in
   return fail(IP_EUNSUPPORTED, "%s: keys must be FP8 or F32", fn);
 }
 
+// ------------------------------------------------------------------ decode append
+ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cache* kv, const void* v_new,
+                           const ip_cache* v, const void* key_new, int32_t key_dtype, const ip_cache* keys,
+                           const float* logit_new, float* logits, const ip_cache* pooled, hipStream_t stream) {
+  const char* fn = "indexpool_append";
+  if (ip_status st = check_seqs(seqs, fn)) return st;
+  if (ip_status st = check_cache(kv, fn, "kv")) return st;
+  if (ip_status st = check_cache(keys, fn, "keys")) return st;
+  if (ip_status st = check_cache(pooled, fn, "pooled")) return st;
+  if (!kv_new || !key_new || !logit_new || !logits)
+    return fail(IP_EINVAL, "%s: kv_new, key_new, logit_new and logits must not be NULL", fn);
+  if (v) {
+    if (ip_status st = check_cache(v, fn, "v")) return st;
+    if (!v_new) return fail(IP_EINVAL, "%s: v_new is NULL while v is given", fn);
+  }
+  if (kv->dtype == IP_FP8_E4M3FN || (v && v->dtype == IP_FP8_E4M3FN))
+    return fail(IP_EUNSUPPORTED, "%s: kv / v caches must be BF16 or F32", fn);
+  const int kv_bytes = kv->row_dim * elem_bytes(kv->dtype);
+  const int v_bytes = v ? v->row_dim * elem_bytes(v->dtype) : 0;
+  if (kv_bytes % 16 || v_bytes % 16) return fail(IP_EUNSUPPORTED, "%s: kv / v rows must be whole 16-byte chunks", fn);
+  if (keys->dtype != pooled->dtype || keys->row_dim != pooled->row_dim)
+    return fail(IP_EINVAL, "%s: keys and pooled must share dtype and row_dim", fn);
+  if (keys->dtype == IP_FP8_E4M3FN) {
+    if (keys->row_dim != 128) return fail(IP_EUNSUPPORTED, "%s: FP8 keys need row_dim 128 (got %d)", fn, keys->row_dim);
+    if (key_dtype != IP_BF16 && key_dtype != IP_F32) return fail(IP_EUNSUPPORTED, "%s: key_new must be BF16 or F32", fn);
+  } else if (keys->dtype == IP_F32) {
+    if (keys->row_dim > 256) return fail(IP_EUNSUPPORTED, "%s: F32 keys need row_dim <= 256", fn);
+    if (key_dtype != IP_F32) return fail(IP_EUNSUPPORTED, "%s: F32 keys take an F32 key_new", fn);
+  } else {
+    return fail(IP_EUNSUPPORTED, "%s: keys must be FP8 or F32", fn);
+  }
+  if (seqs->batch > 65535) return fail(IP_EUNSUPPORTED, "%s: batch > 65535", fn);
+  ip::AppendArgs a;
+  a.L = layout_of(seqs);
+  a.batch = seqs->batch;
+  a.kv_new = (const uint8_t*)kv_new;
+  a.kv = (uint8_t*)kv->data;
+  a.kv_stride = kv->row_stride;
+  a.kv_row_bytes = kv_bytes;
+  a.v_new = (const uint8_t*)v_new;
+  a.v = v ? (uint8_t*)v->data : nullptr;
+  a.v_stride = v ? v->row_stride : 0;
+  a.v_row_bytes = v_bytes;
+  a.key_new = key_new;
+  a.key_bf16 = key_dtype == IP_BF16;
+  a.keys = (uint8_t*)keys->data;
+  a.key_stride = keys->row_stride;
+  a.key_scale = keys->dtype == IP_FP8_E4M3FN ? keys->scale : nullptr;
+  a.dim = keys->row_dim;
+  a.logit_new = logit_new;
+  a.logits = logits;
+  a.pooled = (uint8_t*)pooled->data;
+  a.pooled_stride = pooled->row_stride;
+  a.pooled_scale = keys->dtype == IP_FP8_E4M3FN ? pooled->scale : nullptr;
+  return device_status(ip::launch_append(a, stream), fn);
+}
+
 // ------------------------------------------------------------------ indexer + top-k
 size_t index_score_topk_workspace_bytes(const ip_seqs* seqs, int32_t n_q, int32_t top_k,
                                         int32_t scores_given) {

@@ -113,7 +113,101 @@ __global__ __launch_bounds__(NT) void compress_f32_kernel(CompressArgs a) {
   *(float4*)(a.out + prow * a.out_stride + e4 * 16) = acc;
 }
 
+// ---------------------------------------------------------------- decode append
+// One workgroup per sequence writes its new token (position seq_lens[b] - 1) into
+// the caches and, when that token completes a block, pools the block.  The new
+// key's codes and scale stay in registers for the pooling, which follows the same
+// arithmetic, in the same order, as compress_fp8_kernel / compress_f32_kernel.
+constexpr int APPEND_MAX_DIM = 256;
+__global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
+  __shared__ float red[NT / 64];
+  const int b = blockIdx.x;
+  const int len = a.L.seq_lens[b];
+  if (len < 1) return;
+  const int64_t t = len - 1;
+  const int64_t row = a.L.tok_row(b, t);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // latent (or K) and V rows: plain 16-byte copies
+  for (int i = tid; i < a.kv_row_bytes / 16; i += NT)
+    *(uint4*)(a.kv + row * a.kv_stride + 16 * i) = *(const uint4*)(a.kv_new + (int64_t)b * a.kv_row_bytes + 16 * i);
+  if (a.v)
+    for (int i = tid; i < a.v_row_bytes / 16; i += NT)
+      *(uint4*)(a.v + row * a.v_stride + 16 * i) = *(const uint4*)(a.v_new + (int64_t)b * a.v_row_bytes + 16 * i);
+  const bool on = tid < a.dim;
+  float x = 0.f;
+  if (on)
+    x = a.key_bf16 ? bf16_to_f32(((const uint16_t*)a.key_new)[(int64_t)b * a.dim + tid])
+                   : ((const float*)a.key_new)[(int64_t)b * a.dim + tid];
+  const float lnew = a.logit_new[b];
+  if (tid == 0) a.logits[row] = lnew;
+  const bool fp8 = a.key_scale != nullptr;
+  auto block_max = [&](float v) {                // max over the workgroup (all threads call)
+    v = wave_max(v);
+    if (lane == 0) red[wv] = v;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
+    __syncthreads();
+    return m;
+  };
+  // the new token's key: fp8 with sigma = amax / 448, or the float key as is
+  uint32_t code = 0;
+  float sigma = 0.f;
+  if (fp8) {
+    const float amax = block_max(on ? fabsf(x) : 0.f);
+    sigma = amax / 448.0f;
+    if (amax > 0.f) code = f32_to_e4m3(fminf(fmaxf(x * (448.0f / amax), -448.f), 448.f));
+    if (on) a.keys[row * a.key_stride + tid] = (uint8_t)code;
+    if (tid == 0) a.key_scale[row] = sigma;
+  } else if (on) {
+    ((float*)(a.keys + row * a.key_stride))[tid] = x;
+  }
+  if ((len & 3) != 0) return;                    // uniform: no block completed
+  // block t/4: tokens t-3 .. t (the block's rows are contiguous)
+  const int64_t r0 = row - 3;
+  const int64_t prow = a.L.pool_row(b, t >> 2);
+  float lg[4], w[4];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) lg[i] = a.logits[r0 + i];
+  lg[3] = lnew;
+  softmax4(lg, w);
+  if (fp8) {
+    float acc = 0.f;
+    if (on) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = i < 3 ? a.key_scale[r0 + i] : sigma;
+        const uint32_t c = i < 3 ? a.keys[(r0 + i) * a.key_stride + tid] : code;
+        float f[4];
+        fp8x4_to_f32(c, f);
+        acc = fmaf(w[i] * sc, f[0], acc);
+      }
+    }
+    const float amax = block_max(on ? fabsf(acc) : 0.f);
+    uint32_t pc = 0;
+    if (amax > 0.f) pc = f32_to_e4m3(fminf(fmaxf(acc * (448.0f / amax), -448.f), 448.f));
+    if (on) a.pooled[prow * a.pooled_stride + tid] = (uint8_t)pc;
+    if (tid == 0) a.pooled_scale[prow] = amax / 448.0f;
+  } else if (on) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float k = i < 3 ? ((const float*)(a.keys + (r0 + i) * a.key_stride))[tid] : x;
+      acc = fmaf(w[i], k, acc);
+    }
+    ((float*)(a.pooled + prow * a.pooled_stride))[tid] = acc;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  if (a.batch <= 0) return hipSuccess;
+  if (a.dim > APPEND_MAX_DIM) return hipErrorInvalidValue;
+  launch(K_APPEND, append_kernel, dim3(a.batch), dim3(NT), s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_compress_fp8(const CompressArgs& a, hipStream_t s) {
   if (a.max_blocks <= 0) return hipSuccess;

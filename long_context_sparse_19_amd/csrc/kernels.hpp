@@ -8,7 +8,7 @@
 
 namespace ip {
 
-enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3, K_ATTN = 4, K_COMBINE = 5, K_LAST = 5 };
+enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3, K_ATTN = 4, K_COMBINE = 5, K_APPEND = 6, K_LAST = 6 };
 
 // Takes (and disarms) the timing hook's events if one is armed for kernel `id`.
 bool hook_take(int id, hipEvent_t* start, hipEvent_t* stop);
@@ -42,6 +42,32 @@ struct CompressArgs {
 };
 hipError_t launch_compress_fp8(const CompressArgs& a, hipStream_t s);
 hipError_t launch_compress_f32(const CompressArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------ decode cache append
+struct AppendArgs {
+  Layout L;
+  int batch;
+  const uint8_t* kv_new;       // [batch, kv_row_bytes]
+  uint8_t* kv;                 // token rows
+  int64_t kv_stride;
+  int kv_row_bytes;            // a multiple of 16
+  const uint8_t* v_new;        // [batch, v_row_bytes] or null
+  uint8_t* v;
+  int64_t v_stride;
+  int v_row_bytes;
+  const void* key_new;         // [batch, dim], bf16 or f32
+  int key_bf16;
+  uint8_t* keys;               // token key rows: fp8 codes (+ key_scale) or f32
+  int64_t key_stride;
+  float* key_scale;            // [token rows] (fp8) or null
+  int dim;
+  const float* logit_new;      // [batch]
+  float* logits;               // [token rows]
+  uint8_t* pooled;             // pooled rows
+  int64_t pooled_stride;
+  float* pooled_scale;         // [pooled rows] (fp8) or null
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------ indexer scoring
 struct ScoreArgs {

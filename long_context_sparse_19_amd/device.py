@@ -87,6 +87,24 @@ def compress(d: DeviceInputs, block_begin: Optional[torch.Tensor] = None, max_bl
     _lib.indexpool_compress(d.seqs, d.keys, d.logits, d.pooled, block_begin, max_blocks, stream)
 
 
+class NewTokens:
+    """One decode step's new tokens on the device (see inputs.new_tokens)."""
+
+    def __init__(self, new: dict, device="cuda"):
+        bf16 = new["kv_new"].dtype == np.uint16
+        self.kv_new = _dev(new["kv_new"], device, torch.bfloat16 if bf16 else None)
+        self.v_new = None if new["v_new"] is None else _dev(new["v_new"], device)
+        kbf16 = new["key_new"].dtype == np.uint16
+        self.key_new = _dev(new["key_new"], device, torch.bfloat16 if kbf16 else None)
+        self.logit_new = _dev(new["logit_new"], device)
+
+
+def append(d: DeviceInputs, t: NewTokens, stream=None) -> None:
+    """Write each sequence's new token (at seq_lens[b] - 1) and pool a completed block."""
+    _lib.indexpool_append(d.seqs, t.kv_new, d.kv, t.key_new, d.keys, t.logit_new, d.logits, d.pooled,
+                          v_new=t.v_new, v=d.v, stream=stream)
+
+
 class Workspaces:
     """Outputs and workspaces of one pipeline pass, allocated once."""
 

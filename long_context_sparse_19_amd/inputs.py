@@ -36,7 +36,7 @@ _CHUNK_ROWS = 1 << 16
 
 _TAGS = {
     "lens": 1, "perm": 2, "idx_keys": 3, "logits": 4, "latent": 5, "k": 6, "v": 7,
-    "q": 8, "q_idx": 9, "gates": 10, "salient": 11,
+    "q": 8, "q_idx": 9, "gates": 10, "salient": 11, "append": 12,
 }
 
 
@@ -215,3 +215,20 @@ def make_inputs(w: Workload, with_attention: bool = True) -> Inputs:
         pool_logits=logits, latent=latent, k_cache=k_cache, v_cache=v_cache, q=q,
         q_idx=q_idx, gates=gates, q_seq=q_seq, q_pos=q_pos, salient_rows=salient,
     )
+
+
+def new_tokens(w: Workload, batch: int, seed: int) -> dict:
+    """One decode step's new token per sequence, seeded N(0,1) like the caches:
+    kv_new (bf16 bits [B, dk] latent rows, or float32 K rows), v_new (float32 [B, dv]
+    or None), key_new (bf16 bits [B, D_I] for fp8 key caches, float32 otherwise) and
+    logit_new (float32 [B])."""
+    rng = _rng(seed, "append")
+    bf16 = w.attn_dtype == "bf16"
+    kv = rng.standard_normal((batch, w.dk), dtype=np.float32)
+    key = rng.standard_normal((batch, w.idx_dim), dtype=np.float32)
+    return {
+        "kv_new": to_bf16_bits(kv) if bf16 else kv,
+        "v_new": None if bf16 else rng.standard_normal((batch, w.dv), dtype=np.float32),
+        "key_new": to_bf16_bits(key) if w.idx_key_dtype == "fp8" else key,
+        "logit_new": rng.standard_normal(batch, dtype=np.float32),
+    }

@@ -41,6 +41,14 @@ in the design notes):
   logits scale * q.K_t, softmax, weighted sum of V_t; lse = log sum exp.  For the
   576-dim latent row, K is the whole row and V its first 512 dims.
 * R7 e4m3fn: bias 7, no infinities, S.1111.111 is NaN, max finite 448.
+* R8 decode cache growth: the new token of sequence b sits at t = seq_lens[b] - 1
+  (the length already counts it).  Its latent row and logit are stored as given;
+  an fp8 key cache stores the key quantised per token like R3 (sigma_t = max|x| /
+  448); a float key cache stores the key as given.  When seq_lens[b] % 4 == 0 the
+  token completes block t // 4, which is pooled from tokens t-3 .. t (R1-R3).  G2C
+  Brief, section "DSA keeps selected global access in eleven layers" (a
+  token-addressable history that grows with the sequence); reading notes, section
+  4 "The serving stack" (the FP8 tier).
 """
 from __future__ import annotations
 
@@ -180,6 +188,60 @@ def pooled_values(pooled, sigma) -> np.ndarray:
     if sigma is None:
         return np.asarray(pooled, dtype=F64)
     return np.asarray(sigma, dtype=F64)[:, None] * fp8_decode(pooled)
+
+
+# ----------------------------------------------------------------------------- decode append
+def quantize_tokens(x):
+    """Per-token fp8 quantisation of key rows (R8, with R3's rule): sigma =
+    max_d |x_d| / 448, codes = e4m3fn(x / sigma), zero codes when sigma = 0.
+    x [N, D] -> codes [N, D] uint8, sigma [N] float64, v [N, D] = x / sigma."""
+    x = np.asarray(x, dtype=F64)
+    sigma = np.abs(x).max(axis=1) / E4M3_MAX
+    safe = np.where(sigma > 0, sigma, 1.0)
+    v = np.where(sigma[:, None] > 0, x / safe[:, None], 0.0)
+    codes = fp8_encode(v)
+    codes[sigma == 0] = 0
+    return codes, sigma, v
+
+
+def append(inp, kv_new, key_new, logit_new):
+    """What one decode step's cache growth writes (R8), per sequence.
+
+    inp holds the caches before the step (idx_keys, idx_scale, pool_logits and the
+    layout) and seq_lens counting the new tokens.  kv_new [B, ...], key_new [B, D]
+    (bf16 bit patterns or floats), logit_new [B].  Returns one dict per sequence with
+    a new token: row, kv, key (codes, or floats for a float cache), sigma, v (x /
+    sigma), logit, and when a block completes prow, pooled, psigma, pv, pmag (the
+    outputs of pool_fp8, or the float pooled key)."""
+    out = []
+    fp8 = inp.idx_scale is not None
+    for b, L in enumerate(np.asarray(inp.seq_lens, dtype=np.int64)):
+        if L < 1:
+            out.append(None)
+            continue
+        t = int(L) - 1
+        row = int(token_rows(inp, b, t))
+        x = _to_f64(np.asarray(key_new)[b])
+        e = {"row": row, "kv": np.asarray(kv_new)[b], "logit": float(np.asarray(logit_new)[b])}
+        if fp8:
+            codes, sigma, v = quantize_tokens(x[None])
+            e.update(key=codes[0], sigma=float(sigma[0]), v=v[0])
+        else:
+            e.update(key=x, sigma=None, v=None)
+        if L % 4 == 0:
+            prev = token_rows(inp, b, np.arange(t - 3, t))
+            lg4 = np.concatenate([np.asarray(inp.pool_logits, dtype=F64)[prev], [e["logit"]]])[None]
+            e["prow"] = int(pooled_rows(inp, b, t // 4))
+            if fp8:
+                c4 = np.concatenate([inp.idx_keys[prev], e["key"][None]])[None]
+                s4 = np.concatenate([np.asarray(inp.idx_scale, dtype=F64)[prev], [e["sigma"]]])[None]
+                pc, ps, pv, pm = pool_fp8(c4, s4, lg4)
+                e.update(pooled=pc[0], psigma=float(ps[0]), pv=pv[0], pmag=pm[0])
+            else:
+                k4 = np.concatenate([np.asarray(inp.idx_keys, dtype=F64)[prev], x[None]])[None]
+                e.update(pooled=pool_f32(k4, lg4)[0], psigma=None, pv=None, pmag=None)
+        out.append(e)
+    return out
 
 
 # ----------------------------------------------------------------------------- indexer

@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_pipeline_calls():
     names = declared_functions()
-    for fn in ("indexpool_compress", "index_score_topk", "sparse_attn_decode", "sparse_attn_prefill",
-               "ip_last_error"):
+    for fn in ("indexpool_compress", "indexpool_append", "index_score_topk", "sparse_attn_decode",
+               "sparse_attn_prefill", "ip_last_error"):
         assert fn in names
 
 
@@ -78,6 +78,37 @@ def test_compress_rejects_bad_arguments(L):
     assert compress(L, seqs(), cache(L, dtype=L.IP_BF16, stride=256)) == L.IP_EUNSUPPORTED
     assert compress(L, seqs(), good, pooled=cache(L, dtype=L.IP_F32, stride=512)) == L.IP_EINVAL
     assert compress(L, seqs(), cache(L, dtype=L.IP_F32, row_dim=512, stride=2048, scale=None)) == L.IP_EUNSUPPORTED
+
+
+def append(L, s, kv=None, v=None, v_new=None, key_dtype=None, keys=None, pooled=None, kv_new=FAKE,
+           key_new=FAKE, logit_new=FAKE, logits=FAKE):
+    kv = cache(L, dtype=L.IP_BF16, row_dim=576, stride=1152, scale=None) if kv is None else kv
+    keys = cache(L) if keys is None else keys
+    pooled = keys if pooled is None else pooled
+    key_dtype = L.IP_BF16 if key_dtype is None else key_dtype
+    return L.LIB.indexpool_append(ctypes.byref(s), kv_new, ctypes.byref(kv), v_new,
+                                  None if v is None else ctypes.byref(v), key_new, key_dtype,
+                                  ctypes.byref(keys), logit_new, logits, ctypes.byref(pooled), None)
+
+
+def test_append_rejects_bad_arguments(L):
+    s = seqs()
+    f32 = cache(L, dtype=L.IP_F32, row_dim=64, stride=256, scale=None)
+    assert append(L, seqs(batch=0)) == L.IP_EINVAL
+    assert append(L, s, kv_new=None) == L.IP_EINVAL
+    assert append(L, s, key_new=None) == L.IP_EINVAL
+    assert append(L, s, logit_new=None) == L.IP_EINVAL
+    assert append(L, s, logits=None) == L.IP_EINVAL
+    assert append(L, s, v=f32) == L.IP_EINVAL                                   # v without v_new
+    assert append(L, s, kv=cache(L)) == L.IP_EUNSUPPORTED                        # fp8 latent
+    assert append(L, s, kv=cache(L, dtype=L.IP_BF16, row_dim=12, stride=32, scale=None)) == L.IP_EUNSUPPORTED
+    assert append(L, s, key_dtype=L.IP_FP8_E4M3FN) == L.IP_EUNSUPPORTED
+    assert append(L, s, keys=cache(L, row_dim=64, stride=64)) == L.IP_EUNSUPPORTED
+    assert append(L, s, keys=cache(L, scale=None)) == L.IP_EINVAL
+    assert append(L, s, pooled=cache(L, dtype=L.IP_F32, stride=512, scale=None)) == L.IP_EINVAL
+    assert append(L, s, kv=f32, keys=f32, key_dtype=L.IP_BF16) == L.IP_EUNSUPPORTED   # F32 keys take F32
+    assert append(L, s, kv=f32, keys=cache(L, dtype=L.IP_F32, row_dim=512, stride=2048, scale=None),
+                  key_dtype=L.IP_F32) == L.IP_EUNSUPPORTED
 
 
 def score(L, s, n_q=2, q_dtype=None, H=32, D=128, pooled=None, top_k=512, ws=FAKE, ws_bytes=1 << 30,
@@ -163,7 +194,7 @@ def test_workspace_sizes_are_consistent(L):
 
 def test_timing_hook_arguments(L):
     assert L.LIB.ip_time_next_launch(99, FAKE, FAKE) == L.IP_EINVAL
-    assert L.LIB.ip_time_next_launch(6, FAKE, FAKE) == L.IP_EINVAL
+    assert L.LIB.ip_time_next_launch(7, FAKE, FAKE) == L.IP_EINVAL
     assert L.LIB.ip_time_next_launch(2, FAKE, None) == L.IP_EINVAL      # one event only
-    assert L.LIB.ip_time_next_launch(5, FAKE, FAKE) == L.IP_OK          # split combine is hookable
+    assert L.LIB.ip_time_next_launch(6, FAKE, FAKE) == L.IP_OK          # append is hookable
     assert L.LIB.ip_time_next_launch(0, None, None) == L.IP_OK          # disarms all

@@ -14,7 +14,7 @@ import torch
 from long_context_sparse_19_amd.configs import (
     TINY, DECODE, PREFILL, MAX_CTX, RAGGED, scaled_down,
 )
-from long_context_sparse_19_amd.inputs import make_inputs
+from long_context_sparse_19_amd.inputs import make_inputs, new_tokens
 from oracle import oracle as O
 from tests import parity as P
 
@@ -259,6 +259,72 @@ def test_determinism():
 
 
 # ---------------------------------------------------------------- full sizes
+# ---------------------------------------------------------------- decode append
+_RAGGED_SMALL = scaled_down(RAGGED, 8192, batch=5, min_blocks=50)
+APPEND = {
+    # new tokens at every position of a block (only a length % 4 == 0 pools)
+    "decode_positions": (scaled_down(DECODE, 1024, batch=4), lambda L: L - np.arange(4)),
+    "ragged_paged": (_RAGGED_SMALL, lambda L: L),
+    "ragged_paged_open_block": (_RAGGED_SMALL, lambda L: L - 1),
+    "tiny_f32": (TINY, lambda L: L),
+    "tiny_f32_open_block": (TINY, lambda L: L - 3),
+    "decode_full": (DECODE, lambda L: L),
+}
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", list(APPEND))
+def test_append_parity(name):
+    """indexpool_append against the oracle's cache growth: the new rows, the
+    per-token fp8 key, the logit, and the block it completes; nothing else moves."""
+    D = _dev()
+    w, lens = APPEND[name]
+    inp = make_inputs(w)
+    inp.seq_lens = np.asarray(lens(inp.seq_lens), dtype=np.int32)
+    log(f"[case] append {name} B={w.batch} lens={inp.seq_lens[:4].tolist()}")
+    d = D.upload(inp)
+    new = new_tokens(w, len(inp.seq_lens), seed=7)
+    exp = O.append(inp, new["kv_new"], new["key_new"], new["logit_new"])
+    fp8 = inp.idx_scale is not None
+    pooled0, keys0 = _bits(d.pooled.data), _bits(d.keys.data)
+    D.append(d, D.NewTokens(new))
+    torch.cuda.synchronize()
+    kv, keys, pooled, logits = _bits(d.kv.data), _bits(d.keys.data), _bits(d.pooled.data), d.logits.cpu().numpy()
+    v = None if d.v is None else d.v.data.cpu().numpy()
+    ksc = d.keys.scale.cpu().numpy() if fp8 else None
+    psc = d.pooled.scale.cpu().numpy() if fp8 else None
+    prows, krows = [], []
+    for b, e in enumerate(exp):
+        row = e["row"]
+        krows.append(row)
+        assert np.array_equal(kv[row], e["kv"]), f"seq {b}: kv row"
+        if v is not None:
+            assert np.array_equal(v[row], new["v_new"][b]), f"seq {b}: v row"
+        assert logits[row] == np.float32(e["logit"])
+        if fp8:
+            P.check_pooled_fp8(keys[row][None], ksc[row][None], e["key"][None], np.array([e["sigma"]]),
+                               e["v"][None], np.abs(e["v"])[None], [0])
+        else:
+            assert np.array_equal(keys[row], new["key_new"][b])
+        if "prow" in e:
+            pr = e["prow"]
+            prows.append(pr)
+            if fp8:
+                P.check_pooled_fp8(pooled[pr][None], psc[pr][None], e["pooled"][None], np.array([e["psigma"]]),
+                                   e["pv"][None], e["pmag"][None], [0])
+            else:
+                np.testing.assert_allclose(pooled[pr], e["pooled"], rtol=0, atol=1e-5 * np.abs(e["pooled"]).max())
+    # nothing else changed
+    other = np.setdiff1d(np.arange(pooled.shape[0]), prows)
+    assert np.array_equal(pooled[other], pooled0[other])
+    other = np.setdiff1d(np.arange(keys.shape[0]), krows)
+    assert np.array_equal(keys[other], keys0[other])
+    log(f"  append ok ({len(prows)} blocks pooled)")
+
+
 @pytest.mark.parametrize("w", [DECODE, MAX_CTX, RAGGED], ids=["decode", "max_ctx", "ragged"])
 def test_full_size_decode(w):
     full_case(w, keep_scores=False)

@@ -323,3 +323,90 @@ def test_end_to_end_all_blocks_equals_dense_causal():
     q = bf16_bits_to_f32(inp.q).astype(np.float64)
     ref = _sdpa_causal(q, KV, KV[:, : w.dv].copy(), w.scale, inp.q_pos.astype(np.int64))
     np.testing.assert_allclose(Os, ref, rtol=1e-11, atol=1e-11)
+
+
+# --------------------------------------------------------------------------- decode append
+def test_quantize_token_closed_form():
+    c = 0.37
+    x = np.zeros((2, 128))
+    x[0, :4] = [448 * c, -224 * c, 1.5 * c, -0.0]
+    codes, sigma, v = O.quantize_tokens(x)
+    assert sigma[0] == pytest.approx(c, rel=1e-15) and sigma[1] == 0.0
+    assert list(codes[0, :3]) == [0x7E, 0xF6, 0x3C]      # +448, -224, +1.5
+    assert codes[0, 3] == 0x80 and not codes[0, 4:].any()   # -0.0 keeps its sign
+    assert not codes[1].any()
+
+
+def test_quantize_token_matches_torch_and_error_bound():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((64, 128))
+    x[::7] *= 8.0                                     # some larger rows
+    codes, sigma, v = O.quantize_tokens(x)
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # away from rounding midpoints the float32 cast in torch cannot change the code
+    val = O.fp8_decode(codes)
+    near_tie = np.zeros_like(v, dtype=bool)
+    for delta in (1, -1):
+        other = O.fp8_decode(np.clip(codes.astype(np.int64) + delta, 0, 255).astype(np.uint8))
+        near_tie |= np.abs(np.abs(v) - (np.abs(val) + np.abs(other)) / 2) <= 1e-6 * np.abs(v)
+    assert np.array_equal(codes[~near_tie], ref[~near_tie])
+    err = np.abs(sigma[:, None] * val - x)
+    bound = np.maximum(2.0 ** -4 * np.abs(x), sigma[:, None] * 2.0 ** -10)
+    assert np.all(err <= bound * (1 + 1e-12))
+    assert np.all(np.abs(val).max(axis=1) == 448.0)
+
+
+def _append_state(fp8, paged=False, seed=5):
+    """A small cache (3 sequences of up to 16 tokens) and new tokens for append."""
+    from types import SimpleNamespace
+    rng = np.random.default_rng(seed)
+    B, S, D = 3, 16, 128 if fp8 else 8
+    lens = np.array([8, 7, 13], dtype=np.int32)
+    if fp8:
+        keys, scale = O.quantize_tokens(rng.standard_normal((B * S, D)))[:2]
+    else:
+        keys, scale = rng.standard_normal((B * S, D)), None
+    st = SimpleNamespace(idx_keys=keys, idx_scale=scale, pool_logits=rng.standard_normal(B * S),
+                         seq_lens=lens, page_table=None, seq_stride=S, page_tokens=0)
+    if paged:
+        perm = rng.permutation(B * S // 8).reshape(B, S // 8)     # 8-token pages, shuffled
+        st.page_table, st.page_tokens = perm.astype(np.int32), 8
+    new = dict(kv_new=rng.standard_normal((B, 576)), key_new=rng.standard_normal((B, D)),
+               logit_new=rng.standard_normal(B))
+    return st, new
+
+
+@pytest.mark.parametrize("fp8", [True, False])
+@pytest.mark.parametrize("paged", [False, True])
+def test_append_writes_the_new_token_and_pools_completed_blocks(fp8, paged):
+    """Growth then pooling agree with a cache build: writing the new token into the
+    cache and running compress over it gives the pooled block that append reports;
+    only a length that is a multiple of 4 pools, and the token goes to row L - 1."""
+    st, new = _append_state(fp8, paged)
+    res = O.append(st, **new)
+    for b, e in enumerate(res):
+        L = int(st.seq_lens[b])
+        assert e["row"] == int(O.token_rows(st, b, L - 1))
+        assert ("prow" in e) == (L % 4 == 0)
+        assert e["logit"] == new["logit_new"][b]
+        if fp8:
+            c, s, _ = O.quantize_tokens(new["key_new"][b][None])
+            assert np.array_equal(e["key"], c[0]) and e["sigma"] == s[0]
+    # the cache after the step, pooled by the cache build
+    grown = type(st)(**vars(st))
+    grown.idx_keys = st.idx_keys.copy()
+    grown.pool_logits = st.pool_logits.copy()
+    if fp8:
+        grown.idx_scale = st.idx_scale.copy()
+    for e in res:
+        grown.idx_keys[e["row"]] = e["key"]
+        grown.pool_logits[e["row"]] = e["logit"]
+        if fp8:
+            grown.idx_scale[e["row"]] = e["sigma"]
+    pooled, sigma, *_ = O.compress(grown)
+    e = res[0]                                        # L = 8 completes block 1
+    assert e["prow"] == int(O.pooled_rows(st, 0, 1))
+    if fp8:
+        assert np.array_equal(pooled[e["prow"]], e["pooled"]) and sigma[e["prow"]] == e["psigma"]
+    else:
+        np.testing.assert_allclose(pooled[e["prow"]], e["pooled"], rtol=1e-15, atol=0)
