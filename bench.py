@@ -2,9 +2,10 @@
 """Benchmark of the IndexPool indexer + block-sparse attention path on one MI355X.
 
 One step = one pass of the whole path over one batch:
-  decode:  pool the block each query just completed (indexpool_compress), score
-           every earlier pooled block and select the top-k (index_score_topk),
-           attend over the selected tokens (sparse_attn_decode);
+  decode:  append each sequence's new token to the caches and pool the block it
+           completes (indexpool_append), score every earlier pooled block and
+           select the top-k (index_score_topk), attend over the selected tokens
+           (sparse_attn_decode);
   prefill: pool the chunk's new blocks, score/select for every query token,
            sparse_attn_prefill.
 The default workload is decode of 8 sequences x 131072 tokens with top-512
@@ -56,7 +57,10 @@ def algorithmic_bytes(inp, w):
       attention + |U|*dk*2 (gathered latent rows, |U| = selected tokens <= p)
                 + H*dk*2 + H*dv*2     bf16 query in, bf16 output
                 + k*4                 ids read
-    plus the pooling of the new blocks: 4*(D_I + 4 + 4) read + (D_I + 4) written per block.
+    plus, for decode, each sequence's cache growth: the new token's latent row, key
+    and logit read and written, and its completed block pooled (3 cached tokens read,
+    one pooled row written); for prefill the pooling of the chunk's new blocks,
+    4*(D_I + 4 + 4) read + (D_I + 4) written per block.
     """
     import numpy as np
     D, HI, H = w.idx_dim, w.idx_heads, w.n_heads
@@ -69,8 +73,15 @@ def algorithmic_bytes(inp, w):
     score_b = n * (D + 4) + HI * D * 2 + HI * 4
     attn_b = U * w.dk * 2 + H * w.dk * 2 + H * w.dv * 2 + k * 4
     sel_b = k * 4
-    new_blocks = len(inp.seq_lens) if w.mode == "decode" else w.n_query // 4
-    pool_b = new_blocks * (4 * (D + 4 + 4) + D + 4)
+    fp8 = inp.idx_scale is not None
+    if w.mode == "decode":
+        kv_row = w.dk * (2 if w.attn_dtype == "bf16" else 4) + (0 if w.attn_dtype == "bf16" else w.dv * 4)
+        key_in, key_out = (D * 2, D + 4) if fp8 else (D * 4, D * 4)
+        tok_b = 3 * ((D + 4) if fp8 else D * 4) + 3 * 4          # cached tokens of the block
+        grow = 2 * kv_row + key_in + key_out + 4 + 4 + tok_b + key_out
+        pool_b = len(inp.seq_lens) * grow
+    else:
+        pool_b = (w.n_query // 4) * (4 * (D + 4 + 4) + D + 4)
     return dict(score=int(score_b.sum()), select=int(sel_b * len(n)), attention=int(attn_b.sum()),
                 pool=int(pool_b), total=int(score_b.sum() + sel_b * len(n) + attn_b.sum() + pool_b),
                 U=U)
@@ -94,7 +105,8 @@ def kernel_bytes(inp, w, ab):
     nq = len(n)
     part = _lib.LIB.sparse_attn_workspace_bytes(nq, w.n_heads, w.dv, k, _lib.IP_BF16 if w.attn_dtype == "bf16" else _lib.IP_F32)
     comb = part + nq * w.n_heads * (w.dv * 2 + 4) if part else None
-    return {"compress": ab["pool"], "score": ab["score"], "topk": int(topk.sum()),
+    grow = "append" if w.mode == "decode" else "compress"
+    return {grow: ab["pool"], "score": ab["score"], "topk": int(topk.sum()),
             "attention": ab["attention"], "combine": comb}
 
 
@@ -109,7 +121,7 @@ def _chunk_size(max_seq_len):
 
 # the sources each kernel is built from (the HBM counters in profiles/ are tied to them)
 _KERNEL_SOURCES = {"attention": "attn.hip", "combine": "attn.hip", "score": "score.hip", "topk": "topk.hip",
-                   "compress": "compress.hip"}
+                   "compress": "compress.hip", "append": "compress.hip"}
 
 
 def _source_hash(kind):
@@ -140,10 +152,13 @@ def attention_flops(U, w):
 
 
 def cpu_baseline(inp, w, budget_s=12.0):
-    """The oracle's step (pool the new block, score, select, attend) on whole query
-    rows of the same workload, for about budget_s seconds of CPU time."""
+    """The oracle's step (decode: append the new token and pool its block; prefill:
+    pool the row's block; then score, select, attend) on whole query rows of the
+    same workload, for about budget_s seconds of CPU time."""
     import numpy as np
     from oracle import oracle as O
+    from long_context_sparse_19_amd.inputs import new_tokens
+    new = new_tokens(w, len(inp.seq_lens), seed=w.seed) if w.mode == "decode" else None
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -173,10 +188,13 @@ def cpu_baseline(inp, w, budget_s=12.0):
             b = int(inp.q_seq[r])
             p = int(inp.q_pos[r])
             b_q = p // 4
-            prow = O.pooled_rows(inp, b, np.array([b_q]))
-            tok = 4 * prow[:, None] + np.arange(4)[None]
-            if inp.idx_scale is not None:
-                O.pool_fp8(inp.idx_keys[tok], inp.idx_scale[tok], inp.pool_logits[tok])
+            if new is not None:
+                O.append(inp, new["kv_new"], new["key_new"], new["logit_new"], only={b})
+            else:
+                prow = O.pooled_rows(inp, b, np.array([b_q]))
+                tok = 4 * prow[:, None] + np.arange(4)[None]
+                if inp.idx_scale is not None:
+                    O.pool_fp8(inp.idx_keys[tok], inp.idx_scale[tok], inp.pool_logits[tok])
             keys = vals[O.pooled_rows(inp, b, np.arange(b_q))]
             S = O.score(O._to_f64(inp.q_idx[r]), inp.gates[r], keys)
             ids = O.select(S, b_q, w.top_k)
@@ -189,8 +207,8 @@ def cpu_baseline(inp, w, budget_s=12.0):
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "query-tokens/s", "cores": blas_threads,
             "kind": "oracle", "host_cores_available": cores,
-            "sample": f"{done} query rows of the {w.name} workload (sequences {seqs}), oracle pooling of the "
-                      f"new block + float64 scoring over every earlier block + selection + attention, "
+            "sample": f"{done} query rows of the {w.name} workload (sequences {seqs}), oracle cache growth / "
+                      f"pooling of the new block + float64 scoring over every earlier block + selection + attention, "
                       f"{dt:.1f} s"}
 
 
@@ -235,7 +253,7 @@ def main():
     import torch
     from long_context_sparse_19_amd import _lib, device as D
     from long_context_sparse_19_amd.configs import WORKLOADS
-    from long_context_sparse_19_amd.inputs import make_inputs
+    from long_context_sparse_19_amd.inputs import make_inputs, new_tokens
 
     w = WORKLOADS[args.workload]
     t_gen = time.perf_counter()
@@ -260,8 +278,8 @@ def main():
     # library otherwise scores in passes of at most 256 MB)
     wss = [D.Workspaces(d, keep_scores=(w.mode == "prefill")) for d in reps]
     if w.mode == "decode":
-        begin = torch.from_numpy((inp.q_pos // 4).astype(np.int32)).cuda()
-        max_new = 1
+        # each sequence's new token (at seq_lens - 1, the query position)
+        toks = D.NewTokens(new_tokens(w, len(inp.seq_lens), seed=w.seed))
     else:
         begin = torch.full((1,), int(inp.q_pos[0]) // 4, dtype=torch.int32, device="cuda")
         max_new = (int(inp.q_pos[-1]) // 4) - (int(inp.q_pos[0]) // 4) + 1
@@ -270,7 +288,10 @@ def main():
 
     def step(i):
         d, ws = reps[i % R], wss[i % R]
-        D.compress(d, block_begin=begin, max_blocks=max_new)
+        if w.mode == "decode":
+            D.append(d, toks)
+        else:
+            D.compress(d, block_begin=begin, max_blocks=max_new)
         D.score_topk(d, ws)
         D.attention(d, ws)
 
@@ -316,7 +337,7 @@ def main():
     # launch carrying HIP events that receive its dispatch start / end times (the
     # timestamps a kernel trace reports), on the stream the kernel runs on
     kbytes = kernel_bytes(inp, w, ab)
-    ids = {"compress": _lib.K_COMPRESS, "score": _lib.K_SCORE, "topk": _lib.K_TOPK,
+    ids = {"compress": _lib.K_COMPRESS, "append": _lib.K_APPEND, "score": _lib.K_SCORE, "topk": _lib.K_TOPK,
            "attention": _lib.K_ATTN, "combine": _lib.K_COMBINE}
     ids = {n: kid for n, kid in ids.items() if kbytes.get(n)}     # the kernels this workload launches
     evk = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]

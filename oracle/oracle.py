@@ -204,7 +204,7 @@ def quantize_tokens(x):
     return codes, sigma, v
 
 
-def append(inp, kv_new, key_new, logit_new):
+def append(inp, kv_new, key_new, logit_new, only=None):
     """What one decode step's cache growth writes (R8), per sequence.
 
     inp holds the caches before the step (idx_keys, idx_scale, pool_logits and the
@@ -212,11 +212,12 @@ def append(inp, kv_new, key_new, logit_new):
     (bf16 bit patterns or floats), logit_new [B].  Returns one dict per sequence with
     a new token: row, kv, key (codes, or floats for a float cache), sigma, v (x /
     sigma), logit, and when a block completes prow, pooled, psigma, pv, pmag (the
-    outputs of pool_fp8, or the float pooled key)."""
+    outputs of pool_fp8, or the float pooled key).  `only`: a subset of sequences
+    (the others get None)."""
     out = []
     fp8 = inp.idx_scale is not None
     for b, L in enumerate(np.asarray(inp.seq_lens, dtype=np.int64)):
-        if L < 1:
+        if L < 1 or (only is not None and b not in only):
             out.append(None)
             continue
         t = int(L) - 1
