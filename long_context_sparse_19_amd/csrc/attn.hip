@@ -549,6 +549,7 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(AttnArgs a) {
   __shared__ __align__(16) float qs[F_MAXH * F_MAXD];
   __shared__ float ps[F_MAXH][F_TILE];
   __shared__ int64_t rows[F_TILE];
+  __shared__ __align__(16) float vs[F_TILE / 2][F_MAXD + 4];   // V rows of half a tile
   const int r = a.row0 + blockIdx.x;
   const RowCtx c = row_ctx(a, r);
   const int H = a.heads, dk = a.dk, dv = a.dv, dk4 = dk >> 2;
@@ -618,18 +619,26 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(AttnArgs a) {
         acc[i][1] *= al;
       }
     }
-    __syncthreads();
-    // O += P V over the tile
+    // O += P V over the tile.  V rows are staged through LDS half a tile at a time
+    // (every row load of a half is in flight at once; rows F_MAXD + 4 floats apart)
+    const int dv4 = dv >> 2;
+    for (int hf = 0; hf < 2; ++hf) {
+      __syncthreads();                             // P written / previous half read
+      for (int i = threadIdx.x; i < (F_TILE / 2) * dv4; i += NT) {
+        const int k = i / dv4, ch = i - k * dv4;
+        *(float4*)&vs[k][4 * ch] = ((const float4*)(a.v + rows[hf * (F_TILE / 2) + k] * a.v_stride))[ch];
+      }
+      __syncthreads();
 #pragma unroll 4
-    for (int k = 0; k < F_TILE; ++k) {
-      const float* vr = (const float*)(a.v + rows[k] * a.v_stride);
-      const float v0 = vr[d0], v1 = vr[d1];
+      for (int k = 0; k < F_TILE / 2; ++k) {
+        const float v0 = vs[k][d0], v1 = vs[k][d1];
 #pragma unroll
-      for (int i = 0; i < F_HPW; ++i) {
-        const int h = min(wv + 4 * i, H - 1);
-        const float pk = ps[h][k];
-        acc[i][0] = fmaf(pk, v0, acc[i][0]);
-        acc[i][1] = fmaf(pk, v1, acc[i][1]);
+        for (int i = 0; i < F_HPW; ++i) {
+          const int h = min(wv + 4 * i, H - 1);
+          const float pk = ps[h][hf * (F_TILE / 2) + k];
+          acc[i][0] = fmaf(pk, v0, acc[i][0]);
+          acc[i][1] = fmaf(pk, v1, acc[i][1]);
+        }
       }
     }
   }
