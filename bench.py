@@ -297,8 +297,8 @@ def main():
 
     graphs = None
     if not args.eager:
-        # one HIP graph per replica holding one whole step (a forked branch for the
-        # decode pooling, which the rest of the step does not read, measured slower)
+        # one HIP graph per replica holding one whole step (running the decode append on
+        # a forked stream beside scoring measured 71 us per step against 60 serial)
         graphs = []
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
