@@ -182,7 +182,7 @@ hipError_t launch_score_fp8_bf16(const ScoreArgs& a, hipStream_t s) {
   const unsigned gx = (a.max_blocks + KEYS_PER_WG - 1) / KEYS_PER_WG;
   if (a.q_seq && a.n_rows >= 64) {
     // prefill: consecutive rows are query tokens of one sequence and share its keys
-    constexpr int R = 16;
+    constexpr int R = 32;
     launch(K_SCORE, score_fp8_bf16_kernel<R>, dim3(gx, (a.n_rows + R - 1) / R), dim3(NT), s, a);
   } else {
     launch(K_SCORE, score_fp8_bf16_kernel<1>, dim3(gx, a.n_rows), dim3(NT), s, a);
