@@ -54,7 +54,8 @@ def algorithmic_bytes(inp, w):
       scoring   n*(D_I + 4)          pooled fp8 codes + fp32 scale
                 + H_I*D_I*2 + H_I*4   bf16 query, fp32 gates
       selection k*4                  ids written
-      attention + |U|*dk*2 (gathered latent rows, |U| = selected tokens <= p)
+      attention + |U|*dk*2 (gathered latent rows, |U| = selected tokens <= p;
+                            |U|*(dk + 4) for the fp8 latent tier: codes + scale)
                 + H*dk*2 + H*dv*2     bf16 query in, bf16 output
                 + k*4                 ids read
     plus, for decode, each sequence's cache growth: the new token's latent row, key
@@ -71,14 +72,16 @@ def algorithmic_bytes(inp, w):
     own = inp.q_pos.astype(np.int64) % 4 + 1
     U = (kp - 1) * 4 + own
     score_b = n * (D + 4) + HI * D * 2 + HI * 4
-    attn_b = U * w.dk * 2 + H * w.dk * 2 + H * w.dv * 2 + k * 4
+    row_b = (w.dk + 4) if w.latent_fp8 else w.dk * 2
+    attn_b = U * row_b + H * w.dk * 2 + H * w.dv * 2 + k * 4
     sel_b = k * 4
     fp8 = inp.idx_scale is not None
     if w.mode == "decode":
-        kv_row = w.dk * (2 if w.attn_dtype == "bf16" else 4) + (0 if w.attn_dtype == "bf16" else w.dv * 4)
+        kv_in = w.dk * (2 if w.attn_dtype == "bf16" else 4) + (0 if w.attn_dtype == "bf16" else w.dv * 4)
+        kv_out = (w.dk + 4) if w.latent_fp8 else kv_in                # fp8 tier: codes + scale
         key_in, key_out = (D * 2, D + 4) if fp8 else (D * 4, D * 4)
         tok_b = 3 * ((D + 4) if fp8 else D * 4) + 3 * 4          # cached tokens of the block
-        grow = 2 * kv_row + key_in + key_out + 4 + 4 + tok_b + key_out
+        grow = kv_in + kv_out + key_in + key_out + 4 + 4 + tok_b + key_out
         pool_b = len(inp.seq_lens) * grow
     else:
         pool_b = (w.n_query // 4) * (4 * (D + 4 + 4) + D + 4)
@@ -234,7 +237,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "max_ctx", "ragged", "prefill", "tiny"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "max_ctx", "ragged", "prefill", "tiny", "decode_fp8kv"])
     ap.add_argument("--replicas", type=int, default=0, help="rotated input copies (0 = auto, >= 1 GiB touched)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of HIP graphs")
@@ -269,7 +272,7 @@ def main():
                                       "keys": _lib.Cache(base.keys.data.clone(), None if base.keys.scale is None else base.keys.scale.clone()),
                                       "logits": base.logits.clone(),
                                       "pooled": _lib.Cache(base.pooled.data.clone(), None if base.pooled.scale is None else base.pooled.scale.clone()),
-                                      "kv": _lib.Cache(base.kv.data.clone()),
+                                      "kv": _lib.Cache(base.kv.data.clone(), None if base.kv.scale is None else base.kv.scale.clone()),
                                       "v": None if base.v is None else _lib.Cache(base.v.data.clone()),
                                       "q": base.q.clone(), "q_idx": base.q_idx.clone(), "gates": base.gates.clone()}))
     for d in reps:
@@ -391,7 +394,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "context": w.seq_len, "query_rows": w.n_rows,
-                   "top_k_blocks": w.top_k, "index_keys": w.idx_key_dtype, "latent": w.attn_dtype,
+                   "top_k_blocks": w.top_k, "index_keys": w.idx_key_dtype, "latent": "fp8" if w.latent_fp8 else w.attn_dtype,
                    "replicas": R, "launch": "eager" if args.eager else "hip-graph",
                    "parallelism": "single GPU"},
         "hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,

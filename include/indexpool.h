@@ -117,7 +117,10 @@ ip_status indexpool_compress(const ip_seqs* seqs, const int32_t* block_begin, in
  *
  * seq_lens[b] already counts the new token, which goes to position
  * t = seq_lens[b] - 1 of sequence b (sequences with seq_lens[b] < 1 are skipped):
- *     kv[t]     = kv_new[b]       row copy (BF16 or F32 cache, same dtype as kv_new)
+ *     kv[t]     = kv_new[b]       row copy (BF16 or F32 cache, same dtype as kv_new);
+ *                                 FP8 cache (the lower-precision latent tier): kv_new
+ *                                 is BF16, quantised per token like the FP8 keys
+ *                                 below into codes and kv->scale[t]
  *     v[t]      = v_new[b]        only when v is not NULL (separate V cache)
  *     keys[t]   = key_new[b]      FP8 keys: sigma_t = max_d |x_d| / 448 and codes
  *                                 e4m3fn(x / sigma_t), rounded to nearest even and
@@ -128,7 +131,8 @@ ip_status indexpool_compress(const ip_seqs* seqs, const int32_t* block_begin, in
  * into `pooled` exactly as indexpool_compress pools it.
  *
  *  kv_new   device [batch, kv->row_dim], kv->dtype; kv->row_dim * element size a
- *           multiple of 16 bytes (the same for v_new / v)
+ *           multiple of 16 bytes (the same for v_new / v).  FP8 kv: kv_new BF16,
+ *           8-byte aligned, kv->row_dim a multiple of 4 and <= 1024, v NULL
  *  key_new  device [batch, keys->row_dim], key_dtype BF16 or F32 (F32 for F32 keys)
  *  logit_new  device [batch] fp32;  logits  device [token rows] fp32
  *  keys, pooled  as in indexpool_compress (FP8 with scales, row_dim 128; or F32)
@@ -191,6 +195,11 @@ ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_se
  *   BF16 latent (MQA): q BF16 [n_q, 64, 576]; k is the 576-dim BF16 latent cache,
  *     v must be NULL: V is the first 512 dims of the same rows (dk 576, dv 512);
  *     out BF16 [n_q, 64, 512] (round to nearest even).
+ *   FP8 latent tier (reading notes, section 4 "The serving stack": FP8 as a cache
+ *     tier): as BF16 latent, but k is FP8 e4m3fn codes with k->scale[row] per token
+ *     row, K_t = scale_t * code_t; the products run in bf16 with fp32 accumulation
+ *     (codes widen to bf16 exactly; P_t * scale_t is rounded to bf16 for P V).
+ *   Latent paths: token rows (physical row indices) must be below 2^29.
  *   F32: q F32 [n_q, n_heads, dk]; separate F32 k [rows, dk] and v [rows, dv]
  *     caches; n_heads <= 16, dk, dv <= 128 and multiples of 4; out F32.
  *  sel_idx  device [n_q, top_k] ascending block ids, -1 entries ignored

@@ -64,6 +64,7 @@ class Workload:
     page_tokens: int = 0      # 0 = contiguous cache
     salient_frac: float = 0.0  # fraction of index-key rows whose scale is x8
     salient_mult: float = 8.0
+    latent_fp8: bool = False  # latent cache in fp8 e4m3fn with a per-token scale
 
     @property
     def n_rows(self) -> int:
@@ -95,7 +96,10 @@ MAX_CTX = _g1("max_ctx", mode="decode", batch=1, seq_len=1048576, seed=3, salien
 RAGGED = _g1("ragged", mode="decode", batch=64, seq_len=32768, ragged=True,
              min_blocks=1024, page_tokens=64, seed=4)
 
-WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, MAX_CTX, RAGGED)}
+# The lower-precision latent tier: decode as above over an fp8 latent cache
+DECODE_FP8KV = DECODE.with_(name="decode_fp8kv", latent_fp8=True)
+
+WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, MAX_CTX, RAGGED, DECODE_FP8KV)}
 
 
 def scaled_down(w: Workload, seq_len: int, batch: Optional[int] = None,

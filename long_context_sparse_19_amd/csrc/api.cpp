@@ -223,9 +223,13 @@ ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cac
     if (ip_status st = check_cache(v, fn, "v")) return st;
     if (!v_new) return fail(IP_EINVAL, "%s: v_new is NULL while v is given", fn);
   }
-  if (kv->dtype == IP_FP8_E4M3FN || (v && v->dtype == IP_FP8_E4M3FN))
-    return fail(IP_EUNSUPPORTED, "%s: kv / v caches must be BF16 or F32", fn);
-  const int kv_bytes = kv->row_dim * elem_bytes(kv->dtype);
+  const bool kv8 = kv->dtype == IP_FP8_E4M3FN;
+  if (v && v->dtype == IP_FP8_E4M3FN) return fail(IP_EUNSUPPORTED, "%s: a separate v cache must be BF16 or F32", fn);
+  if (kv8 && (v || kv->row_dim % 4 || kv->row_dim > 1024))
+    return fail(IP_EUNSUPPORTED, "%s: an FP8 kv cache needs v = NULL and row_dim a multiple of 4, <= 1024", fn);
+  if (kv8 && ((uintptr_t)kv_new & 7))
+    return fail(IP_EINVAL, "%s: kv_new must be 8-byte aligned", fn);
+  const int kv_bytes = kv8 ? 0 : kv->row_dim * elem_bytes(kv->dtype);
   const int v_bytes = v ? v->row_dim * elem_bytes(v->dtype) : 0;
   if (kv_bytes % 16 || v_bytes % 16) return fail(IP_EUNSUPPORTED, "%s: kv / v rows must be whole 16-byte chunks", fn);
   if (keys->dtype != pooled->dtype || keys->row_dim != pooled->row_dim)
@@ -247,6 +251,8 @@ ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cac
   a.kv = (uint8_t*)kv->data;
   a.kv_stride = kv->row_stride;
   a.kv_row_bytes = kv_bytes;
+  a.kv_scale = kv8 ? kv->scale : nullptr;
+  a.kv_dim = kv->row_dim;
   a.v_new = (const uint8_t*)v_new;
   a.v = v ? (uint8_t*)v->data : nullptr;
   a.v_stride = v ? v->row_stride : 0;
@@ -387,10 +393,14 @@ static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, c
   a.heads = n_heads;
   a.dk = dk;
   a.dv = dv;
+  a.k_scale = nullptr;
   if (q_dtype == IP_BF16) {
-    if (k->dtype != IP_BF16 || n_heads != ip::LAT_H || dk != ip::LAT_DK || dv != ip::LAT_DV || k->row_dim < ip::LAT_DK)
-      return fail(IP_EUNSUPPORTED, "%s: BF16 attention needs 64 heads, dk 576, dv 512 over a BF16 latent cache", fn);
+    if ((k->dtype != IP_BF16 && k->dtype != IP_FP8_E4M3FN) || n_heads != ip::LAT_H || dk != ip::LAT_DK ||
+        dv != ip::LAT_DV || k->row_dim < ip::LAT_DK)
+      return fail(IP_EUNSUPPORTED, "%s: BF16 attention needs 64 heads, dk 576, dv 512 over a BF16 or FP8 latent cache", fn);
     if (v) return fail(IP_EUNSUPPORTED, "%s: BF16 latent attention takes V from the latent rows; pass v = NULL", fn);
+    if (!seqs->page_table && (int64_t)seqs->batch * seqs->seq_stride > (int64_t(1) << 29))
+      return fail(IP_EUNSUPPORTED, "%s: latent attention addresses token rows below 2^29 (batch * seq_stride too large)", fn);
     if (n_q > 65535) return fail(IP_EUNSUPPORTED, "%s: n_q > 65535", fn);
     const AttnPlan p = attn_plan(n_q, n_heads, dv, top_k, q_dtype);
     if (p.bytes > 0 && (!ws || ws_bytes < p.bytes))
@@ -402,6 +412,10 @@ static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, c
     a.blocks_per_split = p.blocks_per_split;
     a.part_o = (uint16_t*)ws;
     a.part_ml = p.n_split > 1 ? (float*)(a.part_o + (size_t)n_q * p.n_split * n_heads * dv) : nullptr;
+    if (k->dtype == IP_FP8_E4M3FN) {
+      a.k_scale = k->scale;
+      return device_status(ip::launch_attn_fp8(a, stream), fn);
+    }
     return device_status(ip::launch_attn_bf16(a, stream), fn);
   }
   if (q_dtype == IP_F32) {

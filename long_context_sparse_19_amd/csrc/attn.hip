@@ -135,9 +135,35 @@ __device__ __forceinline__ BlockIds fetch_blocks(const RowCtx& c, int sb0, int s
 }
 
 __device__ __forceinline__ uint32_t block_entry(const AttnArgs& a, const RowCtx& c, int blk) {
-  if (blk >= 0 && blk * 4 <= c.p)
-    return (uint32_t)a.L.tok_row(c.b, (int64_t)blk * 4) | ((uint32_t)min(4, c.p - blk * 4 + 1) << VIS_SHIFT);
-  return (uint32_t)a.L.tok_row(c.b, (int64_t)(c.p >> 2) * 4);
+  const bool vis = blk >= 0 && blk * 4 <= c.p;
+  const int t0 = vis ? blk * 4 : (c.p >> 2) * 4;
+  return (uint32_t)a.L.tok_row(c.b, t0) | (vis ? (uint32_t)min(4, c.p - t0 + 1) << VIS_SHIFT : 0u);
+}
+
+// block_entry of N blocks at once: one branch on the layout around all N, so that
+// their page-table reads are in flight together (one wait instead of N)
+template <int N>
+__device__ __forceinline__ void block_entries(const AttnArgs& a, const RowCtx& c, const int (&blk)[N],
+                                              uint32_t (&out)[N]) {
+  uint32_t t0[N], vis[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bool v = blk[i] >= 0 && blk[i] * 4 <= c.p;
+    t0[i] = (uint32_t)(v ? blk[i] * 4 : (c.p >> 2) * 4);
+    vis[i] = v ? (uint32_t)min(4, c.p - (int)t0[i] + 1) << VIS_SHIFT : 0u;
+  }
+  if (a.L.page_table) {
+    const uint32_t pt = (uint32_t)a.L.page_tokens;
+    const int32_t* pr = a.L.page_table + (int64_t)c.b * a.L.max_pages;
+    int32_t pg[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) pg[i] = pr[t0[i] / pt];
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = ((uint32_t)pg[i] * pt + t0[i] % pt) | vis[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = (uint32_t)((int64_t)c.b * a.L.seq_stride + t0[i]) | vis[i];
+  }
 }
 
 __device__ __forceinline__ void build_block_table(const AttnArgs& a, const RowCtx& c, const BlockIds& ids, int sb0,
@@ -490,6 +516,361 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ fp8 latent tier
+// Latent rows stored as e4m3fn codes (576 bytes) with one fp32 scale per token;
+// K_t = sigma_t dec(code_t), V_t its first 512 dims.  Same work split and softmax
+// as the bf16 kernel; what changes:
+//  - a sub-tile buffer holds 64 rows of codes in 5 segments of the same layout
+//    (segment 4 = bytes 512 .. 575; its DMA reads those 64 bytes twice, so that
+//    every slot is filled from inside the row) and the 64 scales of the sub-tile
+//    arrive by one dword DMA issued by wave 0;
+//  - K fragments: one 16-byte read gives the codes of two k-steps, widened to bf16
+//    in registers (exact); q comes from global memory in the matching dim order
+//    (k-step 2p: dims 32p + 16lh .. +7, k-step 2p+1: the next 8);
+//  - S is multiplied by sigma_t per token (fp32), P carries sigma_t (P_t sigma_t in
+//    bf16) while l sums the unscaled P;
+//  - at the start of a step the 512 V dims of the sub-tile's codes are widened
+//    into a bf16 copy in the bf16 layout, and O += V^T P^T runs as in the bf16
+//    kernel.
+constexpr int NSEG8 = 5;
+constexpr int KVBUF8 = NSEG8 * SEGB;             // 40960 bytes
+constexpr int KV_LOADS8 = NSEG8 * 8 / NWA;       // 10 per wave
+constexpr int KPAIRS = LAT_DK / 32;              // 18 fragments of 16 codes (two k-steps)
+constexpr int VCH8 = LAT_DV / 16;                // 32 16-byte chunks of V codes per row
+
+struct SubtileSrc8 {
+  const uint8_t* row[2];
+  int cofs[2];                                   // byte of this lane's slot within a 128-byte piece
+};
+
+__device__ __forceinline__ SubtileSrc8 src8_from_rows(const AttnArgs& a, const uint32_t (&grow)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  SubtileSrc8 src;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = 8 * (2 * wv + h) + (lane >> 3);
+    src.row[h] = a.k + (uint64_t)grow[h] * a.k_stride;
+    src.cofs[h] = 16 * ((lane & 7) ^ kv_swz(t));
+  }
+  return src;
+}
+
+__device__ __forceinline__ SubtileSrc8 subtile_src8(const AttnArgs& a, const AttnShared& sh, int n) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t grow[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = 8 * (2 * wv + h) + (lane >> 3);
+    grow[h] = (lds_ld(&sh.brow[n * 16 + (t >> 2)]) & ROW_BITS) + (t & 3);
+  }
+  return src8_from_rows(a, grow);
+}
+
+// load k (0..9): segment k/2 of row half k%2
+__device__ __forceinline__ void load_column8(const SubtileSrc8& src, uint8_t* buf, int k) {
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = k >> 1, h = k & 1;
+  const int off = g < 4 ? 128 * g + src.cofs[h] : 512 + (src.cofs[h] & 48);
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src.row[h] + off),
+                                   (void __attribute__((address_space(3)))*)(buf + g * SEGB + (2 * wv + h) * 1024),
+                                   16, 0, 0);
+}
+
+// the scales of the sub-tile's 64 tokens: lane l brings that of token l (wave 0 only)
+__device__ __forceinline__ void load_scales(const float* src, float* sg) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)sg, 4, 0, 0);
+}
+
+__device__ __forceinline__ const float* scale_src(const AttnArgs& a, const AttnShared& sh, int n) {
+  const int lane = threadIdx.x & 63;
+  return a.k_scale + (lds_ld(&sh.brow[n * 16 + (lane >> 2)]) & ROW_BITS) + (lane & 3);
+}
+
+__global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
+  __shared__ AttnShared sh;
+  __shared__ __align__(16) uint8_t kv0[KVBUF8];
+  __shared__ __align__(16) uint8_t kv1[KVBUF8];
+  __shared__ __align__(16) uint8_t vb[LAT_DV / 64 * SEGB];   // bf16 V of the current sub-tile
+  __shared__ __align__(16) float sg0[SUBT];
+  __shared__ __align__(16) float sg1[SUBT];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int hb = wv & 1, th = wv >> 1;
+  const int bid = blockIdx.x;
+  if (bid >= a.n_rows * a.n_split) return;
+  const int split = bid % a.n_split;
+  const int rl = bid / a.n_split;
+  const int r = a.row0 + rl;
+  const RowCtx c = row_ctx(a, r);
+  const int sb0 = split * a.blocks_per_split;
+  const int send = min(a.top_k, sb0 + a.blocks_per_split);
+  const int nsub = (send - sb0 + 15) >> 4;
+  const int hs = 32 * hb + l32;
+
+  // prologue: the ids (block table entries, this lane's rows of sub-tiles 0 and 1,
+  // the tokens whose scales it brings), then every load at once: sub-tiles 0 and
+  // 1 with their scales and the query fragments
+  const BlockIds ids = fetch_blocks(c, sb0, send);
+  int pid[2][2], sid[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int bi = sb0 + 16 * n + ((8 * (2 * wv + h) + (lane >> 3)) >> 2);
+      pid[n][h] = bi < send ? c.sel[bi] : -1;
+    }
+    const int bi = sb0 + 16 * n + (lane >> 2);
+    sid[n] = bi < send ? c.sel[bi] : -1;
+  }
+  // entries: [0, 1] this thread's block-table entries, [2 + 2n + h] its source
+  // rows of sub-tile n, [6 + n] the token whose scale it brings
+  constexpr int NE = MAX_BLOCKS_PER_SPLIT / NTA;
+  static_assert(NE == 2, "two block-table entries per thread");
+  const int eb[8] = {ids.blk[0], ids.blk[1], pid[0][0], pid[0][1], pid[1][0], pid[1][1], sid[0], sid[1]};
+  uint32_t ent[8];
+  block_entries(a, c, eb, ent);
+  const int nbt = ((send - sb0 + 15) >> 4) << 4;
+  SubtileSrc8 src[2];
+  const float* ssrc[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    uint32_t grow[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = 8 * (2 * wv + h) + (lane >> 3);
+      grow[h] = (ent[2 + 2 * n + h] & ROW_BITS) + (t & 3);
+    }
+    src[n] = src8_from_rows(a, grow);
+    ssrc[n] = a.k_scale + (ent[6 + n] & ROW_BITS) + (lane & 3);
+  }
+  // the entries have landed before any DMA is issued (a use of a loaded register
+  // while LDS DMA is in flight would wait for every load)
+#pragma unroll
+  for (int k = 0; k < NE; ++k) asm volatile("" ::"v"(ent[k]));
+  if (nsub > 0) {
+    if (wv == 0) load_scales(ssrc[0], sg0);
+#pragma unroll
+    for (int k = 0; k < KV_LOADS8; ++k) load_column8(src[0], kv0, k);
+  }
+  if (nsub > 1) {
+    if (wv == 0) load_scales(ssrc[1], sg1);
+#pragma unroll
+    for (int k = 0; k < KV_LOADS8; ++k) load_column8(src[1], kv1, k);
+  }
+  // q fragments of head hs: qf[2p] = dims 32p + 16lh .. +7, qf[2p+1] = the next 8
+  bf16x8_t qf[2 * KPAIRS];
+  {
+    const uint8_t* qrow = (const uint8_t*)a.q + ((int64_t)r * LAT_H + hs) * (LAT_DK * 2) + 32 * lh;
+#pragma unroll
+    for (int p = 0; p < KPAIRS; ++p) {
+      qf[2 * p] = *(const bf16x8_t*)(qrow + 64 * p);
+      qf[2 * p + 1] = *(const bf16x8_t*)(qrow + 64 * p + 16);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    const int i = (int)threadIdx.x + k * NTA;
+    if (i < nbt) lds_st(&sh.brow[i], ent[k]);
+  }
+  if (threadIdx.x < 4) lds_st(&sh.need[threadIdx.x], 0);
+  wait_loads(0);
+  block_sync_lds();
+#pragma unroll
+  for (int s = 0; s < 2 * KPAIRS; ++s) asm volatile("" : "+a"(qf[s]));
+  const float cs = a.scale * LOG2E;
+
+  f32x16_t o[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[i][d] = f32x16_t{};
+  float ms = -INFINITY, mo[2] = {-INFINITY, -INFINITY};
+  float l_half = 0.f;
+
+  auto step = [&](const int n, const uint8_t* buf, const float* sgb, uint8_t* nxt, float* sgn) {
+    const bool fetch = n >= 1 && n + 1 < nsub;
+    const SubtileSrc8 fsrc = subtile_src8(a, sh, fetch ? n + 1 : n);
+    const float* fssrc = scale_src(a, sh, fetch ? n + 1 : n);
+    const u32x4_t bv0 = lds_ld((const u32x4_t*)&sh.brow[n * 16 + 8 * th]);
+    const u32x4_t bv1 = lds_ld((const u32x4_t*)&sh.brow[n * 16 + 8 * th + 4]);
+    // ---- widen the V codes of the sub-tile into vb (bf16 layout): token l of
+    //      the 64, chunks wv + 4i of its 32 16-code chunks
+    {
+      const int tt = lane;
+#pragma unroll
+      for (int i = 0; i < VCH8 / NWA; ++i) {
+        const int j = wv + NWA * i;
+        const u32x4_t w = *(const u32x4_t*)(buf + kv_off(tt, j));
+        *(bf16x8_t*)(vb + kv_off(tt, 2 * j)) = fp8x8_to_bf16x8_pk(w[0], w[1]);
+        *(bf16x8_t*)(vb + kv_off(tt, 2 * j + 1)) = fp8x8_to_bf16x8_pk(w[2], w[3]);
+      }
+    }
+    // ---- S^T[token, head] over the codes, as in the bf16 kernel with fragments of
+    //      two k-steps; sub-tile n+1 is fetched in between
+    f32x16_t sacc;
+    {
+      f32x16_t sa[2] = {f32x16_t{}, f32x16_t{}};
+      const int t = 32 * th + l32;
+      constexpr int KPF = 3;
+      u32x4_t kr[KPF];
+#pragma unroll
+      for (int p = 0; p < KPF; ++p) kr[p] = *(const u32x4_t*)(buf + kv_off(t, 2 * p + lh));
+      if (fetch && wv == 0) load_scales(fssrc, sgn);
+#pragma unroll
+      for (int p = 0; p < KPAIRS; ++p) {
+        const u32x4_t w = kr[p % KPF];
+        if (p + KPF < KPAIRS) kr[p % KPF] = *(const u32x4_t*)(buf + kv_off(t, 2 * (p + KPF) + lh));
+        sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8_pk(w[0], w[1]), qf[2 * p], sa[0], 0, 0, 0);
+        sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8_pk(w[2], w[3]), qf[2 * p + 1], sa[1], 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < KV_LOADS8; ++k)
+          if ((KPAIRS * k) / KV_LOADS8 == p && fetch) load_column8(fsrc, nxt, k);
+      }
+      sacc = sa[0] + sa[1];
+    }
+    // ---- per-token scales, masking, this half's tile maximum of head hs
+    f32x4v sgv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sgv[q] = *(const f32x4v*)(sgb + 32 * th + 8 * q + 4 * lh);
+    float tm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t e = q < 2 ? (lh ? bv0[2 * q + 1] : bv0[2 * q]) : (lh ? bv1[2 * q - 3] : bv1[2 * q - 4]);
+      const int vis = (int)(e >> VIS_SHIFT);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sacc[4 * q + u] = u < vis ? sacc[4 * q + u] * (cs * sgv[q][u]) : -INFINITY;
+        tm = fmaxf(tm, sacc[4 * q + u]);
+      }
+    }
+    tm = pair_max32(tm);
+    if (lh == 0) lds_st(&sh.tmax[th][hs], tm);
+    const bool need = __ballot(tm > ms + RESCALE_LOG2) != 0ull;
+    if (need && lane == 0) lds_st(&sh.need[wv], 1);
+    auto write_p = [&](float m) {
+      const float mu = m == -INFINITY ? 0.f : m;
+      float ls = 0.f;
+      uint8_t* pr = sh.p + hs * PROW + (32 * th + 4 * lh) * 2;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float pv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { pv[u] = exp2f(sacc[4 * q + u] - mu); ls += pv[u]; }
+        lds_st((uint2*)(pr + 16 * q), make_uint2(pack_bf16x2(pv[0] * sgv[q][0], pv[1] * sgv[q][1]),
+                                                 pack_bf16x2(pv[2] * sgv[q][2], pv[3] * sgv[q][3])));
+      }
+      return ls;
+    };
+    float ls = write_p(ms);
+    block_sync_lds();
+    bool moved = false;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) moved |= lds_ld(&sh.need[w]) != 0;
+    if (moved) {
+      const float msn = fmaxf(ms, fmaxf(lds_ld(&sh.tmax[0][hs]), lds_ld(&sh.tmax[1][hs])));
+      l_half *= ms == -INFINITY ? 0.f : exp2f(ms - msn);
+      ms = msn;
+      ls = write_p(ms);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int h = 32 * i + l32;
+        const float mon = fmaxf(mo[i], fmaxf(lds_ld(&sh.tmax[0][h]), lds_ld(&sh.tmax[1][h])));
+        const float al = mo[i] == -INFINITY ? 0.f : exp2f(mo[i] - mon);
+        mo[i] = mon;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[i][d] *= al;
+      }
+      block_sync_lds();
+      if (threadIdx.x < 4) lds_st(&sh.need[threadIdx.x], 0);
+    }
+    l_half += pair_sum32(ls);
+    // ---- O^T += V^T . P^T over the widened V, as in the bf16 kernel
+    {
+      typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+      const int g4 = lane >> 4, s16 = lane & 15;
+      const int vt = 8 * (g4 >> 1) + (s16 >> 2);
+      const int vd = 16 * (g4 & 1) + 4 * (s16 & 3);
+      const int vch = vd >> 3, vin = (vd & 7) * 2;
+      // kv_off(16ks + vt (+4), 4(4wv + db) + vch) + vin = vofs[+4][db & 1] + 2048ks +
+      // SEGB (db / 2): one lane offset per (token half, db parity), the rest constant.
+      // Addresses formed as vb + one offset keep the LDS object visible to the
+      // compiler, which then knows these reads do not touch the buffer in flight.
+      int vofs[2][2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) vofs[hf][par] = kv_off(vt + 4 * hf, 16 * wv + 4 * par + vch) + vin;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8_t pb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) pb[i] = lds_ld((const bf16x8_t*)(sh.p + (32 * i + l32) * PROW + (16 * ks + 8 * lh) * 2));
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int cofs = 2048 * ks + SEGB * (db >> 1);
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + (vofs[0][db & 1] + cofs)));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + (vofs[1][db & 1] + cofs)));
+          const s16x4_t v8[2] = {lo, hi};
+          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, v8);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) o[i][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[i], o[i][db], 0, 0, 0);
+        }
+      }
+    }
+    // ---- sub-tile n+1 (codes and scales) has landed, and every wave is done with
+    //      `buf`, vb and P, past this barrier
+    if (n + 1 < nsub) {
+      wait_loads(0);
+      block_sync_lds();
+    }
+  };
+  for (int n = 0; n < nsub; n += 2) {
+    step(n, kv0, sg0, kv1, sg1);
+    if (n + 1 < nsub) step(n + 1, kv1, sg1, kv0, sg0);
+  }
+
+  // ---- epilogue as in the bf16 kernel; heads 0..31 go through kv0, 32..63 kv1
+  if (lh == 0) lds_st(&sh.lpart[th][hs], l_half);
+  block_sync_lds();
+  const bool final_out = a.n_split == 1;
+  const int64_t pi = (int64_t)rl * a.n_split + split;
+  constexpr int OPITCH = LAT_DV * 2 + 16;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int h = 32 * i + l32;
+    const float sc = final_out ? 1.f / (lds_ld(&sh.lpart[0][h]) + lds_ld(&sh.lpart[1][h])) : 1.f;
+    uint8_t* row = (i == 0 ? kv0 : kv1) + l32 * OPITCH + (128 * wv + 4 * lh) * 2;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(uint2*)(row + (32 * d + 8 * q) * 2) = make_uint2(pack_bf16x2(o[i][d][4 * q] * sc, o[i][d][4 * q + 1] * sc),
+                                                           pack_bf16x2(o[i][d][4 * q + 2] * sc, o[i][d][4 * q + 3] * sc));
+  }
+  if (th == 0 && lh == 0) {
+    const float lt = lds_ld(&sh.lpart[0][hs]) + lds_ld(&sh.lpart[1][hs]);
+    if (final_out) {
+      if (a.lse) a.lse[(int64_t)r * LAT_H + hs] = ((ms == -INFINITY ? 0.f : ms) + log2f(lt)) * LN2;
+    } else {
+      a.part_ml[(pi * LAT_H + hs) * 2] = ms == -INFINITY ? 0.f : ms;
+      a.part_ml[(pi * LAT_H + hs) * 2 + 1] = lt;
+    }
+  }
+  block_sync_lds();
+  uint16_t* dst = final_out ? (uint16_t*)a.out + (int64_t)r * LAT_H * LAT_DV : a.part_o + pi * LAT_H * LAT_DV;
+#pragma unroll
+  for (int k = 0; k < LAT_H / NWA; ++k) {
+    const int h = wv + NWA * k;
+    const uint8_t* srow = (k < LAT_H / NWA / 2 ? kv0 + h * OPITCH : kv1 + (h - 32) * OPITCH) + lane * 16;
+    *(u32x4_t*)(dst + h * LAT_DV + lane * 8) = *(const u32x4_t*)srow;
+  }
+}
+
 // Merge split partials: per (row, head) O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s.
 // Two heads per workgroup, 128 threads x 4 dims per head; the split weights are
 // computed once per wave (lane s holds split s) and broadcast.
@@ -660,6 +1041,15 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(AttnArgs a) {
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   launch(K_ATTN, attn_bf16_kernel, dim3((unsigned)((int64_t)a.n_rows * a.n_split)), dim3(NTA), s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1) return e;
+  launch(K_COMBINE, attn_combine_kernel, dim3(LAT_H / 2, a.n_rows), dim3(256), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  launch(K_ATTN, attn_fp8_kernel, dim3((unsigned)((int64_t)a.n_rows * a.n_split)), dim3(NTA), s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   launch(K_COMBINE, attn_combine_kernel, dim3(LAT_H / 2, a.n_rows), dim3(256), s, a);

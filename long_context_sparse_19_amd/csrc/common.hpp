@@ -21,18 +21,23 @@ struct Layout {
   int32_t page_tokens;
   int64_t seq_stride;
 
+  // token positions and block indices are below 2^31 (int32 sequence lengths), so
+  // the in-page split is a 32-bit unsigned division
   __device__ __forceinline__ int64_t tok_row(int b, int64_t t) const {
     if (page_table) {
-      const int64_t pg = page_table[(int64_t)b * max_pages + t / page_tokens];
-      return pg * page_tokens + t % page_tokens;
+      const uint32_t pt = (uint32_t)page_tokens, tt = (uint32_t)t;
+      const uint32_t pi = tt / pt;
+      const int64_t pg = page_table[(int64_t)b * max_pages + pi];
+      return pg * page_tokens + (tt - pi * pt);
     }
     return (int64_t)b * seq_stride + t;
   }
   __device__ __forceinline__ int64_t pool_row(int b, int64_t j) const {
     if (page_table) {
-      const int pr = page_tokens >> 2;
-      const int64_t pg = page_table[(int64_t)b * max_pages + j / pr];
-      return pg * pr + j % pr;
+      const uint32_t pr = (uint32_t)page_tokens >> 2, jj = (uint32_t)j;
+      const uint32_t pi = jj / pr;
+      const int64_t pg = page_table[(int64_t)b * max_pages + pi];
+      return pg * pr + (jj - pi * pr);
     }
     return (int64_t)b * (seq_stride >> 2) + j;
   }
@@ -75,6 +80,17 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     p[i] = (__float_as_uint(f[2 * i]) >> 16) | (__float_as_uint(f[2 * i + 1]) & 0xFFFF0000u);
+  return __builtin_bit_cast(bf16x8_t, p);
+}
+
+// The same widening by gfx950's v_cvt_scalef32_pk_bf16_fp8 with scale 1 (two codes
+// per instruction; word_sel picks bytes 0-1 or 2-3, the lower byte to the lower half).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8_pk(uint32_t w0, uint32_t w1) {
+  u32x4_t p;
+  p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  p[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  p[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
   return __builtin_bit_cast(bf16x8_t, p);
 }
 

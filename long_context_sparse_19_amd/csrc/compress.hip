@@ -127,9 +127,10 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
   const int64_t t = len - 1;
   const int64_t row = a.L.tok_row(b, t);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // latent (or K) and V rows: plain 16-byte copies
-  for (int i = tid; i < a.kv_row_bytes / 16; i += NT)
-    *(uint4*)(a.kv + row * a.kv_stride + 16 * i) = *(const uint4*)(a.kv_new + (int64_t)b * a.kv_row_bytes + 16 * i);
+  // latent (or K) and V rows: plain 16-byte copies (the fp8 latent tier below)
+  if (!a.kv_scale)
+    for (int i = tid; i < a.kv_row_bytes / 16; i += NT)
+      *(uint4*)(a.kv + row * a.kv_stride + 16 * i) = *(const uint4*)(a.kv_new + (int64_t)b * a.kv_row_bytes + 16 * i);
   if (a.v)
     for (int i = tid; i < a.v_row_bytes / 16; i += NT)
       *(uint4*)(a.v + row * a.v_stride + 16 * i) = *(const uint4*)(a.v_new + (int64_t)b * a.v_row_bytes + 16 * i);
@@ -151,6 +152,28 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
     __syncthreads();
     return m;
   };
+  // fp8 latent tier: the bf16 latent row quantised per token like the keys
+  // (sigma = amax / 448); thread i takes values 4i .. 4i+3
+  if (a.kv_scale) {
+    const bool kon = 4 * tid < a.kv_dim;
+    float kx[4] = {0.f, 0.f, 0.f, 0.f};
+    if (kon) {
+      const uint2 w = *(const uint2*)(a.kv_new + ((int64_t)b * a.kv_dim + 4 * tid) * 2);
+      kx[0] = __uint_as_float(w.x << 16);
+      kx[1] = __uint_as_float(w.x & 0xFFFF0000u);
+      kx[2] = __uint_as_float(w.y << 16);
+      kx[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    }
+    const float kamax = block_max(fmaxf(fmaxf(fabsf(kx[0]), fabsf(kx[1])), fmaxf(fabsf(kx[2]), fabsf(kx[3]))));
+    uint32_t packed = 0;
+    if (kamax > 0.f) {
+      const float inv = 448.0f / kamax;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed |= f32_to_e4m3(fminf(fmaxf(kx[i] * inv, -448.f), 448.f)) << (8 * i);
+    }
+    if (kon) *(uint32_t*)(a.kv + row * a.kv_stride + 4 * tid) = packed;
+    if (tid == 0) a.kv_scale[row] = kamax / 448.0f;
+  }
   // the new token's key: fp8 with sigma = amax / 448, or the float key as is
   uint32_t code = 0;
   float sigma = 0.f;
@@ -204,7 +227,7 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (a.batch <= 0) return hipSuccess;
-  if (a.dim > APPEND_MAX_DIM) return hipErrorInvalidValue;
+  if (a.dim > APPEND_MAX_DIM || (a.kv_scale && (a.kv_dim % 4 || a.kv_dim > 4 * NT))) return hipErrorInvalidValue;
   launch(K_APPEND, append_kernel, dim3(a.batch), dim3(NT), s, a);
   return hipGetLastError();
 }

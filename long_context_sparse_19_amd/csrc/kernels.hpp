@@ -50,7 +50,9 @@ struct AppendArgs {
   const uint8_t* kv_new;       // [batch, kv_row_bytes]
   uint8_t* kv;                 // token rows
   int64_t kv_stride;
-  int kv_row_bytes;            // a multiple of 16
+  int kv_row_bytes;            // a multiple of 16 (bytes copied when kv_scale is null)
+  float* kv_scale;             // fp8 latent tier: [token rows] scales, kv_new is bf16
+  int kv_dim;                  // fp8 latent tier: values per row (a multiple of 4, <= 1024)
   const uint8_t* v_new;        // [batch, v_row_bytes] or null
   uint8_t* v;
   int64_t v_stride;
@@ -117,8 +119,9 @@ struct AttnArgs {
   const int32_t* q_seq;
   const int32_t* q_pos;
   const void* q;               // [n_q, H, dk]
-  const uint8_t* k;            // K rows (bf16 latent or f32)
+  const uint8_t* k;            // K rows (bf16 or fp8 latent, or f32)
   int64_t k_stride;
+  const float* k_scale;        // per-token scales of an fp8 latent cache, else null
   const uint8_t* v;            // V rows (f32 path)
   int64_t v_stride;
   const int32_t* sel;          // [n_q, top_k]
@@ -134,6 +137,7 @@ struct AttnArgs {
 // bf16 latent MQA: 64 heads, dk 576, dv 512
 constexpr int LAT_H = 64, LAT_DK = 576, LAT_DV = 512;
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
 }  // namespace ip

@@ -31,7 +31,7 @@ class DeviceInputs:
     keys: _lib.Cache          # token-level index keys
     logits: torch.Tensor
     pooled: _lib.Cache        # pooled keys (output of compress)
-    kv: _lib.Cache            # latent (bf16) or K (f32)
+    kv: _lib.Cache            # latent (bf16, or fp8 codes + scales) or K (f32)
     v: Optional[_lib.Cache]   # V (f32 only)
     q: torch.Tensor
     q_idx: torch.Tensor
@@ -67,7 +67,9 @@ def upload(inp: Inputs, device="cuda") -> DeviceInputs:
     logits = _dev(inp.pool_logits, device)
     kv = v = None
     if w.attn_dtype == "bf16":
-        if inp.latent is not None:
+        if inp.latent is not None and inp.latent_scale is not None:   # fp8 latent tier
+            kv = _lib.Cache(_dev(inp.latent, device), _dev(inp.latent_scale, device))
+        elif inp.latent is not None:
             kv = _lib.Cache(_dev(inp.latent, device, torch.bfloat16))
         q = _dev(inp.q, device, torch.bfloat16)
         q_idx = _dev(inp.q_idx, device, torch.bfloat16)

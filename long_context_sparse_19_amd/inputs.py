@@ -77,17 +77,24 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
-def _fp8_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
-    """Per-row fp8 e4m3fn storage of float32 rows (codes, scale) using torch's cast."""
+def _fp8_span(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row fp8 e4m3fn storage of float32 rows (codes, scale = amax / 448) using
+    torch's cast; runs on the calling thread."""
     import torch
     amax = np.abs(x).max(axis=1)
     s = (amax / np.float32(448.0)).astype(np.float32)
     s_safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    y = torch.from_numpy(np.ascontiguousarray(x)) / torch.from_numpy(s_safe[:, None])
+    return y.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy(), s
+
+
+def _fp8_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """_fp8_span over row chunks on the thread pool."""
     codes = np.empty(x.shape, dtype=np.uint8)
+    s = np.empty(x.shape[0], dtype=np.float32)
 
     def conv(c, r0, r1):
-        y = torch.from_numpy(x[r0:r1]) / torch.from_numpy(s_safe[r0:r1, None])
-        codes[r0:r1] = y.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        codes[r0:r1], s[r0:r1] = _fp8_span(x[r0:r1])
     _chunked(x.shape[0], conv)
     return codes, s
 
@@ -103,7 +110,8 @@ class Inputs:
     idx_keys: np.ndarray            # uint8 fp8 codes [R, D_I] or float32 [R, D_I]
     idx_scale: Optional[np.ndarray]  # float32 [R] (fp8 keys) or None
     pool_logits: np.ndarray         # float32 [R]
-    latent: Optional[np.ndarray]    # uint16 bf16 bits [R, dk] (bf16 workloads)
+    latent: Optional[np.ndarray]    # uint16 bf16 bits [R, dk] (bf16 workloads), or uint8
+                                    # fp8 e4m3fn codes with latent_scale (fp8 latent tier)
     k_cache: Optional[np.ndarray]   # float32 [R, dk] (f32 workload)
     v_cache: Optional[np.ndarray]   # float32 [R, dv] (f32 workload)
     q: np.ndarray                   # uint16 bf16 bits or float32 [n_q, H, dk]
@@ -112,6 +120,7 @@ class Inputs:
     q_seq: np.ndarray               # int32 [n_q]
     q_pos: np.ndarray               # int32 [n_q]
     salient_rows: np.ndarray        # int64 physical token rows whose scale was x8
+    latent_scale: Optional[np.ndarray] = None   # float32 [R] (fp8 latent tier)
 
     @property
     def max_pages(self) -> int:
@@ -178,9 +187,19 @@ def make_inputs(w: Workload, with_attention: bool = True) -> Inputs:
     logits = _normal_rows(seed, "logits", n_rows, 1)[:, 0].copy()
 
     # attention caches
-    latent = k_cache = v_cache = None
+    latent = k_cache = v_cache = latent_scale = None
     if with_attention:
-        if w.attn_dtype == "bf16":
+        if w.attn_dtype == "bf16" and w.latent_fp8:
+            # fp8 latent tier: the same N(0,1) rows stored as e4m3fn codes with a
+            # per-token scale (amax / 448)
+            latent = np.empty((n_rows, w.dk), dtype=np.uint8)
+            latent_scale = np.empty(n_rows, dtype=np.float32)
+
+            def fill8(c, r0, r1):
+                x = _rng(seed, "latent", c).standard_normal((r1 - r0, w.dk), dtype=np.float32)
+                latent[r0:r1], latent_scale[r0:r1] = _fp8_span(x)
+            _chunked(n_rows, fill8)
+        elif w.attn_dtype == "bf16":
             latent = np.empty((n_rows, w.dk), dtype=np.uint16)
 
             def fill(c, r0, r1):
@@ -214,6 +233,7 @@ def make_inputs(w: Workload, with_attention: bool = True) -> Inputs:
         seq_stride=seq_stride, n_rows_tok=n_rows, idx_keys=idx_keys, idx_scale=idx_scale,
         pool_logits=logits, latent=latent, k_cache=k_cache, v_cache=v_cache, q=q,
         q_idx=q_idx, gates=gates, q_seq=q_seq, q_pos=q_pos, salient_rows=salient,
+        latent_scale=latent_scale,
     )
 
 

@@ -49,6 +49,11 @@ in the design notes):
   Brief, section "DSA keeps selected global access in eleven layers" (a
   token-addressable history that grows with the sequence); reading notes, section
   4 "The serving stack" (the FP8 tier).
+* R9 lower-precision latent tier: the latent row of token t is stored as e4m3fn
+  codes with one fp32 scale per token, sigma_t = max|row| / 448 (R3's rule over the
+  576 dims), and attention uses sigma_t * dec(code_t) for K and its first 512 dims
+  for V.  Reading notes, section 4 "The serving stack" (INT8 / FP8 / BF16 chosen
+  per cache tier).
 """
 from __future__ import annotations
 
@@ -210,8 +215,8 @@ def append(inp, kv_new, key_new, logit_new, only=None):
     inp holds the caches before the step (idx_keys, idx_scale, pool_logits and the
     layout) and seq_lens counting the new tokens.  kv_new [B, ...], key_new [B, D]
     (bf16 bit patterns or floats), logit_new [B].  Returns one dict per sequence with
-    a new token: row, kv, key (codes, or floats for a float cache), sigma, v (x /
-    sigma), logit, and when a block completes prow, pooled, psigma, pv, pmag (the
+    a new token: row, kv (for an fp8 latent tier (R9) its codes, with kv_sigma and
+    kv_v), key (codes, or floats for a float cache), sigma, v (x / sigma), logit, and when a block completes prow, pooled, psigma, pv, pmag (the
     outputs of pool_fp8, or the float pooled key).  `only`: a subset of sequences
     (the others get None)."""
     out = []
@@ -224,6 +229,10 @@ def append(inp, kv_new, key_new, logit_new, only=None):
         row = int(token_rows(inp, b, t))
         x = _to_f64(np.asarray(key_new)[b])
         e = {"row": row, "kv": np.asarray(kv_new)[b], "logit": float(np.asarray(logit_new)[b])}
+        if getattr(inp, "latent_scale", None) is not None:
+            # R9: the latent row goes into the fp8 tier quantised per token
+            kc, ks, kvv = quantize_tokens(_to_f64(e["kv"])[None])
+            e.update(kv=kc[0], kv_sigma=float(ks[0]), kv_v=kvv[0])
         if fp8:
             codes, sigma, v = quantize_tokens(x[None])
             e.update(key=codes[0], sigma=float(sigma[0]), v=v[0])
@@ -310,6 +319,14 @@ def _to_f64(x) -> np.ndarray:
     return x.astype(F64)
 
 
+def latent_rows(inp, phys) -> np.ndarray:
+    """Latent rows as float64: bf16 rows widened, or (R9) the fp8 tier's
+    sigma_t * dec(code_t) with one scale per token row."""
+    if getattr(inp, "latent_scale", None) is not None:
+        return np.asarray(inp.latent_scale, dtype=F64)[phys][:, None] * fp8_decode(inp.latent[phys])
+    return _to_f64(inp.latent[phys])
+
+
 def attention_rows(inp, ids, scale: float, dv: int, rows=None):
     """Sparse attention for query rows (default all): O [n, H, dv], lse [n, H]."""
     rows = range(len(inp.q_pos)) if rows is None else rows
@@ -319,7 +336,7 @@ def attention_rows(inp, ids, scale: float, dv: int, rows=None):
         t = selected_tokens(ids[n], int(inp.q_pos[r]))
         phys = token_rows(inp, b, t)
         if inp.latent is not None:
-            KV = _to_f64(inp.latent[phys])
+            KV = latent_rows(inp, phys)
             K, V = KV, KV[:, :dv]
         else:
             K = _to_f64(inp.k_cache[phys])

@@ -100,7 +100,12 @@ def test_append_rejects_bad_arguments(L):
     assert append(L, s, logit_new=None) == L.IP_EINVAL
     assert append(L, s, logits=None) == L.IP_EINVAL
     assert append(L, s, v=f32) == L.IP_EINVAL                                   # v without v_new
-    assert append(L, s, kv=cache(L)) == L.IP_EUNSUPPORTED                        # fp8 latent
+    kv8 = cache(L, row_dim=576, stride=576)                                      # fp8 latent tier
+    assert append(L, s, kv=kv8, v=f32, v_new=FAKE) == L.IP_EUNSUPPORTED           # no separate v
+    assert append(L, s, kv=cache(L, row_dim=574, stride=576)) == L.IP_EUNSUPPORTED
+    assert append(L, s, kv=cache(L, row_dim=1028, stride=1040)) == L.IP_EUNSUPPORTED
+    assert append(L, s, kv=kv8, kv_new=FAKE + 4) == L.IP_EINVAL                   # bf16 rows, 8-byte aligned
+    assert append(L, s, kv=cache(L, row_dim=576, stride=576, scale=None)) == L.IP_EINVAL
     assert append(L, s, kv=cache(L, dtype=L.IP_BF16, row_dim=12, stride=32, scale=None)) == L.IP_EUNSUPPORTED
     assert append(L, s, key_dtype=L.IP_FP8_E4M3FN) == L.IP_EUNSUPPORTED
     assert append(L, s, keys=cache(L, row_dim=64, stride=64)) == L.IP_EUNSUPPORTED
@@ -162,6 +167,13 @@ def test_attention_rejects_bad_arguments(L):
     f = cache(L, dtype=L.IP_F32, row_dim=64, stride=256, scale=None)
     assert attn(L, s, q_dtype=L.IP_F32, H=16, dk=64, dv=64, k=f, v=None) == L.IP_EINVAL   # v required
     assert attn(L, s, q_dtype=L.IP_F32, H=32, dk=64, dv=64, k=f, v=f) == L.IP_EUNSUPPORTED
+    # the fp8 latent tier: codes with per-token scales, the same geometry
+    assert attn(L, s, k=cache(L, row_dim=576, stride=576, scale=None)) == L.IP_EINVAL
+    assert attn(L, s, k=cache(L, row_dim=512, stride=512)) == L.IP_EUNSUPPORTED
+    assert attn(L, s, k=cache(L, row_dim=576, stride=576), v=cache(L, row_dim=512, stride=512)) == L.IP_EUNSUPPORTED
+    big = seqs(batch=1024, max_seq_len=1 << 20, seq_stride=1 << 20)               # rows beyond 2^29
+    assert attn(L, big, k=cache(L, row_dim=576, stride=576)) == L.IP_EUNSUPPORTED
+    assert attn(L, big) == L.IP_EUNSUPPORTED
     assert L.LIB.sparse_attn_prefill(ctypes.byref(s), 2, None, None, FAKE, L.IP_BF16, 64, 576, 512, 0.1,
                                      ctypes.byref(cache(L, dtype=L.IP_BF16, row_dim=576, stride=1152, scale=None)),
                                      None, FAKE, 512, FAKE, None, None, 0, None) == L.IP_EINVAL  # q_pos

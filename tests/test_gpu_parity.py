@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from long_context_sparse_19_amd.configs import (
-    TINY, DECODE, PREFILL, MAX_CTX, RAGGED, scaled_down,
+    TINY, DECODE, PREFILL, MAX_CTX, RAGGED, DECODE_FP8KV, scaled_down,
 )
 from long_context_sparse_19_amd.inputs import make_inputs, new_tokens
 from oracle import oracle as O
@@ -158,6 +158,13 @@ SMALL = {
     "k1": scaled_down(DECODE, 1024, batch=2, top_k=1),
     "k_exceeds": scaled_down(DECODE, 256, batch=2, top_k=100),
     "tiny_prefill_f32": TINY.with_(mode="prefill", n_query=40, seq_len=512, top_k=16),
+    # the fp8 latent tier: codes + per-token scales in the attention
+    "fp8kv_decode_split": scaled_down(DECODE_FP8KV, 4 * 9000 + 12, batch=2),
+    "fp8kv_decode_short": scaled_down(DECODE_FP8KV, 300, batch=3),
+    "fp8kv_k_exceeds": scaled_down(DECODE_FP8KV, 256, batch=2, top_k=100),
+    "fp8kv_ragged_paged": scaled_down(RAGGED.with_(latent_fp8=True), 8192, batch=5, min_blocks=50),
+    "fp8kv_prefill_tail": scaled_down(PREFILL.with_(latent_fp8=True), 3000, n_query=130),
+    "fp8kv_prefill_from_zero": scaled_down(PREFILL.with_(latent_fp8=True), 64, n_query=64, top_k=6),
 }
 
 
@@ -217,7 +224,8 @@ def test_codec_roundtrip_through_compress():
 def test_end_to_end_chain_small():
     """compress -> score/top-k -> attention on the device vs the oracle chain."""
     D = _dev()
-    for w in (scaled_down(DECODE, 4 * 9001, batch=2), TINY, scaled_down(RAGGED, 4096, batch=3, min_blocks=200)):
+    for w in (scaled_down(DECODE, 4 * 9001, batch=2), TINY, scaled_down(RAGGED, 4096, batch=3, min_blocks=200),
+              scaled_down(DECODE_FP8KV, 4 * 5001, batch=2)):
         log(f"[e2e] {w.name}")
         inp = make_inputs(w)
         d = D.upload(inp)
@@ -269,6 +277,10 @@ APPEND = {
     "tiny_f32": (TINY, lambda L: L),
     "tiny_f32_open_block": (TINY, lambda L: L - 3),
     "decode_full": (DECODE, lambda L: L),
+    # the fp8 latent tier: the new latent row is quantised per token
+    "fp8kv_positions": (scaled_down(DECODE_FP8KV, 1024, batch=4), lambda L: L - np.arange(4)),
+    "fp8kv_ragged_paged": (scaled_down(RAGGED.with_(latent_fp8=True), 8192, batch=5, min_blocks=50), lambda L: L),
+    "fp8kv_decode_full": (DECODE_FP8KV, lambda L: L),
 }
 
 
@@ -289,10 +301,14 @@ def test_append_parity(name):
     new = new_tokens(w, len(inp.seq_lens), seed=7)
     exp = O.append(inp, new["kv_new"], new["key_new"], new["logit_new"])
     fp8 = inp.idx_scale is not None
+    kv8 = inp.latent_scale is not None
+    small = d.kv.data.numel() * d.kv.data.element_size() <= (64 << 20)
     pooled0, keys0 = _bits(d.pooled.data), _bits(d.keys.data)
+    kv0 = _bits(d.kv.data) if small else None
     D.append(d, D.NewTokens(new))
     torch.cuda.synchronize()
     kv, keys, pooled, logits = _bits(d.kv.data), _bits(d.keys.data), _bits(d.pooled.data), d.logits.cpu().numpy()
+    kvsc = d.kv.scale.cpu().numpy() if kv8 else None
     v = None if d.v is None else d.v.data.cpu().numpy()
     ksc = d.keys.scale.cpu().numpy() if fp8 else None
     psc = d.pooled.scale.cpu().numpy() if fp8 else None
@@ -300,7 +316,11 @@ def test_append_parity(name):
     for b, e in enumerate(exp):
         row = e["row"]
         krows.append(row)
-        assert np.array_equal(kv[row], e["kv"]), f"seq {b}: kv row"
+        if kv8:
+            P.check_pooled_fp8(kv[row][None], kvsc[row][None], e["kv"][None], np.array([e["kv_sigma"]]),
+                               e["kv_v"][None], np.abs(e["kv_v"])[None], [0])
+        else:
+            assert np.array_equal(kv[row], e["kv"]), f"seq {b}: kv row"
         if v is not None:
             assert np.array_equal(v[row], new["v_new"][b]), f"seq {b}: v row"
         assert logits[row] == np.float32(e["logit"])
@@ -322,6 +342,8 @@ def test_append_parity(name):
     assert np.array_equal(pooled[other], pooled0[other])
     other = np.setdiff1d(np.arange(keys.shape[0]), krows)
     assert np.array_equal(keys[other], keys0[other])
+    if kv0 is not None:
+        assert np.array_equal(kv[other], kv0[other])
     log(f"  append ok ({len(prows)} blocks pooled)")
 
 
