@@ -57,7 +57,6 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 constexpr int PROW = SUBT * 2 + 16;            // P row of one head: 64 bf16 + pad = 144 bytes
 
 struct __align__(16) AttnShared {
-  uint8_t p[LAT_H * PROW];                     // P[head][token] bf16
   uint32_t brow[MAX_BLOCKS_PER_SPLIT];
   float tmax[2][LAT_H];                        // tile maxima of the two token halves
   float lpart[2][LAT_H];                       // l of the two token halves (end)
@@ -118,8 +117,8 @@ __device__ __forceinline__ float quad_sum16(float x) {
 // top bits.  Entries that are -1, past the split or entirely after the query
 // point at the query's own block (whose 4 rows exist) with 0 visible tokens, so
 // every load stays inside the cache.  Thread t handles entries t and t + NTA: the
-// selection ids are fetched first (fetch_blocks) and turned into entries later
-// (build_block_table), so other loads can be issued in between.
+// selection ids are fetched first (fetch_blocks) and turned into entries together
+// with the other ids of the prologue (block_entries).
 struct BlockIds {
   int blk[MAX_BLOCKS_PER_SPLIT / NTA];
 };
@@ -166,16 +165,6 @@ __device__ __forceinline__ void block_entries(const AttnArgs& a, const RowCtx& c
   }
 }
 
-__device__ __forceinline__ void build_block_table(const AttnArgs& a, const RowCtx& c, const BlockIds& ids, int sb0,
-                                                  int send, AttnShared& sh) {
-  const int nb = ((send - sb0 + 15) >> 4) << 4;
-#pragma unroll
-  for (int k = 0; k < MAX_BLOCKS_PER_SPLIT / NTA; ++k) {
-    const int i = (int)threadIdx.x + k * NTA;
-    if (i < nb) lds_st(&sh.brow[i], block_entry(a, c, ids.blk[k]));
-  }
-}
-
 // Sub-tile layout in LDS: 9 segments of 8 KB, segment g holding bytes 128g ..
 // 128g+127 (dims 64g .. 64g+63) of all 64 rows, row t at 128t, with the eight
 // 16-byte chunks of each 128-byte piece stored in slots chunk ^ x(t),
@@ -205,30 +194,28 @@ struct SubtileSrc {
   const uint8_t* row[2];
 };
 
+// The entries of this lane's two blocks, 4wv + (l >> 5) and that + 2, from one
+// 16-byte read of entries 4wv .. 4wv+3.  (Two 4-byte reads get merged into one
+// ds_read2 that the compiler can no longer tell apart from the LDS DMA in flight,
+// and it then waits for all of it.)
+__device__ __forceinline__ void subtile_entries(const AttnShared& sh, int n, uint32_t (&e)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const u32x4_t q = lds_ld((const u32x4_t*)&sh.brow[n * 16 + 4 * wv]);
+  e[0] = (lane >> 5) ? q[1] : q[0];
+  e[1] = (lane >> 5) ? q[3] : q[2];
+}
+
 __device__ __forceinline__ SubtileSrc subtile_src(const AttnArgs& a, const AttnShared& sh, int n) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t e[2];
+  subtile_entries(sh, n, e);
   SubtileSrc src;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = 8 * (2 * wv + h) + (lane >> 3);
-    const uint32_t grow = (lds_ld(&sh.brow[n * 16 + (t >> 2)]) & ROW_BITS) + (t & 3);
-    src.row[h] = a.k + (uint64_t)grow * a.k_stride + 16 * ((lane & 7) ^ kv_swz(t));
-  }
-  return src;
-}
-
-// The same rows for sub-tile n straight from the selection ids (blk[h]: the block
-// of row half h, -1 past the split), for the prologue: the block table is not
-// built yet, and reading it while LDS DMA is in flight would wait for the DMA.
-__device__ __forceinline__ SubtileSrc subtile_src_ids(const AttnArgs& a, const RowCtx& c, const int (&blk)[2]) {
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  SubtileSrc src;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int t = 8 * (2 * wv + h) + (lane >> 3);
-    const uint32_t grow = (block_entry(a, c, blk[h]) & ROW_BITS) + (t & 3);
+    const uint32_t grow = (e[h] & ROW_BITS) + (t & 3);
     src.row[h] = a.k + (uint64_t)grow * a.k_stride + 16 * ((lane & 7) ^ kv_swz(t));
   }
   return src;
@@ -242,25 +229,19 @@ __device__ __forceinline__ void load_column(const SubtileSrc& src, uint8_t* buf,
                                    16, 0, 0);
 }
 
-__device__ __forceinline__ void load_subtile(const AttnArgs& a, const AttnShared& sh, int n, uint8_t* buf) {
-  const SubtileSrc src = subtile_src(a, sh, n);
-#pragma unroll
-  for (int c = 0; c < KV_LOADS; ++c) load_column(src, buf, c);
-}
-
-// Waits until at most `pending` (0 or 18) of this wave's global loads are
+// Waits until at most N of this wave's global loads (LDS DMA included) are
 // outstanding.  The vmcnt field of the s_waitcnt immediate is bits 0..3 (low) and
 // 14..15 (high); expcnt (bits 4..6) and lgkmcnt (bits 8..11) stay at their maxima
 // (no wait).
-__device__ __forceinline__ void wait_loads(int pending) {
-  constexpr int NOWAIT = (0x7 << 4) | (0xF << 8);
-  constexpr int VM18 = (KV_LOADS & 0xF) | ((KV_LOADS >> 4) << 14);
-  if (pending >= KV_LOADS) __builtin_amdgcn_s_waitcnt(VM18 | NOWAIT);
-  else __builtin_amdgcn_s_waitcnt(NOWAIT);
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
   __shared__ AttnShared sh;
+  __shared__ __align__(16) uint8_t pmat[LAT_H * PROW];   // P[head][token] bf16
   __shared__ __align__(16) uint8_t kv0[KVBUF];
   __shared__ __align__(16) uint8_t kv1[KVBUF];
   const int lane = threadIdx.x & 63;
@@ -278,9 +259,11 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
   const int nsub = (send - sb0 + 15) >> 4;
   const int hs = 32 * hb + l32;                  // head of this lane in the S^T layout
 
-  // prologue loads, in this order: selection ids, the query row (into kv1), then
-  // sub-tile 0; building the block table waits only for the ids, and q is read
-  // into registers while sub-tile 0 is fetched
+  // prologue: the selection ids (block-table entries and this lane's rows of
+  // sub-tiles 0 and 1); the query row into kv1; sub-tile 0; q into registers; then
+  // sub-tile 1 into kv1.  The query goes by LDS DMA in whole 128-byte lines (loads
+  // of each lane's q fragments straight from memory measured 2.3 us slower per
+  // decode step).
   const BlockIds ids = fetch_blocks(c, sb0, send);
   // ids of this lane's source blocks for sub-tiles 0 and 1 (rows 8(2w + h) + l/8)
   int pid[2][2];
@@ -292,9 +275,9 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
       pid[n][h] = bi < send ? c.sel[bi] : -1;
     }
   {
-    // the query row (64 heads x 576 dims = one sub-tile's bytes) goes to kv1 by LDS
-    // DMA in the sub-tile layout, head h as row h: whole 128-byte lines, and the
-    // fragment reads below are the conflict-free K-fragment pattern
+    // the query row (64 heads x 576 dims = one sub-tile's bytes) goes to kv1 in the
+    // sub-tile layout, head h as row h: whole 128-byte lines, and the fragment
+    // reads below are the conflict-free K-fragment pattern
     SubtileSrc qsrc;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -304,9 +287,50 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < KV_LOADS; ++k) load_column(qsrc, kv1, k);
   }
-  // every query DMA is issued before anything consumes the ids: a use of a loaded
-  // register while LDS DMA is in flight makes the compiler wait for all loads
+  // every query DMA is issued before anything consumes the ids
   __builtin_amdgcn_sched_barrier(0);
+  // entries: [0, 1] this thread's block-table entries, [2 + 2n + h] its source
+  // rows of sub-tile n
+  constexpr int NE = MAX_BLOCKS_PER_SPLIT / NTA;
+  static_assert(NE == 2, "two block-table entries per thread");
+  const int eb[6] = {ids.blk[0], ids.blk[1], pid[0][0], pid[0][1], pid[1][0], pid[1][1]};
+  uint32_t ent[6];
+  block_entries(a, c, eb, ent);
+  const int nbt = ((send - sb0 + 15) >> 4) << 4;
+  SubtileSrc src[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = 8 * (2 * wv + h) + (lane >> 3);
+      const uint32_t grow = (ent[2 + 2 * n + h] & ROW_BITS) + (t & 3);
+      src[n].row[h] = a.k + (uint64_t)grow * a.k_stride + 16 * ((lane & 7) ^ kv_swz(t));
+    }
+#pragma unroll
+  for (int k = 0; k < KV_LOADS; ++k) load_column(src[0], kv0, k);
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    const int i = (int)threadIdx.x + k * NTA;
+    if (i < nbt) lds_st(&sh.brow[i], ent[k]);
+  }
+  if (threadIdx.x < 4) lds_st(&sh.need[threadIdx.x], 0);
+  wait_vm<KV_LOADS>();                           // this wave's part of q landed
+  block_sync_lds();
+  // q fragments: head hs, dims 16s + 8lh .. +8 for k-step s.  q only feeds MFMA B
+  // operands, which may sit in accumulation registers: keep it there, leaving the
+  // ordinary VGPRs to the O accumulators
+  bf16x8_t qf[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const bf16x8_t*)(kv1 + kv_off(hs, 2 * s + lh));
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+a"(qf[s]));
+  block_sync_lds();                              // every wave has its q: kv1 is free
+  // sub-tile 1, unconditionally (past the split the rows are the query's own
+  // block), so that every path has the same loads in flight
+#pragma unroll
+  for (int k = 0; k < KV_LOADS; ++k) load_column(src[1], kv1, k);
+  wait_vm<KV_LOADS>();                           // sub-tile 0 landed (this wave's part)
+  block_sync_lds();
   const float cs = a.scale * LOG2E;
 
   // O^T tiles [32 dims, 32 heads]: o[i][db][k] = head 32i + l32, dim 128wv + 32db +
@@ -319,35 +343,6 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
   // reference maxima: ms for head hs (S^T layout), mo[i] for head 32i + l32 (O layout)
   float ms = -INFINITY, mo[2] = {-INFINITY, -INFINITY};
   float l_half = 0.f;                            // l of head hs over this wave's token half
-
-  const SubtileSrc src0 = subtile_src_ids(a, c, pid[0]);
-  const SubtileSrc src1 = subtile_src_ids(a, c, pid[1]);
-  if (nsub > 0) {
-#pragma unroll
-    for (int k = 0; k < KV_LOADS; ++k) load_column(src0, kv0, k);
-  }
-  build_block_table(a, c, ids, sb0, send, sh);
-  if (threadIdx.x < 4) lds_st(&sh.need[threadIdx.x], 0);
-  if (nsub > 0) wait_loads(KV_LOADS);            // this wave's part of q landed
-  else wait_loads(0);
-  block_sync_lds();
-  // q fragments: head hs, dims 16s + 8lh .. +8 for k-step s.  q only feeds MFMA B
-  // operands, which may sit in accumulation registers: keep it there, leaving the
-  // ordinary VGPRs to the O accumulators
-  bf16x8_t qf[KSTEPS];
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const bf16x8_t*)(kv1 + kv_off(hs, 2 * s + lh));
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+a"(qf[s]));
-  block_sync_lds();                              // every wave has its q: kv1 is free
-  if (nsub > 1) {
-#pragma unroll
-    for (int k = 0; k < KV_LOADS; ++k) load_column(src1, kv1, k);
-    wait_loads(KV_LOADS);                        // sub-tile 0 landed (this wave's part)
-  } else {
-    wait_loads(0);
-  }
-  block_sync_lds();
 
   // one sub-tile: compute on `buf`, while sub-tile n+1 streams into `nxt`
   auto step = [&](const int n, const uint8_t* buf, uint8_t* nxt) {
@@ -399,7 +394,7 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
     auto write_p = [&](float m) {
       const float mu = m == -INFINITY ? 0.f : m;
       float ls = 0.f;
-      uint8_t* pr = sh.p + hs * PROW + (32 * th + 4 * lh) * 2;
+      uint8_t* pr = pmat + hs * PROW + (32 * th + 4 * lh) * 2;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float pv[4];
@@ -449,7 +444,7 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
       for (int ks = 0; ks < 4; ++ks) {
         bf16x8_t pb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) pb[i] = lds_ld((const bf16x8_t*)(sh.p + (32 * i + l32) * PROW + (16 * ks + 8 * lh) * 2));
+        for (int i = 0; i < 2; ++i) pb[i] = lds_ld((const bf16x8_t*)(pmat + (32 * i + l32) * PROW + (16 * ks + 8 * lh) * 2));
         // ks-step operands: 2 P reads and 8 V reads for 8 MFMAs
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
@@ -465,11 +460,11 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
       }
     }
     // ---- sub-tile n+1 has landed for every wave, and every wave is done with
-    //      `buf` and with P, past this barrier
-    if (n + 1 < nsub) {
-      wait_loads(0);
-      block_sync_lds();
-    }
+    //      `buf` and with P, past this barrier.  The wait is unconditional: the
+    //      compiler then knows no load is in flight when the next step starts
+    //      (else it waits for sub-tile 1 at the top of step 0)
+    wait_vm<0>();
+    if (n + 1 < nsub) block_sync_lds();
   };
   for (int n = 0; n < nsub; n += 2) {
     step(n, kv0, kv1);
@@ -559,11 +554,12 @@ __device__ __forceinline__ SubtileSrc8 src8_from_rows(const AttnArgs& a, const u
 __device__ __forceinline__ SubtileSrc8 subtile_src8(const AttnArgs& a, const AttnShared& sh, int n) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint32_t grow[2];
+  uint32_t e[2], grow[2];
+  subtile_entries(sh, n, e);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = 8 * (2 * wv + h) + (lane >> 3);
-    grow[h] = (lds_ld(&sh.brow[n * 16 + (t >> 2)]) & ROW_BITS) + (t & 3);
+    grow[h] = (e[h] & ROW_BITS) + (t & 3);
   }
   return src8_from_rows(a, grow);
 }
@@ -578,7 +574,7 @@ __device__ __forceinline__ void load_column8(const SubtileSrc8& src, uint8_t* bu
                                    16, 0, 0);
 }
 
-// the scales of the sub-tile's 64 tokens: lane l brings that of token l (wave 0 only)
+// the scales of the sub-tile's 64 tokens: lane l brings that of token l
 __device__ __forceinline__ void load_scales(const float* src, float* sg) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                    (void __attribute__((address_space(3)))*)sg, 4, 0, 0);
@@ -591,6 +587,7 @@ __device__ __forceinline__ const float* scale_src(const AttnArgs& a, const AttnS
 
 __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
   __shared__ AttnShared sh;
+  __shared__ __align__(16) uint8_t pmat[LAT_H * PROW];   // P[head][token] bf16
   __shared__ __align__(16) uint8_t kv0[KVBUF8];
   __shared__ __align__(16) uint8_t kv1[KVBUF8];
   __shared__ __align__(16) uint8_t vb[LAT_DV / 64 * SEGB];   // bf16 V of the current sub-tile
@@ -612,8 +609,10 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
   const int hs = 32 * hb + l32;
 
   // prologue: the ids (block table entries, this lane's rows of sub-tiles 0 and 1,
-  // the tokens whose scales it brings), then every load at once: sub-tiles 0 and
-  // 1 with their scales and the query fragments
+  // the tokens whose scales it brings); the query row by LDS DMA in whole 128-byte
+  // lines, dims 0..511 into vb and 512..575 into pmat (both free until step 0),
+  // head h as row h in the sub-tile layout; sub-tiles 0 and 1 with their scales;
+  // then q into registers.
   const BlockIds ids = fetch_blocks(c, sb0, send);
   int pid[2][2], sid[2];
 #pragma unroll
@@ -626,6 +625,22 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
     const int bi = sb0 + 16 * n + (lane >> 2);
     sid[n] = bi < send ? c.sel[bi] : -1;
   }
+  {
+    SubtileSrc qsrc;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = 8 * (2 * wv + h) + (lane >> 3);
+      qsrc.row[h] = (const uint8_t*)a.q + ((int64_t)r * LAT_H + t) * (LAT_DK * 2) + 16 * ((lane & 7) ^ kv_swz(t));
+    }
+#pragma unroll
+    for (int k = 0; k < KV_LOADS; ++k) {
+      const int g = k >> 1, h = k & 1;
+      uint8_t* dst = (g < 8 ? vb + g * SEGB : pmat) + (2 * wv + h) * 1024;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(qsrc.row[h] + 128 * g),
+                                       (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   // entries: [0, 1] this thread's block-table entries, [2 + 2n + h] its source
   // rows of sub-tile n, [6 + n] the token whose scale it brings
   constexpr int NE = MAX_BLOCKS_PER_SPLIT / NTA;
@@ -647,41 +662,38 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
     src[n] = src8_from_rows(a, grow);
     ssrc[n] = a.k_scale + (ent[6 + n] & ROW_BITS) + (lane & 3);
   }
-  // the entries have landed before any DMA is issued (a use of a loaded register
-  // while LDS DMA is in flight would wait for every load)
+  // sub-tiles 0 and 1 with their scales, unconditionally (past the split the
+  // rows are the query's own block), so that every wave has the same loads in
+  // flight on every path; all four waves bring the same scales
 #pragma unroll
-  for (int k = 0; k < NE; ++k) asm volatile("" ::"v"(ent[k]));
-  if (nsub > 0) {
-    if (wv == 0) load_scales(ssrc[0], sg0);
+  for (int n = 0; n < 2; ++n) {
+    load_scales(ssrc[n], n ? sg1 : sg0);
 #pragma unroll
-    for (int k = 0; k < KV_LOADS8; ++k) load_column8(src[0], kv0, k);
+    for (int k = 0; k < KV_LOADS8; ++k) load_column8(src[n], n ? kv1 : kv0, k);
   }
-  if (nsub > 1) {
-    if (wv == 0) load_scales(ssrc[1], sg1);
-#pragma unroll
-    for (int k = 0; k < KV_LOADS8; ++k) load_column8(src[1], kv1, k);
-  }
-  // q fragments of head hs: qf[2p] = dims 32p + 16lh .. +7, qf[2p+1] = the next 8
-  bf16x8_t qf[2 * KPAIRS];
-  {
-    const uint8_t* qrow = (const uint8_t*)a.q + ((int64_t)r * LAT_H + hs) * (LAT_DK * 2) + 32 * lh;
-#pragma unroll
-    for (int p = 0; p < KPAIRS; ++p) {
-      qf[2 * p] = *(const bf16x8_t*)(qrow + 64 * p);
-      qf[2 * p + 1] = *(const bf16x8_t*)(qrow + 64 * p + 16);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < NE; ++k) {
     const int i = (int)threadIdx.x + k * NTA;
     if (i < nbt) lds_st(&sh.brow[i], ent[k]);
   }
   if (threadIdx.x < 4) lds_st(&sh.need[threadIdx.x], 0);
-  wait_loads(0);
+  wait_vm<2 * (KV_LOADS8 + 1)>();                // the query landed
   block_sync_lds();
+  // q fragments of head hs: qf[2p] = dims 32p + 16lh .. +7 (bf16 chunk 4p + 2lh of
+  // the row), qf[2p+1] = the next 8
+  bf16x8_t qf[2 * KPAIRS];
+#pragma unroll
+  for (int p = 0; p < KPAIRS; ++p)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int ch = 4 * p + 2 * lh + e;
+      qf[2 * p + e] = p < 16 ? lds_ld((const bf16x8_t*)(vb + kv_off(hs, ch)))
+                             : lds_ld((const bf16x8_t*)(pmat + hs * 128 + 16 * ((ch & 7) ^ kv_swz(hs))));
+    }
 #pragma unroll
   for (int s = 0; s < 2 * KPAIRS; ++s) asm volatile("" : "+a"(qf[s]));
+  wait_vm<KV_LOADS8 + 1>();                      // sub-tile 0 landed
+  block_sync_lds();                              // and every wave has its q: vb, pmat free
   const float cs = a.scale * LOG2E;
 
   f32x16_t o[2][4];
@@ -698,20 +710,10 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
     const float* fssrc = scale_src(a, sh, fetch ? n + 1 : n);
     const u32x4_t bv0 = lds_ld((const u32x4_t*)&sh.brow[n * 16 + 8 * th]);
     const u32x4_t bv1 = lds_ld((const u32x4_t*)&sh.brow[n * 16 + 8 * th + 4]);
-    // ---- widen the V codes of the sub-tile into vb (bf16 layout): token l of
-    //      the 64, chunks wv + 4i of its 32 16-code chunks
-    {
-      const int tt = lane;
-#pragma unroll
-      for (int i = 0; i < VCH8 / NWA; ++i) {
-        const int j = wv + NWA * i;
-        const u32x4_t w = *(const u32x4_t*)(buf + kv_off(tt, j));
-        *(bf16x8_t*)(vb + kv_off(tt, 2 * j)) = fp8x8_to_bf16x8_pk(w[0], w[1]);
-        *(bf16x8_t*)(vb + kv_off(tt, 2 * j + 1)) = fp8x8_to_bf16x8_pk(w[2], w[3]);
-      }
-    }
     // ---- S^T[token, head] over the codes, as in the bf16 kernel with fragments of
-    //      two k-steps; sub-tile n+1 is fetched in between
+    //      two k-steps.  In between: sub-tile n+1 is fetched, and the V codes of
+    //      this sub-tile are widened into vb (bf16 layout; lane l takes token l,
+    //      chunks wv + 4i of its 32 16-code chunks: read at pair 2i, written at 2i+1)
     f32x16_t sacc;
     {
       f32x16_t sa[2] = {f32x16_t{}, f32x16_t{}};
@@ -720,7 +722,15 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
       u32x4_t kr[KPF];
 #pragma unroll
       for (int p = 0; p < KPF; ++p) kr[p] = *(const u32x4_t*)(buf + kv_off(t, 2 * p + lh));
-      if (fetch && wv == 0) load_scales(fssrc, sgn);
+      if (fetch) load_scales(fssrc, sgn);
+      // the widening's LDS offsets: kv_off(l, wv + 4i) = dro[i & 1] + SEGB (i / 2) and
+      // kv_off(l, 2(wv + 4i) + e) = dwo[e] + SEGB i.  In these address forms (and
+      // with the stores through lds_st) the compiler can tell the widening and the
+      // PV reads below from the DMA in flight; checked in the generated code, where
+      // the only vmcnt waits in the loop are the end-of-step ones.
+      const int dro[2] = {kv_off(lane, wv), kv_off(lane, wv + 4)};
+      const int dwo[2] = {kv_off(lane, 2 * wv), kv_off(lane, 2 * wv + 1)};
+      u32x4_t dq;
 #pragma unroll
       for (int p = 0; p < KPAIRS; ++p) {
         const u32x4_t w = kr[p % KPF];
@@ -730,6 +740,15 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
 #pragma unroll
         for (int k = 0; k < KV_LOADS8; ++k)
           if ((KPAIRS * k) / KV_LOADS8 == p && fetch) load_column8(fsrc, nxt, k);
+        if (p < 2 * (VCH8 / NWA)) {
+          const int i = p >> 1;
+          if ((p & 1) == 0) {
+            dq = *(const u32x4_t*)(buf + (dro[i & 1] + SEGB * (i >> 1)));
+          } else {
+            lds_st((bf16x8_t*)(vb + (dwo[0] + SEGB * i)), fp8x8_to_bf16x8_pk(dq[0], dq[1]));
+            lds_st((bf16x8_t*)(vb + (dwo[1] + SEGB * i)), fp8x8_to_bf16x8_pk(dq[2], dq[3]));
+          }
+        }
       }
       sacc = sa[0] + sa[1];
     }
@@ -755,7 +774,7 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
     auto write_p = [&](float m) {
       const float mu = m == -INFINITY ? 0.f : m;
       float ls = 0.f;
-      uint8_t* pr = sh.p + hs * PROW + (32 * th + 4 * lh) * 2;
+      uint8_t* pr = pmat + hs * PROW + (32 * th + 4 * lh) * 2;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float pv[4];
@@ -809,7 +828,7 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
       for (int ks = 0; ks < 4; ++ks) {
         bf16x8_t pb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) pb[i] = lds_ld((const bf16x8_t*)(sh.p + (32 * i + l32) * PROW + (16 * ks + 8 * lh) * 2));
+        for (int i = 0; i < 2; ++i) pb[i] = lds_ld((const bf16x8_t*)(pmat + (32 * i + l32) * PROW + (16 * ks + 8 * lh) * 2));
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int cofs = 2048 * ks + SEGB * (db >> 1);
@@ -823,11 +842,9 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
       }
     }
     // ---- sub-tile n+1 (codes and scales) has landed, and every wave is done with
-    //      `buf`, vb and P, past this barrier
-    if (n + 1 < nsub) {
-      wait_loads(0);
-      block_sync_lds();
-    }
+    //      `buf`, vb and P, past this barrier (the wait unconditional, as above)
+    wait_vm<0>();
+    if (n + 1 < nsub) block_sync_lds();
   };
   for (int n = 0; n < nsub; n += 2) {
     step(n, kv0, sg0, kv1, sg1);
@@ -835,7 +852,9 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
   }
 
   // ---- epilogue as in the bf16 kernel; heads 0..31 go through kv0, 32..63 kv1
+  //      (with one sub-tile, sub-tile 1's unused loads into kv1 land first)
   if (lh == 0) lds_st(&sh.lpart[th][hs], l_half);
+  wait_vm<0>();
   block_sync_lds();
   const bool final_out = a.n_split == 1;
   const int64_t pi = (int64_t)rl * a.n_split + split;
