@@ -133,6 +133,9 @@ ip_status indexpool_compress(const ip_seqs* seqs, const int32_t* block_begin, in
  *  kv_new   device [batch, kv->row_dim], kv->dtype; kv->row_dim * element size a
  *           multiple of 16 bytes (the same for v_new / v).  FP8 kv: kv_new BF16,
  *           8-byte aligned, kv->row_dim a multiple of 4 and <= 1024, v NULL
+ *  keys NULL: a DSA layer without indexer state (an IndexCache follower, reading
+ *           notes, section 2 "IndexPool": the cross-layer variant): only kv (and v)
+ *           rows are written; key_new, logit_new, logits and pooled must be NULL too
  *  key_new  device [batch, keys->row_dim], key_dtype BF16 or F32 (F32 for F32 keys)
  *  logit_new  device [batch] fp32;  logits  device [token rows] fp32
  *  keys, pooled  as in indexpool_compress (FP8 with scales, row_dim 128; or F32)
@@ -203,7 +206,8 @@ ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_se
  *   F32: q F32 [n_q, n_heads, dk]; separate F32 k [rows, dk] and v [rows, dv]
  *     caches; n_heads <= 16, dk, dv <= 128 and multiples of 4; out F32.
  *  sel_idx  device [n_q, top_k] ascending block ids, -1 entries ignored
- *           (index_score_topk's output)
+ *           (index_score_topk's output; under IndexCache, that of the group's first
+ *           layer, passed unchanged to the group's other layers)
  *  lse      device [n_q, n_heads] fp32 or NULL
  *  ws       device workspace of ws_bytes >= sparse_attn_workspace_bytes(...) (may be
  *           0 bytes, then ws may be NULL)

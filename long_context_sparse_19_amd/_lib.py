@@ -137,15 +137,21 @@ def indexpool_compress(seqs: Seqs, keys: Cache, logits: torch.Tensor, pooled: Ca
         _stream(stream)))
 
 
-def indexpool_append(seqs: Seqs, kv_new: torch.Tensor, kv: Cache, key_new: torch.Tensor, keys: Cache,
-                     logit_new: torch.Tensor, logits: torch.Tensor, pooled: Cache,
-                     v_new: Optional[torch.Tensor] = None, v: Optional[Cache] = None, stream=None) -> None:
-    s, kc, k, p = seqs.c(), kv.c(), keys.c(), pooled.c()
+def indexpool_append(seqs: Seqs, kv_new: torch.Tensor, kv: Cache, key_new: Optional[torch.Tensor],
+                     keys: Optional[Cache], logit_new: Optional[torch.Tensor], logits: Optional[torch.Tensor],
+                     pooled: Optional[Cache], v_new: Optional[torch.Tensor] = None, v: Optional[Cache] = None,
+                     stream=None) -> None:
+    """keys (with key_new, logit_new, logits, pooled) None: a layer without indexer
+    state, only kv (and v) rows are written."""
+    s, kc = seqs.c(), kv.c()
+    k = None if keys is None else keys.c()
+    p = None if pooled is None else pooled.c()
     vc = None if v is None else v.c()
     _check("indexpool_append", LIB.indexpool_append(
         ctypes.byref(s), kv_new.data_ptr(), ctypes.byref(kc), _ptr(v_new),
-        None if vc is None else ctypes.byref(vc), key_new.data_ptr(), _DT[key_new.dtype], ctypes.byref(k),
-        logit_new.data_ptr(), logits.data_ptr(), ctypes.byref(p), _stream(stream)))
+        None if vc is None else ctypes.byref(vc), _ptr(key_new),
+        _DT[key_new.dtype] if key_new is not None else IP_BF16, None if k is None else ctypes.byref(k),
+        _ptr(logit_new), _ptr(logits), None if p is None else ctypes.byref(p), _stream(stream)))
 
 
 def index_scores_ld(max_seq_len: int) -> int:

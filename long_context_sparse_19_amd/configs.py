@@ -65,6 +65,7 @@ class Workload:
     salient_frac: float = 0.0  # fraction of index-key rows whose scale is x8
     salient_mult: float = 8.0
     latent_fp8: bool = False  # latent cache in fp8 e4m3fn with a per-token scale
+    layers: int = 1           # DSA layers of an IndexCache group (the first runs the indexer)
 
     @property
     def n_rows(self) -> int:
@@ -99,7 +100,11 @@ RAGGED = _g1("ragged", mode="decode", batch=64, seq_len=32768, ragged=True,
 # The lower-precision latent tier: decode as above over an fp8 latent cache
 DECODE_FP8KV = DECODE.with_(name="decode_fp8kv", latent_fp8=True)
 
-WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, MAX_CTX, RAGGED, DECODE_FP8KV)}
+# IndexCache: a group of 4 DSA layers, decode as above; the first layer's selection
+# serves the other three, which keep no indexer state
+DECODE_INDEXCACHE = DECODE.with_(name="decode_indexcache", layers=4)
+
+WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, MAX_CTX, RAGGED, DECODE_FP8KV, DECODE_INDEXCACHE)}
 
 
 def scaled_down(w: Workload, seq_len: int, batch: Optional[int] = None,

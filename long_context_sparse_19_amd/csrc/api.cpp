@@ -215,10 +215,16 @@ ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cac
   const char* fn = "indexpool_append";
   if (ip_status st = check_seqs(seqs, fn)) return st;
   if (ip_status st = check_cache(kv, fn, "kv")) return st;
-  if (ip_status st = check_cache(keys, fn, "keys")) return st;
-  if (ip_status st = check_cache(pooled, fn, "pooled")) return st;
-  if (!kv_new || !key_new || !logit_new || !logits)
-    return fail(IP_EINVAL, "%s: kv_new, key_new, logit_new and logits must not be NULL", fn);
+  if (!kv_new) return fail(IP_EINVAL, "%s: kv_new must not be NULL", fn);
+  const bool idx = keys != nullptr;              // NULL keys: a layer without indexer state
+  if (idx) {
+    if (ip_status st = check_cache(keys, fn, "keys")) return st;
+    if (ip_status st = check_cache(pooled, fn, "pooled")) return st;
+    if (!key_new || !logit_new || !logits)
+      return fail(IP_EINVAL, "%s: key_new, logit_new and logits must not be NULL when keys are given", fn);
+  } else if (key_new || logit_new || logits || pooled) {
+    return fail(IP_EINVAL, "%s: without keys, key_new, logit_new, logits and pooled must be NULL", fn);
+  }
   if (v) {
     if (ip_status st = check_cache(v, fn, "v")) return st;
     if (!v_new) return fail(IP_EINVAL, "%s: v_new is NULL while v is given", fn);
@@ -232,16 +238,18 @@ ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cac
   const int kv_bytes = kv8 ? 0 : kv->row_dim * elem_bytes(kv->dtype);
   const int v_bytes = v ? v->row_dim * elem_bytes(v->dtype) : 0;
   if (kv_bytes % 16 || v_bytes % 16) return fail(IP_EUNSUPPORTED, "%s: kv / v rows must be whole 16-byte chunks", fn);
-  if (keys->dtype != pooled->dtype || keys->row_dim != pooled->row_dim)
-    return fail(IP_EINVAL, "%s: keys and pooled must share dtype and row_dim", fn);
-  if (keys->dtype == IP_FP8_E4M3FN) {
-    if (keys->row_dim != 128) return fail(IP_EUNSUPPORTED, "%s: FP8 keys need row_dim 128 (got %d)", fn, keys->row_dim);
-    if (key_dtype != IP_BF16 && key_dtype != IP_F32) return fail(IP_EUNSUPPORTED, "%s: key_new must be BF16 or F32", fn);
-  } else if (keys->dtype == IP_F32) {
-    if (keys->row_dim > 256) return fail(IP_EUNSUPPORTED, "%s: F32 keys need row_dim <= 256", fn);
-    if (key_dtype != IP_F32) return fail(IP_EUNSUPPORTED, "%s: F32 keys take an F32 key_new", fn);
-  } else {
-    return fail(IP_EUNSUPPORTED, "%s: keys must be FP8 or F32", fn);
+  if (idx) {
+    if (keys->dtype != pooled->dtype || keys->row_dim != pooled->row_dim)
+      return fail(IP_EINVAL, "%s: keys and pooled must share dtype and row_dim", fn);
+    if (keys->dtype == IP_FP8_E4M3FN) {
+      if (keys->row_dim != 128) return fail(IP_EUNSUPPORTED, "%s: FP8 keys need row_dim 128 (got %d)", fn, keys->row_dim);
+      if (key_dtype != IP_BF16 && key_dtype != IP_F32) return fail(IP_EUNSUPPORTED, "%s: key_new must be BF16 or F32", fn);
+    } else if (keys->dtype == IP_F32) {
+      if (keys->row_dim > 256) return fail(IP_EUNSUPPORTED, "%s: F32 keys need row_dim <= 256", fn);
+      if (key_dtype != IP_F32) return fail(IP_EUNSUPPORTED, "%s: F32 keys take an F32 key_new", fn);
+    } else {
+      return fail(IP_EUNSUPPORTED, "%s: keys must be FP8 or F32", fn);
+    }
   }
   if (seqs->batch > 65535) return fail(IP_EUNSUPPORTED, "%s: batch > 65535", fn);
   ip::AppendArgs a;
@@ -259,15 +267,15 @@ ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cac
   a.v_row_bytes = v_bytes;
   a.key_new = key_new;
   a.key_bf16 = key_dtype == IP_BF16;
-  a.keys = (uint8_t*)keys->data;
-  a.key_stride = keys->row_stride;
-  a.key_scale = keys->dtype == IP_FP8_E4M3FN ? keys->scale : nullptr;
-  a.dim = keys->row_dim;
+  a.keys = idx ? (uint8_t*)keys->data : nullptr;
+  a.key_stride = idx ? keys->row_stride : 0;
+  a.key_scale = idx && keys->dtype == IP_FP8_E4M3FN ? keys->scale : nullptr;
+  a.dim = idx ? keys->row_dim : 0;
   a.logit_new = logit_new;
   a.logits = logits;
-  a.pooled = (uint8_t*)pooled->data;
-  a.pooled_stride = pooled->row_stride;
-  a.pooled_scale = keys->dtype == IP_FP8_E4M3FN ? pooled->scale : nullptr;
+  a.pooled = idx ? (uint8_t*)pooled->data : nullptr;
+  a.pooled_stride = idx ? pooled->row_stride : 0;
+  a.pooled_scale = idx && keys->dtype == IP_FP8_E4M3FN ? pooled->scale : nullptr;
   return device_status(ip::launch_append(a, stream), fn);
 }
 

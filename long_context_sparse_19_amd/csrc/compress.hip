@@ -134,6 +134,7 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
   if (a.v)
     for (int i = tid; i < a.v_row_bytes / 16; i += NT)
       *(uint4*)(a.v + row * a.v_stride + 16 * i) = *(const uint4*)(a.v_new + (int64_t)b * a.v_row_bytes + 16 * i);
+  if (!a.keys) return;                           // a layer without indexer state (uniform)
   const bool on = tid < a.dim;
   float x = 0.f;
   if (on)

@@ -59,7 +59,8 @@ struct AppendArgs {
   int v_row_bytes;
   const void* key_new;         // [batch, dim], bf16 or f32
   int key_bf16;
-  uint8_t* keys;               // token key rows: fp8 codes (+ key_scale) or f32
+  uint8_t* keys;               // token key rows: fp8 codes (+ key_scale) or f32; null: the
+                               // layer keeps no indexer state (only kv / v are written)
   int64_t key_stride;
   float* key_scale;            // [token rows] (fp8) or null
   int dim;

@@ -28,14 +28,14 @@ def _dev(x: np.ndarray, device, dtype=None) -> torch.Tensor:
 class DeviceInputs:
     inp: Inputs
     seqs: _lib.Seqs
-    keys: _lib.Cache          # token-level index keys
-    logits: torch.Tensor
-    pooled: _lib.Cache        # pooled keys (output of compress)
+    keys: Optional[_lib.Cache]   # token-level index keys (None: an IndexCache follower)
+    logits: Optional[torch.Tensor]
+    pooled: Optional[_lib.Cache]  # pooled keys (output of compress)
     kv: _lib.Cache            # latent (bf16, or fp8 codes + scales) or K (f32)
     v: Optional[_lib.Cache]   # V (f32 only)
     q: torch.Tensor
-    q_idx: torch.Tensor
-    gates: torch.Tensor
+    q_idx: Optional[torch.Tensor]
+    gates: Optional[torch.Tensor]
     q_seq: torch.Tensor
     q_pos: torch.Tensor
     top_k: int
@@ -102,9 +102,45 @@ class NewTokens:
 
 
 def append(d: DeviceInputs, t: NewTokens, stream=None) -> None:
-    """Write each sequence's new token (at seq_lens[b] - 1) and pool a completed block."""
+    """Write each sequence's new token (at seq_lens[b] - 1) and pool a completed block
+    (a layer without indexer state: only the latent row)."""
+    if d.keys is None:
+        _lib.indexpool_append(d.seqs, t.kv_new, d.kv, None, None, None, None, None, v_new=t.v_new, v=d.v,
+                              stream=stream)
+        return
     _lib.indexpool_append(d.seqs, t.kv_new, d.kv, t.key_new, d.keys, t.logit_new, d.logits, d.pooled,
                           v_new=t.v_new, v=d.v, stream=stream)
+
+
+def upload_follower(f: Inputs, anchor: DeviceInputs, device="cuda") -> DeviceInputs:
+    """An IndexCache follower layer: its own latent cache and queries on the device,
+    the anchor's sequences; no indexer state (it attends over the anchor's selection)."""
+    w = f.w
+    kv = v = None
+    if f.latent is not None and f.latent_scale is not None:
+        kv = _lib.Cache(_dev(f.latent, device), _dev(f.latent_scale, device))
+    elif f.latent is not None:
+        kv = _lib.Cache(_dev(f.latent, device, torch.bfloat16))
+    else:
+        kv = _lib.Cache(_dev(f.k_cache, device))
+        v = _lib.Cache(_dev(f.v_cache, device))
+    q = _dev(f.q, device, torch.bfloat16 if w.attn_dtype == "bf16" else None)
+    return DeviceInputs(inp=f, seqs=anchor.seqs, keys=None, logits=None, pooled=None, kv=kv, v=v, q=q,
+                        q_idx=None, gates=None, q_seq=anchor.q_seq, q_pos=anchor.q_pos, top_k=anchor.top_k,
+                        scale=anchor.scale, dv=anchor.dv)
+
+
+class FollowerWorkspaces:
+    """Outputs of a follower layer's attention; the selection is the anchor's."""
+
+    def __init__(self, d: DeviceInputs, anchor_ws: "Workspaces"):
+        dev = d.q.device
+        self.sel = anchor_ws.sel
+        qdt = _lib.IP_BF16 if d.q.dtype == torch.bfloat16 else _lib.IP_F32
+        na = _lib.sparse_attn_workspace_bytes(d.n_q, d.q.shape[1], d.dv, d.top_k, qdt)
+        self.ws_attn = torch.empty(max(na, 16), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((d.n_q, d.q.shape[1], d.dv), dtype=d.q.dtype, device=dev)
+        self.lse = torch.empty((d.n_q, d.q.shape[1]), dtype=torch.float32, device=dev)
 
 
 class Workspaces:

@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import os
 from concurrent.futures import ThreadPoolExecutor
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 from typing import Optional
 
 import numpy as np
@@ -40,8 +40,9 @@ _TAGS = {
 }
 
 
-def _rng(seed: int, tag: str, chunk: int = 0) -> np.random.Generator:
-    return np.random.default_rng(np.random.SeedSequence([seed, _TAGS[tag], chunk]))
+def _rng(seed: int, tag: str, chunk: int = 0, layer: int = 0) -> np.random.Generator:
+    key = [seed, _TAGS[tag], chunk] + ([layer] if layer else [])
+    return np.random.default_rng(np.random.SeedSequence(key))
 
 
 def _threads() -> int:
@@ -57,11 +58,11 @@ def _chunked(rows: int, fn) -> None:
         list(ex.map(lambda a: fn(*a), spans))
 
 
-def _normal_rows(seed: int, tag: str, rows: int, cols: int) -> np.ndarray:
+def _normal_rows(seed: int, tag: str, rows: int, cols: int, layer: int = 0) -> np.ndarray:
     out = np.empty((rows, cols), dtype=np.float32)
 
     def fill(c, r0, r1):
-        _rng(seed, tag, c).standard_normal((r1 - r0, cols), dtype=np.float32, out=out[r0:r1])
+        _rng(seed, tag, c, layer).standard_normal((r1 - r0, cols), dtype=np.float32, out=out[r0:r1])
     _chunked(rows, fill)
     return out
 
@@ -131,6 +132,51 @@ class Inputs:
         return self.n_rows_tok // INDEX_KPOOL
 
 
+def _attention_cache(w: Workload, n_rows: int, layer: int):
+    """The latent cache of one DSA layer (bf16 bits, or fp8 codes + per-token scale),
+    or the float K and V caches of the f32 workload."""
+    seed = w.seed
+    latent = latent_scale = k_cache = v_cache = None
+    if w.attn_dtype == "bf16" and w.latent_fp8:
+        # fp8 latent tier: the same N(0,1) rows stored as e4m3fn codes with a
+        # per-token scale (amax / 448)
+        latent = np.empty((n_rows, w.dk), dtype=np.uint8)
+        latent_scale = np.empty(n_rows, dtype=np.float32)
+
+        def fill8(c, r0, r1):
+            x = _rng(seed, "latent", c, layer).standard_normal((r1 - r0, w.dk), dtype=np.float32)
+            latent[r0:r1], latent_scale[r0:r1] = _fp8_span(x)
+        _chunked(n_rows, fill8)
+    elif w.attn_dtype == "bf16":
+        latent = np.empty((n_rows, w.dk), dtype=np.uint16)
+
+        def fill(c, r0, r1):
+            latent[r0:r1] = to_bf16_bits(
+                _rng(seed, "latent", c, layer).standard_normal((r1 - r0, w.dk), dtype=np.float32))
+        _chunked(n_rows, fill)
+    else:
+        k_cache = _normal_rows(seed, "k", n_rows, w.dk, layer)
+        v_cache = _normal_rows(seed, "v", n_rows, w.dv, layer)
+    return latent, latent_scale, k_cache, v_cache
+
+
+def _query_rows(w: Workload, n_q: int, layer: int) -> np.ndarray:
+    return _normal_rows(w.seed, "q", n_q, w.n_heads * w.dk, layer).reshape(n_q, w.n_heads, w.dk)
+
+
+def follower_layer(inp: "Inputs", layer: int) -> "Inputs":
+    """DSA layer `layer` (>= 1) of an IndexCache group whose first layer is `inp`: the
+    same sequences and query positions, its own latent cache and attention queries,
+    and no indexer state (it attends over the first layer's selection)."""
+    w = inp.w
+    latent, latent_scale, k_cache, v_cache = _attention_cache(w, inp.n_rows_tok, layer)
+    qf = _query_rows(w, len(inp.q_pos), layer)
+    q = to_bf16_bits(qf) if w.attn_dtype == "bf16" else qf
+    return replace(inp, idx_keys=None, idx_scale=None, pool_logits=None, q_idx=None, gates=None,
+                   latent=latent, latent_scale=latent_scale, k_cache=k_cache, v_cache=v_cache, q=q,
+                   salient_rows=np.zeros(0, dtype=np.int64))
+
+
 def make_inputs(w: Workload, with_attention: bool = True) -> Inputs:
     """Draw every input of workload ``w`` (host numpy arrays)."""
     B = w.batch
@@ -189,26 +235,7 @@ def make_inputs(w: Workload, with_attention: bool = True) -> Inputs:
     # attention caches
     latent = k_cache = v_cache = latent_scale = None
     if with_attention:
-        if w.attn_dtype == "bf16" and w.latent_fp8:
-            # fp8 latent tier: the same N(0,1) rows stored as e4m3fn codes with a
-            # per-token scale (amax / 448)
-            latent = np.empty((n_rows, w.dk), dtype=np.uint8)
-            latent_scale = np.empty(n_rows, dtype=np.float32)
-
-            def fill8(c, r0, r1):
-                x = _rng(seed, "latent", c).standard_normal((r1 - r0, w.dk), dtype=np.float32)
-                latent[r0:r1], latent_scale[r0:r1] = _fp8_span(x)
-            _chunked(n_rows, fill8)
-        elif w.attn_dtype == "bf16":
-            latent = np.empty((n_rows, w.dk), dtype=np.uint16)
-
-            def fill(c, r0, r1):
-                latent[r0:r1] = to_bf16_bits(
-                    _rng(seed, "latent", c).standard_normal((r1 - r0, w.dk), dtype=np.float32))
-            _chunked(n_rows, fill)
-        else:
-            k_cache = _normal_rows(seed, "k", n_rows, w.dk)
-            v_cache = _normal_rows(seed, "v", n_rows, w.dv)
+        latent, latent_scale, k_cache, v_cache = _attention_cache(w, n_rows, 0)
 
     # queries
     n_q = w.n_rows
@@ -219,7 +246,7 @@ def make_inputs(w: Workload, with_attention: bool = True) -> Inputs:
         assert B == 1
         q_seq = np.zeros(n_q, dtype=np.int32)
         q_pos = (int(seq_lens[0]) - n_q + np.arange(n_q)).astype(np.int32)
-    qf = _normal_rows(seed, "q", n_q, w.n_heads * w.dk).reshape(n_q, w.n_heads, w.dk)
+    qf = _query_rows(w, n_q, 0)
     qif = _normal_rows(seed, "q_idx", n_q, w.idx_heads * w.idx_dim).reshape(n_q, w.idx_heads, w.idx_dim)
     gates = (_normal_rows(seed, "gates", n_q, w.idx_heads) * np.float32(0.5)).astype(np.float32)
     if w.attn_dtype == "bf16":

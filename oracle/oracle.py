@@ -54,6 +54,11 @@ in the design notes):
   576 dims), and attention uses sigma_t * dec(code_t) for K and its first 512 dims
   for V.  Reading notes, section 4 "The serving stack" (INT8 / FP8 / BF16 chosen
   per cache tier).
+* R10 IndexCache: the DSA layers form groups; the first layer of a group runs the
+  indexer (pool, score, select) and every other layer of the group attends, with its
+  own queries and latent cache, over that layer's selected blocks, keeping no
+  indexer state of its own.  Reading notes, section 2, sub-section "IndexPool" (the
+  cross-layer variant of pooling the index is named IndexCache, nothing more).
 """
 from __future__ import annotations
 
@@ -345,3 +350,15 @@ def attention_rows(inp, ids, scale: float, dv: int, rows=None):
         outs.append(O)
         lses.append(lse)
     return np.stack(outs), np.stack(lses)
+
+
+# ----------------------------------------------------------------------------- IndexCache
+def indexcache_group(anchor, followers, scale: float, dv: int, top_k: int, rows=None):
+    """R10: the first layer (`anchor`) selects; it and every follower layer attend over
+    that one selection.  Returns the anchor's ids [n, top_k] and one (O, lse) per layer,
+    anchor first."""
+    pooled, sigma, *_ = compress(anchor)
+    ids, _ = score_select(anchor, pooled_values(pooled, sigma), top_k, rows=rows)
+    outs = [attention_rows(x, ids, scale, dv, rows=rows) for x in [anchor, *followers]]
+    return ids, outs
+

@@ -80,15 +80,19 @@ def test_compress_rejects_bad_arguments(L):
     assert compress(L, seqs(), cache(L, dtype=L.IP_F32, row_dim=512, stride=2048, scale=None)) == L.IP_EUNSUPPORTED
 
 
-def append(L, s, kv=None, v=None, v_new=None, key_dtype=None, keys=None, pooled=None, kv_new=FAKE,
+_DEFAULT = object()
+
+
+def append(L, s, kv=None, v=None, v_new=None, key_dtype=None, keys=_DEFAULT, pooled=_DEFAULT, kv_new=FAKE,
            key_new=FAKE, logit_new=FAKE, logits=FAKE):
     kv = cache(L, dtype=L.IP_BF16, row_dim=576, stride=1152, scale=None) if kv is None else kv
-    keys = cache(L) if keys is None else keys
-    pooled = keys if pooled is None else pooled
+    keys = cache(L) if keys is _DEFAULT else keys
+    pooled = keys if pooled is _DEFAULT else pooled
     key_dtype = L.IP_BF16 if key_dtype is None else key_dtype
     return L.LIB.indexpool_append(ctypes.byref(s), kv_new, ctypes.byref(kv), v_new,
                                   None if v is None else ctypes.byref(v), key_new, key_dtype,
-                                  ctypes.byref(keys), logit_new, logits, ctypes.byref(pooled), None)
+                                  None if keys is None else ctypes.byref(keys), logit_new, logits,
+                                  None if pooled is None else ctypes.byref(pooled), None)
 
 
 def test_append_rejects_bad_arguments(L):
@@ -107,6 +111,12 @@ def test_append_rejects_bad_arguments(L):
     assert append(L, s, kv=kv8, kv_new=FAKE + 4) == L.IP_EINVAL                   # bf16 rows, 8-byte aligned
     assert append(L, s, kv=cache(L, row_dim=576, stride=576, scale=None)) == L.IP_EINVAL
     assert append(L, s, kv=cache(L, dtype=L.IP_BF16, row_dim=12, stride=32, scale=None)) == L.IP_EUNSUPPORTED
+    # a layer without indexer state: keys NULL, and then every indexer argument NULL
+    nokeys = dict(keys=None, key_new=None, logit_new=None, logits=None, pooled=None)
+    assert append(L, s, **{**nokeys, "key_new": FAKE}) == L.IP_EINVAL
+    assert append(L, s, **{**nokeys, "logits": FAKE}) == L.IP_EINVAL
+    assert append(L, s, **{**nokeys, "pooled": cache(L)}) == L.IP_EINVAL
+    assert append(L, s, **{**nokeys, "kv_new": None}) == L.IP_EINVAL
     assert append(L, s, key_dtype=L.IP_FP8_E4M3FN) == L.IP_EUNSUPPORTED
     assert append(L, s, keys=cache(L, row_dim=64, stride=64)) == L.IP_EUNSUPPORTED
     assert append(L, s, keys=cache(L, scale=None)) == L.IP_EINVAL

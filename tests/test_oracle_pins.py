@@ -454,3 +454,58 @@ def test_append_quantises_the_latent_row_for_the_fp8_tier():
         assert np.array_equal(e["kv"], y.view(torch.uint8).numpy())
         back = s * y.to(torch.float64).numpy()
         assert np.all(np.abs(back - x) <= np.maximum(np.abs(x) * 2.0 ** -4, s * 2.0 ** -9) + 1e-300)
+
+
+# --------------------------------------------------------------------------- IndexCache
+def _masked_sdpa(q, K, V, scale, mask):
+    """torch SDPA in float64 over all tokens with a boolean [n, T] mask."""
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]              # [1, H, n, d]
+    Kt = torch.from_numpy(K)[None, None].expand(1, q.shape[1], -1, -1)
+    Vt = torch.from_numpy(V)[None, None].expand(1, q.shape[1], -1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=torch.from_numpy(mask)[None, None],
+                                                         scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def test_indexcache_followers_attend_over_the_first_layers_selection():
+    """R10: a follower layer's output is dense attention over its own latent rows
+    restricted (by a token mask built from the first layer's ids, not by a gather) to
+    the selected blocks' tokens at or before the query; the followers' caches differ
+    from the first layer's."""
+    from long_context_sparse_19_amd.configs import DECODE_INDEXCACHE, scaled_down
+    from long_context_sparse_19_amd.inputs import make_inputs, follower_layer, bf16_bits_to_f32
+    w = scaled_down(DECODE_INDEXCACHE, 512, batch=2, top_k=16)
+    anchor = make_inputs(w)
+    followers = [follower_layer(anchor, l) for l in range(1, w.layers)]
+    ids, outs = O.indexcache_group(anchor, followers, w.scale, w.dv, w.top_k)
+    assert len(outs) == w.layers
+    for l, x in enumerate([anchor, *followers]):
+        assert l == 0 or not np.array_equal(x.latent, anchor.latent)
+        q = bf16_bits_to_f32(x.q).astype(np.float64)
+        for b in range(w.batch):
+            T = int(x.seq_lens[b])
+            KV = bf16_bits_to_f32(x.latent[O.token_rows(x, b, np.arange(T))]).astype(np.float64)
+            t = np.arange(T)
+            sel = np.zeros(T, bool)
+            for j in ids[b][ids[b] >= 0]:
+                sel[4 * j: 4 * j + 4] = True
+            mask = (sel & (t <= int(x.q_pos[b])))[None]
+            ref = _masked_sdpa(q[b:b + 1], KV, KV[:, : w.dv].copy(), w.scale, mask)
+            np.testing.assert_allclose(outs[l][0][b], ref[0], rtol=1e-10, atol=1e-12)
+
+
+def test_indexcache_with_every_block_selected_is_each_layers_own_dense_attention():
+    """When the first layer keeps every block, each follower's output is its own dense
+    causal attention, whatever the first layer's scores were."""
+    from long_context_sparse_19_amd.configs import DECODE_INDEXCACHE, scaled_down
+    from long_context_sparse_19_amd.inputs import make_inputs, follower_layer, bf16_bits_to_f32
+    w = scaled_down(DECODE_INDEXCACHE, 128, batch=2, top_k=64)
+    anchor = make_inputs(w)
+    f = follower_layer(anchor, 2)
+    _, outs = O.indexcache_group(anchor, [f], w.scale, w.dv, w.top_k)
+    q = bf16_bits_to_f32(f.q).astype(np.float64)
+    for b in range(w.batch):
+        T = int(f.seq_lens[b])
+        KV = bf16_bits_to_f32(f.latent[O.token_rows(f, b, np.arange(T))]).astype(np.float64)
+        ref = _sdpa_causal(q[b:b + 1], KV, KV[:, : w.dv].copy(), w.scale, np.array([T - 1]))
+        np.testing.assert_allclose(outs[1][0][b], ref[0], rtol=1e-11, atol=1e-12)
