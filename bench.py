@@ -7,7 +7,11 @@ One step = one pass of the whole path over one batch:
            select the top-k (index_score_topk), attend over the selected tokens
            (sparse_attn_decode);
   prefill: pool the chunk's new blocks, score/select for every query token,
-           sparse_attn_prefill.
+           sparse_attn_prefill;
+  IndexCache group (decode_indexcache): the decode step of the group's first DSA
+           layer, then for each other layer of the group its new latent row
+           (indexpool_append without indexer state) and its attention over the
+           first layer's selection; `value` counts (query token, layer) pairs.
 The default workload is decode of 8 sequences x 131072 tokens with top-512
 blocks (2048 tokens).  Inputs are seeded synthetic data of the workload's shape,
 resident in HBM before timing; R replicas of every device buffer are rotated so
@@ -76,6 +80,7 @@ def algorithmic_bytes(inp, w):
     attn_b = U * row_b + H * w.dk * 2 + H * w.dv * 2 + k * 4
     sel_b = k * 4
     fp8 = inp.idx_scale is not None
+    kv_in = kv_out = 0
     if w.mode == "decode":
         kv_in = w.dk * (2 if w.attn_dtype == "bf16" else 4) + (0 if w.attn_dtype == "bf16" else w.dv * 4)
         kv_out = (w.dk + 4) if w.latent_fp8 else kv_in                # fp8 tier: codes + scale
@@ -85,9 +90,12 @@ def algorithmic_bytes(inp, w):
         pool_b = len(inp.seq_lens) * grow
     else:
         pool_b = (w.n_query // 4) * (4 * (D + 4 + 4) + D + 4)
+    # an IndexCache follower layer: its new latent row written, then attention over the
+    # first layer's selection (ids read again), no indexer traffic
+    fol_b = attn_b.sum() + (len(inp.seq_lens) * (kv_in + kv_out) if w.mode == "decode" else 0)
     return dict(score=int(score_b.sum()), select=int(sel_b * len(n)), attention=int(attn_b.sum()),
                 pool=int(pool_b), total=int(score_b.sum() + sel_b * len(n) + attn_b.sum() + pool_b),
-                U=U)
+                follower=int(fol_b), U=U)
 
 
 def kernel_bytes(inp, w, ab):
@@ -154,7 +162,7 @@ def attention_flops(U, w):
     return int(2 * w.n_heads * (w.dk + w.dv) * U.sum())
 
 
-def cpu_baseline(inp, w, budget_s=12.0):
+def cpu_baseline(inp, w, budget_s=12.0, followers=()):
     """The oracle's step (decode: append the new token and pool its block; prefill:
     pool the row's block; then score, select, attend) on whole query rows of the
     same workload, for about budget_s seconds of CPU time."""
@@ -202,7 +210,11 @@ def cpu_baseline(inp, w, budget_s=12.0):
             S = O.score(O._to_f64(inp.q_idx[r]), inp.gates[r], keys)
             ids = O.select(S, b_q, w.top_k)
             O.attention_rows(inp, ids[None], w.scale, w.dv, rows=[r])
-            done += 1
+            for f in followers:      # IndexCache: the other layers over the same ids
+                if new is not None:
+                    O.append(f, new["kv_new"], new["key_new"], new["logit_new"], only={b})
+                O.attention_rows(f, ids[None], w.scale, w.dv, rows=[r])
+            done += w.layers
             if time.perf_counter() - t0 > budget_s:
                 break
         if time.perf_counter() - t0 > budget_s:
@@ -210,7 +222,7 @@ def cpu_baseline(inp, w, budget_s=12.0):
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "query-tokens/s", "cores": blas_threads,
             "kind": "oracle", "host_cores_available": cores,
-            "sample": f"{done} query rows of the {w.name} workload (sequences {seqs}), oracle cache growth / "
+            "sample": f"{done} (query row, layer) pairs of the {w.name} workload (sequences {seqs}), oracle cache growth / "
                       f"pooling of the new block + float64 scoring over every earlier block + selection + attention, "
                       f"{dt:.1f} s"}
 
@@ -237,7 +249,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "max_ctx", "ragged", "prefill", "tiny", "decode_fp8kv"])
+    from long_context_sparse_19_amd.configs import WORKLOADS as _W
+    ap.add_argument("--workload", default="decode", choices=list(_W))
     ap.add_argument("--replicas", type=int, default=0, help="rotated input copies (0 = auto, >= 1 GiB touched)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of HIP graphs")
@@ -256,15 +269,17 @@ def main():
     import torch
     from long_context_sparse_19_amd import _lib, device as D
     from long_context_sparse_19_amd.configs import WORKLOADS
-    from long_context_sparse_19_amd.inputs import make_inputs, new_tokens
+    from long_context_sparse_19_amd.inputs import make_inputs, new_tokens, follower_layer
 
     w = WORKLOADS[args.workload]
     t_gen = time.perf_counter()
     inp = make_inputs(w)
+    # IndexCache: the group's other DSA layers (own latent cache and queries, no indexer)
+    followers = [follower_layer(inp, l) for l in range(1, w.layers)]
     print(f"[bench] {w.name}: inputs drawn in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     ab = algorithmic_bytes(inp, w)
-    step_bytes = ab["total"]
-    R = args.replicas or max(1, min(32, math.ceil((1 << 30) / max(1, step_bytes))))
+    step_bytes = ab["total"] + len(followers) * ab["follower"]
+    R = args.replicas or max(1, min(32 // w.layers, math.ceil((1 << 30) / max(1, step_bytes))))
     base = D.upload(inp)
     reps = [base]
     for _ in range(R - 1):
@@ -277,9 +292,14 @@ def main():
                                       "q": base.q.clone(), "q_idx": base.q_idx.clone(), "gates": base.gates.clone()}))
     for d in reps:
         D.compress(d)            # cache build (untimed)
+    fbase = [D.upload_follower(f, base) for f in followers]
+    freps = [fbase] + [[D.DeviceInputs(**{**fd.__dict__, "seqs": reps[i].seqs,
+                                           "kv": _lib.Cache(fd.kv.data.clone(), None if fd.kv.scale is None else fd.kv.scale.clone()),
+                                           "q": fd.q.clone()}) for fd in fbase] for i in range(1, R)]
     # prefill keeps its whole score matrix (one pass over the 8192 rows; the
     # library otherwise scores in passes of at most 256 MB)
     wss = [D.Workspaces(d, keep_scores=(w.mode == "prefill")) for d in reps]
+    fwss = [[D.FollowerWorkspaces(fd, wss[i]) for fd in freps[i]] for i in range(R)]
     if w.mode == "decode":
         # each sequence's new token (at seq_lens - 1, the query position)
         toks = D.NewTokens(new_tokens(w, len(inp.seq_lens), seed=w.seed))
@@ -297,6 +317,9 @@ def main():
             D.compress(d, block_begin=begin, max_blocks=max_new)
         D.score_topk(d, ws)
         D.attention(d, ws)
+        for fd, fws in zip(freps[i % R], fwss[i % R]):
+            D.append(fd, toks)
+            D.attention(fd, fws)
 
     graphs = None
     if not args.eager:
@@ -334,7 +357,7 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt * 1e3 / K
-    value = w.n_rows / (ms / 1e3)
+    value = w.n_rows * w.layers / (ms / 1e3)     # (query token, DSA layer) pairs per second
 
     # --- timed region 2: the same K steps launched one call at a time, every kernel
     # launch carrying HIP events that receive its dispatch start / end times (the
@@ -387,7 +410,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, w)
+        cpu = cpu_baseline(inp, w, followers=followers)
 
     line = {
         "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": K,
@@ -395,7 +418,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "context": w.seq_len, "query_rows": w.n_rows,
                    "top_k_blocks": w.top_k, "index_keys": w.idx_key_dtype, "latent": "fp8" if w.latent_fp8 else w.attn_dtype,
-                   "replicas": R, "launch": "eager" if args.eager else "hip-graph",
+                   "dsa_layers": w.layers, "replicas": R, "launch": "eager" if args.eager else "hip-graph",
                    "parallelism": "single GPU"},
         "hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "algorithmic_bytes_per_step": step_bytes,

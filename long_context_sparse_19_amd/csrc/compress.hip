@@ -134,15 +134,6 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
   if (a.v)
     for (int i = tid; i < a.v_row_bytes / 16; i += NT)
       *(uint4*)(a.v + row * a.v_stride + 16 * i) = *(const uint4*)(a.v_new + (int64_t)b * a.v_row_bytes + 16 * i);
-  if (!a.keys) return;                           // a layer without indexer state (uniform)
-  const bool on = tid < a.dim;
-  float x = 0.f;
-  if (on)
-    x = a.key_bf16 ? bf16_to_f32(((const uint16_t*)a.key_new)[(int64_t)b * a.dim + tid])
-                   : ((const float*)a.key_new)[(int64_t)b * a.dim + tid];
-  const float lnew = a.logit_new[b];
-  if (tid == 0) a.logits[row] = lnew;
-  const bool fp8 = a.key_scale != nullptr;
   auto block_max = [&](float v) {                // max over the workgroup (all threads call)
     v = wave_max(v);
     if (lane == 0) red[wv] = v;
@@ -175,6 +166,15 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
     if (kon) *(uint32_t*)(a.kv + row * a.kv_stride + 4 * tid) = packed;
     if (tid == 0) a.kv_scale[row] = kamax / 448.0f;
   }
+  if (!a.keys) return;                           // a layer without indexer state (uniform)
+  const bool on = tid < a.dim;
+  float x = 0.f;
+  if (on)
+    x = a.key_bf16 ? bf16_to_f32(((const uint16_t*)a.key_new)[(int64_t)b * a.dim + tid])
+                   : ((const float*)a.key_new)[(int64_t)b * a.dim + tid];
+  const float lnew = a.logit_new[b];
+  if (tid == 0) a.logits[row] = lnew;
+  const bool fp8 = a.key_scale != nullptr;
   // the new token's key: fp8 with sigma = amax / 448, or the float key as is
   uint32_t code = 0;
   float sigma = 0.f;

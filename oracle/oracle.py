@@ -238,6 +238,10 @@ def append(inp, kv_new, key_new, logit_new, only=None):
             # R9: the latent row goes into the fp8 tier quantised per token
             kc, ks, kvv = quantize_tokens(_to_f64(e["kv"])[None])
             e.update(kv=kc[0], kv_sigma=float(ks[0]), kv_v=kvv[0])
+        if inp.idx_keys is None:
+            # R10: a layer without indexer state keeps only the latent row
+            out.append(e)
+            continue
         if fp8:
             codes, sigma, v = quantize_tokens(x[None])
             e.update(key=codes[0], sigma=float(sigma[0]), v=v[0])

@@ -357,3 +357,72 @@ def test_full_size_prefill_sampled():
     rows = np.sort(rng.choice(PREFILL.n_query, 24, replace=False))
     rows = np.unique(np.concatenate([[0, PREFILL.n_query - 1], rows]))
     full_case(PREFILL, rows=rows, keep_scores=False)
+
+
+# ---------------------------------------------------------------- IndexCache
+@pytest.mark.parametrize("fp8kv", [False, True], ids=["bf16kv", "fp8kv"])
+def test_indexcache_group_parity(fp8kv):
+    """A group of 4 DSA layers: the first runs pool -> score -> top-k on the device;
+    every layer (the first included) attends over that one selection with its own
+    queries and latent cache, against the oracle's attention over the same ids."""
+    from long_context_sparse_19_amd.configs import DECODE_INDEXCACHE
+    from long_context_sparse_19_amd.inputs import follower_layer
+    D = _dev()
+    w = scaled_down(DECODE_INDEXCACHE.with_(latent_fp8=fp8kv), 4 * 6001, batch=3)
+    log(f"[case] indexcache {w.name} layers={w.layers} fp8kv={fp8kv}")
+    anchor = make_inputs(w)
+    d = D.upload(anchor)
+    D.compress(d)
+    ws = D.Workspaces(d)
+    D.score_topk(d, ws)
+    D.attention(d, ws)
+    followers = [follower_layer(anchor, l) for l in range(1, w.layers)]
+    fds = [D.upload_follower(f, d) for f in followers]
+    fws = [D.FollowerWorkspaces(fd, ws) for fd in fds]
+    for fd, fw in zip(fds, fws):
+        D.attention(fd, fw)
+    torch.cuda.synchronize()
+    gsel = ws.sel.cpu().numpy()
+    # the selection against the oracle's, within the tie band
+    pooled, sigma, *_ = O.compress(anchor)
+    o_ids, scores = O.score_select(anchor, O.pooled_values(pooled, sigma), w.top_k)
+    for r in range(w.n_rows):
+        P.check_selection(gsel[r], o_ids[r], scores[r], int(anchor.q_pos[r]) // 4, w.top_k)
+    # every layer over the device's selection
+    for l, (x, out, lse) in enumerate([(anchor, ws.out, ws.lse)] + [(f, fw.out, fw.lse) for f, fw in zip(followers, fws)]):
+        o_out, o_lse = O.attention_rows(x, gsel, w.scale, w.dv)
+        err = P.check_attention(_out_np(out), o_out, "bf16")
+        P.check_lse(lse.cpu().numpy(), o_lse, "bf16")
+        log(f"  layer {l} ok (max-abs {err:.2e})")
+
+
+def test_append_without_indexer_state():
+    """indexpool_append with no keys (an IndexCache follower) writes only the new
+    latent rows: bf16 copied, fp8 quantised per token; no other row moves."""
+    from long_context_sparse_19_amd.configs import DECODE_INDEXCACHE
+    from long_context_sparse_19_amd.inputs import follower_layer
+    D = _dev()
+    for fp8kv in (False, True):
+        w = scaled_down(DECODE_INDEXCACHE.with_(latent_fp8=fp8kv), 1024, batch=4)
+        anchor = make_inputs(w)
+        anchor.seq_lens = (anchor.seq_lens - np.arange(4)).astype(np.int32)
+        f = follower_layer(anchor, 1)
+        log(f"[case] append without indexer state fp8kv={fp8kv} lens={anchor.seq_lens.tolist()}")
+        d = D.upload(anchor)
+        fd = D.upload_follower(f, d)
+        new = new_tokens(w, len(anchor.seq_lens), seed=11)
+        kv0 = _bits(fd.kv.data)
+        D.append(fd, D.NewTokens(new))
+        torch.cuda.synchronize()
+        kv = _bits(fd.kv.data)
+        rows = []
+        for b in range(len(anchor.seq_lens)):
+            row = int(O.token_rows(f, b, int(anchor.seq_lens[b]) - 1))
+            rows.append(row)
+            if fp8kv:
+                c, s_, v = O.quantize_tokens(O._to_f64(new["kv_new"][b])[None])
+                P.check_pooled_fp8(kv[row][None], fd.kv.scale.cpu().numpy()[row][None], c, s_, v, np.abs(v), [0])
+            else:
+                assert np.array_equal(kv[row], new["kv_new"][b])
+        other = np.setdiff1d(np.arange(kv.shape[0]), rows)
+        assert np.array_equal(kv[other], kv0[other])
