@@ -132,7 +132,7 @@ def _chunk_size(max_seq_len):
 
 # the sources each kernel is built from (the HBM counters in profiles/ are tied to them)
 _KERNEL_SOURCES = {"attention": "attn.hip", "combine": "attn.hip", "score": "score.hip", "topk": "topk.hip",
-                   "compress": "compress.hip", "append": "compress.hip"}
+                   "compress": "compress.hip", "append": "compress.hip", "kda": "kda.hip"}
 
 
 def _source_hash(kind):
@@ -244,13 +244,119 @@ def copy_probe(mb):
     print(json.dumps({"copy_probe_bytes": n, "copies": 10}))
 
 
+KDA_METRIC = "KDA decode tokens/s + achieved HBM GB/s (linear-attention state step, 64 heads x 128^2 fp32 state)"
+
+
+def kda_bytes(kw):
+    """Algorithmic bytes of one KDA decode step.  Per (sequence, head): the 128 x 128
+    fp32 state read and written, x_q / x_k / x_v (3 x 128 bf16), alpha (128 fp32),
+    beta, the conv state (3 x 3 x 128 fp32) read and written, the output (128 fp32);
+    per head once: the conv weights (3 x 128 x 4 fp32)."""
+    d = kw.head_dim
+    per = 2 * d * d * 4 + 3 * d * 2 + d * 4 + 4 + 2 * 9 * d * 4 + d * 4
+    return kw.batch * kw.heads * per + kw.heads * 3 * d * 4 * 4
+
+
+def kda_cpu_baseline(kin, kw, budget_s=12.0):
+    """The oracle's decode step on whole sequences for about budget_s of CPU time."""
+    import numpy as np
+    from oracle import kda as K
+    from long_context_sparse_19_amd.inputs import bf16_bits_to_f32
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b = done % kw.batch
+        K.decode_step(kin["state"][b:b + 1], kin["conv_state"][b:b + 1], bf16_bits_to_f32(kin["xq"][0][b:b + 1]),
+                      bf16_bits_to_f32(kin["xk"][0][b:b + 1]), bf16_bits_to_f32(kin["xv"][0][b:b + 1]),
+                      kin["alpha"][0][b:b + 1], kin["beta"][0][b:b + 1], kin["conv_w"])
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": blas_threads, "kind": "oracle",
+            "host_cores_available": len(os.sched_getaffinity(0)),
+            "sample": f"{done} sequence steps of the {kw.name} workload (all {kw.heads} heads, float64), {dt:.1f} s"}
+
+
+def kda_main(args, kw):
+    """KDA decode step: every timed step updates the state of all sequences and heads
+    in place; R state replicas rotate so that successive steps miss the 256 MB cache."""
+    import numpy as np
+    import torch
+    from long_context_sparse_19_amd import _lib, device as D
+    from long_context_sparse_19_amd.inputs import kda_inputs
+    kin = kda_inputs(kw, 1)
+    nbytes = kda_bytes(kw)
+    R = args.replicas or max(1, min(32, math.ceil((1 << 30) / nbytes)))
+    reps = [D.KdaDevice(kin) for _ in range(R)]
+    torch.cuda.synchronize()
+    K = args.steps
+    graph = None
+    if not args.eager:
+        # the K timed steps in one HIP graph (one kernel per step: replaying a graph
+        # per step would leave the GPU waiting on the host)
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for d in reps:
+                d.step(0, alternate=False)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(K):
+                reps[(args.warmup + i) % R].step(0, alternate=False)
+        torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        reps[i % R].step(0, alternate=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K):
+            reps[(args.warmup + i) % R].step(0, alternate=False)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for e0, e1 in ev:
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    for i in range(K):
+        _lib.time_next_launch(_lib.K_KDA, *ev[i])
+        reps[(args.warmup + i) % R].step(0, alternate=False)
+    torch.cuda.synchronize()
+    kt = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    ach = nbytes / (kt * 1e-3) / 1e9
+    line = {
+        "metric": KDA_METRIC, "value": kw.batch / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": kw.name, "batch": kw.batch, "heads": kw.heads, "head_dim": kw.head_dim,
+                   "state": "fp32", "replicas": R, "launch": "eager" if args.eager else "hip-graph",
+                   "parallelism": "single GPU"},
+        "algorithmic_bytes_per_step": nbytes,
+        "hbm_gbps": nbytes / (ms * 1e-3) / 1e9,
+        "kernels": {"kda": {"avg_ms": kt, "bytes": nbytes, "GBps": ach}},
+        "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel", "achieved": ach, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": measured_traffic("kda", kw.name),
+                     "avg_ms": kt, "launches": K},
+        "cpu_baseline": None if args.no_cpu_baseline else kda_cpu_baseline(kin, kw),
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    from long_context_sparse_19_amd.configs import WORKLOADS as _W
-    ap.add_argument("--workload", default="decode", choices=list(_W))
+    from long_context_sparse_19_amd.configs import WORKLOADS as _W, KDA_WORKLOADS as _KW
+    ap.add_argument("--workload", default="decode", choices=list(_W) + list(_KW))
     ap.add_argument("--replicas", type=int, default=0, help="rotated input copies (0 = auto, >= 1 GiB touched)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of HIP graphs")
@@ -264,6 +370,10 @@ def main():
         print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (got --gpus {args.gpus}); "
               f"sharding across GPUs is described in the design notes but not built.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in _KW:
+        kda_main(args, _KW[args.workload])
+        return
 
     import numpy as np
     import torch

@@ -230,6 +230,43 @@ ip_status sparse_attn_prefill(const ip_seqs* seqs, int32_t n_q, const int32_t* q
                               int32_t top_k, void* out, float* lse, void* ws, size_t ws_bytes,
                               hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------
+ * kda_decode_step -- one decode step of the linear-attention (KDA) half of the
+ * hybrid layer.  G2C Brief, section "KDA carries fixed state through most layers":
+ * a gated delta-rule recurrence over a fixed matrix state per head, with a short
+ * convolution of width 4 and learned gates; the release summary gives 64 heads of
+ * width 128 (a 128 x 128 state per head, independent of the context length).
+ *
+ * For every sequence b and head h (d = 128, channels c of head h = h*128 + 0..127):
+ *     y_c = SiLU(w_c0 x_{t-3,c} + w_c1 x_{t-2,c} + w_c2 x_{t-1,c} + w_c3 x_{t,c})
+ *           for each of q, k, v, with x_{t-3..t-1} from conv_in; conv_out receives
+ *           them shifted by one token (x_{t-2}, x_{t-1}, x_t)
+ *     q, k  scaled by 1 / sqrt(|.|^2 + 1e-6) over the head's 128 channels
+ *     S'    = Diag(alpha[b, h, :]) S          (row i = key channel i)
+ *     S     = S' + beta[b, h] * k (v - S'^T k)^T
+ *     out[b, h, :] = S^T q / sqrt(128)
+ *
+ *  xq, xk, xv  device [batch, n_heads * 128], BF16 (x_dtype = IP_BF16), before the
+ *              convolution
+ *  alpha    device [batch, n_heads, 128] fp32 decay per key channel, in (0, 1]
+ *  beta     device [batch, n_heads] fp32 write strength
+ *  conv_w   device [3 (q, k, v), n_heads * 128, 4] fp32 taps (t-3 .. t), 16-byte
+ *           aligned
+ *  conv_in  device [batch, 3 (q, k, v), 3 (t-3 .. t-1), n_heads * 128] fp32, read
+ *  conv_out device, the same layout, written; must not overlap conv_in (the caller
+ *           alternates two buffers from step to step)
+ *  state    device [batch, n_heads, 128, 128] fp32, read and updated in place,
+ *           16-byte aligned
+ *  out      device [batch, n_heads, 128] fp32, 16-byte aligned
+ * Errors: head_dim other than 128, a dtype other than BF16, NULL or misaligned
+ * pointers, overlapping conv buffers -> IP_EUNSUPPORTED / IP_EINVAL before any
+ * launch.
+ * ------------------------------------------------------------------------------- */
+ip_status kda_decode_step(int32_t batch, int32_t n_heads, int32_t head_dim, const void* xq,
+                          const void* xk, const void* xv, int32_t x_dtype, const float* alpha,
+                          const float* beta, const float* conv_w, const float* conv_in,
+                          float* conv_out, float* state, float* out, hipStream_t stream);
+
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char* ip_last_error(void);
 
@@ -237,7 +274,7 @@ const char* ip_last_error(void);
  * goes through hipExtLaunchKernelGGL with `start` / `stop`, so the two events
  * receive that dispatch's own start and end times (the timestamps a kernel trace
  * reports).  kernel_id: 1 compress, 2 score, 3 top-k, 4 attention, 5 split
- * combine, 6 append.  Hooks for different ids may be
+ * combine, 6 append, 7 KDA decode step.  Hooks for different ids may be
  * armed together; each is consumed by one launch.  Passing NULL for one event
  * only is IP_EINVAL; kernel_id 0 with both NULL disarms every hook.  Use it
  * outside stream capture.  Not needed for normal use. */

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libindexpool.so")
 
 IP_OK, IP_EINVAL, IP_EUNSUPPORTED, IP_EWORKSPACE, IP_EDEVICE = range(5)
 IP_F32, IP_BF16, IP_FP8_E4M3FN = range(3)
-K_COMPRESS, K_SCORE, K_TOPK, K_ATTN, K_COMBINE, K_APPEND = 1, 2, 3, 4, 5, 6
+K_COMPRESS, K_SCORE, K_TOPK, K_ATTN, K_COMBINE, K_APPEND, K_KDA = 1, 2, 3, 4, 5, 6, 7
 
 _c_void_p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -68,11 +68,13 @@ def _load() -> ctypes.CDLL:
     lib.sparse_attn_prefill.argtypes = [P(IpSeqs), _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                         _i32, ctypes.c_float, P(IpCache), P(IpCache), _c_void_p, _i32,
                                         _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]
+    lib.kda_decode_step.argtypes = [_i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p,
+                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]
     lib.ip_last_error.restype = ctypes.c_char_p
     lib.ip_version.restype = ctypes.c_char_p
     lib.ip_time_next_launch.argtypes = [_i32, _c_void_p, _c_void_p]
     for fn in ("indexpool_compress", "indexpool_append", "index_score_topk", "sparse_attn_decode",
-               "sparse_attn_prefill", "ip_time_next_launch"):
+               "sparse_attn_prefill", "kda_decode_step", "ip_time_next_launch"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -80,7 +82,7 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 EXPORTED = ("indexpool_compress", "indexpool_append", "index_scores_ld", "index_score_topk_workspace_bytes", "index_score_topk",
-            "sparse_attn_workspace_bytes", "sparse_attn_decode", "sparse_attn_prefill", "ip_last_error",
+            "sparse_attn_workspace_bytes", "sparse_attn_decode", "sparse_attn_prefill", "kda_decode_step", "ip_last_error",
             "ip_time_next_launch", "ip_version")
 
 
@@ -217,3 +219,16 @@ def time_next_launch(kernel_id: int, start, stop) -> None:
 
 def version() -> str:
     return LIB.ip_version().decode()
+
+
+def kda_decode_step(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                    conv_w: torch.Tensor, conv_in: torch.Tensor, conv_out: torch.Tensor, state: torch.Tensor,
+                    out: torch.Tensor, stream=None) -> None:
+    """One KDA decode step; state [B, H, 128, 128] is updated in place, the shifted
+    conv taps go from conv_in to conv_out."""
+    B, H = state.shape[0], state.shape[1]
+    _check("kda_decode_step", LIB.kda_decode_step(
+        B, H, state.shape[2], xq.data_ptr(), xk.data_ptr(), xv.data_ptr(), _DT[xq.dtype], alpha.data_ptr(),
+        beta.data_ptr(), conv_w.data_ptr(), conv_in.data_ptr(), conv_out.data_ptr(), state.data_ptr(),
+        out.data_ptr(), _stream(stream)))
+

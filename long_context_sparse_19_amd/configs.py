@@ -107,6 +107,21 @@ DECODE_INDEXCACHE = DECODE.with_(name="decode_indexcache", layers=4)
 WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, MAX_CTX, RAGGED, DECODE_FP8KV, DECODE_INDEXCACHE)}
 
 
+@dataclass(frozen=True)
+class KdaWorkload:
+    """A decode step of the linear-attention (KDA) half: 64 heads of width 128 (a
+    128 x 128 fp32 state per head), short convolution of width 4."""
+    name: str
+    batch: int
+    heads: int = 64
+    head_dim: int = 128
+    seed: int = 7
+
+
+KDA_DECODE = KdaWorkload("kda_decode", batch=8)
+KDA_WORKLOADS = {KDA_DECODE.name: KDA_DECODE}
+
+
 def scaled_down(w: Workload, seq_len: int, batch: Optional[int] = None,
                 n_query: Optional[int] = None, top_k: Optional[int] = None,
                 min_blocks: Optional[int] = None, seed: Optional[int] = None) -> Workload:

@@ -461,4 +461,39 @@ ip_status sparse_attn_prefill(const ip_seqs* seqs, int32_t n_q, const int32_t* q
                      sel_idx, top_k, out, lse, ws, ws_bytes, stream);
 }
 
+// ------------------------------------------------------------------ KDA decode step
+ip_status kda_decode_step(int32_t batch, int32_t n_heads, int32_t head_dim, const void* xq, const void* xk,
+                          const void* xv, int32_t x_dtype, const float* alpha, const float* beta,
+                          const float* conv_w, const float* conv_in, float* conv_out, float* state, float* out,
+                          hipStream_t stream) {
+  const char* fn = "kda_decode_step";
+  if (batch < 1 || batch > 65535 || n_heads < 1 || n_heads > 65535)
+    return fail(IP_EINVAL, "%s: batch and n_heads must be in 1..65535 (got %d, %d)", fn, batch, n_heads);
+  if (head_dim != ip::KDA_D) return fail(IP_EUNSUPPORTED, "%s: head_dim must be 128 (got %d)", fn, head_dim);
+  if (x_dtype != IP_BF16) return fail(IP_EUNSUPPORTED, "%s: xq, xk, xv must be BF16", fn);
+  if (!xq || !xk || !xv || !alpha || !beta || !conv_w || !conv_in || !conv_out || !state || !out)
+    return fail(IP_EINVAL, "%s: every pointer is required", fn);
+  const uintptr_t cb = (uintptr_t)batch * 9 * n_heads * ip::KDA_D * sizeof(float);
+  const uintptr_t ci = (uintptr_t)conv_in, co = (uintptr_t)conv_out;
+  if (ci < co + cb && co < ci + cb)
+    return fail(IP_EINVAL, "%s: conv_in and conv_out must not overlap", fn);
+  for (const void* p : {(const void*)conv_w, (const void*)state, (const void*)out})
+    if ((reinterpret_cast<uintptr_t>(p) & 15) != 0)
+      return fail(IP_EINVAL, "%s: conv_w, state and out must be 16-byte aligned", fn);
+  ip::KdaArgs a;
+  a.batch = batch;
+  a.heads = n_heads;
+  a.xq = (const uint16_t*)xq;
+  a.xk = (const uint16_t*)xk;
+  a.xv = (const uint16_t*)xv;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.conv_w = conv_w;
+  a.conv_in = conv_in;
+  a.conv_out = conv_out;
+  a.state = state;
+  a.out = out;
+  return device_status(ip::launch_kda_decode(a, stream), fn);
+}
+
 }  // extern "C"

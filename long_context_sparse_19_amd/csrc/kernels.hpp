@@ -8,7 +8,7 @@
 
 namespace ip {
 
-enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3, K_ATTN = 4, K_COMBINE = 5, K_APPEND = 6, K_LAST = 6 };
+enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3, K_ATTN = 4, K_COMBINE = 5, K_APPEND = 6, K_KDA = 7, K_LAST = 7 };
 
 // Takes (and disarms) the timing hook's events if one is armed for kernel `id`.
 bool hook_take(int id, hipEvent_t* start, hipEvent_t* stop);
@@ -139,6 +139,23 @@ struct AttnArgs {
 constexpr int LAT_H = 64, LAT_DK = 576, LAT_DV = 512;
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t s);
+
+// KDA decode step (the linear-attention half): 128 key and value channels per head
+constexpr int KDA_D = 128;
+struct KdaArgs {
+  int batch, heads;
+  const uint16_t* xq;          // [batch, heads * 128] bf16, before the convolution
+  const uint16_t* xk;
+  const uint16_t* xv;
+  const float* alpha;          // [batch, heads, 128] per-key-channel decay
+  const float* beta;           // [batch, heads] write strength
+  const float* conv_w;         // [3 (q, k, v), heads * 128, 4] taps t-3 .. t
+  const float* conv_in;        // [batch, 3, 3 (t-3 .. t-1), heads * 128] taps before the step
+  float* conv_out;             // the same layout, taps after the step (a different buffer)
+  float* state;                // [batch, heads, 128, 128] rows = key channels, updated
+  float* out;                  // [batch, heads, 128]
+};
+hipError_t launch_kda_decode(const KdaArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
 }  // namespace ip

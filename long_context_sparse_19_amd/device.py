@@ -177,3 +177,35 @@ def attention(d: DeviceInputs, ws: Workspaces, sel: Optional[torch.Tensor] = Non
     else:
         _lib.sparse_attn_prefill(d.seqs, d.q, d.kv, d.v, sel, ws.out, d.scale, d.dv, d.q_seq, d.q_pos,
                                  lse=ws.lse, ws=ws.ws_attn, stream=stream)
+
+
+class KdaDevice:
+    """Device copies of KDA decode inputs (inputs.kda_inputs): per-step x / alpha /
+    beta, the conv weights, and the state and conv state that each step updates."""
+
+    def __init__(self, kin: dict, device="cuda"):
+        self.xq = _dev(kin["xq"], device, torch.bfloat16)
+        self.xk = _dev(kin["xk"], device, torch.bfloat16)
+        self.xv = _dev(kin["xv"], device, torch.bfloat16)
+        self.alpha = _dev(kin["alpha"], device)
+        self.beta = _dev(kin["beta"], device)
+        self.conv_w = _dev(kin["conv_w"], device)
+        self.conv = [_dev(kin["conv_state"], device), torch.empty_like(_dev(kin["conv_state"], device))]
+        self.parity = 0               # conv[parity] holds the current taps
+        self.state = _dev(kin["state"], device)
+        B, H, d = self.state.shape[0], self.state.shape[1], self.state.shape[3]
+        self.out = torch.empty((B, H, d), dtype=torch.float32, device=device)
+
+    @property
+    def conv_state(self) -> torch.Tensor:
+        return self.conv[self.parity]
+
+    def step(self, t: int, stream=None, alternate: bool = True) -> None:
+        """Step t's inputs; the conv taps move to the other buffer, which becomes
+        the current one (alternate=False keeps reading the same buffer, for
+        repeated timing of one step)."""
+        _lib.kda_decode_step(self.xq[t], self.xk[t], self.xv[t], self.alpha[t], self.beta[t], self.conv_w,
+                             self.conv[self.parity], self.conv[1 - self.parity], self.state, self.out,
+                             stream=stream)
+        if alternate:
+            self.parity = 1 - self.parity

@@ -30,13 +30,14 @@ from typing import Optional
 
 import numpy as np
 
-from .configs import Workload, INDEX_KPOOL
+from .configs import Workload, KdaWorkload, INDEX_KPOOL
 
 _CHUNK_ROWS = 1 << 16
 
 _TAGS = {
     "lens": 1, "perm": 2, "idx_keys": 3, "logits": 4, "latent": 5, "k": 6, "v": 7,
     "q": 8, "q_idx": 9, "gates": 10, "salient": 11, "append": 12,
+    "kda_x": 13, "kda_gate": 14, "kda_state": 15, "kda_conv": 16,
 }
 
 
@@ -279,3 +280,24 @@ def new_tokens(w: Workload, batch: int, seed: int) -> dict:
         "key_new": to_bf16_bits(key) if w.idx_key_dtype == "fp8" else key,
         "logit_new": rng.standard_normal(batch, dtype=np.float32),
     }
+
+
+def kda_inputs(kw: KdaWorkload, steps: int = 1) -> dict:
+    """Seeded inputs of `steps` KDA decode steps.  Per step t: xq, xk, xv (bf16 bits
+    [B, H*d], N(0,1)), alpha = sigmoid(N(0,1) + 3) per key channel (a slow decay,
+    about 0.95) and beta = sigmoid(N(0,1)) per head.  Shared: conv_w N(0,1)/2
+    [3, H*d, 4], the initial state N(0,1)/sqrt(d) [B, H, d, d] and the initial conv
+    state N(0,1) [B, 3, 3, H*d], all float32."""
+    B, H, d = kw.batch, kw.heads, kw.head_dim
+    seed = kw.seed
+    x = _normal_rows(seed, "kda_x", steps * 3 * B, H * d).reshape(steps, 3, B, H * d)
+    g = _rng(seed, "kda_gate")
+    alpha = (1.0 / (1.0 + np.exp(-(g.standard_normal((steps, B, H, d), dtype=np.float32) + 3.0)))).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-g.standard_normal((steps, B, H), dtype=np.float32)))).astype(np.float32)
+    c = _rng(seed, "kda_conv")
+    conv_w = (c.standard_normal((3, H * d, 4), dtype=np.float32) * np.float32(0.5)).astype(np.float32)
+    conv_state = c.standard_normal((B, 3, 3, H * d), dtype=np.float32)
+    state = (_normal_rows(seed, "kda_state", B * H * d, d) * np.float32(1.0 / np.sqrt(d))).reshape(B, H, d, d)
+    return {"xq": to_bf16_bits(x[:, 0]), "xk": to_bf16_bits(x[:, 1]), "xv": to_bf16_bits(x[:, 2]),
+            "alpha": alpha, "beta": beta, "conv_w": conv_w, "conv_state": conv_state, "state": state}
+

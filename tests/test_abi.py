@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_pipeline_calls():
     names = declared_functions()
     for fn in ("indexpool_compress", "indexpool_append", "index_score_topk", "sparse_attn_decode",
-               "sparse_attn_prefill", "ip_last_error"):
+               "sparse_attn_prefill", "kda_decode_step", "ip_last_error"):
         assert fn in names
 
 
@@ -216,7 +216,26 @@ def test_workspace_sizes_are_consistent(L):
 
 def test_timing_hook_arguments(L):
     assert L.LIB.ip_time_next_launch(99, FAKE, FAKE) == L.IP_EINVAL
-    assert L.LIB.ip_time_next_launch(7, FAKE, FAKE) == L.IP_EINVAL
+    assert L.LIB.ip_time_next_launch(8, FAKE, FAKE) == L.IP_EINVAL
+    assert L.LIB.ip_time_next_launch(7, FAKE, FAKE) == L.IP_OK          # KDA is hookable
     assert L.LIB.ip_time_next_launch(2, FAKE, None) == L.IP_EINVAL      # one event only
     assert L.LIB.ip_time_next_launch(6, FAKE, FAKE) == L.IP_OK          # append is hookable
     assert L.LIB.ip_time_next_launch(0, None, None) == L.IP_OK          # disarms all
+
+
+def kda(L, B=2, H=64, D=128, x_dtype=None, ptr=FAKE, state=FAKE, conv_w=FAKE, out=FAKE, conv_out=FAKE << 4):
+    x_dtype = L.IP_BF16 if x_dtype is None else x_dtype
+    return L.LIB.kda_decode_step(B, H, D, ptr, ptr, ptr, x_dtype, ptr, ptr, conv_w, ptr, conv_out, state, out, None)
+
+
+def test_kda_rejects_bad_arguments(L):
+    assert kda(L, B=0) == L.IP_EINVAL
+    assert kda(L, H=0) == L.IP_EINVAL
+    assert kda(L, D=64) == L.IP_EUNSUPPORTED
+    assert kda(L, x_dtype=L.IP_F32) == L.IP_EUNSUPPORTED
+    assert kda(L, ptr=None) == L.IP_EINVAL
+    assert kda(L, state=FAKE + 4) == L.IP_EINVAL
+    assert kda(L, conv_w=FAKE + 8) == L.IP_EINVAL
+    assert kda(L, out=None) == L.IP_EINVAL
+    assert kda(L, conv_out=FAKE + 1024) == L.IP_EINVAL        # overlaps conv_in
+    assert "kda_decode_step" in L.LIB.ip_last_error().decode()

@@ -1,0 +1,74 @@
+"""KDA decode step on the device vs the oracle (oracle/kda.py), through the C ABI."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_19_amd.configs import KDA_DECODE, KdaWorkload
+from long_context_sparse_19_amd.inputs import kda_inputs, bf16_bits_to_f32
+from oracle import kda as K
+
+pytestmark = pytest.mark.gpu
+
+# fp32 state arithmetic against fp64: the two 128-term column sums per step carry
+# at most ~128 * 2^-24 relative error each; over a few steps 2e-5 of the largest
+# magnitude bounds it with margin
+REL = 2e-5
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _oracle_steps(kin, steps):
+    S, cs = kin["state"].astype(np.float64), kin["conv_state"].astype(np.float64)
+    outs = []
+    for t in range(steps):
+        S, cs, o = K.decode_step(S, cs, bf16_bits_to_f32(kin["xq"][t]), bf16_bits_to_f32(kin["xk"][t]),
+                                 bf16_bits_to_f32(kin["xv"][t]), kin["alpha"][t], kin["beta"][t], kin["conv_w"])
+        outs.append(o)
+    return S, cs, outs
+
+
+def _close(g, o, what):
+    err = np.abs(np.asarray(g, np.float64) - o).max()
+    bound = REL * np.abs(o).max() + 1e-7
+    assert err <= bound, f"{what}: max-abs {err:.3e} > {bound:.3e}"
+    return err
+
+
+@pytest.mark.parametrize("kw,steps", [(KdaWorkload("kda_small", batch=3, heads=5, seed=3), 6),
+                                      (KDA_DECODE, 2)], ids=["small_6_steps", "full_2_steps"])
+def test_kda_decode_parity(kw, steps):
+    from long_context_sparse_19_amd import device as D
+    log(f"[case] kda {kw.name} B={kw.batch} H={kw.heads} steps={steps}")
+    kin = kda_inputs(kw, steps)
+    d = D.KdaDevice(kin)
+    S, cs, outs = _oracle_steps(kin, steps)
+    for t in range(steps):
+        d.step(t)
+        torch.cuda.synchronize()
+        _close(d.out.cpu().numpy(), outs[t], f"out step {t}")
+    err = _close(d.state.cpu().numpy(), S, "state")
+    # the conv state only shifts and widens bf16 inputs: exact
+    assert np.array_equal(d.conv_state.cpu().numpy(), cs.astype(np.float32))
+    log(f"  kda ok (state max-abs {err:.2e})")
+
+
+def test_kda_identity_gates_leave_the_state_unchanged():
+    """alpha = 1 and beta = 0: the state is bit-identical after the step, and the
+    output is S^T q / sqrt(128) of the old state."""
+    from long_context_sparse_19_amd import device as D
+    kw = KdaWorkload("kda_identity", batch=2, heads=3, seed=5)
+    kin = kda_inputs(kw, 1)
+    kin["alpha"][:] = 1.0
+    kin["beta"][:] = 0.0
+    d = D.KdaDevice(kin)
+    S0 = d.state.clone()
+    d.step(0)
+    torch.cuda.synchronize()
+    assert torch.equal(d.state, S0)
+    _, _, outs = _oracle_steps(kin, 1)
+    _close(d.out.cpu().numpy(), outs[0], "out")
