@@ -3,9 +3,9 @@
 
 One step = one pass of the whole path over one batch:
   decode:  append each sequence's new token to the caches and pool the block it
-           completes (indexpool_append), score every earlier pooled block and
-           select the top-k (index_score_topk), attend over the selected tokens
-           (sparse_attn_decode);
+           completes, score every earlier pooled block and select the top-k (both
+           in indexpool_decode_index: the append rides in the scoring launch),
+           attend over the selected tokens (sparse_attn_decode);
   prefill: pool the chunk's new blocks, score/select for every query token,
            sparse_attn_prefill;
   IndexCache group (decode_indexcache): the decode step of the group's first DSA
@@ -116,8 +116,11 @@ def kernel_bytes(inp, w, ab):
     nq = len(n)
     part = _lib.LIB.sparse_attn_workspace_bytes(nq, w.n_heads, w.dv, k, _lib.IP_BF16 if w.attn_dtype == "bf16" else _lib.IP_F32)
     comb = part + nq * w.n_heads * (w.dv * 2 + 4) if part else None
-    grow = "append" if w.mode == "decode" else "compress"
-    return {grow: ab["pool"], "score": ab["score"], "topk": int(topk.sum()),
+    if w.mode == "decode":
+        # the decode append rides in the scoring launch (indexpool_decode_index)
+        return {"score": ab["score"] + ab["pool"], "topk": int(topk.sum()), "attention": ab["attention"],
+                "combine": comb}
+    return {"compress": ab["pool"], "score": ab["score"], "topk": int(topk.sum()),
             "attention": ab["attention"], "combine": comb}
 
 
@@ -422,10 +425,10 @@ def main():
     def step(i):
         d, ws = reps[i % R], wss[i % R]
         if w.mode == "decode":
-            D.append(d, toks)
+            D.decode_index(d, toks, ws)          # append + score + top-k
         else:
             D.compress(d, block_begin=begin, max_blocks=max_new)
-        D.score_topk(d, ws)
+            D.score_topk(d, ws)
         D.attention(d, ws)
         for fd, fws in zip(freps[i % R], fwss[i % R]):
             D.append(fd, toks)
@@ -489,6 +492,7 @@ def main():
             _lib.time_next_launch(kid, *evk[n][i])
         step(args.warmup + i)
     torch.cuda.synchronize()
+    _lib.time_next_launch(0, None, None)          # disarm what a step did not consume
     eager_ms = (time.perf_counter() - t1) * 1e3 / K
     kern_ms = {}
     for n in ids:

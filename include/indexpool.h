@@ -185,6 +185,30 @@ ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_se
                            float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * indexpool_decode_index -- one decode step's cache growth and indexer together:
+ * exactly indexpool_append(...) followed by index_score_topk(...) for the decode
+ * rows (row r = sequence r at p = seq_lens[r] - 1, n_q = batch; q_seq, q_pos NULL),
+ * with the same arguments as those two calls (`pooled` serves both).  G2C Brief,
+ * "DSA keeps selected global access in eleven layers" (the growing history and the
+ * learned selection).
+ *
+ * The results are those of the two calls in order, bit for bit: scoring reads the
+ * pooled rows of blocks j < b_q only, while the append writes the new token's rows
+ * and the pooled row of the block it completes, which is b_q itself.  So with FP8
+ * keys the append runs as extra workgroups of the first scoring launch (one launch
+ * fewer per step); with F32 keys it is launched first.
+ * Errors: those of the two calls (keys must not be NULL); workspace as for
+ * index_score_topk_workspace_bytes(seqs, batch, top_k, scores != NULL).
+ * ------------------------------------------------------------------------------- */
+ip_status indexpool_decode_index(const ip_seqs* seqs, const void* kv_new, const ip_cache* kv,
+                                 const void* v_new, const ip_cache* v, const void* key_new,
+                                 int32_t key_dtype, const ip_cache* keys, const float* logit_new,
+                                 float* logits, const ip_cache* pooled, const void* q_idx,
+                                 int32_t q_dtype, int32_t n_heads, int32_t head_dim,
+                                 const float* gates, int32_t top_k, int32_t* out_idx, float* scores,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * sparse_attn_decode / sparse_attn_prefill -- attention over the selected history.
  * G2C Brief, "DSA keeps selected global access in eleven layers": the layer keeps
  * a token-addressable MLA latent history of rank 512 and attends over the

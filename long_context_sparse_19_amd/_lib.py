@@ -68,20 +68,23 @@ def _load() -> ctypes.CDLL:
     lib.sparse_attn_prefill.argtypes = [P(IpSeqs), _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                         _i32, ctypes.c_float, P(IpCache), P(IpCache), _c_void_p, _i32,
                                         _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]
+    lib.indexpool_decode_index.argtypes = [P(IpSeqs), _c_void_p, P(IpCache), _c_void_p, P(IpCache), _c_void_p, _i32,
+                                           P(IpCache), _c_void_p, _c_void_p, P(IpCache), _c_void_p, _i32, _i32, _i32,
+                                           _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]
     lib.kda_decode_step.argtypes = [_i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p,
                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]
     lib.ip_last_error.restype = ctypes.c_char_p
     lib.ip_version.restype = ctypes.c_char_p
     lib.ip_time_next_launch.argtypes = [_i32, _c_void_p, _c_void_p]
-    for fn in ("indexpool_compress", "indexpool_append", "index_score_topk", "sparse_attn_decode",
-               "sparse_attn_prefill", "kda_decode_step", "ip_time_next_launch"):
+    for fn in ("indexpool_compress", "indexpool_append", "index_score_topk", "indexpool_decode_index",
+               "sparse_attn_decode", "sparse_attn_prefill", "kda_decode_step", "ip_time_next_launch"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
 
 LIB = _load()
 
-EXPORTED = ("indexpool_compress", "indexpool_append", "index_scores_ld", "index_score_topk_workspace_bytes", "index_score_topk",
+EXPORTED = ("indexpool_compress", "indexpool_append", "indexpool_decode_index", "index_scores_ld", "index_score_topk_workspace_bytes", "index_score_topk",
             "sparse_attn_workspace_bytes", "sparse_attn_decode", "sparse_attn_prefill", "kda_decode_step", "ip_last_error",
             "ip_time_next_launch", "ip_version")
 
@@ -231,4 +234,20 @@ def kda_decode_step(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, alpha:
         B, H, state.shape[2], xq.data_ptr(), xk.data_ptr(), xv.data_ptr(), _DT[xq.dtype], alpha.data_ptr(),
         beta.data_ptr(), conv_w.data_ptr(), conv_in.data_ptr(), conv_out.data_ptr(), state.data_ptr(),
         out.data_ptr(), _stream(stream)))
+
+
+def indexpool_decode_index(seqs: Seqs, kv_new: torch.Tensor, kv: Cache, key_new: torch.Tensor, keys: Cache,
+                           logit_new: torch.Tensor, logits: torch.Tensor, pooled: Cache, q_idx: torch.Tensor,
+                           gates: torch.Tensor, top_k: int, out_idx: torch.Tensor, scores: Optional[torch.Tensor] = None,
+                           ws: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+                           v: Optional[Cache] = None, stream=None) -> None:
+    """indexpool_append then index_score_topk for the decode rows, in one call."""
+    s, kc, k, p = seqs.c(), kv.c(), keys.c(), pooled.c()
+    vc = None if v is None else v.c()
+    _check("indexpool_decode_index", LIB.indexpool_decode_index(
+        ctypes.byref(s), kv_new.data_ptr(), ctypes.byref(kc), _ptr(v_new), None if vc is None else ctypes.byref(vc),
+        key_new.data_ptr(), _DT[key_new.dtype], ctypes.byref(k), logit_new.data_ptr(), logits.data_ptr(),
+        ctypes.byref(p), q_idx.data_ptr(), _DT[q_idx.dtype], q_idx.shape[1], q_idx.shape[2], gates.data_ptr(),
+        top_k, out_idx.data_ptr(), _ptr(scores), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
 

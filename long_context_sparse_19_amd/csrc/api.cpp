@@ -209,10 +209,13 @@ ip_status indexpool_compress(const ip_seqs* seqs, const int32_t* block_begin, in
 }
 
 // ------------------------------------------------------------------ decode append
-ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cache* kv, const void* v_new,
-                           const ip_cache* v, const void* key_new, int32_t key_dtype, const ip_cache* keys,
-                           const float* logit_new, float* logits, const ip_cache* pooled, hipStream_t stream) {
-  const char* fn = "indexpool_append";
+}  // extern "C"
+
+// Checks the append arguments and fills `a` (no launch).
+static ip_status build_append(const char* fn, const ip_seqs* seqs, const void* kv_new, const ip_cache* kv,
+                              const void* v_new, const ip_cache* v, const void* key_new, int32_t key_dtype,
+                              const ip_cache* keys, const float* logit_new, float* logits, const ip_cache* pooled,
+                              ip::AppendArgs& a) {
   if (ip_status st = check_seqs(seqs, fn)) return st;
   if (ip_status st = check_cache(kv, fn, "kv")) return st;
   if (!kv_new) return fail(IP_EINVAL, "%s: kv_new must not be NULL", fn);
@@ -252,7 +255,6 @@ ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cac
     }
   }
   if (seqs->batch > 65535) return fail(IP_EUNSUPPORTED, "%s: batch > 65535", fn);
-  ip::AppendArgs a;
   a.L = layout_of(seqs);
   a.batch = seqs->batch;
   a.kv_new = (const uint8_t*)kv_new;
@@ -276,6 +278,19 @@ ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cac
   a.pooled = idx ? (uint8_t*)pooled->data : nullptr;
   a.pooled_stride = idx ? pooled->row_stride : 0;
   a.pooled_scale = idx && keys->dtype == IP_FP8_E4M3FN ? pooled->scale : nullptr;
+  return IP_OK;
+}
+
+extern "C" {
+
+ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cache* kv, const void* v_new,
+                           const ip_cache* v, const void* key_new, int32_t key_dtype, const ip_cache* keys,
+                           const float* logit_new, float* logits, const ip_cache* pooled, hipStream_t stream) {
+  const char* fn = "indexpool_append";
+  ip::AppendArgs a;
+  if (ip_status st = build_append(fn, seqs, kv_new, kv, v_new, v, key_new, key_dtype, keys, logit_new, logits,
+                                  pooled, a))
+    return st;
   return device_status(ip::launch_append(a, stream), fn);
 }
 
@@ -286,12 +301,15 @@ size_t index_score_topk_workspace_bytes(const ip_seqs* seqs, int32_t n_q, int32_
   return score_plan(seqs, n_q, top_k, scores_given != 0).total;
 }
 
-ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
-                           const int32_t* q_pos, const void* q_idx, int32_t q_dtype,
-                           int32_t n_heads, int32_t head_dim, const float* gates,
-                           const ip_cache* pooled, int32_t top_k, int32_t* out_idx,
-                           float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "index_score_topk";
+}  // extern "C"
+
+// index_score_topk, optionally with a decode append fused into the first scoring
+// launch (FP8 keys) or launched just before it (F32 keys).
+static ip_status score_topk_impl(const char* fn, const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
+                                 const int32_t* q_pos, const void* q_idx, int32_t q_dtype, int32_t n_heads,
+                                 int32_t head_dim, const float* gates, const ip_cache* pooled, int32_t top_k,
+                                 int32_t* out_idx, float* scores, void* ws, size_t ws_bytes, hipStream_t stream,
+                                 const ip::AppendArgs* append) {
   if (ip_status st = check_seqs(seqs, fn)) return st;
   if (ip_status st = check_cache(pooled, fn, "pooled")) return st;
   if (n_q < 1) return fail(IP_EINVAL, "%s: n_q must be >= 1", fn);
@@ -317,6 +335,10 @@ ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_se
     return fail(IP_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.total, ws ? ws_bytes : 0);
   if (((uintptr_t)ws & 255) != 0) return fail(IP_EINVAL, "%s: ws must be 256-byte aligned", fn);
 
+  if (append && !fp8) {
+    if (ip_status st = device_status(ip::launch_append(*append, stream), fn)) return st;
+    append = nullptr;
+  }
   float* score_buf = scores ? scores : (float*)ws;
   uint32_t* cand_key = (uint32_t*)((char*)ws + plan.score_bytes);
   int32_t* cand_idx = (int32_t*)(cand_key + (plan.cand_bytes / 8));
@@ -341,6 +363,8 @@ ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_se
     sa.dim = head_dim;
     sa.max_blocks = plan.max_blocks;
     sa.topk_count = topk_count;
+    sa.with_append = append && row0 == 0;
+    if (sa.with_append) sa.append = *append;
     // the kernels index scores by (r - row0)
     ip_status st = device_status(fp8 ? ip::launch_score_fp8_bf16(sa, stream) : ip::launch_score_f32(sa, stream), fn);
     if (st) return st;
@@ -363,6 +387,33 @@ ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_se
     if (st) return st;
   }
   return IP_OK;
+}
+
+extern "C" {
+
+ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
+                           const int32_t* q_pos, const void* q_idx, int32_t q_dtype,
+                           int32_t n_heads, int32_t head_dim, const float* gates,
+                           const ip_cache* pooled, int32_t top_k, int32_t* out_idx,
+                           float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return score_topk_impl("index_score_topk", seqs, n_q, q_seq, q_pos, q_idx, q_dtype, n_heads, head_dim, gates,
+                         pooled, top_k, out_idx, scores, ws, ws_bytes, stream, nullptr);
+}
+
+ip_status indexpool_decode_index(const ip_seqs* seqs, const void* kv_new, const ip_cache* kv, const void* v_new,
+                                 const ip_cache* v, const void* key_new, int32_t key_dtype, const ip_cache* keys,
+                                 const float* logit_new, float* logits, const ip_cache* pooled, const void* q_idx,
+                                 int32_t q_dtype, int32_t n_heads, int32_t head_dim, const float* gates,
+                                 int32_t top_k, int32_t* out_idx, float* scores, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  const char* fn = "indexpool_decode_index";
+  if (!keys) return fail(IP_EINVAL, "%s: keys are required (the scoring reads the pooled keys)", fn);
+  ip::AppendArgs a;
+  if (ip_status st = build_append(fn, seqs, kv_new, kv, v_new, v, key_new, key_dtype, keys, logit_new, logits,
+                                  pooled, a))
+    return st;
+  return score_topk_impl(fn, seqs, seqs->batch, nullptr, nullptr, q_idx, q_dtype, n_heads, head_dim, gates, pooled,
+                         top_k, out_idx, scores, ws, ws_bytes, stream, &a);
 }
 
 // ------------------------------------------------------------------ sparse attention

@@ -88,6 +88,8 @@ struct ScoreArgs {
   int heads, dim;
   int max_blocks;              // key range covered by the grid
   int32_t* topk_count;         // [n_rows] or null: zeroed here for the top-k that follows
+  int with_append;             // decode: extra grid rows of workgroups run `append`,
+  AppendArgs append;           // one sequence each (see append.hpp)
 };
 hipError_t launch_score_fp8_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s);

@@ -11,13 +11,14 @@
 // scale sigma_j > 0 is applied after the ReLU (relu(sigma x) = sigma relu(x)).
 // The output layout puts one key per lane and 16 heads per lane, so the gated
 // head-sum is 16 local FMAs plus one cross-half exchange.
-#include "kernels.hpp"
+#include "append.hpp"
 
 namespace ip {
 
 namespace {
 
 constexpr int NT = 256;
+static_assert(NT == APPEND_NT, "the fused append runs in scoring workgroups");
 constexpr int TILES = 4;                        // 32-key tiles per wave
 constexpr int KEYS_PER_WG = 4 * TILES * 32;     // 512
 constexpr int HI = 32, DI = 128;
@@ -31,6 +32,15 @@ __global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
   constexpr int QROW = DI + 8;                  // padded LDS row (272 bytes): conflict-free reads
   __shared__ __align__(16) uint16_t qs[2][HI * QROW];   // double-buffered query rows
   __shared__ float gs[2][HI];
+  if (a.with_append && (int)blockIdx.y >= a.n_rows) {
+    // the fused decode append, one sequence per workgroup of the extra grid rows:
+    // scoring reads pooled rows of blocks before the query's own block only, and
+    // the append writes the new token's rows and the pooled row of the block it
+    // completes (the query's own block)
+    const int b = ((int)blockIdx.y - a.n_rows) * (int)gridDim.x + (int)blockIdx.x;
+    if (b < a.append.batch) append_one(a.append, b);
+    return;
+  }
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int kl = lane & 31, hh = lane >> 5;
   const int kc0 = blockIdx.x * KEYS_PER_WG;
@@ -180,12 +190,13 @@ __global__ __launch_bounds__(NT) void score_f32_kernel(ScoreArgs a) {
 hipError_t launch_score_fp8_bf16(const ScoreArgs& a, hipStream_t s) {
   if (a.n_rows <= 0 || a.max_blocks <= 0) return hipSuccess;
   const unsigned gx = (a.max_blocks + KEYS_PER_WG - 1) / KEYS_PER_WG;
-  if (a.q_seq && a.n_rows >= 64) {
+  if (a.q_seq && a.n_rows >= 64 && !a.with_append) {
     // prefill: consecutive rows are query tokens of one sequence and share its keys
     constexpr int R = 32;
     launch(K_SCORE, score_fp8_bf16_kernel<R>, dim3(gx, (a.n_rows + R - 1) / R), dim3(NT), s, a);
   } else {
-    launch(K_SCORE, score_fp8_bf16_kernel<1>, dim3(gx, a.n_rows), dim3(NT), s, a);
+    const unsigned app_rows = a.with_append ? (a.append.batch + gx - 1) / gx : 0;
+    launch(K_SCORE, score_fp8_bf16_kernel<1>, dim3(gx, a.n_rows + app_rows), dim3(NT), s, a);
   }
   return hipGetLastError();
 }

@@ -169,6 +169,14 @@ def score_topk(d: DeviceInputs, ws: Workspaces, stream=None) -> None:
                           scores=ws.scores, ws=ws.ws_idx, stream=stream)
 
 
+def decode_index(d: DeviceInputs, t: NewTokens, ws: Workspaces, stream=None) -> None:
+    """append(d, t) then score_topk(d, ws) for the decode rows, in one call (the
+    append rides in the scoring launch)."""
+    _lib.indexpool_decode_index(d.seqs, t.kv_new, d.kv, t.key_new, d.keys, t.logit_new, d.logits, d.pooled,
+                                d.q_idx, d.gates, d.top_k, ws.sel, scores=ws.scores, ws=ws.ws_idx, v_new=t.v_new,
+                                v=d.v, stream=stream)
+
+
 def attention(d: DeviceInputs, ws: Workspaces, sel: Optional[torch.Tensor] = None, stream=None) -> None:
     sel = ws.sel if sel is None else sel
     if d.is_decode:

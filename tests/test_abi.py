@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_pipeline_calls():
     names = declared_functions()
-    for fn in ("indexpool_compress", "indexpool_append", "index_score_topk", "sparse_attn_decode",
-               "sparse_attn_prefill", "kda_decode_step", "ip_last_error"):
+    for fn in ("indexpool_compress", "indexpool_append", "index_score_topk", "indexpool_decode_index",
+               "sparse_attn_decode", "sparse_attn_prefill", "kda_decode_step", "ip_last_error"):
         assert fn in names
 
 
@@ -239,3 +239,22 @@ def test_kda_rejects_bad_arguments(L):
     assert kda(L, out=None) == L.IP_EINVAL
     assert kda(L, conv_out=FAKE + 1024) == L.IP_EINVAL        # overlaps conv_in
     assert "kda_decode_step" in L.LIB.ip_last_error().decode()
+
+
+def test_decode_index_rejects_bad_arguments(L):
+    s = seqs()
+    kv = cache(L, dtype=L.IP_BF16, row_dim=576, stride=1152, scale=None)
+    keys = cache(L)
+
+    def call(keys=keys, q_dtype=None, H=32, top_k=512, ws_bytes=1 << 30):
+        q_dtype = L.IP_BF16 if q_dtype is None else q_dtype
+        return L.LIB.indexpool_decode_index(ctypes.byref(s), FAKE, ctypes.byref(kv), None, None, FAKE, L.IP_BF16,
+                                            None if keys is None else ctypes.byref(keys), FAKE, FAKE,
+                                            ctypes.byref(cache(L)), FAKE, q_dtype, H, 128, FAKE, top_k, FAKE, None,
+                                            FAKE, ws_bytes, None)
+    assert call(keys=None) == L.IP_EINVAL
+    assert call(q_dtype=L.IP_F32) == L.IP_EUNSUPPORTED
+    assert call(H=16) == L.IP_EUNSUPPORTED
+    assert call(top_k=0) == L.IP_EUNSUPPORTED
+    assert call(ws_bytes=16) == L.IP_EWORKSPACE
+    assert "indexpool_decode_index" in L.LIB.ip_last_error().decode()

@@ -426,3 +426,32 @@ def test_append_without_indexer_state():
                 assert np.array_equal(kv[row], new["kv_new"][b])
         other = np.setdiff1d(np.arange(kv.shape[0]), rows)
         assert np.array_equal(kv[other], kv0[other])
+
+
+# ---------------------------------------------------------------- fused decode index
+@pytest.mark.parametrize("name", ["decode_positions", "ragged_paged", "tiny_f32", "fp8kv_positions"])
+def test_decode_index_equals_append_then_score_topk(name):
+    """indexpool_decode_index (the append riding in the scoring launch) gives the
+    results of indexpool_append followed by index_score_topk, bit for bit."""
+    D = _dev()
+    w, lens = APPEND[name]
+    inp = make_inputs(w)
+    inp.seq_lens = np.asarray(lens(inp.seq_lens), dtype=np.int32)
+    log(f"[case] decode_index {name} B={w.batch} lens={inp.seq_lens[:4].tolist()}")
+    new = new_tokens(w, len(inp.seq_lens), seed=9)
+    outs = []
+    for fused in (False, True):
+        d = D.upload(inp)
+        D.compress(d)
+        ws = D.Workspaces(d, keep_scores=True)
+        t = D.NewTokens(new)
+        if fused:
+            D.decode_index(d, t, ws)
+        else:
+            D.append(d, t)
+            D.score_topk(d, ws)
+        torch.cuda.synchronize()
+        outs.append([ws.sel, ws.scores, d.kv.data, d.keys.data, d.pooled.data, d.logits] +
+                    [x for x in (d.kv.scale, d.keys.scale, d.pooled.scale) if x is not None])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
