@@ -141,7 +141,7 @@ _KERNEL_SOURCES = {"attention": "attn.hip", "combine": "attn.hip", "score": "sco
 def _source_hash(kind):
     import hashlib
     h = hashlib.sha256()
-    for f in (_KERNEL_SOURCES[kind], "common.hpp", "kernels.hpp"):
+    for f in (_KERNEL_SOURCES[kind], "common.hpp", "kernels.hpp", "append.hpp"):
         with open(os.path.join(ROOT, "long_context_sparse_19_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
