@@ -40,7 +40,10 @@ def _close(g, o, what):
 
 
 @pytest.mark.parametrize("kw,steps", [(KdaWorkload("kda_small", batch=3, heads=5, seed=3), 6),
-                                      (KDA_DECODE, 2)], ids=["small_6_steps", "full_2_steps"])
+                                      (KdaWorkload("kda_one_head", batch=1, heads=1, seed=4), 3),
+                                      (KdaWorkload("kda_wide_batch", batch=33, heads=2, seed=6), 2),
+                                      (KDA_DECODE, 2)],
+                         ids=["small_6_steps", "one_head", "batch_33", "full_2_steps"])
 def test_kda_decode_parity(kw, steps):
     from long_context_sparse_19_amd import device as D
     log(f"[case] kda {kw.name} B={kw.batch} H={kw.heads} steps={steps}")

@@ -347,7 +347,7 @@ def test_append_parity(name):
     log(f"  append ok ({len(prows)} blocks pooled)")
 
 
-@pytest.mark.parametrize("w", [DECODE, MAX_CTX, RAGGED], ids=["decode", "max_ctx", "ragged"])
+@pytest.mark.parametrize("w", [DECODE, MAX_CTX, RAGGED, DECODE_FP8KV], ids=["decode", "max_ctx", "ragged", "decode_fp8kv"])
 def test_full_size_decode(w):
     full_case(w, keep_scores=False)
 
@@ -429,7 +429,7 @@ def test_append_without_indexer_state():
 
 
 # ---------------------------------------------------------------- fused decode index
-@pytest.mark.parametrize("name", ["decode_positions", "ragged_paged", "tiny_f32", "fp8kv_positions"])
+@pytest.mark.parametrize("name", ["decode_positions", "ragged_paged", "tiny_f32", "fp8kv_positions", "decode_full"])
 def test_decode_index_equals_append_then_score_topk(name):
     """indexpool_decode_index (the append riding in the scoring launch) gives the
     results of indexpool_append followed by index_score_topk, bit for bit."""
