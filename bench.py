@@ -134,14 +134,15 @@ def _chunk_size(max_seq_len):
 
 
 # the sources each kernel is built from (the HBM counters in profiles/ are tied to them)
-_KERNEL_SOURCES = {"attention": "attn.hip", "combine": "attn.hip", "score": "score.hip", "topk": "topk.hip",
-                   "compress": "compress.hip", "append": "compress.hip", "kda": "kda.hip"}
+_KERNEL_SOURCES = {"attention": ("attn.hip", "attn_pipe.hip", "attn_common.hpp"), "combine": ("attn.hip", "attn_common.hpp"),
+                   "score": ("score.hip",), "topk": ("topk.hip",), "compress": ("compress.hip",),
+                   "append": ("compress.hip",), "kda": ("kda.hip",)}
 
 
 def _source_hash(kind):
     import hashlib
     h = hashlib.sha256()
-    for f in (_KERNEL_SOURCES[kind], "common.hpp", "kernels.hpp", "append.hpp"):
+    for f in (*_KERNEL_SOURCES[kind], "common.hpp", "kernels.hpp", "append.hpp"):
         with open(os.path.join(ROOT, "long_context_sparse_19_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libindexpool.so")
-SOURCES = ["compress.hip", "score.hip", "topk.hip", "attn.hip", "kda.hip", "api.cpp"]
+SOURCES = ["compress.hip", "score.hip", "topk.hip", "attn.hip", "attn_pipe.hip", "kda.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

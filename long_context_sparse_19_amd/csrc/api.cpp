@@ -467,6 +467,10 @@ static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, c
     if (((uintptr_t)ws & 15) != 0) return fail(IP_EINVAL, "%s: ws must be 16-byte aligned", fn);
     a.v = nullptr;
     a.v_stride = 0;
+    // a contiguous cache whose rows all start below 4 GB - 1 KB from its base can be
+    // read with 32-bit offsets (buffer loads)
+    a.k_off32 = !seqs->page_table &&
+                (int64_t)seqs->batch * seqs->seq_stride * k->row_stride <= (int64_t(1) << 32) - 4096;
     a.n_split = p.n_split;
     a.blocks_per_split = p.blocks_per_split;
     a.part_o = (uint16_t*)ws;
@@ -484,6 +488,7 @@ static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, c
       return fail(IP_EUNSUPPORTED, "%s: F32 attention needs F32 k/v caches, n_heads <= 16, dk and dv <= 128 and multiples of 4", fn);
     a.v = (const uint8_t*)v->data;
     a.v_stride = v->row_stride;
+    a.k_off32 = 0;
     a.n_split = 1;
     a.blocks_per_split = top_k;
     a.part_o = nullptr;

@@ -136,10 +136,15 @@ struct AttnArgs {
   float* part_ml;              // [n_rows, n_split, H, 2]
   int n_split, blocks_per_split;
   int heads, dk, dv;
+  int k_off32;                 // every K row lies within 4 GB of k (32-bit byte offsets)
 };
 // bf16 latent MQA: 64 heads, dk 576, dv 512
 constexpr int LAT_H = 64, LAT_DK = 576, LAT_DV = 512;
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+// the pipelined bf16 kernel alone (no combine); launch_attn_bf16 picks it for splits
+// of at least PIPE_MIN_BLOCKS blocks when every K row lies within 4 GB of k
+constexpr int PIPE_MIN_BLOCKS = 128;
+hipError_t launch_attn_bf16_pipe(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t s);
 
 // KDA decode step (the linear-attention half): 128 key and value channels per head

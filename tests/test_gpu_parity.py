@@ -154,6 +154,12 @@ SMALL = {
     "decode_short": scaled_down(DECODE, 300, batch=3),
     "prefill_tail": scaled_down(PREFILL, 3000, n_query=130),
     "prefill_from_zero": scaled_down(PREFILL, 64, n_query=64, top_k=6),
+    # long selections take the pipelined attention kernel (32-token sub-tiles):
+    # 200 blocks = 25 sub-tiles padded to 28, rows at blocks 192..255 (some padded
+    # with -1); 700 blocks in two splits (partials + combine); a 128-row decode
+    "prefill_k200": scaled_down(PREFILL, 1024, n_query=256, top_k=200),
+    "prefill_split_k700": scaled_down(PREFILL, 3200, n_query=128, top_k=700),
+    "decode_batch128": scaled_down(DECODE, 4 * 600, batch=128),
     "ragged_paged": scaled_down(RAGGED, 8192, batch=5, min_blocks=50),
     "k1": scaled_down(DECODE, 1024, batch=2, top_k=1),
     "k_exceeds": scaled_down(DECODE, 256, batch=2, top_k=100),
