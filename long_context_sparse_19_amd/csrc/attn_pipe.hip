@@ -230,33 +230,51 @@ __global__ __launch_bounds__(NTW, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
         }
       }
       __builtin_amdgcn_s_setprio(0);
-      // mask (-inf where a block's token is after the query); tile maximum of the
-      // unscaled S (cs > 0) over the 16 tokens; the reference for P: the agreed one,
-      // or (rare) the tile maximum when it passes that by more than 2^8
-      bool moved = false;
+      // mask (-inf where a block's token is after the query), only in sub-tiles
+      // that reach past the query or hold padding
+      if (__ballot(vis < 4) != 0ull) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[g][u] = u < vis ? x[g][u] : -INFINITY;
-        const float tm = quad_max16(fmaxf(fmaxf(x[g][0], x[g][1]), fmaxf(x[g][2], x[g][3]))) * cs;
-        rr[g] = tm > m[g] + RESCALE_LOG2 ? tm : m[g];
-        moved |= rr[g] != m[g];
-        lds_st(&sh.rref[slot][ref_at(32 * hb + 16 * g + l16, th)], rr[g]);  // the 4 lanes of a head agree
+          for (int u = 0; u < 4; ++u) x[g][u] = u < vis ? x[g][u] : -INFINITY;
       }
+      // P = 2^(cs S - rr) against rr = the agreed reference m.  Rare: a P above 2^8
+      // (a tile maximum passes m by more than 2^8) or a head without a reference
+      // yet; then rr = the tile maximum of the unscaled S (cs > 0) over the 16 tokens
+      // where it passes m by more than 2^8, else m, and P again.  Masked scores give 0.
+      float pv[2][4];
+      auto exps = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const float nmu = rr[g] == -INFINITY ? 0.f : -rr[g];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) pv[g][u] = __builtin_amdgcn_exp2f(fmaf(x[g][u], cs, nmu));
+        }
+      };
+      rr[0] = m[0];
+      rr[1] = m[1];
+      exps();
+      const float pmax = fmaxf(fmaxf(fmaxf(pv[0][0], pv[0][1]), fmaxf(pv[0][2], pv[0][3])),
+                               fmaxf(fmaxf(pv[1][0], pv[1][1]), fmaxf(pv[1][2], pv[1][3])));
+      const bool rare = __ballot(pmax > 256.f || m[0] == -INFINITY || m[1] == -INFINITY) != 0ull;
+      bool moved = false;
+      if (rare) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const float tm = quad_max16(fmaxf(fmaxf(x[g][0], x[g][1]), fmaxf(x[g][2], x[g][3]))) * cs;
+          rr[g] = tm > m[g] + RESCALE_LOG2 ? tm : m[g];
+          moved |= rr[g] != m[g];
+        }
+        exps();
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) lds_st(&sh.rref[slot][ref_at(32 * hb + 16 * g + l16, th)], rr[g]);  // the 4 lanes of a head agree
       lds_st(&sh.changed[slot][pw], (int)(__ballot(moved) != 0ull));
-      // P = 2^(cs S - rr): masked scores give 0, the others at most 2^8
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const float nmu = rr[g] == -INFINITY ? 0.f : -rr[g];
-        float pv[4];
-        ls[g] = 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          pv[u] = __builtin_amdgcn_exp2f(fmaf(x[g][u], cs, nmu));
-          ls[g] += pv[u];
-        }
-        lds_st8(pout, (32 * hb + 16 * g + l16) * PROWP + (16 * th + 4 * lq) * 2, pack_bf16x2(pv[0], pv[1]),
-                pack_bf16x2(pv[2], pv[3]));
+        ls[g] = (pv[g][0] + pv[g][1]) + (pv[g][2] + pv[g][3]);
+        lds_st8(pout, (32 * hb + 16 * g + l16) * PROWP + (16 * th + 4 * lq) * 2, pack_bf16x2(pv[g][0], pv[g][1]),
+                pack_bf16x2(pv[g][2], pv[g][3]));
       }
     };
     for (int n = 0; n < nsub; n += 4) {
