@@ -210,7 +210,6 @@ __global__ __launch_bounds__(NTW, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
     // S^T, softmax and P of sub-tile n from `buf` into `pout`
     auto sjob = [&](const int n, const uint8_t* buf, uint8_t* pout) __attribute__((always_inline)) {
       const int slot = n & 1;
-      if (n > 0) fold(slot ^ 1);
       const int vis = (int)(lds_ld(&sh.brow[8 * n + 4 * th + lq]) >> VIS_SHIFT);
       // S^T[token, head]: x[g][u] = token 16th + 4lq + u, head 32hb + 16g + l16
       f32x4_t x[2] = {f32x4_t{}, f32x4_t{}};
@@ -230,6 +229,9 @@ __global__ __launch_bounds__(NTW, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
         }
       }
       __builtin_amdgcn_s_setprio(0);
+      // the last step's references, needed from here on (folded after the S^T MFMAs,
+      // so that they start without waiting for the flags)
+      if (n > 0) fold(slot ^ 1);
       // mask (-inf where a block's token is after the query), only in sub-tiles
       // that reach past the query or hold padding
       if (__ballot(vis < 4) != 0ull) {
@@ -326,8 +328,31 @@ __global__ __launch_bounds__(NTW, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
     // references the S-waves used for it
     auto ojob = [&](const int n, const uint8_t* buf, const uint8_t* pin) __attribute__((always_inline)) {
       const int slot = n & 1;
+      typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+      const int g4 = lane >> 4, s16 = lane & 15;
+      const int vt = 8 * (g4 >> 1) + (s16 >> 2);
+      const int vd = 16 * (g4 & 1) + 4 * (s16 & 3);
+      const int vch = vd >> 3, vin = (vd & 7) * 2;
+      // operands of k-step ks: P fragments of the two head tiles, V^T of the four
+      // 32-dim blocks (k-step 0's are read before the flags, so that their latency
+      // overlaps the flag read)
+      auto load_ks = [&](int ks, bf16x8_t (&pbv)[2], bf16x8_t (&va)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) pbv[i] = lds_ld((const bf16x8_t*)(pin + (32 * i + l32) * PROWP + (16 * ks + 8 * lh) * 2));
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int ch = 4 * (4 * pw + db) + vch;
+          const int t0 = 16 * ks + vt;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + kvp_off(t0, ch) + vin));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + kvp_off(t0 + 4, ch) + vin));
+          const s16x4_t v8[2] = {lo, hi};
+          va[db] = __builtin_bit_cast(bf16x8_t, v8);
+        }
+      };
+      bf16x8_t pb0[2], va0[4];
+      load_ks(0, pb0, va0);
       // rare: move O to the new agreed references R (the larger of the two halves'),
-      // and below the P of each half from its reference to R (factor f[i][half])
+      // and the P of each half from its reference to R (factor f[i][half])
       const u32x4_t ch = lds_ld((const u32x4_t*)sh.changed[slot]);
       const bool rescale = (ch[0] | ch[1] | ch[2] | ch[3]) != 0u;
       float f[2][2] = {{1.f, 1.f}, {1.f, 1.f}};
@@ -345,16 +370,7 @@ __global__ __launch_bounds__(NTW, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
           for (int k = 0; k < 2; ++k) f[i][k] = rh[i][k] == -INFINITY ? 0.f : exp2f(rh[i][k] - R);
         }
       }
-      typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
-      const int g4 = lane >> 4, s16 = lane & 15;
-      const int vt = 8 * (g4 >> 1) + (s16 >> 2);
-      const int vd = 16 * (g4 & 1) + 4 * (s16 & 3);
-      const int vch = vd >> 3, vin = (vd & 7) * 2;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8_t pbv[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) pbv[i] = lds_ld((const bf16x8_t*)(pin + (32 * i + l32) * PROWP + (16 * ks + 8 * lh) * 2));
+      auto mfma_ks = [&](int ks, bf16x8_t (&pbv)[2], const bf16x8_t (&va)[4]) __attribute__((always_inline)) {
         if (rescale) {
 #pragma unroll
           for (int i = 0; i < 2; ++i)
@@ -362,17 +378,14 @@ __global__ __launch_bounds__(NTW, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
             for (int e = 0; e < 8; ++e) pbv[i][e] = (__bf16)((float)pbv[i][e] * f[i][ks]);
         }
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int ch = 4 * (4 * pw + db) + vch;
-          const int t0 = 16 * ks + vt;
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + kvp_off(t0, ch) + vin));
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + kvp_off(t0 + 4, ch) + vin));
-          const s16x4_t v8[2] = {lo, hi};
-          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, v8);
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int i = 0; i < 2; ++i) o[i][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbv[i], o[i][db], 0, 0, 0);
-        }
-      }
+          for (int i = 0; i < 2; ++i) o[i][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pbv[i], o[i][db], 0, 0, 0);
+      };
+      mfma_ks(0, pb0, va0);
+      bf16x8_t pb1[2], va1[4];
+      load_ks(1, pb1, va1);
+      mfma_ks(1, pb1, va1);
     };
     // step n: stream sub-tile n+2 (clamped to the last) into `db`, add sub-tile
     // n-1 (`ob`, P from `pr`); past the barrier sub-tile n+1 has landed
