@@ -120,11 +120,12 @@ def check_attention(d, inp, o_ids, rows, ws, base_sel=None):
     return err
 
 
-def full_case(w, rows=None, keep_scores=True):
-    """Stage parity (compress, score + select, attention) on workload w."""
+def full_case(w, rows=None, keep_scores=True, inp=None):
+    """Stage parity (compress, score + select, attention) on workload w (inputs
+    drawn for it unless given)."""
     D = _dev()
     log(f"[case] {w.name} B={w.batch} L={w.seq_len} n_q={w.n_rows} k={w.top_k} seed={w.seed}")
-    inp = make_inputs(w)
+    inp = make_inputs(w) if inp is None else inp
     d = D.upload(inp)
     rows = np.arange(w.n_rows) if rows is None else np.asarray(rows)
     opooled = _oracle_pooled(inp)
@@ -177,6 +178,21 @@ SMALL = {
 @pytest.mark.parametrize("name", list(SMALL))
 def test_stage_parity_small(name):
     full_case(SMALL[name])
+
+
+def test_reference_moves_within_a_row():
+    """Salient latent rows: the rope dims (512..575, outside V) of 2% of the rows
+    scaled by 16, so a head's tile maximum jumps by about 2^13 partway through a
+    row.  In the long-selection kernel one token half of a head then moves its
+    reference while the other keeps it, and O and that half's P are rescaled."""
+    w = SMALL["prefill_k200"]
+    inp = make_inputs(w)
+    rng = np.random.default_rng(11)
+    rows = rng.choice(len(inp.latent), size=len(inp.latent) // 50, replace=False)
+    x = (inp.latent[rows].astype(np.uint32) << 16).view(np.float32)
+    x[:, 512:] *= 16.0
+    inp.latent[rows] = (x.view(np.uint32) >> 16).astype(np.uint16)   # exact: a power of 2
+    full_case(w, inp=inp)
 
 
 def test_zero_queries_tie_to_lowest_ids():
