@@ -15,7 +15,10 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Memory: every pointer named "device" is device memory owned by the caller.
- *    The library allocates nothing and keeps no state between calls.
+ *    The library allocates nothing.  Its only state between calls is per host
+ *    thread: the text behind ip_last_error() and the benchmarking hook armed by
+ *    ip_time_next_launch() (see the end of this header), which no compute call
+ *    needs.
  *  - Streams: every call only enqueues work on `stream` (0 = the null stream) and
  *    never synchronises the host.  Outputs are ready when the stream reaches them.
  *  - Errors: arguments the host can check (null pointers, unsupported dtypes or

@@ -309,6 +309,49 @@ def test_paged_and_contiguous_layouts_agree():
     assert np.array_equal(outs[0][2], outs[1][2])
 
 
+def test_paged_row_mapping_worked_example():
+    """token_rows / pooled_rows against rows worked by hand for a shuffled 8-token
+    page table over three sequences, and for a contiguous cache."""
+    from types import SimpleNamespace
+    g = _golden("paged_rows_worked_example.json")
+    pg = g["paged"]
+    inp = SimpleNamespace(page_table=np.array(pg["page_table"], dtype=np.int32), page_tokens=pg["page_tokens"],
+                          seq_stride=0)
+    for b, t, row in pg["token_rows"]:
+        assert int(O.token_rows(inp, b, t)) == row, (b, t)
+    for b, j, row in pg["pooled_rows"]:
+        assert int(O.pooled_rows(inp, b, j)) == row, (b, j)
+        # the pooled row covers the token rows of its block's four tokens
+        assert (O.token_rows(inp, b, 4 * j + np.arange(4)) // 4 == row).all()
+    # vectorised calls give the same rows as the scalar ones
+    b, t, rows = zip(*[x for x in pg["token_rows"] if x[0] == 2])
+    assert O.token_rows(inp, 2, np.array(t)).tolist() == list(rows)
+    ct = g["contiguous"]
+    flat = SimpleNamespace(page_table=None, page_tokens=0, seq_stride=ct["seq_stride"])
+    for b, t, row in ct["token_rows"]:
+        assert int(O.token_rows(flat, b, t)) == row, (b, t)
+    for b, j, row in ct["pooled_rows"]:
+        assert int(O.pooled_rows(flat, b, j)) == row, (b, j)
+
+
+def test_score_select_rows_worked_example():
+    """Per-row wiring of score_select (sequence of each row, eligible blocks j < b_q,
+    the own block kept, k < b_q and k > b_q) against ids and scores worked by hand
+    for three prefill rows over two sequences."""
+    from types import SimpleNamespace
+    g = _golden("score_select_rows_worked_example.json")
+    inp = SimpleNamespace(page_table=None, page_tokens=0, seq_stride=g["seq_stride"],
+                          seq_lens=np.array(g["seq_lens"], dtype=np.int32),
+                          q_seq=np.array(g["q_seq"], dtype=np.int32), q_pos=np.array(g["q_pos"], dtype=np.int32),
+                          q_idx=np.array(g["q_idx"]), gates=np.array(g["gates"]))
+    ids, scores = O.score_select(inp, np.array(g["pooled"]), g["top_k"])
+    assert ids.tolist() == g["ids"]
+    assert [s.tolist() for s in scores] == g["scores"]
+    # one row at a time through row_scores gives the same scores
+    for r in range(len(g["q_pos"])):
+        assert O.row_scores(inp, np.array(g["pooled"]), r).tolist() == g["scores"][r]
+
+
 def test_end_to_end_all_blocks_equals_dense_causal():
     """pool -> score -> select (k covering every block) -> attend reproduces dense
     causal attention over the whole history, for a prefill chunk."""
