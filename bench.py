@@ -3,34 +3,38 @@
 
 One step = one pass of the whole path over one batch:
   decode:  append each sequence's new token to the caches and pool the block it
-           completes, score every earlier pooled block and select the top-k (both
-           in indexpool_decode_index: the append rides in the scoring launch),
-           attend over the selected tokens (sparse_attn_decode);
-  prefill: pool the chunk's new blocks, score/select for every query token,
-           sparse_attn_prefill;
+           completes, score every earlier pooled block and select the top-k (one
+           launch: the append rides in the scoring launch and the last scoring
+           workgroup of each row selects it), attend over the selected tokens
+           (sparse_attn_decode);
+  prefill: pool the chunk's new blocks, score and select for every query token
+           (scoring launch + selection launch), sparse_attn_prefill;
   IndexCache group (decode_indexcache): the decode step of the group's first DSA
            layer, then for each other layer of the group its new latent row
            (indexpool_append without indexer state) and its attention over the
            first layer's selection; `value` counts (query token, layer) pairs.
-The default workload is decode of 8 sequences x 131072 tokens with top-512
-blocks (2048 tokens).  Inputs are seeded synthetic data of the workload's shape,
-resident in HBM before timing; R replicas of every device buffer are rotated so
-that successive steps do not hit in the 256 MB last-level cache.  Each replica's
-step is captured once into a HIP graph and replayed (--eager launches every call
-from Python instead).
+The headline workload is decode of 8 sequences x 131072 tokens with top-512 blocks
+(2048 tokens).  Inputs are seeded synthetic data of the workload's shape, resident
+in HBM before timing; R replicas of every device buffer are rotated so that
+successive steps do not hit in the 256 MB last-level cache.  Each replica's step is
+captured once into a HIP graph and replayed (--eager launches every call from
+Python instead).
 
 Two timed regions of K steps each:
   1. the graph replays -> `value` (query tokens per second) and `ms_per_step`;
   2. the same K steps launched call by call, every kernel launch carrying a pair
      of HIP events that receive its dispatch start and end times
      (hipExtLaunchKernelGGL, on the stream the kernel runs on) -> the per-kernel
-     averages in `kernels`, `kernel_sum_ms` and `roofline` (the kernel with the
-     longest average).  These are the same timestamps rocprofv3's kernel trace
-     reports, so the two agree.
-`hbm_gbps` is the step's algorithmic bytes over the step time, and
-`hbm_frac_kernel_sum` the same bytes over the summed kernel times of the path
-(scoring, both top-k stages, attention and its split combine) against 8 TB/s.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+     averages in `kernels`, `kernel_sum_ms` and `roofline`.  These are the same
+     timestamps rocprofv3's kernel trace reports.
+`roofline` for decode is the path: the step's algorithmic bytes (what the method
+must move: pooled keys, queries, selected ids, gathered latent rows, outputs and
+the cache growth; no score workspace or split partials) over the summed average
+durations of the path's kernels, against 8 TB/s; for prefill it is the attention
+kernel's FLOPs against the 2.5 PFLOP/s bf16 MFMA peak.  Without --workload the
+line also carries `configs`: the same measurement (fewer steps) on the tiny fp32
+decode, the chunked prefill, the 1M-token decode and the ragged paged decode.
+`cpu_baseline` times the CPU oracle on a bounded sample of the headline workload.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -98,44 +102,36 @@ def algorithmic_bytes(inp, w):
                 follower=int(fol_b), U=U)
 
 
-def kernel_bytes(inp, w, ab):
-    """Bytes each kernel must move given the path's stages (for the per-kernel
-    rates; the step's algorithmic total above excludes the score and candidate
-    intermediates counted here)."""
-    import numpy as np
-    n = inp.q_pos.astype(np.int64) // 4
-    k = w.top_k
-    chunk = _chunk_size(int(inp.seq_lens.max()))
-    n_chunks = np.maximum(1, (n + chunk - 1) // chunk)
-    multi = n_chunks > 1
-    # multi-chunk rows: the chunk winners are written, then read back by the
-    # row's last chunk workgroup, which selects among them
-    topk = n * 4 + k * 4 + np.where(multi, n_chunks * (k - 1) * 8 * 2, 0)
-    # split-softmax partials: read once by the combine, which writes the bf16 output and lse
-    from long_context_sparse_19_amd import _lib
-    nq = len(n)
-    part = _lib.LIB.sparse_attn_workspace_bytes(nq, w.n_heads, w.dv, k, _lib.IP_BF16 if w.attn_dtype == "bf16" else _lib.IP_F32)
-    comb = part + nq * w.n_heads * (w.dv * 2 + 4) if part else None
+def kernel_bytes(inp, w, ab, fused):
+    """Algorithmic bytes per kernel (the same units as the step total; split
+    partials and the score workspace are not counted).  fused: the scoring launch
+    also selects (and, for decode, appends)."""
+    n = len(inp.q_pos)
+    sel_b = ab["select"]
     if w.mode == "decode":
-        # the decode append rides in the scoring launch (indexpool_decode_index)
-        return {"score": ab["score"] + ab["pool"], "topk": int(topk.sum()), "attention": ab["attention"],
-                "combine": comb}
-    return {"compress": ab["pool"], "score": ab["score"], "topk": int(topk.sum()),
-            "attention": ab["attention"], "combine": comb}
+        out = {"score": ab["score"] + ab["pool"] + (sel_b if fused else 0), "attention": ab["attention"]}
+    else:
+        out = {"compress": ab["pool"], "score": ab["score"] + (sel_b if fused else 0), "attention": ab["attention"]}
+    if not fused:
+        out["topk"] = sel_b
+    from long_context_sparse_19_amd import _lib
+    part = _lib.LIB.sparse_attn_workspace_bytes(n, w.n_heads, w.dv, w.top_k,
+                                                _lib.IP_BF16 if w.attn_dtype == "bf16" else _lib.IP_F32)
+    if part:
+        out["combine"] = 0          # merges split partials: no algorithmic bytes of its own
+    return out
 
 
-def _chunk_size(max_seq_len):
-    nb = max(1, (max_seq_len - 1) // 4)
-    # the library pads score rows to whole chunks; the chunk is the row padding unit
-    c = 512
-    while c < min(nb, 16384):
-        c *= 2
-    return c
+def fuses_select(w):
+    """Whether index_score_topk selects inside the scoring launch for this workload
+    (fp8 keys and decode-shaped rows: fewer than 64 rows, or no per-row sequence
+    table)."""
+    return w.idx_key_dtype == "fp8" and w.mode == "decode"
 
 
 # the sources each kernel is built from (the HBM counters in profiles/ are tied to them)
 _KERNEL_SOURCES = {"attention": ("attn.hip", "attn_pipe.hip", "attn_common.hpp"), "combine": ("attn.hip", "attn_common.hpp"),
-                   "score": ("score.hip",), "topk": ("topk.hip",), "compress": ("compress.hip",),
+                   "score": ("score.hip", "select.hpp"), "topk": ("select.hip", "select.hpp"), "compress": ("compress.hip",),
                    "append": ("compress.hip",), "kda": ("kda.hip",)}
 
 
@@ -164,6 +160,25 @@ def measured_traffic(kind, workload):
 
 def attention_flops(U, w):
     return int(2 * w.n_heads * (w.dk + w.dv) * U.sum())
+
+
+def indexer_flops(inp, w):
+    """Dense indexer work: 2 * H_I * D_I flop per (query row, eligible block)."""
+    import numpy as np
+    n = inp.q_pos.astype(np.int64) // 4
+    return int(2 * w.idx_heads * w.idx_dim * n.sum())
+
+
+def path_traffic(path, workload):
+    """Counted HBM bytes of one step's path kernels (sum over them), or None when any
+    is missing or stale."""
+    tot = 0.0
+    for n in path:
+        t = measured_traffic(n, workload)
+        if t is None:
+            return None
+        tot += t
+    return tot
 
 
 def cpu_baseline(inp, w, budget_s=12.0, followers=()):
@@ -363,6 +378,7 @@ def main():
     ap.add_argument("--workload", default="decode", choices=list(_W) + list(_KW))
     ap.add_argument("--replicas", type=int, default=0, help="rotated input copies (0 = auto, >= 1 GiB touched)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="headline workload only (no `configs` key)")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of HIP graphs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run 10 plain device copies of MB megabytes (calibrates HBM byte counters)")
@@ -379,13 +395,28 @@ def main():
         kda_main(args, _KW[args.workload])
         return
 
+    from long_context_sparse_19_amd.configs import WORKLOADS
+    w = WORKLOADS[args.workload]
+    res, line = run_workload(w, args.steps, args.warmup, args.replicas, args.eager, with_cpu=not args.no_cpu_baseline)
+    if args.workload == "decode" and not args.no_configs:
+        # the other configurations, fewer steps each: tiny fp32 decode, chunked
+        # prefill, 1M-token decode, ragged paged decode
+        extra = {}
+        for name in ("tiny", "prefill", "max_ctx", "ragged"):
+            steps = max(3, min(args.steps, 10))
+            r, _ = run_workload(WORKLOADS[name], steps, 2, 2 if name != "max_ctx" else 1, args.eager, with_cpu=False)
+            extra[name] = r
+        line["configs"] = extra
+    print(json.dumps(line))
+
+
+def run_workload(w, K, warmup, replicas, eager, with_cpu):
+    """Times workload w; returns (a summary dict, the full JSON line)."""
     import numpy as np
     import torch
     from long_context_sparse_19_amd import _lib, device as D
-    from long_context_sparse_19_amd.configs import WORKLOADS
     from long_context_sparse_19_amd.inputs import make_inputs, new_tokens, follower_layer
 
-    w = WORKLOADS[args.workload]
     t_gen = time.perf_counter()
     inp = make_inputs(w)
     # IndexCache: the group's other DSA layers (own latent cache and queries, no indexer)
@@ -393,7 +424,7 @@ def main():
     print(f"[bench] {w.name}: inputs drawn in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     ab = algorithmic_bytes(inp, w)
     step_bytes = ab["total"] + len(followers) * ab["follower"]
-    R = args.replicas or max(1, min(32 // w.layers, math.ceil((1 << 30) / max(1, step_bytes))))
+    R = replicas or max(1, min(32 // w.layers, math.ceil((1 << 30) / max(1, step_bytes))))
     base = D.upload(inp)
     reps = [base]
     for _ in range(R - 1):
@@ -421,7 +452,8 @@ def main():
         begin = torch.full((1,), int(inp.q_pos[0]) // 4, dtype=torch.int32, device="cuda")
         max_new = (int(inp.q_pos[-1]) // 4) - (int(inp.q_pos[0]) // 4) + 1
     torch.cuda.synchronize()
-    print(f"[bench] {R} replicas resident, {step_bytes / 1e6:.2f} MB algorithmic per step", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: {R} replicas resident, {step_bytes / 1e6:.2f} MB algorithmic per step", file=sys.stderr,
+          flush=True)
 
     def step(i):
         d, ws = reps[i % R], wss[i % R]
@@ -436,9 +468,8 @@ def main():
             D.attention(fd, fws)
 
     graphs = None
-    if not args.eager:
-        # one HIP graph per replica holding one whole step (running the decode append on
-        # a forked stream beside scoring measured 71 us per step against 60 serial)
+    if not eager:
+        # one HIP graph per replica holding one whole step
         graphs = []
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
@@ -461,13 +492,12 @@ def main():
             step(i)
 
     # --- timed region 1: K whole steps -> value
-    for i in range(args.warmup):
+    for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
-    K = args.steps
     t0 = time.perf_counter()
     for i in range(K):
-        run(args.warmup + i)
+        run(warmup + i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt * 1e3 / K
@@ -476,10 +506,11 @@ def main():
     # --- timed region 2: the same K steps launched one call at a time, every kernel
     # launch carrying HIP events that receive its dispatch start / end times (the
     # timestamps a kernel trace reports), on the stream the kernel runs on
-    kbytes = kernel_bytes(inp, w, ab)
-    ids = {"compress": _lib.K_COMPRESS, "append": _lib.K_APPEND, "score": _lib.K_SCORE, "topk": _lib.K_TOPK,
-           "attention": _lib.K_ATTN, "combine": _lib.K_COMBINE}
-    ids = {n: kid for n, kid in ids.items() if kbytes.get(n)}     # the kernels this workload launches
+    fused = fuses_select(w)
+    kbytes = kernel_bytes(inp, w, ab, fused)
+    ids = {"compress": _lib.K_COMPRESS, "score": _lib.K_SCORE, "topk": _lib.K_TOPK, "attention": _lib.K_ATTN,
+           "combine": _lib.K_COMBINE}
+    ids = {n: kid for n, kid in ids.items() if n in kbytes}     # the kernels this workload launches
     evk = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
            for n in ids}
     for n in ids:
@@ -491,7 +522,7 @@ def main():
     for i in range(K):
         for n, kid in ids.items():
             _lib.time_next_launch(kid, *evk[n][i])
-        step(args.warmup + i)
+        step(warmup + i)
     torch.cuda.synchronize()
     _lib.time_next_launch(0, None, None)          # disarm what a step did not consume
     eager_ms = (time.perf_counter() - t1) * 1e3 / K
@@ -505,35 +536,39 @@ def main():
     U = ab["U"]
     kernels = {}
     for n, t in kern_ms.items():
-        kernels[n] = {"avg_ms": t, "bytes": kbytes.get(n), "GBps": (kbytes[n] / (t * 1e-3) / 1e9) if kbytes.get(n) else None}
+        b = kbytes.get(n)
+        kernels[n] = {"avg_ms": t, "bytes": b, "GBps": (b / (t * 1e-3) / 1e9) if b else None,
+                      "hbm_frac": (b / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS) if b else None}
     if "attention" in kernels:
         fl = attention_flops(U, w)
         kernels["attention"].update(flops=fl, TFLOPs=fl / (kern_ms["attention"] * 1e-3) / 1e12)
-    path_ms = sum(kern_ms.get(n, 0.0) for n in ("score", "topk", "attention", "combine"))
-    dom = max(kern_ms, key=kern_ms.get)
-    if w.mode == "prefill" and dom == "attention":
+    if w.mode == "prefill" and "score" in kernels:
+        ifl = indexer_flops(inp, w)
+        kernels["score"].update(flops=ifl, TFLOPs=ifl / (kern_ms["score"] * 1e-3) / 1e12)
+    path = [n for n in ("score", "topk", "attention", "combine") if n in kern_ms]
+    path_ms = sum(kern_ms[n] for n in path)
+    if w.mode == "prefill":
         ach = kernels["attention"]["TFLOPs"]
         roof = {"bound": "mfma", "kernel": "attention (sparse_attn_prefill)", "achieved": ach,
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None}
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                "traffic": measured_traffic("attention", w.name), "avg_ms": kern_ms["attention"], "launches": K}
     else:
-        ach = kernels[dom]["GBps"]
-        roof = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": ach / HBM_PEAK_GBPS, "traffic": None}
-    roof["traffic"] = measured_traffic(dom, w.name)
-    roof["avg_ms"] = kern_ms[dom]
-    roof["launches"] = K
+        ach = step_bytes / (path_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "decode path: " + " + ".join(path), "achieved": ach, "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": path_traffic(path, w.name),
+                "avg_ms": path_ms, "launches": K}
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, w, followers=followers)
-
+    cpu = cpu_baseline(inp, w, followers=followers) if with_cpu else None
+    summary = {"workload": w.name, "ms_per_step": ms, "value": value, "unit": "query-tokens/s",
+               "algorithmic_bytes_per_step": step_bytes, "kernel_sum_ms": path_ms, "roofline": roof,
+               "kernels": kernels, "steps": K, "replicas": R}
     line = {
         "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.attn_dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "context": w.seq_len, "query_rows": w.n_rows,
                    "top_k_blocks": w.top_k, "index_keys": w.idx_key_dtype, "latent": "fp8" if w.latent_fp8 else w.attn_dtype,
-                   "dsa_layers": w.layers, "replicas": R, "launch": "eager" if args.eager else "hip-graph",
+                   "dsa_layers": w.layers, "replicas": R, "launch": "eager" if eager else "hip-graph",
                    "parallelism": "single GPU"},
         "hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "algorithmic_bytes_per_step": step_bytes,
@@ -544,7 +579,9 @@ def main():
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line))
+    del reps, freps, wss, fwss, graphs
+    torch.cuda.empty_cache()
+    return summary, line
 
 
 if __name__ == "__main__":

@@ -79,33 +79,39 @@ ip_status check_cache(const ip_cache* c, const char* fn, const char* name) {
   return IP_OK;
 }
 
-// Score workspace plan shared by the size query and the call.
+// Score workspace plan shared by the size query and the call: per-row counters
+// of the fused selection, group maxima, then (unless the caller keeps the scores)
+// the scores of one pass of rows.
 struct ScorePlan {
-  int64_t ld;          // floats per score row
+  int64_t ld, gld;     // floats per score row / per group-maximum row
   int max_blocks;      // eligible blocks bound
-  int chunk;           // scores per top-k chunk
-  int n_chunks;        // top-k chunks per row
-  int rows_per_chunk;  // query rows per pass
-  size_t score_bytes, cand_bytes, count_bytes, total;
+  int rows_per_pass;   // query rows per pass
+  int max_lists;       // per-wave candidate lists per row (0: rows too long for them)
+  size_t count_bytes, gm_bytes, list_bytes, score_bytes, total;
 };
 
-ScorePlan score_plan(const ip_seqs* s, int n_q, int top_k, bool scores_given) {
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+ScorePlan score_plan(const ip_seqs* s, int n_q, bool scores_given) {
   ScorePlan p;
   p.max_blocks = (s->max_seq_len - 1) / 4;          // j < b_q <= (max_seq_len - 1) / 4
   p.ld = index_scores_ld(s->max_seq_len);
-  p.chunk = ip::topk_chunk_size(std::max(1, p.max_blocks));
-  p.n_chunks = p.max_blocks <= 0 ? 1 : (p.max_blocks + p.chunk - 1) / p.chunk;
+  p.gld = p.ld / 16;
   if (scores_given) {
-    p.rows_per_chunk = n_q;
+    p.rows_per_pass = n_q;
   } else {
     const size_t per_row = (size_t)p.ld * 4;
-    p.rows_per_chunk = (int)std::max<size_t>(1, std::min<size_t>(n_q, kScoreBudget / per_row));
+    p.rows_per_pass = (int)std::max<size_t>(1, std::min<size_t>(n_q, kScoreBudget / per_row));
   }
-  p.score_bytes = scores_given ? 0 : (size_t)p.rows_per_chunk * p.ld * 4;
-  p.cand_bytes = p.n_chunks > 1 ? (size_t)p.rows_per_chunk * p.n_chunks * (size_t)(top_k - 1) * 8 : 0;
-  p.count_bytes = p.n_chunks > 1 ? (size_t)p.rows_per_chunk * 4 : 0;
-  p.score_bytes = (p.score_bytes + 255) & ~size_t(255);
-  p.total = p.score_bytes + p.cand_bytes + p.count_bytes;
+  p.count_bytes = align256((size_t)p.rows_per_pass * 4);
+  p.gm_bytes = align256((size_t)p.rows_per_pass * p.gld * 4);
+  // decode-shaped calls (fewer than 64 rows): 16-entry lists of each 128-block wave
+  // of a row, when a row has at most 256 of them (the selection merges them in LDS)
+  const int waves = 8 * (int)((std::max(1, p.max_blocks) + 1023) / 1024);
+  p.max_lists = waves <= 256 && n_q < 64 ? waves : 0;
+  p.list_bytes = align256((size_t)p.rows_per_pass * p.max_lists * (16 * 8 + 8));
+  p.score_bytes = scores_given ? 0 : align256((size_t)p.rows_per_pass * p.ld * 4);
+  p.total = p.count_bytes + p.gm_bytes + p.list_bytes + p.score_bytes;
   return p;
 }
 
@@ -164,11 +170,10 @@ ip_status ip_time_next_launch(int32_t kernel_id, hipEvent_t start, hipEvent_t st
 }
 
 int64_t index_scores_ld(int32_t max_seq_len) {
-  // whole top-k chunks, so every chunk workgroup reads inside its row
-  const int max_blocks = std::max(1, (max_seq_len - 1) / 4);
-  const int64_t chunk = ip::topk_chunk_size(max_blocks);
+  // whole scoring tiles, so every scoring workgroup stores inside its row and the
+  // selection's vector reads stay inside the row
   const int64_t n = std::max<int64_t>(1, max_seq_len / 4);
-  return (n + chunk - 1) / chunk * chunk;
+  return (n + ip::SCORE_TILE - 1) / ip::SCORE_TILE * ip::SCORE_TILE;
 }
 
 // ------------------------------------------------------------------ IndexPool
@@ -298,7 +303,7 @@ ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cac
 size_t index_score_topk_workspace_bytes(const ip_seqs* seqs, int32_t n_q, int32_t top_k,
                                         int32_t scores_given) {
   if (!seqs || n_q < 1 || top_k < 1 || seqs->max_seq_len < 1) return 0;
-  return score_plan(seqs, n_q, top_k, scores_given != 0).total;
+  return score_plan(seqs, n_q, scores_given != 0).total;
 }
 
 }  // extern "C"
@@ -327,11 +332,8 @@ static ip_status score_topk_impl(const char* fn, const ip_seqs* seqs, int32_t n_
   } else {
     return fail(IP_EUNSUPPORTED, "%s: pooled keys must be FP8 or F32", fn);
   }
-  const ScorePlan plan = score_plan(seqs, n_q, top_k, scores != nullptr);
-  if ((int64_t)plan.n_chunks * (top_k - 1) > ip::TOPK_MERGE_CAP)
-    return fail(IP_EUNSUPPORTED, "%s: %d score chunks x (top_k-1) exceeds the merge capacity %d; lower max_seq_len or top_k",
-                fn, plan.n_chunks, ip::TOPK_MERGE_CAP);
-  if (plan.total > 0 && (!ws || ws_bytes < plan.total))
+  const ScorePlan plan = score_plan(seqs, n_q, scores != nullptr);
+  if (!ws || ws_bytes < plan.total)
     return fail(IP_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.total, ws ? ws_bytes : 0);
   if (((uintptr_t)ws & 255) != 0) return fail(IP_EINVAL, "%s: ws must be 256-byte aligned", fn);
 
@@ -339,13 +341,13 @@ static ip_status score_topk_impl(const char* fn, const ip_seqs* seqs, int32_t n_
     if (ip_status st = device_status(ip::launch_append(*append, stream), fn)) return st;
     append = nullptr;
   }
-  float* score_buf = scores ? scores : (float*)ws;
-  uint32_t* cand_key = (uint32_t*)((char*)ws + plan.score_bytes);
-  int32_t* cand_idx = (int32_t*)(cand_key + (plan.cand_bytes / 8));
-  int32_t* topk_count = plan.count_bytes ? (int32_t*)((char*)ws + plan.score_bytes + plan.cand_bytes) : nullptr;
+  int32_t* count = (int32_t*)ws;
+  float* gm = (float*)((char*)ws + plan.count_bytes);
+  char* lists = (char*)ws + plan.count_bytes + plan.gm_bytes;
+  float* score_buf = scores ? scores : (float*)(lists + plan.list_bytes);
 
-  for (int row0 = 0; row0 < n_q; row0 += plan.rows_per_chunk) {
-    const int nr = std::min(plan.rows_per_chunk, n_q - row0);
+  for (int row0 = 0; row0 < n_q; row0 += plan.rows_per_pass) {
+    const int nr = std::min(plan.rows_per_pass, n_q - row0);
     ip::ScoreArgs sa;
     sa.L = layout_of(seqs);
     sa.row0 = row0;
@@ -357,18 +359,28 @@ static ip_status score_topk_impl(const char* fn, const ip_seqs* seqs, int32_t n_
     sa.keys = (const uint8_t*)pooled->data;
     sa.key_stride = pooled->row_stride;
     sa.key_scale = pooled->scale;
+    // the kernels index scores, maxima and counters by (r - row0)
     sa.scores = scores ? score_buf + (int64_t)row0 * plan.ld : score_buf;
     sa.ld = plan.ld;
+    sa.gm = gm;
+    sa.gld = plan.gld;
     sa.heads = n_heads;
     sa.dim = head_dim;
     sa.max_blocks = plan.max_blocks;
-    sa.topk_count = topk_count;
+    sa.top_k = top_k;
+    sa.out = out_idx;
+    sa.count = count;
+    sa.max_lists = plan.max_lists;
+    sa.lists = plan.max_lists ? (uint64_t*)lists : nullptr;
+    sa.lists_meta = plan.max_lists ? (uint2*)(lists + (size_t)plan.rows_per_pass * plan.max_lists * 16 * 8) : nullptr;
     sa.with_append = append && row0 == 0;
     if (sa.with_append) sa.append = *append;
-    // the kernels index scores by (r - row0)
+    sa.fuse = 0;
+    sa.fuse = fp8 && ip::score_fuses_select(sa);
     ip_status st = device_status(fp8 ? ip::launch_score_fp8_bf16(sa, stream) : ip::launch_score_f32(sa, stream), fn);
     if (st) return st;
-    ip::TopkArgs ta;
+    if (sa.fuse) continue;
+    ip::SelectArgs ta;
     ta.L = sa.L;
     ta.row0 = row0;
     ta.n_rows = nr;
@@ -376,14 +388,11 @@ static ip_status score_topk_impl(const char* fn, const ip_seqs* seqs, int32_t n_
     ta.q_pos = q_pos;
     ta.scores = sa.scores;
     ta.ld = plan.ld;
+    ta.gm = gm;
+    ta.gld = plan.gld;
     ta.top_k = top_k;
     ta.out = out_idx;
-    ta.cand_key = cand_key;
-    ta.cand_idx = cand_idx;
-    ta.n_chunks = plan.n_chunks;
-    ta.chunk = plan.chunk;
-    ta.count = topk_count;
-    st = device_status(ip::launch_topk(ta, stream), fn);
+    st = device_status(ip::launch_select(ta, stream), fn);
     if (st) return st;
   }
   return IP_OK;

@@ -6,7 +6,7 @@
 
 namespace ip {
 
-constexpr int APPEND_NT = 256;           // threads of a workgroup that runs append_one
+constexpr int APPEND_NT = 256;           // threads of the append kernel's workgroups
 constexpr int APPEND_MAX_DIM = 256;
 
 __device__ __forceinline__ void softmax4(const float* lg, float* w) {
@@ -22,8 +22,12 @@ __device__ __forceinline__ void softmax4(const float* lg, float* w) {
 // the caches and, when that token completes a block, pools the block.  The new
 // key's codes and scale stay in registers for the pooling, which follows the same
 // arithmetic, in the same order, as compress_fp8_kernel / compress_f32_kernel.
+// NT: the workgroup's threads (at least 256: one key dim per thread, 4 latent
+// values per thread), all of which call it.
+template <int NT = APPEND_NT>
 __device__ __forceinline__ void append_one(const AppendArgs& a, int b) {
-  __shared__ float red[APPEND_NT / 64];
+  static_assert(NT >= 256 && NT % 64 == 0, "append workgroup size");
+  __shared__ float red[NT / 64];
   const int len = a.L.seq_lens[b];
   if (len < 1) return;
   const int64_t t = len - 1;
@@ -31,10 +35,10 @@ __device__ __forceinline__ void append_one(const AppendArgs& a, int b) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   // latent (or K) and V rows: plain 16-byte copies (the fp8 latent tier below)
   if (!a.kv_scale)
-    for (int i = tid; i < a.kv_row_bytes / 16; i += APPEND_NT)
+    for (int i = tid; i < a.kv_row_bytes / 16; i += NT)
       *(uint4*)(a.kv + row * a.kv_stride + 16 * i) = *(const uint4*)(a.kv_new + (int64_t)b * a.kv_row_bytes + 16 * i);
   if (a.v)
-    for (int i = tid; i < a.v_row_bytes / 16; i += APPEND_NT)
+    for (int i = tid; i < a.v_row_bytes / 16; i += NT)
       *(uint4*)(a.v + row * a.v_stride + 16 * i) = *(const uint4*)(a.v_new + (int64_t)b * a.v_row_bytes + 16 * i);
   auto block_max = [&](float v) {                // max over the workgroup (all threads call)
     v = wave_max(v);
@@ -42,7 +46,7 @@ __device__ __forceinline__ void append_one(const AppendArgs& a, int b) {
     __syncthreads();
     float m = red[0];
 #pragma unroll
-    for (int w = 1; w < APPEND_NT / 64; ++w) m = fmaxf(m, red[w]);
+    for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
     __syncthreads();
     return m;
   };

@@ -8,7 +8,7 @@
 
 namespace ip {
 
-enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3, K_ATTN = 4, K_COMBINE = 5, K_APPEND = 6, K_KDA = 7, K_LAST = 7 };
+enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3 /* select */, K_ATTN = 4, K_COMBINE = 5, K_APPEND = 6, K_KDA = 7, K_LAST = 7 };
 
 // Takes (and disarms) the timing hook's events if one is armed for kernel `id`.
 bool hook_take(int id, hipEvent_t* start, hipEvent_t* stop);
@@ -72,7 +72,7 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
-// ------------------------------------------------------------ indexer scoring
+// ------------------------------------------------------------ indexer scoring + selection
 struct ScoreArgs {
   Layout L;
   int row0, n_rows;            // query rows [row0, row0 + n_rows)
@@ -84,36 +84,42 @@ struct ScoreArgs {
   int64_t key_stride;
   const float* key_scale;      // [pooled rows] (fp8) or null
   float* scores;               // [n_rows, ld], row r - row0
-  int64_t ld;
+  int64_t ld;                  // a multiple of 512
+  float* gm;                   // [n_rows, gld] maxima of groups of 16 consecutive scores
+  int64_t gld;                 // ld / 16
   int heads, dim;
   int max_blocks;              // key range covered by the grid
-  int32_t* topk_count;         // [n_rows] or null: zeroed here for the top-k that follows
+  int fuse;                    // select in the same launch (one row per workgroup)
+  int top_k;                   // fused selection: ids out
+  int32_t* out;                // [n_q, top_k], row r
+  int32_t* count;              // [n_rows] per-row counters, zero on entry and on exit
+  uint64_t* lists;             // fused: [n_rows, max_lists, 16] per-wave candidate lists, or null
+  uint2* lists_meta;           // [n_rows, max_lists] (count, threshold) of each list
+  int max_lists;               // waves per row covered by the grid
   int with_append;             // decode: extra grid rows of workgroups run `append`,
   AppendArgs append;           // one sequence each (see append.hpp)
 };
 hipError_t launch_score_fp8_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s);
+// whether launch_score_fp8_bf16 selects in the same launch for these arguments
+// (then a.fuse must be set; otherwise launch_select follows)
+bool score_fuses_select(const ScoreArgs& a);
+constexpr int SCORE_TILE = 1024;    // score rows pad to whole tiles of the scoring workgroups
 
 // ------------------------------------------------------------ top-k selection
-struct TopkArgs {
+struct SelectArgs {
   Layout L;
   int row0, n_rows;
   const int32_t* q_seq;
   const int32_t* q_pos;
   const float* scores;         // [n_rows, ld]
   int64_t ld;
+  const float* gm;             // [n_rows, gld]
+  int64_t gld;
   int top_k;
   int32_t* out;                // [n_q, top_k], row r
-  uint32_t* cand_key;          // [n_rows, n_chunks, top_k - 1]
-  int32_t* cand_idx;           // same
-  int n_chunks;                // chunks per row covered by the grid
-  int chunk;                   // scores per chunk (topk_chunk_size)
-  int32_t* count;              // [n_rows] chunks done per row, zero on entry (n_chunks > 1)
 };
-constexpr int TOPK_MAX_CHUNK = 16384;   // scores per chunk workgroup (512 threads x 32)
-constexpr int TOPK_MERGE_CAP = 16384;   // candidate slots per row in the in-kernel merge (512 x 32)
-int topk_chunk_size(int max_blocks);
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------ sparse attention
 struct AttnArgs {

@@ -11,60 +11,99 @@
 // scale sigma_j > 0 is applied after the ReLU (relu(sigma x) = sigma relu(x)).
 // The output layout puts one key per lane and 16 heads per lane, so the gated
 // head-sum is 16 local FMAs plus one cross-half exchange.
+//
+// Every scoring kernel also writes the largest score of each group of 16
+// consecutive blocks (the group maxima the selection starts from).  Decode-shaped
+// launches (one query row per workgroup) select in the same launch: each
+// workgroup counts itself in on a per-row counter once its scores are stored, and
+// the one that completes the count selects the row (select.hpp) and clears the
+// counter for the next call.
 #include "append.hpp"
+#include "select.hpp"
 
 namespace ip {
 
 namespace {
 
-constexpr int NT = 256;
-static_assert(NT == APPEND_NT, "the fused append runs in scoring workgroups");
+constexpr int NT = 256;                         // f32 kernel; prefill fp8 workgroups
 constexpr int TILES = 4;                        // 32-key tiles per wave
-constexpr int KEYS_PER_WG = 4 * TILES * 32;     // 512
 constexpr int HI = 32, DI = 128;
+
+struct QStage {
+  static constexpr int QROW = DI + 8;           // padded LDS row (272 bytes): conflict-free reads
+  uint16_t qs[2][HI * QROW];                    // double-buffered query rows
+  float gs[2][HI];
+};
+
+// the largest of the 16 values of this lane's 16-lane row (DPP within rows)
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(-INFINITY, x));      // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(-INFINITY, x));      // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(-INFINITY, x));     // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(-INFINITY, x));     // row_mirror
+  return x;
+}
+
+template <int NWV, bool FUSE>
+constexpr size_t score_smem() {
+  return FUSE && sizeof(sel::Shared<NWV * 64>) > sizeof(QStage) ? sizeof(sel::Shared<NWV * 64>) : sizeof(QStage);
+}
 
 // RPW query rows share one key chunk held in registers (prefill, where consecutive
 // rows are tokens of one sequence); decode rows are separate sequences and use 1.
-// All key loads of a wave are issued before the first MFMA, so each compute unit
-// keeps ~128 KB of the pooled cache in flight.
-template <int RPW>
-__global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
-  constexpr int QROW = DI + 8;                  // padded LDS row (272 bytes): conflict-free reads
-  __shared__ __align__(16) uint16_t qs[2][HI * QROW];   // double-buffered query rows
-  __shared__ float gs[2][HI];
+// A workgroup of NWV waves covers NWV * 128 keys.  All key loads of a wave are
+// issued before the first MFMA: decode launches use 8 waves (1024 keys, 132 KB of
+// pooled rows in flight per workgroup) so that one workgroup per compute unit
+// covers the whole batch of the 128K-token decode workload at once.
+template <int RPW, int NWV, bool FUSE>
+__global__ __launch_bounds__(NWV * 64) void score_fp8_bf16_kernel(ScoreArgs a) {
+  static_assert(!FUSE || RPW == 1, "the fused selection handles one row per workgroup");
+  constexpr int NTW = NWV * 64;
+  constexpr int KEYS = NWV * TILES * 32;
+  static_assert(SCORE_TILE % KEYS == 0, "score rows pad to whole workgroup tiles");
+  constexpr int QROW = QStage::QROW;
+  // the query stage, and (fused) the selection's state once scoring is done
+  __shared__ __align__(16) uint8_t smem[score_smem<NWV, FUSE>()];
+  __shared__ int last_here;
+  QStage& st = *reinterpret_cast<QStage*>(smem);
+  auto& qs = st.qs;
+  auto& gs = st.gs;
   if (a.with_append && (int)blockIdx.y >= a.n_rows) {
     // the fused decode append, one sequence per workgroup of the extra grid rows:
     // scoring reads pooled rows of blocks before the query's own block only, and
     // the append writes the new token's rows and the pooled row of the block it
     // completes (the query's own block)
     const int b = ((int)blockIdx.y - a.n_rows) * (int)gridDim.x + (int)blockIdx.x;
-    if (b < a.append.batch) append_one(a.append, b);
+    if (b < a.append.batch) append_one<NTW>(a.append, b);
     return;
   }
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int kl = lane & 31, hh = lane >> 5;
-  const int kc0 = blockIdx.x * KEYS_PER_WG;
+  const int kc0 = blockIdx.x * KEYS;
   const int rbeg = a.row0 + blockIdx.y * RPW;
   const int rend = min(rbeg + RPW, a.row0 + a.n_rows);
-  if (a.topk_count && blockIdx.x == 0 && (int)threadIdx.x < rend - rbeg)
-    a.topk_count[rbeg + threadIdx.x - a.row0] = 0;
 
   // query rows (8 KB) and gates go through LDS; row r+1's are loaded while row r
   // is computed, and staged in the other buffer, so one barrier per row suffices
   // and the load latency of a row is hidden behind the previous one.  Thread t
-  // holds elements 16t .. 16t+15 = head t/8, dims (t%8)*16 ..
+  // (t < 256) holds elements 16t .. 16t+15 = head t/8, dims (t%8)*16 ..
+  const bool qt = threadIdx.x < 256;
   u32x4_t qv0, qv1;
   float gv = 0.f;
   auto load_q = [&](int r) {
     const u32x4_t* qg = (const u32x4_t*)((const uint16_t*)a.q + (int64_t)r * HI * DI);
-    qv0 = qg[2 * threadIdx.x];
-    qv1 = qg[2 * threadIdx.x + 1];
+    if (qt) {
+      qv0 = qg[2 * threadIdx.x];
+      qv1 = qg[2 * threadIdx.x + 1];
+    }
     if (threadIdx.x < HI) gv = a.gates[(int64_t)r * HI + threadIdx.x];
   };
   auto stage_q = [&](int buf) {
     const int h = threadIdx.x >> 3, d = (threadIdx.x & 7) * 16;
-    *(u32x4_t*)(qs[buf] + h * QROW + d) = qv0;
-    *(u32x4_t*)(qs[buf] + h * QROW + d + 8) = qv1;
+    if (qt) {
+      *(u32x4_t*)(qs[buf] + h * QROW + d) = qv0;
+      *(u32x4_t*)(qs[buf] + h * QROW + d + 8) = qv1;
+    }
     if (threadIdx.x < HI) gs[buf][threadIdx.x] = gv;
   };
   // per-row sequence, position and pooled-row count, one row per lane, read once
@@ -83,6 +122,7 @@ __global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
 
   bf16x8_t kf[TILES][8];
   float ksig[TILES];
+  float scv[TILES];                             // this lane's scores of the last row (all tiles)
   int cur_b = -1;
 
   for (int r = rbeg, i = 0; r < rend; ++r, ++i) {
@@ -142,6 +182,8 @@ __global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
     }
     if (!run) continue;
 
+    float* srow = a.scores + (int64_t)(r - a.row0) * a.ld;
+    float* grow = a.gm + (int64_t)(r - a.row0) * a.gld;
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       f32x16_t acc = {};
@@ -152,8 +194,73 @@ __global__ __launch_bounds__(NT) void score_fp8_bf16_kernel(ScoreArgs a) {
       for (int e = 0; e < 16; ++e) part = fmaf(g[e], fmaxf(acc[e], 0.f), part);
       part += __shfl_xor(part, 32);
       const int j = kc0 + (wv * TILES + t) * 32 + kl;
-      if (hh == 0 && j < nel) a.scores[(int64_t)(r - a.row0) * a.ld + j] = part * ksig[t];
+      const float sc = j < nel ? part * ksig[t] : -INFINITY;
+      scv[t] = sc;
+      // the maximum of each group of 16 consecutive blocks: lanes kl 0..15 and
+      // 16..31 of the tile are 16-lane rows
+      const float gmax = row16_max(sc);
+      if (hh == 0 && j < nel) {
+        if constexpr (FUSE) sel::st_agent(srow + j, sc);
+        else srow[j] = sc;
+        if ((kl & 15) == 0) {
+          if constexpr (FUSE) sel::st_agent(grow + (j >> 4), gmax);
+          else grow[j >> 4] = gmax;
+        }
+      }
     }
+  }
+  if constexpr (FUSE) {
+    // one row: select it once every workgroup that scored it has stored its part
+    const int r = rbeg;
+    const int p = __builtin_amdgcn_readlane(rp, 0);
+    const int nel = p >> 2;
+    const int need = min(a.top_k, nel + 1) - 1;
+    int32_t* out = a.out + (int64_t)r * a.top_k;
+    sel::Shared<NTW>& ss = *reinterpret_cast<sel::Shared<NTW>*>(smem);
+    if (need == 0 || need >= nel) {
+      // nothing to rank: the own block alone, or every eligible block
+      if (blockIdx.x == 0) {
+        __syncthreads();
+        sel::select_row<NTW>(nullptr, nullptr, nel, nel, a.top_k, out, ss);
+      }
+      return;
+    }
+    if (kc0 >= nel) return;                      // this workgroup scored nothing
+    const int n_run = (nel + KEYS - 1) / KEYS;
+    const int n_lists = n_run * NWV;
+    // rows long enough for about 2 winners per wave: every wave lists its best
+    // (see sel::wave_list) and the last workgroup merges the lists
+    const bool lists = a.lists && n_lists * sel::LIST <= sel::C_CAP && n_lists <= NTW && need <= 2 * n_lists;
+    uint64_t* lrow = lists ? a.lists + (int64_t)(r - a.row0) * a.max_lists * sel::LIST : nullptr;
+    uint2* mrow = lists ? a.lists_meta + (int64_t)(r - a.row0) * a.max_lists : nullptr;
+    if (lists) {
+      const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hh = lane >> 5, kl = lane & 31;
+      uint32_t k[2];
+      int id[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int t = 2 * hh + i;
+        id[i] = kc0 + (wv * TILES + t) * 32 + kl;
+        k[i] = id[i] < nel ? float_key(scv[t]) : 0u;
+      }
+      const int slot = blockIdx.x * NWV + wv;
+      sel::wave_list<4>(k, id, lrow + (int64_t)slot * sel::LIST, mrow + slot);
+    }
+    // every score, maximum and list entry of this workgroup is stored (acknowledged
+    // by memory) before it counts itself in: the stores are device-coherent, so the
+    // workgroup that completes the count reads them with device-coherent loads
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (threadIdx.x == 0) last_here = atomicAdd(a.count + (r - a.row0), 1) == n_run - 1;
+    __syncthreads();
+    if (!last_here) return;
+    if (threadIdx.x == 0) sel::st_agent(a.count + (r - a.row0), 0);   // clear for the next call
+    if (lists && sel::merge_lists<NTW>(lrow, mrow, n_lists, need, nel, a.top_k, out, ss)) return;
+    __syncthreads();
+    sel::select_row<NTW>(a.scores + (int64_t)(r - a.row0) * a.ld, a.gm + (int64_t)(r - a.row0) * a.gld, nel,
+                         nel, a.top_k, out, ss);
   }
 }
 
@@ -167,39 +274,48 @@ __global__ __launch_bounds__(NT) void score_f32_kernel(ScoreArgs a) {
   const int p = a.q_pos ? a.q_pos[r] : a.L.seq_lens[b] - 1;
   const int nel = p >> 2;
   const int j = blockIdx.x * NT + threadIdx.x;
-  if (a.topk_count && blockIdx.x == 0 && threadIdx.x == 0) a.topk_count[blockIdx.y] = 0;
   if ((int)(blockIdx.x * NT) >= nel) return;
   const int HD = a.heads * a.dim;
   const float* q = (const float*)a.q + (int64_t)r * HD;
   for (int i = threadIdx.x; i < HD; i += NT) qs[i] = q[i];
   for (int i = threadIdx.x; i < a.heads; i += NT) gs[i] = a.gates[(int64_t)r * a.heads + i];
   __syncthreads();
-  if (j >= nel) return;
-  const float* k = (const float*)(a.keys + a.L.pool_row(b, j) * a.key_stride);
-  float s = 0.f;
-  for (int h = 0; h < a.heads; ++h) {
-    float d = 0.f;
-    for (int e = 0; e < a.dim; ++e) d = fmaf(qs[h * a.dim + e], k[e], d);
-    s = fmaf(gs[h], fmaxf(d, 0.f), s);
+  float s = -INFINITY;
+  if (j < nel) {
+    const float* k = (const float*)(a.keys + a.L.pool_row(b, j) * a.key_stride);
+    s = 0.f;
+    for (int h = 0; h < a.heads; ++h) {
+      float d = 0.f;
+      for (int e = 0; e < a.dim; ++e) d = fmaf(qs[h * a.dim + e], k[e], d);
+      s = fmaf(gs[h], fmaxf(d, 0.f), s);
+    }
+    a.scores[(int64_t)(r - a.row0) * a.ld + j] = s;
   }
-  a.scores[(int64_t)(r - a.row0) * a.ld + j] = s;
+  // groups of 16 consecutive blocks are 16-lane rows of the wave
+  const float gmax = row16_max(s);
+  if ((threadIdx.x & 15) == 0 && j < nel) a.gm[(int64_t)(r - a.row0) * a.gld + (j >> 4)] = gmax;
 }
 
 }  // namespace
 
 hipError_t launch_score_fp8_bf16(const ScoreArgs& a, hipStream_t s) {
   if (a.n_rows <= 0 || a.max_blocks <= 0) return hipSuccess;
-  const unsigned gx = (a.max_blocks + KEYS_PER_WG - 1) / KEYS_PER_WG;
-  if (a.q_seq && a.n_rows >= 64 && !a.with_append) {
+  if (!score_fuses_select(a)) {
     // prefill: consecutive rows are query tokens of one sequence and share its keys
-    constexpr int R = 32;
-    launch(K_SCORE, score_fp8_bf16_kernel<R>, dim3(gx, (a.n_rows + R - 1) / R), dim3(NT), s, a);
+    constexpr int R = 32, W = 4, KEYS = W * TILES * 32;
+    const unsigned gx = (a.max_blocks + KEYS - 1) / KEYS;
+    launch(K_SCORE, score_fp8_bf16_kernel<R, W, false>, dim3(gx, (a.n_rows + R - 1) / R), dim3(W * 64), s, a);
   } else {
+    constexpr int W = 8, KEYS = W * TILES * 32;
+    const unsigned gx = (a.max_blocks + KEYS - 1) / KEYS;
     const unsigned app_rows = a.with_append ? (a.append.batch + gx - 1) / gx : 0;
-    launch(K_SCORE, score_fp8_bf16_kernel<1>, dim3(gx, a.n_rows + app_rows), dim3(NT), s, a);
+    if (!a.fuse) return hipErrorInvalidValue;
+    launch(K_SCORE, score_fp8_bf16_kernel<1, W, true>, dim3(gx, a.n_rows + app_rows), dim3(W * 64), s, a);
   }
   return hipGetLastError();
 }
+
+bool score_fuses_select(const ScoreArgs& a) { return !(a.q_seq && a.n_rows >= 64 && !a.with_append); }
 
 hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s) {
   if (a.n_rows <= 0 || a.max_blocks <= 0) return hipSuccess;

@@ -1,0 +1,728 @@
+// Learned sparse selection of one query row: keep the query's own block plus the
+// k'-1 best-scoring earlier blocks (k' = min(top_k, b_q + 1)), ties to the lower
+// block id, ids out in ascending order.  G2C Brief "GLM-5.3-Flash: hybrid
+// attention becomes the product", section "DSA keeps selected global access in
+// eleven layers" (top 2048 tokens = 512 pooled blocks).
+//
+// Scores are compared through their order-preserving uint32 keys.  Every
+// threshold below is found by narrowing a key interval: the keys of the interval
+// are bucketed linearly over it (2048 buckets), the bucket that holds the wanted
+// rank becomes the next interval, until it holds few keys, is kept whole, or is a
+// single key.  That works for any score distribution, heavy tails included.  The
+// scoring kernels also write, for every group of 16 consecutive blocks, the
+// largest score of the group.  One workgroup selects the need = k'-1 best of the
+// row's n eligible scores:
+//   1. a key bound G from the group maxima: the lower end of a narrow interval
+//      holding the need-th largest maximum.  At least need maxima -- so at least
+//      need scores -- have keys >= G, so every winner has a key >= G, and so has
+//      the maximum of its group;
+//   2. the scores with keys >= G: a superset of the winners, typically a few
+//      percent larger than need, compacted in ascending id order into LDS.  Rows
+//      of up to 32 scores per thread are read whole in one pass (their group
+//      maxima are taken in registers); longer rows read the stored maxima first
+//      and then only the groups whose maximum reaches G;
+//   3. the exact select among those candidates, narrowing to the need-th largest
+//      key; equal keys at the boundary go to the lower id.
+// Rows with fewer than 2 need groups take the bound from the scores themselves.
+// When the candidates do not fit in LDS (scores that are largely equal), a radix
+// select over the keys of the whole row runs instead.
+//
+// Scores and group maxima written by other workgroups of the same kernel are read
+// with device-coherent loads (they bypass this die's L2, which may not have seen
+// them); data written by an earlier kernel reads the same way.
+#pragma once
+#include "kernels.hpp"
+
+namespace ip {
+namespace sel {
+
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int GROUP = 16;          // scores per group maximum
+constexpr int NBINS = 2048;        // buckets of a key interval (and one 11-bit digit)
+constexpr int CG_CAP = 2048;       // candidate groups held in LDS
+constexpr int C_CAP = 4096;        // candidate scores held in LDS (> top_k - 1)
+constexpr int RE = 16;             // scores per thread per tile of the row-wide radix path
+constexpr int REFINE = 32;         // a bound's interval holding more keys is narrowed further
+constexpr int VB = 16;             // values of the bound's source per thread per tile
+
+template <int NT>
+struct Shared {
+  static constexpr int NW = NT / 64;
+  int hist[NBINS + 64];            // + one spare bin per lane for empty slots (never read)
+  int xi[2][NW], xj[2][NW];        // per-wave exchange slots, two sets
+  int digit, above, count;         // find_bin's result
+  int wn[2][NW];                   // per-wave counts, two sets
+  int fb[NW];                      // find_bin's per-wave bin sums
+  int cg[CG_CAP];                  // candidate groups, ascending
+  uint32_t ckey[C_CAP + 64];       // candidates (order-preserving key, id), ascending id;
+  int32_t cid[C_CAP + 64];         // + one spare entry per lane
+};
+
+// digit l of a key: bits 31..21, 20..10, 9..0
+__device__ __forceinline__ int dshift(int l) { return l == 0 ? 21 : (l == 1 ? 10 : 0); }
+__device__ __forceinline__ uint32_t dmask(int l) { return l == 2 ? 0x3FFu : 0x7FFu; }
+__device__ __forceinline__ int digit_of(uint32_t k, int l) { return (int)((k >> dshift(l)) & dmask(l)); }
+
+// ---------------------------------------------------------------- device-coherent access
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Device-coherent 16-byte reads of data other workgroups of the kernel stored with
+// st_agent: plain buffer loads with the device-scope cache policy (sc1), which the
+// compiler keeps in flight together (an atomic load waits for each one in turn).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0xFFFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t ld16_dev(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 16 /* sc1 */);
+}
+
+// ---------------------------------------------------------------- workgroup exchanges
+// Each holds exactly one barrier.  Two consecutive calls must use different slot
+// sets p (a call's slots may still be read by slower waves until the next barrier).
+
+// exclusive prefix of x over the threads (thread order), its total, and the sum of y
+template <int NT>
+__device__ __forceinline__ int x_scan(int x, int y, Shared<NT>& sh, int p, int* total, int* ysum) {
+  const int wv = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(x);
+  y = wave_sum(y);
+  if ((threadIdx.x & 63) == 0) { sh.xi[p][wv] = lane63(incl); sh.xj[p][wv] = y; }
+  __syncthreads();
+  int before = 0, tot = 0, ys = 0;
+#pragma unroll
+  for (int i = 0; i < Shared<NT>::NW; ++i) {
+    const int c = sh.xi[p][i];
+    before += i < wv ? c : 0;
+    tot += c;
+    ys += sh.xj[p][i];
+  }
+  *total = tot;
+  *ysum = ys;
+  return before + incl - x;
+}
+
+// min and max of unsigned keys over the threads (DPP within waves, one exchange)
+__device__ __forceinline__ uint32_t wave_umin(uint32_t x) {
+  x = min(x, (uint32_t)dpp_i<0xB1>((int)0xFFFFFFFF, (int)x));
+  x = min(x, (uint32_t)dpp_i<0x4E>((int)0xFFFFFFFF, (int)x));
+  x = min(x, (uint32_t)dpp_i<0x141>((int)0xFFFFFFFF, (int)x));
+  x = min(x, (uint32_t)dpp_i<0x140>((int)0xFFFFFFFF, (int)x));
+  x = min(x, (uint32_t)dpp_i<0x142, 0xA>((int)0xFFFFFFFF, (int)x));
+  x = min(x, (uint32_t)dpp_i<0x143, 0xC>((int)0xFFFFFFFF, (int)x));
+  return (uint32_t)lane63((int)x);
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+  x = max(x, (uint32_t)dpp_i<0xB1>(0, (int)x));
+  x = max(x, (uint32_t)dpp_i<0x4E>(0, (int)x));
+  x = max(x, (uint32_t)dpp_i<0x141>(0, (int)x));
+  x = max(x, (uint32_t)dpp_i<0x140>(0, (int)x));
+  x = max(x, (uint32_t)dpp_i<0x142, 0xA>(0, (int)x));
+  x = max(x, (uint32_t)dpp_i<0x143, 0xC>(0, (int)x));
+  return (uint32_t)lane63((int)x);
+}
+template <int NT>
+__device__ __forceinline__ void x_uminmax(uint32_t& mn, uint32_t& mx, Shared<NT>& sh, int p) {
+  const int wv = threadIdx.x >> 6;
+  mn = wave_umin(mn);
+  mx = wave_umax(mx);
+  if ((threadIdx.x & 63) == 0) { sh.xi[p][wv] = (int)mn; sh.xj[p][wv] = (int)mx; }
+  __syncthreads();
+  uint32_t a = 0xFFFFFFFFu, b = 0u;
+#pragma unroll
+  for (int i = 0; i < Shared<NT>::NW; ++i) { a = min(a, (uint32_t)sh.xi[p][i]); b = max(b, (uint32_t)sh.xj[p][i]); }
+  mn = a;
+  mx = b;
+}
+
+// exclusive prefix of x over the lanes, and the wave total
+__device__ __forceinline__ int wave_excl(int x, int& total) {
+  const int incl = wave_incl_scan(x);
+  total = lane63(incl);
+  return incl - x;
+}
+
+// Histogram scan over bins [0, NB) by the whole workgroup: thread t owns the
+// C = NB / NT bins below NB - C t (descending order over the threads), reads them
+// with 16-byte LDS reads (adjacent threads, adjacent addresses: no bank
+// conflicts), and one workgroup scan of the per-thread sums finds the thread whose
+// bins hold the bin d with count(bins > d) < remaining <= count(bins >= d); it
+// resolves d among its own bins.  Leaves sh.digit = d, sh.above = count(bins > d)
+// and sh.count = count(bin d), and clears the bins for the next use.  Enters after
+// the barrier that completed the histogram; two barriers.  Needs 1 <= remaining
+// <= total.
+template <int NB, int NT>
+__device__ __forceinline__ void find_bin(Shared<NT>& sh, int remaining) {
+  constexpr int C = NB / NT;
+  static_assert(C >= 4 && C % 4 == 0, "bins per thread");
+  const int t = threadIdx.x, wv = t >> 6;
+  const int lo = NB - C * (t + 1);
+  int v[C];
+#pragma unroll
+  for (int q = 0; q < C; q += 4) {
+    const i32x4_t x = *(const i32x4_t*)&sh.hist[lo + q];
+    v[q] = x[0]; v[q + 1] = x[1]; v[q + 2] = x[2]; v[q + 3] = x[3];
+  }
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < C; ++q) sum += v[q];
+  int wt;
+  const int excl = wave_excl(sum, wt);
+  if ((t & 63) == 0) sh.fb[wv] = wt;
+  // every read above is done before the bins are cleared (in issue order for this
+  // wave; the other waves read only their own bins)
+#pragma unroll
+  for (int q = 0; q < C; q += 4) *(i32x4_t*)&sh.hist[lo + q] = i32x4_t{0, 0, 0, 0};
+  __syncthreads();
+  int before = excl;
+#pragma unroll
+  for (int i = 0; i < Shared<NT>::NW; ++i) before += i < wv ? sh.fb[i] : 0;
+  if (before < remaining && before + sum >= remaining) {
+    int acc = before;
+#pragma unroll
+    for (int q = C - 1; q >= 0; --q) {
+      if (acc < remaining && acc + v[q] >= remaining) {
+        sh.digit = lo + q;
+        sh.above = acc;
+        sh.count = v[q];
+      }
+      acc += v[q];
+    }
+  }
+  __syncthreads();
+}
+
+// Histogram update of one value per lane (an LDS atomic costs the same per wave
+// instruction whether its lanes' buckets are spread or shared).
+__device__ __forceinline__ void hist_add(int* hist, int bin, bool valid) {
+  if (valid) atomicAdd(&hist[bin], 1);
+}
+
+// Narrows to the key interval [base, base + width) holding the need-th largest of
+// the keys the threads hold (key 0 = none; need <= their number): the interval of
+// all keys, then repeatedly the one of its 2048 linear buckets that holds the
+// rank, until that bucket holds at most `stop` keys (stop = 0: never), is kept
+// whole, or is a single key (width 1).  On return every key >= base + width
+// ranks above the need-th, and `rem` (1 .. count) keys of the interval complete
+// the need; whole: rem equals the interval's count.  Enters after a barrier.
+template <int NT, int E>
+__device__ __forceinline__ void narrow(const uint32_t (&key)[E], int need, int stop, Shared<NT>& sh,
+                                       uint32_t& base, uint64_t& width, int& rem, bool& whole, uint32_t kmin = 0,
+                                       uint32_t kmax = 0) {
+  // the keys' range, unless the caller knows it (kmax != 0)
+  uint32_t mn = kmin, mx = kmax;
+  if (!kmax) {
+    mn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (key[e]) { mn = min(mn, key[e]); mx = max(mx, key[e]); }
+    x_uminmax(mn, mx, sh, 0);
+  }
+  base = mn;
+  width = (uint64_t)(mx - mn) + 1;
+  const uint32_t span = mx - mn;
+  int shift = (span >> 11) ? 32 - __clz((int)(span >> 11)) : 0;   // span >> shift < 2048
+  rem = need;
+  whole = false;
+#pragma unroll 1
+  for (;;) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool in = key[e] && key[e] >= base && (uint64_t)(key[e] - base) < width;
+      hist_add(sh.hist, in ? (int)((key[e] - base) >> shift) : 0, in);
+    }
+    __syncthreads();
+    find_bin<NBINS>(sh, rem);
+    rem -= sh.above;
+    const int cnt = sh.count;
+    base += (uint32_t)sh.digit << shift;
+    width = (uint64_t)1 << shift;
+    whole = cnt == rem;
+    if (whole || shift == 0 || cnt <= stop) break;
+    shift = shift > 11 ? shift - 11 : 0;
+  }
+}
+
+// ---------------------------------------------------------------- ordered compaction
+// A workgroup's waves each hold `n` consecutive entries of an ascending list and
+// keep some of them: the kept entries are written to dst [0, ...) in list order.
+// Wave w's entries come first in the list when w is lower; within a wave lane l's
+// entries of round q come before lane l+1's, and round q's before round q+1's.
+// Counting and writing are two steps around one exchange of the wave totals.
+
+// wave totals -> this wave's offset in the workgroup and the workgroup total (one
+// barrier; set p alternates between consecutive calls)
+template <int NT>
+__device__ __forceinline__ int wave_base(int wave_total, Shared<NT>& sh, int p, int& all) {
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh.wn[p][wv] = wave_total;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < Shared<NT>::NW; ++i) {
+    const int c = sh.wn[p][i];
+    before += i < wv ? c : 0;
+    tot += c;
+  }
+  all = tot;
+  return before;
+}
+
+// Keeps the need best (ties to the lower id) of a flat candidate list held in
+// registers: wave w holds entries [w per, (w+1) per), lane l of round i entry
+// w per + 64 i + l (key 0 = an empty slot; more than need entries in all), and
+// writes their ids to out[0, need) in list (ascending id) order.  Writes nothing
+// and returns false when `limit` exceeds the lower end of the interval found for
+// the need-th key (the caller's lists may then miss a winner); `limit` 0 never
+// does.  kmax != 0: [kmin, kmax] is the keys' range.  Enters after a barrier.
+template <int NT, int E>
+__device__ __forceinline__ bool keep_best_regs(const uint32_t (&key)[E], const int32_t (&cid)[E], int need,
+                                               int32_t* out, Shared<NT>& sh, uint32_t limit, uint32_t kmin,
+                                               uint32_t kmax) {
+  uint32_t base;
+  uint64_t width;
+  int rem;
+  bool whole;
+  narrow<NT, E>(key, need, 0, sh, base, width, rem, whole, kmin, kmax);
+  if (limit > base) return false;                 // uniform
+  const uint64_t top = (uint64_t)base + width;    // keys >= top are kept
+  // ties at the boundary (width 1, not kept whole) go to the lowest ids: their
+  // rank in list order
+  int tie_w = 0;
+  int pos[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const bool in = key[i] && key[i] >= base && (uint64_t)key[i] < top;
+    int t;
+    pos[i] = tie_w + wave_excl(in, t);
+    tie_w += t;
+  }
+  int all;
+  const int tie0 = whole ? 0 : wave_base(tie_w, sh, 1, all);
+  bool k[E];
+  int kept_w = 0;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const bool in = key[i] && key[i] >= base && (uint64_t)key[i] < top;
+    k[i] = (uint64_t)key[i] >= top || (in && (whole || tie0 + pos[i] < rem));
+    int t;
+    pos[i] = kept_w + wave_excl(k[i], t);         // now: this entry's place among the wave's kept
+    kept_w += t;
+  }
+  const int off = wave_base(kept_w, sh, 0, all);
+#pragma unroll
+  for (int i = 0; i < E; ++i)
+    if (k[i]) out[off + pos[i]] = cid[i];
+  return true;
+}
+
+// keep_best_regs over the flat candidate list sh.ckey / sh.cid [0, M), M <= C_CAP.
+template <int NT>
+__device__ __noinline__ bool keep_best(int M, int need, int32_t* out, Shared<NT>& sh, uint32_t limit = 0) {
+  constexpr int NW = Shared<NT>::NW, E = C_CAP / NT;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int per = (M + NW - 1) / NW;
+  const int lo = wv * per, hi = min(M, lo + per);
+  uint32_t key[E];
+  int32_t cid[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int at = lo + 64 * i + lane;
+    key[i] = at < hi ? sh.ckey[at] : 0u;          // key 0: no entry (no score maps to it)
+    cid[i] = at < hi ? sh.cid[at] : 0;
+  }
+  return keep_best_regs<NT, E>(key, cid, need, out, sh, limit, 0u, 0u);
+}
+
+// Radix select over the order-preserving keys of the whole row (any score
+// distribution): the need-th largest key digit by digit, then the kept ids (keys
+// above it, then ties in id order) are written straight to `out`.
+template <int NT>
+__device__ __noinline__ void radix_row(const float* S, int nel, int need, int bq, int top_k, int32_t* out,
+                                       Shared<NT>& sh) {
+  const int t0 = threadIdx.x * RE;
+  const __amdgpu_buffer_rsrc_t rs = dev_rsrc(S);
+  auto load_keys = [&](int base, uint32_t (&key)[RE]) {
+    const int j0 = base + t0;
+    u32x4_t v[RE / 4];
+    // rows are padded past nel to whole tiles of 1024: a started chunk stays inside
+#pragma unroll
+    for (int q = 0; q < RE / 4; ++q) v[q] = j0 < nel ? ld16_dev(rs, (uint32_t)(j0 + 4 * q) * 4u) : u32x4_t{};
+#pragma unroll
+    for (int e = 0; e < RE; ++e) key[e] = j0 + e < nel ? float_key(__uint_as_float(v[e >> 2][e & 3])) : 0u;
+  };
+  for (int i = threadIdx.x; i < NBINS; i += NT) sh.hist[i] = 0;
+  __syncthreads();
+  uint32_t prefix = 0, pmask = 0;
+  int rem = need;
+#pragma unroll 1
+  for (int l = 0; l < 3; ++l) {
+#pragma unroll 1
+    for (int base = 0; base < nel; base += NT * RE) {
+      uint32_t key[RE];
+      load_keys(base, key);
+#pragma unroll
+      for (int e = 0; e < RE; ++e) {
+        const bool in = key[e] && (key[e] & pmask) == prefix;
+        hist_add(sh.hist, in ? digit_of(key[e], l) : 0, in);
+      }
+    }
+    __syncthreads();
+    find_bin<NBINS>(sh, rem);
+    rem -= sh.above;
+    prefix |= (uint32_t)sh.digit << dshift(l);
+    pmask |= dmask(l) << dshift(l);
+  }
+  // prefix is the need-th largest key; keep every key above it and the first rem
+  // equal to it, in id order
+  int done = 0, ties = 0, par = 0;
+#pragma unroll 1
+  for (int base = 0; base < nel; base += NT * RE) {
+    uint32_t key[RE];
+    load_keys(base, key);
+    int nt = 0;
+#pragma unroll
+    for (int e = 0; e < RE; ++e) nt += key[e] == prefix;
+    int tt, unused;
+    int tie = ties + x_scan(nt, 0, sh, par, &tt, &unused);
+    uint32_t km = 0;
+    int nk = 0;
+#pragma unroll
+    for (int e = 0; e < RE; ++e) {
+      const bool eq = key[e] == prefix;
+      const bool k = key[e] > prefix || (eq && tie < rem);
+      tie += eq;
+      km |= (uint32_t)k << e;
+      nk += k;
+    }
+    int kt;
+    int off = done + x_scan(nk, 0, sh, par ^ 1, &kt, &unused);
+#pragma unroll
+    for (int e = 0; e < RE; ++e)
+      if ((km >> e) & 1u) out[off++] = base + t0 + e;
+    done += kt;
+    ties += tt;
+  }
+  for (int i = need + threadIdx.x; i < top_k; i += NT) out[i] = i == need ? bq : -1;
+}
+
+// One tile of the bound's source V: wave w holds V [t0 + w 64 VB, + 64 VB), lane l
+// of round q the 4 values at t0 + w 64 VB + 256 q + 4 l (coalesced 16-byte loads).
+template <int NT>
+struct VTile {
+  uint32_t k[VB];                                // keys, 0 = none
+  __device__ __forceinline__ int first(int t0, int q) const {
+    return t0 + (threadIdx.x >> 6) * 64 * VB + 256 * q + 4 * (threadIdx.x & 63);
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rv, int nv, int t0) {
+#pragma unroll
+    for (int q = 0; q < VB / 4; ++q) {
+      const int g = first(t0, q);
+      // V is padded past nv (maxima to whole tiles of 64, scores of 1024): a
+      // started group of 4 stays inside the row
+      const u32x4_t v = g < nv ? ld16_dev(rv, (uint32_t)g * 4u) : u32x4_t{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) k[4 * q + e] = g + e < nv ? float_key(__uint_as_float(v[e])) : 0u;
+    }
+  }
+};
+
+// Appends the tile's entries with keys >= G, in order, to dst [n0, cap) (ids for
+// dst_id: the entry's index; keys for dst_key when given); returns the new count
+// (entries past cap are counted, not stored).  One barrier.
+template <int NT>
+__device__ __forceinline__ int append_ge(const VTile<NT>& vt, int t0, uint32_t G, int n0, int cap, int32_t* dst_id,
+                                         uint32_t* dst_key, Shared<NT>& sh, int p) {
+  int pos[VB / 4], wt = 0;
+#pragma unroll
+  for (int q = 0; q < VB / 4; ++q) {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c += vt.k[4 * q + e] >= G && vt.k[4 * q + e];
+    int t;
+    pos[q] = wt + wave_excl(c, t);
+    wt += t;
+  }
+  int all;
+  const int base = n0 + wave_base(wt, sh, p, all);
+#pragma unroll
+  for (int q = 0; q < VB / 4; ++q) {
+    int at = base + pos[q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (vt.k[4 * q + e] >= G && vt.k[4 * q + e]) {
+        if (at < cap) {
+          dst_id[at] = vt.first(t0, q) + e;
+          if (dst_key) dst_key[at] = vt.k[4 * q + e];
+        }
+        ++at;
+      }
+  }
+  return n0 + all;
+}
+
+// The selection of one row (called by every thread of the workgroup, after a
+// barrier that frees `sh`).  S: the row's scores [0, nel), GM: its group maxima
+// [0, ceil(nel / 16)), both padded (scores to whole tiles of 1024, maxima to
+// whole tiles of 64); out: [top_k].
+template <int NT>
+__device__ __noinline__ void select_row(const float* S, const float* GM, int nel, int bq, int top_k, int32_t* out,
+                                        Shared<NT>& sh) {
+  constexpr int NW = Shared<NT>::NW;
+  const int need = min(top_k, bq + 1) - 1;
+  if (need == 0 || need >= nel) {
+    // the own block alone, or every eligible block (need == nel)
+    for (int i = threadIdx.x; i < top_k; i += NT) out[i] = i < need ? i : (i == need ? bq : -1);
+    return;
+  }
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ng = (nel + GROUP - 1) / GROUP;
+  const bool direct = ng < 2 * need;             // bound from the scores themselves
+  const float* V = direct ? S : GM;              // the values the bound comes from
+  const int nv = direct ? nel : ng;
+  const __amdgpu_buffer_rsrc_t rv = dev_rsrc(V);
+  constexpr int TILE = NT * VB;
+  for (int i = threadIdx.x; i < NBINS; i += NT) sh.hist[i] = 0;   // visible after the next barrier
+
+  // 1. the bound G: a one-tile V is narrowed directly; a longer one by the digits
+  //    of its keys (one pass over V per digit)
+  VTile<NT> vt;
+  uint32_t G = 0;
+  if (nv <= TILE) {
+    vt.load(rv, nv, 0);
+    uint32_t base;
+    uint64_t width;
+    int rem;
+    bool whole;
+    narrow<NT, VB>(vt.k, need, REFINE, sh, base, width, rem, whole);
+    G = base;
+  } else {
+    uint32_t gmask = 0;
+    int rem = need;
+#pragma unroll 1
+    for (int l = 0; l < 3; ++l) {
+#pragma unroll 1
+      for (int t0 = 0; t0 < nv; t0 += TILE) {
+        vt.load(rv, nv, t0);
+#pragma unroll
+        for (int e = 0; e < VB; ++e) {
+          const bool in = vt.k[e] && (vt.k[e] & gmask) == G;
+          hist_add(sh.hist, in ? digit_of(vt.k[e], l) : 0, in);
+        }
+      }
+      __syncthreads();
+      find_bin<NBINS>(sh, rem);
+      rem -= sh.above;
+      G |= (uint32_t)sh.digit << dshift(l);
+      gmask |= dmask(l) << dshift(l);
+      if (sh.count <= REFINE) break;
+    }
+  }
+
+  // 2. the entries of V with keys >= G, in order: the candidates (direct), or the
+  //    candidate groups
+  int nc = 0, par = 0;
+#pragma unroll 1
+  for (int t0 = 0; t0 < nv; t0 += TILE) {
+    if (nv > TILE) vt.load(rv, nv, t0);
+    nc = direct ? append_ge<NT>(vt, t0, G, nc, C_CAP, sh.cid, sh.ckey, sh, par)
+                : append_ge<NT>(vt, t0, G, nc, CG_CAP, sh.cg, nullptr, sh, par);
+    par ^= 1;
+  }
+  __syncthreads();                                // the list complete
+  if (nc > (direct ? C_CAP : CG_CAP)) {
+    radix_row<NT>(S, nel, need, bq, top_k, out, sh);
+    return;
+  }
+  int M = nc;
+  if (!direct) {
+    // 3. the scores with keys >= G of the candidate groups, in order: wave w takes
+    //    groups [w pg, (w+1) pg), lane l of round q group w pg + 64 q + l
+    constexpr int GR = CG_CAP / NT;               // rounds per wave at most
+    const int pg = (nc + NW - 1) / NW;
+    const int g0 = wv * pg, g1 = min(nc, g0 + pg);
+    const __amdgpu_buffer_rsrc_t rs = dev_rsrc(S);
+    uint32_t keep[GR];                            // 16 keep bits per round
+    int gid[GR], pos[GR], wt = 0;
+    u32x4_t v[GR][GROUP / 4];
+#pragma unroll
+    for (int q = 0; q < GR; ++q) {
+      const int i = g0 + 64 * q + lane;
+      gid[q] = i < g1 ? sh.cg[i] : -1;
+#pragma unroll
+      for (int c = 0; c < GROUP / 4; ++c)
+        v[q][c] = gid[q] >= 0 ? ld16_dev(rs, (uint32_t)(gid[q] * GROUP + 4 * c) * 4u) : u32x4_t{};
+    }
+#pragma unroll
+    for (int q = 0; q < GR; ++q) {
+      keep[q] = 0;
+#pragma unroll
+      for (int e = 0; e < GROUP; ++e) {
+        const uint32_t kk = float_key(__uint_as_float(v[q][e >> 2][e & 3]));
+        keep[q] |= (uint32_t)(gid[q] >= 0 && gid[q] * GROUP + e < nel && kk >= G) << e;
+      }
+      int t;
+      pos[q] = wt + wave_excl(__popc(keep[q]), t);
+      wt += t;
+    }
+    const int base = wave_base(wt, sh, par, M);
+#pragma unroll
+    for (int q = 0; q < GR; ++q) {
+      int at = base + pos[q];
+#pragma unroll
+      for (int e = 0; e < GROUP; ++e)
+        if ((keep[q] >> e) & 1u) {
+          if (at < C_CAP) {
+            sh.ckey[at] = float_key(__uint_as_float(v[q][e >> 2][e & 3]));
+            sh.cid[at] = gid[q] * GROUP + e;
+          }
+          ++at;
+        }
+    }
+    __syncthreads();                              // the candidates complete
+    if (M > C_CAP) {
+      radix_row<NT>(S, nel, need, bq, top_k, out, sh);
+      return;
+    }
+  }
+
+  // 4. the exact select among them (M >= need: the entries of V with keys >= G
+  //    are candidates, or maxima of candidate groups, themselves)
+  if (M > need) {
+    keep_best<NT>(M, need, out, sh);
+  } else {
+    for (int i = threadIdx.x; i < need; i += NT) out[i] = sh.cid[i];
+  }
+  for (int i = need + threadIdx.x; i < top_k; i += NT) out[i] = i == need ? bq : -1;
+}
+
+// ---------------------------------------------------------------- per-wave lists
+// A scoring wave of 128 consecutive blocks writes the blocks whose keys reach its
+// own threshold L (its 16th largest key, found bit by bit with ballots): at most
+// LIST entries (key | id << 32) in ascending id, with (count, L') where L' = L, or
+// L + 1 when ties at L did not all fit (the list then holds every key > L).  The
+// union of the lists of a row holds every score whose key is >= the largest L',
+// so it holds the row's winners whenever the need-th largest key of the union is
+// at least every L' -- which the merge checks.
+constexpr int LIST = 16;
+
+// The wave's list from its two keys per lane (key 0 = none): k[0] covers blocks
+// id0[0] (lanes 0..31) then id0[1] (lanes 32..63) ... see the caller; returns the
+// count; the entries go to `dst` [0, count) in the order (segment, lane).
+template <int NSEG>
+__device__ __forceinline__ void wave_list(const uint32_t (&k)[2], const int (&id)[2], uint64_t* dst, uint2* meta) {
+  const int lane = threadIdx.x & 63;
+  int valid = __popcll(__ballot(k[0] != 0)) + __popcll(__ballot(k[1] != 0));
+  uint32_t T = 0;
+  int c = valid;
+  if (valid > LIST) {
+    // the largest T with count(keys >= T) >= LIST; stop once that count is exactly
+    // LIST (the set is then the wave's LIST best)
+#pragma unroll 1
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t trial = T | (1u << b);
+      const int ct = __popcll(__ballot(k[0] >= trial)) + __popcll(__ballot(k[1] >= trial));
+      if (ct >= LIST) {
+        T = trial;
+        c = ct;
+        if (c == LIST) break;
+      }
+    }
+  }
+  // keys > T all fit; ties at T fill up to LIST in id order
+  const int gt = __popcll(__ballot(k[0] > T && k[0])) + __popcll(__ballot(k[1] > T && k[1]));
+  const int room = LIST - gt;
+  // id order: segment 0 = k[0] on lanes 0..31, 1 = k[1] on lanes 0..31,
+  // 2 = k[0] on lanes 32..63, 3 = k[1] on lanes 32..63
+  int n = 0, ties = 0;
+#pragma unroll
+  for (int sgm = 0; sgm < 4; ++sgm) {
+    const bool mine = (lane >> 5) == (sgm >> 1);
+    const uint32_t kk = k[sgm & 1];
+    const bool tie = mine && kk && kk == T && T;
+    const uint64_t mt = __ballot(tie);
+    const int trank = ties + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mt, 0u));
+    const bool keep = mine && kk && (kk > T || (kk == T && (T == 0 || trank < room)));
+    const uint64_t mk = __ballot(keep);
+    const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+    if (keep && pos < LIST) st_agent(dst + pos, (uint64_t)kk | ((uint64_t)(uint32_t)id[sgm & 1] << 32));
+    n += __popcll(mk);
+    ties += __popcll(mt);
+  }
+  // L' = T, or T + 1 when some ties at T were left out
+  const uint32_t Lp = (T && ties > room) ? T + 1 : T;
+  if (lane == 0) st_agent((uint64_t*)meta, (uint64_t)(uint32_t)min(n, LIST) | ((uint64_t)Lp << 32));
+}
+
+// The last workgroup of a row merges its n_lists wave lists (n_lists * LIST <=
+// C_CAP, n_lists <= NT): returns false (nothing written) when a list's L' exceeds
+// the need-th largest key of the union, or the union holds too few entries.  The
+// entries go straight from memory into the registers of keep_best_regs' layout.
+// Called after a barrier that frees `sh` (whose contents are arbitrary).
+template <int NT>
+__device__ __noinline__ bool merge_lists(const uint64_t* lists, const uint2* meta, int n_lists, int need, int bq,
+                                         int top_k, int32_t* out, Shared<NT>& sh) {
+  constexpr int NW = Shared<NT>::NW, E = C_CAP / NT;
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+  const int M = n_lists * LIST;
+  const int per = (M + NW - 1) / NW;
+  const int lo = wv * per, hi = min(M, lo + per);
+  const __amdgpu_buffer_rsrc_t rl = dev_rsrc(lists), rm = dev_rsrc(meta);
+  uint32_t key[E];
+  int32_t cid[E];
+  uint32_t cnt = 0, kmn = 0xFFFFFFFFu, kmx = 0u, lmax = 0u;
+  {
+    u32x2_t ev[E], mv[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int at = lo + 64 * i + lane;
+      ev[i] = at < hi ? __builtin_amdgcn_raw_buffer_load_b64(rl, (uint32_t)at * 8u, 0, 16 /* sc1 */) : u32x2_t{};
+      mv[i] = at < hi ? __builtin_amdgcn_raw_buffer_load_b64(rm, (uint32_t)(at / LIST) * 8u, 0, 16) : u32x2_t{};
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int at = lo + 64 * i + lane;
+      const bool on = at < hi && (at % LIST) < (int)mv[i][0];
+      key[i] = on ? ev[i][0] : 0u;
+      cid[i] = (int32_t)ev[i][1];
+      cnt += on;
+      if (on) { kmn = min(kmn, key[i]); kmx = max(kmx, key[i]); }
+      if (at < hi) lmax = max(lmax, mv[i][1]);
+    }
+  }
+  for (int i = t; i < NBINS; i += NT) sh.hist[i] = 0;   // visible after the next barrier
+  // one exchange: entries, the largest L', and the keys' range
+  const int tot = wave_sum((int)cnt);
+  lmax = wave_umax(lmax);
+  const uint32_t mn = wave_umin(kmn), mx = wave_umax(kmx);
+  if (lane == 0) {
+    sh.xi[1][wv] = tot;
+    sh.xj[1][wv] = (int)lmax;
+    sh.wn[0][wv] = (int)mn;
+    sh.wn[1][wv] = (int)mx;
+  }
+  __syncthreads();
+  int total = 0;
+  uint32_t limit = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    total += sh.xi[1][i];
+    limit = max(limit, (uint32_t)sh.xj[1][i]);
+    kmin = min(kmin, (uint32_t)sh.wn[0][i]);
+    kmax = max(kmax, (uint32_t)sh.wn[1][i]);
+  }
+  if (total <= need) return false;
+  if (!keep_best_regs<NT, E>(key, cid, need, out, sh, limit, kmin, kmax)) return false;
+  for (int i = need + threadIdx.x; i < top_k; i += NT) out[i] = i == need ? bq : -1;
+  return true;
+}
+
+}  // namespace sel
+}  // namespace ip

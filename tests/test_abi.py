@@ -149,7 +149,7 @@ def test_score_topk_rejects_bad_arguments(L):
     assert score(L, s, ws_bytes=need - 1) == L.IP_EWORKSPACE
     assert "workspace" in L.LIB.ip_last_error().decode()
     big = seqs(max_seq_len=1 << 30, seq_stride=1 << 30)
-    assert score(L, big) == L.IP_EUNSUPPORTED            # beyond the top-k merge capacity
+    assert score(L, big) == L.IP_EWORKSPACE              # one row's scores alone take 1 GiB
     f32 = cache(L, dtype=L.IP_F32, row_dim=32, stride=128, scale=None)
     assert score(L, s, q_dtype=L.IP_F32, H=4, D=32, pooled=f32, top_k=64, ws_bytes=0) == L.IP_EWORKSPACE
 
@@ -192,22 +192,26 @@ def test_attention_rejects_bad_arguments(L):
 def test_workspace_sizes_are_consistent(L):
     s = seqs(batch=8, max_seq_len=131072, seq_stride=131072)
     n = L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 0)
-    # scores for 8 rows; 32767 eligible blocks -> 4 top-k chunks of 8192 with
-    # 511 candidates (key + id) each, and one chunk counter per row
+    # per row: one counter (the block padded to 256 bytes), the maxima of groups of
+    # 16 scores, the 16-entry candidate lists (8 bytes each) and their (count,
+    # threshold) of the 256 waves of 128 blocks, and the scores, each row padded to
+    # whole scoring tiles of 1024
     ld = L.LIB.index_scores_ld(131072)
     assert ld == 32768
-    assert n == 8 * ld * 4 + 8 * 4 * 511 * 8 + 8 * 4
-    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 1) == 8 * 4 * 511 * 8 + 8 * 4
-    # a row of up to 48 x 512 blocks is one chunk: 73728 tokens -> 18431 blocks -> 18432
+    lists = 8 * 256 * (16 * 8 + 8)
+    assert n == 256 + 8 * (ld // 16) * 4 + lists + 8 * ld * 4
+    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 1) == 256 + 8 * (ld // 16) * 4 + lists
+    # 73728 tokens -> 18431 eligible blocks -> 18 tiles of 1024; a prefill chunk of
+    # 8192 rows keeps no lists
     assert L.LIB.index_scores_ld(73728) == 18432
     s2 = seqs(batch=1, max_seq_len=73728, seq_stride=73728)
-    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s2), 8192, 512, 1) == 0
-    # 1M tokens: 262143 blocks -> 16 chunks
+    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s2), 8192, 512, 1) == 8192 * 4 + 8192 * 1152 * 4
+    # 1M tokens: 262143 blocks -> 256 tiles, 2048 waves: too many for lists
     s1 = seqs(batch=1, max_seq_len=1 << 20, seq_stride=1 << 20)
     ld1 = L.LIB.index_scores_ld(1 << 20)
     assert ld1 == 262144
-    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s1), 1, 512, 0) == ld1 * 4 + 16 * 511 * 8 + 4
-    # rows are padded to whole chunks: 1025 blocks -> chunk 2048
+    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s1), 1, 512, 0) == 256 + 16384 * 4 + ld1 * 4
+    # 1025 blocks -> 2 tiles
     assert L.LIB.index_scores_ld(4 * 1026) == 2048
     assert L.LIB.sparse_attn_workspace_bytes(8192, 64, 512, 512, L.IP_BF16) == 0      # prefill: no split
     assert L.LIB.sparse_attn_workspace_bytes(1, 16, 64, 64, L.IP_F32) == 0

@@ -212,6 +212,52 @@ def test_zero_queries_tie_to_lowest_ids():
         assert sel[r].tolist() == list(range(63)) + [b_q]
 
 
+@pytest.mark.parametrize("nblk,period,k", [(9000, 50, 512), (40000, 50, 512), (40000, 701, 512),
+                                            (30000, 3, 2048), (9000, 7, 64), (32500, 50, 512), (32500, 3, 512)])
+def test_selection_with_repeated_scores(nblk, period, k):
+    """Block j of every sequence takes the pooled key of its block j % period, so
+    each distinct score repeats exactly (bit-identical on both sides).  This drives
+    the selection through crowded boundary buckets, group maxima shared by many
+    groups, the scores-as-bound path for short rows (9000 blocks, k 512) and the
+    whole-row radix path (period 3 with k 2048 overflows the candidate store).
+    Ties go to the lowest ids, so the ids must equal the oracle's exactly."""
+    D = _dev()
+    w = scaled_down(DECODE, 4 * nblk + 4, batch=2, top_k=k)
+    log(f"[case] repeated scores: {nblk} blocks, period {period}, k {k}")
+    inp = make_inputs(w, with_attention=False)
+    d = D.upload(inp)
+    pooled, sigma, *_ = _oracle_pooled(inp)
+    for b in range(w.batch):
+        nb = int(inp.seq_lens[b]) // 4
+        dst = O.pooled_rows(inp, b, np.arange(nb))
+        src = O.pooled_rows(inp, b, np.arange(nb) % period)
+        pooled[dst] = pooled[src]
+        sigma[dst] = sigma[src]
+    vals = install_oracle_pooled(d, (pooled, sigma))
+    ws = D.Workspaces(d, keep_scores=True)
+    o_ids, gsel, _ = check_score_select(d, inp, vals, np.arange(w.n_rows), ws)
+    assert np.array_equal(gsel, o_ids)
+
+
+def test_selection_with_winners_in_few_waves():
+    """A decode row long enough for per-wave candidate lists (32500 blocks, k 512),
+    with the pooled scale of 300 consecutive blocks raised 16x: those blocks win and
+    sit in three 128-block waves, more than a wave's list holds, so the merge of
+    the lists must detect it and select from all scores instead."""
+    D = _dev()
+    w = scaled_down(DECODE, 4 * 32500 + 4, batch=2, top_k=512)
+    inp = make_inputs(w, with_attention=False)
+    d = D.upload(inp)
+    pooled, sigma, *_ = _oracle_pooled(inp)
+    for b in range(w.batch):
+        rows = O.pooled_rows(inp, b, np.arange(9000, 9300))
+        sigma[rows] *= 16.0
+    vals = install_oracle_pooled(d, (pooled, sigma))
+    ws = D.Workspaces(d, keep_scores=True)
+    o_ids, gsel, _ = check_score_select(d, inp, vals, np.arange(w.n_rows), ws)
+    assert np.array_equal(gsel, o_ids)
+
+
 def test_codec_roundtrip_through_compress():
     """A one-hot pooling logit copies a token row; with scale 1 and a 448 entry the
     requantised codes must equal the source codes: every finite e4m3fn code goes
