@@ -154,7 +154,9 @@ class Workspaces:
             ld = _lib.index_scores_ld(d.seqs.max_seq_len)
             self.scores = torch.zeros((d.n_q, ld), dtype=torch.float32, device=dev)
         nb = _lib.index_score_topk_workspace_bytes(d.seqs, d.n_q, d.top_k, keep_scores)
-        self.ws_idx = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        # zero-filled once: the fused selection's per-row counters start at zero and
+        # every call leaves them there
+        self.ws_idx = torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev)
         qdt = _lib.IP_BF16 if d.q.dtype == torch.bfloat16 else _lib.IP_F32
         na = _lib.sparse_attn_workspace_bytes(d.n_q, d.q.shape[1], d.dv, d.top_k, qdt)
         self.ws_attn = torch.empty(max(na, 16), dtype=torch.uint8, device=dev)
