@@ -123,6 +123,7 @@ __global__ __launch_bounds__(NWV * 64) void score_fp8_bf16_kernel(ScoreArgs a) {
   bf16x8_t kf[TILES][8];
   float ksig[TILES];
   float scv[TILES];                             // this lane's scores of the last row (all tiles)
+  float gmv[TILES];                             // and their group maxima
   int cur_b = -1;
 
   for (int r = rbeg, i = 0; r < rend; ++r, ++i) {
@@ -199,13 +200,12 @@ __global__ __launch_bounds__(NWV * 64) void score_fp8_bf16_kernel(ScoreArgs a) {
       // the maximum of each group of 16 consecutive blocks: lanes kl 0..15 and
       // 16..31 of the tile are 16-lane rows
       const float gmax = row16_max(sc);
-      if (hh == 0 && j < nel) {
-        if constexpr (FUSE) sel::st_agent(srow + j, sc);
-        else srow[j] = sc;
-        if ((kl & 15) == 0) {
-          if constexpr (FUSE) sel::st_agent(grow + (j >> 4), gmax);
-          else grow[j >> 4] = gmax;
-        }
+      gmv[t] = gmax;
+      // fused: stored after the wave's list (see below), so that building the list
+      // does not wait for these stores
+      if (!FUSE && hh == 0 && j < nel) {
+        srow[j] = sc;
+        if ((kl & 15) == 0) grow[j >> 4] = gmax;
       }
     }
   }
@@ -217,8 +217,43 @@ __global__ __launch_bounds__(NWV * 64) void score_fp8_bf16_kernel(ScoreArgs a) {
     const int need = min(a.top_k, nel + 1) - 1;
     int32_t* out = a.out + (int64_t)r * a.top_k;
     sel::Shared<NTW>& ss = *reinterpret_cast<sel::Shared<NTW>*>(smem);
-    if (need == 0 || need >= nel) {
-      // nothing to rank: the own block alone, or every eligible block
+    const bool trivial = need == 0 || need >= nel;   // nothing to rank: the own block alone, or every block
+    const int n_run = (nel + KEYS - 1) / KEYS;
+    const int n_lists = n_run * NWV;
+    // rows long enough for about 2 winners per wave: every wave lists its best
+    // (see sel::wave_list) and the last workgroup merges the lists
+    const bool lists = !trivial && a.lists && n_lists * sel::LIST <= sel::C_CAP && n_lists <= NTW &&
+                       need <= 2 * n_lists;
+    uint64_t* lrow = lists ? a.lists + (int64_t)(r - a.row0) * a.max_lists * sel::LIST : nullptr;
+    uint2* mrow = lists ? a.lists_meta + (int64_t)(r - a.row0) * a.max_lists : nullptr;
+    if (kc0 < nel) {
+      const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hh = lane >> 5, kl = lane & 31;
+      if (lists) {
+        uint32_t k[2];
+        int id[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int t = 2 * hh + i;
+          id[i] = kc0 + (wv * TILES + t) * 32 + kl;
+          k[i] = id[i] < nel ? float_key(scv[t]) : 0u;
+        }
+        const int slot = blockIdx.x * NWV + wv;
+        sel::wave_list<4>(k, id, lrow + (int64_t)slot * sel::LIST, mrow + slot);
+      }
+      // the scores and group maxima (read by the exact fallback, and the caller's
+      // score output), after the list so that building it does not wait for them
+      float* srow = a.scores + (int64_t)(r - a.row0) * a.ld;
+      float* grow = a.gm + (int64_t)(r - a.row0) * a.gld;
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        const int j = kc0 + (wv * TILES + t) * 32 + kl;
+        if (hh == 0 && j < nel) {
+          sel::st_agent(srow + j, scv[t]);
+          if ((kl & 15) == 0) sel::st_agent(grow + (j >> 4), gmv[t]);
+        }
+      }
+    }
+    if (trivial) {
       if (blockIdx.x == 0) {
         __syncthreads();
         sel::select_row<NTW>(nullptr, nullptr, nel, nel, a.top_k, out, ss);
@@ -226,26 +261,6 @@ __global__ __launch_bounds__(NWV * 64) void score_fp8_bf16_kernel(ScoreArgs a) {
       return;
     }
     if (kc0 >= nel) return;                      // this workgroup scored nothing
-    const int n_run = (nel + KEYS - 1) / KEYS;
-    const int n_lists = n_run * NWV;
-    // rows long enough for about 2 winners per wave: every wave lists its best
-    // (see sel::wave_list) and the last workgroup merges the lists
-    const bool lists = a.lists && n_lists * sel::LIST <= sel::C_CAP && n_lists <= NTW && need <= 2 * n_lists;
-    uint64_t* lrow = lists ? a.lists + (int64_t)(r - a.row0) * a.max_lists * sel::LIST : nullptr;
-    uint2* mrow = lists ? a.lists_meta + (int64_t)(r - a.row0) * a.max_lists : nullptr;
-    if (lists) {
-      const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hh = lane >> 5, kl = lane & 31;
-      uint32_t k[2];
-      int id[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int t = 2 * hh + i;
-        id[i] = kc0 + (wv * TILES + t) * 32 + kl;
-        k[i] = id[i] < nel ? float_key(scv[t]) : 0u;
-      }
-      const int slot = blockIdx.x * NWV + wv;
-      sel::wave_list<4>(k, id, lrow + (int64_t)slot * sel::LIST, mrow + slot);
-    }
     // every score, maximum and list entry of this workgroup is stored (acknowledged
     // by memory) before it counts itself in: the stores are device-coherent, so the
     // workgroup that completes the count reads them with device-coherent loads

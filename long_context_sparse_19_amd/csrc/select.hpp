@@ -621,19 +621,31 @@ __device__ __forceinline__ void wave_list(const uint32_t (&k)[2], const int (&id
   const int lane = threadIdx.x & 63;
   int valid = __popcll(__ballot(k[0] != 0)) + __popcll(__ballot(k[1] != 0));
   uint32_t T = 0;
-  int c = valid;
   if (valid > LIST) {
-    // the largest T with count(keys >= T) >= LIST; stop once that count is exactly
-    // LIST (the set is then the wave's LIST best)
+    // the largest T with count(keys >= T) >= LIST.  T lies between the wave's
+    // smallest and largest keys, so it shares the bits above their highest
+    // differing bit; the bits below are found two at a time (three trial counts per
+    // step, independent of each other).  Stop once the count is exactly LIST (the
+    // set is then the wave's LIST best).
+    const uint32_t kmx = wave_umax(max(k[0], k[1]));
+    const uint32_t kmn = wave_umin(min(k[0] ? k[0] : 0xFFFFFFFFu, k[1] ? k[1] : 0xFFFFFFFFu));
+    const uint32_t diff = kmx ^ kmn;
+    int b = diff ? 31 - __clz((int)diff) : -1;    // highest differing bit
+    T = diff ? kmx & ~((2u << b) - 1u) : kmx;      // the shared prefix (b == 31: none)
+    if (b == 31) T = 0;
 #pragma unroll 1
-    for (int b = 31; b >= 0; --b) {
-      const uint32_t trial = T | (1u << b);
-      const int ct = __popcll(__ballot(k[0] >= trial)) + __popcll(__ballot(k[1] >= trial));
-      if (ct >= LIST) {
-        T = trial;
-        c = ct;
-        if (c == LIST) break;
-      }
+    for (; b >= 1; b -= 2) {
+      const uint32_t t1 = T | (1u << (b - 1)), t2 = T | (2u << (b - 1)), t3 = T | (3u << (b - 1));
+      const int c1 = __popcll(__ballot(k[0] >= t1)) + __popcll(__ballot(k[1] >= t1));
+      const int c2 = __popcll(__ballot(k[0] >= t2)) + __popcll(__ballot(k[1] >= t2));
+      const int c3 = __popcll(__ballot(k[0] >= t3)) + __popcll(__ballot(k[1] >= t3));
+      const int c = c3 >= LIST ? c3 : (c2 >= LIST ? c2 : c1);
+      T = c3 >= LIST ? t3 : (c2 >= LIST ? t2 : (c1 >= LIST ? t1 : T));
+      if (c == LIST) { b = -1; break; }
+    }
+    if (b == 0) {
+      const uint32_t t1 = T | 1u;
+      if (__popcll(__ballot(k[0] >= t1)) + __popcll(__ballot(k[1] >= t1)) >= LIST) T = t1;
     }
   }
   // keys > T all fit; ties at T fill up to LIST in id order
