@@ -188,6 +188,26 @@ ip_status index_score_topk(const ip_seqs* seqs, int32_t n_q, const int32_t* q_se
                            float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * index_score_topk_noalloc -- index_score_topk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments and results, without `ws` /
+ * `ws_bytes`.  The workspace is a static array inside the library, one per GPU,
+ * of index_score_topk_noalloc_max_bytes() bytes (8 MiB), held until the process
+ * ends; calls whose index_score_topk_workspace_bytes(seqs, n_q, top_k, scores !=
+ * NULL) exceeds it return IP_EWORKSPACE.  The call allocates and frees nothing.
+ * The first call on a GPU looks up the array's device address and clears it with
+ * a kernel on `stream`.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (different streams, or different host threads)
+ * race and must not be issued.
+ * ------------------------------------------------------------------------------- */
+size_t index_score_topk_noalloc_max_bytes(void);
+ip_status index_score_topk_noalloc(const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
+                                   const int32_t* q_pos, const void* q_idx, int32_t q_dtype,
+                                   int32_t n_heads, int32_t head_dim, const float* gates,
+                                   const ip_cache* pooled, int32_t top_k, int32_t* out_idx,
+                                   float* scores, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * indexpool_decode_index -- one decode step's cache growth and indexer together:
  * exactly indexpool_append(...) followed by index_score_topk(...) for the decode
  * rows (row r = sequence r at p = seq_lens[r] - 1, n_q = batch; q_seq, q_pos NULL),

@@ -60,6 +60,10 @@ def _load() -> ctypes.CDLL:
     lib.index_score_topk.argtypes = [P(IpSeqs), _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                      _c_void_p, P(IpCache), _i32, _c_void_p, _c_void_p, _c_void_p, _size,
                                      _c_void_p]
+    lib.index_score_topk_noalloc.argtypes = [P(IpSeqs), _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                             _c_void_p, P(IpCache), _i32, _c_void_p, _c_void_p, _c_void_p]
+    lib.index_score_topk_noalloc_max_bytes.argtypes = []
+    lib.index_score_topk_noalloc_max_bytes.restype = _size
     lib.sparse_attn_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
     lib.sparse_attn_workspace_bytes.restype = _size
     lib.sparse_attn_decode.argtypes = [P(IpSeqs), _c_void_p, _i32, _i32, _i32, _i32, ctypes.c_float,
@@ -85,6 +89,7 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 EXPORTED = ("indexpool_compress", "indexpool_append", "indexpool_decode_index", "index_scores_ld", "index_score_topk_workspace_bytes", "index_score_topk",
+            "index_score_topk_noalloc", "index_score_topk_noalloc_max_bytes",
             "sparse_attn_workspace_bytes", "sparse_attn_decode", "sparse_attn_prefill", "kda_decode_step", "ip_last_error",
             "ip_time_next_launch", "ip_version")
 
@@ -179,6 +184,21 @@ def index_score_topk(seqs: Seqs, q_idx: torch.Tensor, gates: torch.Tensor, poole
         ctypes.byref(s), n_q, _ptr(q_seq), _ptr(q_pos), q_idx.data_ptr(), _DT[q_idx.dtype], H, D,
         gates.data_ptr(), ctypes.byref(p), top_k, out_idx.data_ptr(), _ptr(scores), _ptr(ws), ws_bytes,
         _stream(stream)))
+
+
+def index_score_topk_noalloc(seqs: Seqs, q_idx: torch.Tensor, gates: torch.Tensor, pooled: Cache, top_k: int,
+                             out_idx: torch.Tensor, q_seq: Optional[torch.Tensor] = None,
+                             q_pos: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                             stream=None) -> None:
+    s, p = seqs.c(), pooled.c()
+    n_q, H, D = q_idx.shape
+    _check("index_score_topk_noalloc", LIB.index_score_topk_noalloc(
+        ctypes.byref(s), n_q, _ptr(q_seq), _ptr(q_pos), q_idx.data_ptr(), _DT[q_idx.dtype], H, D,
+        gates.data_ptr(), ctypes.byref(p), top_k, out_idx.data_ptr(), _ptr(scores), _stream(stream)))
+
+
+def index_score_topk_noalloc_max_bytes() -> int:
+    return int(LIB.index_score_topk_noalloc_max_bytes())
 
 
 def sparse_attn_workspace_bytes(n_q: int, n_heads: int, dv: int, top_k: int, q_dtype: int) -> int:

@@ -2,6 +2,7 @@
 // Every check that the host can make happens before anything is enqueued.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/indexpool.h"
@@ -559,6 +560,75 @@ ip_status kda_decode_step(int32_t batch, int32_t n_heads, int32_t head_dim, cons
   a.state = state;
   a.out = out;
   return device_status(ip::launch_kda_decode(a, stream), fn);
+}
+
+// ------------------------------------------------------------------ no-allocation indexer
+}  // extern "C"
+
+namespace {
+
+// Workspace of index_score_topk_noalloc: one copy per GPU the library runs on,
+// held until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is a stand-in, not a device address): it uses the address
+// hipGetSymbolAddress returned for the device, kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];         // per device: the array's device address, or null
+
+__global__ void zero_words(uint4* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// The current device's scratch address; on the first call for a device, the
+// symbol address is looked up (with that device current) and the array is
+// cleared on `stream` by a fill kernel (the per-row counters must start at zero;
+// every call leaves them at zero again).
+ip_status scratch_for_current_device(const char* fn, hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(IP_EDEVICE, "%s: no usable current device (%s)", fn, hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(IP_EDEVICE, "%s: hipGetSymbolAddress(scratch) failed: %s", fn, hipGetErrorString(e));
+    hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, stream, (uint4*)ptr, kScratchBytes / 16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(IP_EDEVICE, "%s: clearing the scratch failed: %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return IP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t index_score_topk_noalloc_max_bytes(void) { return kScratchBytes; }
+
+ip_status index_score_topk_noalloc(const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
+                                   const int32_t* q_pos, const void* q_idx, int32_t q_dtype,
+                                   int32_t n_heads, int32_t head_dim, const float* gates,
+                                   const ip_cache* pooled, int32_t top_k, int32_t* out_idx,
+                                   float* scores, hipStream_t stream) {
+  const char* fn = "index_score_topk_noalloc";
+  if (ip_status st = check_seqs(seqs, fn)) return st;
+  if (n_q < 1 || top_k < 1) return fail(IP_EINVAL, "%s: n_q and top_k must be >= 1", fn);
+  const size_t need = score_plan(seqs, n_q, scores != nullptr).total;
+  if (need > kScratchBytes)
+    return fail(IP_EWORKSPACE, "%s: this call needs %zu bytes of workspace, above the built-in %zu; call "
+                "index_score_topk with a workspace instead", fn, need, kScratchBytes);
+  void* ws = nullptr;
+  if (ip_status st = scratch_for_current_device(fn, stream, &ws)) return st;
+  return score_topk_impl(fn, seqs, n_q, q_seq, q_pos, q_idx, q_dtype, n_heads, head_dim, gates, pooled, top_k,
+                         out_idx, scores, ws, kScratchBytes, stream, nullptr);
 }
 
 }  // extern "C"

@@ -189,6 +189,24 @@ def test_attention_rejects_bad_arguments(L):
                                      None, FAKE, 512, FAKE, None, None, 0, None) == L.IP_EINVAL  # q_pos
 
 
+def test_noalloc_rejects_bad_arguments_and_oversized_calls(L):
+    """index_score_topk_noalloc checks its arguments before it looks up or clears
+    its static workspace (nothing reaches the device here), and refuses calls
+    that need more workspace than the built-in array."""
+    assert L.index_score_topk_noalloc_max_bytes() == 8 << 20
+    s = seqs()
+    p = cache(L)
+
+    def call(seqs_=s, n_q=2, top_k=512):
+        return L.LIB.index_score_topk_noalloc(ctypes.byref(seqs_), n_q, None, None, FAKE, L.IP_BF16, 32, 128,
+                                              FAKE, ctypes.byref(p), top_k, FAKE, None, None)
+    assert call(n_q=0) == L.IP_EINVAL
+    assert call(top_k=0) == L.IP_EINVAL
+    big = seqs(batch=8, max_seq_len=1 << 21, seq_stride=1 << 21)     # 8 rows x 2 MiB of scores
+    assert call(seqs_=big, n_q=8) == L.IP_EWORKSPACE
+    assert "workspace" in L.LIB.ip_last_error().decode()
+
+
 def test_workspace_sizes_are_consistent(L):
     s = seqs(batch=8, max_seq_len=131072, seq_stride=131072)
     n = L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 0)
