@@ -270,6 +270,16 @@ def score(q_idx, gates, keys) -> np.ndarray:
     return np.maximum(dots, 0.0) @ np.asarray(gates, dtype=F64)
 
 
+def score_many(q_idx, gates, keys) -> np.ndarray:
+    """R4 for several query rows over one key set: S[r, j] = sum_h g[r, h] *
+    relu(q[r, h] . K_j).  q_idx [R, H, D], gates [R, H], keys [n, D] -> [R, n]."""
+    q = np.asarray(q_idx, dtype=F64)
+    R, H, D = q.shape
+    dots = np.asarray(keys, dtype=F64) @ q.reshape(R * H, D).T            # [n, R*H]
+    dots = np.maximum(dots, 0.0).reshape(-1, R, H)
+    return np.einsum("nrh,rh->rn", dots, np.asarray(gates, dtype=F64))
+
+
 def select(S, b_q: int, k: int) -> np.ndarray:
     """R5: own block plus the best k'-1 blocks j < b_q; ascending; -1 padded to k."""
     S = np.asarray(S, dtype=F64)[:b_q]

@@ -420,11 +420,64 @@ def test_full_size_decode(w):
     full_case(w, keep_scores=False)
 
 
-def test_full_size_prefill_sampled():
-    rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(PREFILL.n_query, 24, replace=False))
-    rows = np.unique(np.concatenate([[0, PREFILL.n_query - 1], rows]))
-    full_case(PREFILL, rows=rows, keep_scores=False)
+def _prefill_selection_all_rows(inp, vals, gsel, top_k, chunk=128):
+    """The oracle's selection for every prefill row (one sequence: the rows share
+    its key prefix, so scores come from score_many over row chunks), checked row by
+    row against the device's; returns the oracle's ids."""
+    b = int(inp.q_seq[0])
+    assert (inp.q_seq == b).all()
+    keys = vals[O.pooled_rows(inp, b, np.arange(int(inp.q_pos.max()) // 4))]
+    o_ids = np.empty_like(gsel)
+    swaps = 0
+    for r0 in range(0, len(inp.q_pos), chunk):
+        rr = np.arange(r0, min(len(inp.q_pos), r0 + chunk))
+        n = int(inp.q_pos[rr].max()) // 4
+        S = O.score_many(O._to_f64(inp.q_idx[rr]), inp.gates[rr], keys[:n])
+        for n, r in enumerate(rr):
+            b_q = int(inp.q_pos[r]) // 4
+            o_ids[r] = O.select(S[n, :b_q], b_q, top_k)
+            swaps += P.check_selection(gsel[r], o_ids[r], S[n, :b_q], b_q, top_k)
+    return o_ids, swaps
+
+
+def _prefill_attention_rows(n_query):
+    """16 whole 32-row scoring groups spread over the chunk (512 rows: every
+    position mod 4, the first and the last row)."""
+    groups = np.linspace(0, n_query // 32 - 1, 16).round().astype(int)
+    return np.concatenate([np.arange(32 * g, 32 * g + 32) for g in groups])
+
+
+@pytest.mark.parametrize("fp8kv", [False, True], ids=["bf16kv", "fp8kv"])
+def test_full_size_prefill(fp8kv):
+    """The chunked-prefill workload at full size (8192 query rows over 73728
+    tokens, top-512): pooling of every block, the selection of all 8192 rows
+    against the oracle, attention on 512 rows (16 whole scoring groups); with
+    fp8kv the attention reads the fp8 latent tier."""
+    D = _dev()
+    w = PREFILL.with_(latent_fp8=fp8kv)
+    log(f"[case] full-size prefill fp8kv={fp8kv}: {w.n_query} rows over {w.seq_len} tokens, k={w.top_k}")
+    inp = make_inputs(w)
+    d = D.upload(inp)
+    opooled = _oracle_pooled(inp)
+    flips = check_compress(d, inp, opooled)
+    vals = install_oracle_pooled(d, opooled)
+    ws = D.Workspaces(d, keep_scores=True)
+    D.score_topk(d, ws)
+    torch.cuda.synchronize()
+    gsel = ws.sel.cpu().numpy()
+    o_ids, swaps = _prefill_selection_all_rows(inp, vals, gsel, w.top_k)
+    log(f"  compress ok (tie flips {flips}); selection of all {w.n_query} rows ok (tie-band swaps {swaps})")
+    # scores on a sample of rows (the selection above used the oracle's)
+    gscores = ws.scores
+    for r in (0, 1, 2, 3, 4095, w.n_query - 1):
+        b_q = int(inp.q_pos[r]) // 4
+        keys = vals[O.pooled_rows(inp, int(inp.q_seq[r]), np.arange(b_q))]
+        qi = O._to_f64(inp.q_idx[r])
+        P.check_scores(gscores[r, :b_q].cpu().numpy(), O.score(qi, inp.gates[r], keys), qi,
+                       inp.gates[r].astype(np.float64), keys)
+    rows = _prefill_attention_rows(w.n_query)
+    err = check_attention(d, inp, o_ids[rows], rows, ws, base_sel=gsel)
+    log(f"  attention on {len(rows)} rows ok (max-abs {err:.2e})")
 
 
 # ---------------------------------------------------------------- IndexCache

@@ -154,6 +154,24 @@ def test_score_select_worked_example():
     assert O.select(S, b_q, 8).tolist() == g["select_k8"]
 
 
+def test_score_many_is_score_per_row_and_the_closed_form():
+    """score_many (several rows at once) equals the per-row score on random rows,
+    and the unit-query closed form row by row."""
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((5, 3, 16))
+    g = rng.standard_normal((5, 3))
+    keys = rng.standard_normal((40, 16))
+    S = O.score_many(q, g, keys)
+    for r in range(5):
+        np.testing.assert_allclose(S[r], O.score(q[r], g[r], keys), rtol=1e-13, atol=1e-13)
+    unit = np.zeros((2, 1, 16))
+    unit[0, 0, 4] = 1.0
+    unit[1, 0, 11] = 1.0
+    S = O.score_many(unit, np.ones((2, 1)), keys)
+    assert np.array_equal(S[0], np.maximum(keys[:, 4], 0.0))
+    assert np.array_equal(S[1], np.maximum(keys[:, 11], 0.0))
+
+
 def test_score_unit_query_is_relu_of_one_coordinate():
     rng = np.random.default_rng(5)
     keys = rng.standard_normal((100, 24))
