@@ -102,12 +102,15 @@ def algorithmic_bytes(inp, w):
                 follower=int(fol_b), U=U)
 
 
-def kernel_bytes(inp, w, ab, fused):
+def kernel_bytes(inp, w, ab, fused, step=False):
     """Algorithmic bytes per kernel (the same units as the step total; split
     partials and the score workspace are not counted).  fused: the scoring launch
-    also selects (and, for decode, appends)."""
+    also selects (and, for decode, appends); step: one launch does all of that and
+    the attention (then only the split combine follows)."""
     n = len(inp.q_pos)
     sel_b = ab["select"]
+    if step:
+        return {"step": ab["score"] + ab["pool"] + sel_b + ab["attention"], "combine": 0}
     if w.mode == "decode":
         out = {"score": ab["score"] + ab["pool"] + (sel_b if fused else 0), "attention": ab["attention"]}
     else:
@@ -122,6 +125,20 @@ def kernel_bytes(inp, w, ab, fused):
     return out
 
 
+def step_fused(w):
+    """Whether indexpool_decode_step runs as one launch (plus the split combine) for
+    this workload: decode over fp8 indexer keys and a bf16 latent cache, with the
+    attention split (the plan of sparse_attn_workspace_bytes) into splits of fewer
+    than 128 blocks."""
+    if not (w.mode == "decode" and w.idx_key_dtype == "fp8" and w.attn_dtype == "bf16" and not w.latent_fp8):
+        return False
+    n, k = w.batch, w.top_k
+    nsub = (k + 15) // 16
+    ns = max(1, min((128 + n - 1) // n, nsub, 64))
+    bps = min((nsub + ns - 1) // ns, 32) * 16
+    return (k + bps - 1) // bps > 1 and bps < 128
+
+
 def fuses_select(w):
     """Whether index_score_topk selects inside the scoring launch for this workload
     (fp8 keys and decode-shaped rows: fewer than 64 rows, or no per-row sequence
@@ -131,7 +148,8 @@ def fuses_select(w):
 
 # the sources each kernel is built from (the HBM counters in profiles/ are tied to them)
 _KERNEL_SOURCES = {"attention": ("attn.hip", "attn_pipe.hip", "attn_common.hpp"), "combine": ("attn.hip", "attn_common.hpp"),
-                   "score": ("score.hip", "select.hpp"), "topk": ("select.hip", "select.hpp"), "compress": ("compress.hip",),
+                   "step": ("attn.hip", "attn_common.hpp", "score_fp8.hpp", "select.hpp"),
+                   "score": ("score.hip", "score_fp8.hpp", "select.hpp"), "topk": ("select.hip", "select.hpp"), "compress": ("compress.hip",),
                    "append": ("compress.hip",), "kda": ("kda.hip",)}
 
 
@@ -458,11 +476,11 @@ def run_workload(w, K, warmup, replicas, eager, with_cpu):
     def step(i):
         d, ws = reps[i % R], wss[i % R]
         if w.mode == "decode":
-            D.decode_index(d, toks, ws)          # append + score + top-k
+            D.decode_step(d, toks, ws)           # append + score + top-k + attention
         else:
             D.compress(d, block_begin=begin, max_blocks=max_new)
             D.score_topk(d, ws)
-        D.attention(d, ws)
+            D.attention(d, ws)
         for fd, fws in zip(freps[i % R], fwss[i % R]):
             D.append(fd, toks)
             D.attention(fd, fws)
@@ -483,21 +501,36 @@ def run_workload(w, K, warmup, replicas, eager, with_cpu):
             with torch.cuda.graph(g):
                 step(i)
             graphs.append(g)
+        # and one graph holding a step on every replica in turn, as a serving loop
+        # launches many steps at once
+        gall = None
+        if R > 1:
+            gall = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gall):
+                for i in range(R):
+                    step(i)
         torch.cuda.synchronize()
 
-    def run(i):
-        if graphs is not None:
-            graphs[i % R].replay()
-        else:
-            step(i)
+    def run_steps(i, n):
+        """Steps i .. i+n-1, step j on replica j mod R."""
+        end = i + n
+        while i < end:
+            if graphs is None:
+                step(i % R)
+                i += 1
+            elif gall is not None and i % R == 0 and end - i >= R:
+                gall.replay()
+                i += R
+            else:
+                graphs[i % R].replay()
+                i += 1
 
-    # --- timed region 1: K whole steps -> value
-    for i in range(warmup):
-        run(i)
+    # --- timed region 1: K whole steps -> value (the warm-up ends on the replica
+    # before the first timed one)
+    run_steps(-warmup, warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        run(warmup + i)
+    run_steps(0, K)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt * 1e3 / K
@@ -507,9 +540,9 @@ def run_workload(w, K, warmup, replicas, eager, with_cpu):
     # launch carrying HIP events that receive its dispatch start / end times (the
     # timestamps a kernel trace reports), on the stream the kernel runs on
     fused = fuses_select(w)
-    kbytes = kernel_bytes(inp, w, ab, fused)
+    kbytes = kernel_bytes(inp, w, ab, fused, step=step_fused(w))
     ids = {"compress": _lib.K_COMPRESS, "score": _lib.K_SCORE, "topk": _lib.K_TOPK, "attention": _lib.K_ATTN,
-           "combine": _lib.K_COMBINE}
+           "combine": _lib.K_COMBINE, "step": _lib.K_STEP}
     ids = {n: kid for n, kid in ids.items() if n in kbytes}     # the kernels this workload launches
     evk = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
            for n in ids}
@@ -536,16 +569,20 @@ def run_workload(w, K, warmup, replicas, eager, with_cpu):
     U = ab["U"]
     kernels = {}
     for n, t in kern_ms.items():
-        b = kbytes.get(n)
+        # prefill rows share their keys and latent rows: per-row gathered bytes are
+        # no HBM figure there, its scoring and attention are priced in flops
+        b = None if (w.mode == "prefill" and n in ("score", "attention")) else kbytes.get(n)
         kernels[n] = {"avg_ms": t, "bytes": b, "GBps": (b / (t * 1e-3) / 1e9) if b else None,
                       "hbm_frac": (b / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS) if b else None}
     if "attention" in kernels:
         fl = attention_flops(U, w)
-        kernels["attention"].update(flops=fl, TFLOPs=fl / (kern_ms["attention"] * 1e-3) / 1e12)
+        tf = fl / (kern_ms["attention"] * 1e-3) / 1e12
+        kernels["attention"].update(flops=fl, TFLOPs=tf, mfma_frac=tf / BF16_PEAK_TFLOPS)
     if w.mode == "prefill" and "score" in kernels:
         ifl = indexer_flops(inp, w)
-        kernels["score"].update(flops=ifl, TFLOPs=ifl / (kern_ms["score"] * 1e-3) / 1e12)
-    path = [n for n in ("score", "topk", "attention", "combine") if n in kern_ms]
+        tf = ifl / (kern_ms["score"] * 1e-3) / 1e12
+        kernels["score"].update(flops=ifl, TFLOPs=tf, mfma_frac=tf / BF16_PEAK_TFLOPS)
+    path = [n for n in ("step", "score", "topk", "attention", "combine") if n in kern_ms]
     path_ms = sum(kern_ms[n] for n in path)
     if w.mode == "prefill":
         ach = kernels["attention"]["TFLOPs"]
@@ -560,8 +597,12 @@ def run_workload(w, K, warmup, replicas, eager, with_cpu):
 
     cpu = cpu_baseline(inp, w, followers=followers) if with_cpu else None
     summary = {"workload": w.name, "ms_per_step": ms, "value": value, "unit": "query-tokens/s",
-               "algorithmic_bytes_per_step": step_bytes, "kernel_sum_ms": path_ms, "roofline": roof,
-               "kernels": kernels, "steps": K, "replicas": R}
+               "kernel_sum_ms": path_ms, "roofline": roof, "kernels": kernels, "steps": K, "replicas": R}
+    if w.mode == "prefill":
+        summary["attention_flops_per_step"] = attention_flops(U, w)
+        summary["indexer_flops_per_step"] = indexer_flops(inp, w)
+    else:
+        summary["algorithmic_bytes_per_step"] = step_bytes
     line = {
         "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": K,
         "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",

@@ -175,7 +175,10 @@ ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cac
  *  scores   device [n_q, ld] fp32 or NULL, ld = index_scores_ld(max_seq_len); when
  *           given, S_j is written at [r, j] for j < b_q (other entries untouched)
  *           and no score workspace is used
- *  ws       device workspace of ws_bytes >= index_score_topk_workspace_bytes(...)
+ *  ws       device workspace of ws_bytes >= index_score_topk_workspace_bytes(...),
+ *           256-byte aligned, zero-filled before its first use; each call leaves
+ *           its per-row counters at zero again, so a workspace serves any number
+ *           of later calls (one call at a time) without being cleared again
  * Contract: 0 <= p < seq_lens[b]; blocks j < b_q were pooled.
  * ------------------------------------------------------------------------------- */
 int64_t index_scores_ld(int32_t max_seq_len);   /* >= max_seq_len/4, rounded up to whole top-k chunks */
@@ -278,6 +281,39 @@ ip_status sparse_attn_prefill(const ip_seqs* seqs, int32_t n_q, const int32_t* q
                               hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * indexpool_decode_step -- a whole DSA decode step: indexpool_decode_index(...)
+ * (append + indexer + selection) followed by sparse_attn_decode(...) over the
+ * selected ids, in one call with the arguments of both (k = kv, v as given; the
+ * indexer's q_dtype / n_heads / head_dim are idx_dtype / idx_heads / idx_dim).
+ * G2C Brief, "DSA keeps selected global access in eleven layers" (the growing
+ * latent history, the learned selection and the attention over it).
+ *
+ * The results are those of the two calls in order: out_idx (and scores when
+ * given) bit for bit, out and lse to the attention's rounding.  With FP8 indexer
+ * keys and the split BF16 latent attention (decode batches of up to 64 rows) the
+ * step is one launch plus the split combine: each row's attention workgroups
+ * start while rows are still being selected, fetch their query, and wait for the
+ * row's ids (published device-coherently by the workgroup that selects the row);
+ * the query's own new token is read from kv_new.  Other geometries run the two
+ * calls.
+ *  ws  device workspace of ws_bytes >= indexpool_decode_step_workspace_bytes(seqs,
+ *      top_k, n_heads, dv, q_dtype, scores != NULL), 256-byte aligned, zero-filled
+ *      before its first use (the call leaves its counters and ready words at zero).
+ * Errors: those of the two calls.  Calls sharing a workspace must not overlap.
+ * ------------------------------------------------------------------------------- */
+size_t indexpool_decode_step_workspace_bytes(const ip_seqs* seqs, int32_t top_k, int32_t n_heads,
+                                             int32_t dv, int32_t q_dtype, int32_t scores_given);
+ip_status indexpool_decode_step(const ip_seqs* seqs, const void* kv_new, const ip_cache* kv,
+                                const void* v_new, const ip_cache* v, const void* key_new,
+                                int32_t key_dtype, const ip_cache* keys, const float* logit_new,
+                                float* logits, const ip_cache* pooled, const void* q_idx,
+                                int32_t idx_dtype, int32_t idx_heads, int32_t idx_dim,
+                                const float* gates, int32_t top_k, int32_t* out_idx, float* scores,
+                                const void* q, int32_t q_dtype, int32_t n_heads, int32_t dk,
+                                int32_t dv, float scale, void* out, float* lse, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * kda_decode_step -- one decode step of the linear-attention (KDA) half of the
  * hybrid layer.  G2C Brief, section "KDA carries fixed state through most layers":
  * a gated delta-rule recurrence over a fixed matrix state per head, with a short
@@ -314,6 +350,32 @@ ip_status kda_decode_step(int32_t batch, int32_t n_heads, int32_t head_dim, cons
                           const float* beta, const float* conv_w, const float* conv_in,
                           float* conv_out, float* state, float* out, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------
+ * kda_prefill_chunk -- the KDA half over a chunk of n_tokens consecutive tokens of
+ * each sequence (prefill): exactly n_tokens successive kda_decode_step calls (token
+ * t of the chunk as the step's input), computed in the chunked form of the gated
+ * delta rule (blocks of 16 tokens: the block's writes solve a 16 x 16 triangular
+ * system and its outputs and state update are dense products, on fp32 MFMA).  G2C
+ * Brief, section "KDA carries fixed state through most layers".
+ *
+ *  xq, xk, xv  device [batch, n_tokens, n_heads * 128] BF16, 16-byte aligned
+ *  alpha    device [batch, n_tokens, n_heads, 128] fp32 in (0, 1], 16-byte aligned
+ *  beta     device [batch, n_tokens, n_heads] fp32
+ *  conv_w, conv_in, conv_out, state  as for kda_decode_step (conv_in: the taps
+ *           before the chunk, conv_out receives those after it; state is read and
+ *           updated in place)
+ *  out      device [batch, n_tokens, n_heads, 128] fp32
+ * Results agree with the token-by-token recurrence to fp32 rounding (the products
+ * with the decay are taken as exponentials of running sums of log alpha).
+ * n_tokens = 0 copies the taps and leaves the state unchanged.
+ * Errors: as kda_decode_step, plus n_tokens < 0 -> IP_EINVAL.
+ * ------------------------------------------------------------------------------- */
+ip_status kda_prefill_chunk(int32_t batch, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                            const void* xq, const void* xk, const void* xv, int32_t x_dtype,
+                            const float* alpha, const float* beta, const float* conv_w,
+                            const float* conv_in, float* conv_out, float* state, float* out,
+                            hipStream_t stream);
+
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char* ip_last_error(void);
 
@@ -321,7 +383,7 @@ const char* ip_last_error(void);
  * goes through hipExtLaunchKernelGGL with `start` / `stop`, so the two events
  * receive that dispatch's own start and end times (the timestamps a kernel trace
  * reports).  kernel_id: 1 compress, 2 score, 3 top-k, 4 attention, 5 split
- * combine, 6 append, 7 KDA decode step.  Hooks for different ids may be
+ * combine, 6 append, 7 KDA decode step, 8 fused decode step.  Hooks for different ids may be
  * armed together; each is consumed by one launch.  Passing NULL for one event
  * only is IP_EINVAL; kernel_id 0 with both NULL disarms every hook.  Use it
  * outside stream capture.  Not needed for normal use. */

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libindexpool.so")
 
 IP_OK, IP_EINVAL, IP_EUNSUPPORTED, IP_EWORKSPACE, IP_EDEVICE = range(5)
 IP_F32, IP_BF16, IP_FP8_E4M3FN = range(3)
-K_COMPRESS, K_SCORE, K_TOPK, K_ATTN, K_COMBINE, K_APPEND, K_KDA = 1, 2, 3, 4, 5, 6, 7
+K_COMPRESS, K_SCORE, K_TOPK, K_ATTN, K_COMBINE, K_APPEND, K_KDA, K_STEP = 1, 2, 3, 4, 5, 6, 7, 8
 
 _c_void_p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -75,22 +75,33 @@ def _load() -> ctypes.CDLL:
     lib.indexpool_decode_index.argtypes = [P(IpSeqs), _c_void_p, P(IpCache), _c_void_p, P(IpCache), _c_void_p, _i32,
                                            P(IpCache), _c_void_p, _c_void_p, P(IpCache), _c_void_p, _i32, _i32, _i32,
                                            _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]
+    lib.indexpool_decode_step_workspace_bytes.argtypes = [P(IpSeqs), _i32, _i32, _i32, _i32, _i32]
+    lib.indexpool_decode_step_workspace_bytes.restype = _size
+    lib.indexpool_decode_step.argtypes = [P(IpSeqs), _c_void_p, P(IpCache), _c_void_p, P(IpCache), _c_void_p, _i32,
+                                          P(IpCache), _c_void_p, _c_void_p, P(IpCache), _c_void_p, _i32, _i32, _i32,
+                                          _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32,
+                                          ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]
     lib.kda_decode_step.argtypes = [_i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p,
                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]
+    lib.kda_prefill_chunk.argtypes = [_i32, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
+                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]
     lib.ip_last_error.restype = ctypes.c_char_p
     lib.ip_version.restype = ctypes.c_char_p
     lib.ip_time_next_launch.argtypes = [_i32, _c_void_p, _c_void_p]
     for fn in ("indexpool_compress", "indexpool_append", "index_score_topk", "indexpool_decode_index",
-               "sparse_attn_decode", "sparse_attn_prefill", "kda_decode_step", "ip_time_next_launch"):
+               "indexpool_decode_step", "sparse_attn_decode", "sparse_attn_prefill", "kda_decode_step",
+               "kda_prefill_chunk", "ip_time_next_launch"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
 
 LIB = _load()
 
-EXPORTED = ("indexpool_compress", "indexpool_append", "indexpool_decode_index", "index_scores_ld", "index_score_topk_workspace_bytes", "index_score_topk",
+EXPORTED = ("indexpool_compress", "indexpool_append", "indexpool_decode_index", "indexpool_decode_step",
+            "indexpool_decode_step_workspace_bytes", "index_scores_ld", "index_score_topk_workspace_bytes", "index_score_topk",
             "index_score_topk_noalloc", "index_score_topk_noalloc_max_bytes",
-            "sparse_attn_workspace_bytes", "sparse_attn_decode", "sparse_attn_prefill", "kda_decode_step", "ip_last_error",
+            "sparse_attn_workspace_bytes", "sparse_attn_decode", "sparse_attn_prefill", "kda_decode_step",
+            "kda_prefill_chunk", "ip_last_error",
             "ip_time_next_launch", "ip_version")
 
 
@@ -271,3 +282,40 @@ def indexpool_decode_index(seqs: Seqs, kv_new: torch.Tensor, kv: Cache, key_new:
         top_k, out_idx.data_ptr(), _ptr(scores), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
 
+
+
+def indexpool_decode_step_workspace_bytes(seqs: Seqs, top_k: int, n_heads: int, dv: int, q_dtype: int,
+                                          scores_given: bool = False) -> int:
+    return int(LIB.indexpool_decode_step_workspace_bytes(ctypes.byref(seqs.c()), top_k, n_heads, dv, q_dtype,
+                                                         int(scores_given)))
+
+
+def indexpool_decode_step(seqs: Seqs, kv_new: torch.Tensor, kv: Cache, key_new: torch.Tensor, keys: Cache,
+                          logit_new: torch.Tensor, logits: torch.Tensor, pooled: Cache, q_idx: torch.Tensor,
+                          gates: torch.Tensor, top_k: int, out_idx: torch.Tensor, q: torch.Tensor, out: torch.Tensor,
+                          scale: float, dv: int, lse: Optional[torch.Tensor] = None,
+                          scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                          v_new: Optional[torch.Tensor] = None, v: Optional[Cache] = None, stream=None) -> None:
+    """indexpool_decode_index then sparse_attn_decode over its selection, in one call."""
+    s, kc, k, p = seqs.c(), kv.c(), keys.c(), pooled.c()
+    vc = None if v is None else v.c()
+    _, H, dk = q.shape
+    _check("indexpool_decode_step", LIB.indexpool_decode_step(
+        ctypes.byref(s), kv_new.data_ptr(), ctypes.byref(kc), _ptr(v_new), None if vc is None else ctypes.byref(vc),
+        key_new.data_ptr(), _DT[key_new.dtype], ctypes.byref(k), logit_new.data_ptr(), logits.data_ptr(),
+        ctypes.byref(p), q_idx.data_ptr(), _DT[q_idx.dtype], q_idx.shape[1], q_idx.shape[2], gates.data_ptr(),
+        top_k, out_idx.data_ptr(), _ptr(scores), q.data_ptr(), _DT[q.dtype], H, dk, dv, scale, out.data_ptr(),
+        _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def kda_prefill_chunk(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                      conv_w: torch.Tensor, conv_in: torch.Tensor, conv_out: torch.Tensor, state: torch.Tensor,
+                      out: torch.Tensor, stream=None) -> None:
+    """KDA over a chunk of tokens: x* [B, T, H*128] bf16, alpha [B, T, H, 128], beta [B, T, H];
+    state [B, H, 128, 128] updated in place, taps from conv_in to conv_out, out [B, T, H, 128]."""
+    B, T = xq.shape[0], xq.shape[1]
+    H = state.shape[1]
+    _check("kda_prefill_chunk", LIB.kda_prefill_chunk(
+        B, T, H, state.shape[2], xq.data_ptr(), xk.data_ptr(), xv.data_ptr(), _DT[xq.dtype], alpha.data_ptr(),
+        beta.data_ptr(), conv_w.data_ptr(), conv_in.data_ptr(), conv_out.data_ptr(), state.data_ptr(),
+        out.data_ptr(), _stream(stream)))

@@ -34,7 +34,10 @@ thread_local Hook g_hook[ip::K_LAST + 1];   // armed events per kernel id
 
 constexpr int64_t kMaxTokens = int64_t(1) << 31;   // int32 token positions
 constexpr size_t kScoreBudget = size_t(256) << 20;  // score workspace per row chunk
-constexpr int kAttnWorkgroups = 128;                // split decode attention up to this many workgroups
+#ifndef IP_ATTN_WG
+#define IP_ATTN_WG 128
+#endif
+constexpr int kAttnWorkgroups = IP_ATTN_WG;               // split decode attention up to this many workgroups
 
 ip_status check_seqs(const ip_seqs* s, const char* fn) {
   if (!s) return fail(IP_EINVAL, "%s: seqs is NULL", fn);
@@ -309,13 +312,10 @@ size_t index_score_topk_workspace_bytes(const ip_seqs* seqs, int32_t n_q, int32_
 
 }  // extern "C"
 
-// index_score_topk, optionally with a decode append fused into the first scoring
-// launch (FP8 keys) or launched just before it (F32 keys).
-static ip_status score_topk_impl(const char* fn, const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
-                                 const int32_t* q_pos, const void* q_idx, int32_t q_dtype, int32_t n_heads,
-                                 int32_t head_dim, const float* gates, const ip_cache* pooled, int32_t top_k,
-                                 int32_t* out_idx, float* scores, void* ws, size_t ws_bytes, hipStream_t stream,
-                                 const ip::AppendArgs* append) {
+// The checks of an indexer call (index_score_topk and the calls built on it).
+static ip_status score_check(const char* fn, const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
+                             const void* q_idx, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
+                             const float* gates, const ip_cache* pooled, int32_t top_k, int32_t* out_idx) {
   if (ip_status st = check_seqs(seqs, fn)) return st;
   if (ip_status st = check_cache(pooled, fn, "pooled")) return st;
   if (n_q < 1) return fail(IP_EINVAL, "%s: n_q must be >= 1", fn);
@@ -323,8 +323,7 @@ static ip_status score_topk_impl(const char* fn, const ip_seqs* seqs, int32_t n_
   if (top_k < 1 || top_k > 2048) return fail(IP_EUNSUPPORTED, "%s: top_k must be in 1..2048 (got %d)", fn, top_k);
   if (!q_seq && n_q > seqs->batch) return fail(IP_EINVAL, "%s: q_seq is NULL but n_q > batch", fn);
   if (pooled->row_dim != head_dim) return fail(IP_EINVAL, "%s: head_dim %d != pooled row_dim %d", fn, head_dim, pooled->row_dim);
-  const bool fp8 = pooled->dtype == IP_FP8_E4M3FN;
-  if (fp8) {
+  if (pooled->dtype == IP_FP8_E4M3FN) {
     if (q_dtype != IP_BF16 || n_heads != 32 || head_dim != 128)
       return fail(IP_EUNSUPPORTED, "%s: FP8 keys need BF16 queries with 32 heads x 128 dims", fn);
   } else if (pooled->dtype == IP_F32) {
@@ -333,6 +332,62 @@ static ip_status score_topk_impl(const char* fn, const ip_seqs* seqs, int32_t n_
   } else {
     return fail(IP_EUNSUPPORTED, "%s: pooled keys must be FP8 or F32", fn);
   }
+  return IP_OK;
+}
+
+// The scoring launch's arguments for rows [row0, row0 + nr) over the workspace ws
+// carved by `plan` (counters, group maxima, lists, then scores unless given).
+static ip::ScoreArgs score_args(const ip_seqs* seqs, const ScorePlan& plan, int row0, int nr, const int32_t* q_seq,
+                                const int32_t* q_pos, const void* q_idx, int32_t n_heads, int32_t head_dim,
+                                const float* gates, const ip_cache* pooled, int32_t top_k, int32_t* out_idx,
+                                float* scores, void* ws, const ip::AppendArgs* append) {
+  int32_t* count = (int32_t*)ws;
+  float* gm = (float*)((char*)ws + plan.count_bytes);
+  char* lists = (char*)ws + plan.count_bytes + plan.gm_bytes;
+  float* score_buf = scores ? scores : (float*)(lists + plan.list_bytes);
+  ip::ScoreArgs sa;
+  sa.L = layout_of(seqs);
+  sa.row0 = row0;
+  sa.n_rows = nr;
+  sa.q_seq = q_seq;
+  sa.q_pos = q_pos;
+  sa.q = q_idx;
+  sa.gates = gates;
+  sa.keys = (const uint8_t*)pooled->data;
+  sa.key_stride = pooled->row_stride;
+  sa.key_scale = pooled->scale;
+  // the kernels index scores, maxima and counters by (r - row0)
+  sa.scores = scores ? score_buf + (int64_t)row0 * plan.ld : score_buf;
+  sa.ld = plan.ld;
+  sa.gm = gm;
+  sa.gld = plan.gld;
+  sa.heads = n_heads;
+  sa.dim = head_dim;
+  sa.max_blocks = plan.max_blocks;
+  sa.top_k = top_k;
+  sa.out = out_idx;
+  sa.count = count;
+  sa.max_lists = plan.max_lists;
+  sa.lists = plan.max_lists ? (uint64_t*)lists : nullptr;
+  sa.lists_meta = plan.max_lists ? (uint2*)(lists + (size_t)plan.rows_per_pass * plan.max_lists * 16 * 8) : nullptr;
+  sa.with_append = append && row0 == 0;
+  if (sa.with_append) sa.append = *append;
+  sa.fuse = 0;
+  sa.fuse = pooled->dtype == IP_FP8_E4M3FN && ip::score_fuses_select(sa);
+  return sa;
+}
+
+// index_score_topk, optionally with a decode append fused into the first scoring
+// launch (FP8 keys) or launched just before it (F32 keys).
+static ip_status score_topk_impl(const char* fn, const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
+                                 const int32_t* q_pos, const void* q_idx, int32_t q_dtype, int32_t n_heads,
+                                 int32_t head_dim, const float* gates, const ip_cache* pooled, int32_t top_k,
+                                 int32_t* out_idx, float* scores, void* ws, size_t ws_bytes, hipStream_t stream,
+                                 const ip::AppendArgs* append) {
+  if (ip_status st = score_check(fn, seqs, n_q, q_seq, q_idx, q_dtype, n_heads, head_dim, gates, pooled, top_k,
+                                 out_idx))
+    return st;
+  const bool fp8 = pooled->dtype == IP_FP8_E4M3FN;
   const ScorePlan plan = score_plan(seqs, n_q, scores != nullptr);
   if (!ws || ws_bytes < plan.total)
     return fail(IP_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.total, ws ? ws_bytes : 0);
@@ -342,42 +397,10 @@ static ip_status score_topk_impl(const char* fn, const ip_seqs* seqs, int32_t n_
     if (ip_status st = device_status(ip::launch_append(*append, stream), fn)) return st;
     append = nullptr;
   }
-  int32_t* count = (int32_t*)ws;
-  float* gm = (float*)((char*)ws + plan.count_bytes);
-  char* lists = (char*)ws + plan.count_bytes + plan.gm_bytes;
-  float* score_buf = scores ? scores : (float*)(lists + plan.list_bytes);
-
   for (int row0 = 0; row0 < n_q; row0 += plan.rows_per_pass) {
     const int nr = std::min(plan.rows_per_pass, n_q - row0);
-    ip::ScoreArgs sa;
-    sa.L = layout_of(seqs);
-    sa.row0 = row0;
-    sa.n_rows = nr;
-    sa.q_seq = q_seq;
-    sa.q_pos = q_pos;
-    sa.q = q_idx;
-    sa.gates = gates;
-    sa.keys = (const uint8_t*)pooled->data;
-    sa.key_stride = pooled->row_stride;
-    sa.key_scale = pooled->scale;
-    // the kernels index scores, maxima and counters by (r - row0)
-    sa.scores = scores ? score_buf + (int64_t)row0 * plan.ld : score_buf;
-    sa.ld = plan.ld;
-    sa.gm = gm;
-    sa.gld = plan.gld;
-    sa.heads = n_heads;
-    sa.dim = head_dim;
-    sa.max_blocks = plan.max_blocks;
-    sa.top_k = top_k;
-    sa.out = out_idx;
-    sa.count = count;
-    sa.max_lists = plan.max_lists;
-    sa.lists = plan.max_lists ? (uint64_t*)lists : nullptr;
-    sa.lists_meta = plan.max_lists ? (uint2*)(lists + (size_t)plan.rows_per_pass * plan.max_lists * 16 * 8) : nullptr;
-    sa.with_append = append && row0 == 0;
-    if (sa.with_append) sa.append = *append;
-    sa.fuse = 0;
-    sa.fuse = fp8 && ip::score_fuses_select(sa);
+    const ip::ScoreArgs sa = score_args(seqs, plan, row0, nr, q_seq, q_pos, q_idx, n_heads, head_dim, gates, pooled,
+                                        top_k, out_idx, scores, ws, append);
     ip_status st = device_status(fp8 ? ip::launch_score_fp8_bf16(sa, stream) : ip::launch_score_f32(sa, stream), fn);
     if (st) return st;
     if (sa.fuse) continue;
@@ -389,7 +412,7 @@ static ip_status score_topk_impl(const char* fn, const ip_seqs* seqs, int32_t n_
     ta.q_pos = q_pos;
     ta.scores = sa.scores;
     ta.ld = plan.ld;
-    ta.gm = gm;
+    ta.gm = sa.gm;
     ta.gld = plan.gld;
     ta.top_k = top_k;
     ta.out = out_idx;
@@ -433,11 +456,14 @@ size_t sparse_attn_workspace_bytes(int32_t n_q, int32_t n_heads, int32_t dv, int
   return attn_plan(n_q, n_heads, dv, top_k, q_dtype).bytes;
 }
 
-static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
-                             const int32_t* q_pos, const void* q, int32_t q_dtype, int32_t n_heads,
-                             int32_t dk, int32_t dv, float scale, const ip_cache* k, const ip_cache* v,
-                             const int32_t* sel_idx, int32_t top_k, void* out, float* lse, void* ws,
-                             size_t ws_bytes, hipStream_t stream) {
+enum AttnKind { ATTN_BF16, ATTN_FP8, ATTN_F32 };
+
+// Checks the arguments of an attention call and fills the kernel arguments.
+static ip_status attn_build(const char* fn, const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
+                            const int32_t* q_pos, const void* q, int32_t q_dtype, int32_t n_heads,
+                            int32_t dk, int32_t dv, float scale, const ip_cache* k, const ip_cache* v,
+                            const int32_t* sel_idx, int32_t top_k, void* out, float* lse, void* ws,
+                            size_t ws_bytes, ip::AttnArgs& a, AttnKind& kind) {
   if (ip_status st = check_seqs(seqs, fn)) return st;
   if (ip_status st = check_cache(k, fn, "k")) return st;
   if (n_q < 1) return fail(IP_EINVAL, "%s: n_q must be >= 1", fn);
@@ -445,7 +471,7 @@ static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, c
   if (top_k < 1 || top_k > 2048) return fail(IP_EUNSUPPORTED, "%s: top_k must be in 1..2048 (got %d)", fn, top_k);
   if (!q_seq && n_q > seqs->batch) return fail(IP_EINVAL, "%s: q_seq is NULL but n_q > batch", fn);
   if (!(scale > 0.f)) return fail(IP_EINVAL, "%s: scale must be positive", fn);
-  ip::AttnArgs a;
+  a = ip::AttnArgs{};
   a.L = layout_of(seqs);
   a.row0 = 0;
   a.n_rows = n_q;
@@ -487,9 +513,11 @@ static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, c
     a.part_ml = p.n_split > 1 ? (float*)(a.part_o + (size_t)n_q * p.n_split * n_heads * dv) : nullptr;
     if (k->dtype == IP_FP8_E4M3FN) {
       a.k_scale = k->scale;
-      return device_status(ip::launch_attn_fp8(a, stream), fn);
+      kind = ATTN_FP8;
+    } else {
+      kind = ATTN_BF16;
     }
-    return device_status(ip::launch_attn_bf16(a, stream), fn);
+    return IP_OK;
   }
   if (q_dtype == IP_F32) {
     if (ip_status st = check_cache(v, fn, "v")) return st;
@@ -503,9 +531,31 @@ static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, c
     a.blocks_per_split = top_k;
     a.part_o = nullptr;
     a.part_ml = nullptr;
-    return device_status(ip::launch_attn_f32(a, stream), fn);
+    kind = ATTN_F32;
+    return IP_OK;
   }
   return fail(IP_EUNSUPPORTED, "%s: q must be BF16 or F32", fn);
+}
+
+static ip_status attn_launch(const char* fn, const ip::AttnArgs& a, AttnKind kind, hipStream_t stream) {
+  switch (kind) {
+    case ATTN_BF16: return device_status(ip::launch_attn_bf16(a, stream), fn);
+    case ATTN_FP8: return device_status(ip::launch_attn_fp8(a, stream), fn);
+    default: return device_status(ip::launch_attn_f32(a, stream), fn);
+  }
+}
+
+static ip_status attn_common(const char* fn, const ip_seqs* seqs, int32_t n_q, const int32_t* q_seq,
+                             const int32_t* q_pos, const void* q, int32_t q_dtype, int32_t n_heads,
+                             int32_t dk, int32_t dv, float scale, const ip_cache* k, const ip_cache* v,
+                             const int32_t* sel_idx, int32_t top_k, void* out, float* lse, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  ip::AttnArgs a;
+  AttnKind kind;
+  if (ip_status st = attn_build(fn, seqs, n_q, q_seq, q_pos, q, q_dtype, n_heads, dk, dv, scale, k, v, sel_idx,
+                                top_k, out, lse, ws, ws_bytes, a, kind))
+    return st;
+  return attn_launch(fn, a, kind, stream);
 }
 
 ip_status sparse_attn_decode(const ip_seqs* seqs, const void* q, int32_t q_dtype, int32_t n_heads,
@@ -526,6 +576,87 @@ ip_status sparse_attn_prefill(const ip_seqs* seqs, int32_t n_q, const int32_t* q
   return attn_common("sparse_attn_prefill", seqs, n_q, q_seq, q_pos, q, q_dtype, n_heads, dk, dv, scale, k, v,
                      sel_idx, top_k, out, lse, ws, ws_bytes, stream);
 }
+
+// ------------------------------------------------------------------ fused decode step
+// workspace: the indexer's, the attention's, then one ready word per sequence
+struct StepPlan {
+  ScorePlan score;
+  AttnPlan attn;
+  size_t idx_bytes, attn_bytes, ready_bytes, total;
+};
+
+static StepPlan step_plan(const ip_seqs* seqs, int32_t top_k, int32_t n_heads, int32_t dv, int32_t q_dtype,
+                          bool scores_given) {
+  StepPlan p;
+  p.score = score_plan(seqs, seqs->batch, scores_given);
+  p.attn = attn_plan(seqs->batch, n_heads, dv, top_k, q_dtype);
+  p.idx_bytes = align256(p.score.total);
+  p.attn_bytes = align256(p.attn.bytes);
+  p.ready_bytes = align256((size_t)seqs->batch * 4);
+  p.total = p.idx_bytes + p.attn_bytes + p.ready_bytes;
+  return p;
+}
+
+extern "C" {
+
+size_t indexpool_decode_step_workspace_bytes(const ip_seqs* seqs, int32_t top_k, int32_t n_heads, int32_t dv,
+                                             int32_t q_dtype, int32_t scores_given) {
+  if (!seqs || seqs->batch < 1 || top_k < 1 || n_heads < 1 || dv < 1 || seqs->max_seq_len < 1) return 0;
+  return step_plan(seqs, top_k, n_heads, dv, q_dtype, scores_given != 0).total;
+}
+
+ip_status indexpool_decode_step(const ip_seqs* seqs, const void* kv_new, const ip_cache* kv, const void* v_new,
+                                const ip_cache* v, const void* key_new, int32_t key_dtype, const ip_cache* keys,
+                                const float* logit_new, float* logits, const ip_cache* pooled, const void* q_idx,
+                                int32_t idx_dtype, int32_t idx_heads, int32_t idx_dim, const float* gates,
+                                int32_t top_k, int32_t* out_idx, float* scores, const void* q, int32_t q_dtype,
+                                int32_t n_heads, int32_t dk, int32_t dv, float scale, void* out, float* lse,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "indexpool_decode_step";
+  if (ip_status st = check_seqs(seqs, fn)) return st;
+  if (!keys) return fail(IP_EINVAL, "%s: keys are required (the scoring reads the pooled keys)", fn);
+  ip::AppendArgs app;
+  if (ip_status st = build_append(fn, seqs, kv_new, kv, v_new, v, key_new, key_dtype, keys, logit_new, logits,
+                                  pooled, app))
+    return st;
+  const int32_t B = seqs->batch;
+  if (ip_status st = score_check(fn, seqs, B, nullptr, q_idx, idx_dtype, idx_heads, idx_dim, gates, pooled, top_k,
+                                 out_idx))
+    return st;
+  if (n_heads < 1 || dv < 1) return fail(IP_EINVAL, "%s: n_heads and dv must be >= 1", fn);
+  const StepPlan plan = step_plan(seqs, top_k, n_heads, dv, q_dtype, scores != nullptr);
+  if (!ws || ws_bytes < plan.total)
+    return fail(IP_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.total, ws ? ws_bytes : 0);
+  if (((uintptr_t)ws & 255) != 0) return fail(IP_EINVAL, "%s: ws must be 256-byte aligned", fn);
+  char* ws_idx = (char*)ws;
+  char* ws_att = ws_idx + plan.idx_bytes;
+  uint32_t* ready = (uint32_t*)(ws_att + plan.attn_bytes);
+  ip::AttnArgs a;
+  AttnKind kind;
+  if (ip_status st = attn_build(fn, seqs, B, nullptr, nullptr, q, q_dtype, n_heads, dk, dv, scale, kv, v, out_idx,
+                                top_k, out, lse, plan.attn_bytes ? ws_att : nullptr, plan.attn_bytes, a, kind))
+    return st;
+  // one launch when the selection is fused into the scoring (FP8 keys, every row
+  // in one pass) and the attention is the split bf16 latent kernel
+  if (kind == ATTN_BF16 && pooled->dtype == IP_FP8_E4M3FN && plan.score.rows_per_pass >= B &&
+      ((uintptr_t)kv_new & 15) == 0 && app.kv_row_bytes >= ip::LAT_DK * 2) {
+    ip::StepArgs st;
+    st.score = score_args(seqs, plan.score, 0, B, nullptr, nullptr, q_idx, idx_heads, idx_dim, gates, pooled, top_k,
+                          out_idx, scores, ws_idx, &app);
+    st.attn = a;
+    st.attn.sel_ready = ready;
+    st.attn.k_new = (const uint8_t*)kv_new;
+    st.attn.k_new_stride = app.kv_row_bytes;
+    if (ip::decode_step_supported(st)) return device_status(ip::launch_decode_step(st, stream), fn);
+  }
+  // otherwise: the indexer call (with the append), then the attention
+  if (ip_status st = score_topk_impl(fn, seqs, B, nullptr, nullptr, q_idx, idx_dtype, idx_heads, idx_dim, gates,
+                                     pooled, top_k, out_idx, scores, ws_idx, plan.idx_bytes, stream, &app))
+    return st;
+  return attn_launch(fn, a, kind, stream);
+}
+
+}  // extern "C"
 
 // ------------------------------------------------------------------ KDA decode step
 ip_status kda_decode_step(int32_t batch, int32_t n_heads, int32_t head_dim, const void* xq, const void* xk,
@@ -560,6 +691,42 @@ ip_status kda_decode_step(int32_t batch, int32_t n_heads, int32_t head_dim, cons
   a.state = state;
   a.out = out;
   return device_status(ip::launch_kda_decode(a, stream), fn);
+}
+
+ip_status kda_prefill_chunk(int32_t batch, int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void* xq,
+                            const void* xk, const void* xv, int32_t x_dtype, const float* alpha, const float* beta,
+                            const float* conv_w, const float* conv_in, float* conv_out, float* state, float* out,
+                            hipStream_t stream) {
+  const char* fn = "kda_prefill_chunk";
+  if (batch < 1 || batch > 65535 || n_heads < 1 || n_heads > 16383)
+    return fail(IP_EINVAL, "%s: batch must be in 1..65535 and n_heads in 1..16383 (got %d, %d)", fn, batch, n_heads);
+  if (n_tokens < 0) return fail(IP_EINVAL, "%s: n_tokens must be >= 0 (got %d)", fn, n_tokens);
+  if (head_dim != ip::KDA_D) return fail(IP_EUNSUPPORTED, "%s: head_dim must be 128 (got %d)", fn, head_dim);
+  if (x_dtype != IP_BF16) return fail(IP_EUNSUPPORTED, "%s: xq, xk, xv must be BF16", fn);
+  if (!conv_w || !conv_in || !conv_out || !state || (n_tokens > 0 && (!xq || !xk || !xv || !alpha || !beta || !out)))
+    return fail(IP_EINVAL, "%s: a required pointer is NULL", fn);
+  const uintptr_t cb = (uintptr_t)batch * 9 * n_heads * ip::KDA_D * sizeof(float);
+  const uintptr_t ci = (uintptr_t)conv_in, co = (uintptr_t)conv_out;
+  if (ci < co + cb && co < ci + cb)
+    return fail(IP_EINVAL, "%s: conv_in and conv_out must not overlap", fn);
+  for (const void* p : {(const void*)conv_w, (const void*)state, xq, xk, xv, (const void*)alpha})
+    if ((reinterpret_cast<uintptr_t>(p) & 15) != 0)
+      return fail(IP_EINVAL, "%s: conv_w, state, xq, xk, xv and alpha must be 16-byte aligned", fn);
+  ip::KdaChunkArgs a;
+  a.batch = batch;
+  a.heads = n_heads;
+  a.n_tokens = n_tokens;
+  a.xq = (const uint16_t*)xq;
+  a.xk = (const uint16_t*)xk;
+  a.xv = (const uint16_t*)xv;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.conv_w = conv_w;
+  a.conv_in = conv_in;
+  a.conv_out = conv_out;
+  a.state = state;
+  a.out = out;
+  return device_status(ip::launch_kda_chunk(a, stream), fn);
 }
 
 // ------------------------------------------------------------------ no-allocation indexer

@@ -23,6 +23,7 @@
 //   combine kernel.
 // f32 path (small geometries): plain VALU, one workgroup per row.
 #include "attn_common.hpp"
+#include "score_fp8.hpp"
 
 namespace ip {
 
@@ -65,12 +66,21 @@ struct BlockIds {
   int blk[MAX_BLOCKS_PER_SPLIT / NTA];
 };
 
+// selection id bi of the row: COH reads ids stored by another workgroup of the same
+// launch (device-coherent load, sc1)
+template <bool COH>
+__device__ __forceinline__ int sel_id(const RowCtx& c, int bi) {
+  if constexpr (COH) return (int)__builtin_amdgcn_raw_buffer_load_b32(sel::dev_rsrc(c.sel), (uint32_t)bi * 4u, 0, 16);
+  return c.sel[bi];
+}
+
+template <bool COH>
 __device__ __forceinline__ BlockIds fetch_blocks(const RowCtx& c, int sb0, int send) {
   BlockIds ids;
 #pragma unroll
   for (int k = 0; k < MAX_BLOCKS_PER_SPLIT / NTA; ++k) {
     const int bi = sb0 + (int)threadIdx.x + k * NTA;
-    ids.blk[k] = bi < send ? c.sel[bi] : -1;
+    ids.blk[k] = bi < send ? sel_id<COH>(c, bi) : -1;
   }
   return ids;
 }
@@ -116,7 +126,23 @@ __device__ __forceinline__ void subtile_entries(const AttnShared& sh, int n, uin
   e[1] = (lane >> 5) ? q[3] : q[2];
 }
 
-__device__ __forceinline__ SubtileSrc subtile_src(const AttnArgs& a, const AttnShared& sh, int n) {
+// The query's own token row in the fused decode step: the cache row the same
+// launch appends (row = its index) is read from the new token's input row (src)
+// instead, so no workgroup reads a cache row while it is being written.  row =
+// ~0u: no redirect.
+struct NewRow {
+  uint32_t row;
+  const uint8_t* src;
+};
+
+template <bool STEP>
+__device__ __forceinline__ const uint8_t* kv_row_src(const AttnArgs& a, const NewRow& nr, uint32_t grow, int swz) {
+  if constexpr (STEP) return (grow == nr.row ? nr.src : a.k + (uint64_t)grow * a.k_stride) + swz;
+  return a.k + (uint64_t)grow * a.k_stride + swz;
+}
+
+template <bool STEP>
+__device__ __forceinline__ SubtileSrc subtile_src(const AttnArgs& a, const AttnShared& sh, int n, const NewRow& nr) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t e[2];
@@ -126,7 +152,7 @@ __device__ __forceinline__ SubtileSrc subtile_src(const AttnArgs& a, const AttnS
   for (int h = 0; h < 2; ++h) {
     const int t = 8 * (2 * wv + h) + (lane >> 3);
     const uint32_t grow = (e[h] & ROW_BITS) + (t & 3);
-    src.row[h] = a.k + (uint64_t)grow * a.k_stride + 16 * ((lane & 7) ^ kv_swz(t));
+    src.row[h] = kv_row_src<STEP>(a, nr, grow, 16 * ((lane & 7) ^ kv_swz(t)));
   }
   return src;
 }
@@ -140,16 +166,19 @@ __device__ __forceinline__ void load_column(const SubtileSrc& src, uint8_t* buf,
 }
 
 
-__global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
-  __shared__ AttnShared sh;
-  __shared__ __align__(16) uint8_t pmat[LAT_H * PROW];   // P[head][token] bf16
-  __shared__ __align__(16) uint8_t kv0[KVBUF];
-  __shared__ __align__(16) uint8_t kv1[KVBUF];
+// The body of the bf16 kernel for workgroup `bid` (4 waves, threads 0..255), over
+// the LDS objects of the calling kernel.  STEP (the fused decode step): the row's
+// selection is produced by another workgroup of the same launch, which sets
+// a.sel_ready[row] once its ids are stored; the query is fetched first, then the
+// workgroup waits for that word and reads the ids device-coherently, and the
+// query's own token row comes from a.k_new.
+template <bool STEP>
+__device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const int bid, AttnShared& sh, uint8_t* pmat,
+                                               uint8_t* kv0, uint8_t* kv1) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
   const int l32 = lane & 31, lh = lane >> 5;
   const int hb = wv & 1, th = wv >> 1;           // S^T tile: heads 32hb .., tokens 32th ..
-  const int bid = blockIdx.x;
   if (bid >= a.n_rows * a.n_split) return;
   const int split = bid % a.n_split;
   const int rl = bid / a.n_split;
@@ -159,22 +188,28 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
   const int send = min(a.top_k, sb0 + a.blocks_per_split);
   const int nsub = (send - sb0 + 15) >> 4;
   const int hs = 32 * hb + l32;                  // head of this lane in the S^T layout
+  NewRow nr{~0u, nullptr};
+  if constexpr (STEP) nr = NewRow{(uint32_t)a.L.tok_row(c.b, c.p), a.k_new + (int64_t)c.b * a.k_new_stride};
 
   // prologue: the selection ids (block-table entries and this lane's rows of
   // sub-tiles 0 and 1); the query row into kv1; sub-tile 0; q into registers; then
   // sub-tile 1 into kv1.  The query goes by LDS DMA in whole 128-byte lines (loads
   // of each lane's q fragments straight from memory measured 2.3 us slower per
   // decode step).
-  const BlockIds ids = fetch_blocks(c, sb0, send);
+  BlockIds ids;
   // ids of this lane's source blocks for sub-tiles 0 and 1 (rows 8(2w + h) + l/8)
   int pid[2][2];
+  auto load_ids = [&]() {
+    ids = fetch_blocks<STEP>(c, sb0, send);
 #pragma unroll
-  for (int n = 0; n < 2; ++n)
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int bi = sb0 + 16 * n + ((8 * (2 * wv + h) + (lane >> 3)) >> 2);
-      pid[n][h] = bi < send ? c.sel[bi] : -1;
-    }
+      for (int h = 0; h < 2; ++h) {
+        const int bi = sb0 + 16 * n + ((8 * (2 * wv + h) + (lane >> 3)) >> 2);
+        pid[n][h] = bi < send ? sel_id<STEP>(c, bi) : -1;
+      }
+  };
+  if constexpr (!STEP) load_ids();
   {
     // the query row (64 heads x 576 dims = one sub-tile's bytes) goes to kv1 in the
     // sub-tile layout, head h as row h: whole 128-byte lines, and the fragment
@@ -187,6 +222,17 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < KV_LOADS; ++k) load_column(qsrc, kv1, k);
+  }
+  if constexpr (STEP) {
+    // wait (bounded) until the row's ids are published; a load of the word waits
+    // for the query loads above as well, which by then have long landed
+    __builtin_amdgcn_sched_barrier(0);
+    if (threadIdx.x == 0) {
+      const uint32_t* f = a.sel_ready + rl;
+      for (int n = 0; sel::ld_agent(f) == 0u && n < STEP_SPIN_LIMIT; ++n) __builtin_amdgcn_s_sleep(1);
+    }
+    block_sync_lds();
+    load_ids();
   }
   // every query DMA is issued before anything consumes the ids
   __builtin_amdgcn_sched_barrier(0);
@@ -205,7 +251,7 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
     for (int h = 0; h < 2; ++h) {
       const int t = 8 * (2 * wv + h) + (lane >> 3);
       const uint32_t grow = (ent[2 + 2 * n + h] & ROW_BITS) + (t & 3);
-      src[n].row[h] = a.k + (uint64_t)grow * a.k_stride + 16 * ((lane & 7) ^ kv_swz(t));
+      src[n].row[h] = kv_row_src<STEP>(a, nr, grow, 16 * ((lane & 7) ^ kv_swz(t)));
     }
 #pragma unroll
   for (int k = 0; k < KV_LOADS; ++k) load_column(src[0], kv0, k);
@@ -252,7 +298,7 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
     // fetched one column per two k-steps of the S^T product below: each DMA
     // instruction takes long to issue, and between MFMAs that time is hidden.
     const bool fetch = n >= 1 && n + 1 < nsub;
-    const SubtileSrc fsrc = subtile_src(a, sh, fetch ? n + 1 : n);
+    const SubtileSrc fsrc = subtile_src<STEP>(a, sh, fetch ? n + 1 : n, nr);
     // visible-token counts of this wave's 8 blocks, read before any fetch is in flight
     const u32x4_t bv0 = lds_ld((const u32x4_t*)&sh.brow[n * 16 + 8 * th]);
     const u32x4_t bv1 = lds_ld((const u32x4_t*)&sh.brow[n * 16 + 8 * th + 4]);
@@ -412,6 +458,50 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
+__global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
+  __shared__ AttnShared sh;
+  __shared__ __align__(16) uint8_t pmat[LAT_H * PROW];   // P[head][token] bf16
+  __shared__ __align__(16) uint8_t kv0[KVBUF];
+  __shared__ __align__(16) uint8_t kv1[KVBUF];
+  attn_bf16_body<false>(a, blockIdx.x, sh, pmat, kv0, kv1);
+}
+
+// ------------------------------------------------------------------ fused decode step
+// One launch for the decode step: workgroups [0, n_score) score and select (one
+// row each; the row's last scoring workgroup selects it and publishes the ids),
+// [n_score, n_score + n_app) append the new tokens, and the rest run the attention
+// of one (row, split) each.  Workgroups start in
+// index order, so every attention workgroup waits only on workgroups that have
+// started before it and never wait themselves: the wait ends.  The attention
+// workgroups take their compute units as the scoring ones finish and fetch their
+// query while the rows are being selected.  The scoring state lives in the first
+// sub-tile buffer.
+struct StepKArgs {
+  ScoreArgs s;
+  AttnArgs at;
+  int gx, n_score, n_app;
+};
+// The scoring role: 4 waves of 8 tiles (1024 keys per workgroup, as the standalone
+// fused scoring's 8 waves of 4 tiles), the register budget of one wave per SIMD
+// that the attention role needs anyway.
+constexpr int STEP_NWV = 4, STEP_TILES = 8;
+static_assert(scorek::score_smem<STEP_NWV, true>() <= KVBUF, "the scoring state fits a sub-tile buffer");
+
+__global__ __launch_bounds__(NTA, 1) void decode_step_kernel(StepKArgs A) {
+  __shared__ AttnShared sh;
+  __shared__ __align__(16) uint8_t pmat[LAT_H * PROW];
+  __shared__ __align__(16) uint8_t kv0[KVBUF];
+  __shared__ __align__(16) uint8_t kv1[KVBUF];
+  __shared__ int last_here;
+  const int L = blockIdx.x;
+  if (L < A.n_score + A.n_app) {
+    scorek::score_fp8_body<1, STEP_NWV, true, STEP_TILES>(A.s, L % A.gx, L / A.gx, A.gx, kv0, last_here,
+                                                           A.at.sel_ready);
+    return;
+  }
+  attn_bf16_body<true>(A.at, L - A.n_score - A.n_app, sh, pmat, kv0, kv1);
+}
+
 // ------------------------------------------------------------------ fp8 latent tier
 // Latent rows stored as e4m3fn codes (576 bytes) with one fp32 scale per token;
 // K_t = sigma_t dec(code_t), V_t its first 512 dims.  Same work split and softmax
@@ -514,7 +604,7 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
   // lines, dims 0..511 into vb and 512..575 into pmat (both free until step 0),
   // head h as row h in the sub-tile layout; sub-tiles 0 and 1 with their scales;
   // then q into registers.
-  const BlockIds ids = fetch_blocks(c, sb0, send);
+  const BlockIds ids = fetch_blocks<false>(c, sb0, send);
   int pid[2][2], sid[2];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
@@ -831,6 +921,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     for (int u = 0; u < 4; ++u) add(__shfl(wgt, s + u), v[u]);
   }
   for (; s < S; ++s) add(__shfl(wgt, s), *(const uint2*)(base + (int64_t)s * LAT_H * LAT_DV));
+  // the fused step's ready word of the row, for the next launch (every reader of it
+  // belongs to the step launch, which has ended)
+  if (a.sel_ready && blockIdx.x == 0 && threadIdx.x == 0) a.sel_ready[rl] = 0u;
   const float inv = 1.f / L;
   uint16_t* out = (uint16_t*)a.out + ((int64_t)r * LAT_H + head) * LAT_DV + t * 4;
   *(uint2*)out = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
@@ -971,6 +1064,30 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   launch(K_COMBINE, attn_combine_kernel, dim3(LAT_H / 2, a.n_rows), dim3(256), s, a);
+  return hipGetLastError();
+}
+
+bool decode_step_supported(const StepArgs& a) {
+  return a.score.fuse && a.score.row0 == 0 && a.attn.row0 == 0 && a.attn.n_rows == a.score.n_rows &&
+         a.attn.n_split > 1 && a.attn.blocks_per_split < PIPE_MIN_BLOCKS && a.attn.sel_ready && a.attn.k_new &&
+         !a.attn.k_scale && a.score.max_blocks > 0;
+}
+
+hipError_t launch_decode_step(const StepArgs& a, hipStream_t s) {
+  if (!decode_step_supported(a)) return hipErrorInvalidValue;
+  constexpr int KEYS = STEP_NWV * STEP_TILES * 32;   // the scoring role's keys per workgroup
+  StepKArgs k;
+  k.s = a.score;
+  k.at = a.attn;
+  k.gx = (a.score.max_blocks + KEYS - 1) / KEYS;
+  k.n_score = k.gx * a.score.n_rows;
+  k.n_app = a.score.with_append ? k.gx * ((a.score.append.batch + k.gx - 1) / k.gx) : 0;
+  const int64_t grid = (int64_t)k.n_score + k.n_app + (int64_t)a.attn.n_rows * a.attn.n_split;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  launch(K_STEP, decode_step_kernel, dim3((unsigned)grid), dim3(NTA), s, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch(K_COMBINE, attn_combine_kernel, dim3(LAT_H / 2, a.attn.n_rows), dim3(256), s, a.attn);
   return hipGetLastError();
 }
 

@@ -151,7 +151,306 @@ __global__ __launch_bounds__(KT) void kda_decode_kernel(KdaArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ chunked form (prefill)
+// The same recurrence over n_tokens consecutive tokens, 16 at a time.  Within a
+// block of C = 16 tokens that starts from state S0, let G_i = sum_{m <= i} log
+// alpha_m (per key channel, running over the block).  Unrolling the token steps
+// gives exactly
+//   u_i = beta_i (v_i - S0^T (k_i e^{G_i}) - sum_{j<i} A_ij u_j),
+//         A_ij = sum_c k_i[c] k_j[c] e^{G_i[c] - G_j[c]}       (a lower-triangular solve)
+//   o_i = (S0^T (q_i e^{G_i}) + sum_{j<=i} B_ij u_j) / sqrt(128),
+//         B_ij = sum_c q_i[c] k_j[c] e^{G_i[c] - G_j[c]}
+//   S   = Diag(e^{G_last}) S0 + sum_j (k_j e^{G_last - G_j}) u_j^T,
+// where u_i is the delta-rule write of token i (S_i = Diag(alpha_i) S_{i-1} + k_i u_i^T).
+// The products with S0, the outputs and the state update are dense contractions
+// on fp32 MFMA (v_mfma_f32_16x16x4_f32).  A and B are (k e^G)(k e^-G)^T and
+// (q e^G)(k e^-G)^T -- unless some e^-G of the block would leave fp32's range (a
+// cumulative decay below e^-80 inside 16 tokens), in which case they are summed
+// term by term with e^{G_i - G_j} <= 1.  One workgroup per (head, 32-column slice,
+// sequence), as in the decode step; the blocks of a sequence run in order inside it,
+// the state slice staying in LDS.  Tokens past the end of the last block enter with
+// zero input, alpha = 1 and beta = 0, which leaves the state and the taps unchanged.
+constexpr int CC = 16;               // tokens per block
+constexpr int CP = KD + 2;           // row of q~, k~, k^ (read [token][channel] by 16 x 4 lanes)
+constexpr int KBP = KD + 16;         // row of k-bar (read [token][channel] by 4 x 16 lanes)
+constexpr int SP = KSL + 16;         // row of the state slice and of u
+constexpr float G_SAFE = -80.f;
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct KdaChunkShared {
+  float hx[3][3][KD];                // conv taps x_{t-3 .. t-1}: q, k (128 channels), v (first 32)
+  float yq[CC][KD], yk[CC][KD];      // raw inputs, then conv + SiLU
+  float yv[CC][KSL];
+  float g[CC][KD];                   // log alpha, then its running sum G
+  float qt[CC][CP], kt[CC][CP], kh[CC][CP];
+  float kb[CC][KBP];
+  float S[KD][SP];
+  float A[CC][CC + 1], B[CC][CC + 1];
+  float U[CC][SP];                   // v - S0^T k~, then u
+  float gl[KD];                      // e^{G_last}
+  float beta[CC], rq[CC], rk[CC];
+  int unsafe;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
+  __shared__ KdaChunkShared sh;
+  const int h = blockIdx.x / KNS, sl = blockIdx.x % KNS, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int64_t HD = (int64_t)a.heads * KD;
+  const int T = a.n_tokens;
+  float* Sg = a.state + ((int64_t)b * a.heads + h) * KD * KD + KSL * sl;
+
+  // ---- the state slice and the conv taps in
+  for (int i = tid; i < KD * KSL / 4; i += KT) {
+    const int row = i / (KSL / 4), c4 = i % (KSL / 4);
+    const float4 v = *(const float4*)(Sg + (int64_t)row * KD + 4 * c4);
+    sh.S[row][4 * c4] = v.x;
+    sh.S[row][4 * c4 + 1] = v.y;
+    sh.S[row][4 * c4 + 2] = v.z;
+    sh.S[row][4 * c4 + 3] = v.w;
+  }
+  for (int i = tid; i < 3 * 3 * KD; i += KT) {
+    const int w = i / (3 * KD), m = (i / KD) % 3, c = i % KD;
+    if (w < 2 || c < KSL)
+      sh.hx[w][m][c] = a.conv_in[((int64_t)b * 3 + w) * 3 * HD + m * HD + (int64_t)h * KD + (w < 2 ? c : KSL * sl + c)];
+  }
+  // conv weights: thread t takes channel t % 128 of q (t < 128) or k; threads < 32 also
+  // the slice's v channel t
+  const int cw = tid >> 7, cc = tid & (KD - 1);
+  const float4 wqk = *(const float4*)(a.conv_w + ((int64_t)cw * HD + (int64_t)h * KD + cc) * 4);
+  float4 wv4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (tid < KSL) wv4 = *(const float4*)(a.conv_w + (2 * HD + (int64_t)h * KD + KSL * sl + tid) * 4);
+  const float rs = rsqrtf((float)KD);
+
+  for (int t0 = 0; t0 < T; t0 += CC) {
+    const int n = min(CC, T - t0);
+    __syncthreads();                             // the previous block is done with every buffer
+    // ---- the block's inputs: x (zero past n), log alpha (0 past n), beta (0 past n)
+    {
+      const int i = tid >> 4, c0 = 8 * (tid & 15);
+      u32x4_t xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
+      if (i < n) {
+        const int64_t off = ((int64_t)b * T + t0 + i) * HD + (int64_t)h * KD + c0;
+        xq = *(const u32x4_t*)(a.xq + off);
+        xk = *(const u32x4_t*)(a.xk + off);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sh.yq[i][c0 + 2 * e] = bf16_lo(xq[e]);
+        sh.yq[i][c0 + 2 * e + 1] = bf16_hi(xq[e]);
+        sh.yk[i][c0 + 2 * e] = bf16_lo(xk[e]);
+        sh.yk[i][c0 + 2 * e + 1] = bf16_hi(xk[e]);
+      }
+      if (tid < CC * KSL / 8) {
+        const int iv = tid >> 2, v0 = 8 * (tid & 3);
+        u32x4_t xv = {0u, 0u, 0u, 0u};
+        if (iv < n) xv = *(const u32x4_t*)(a.xv + ((int64_t)b * T + t0 + iv) * HD + (int64_t)h * KD + KSL * sl + v0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sh.yv[iv][v0 + 2 * e] = bf16_lo(xv[e]);
+          sh.yv[iv][v0 + 2 * e + 1] = bf16_hi(xv[e]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int idx = tid + KT * k, ia = idx >> 5, c4 = idx & 31;
+        float4 al = make_float4(1.f, 1.f, 1.f, 1.f);
+        if (ia < n) al = *(const float4*)(a.alpha + (((int64_t)b * T + t0 + ia) * a.heads + h) * KD + 4 * c4);
+        sh.g[ia][4 * c4] = logf(al.x);
+        sh.g[ia][4 * c4 + 1] = logf(al.y);
+        sh.g[ia][4 * c4 + 2] = logf(al.z);
+        sh.g[ia][4 * c4 + 3] = logf(al.w);
+      }
+      if (tid < CC) sh.beta[tid] = tid < n ? a.beta[((int64_t)b * T + t0 + tid) * a.heads + h] : 0.f;
+      if (tid == 0) sh.unsafe = 0;
+    }
+    __syncthreads();
+    // ---- short convolution + SiLU in place, taps sliding in registers (the taps after
+    //      the block are the last 3 inputs up to token n-1); the running sum G
+    {
+      float (*y)[KD] = cw ? sh.yk : sh.yq;
+      float x0 = sh.hx[cw][0][cc], x1 = sh.hx[cw][1][cc], x2 = sh.hx[cw][2][cc];
+      for (int i = 0; i < CC; ++i) {
+        const float xt = y[i][cc];
+        y[i][cc] = silu(fmaf(wqk.x, x0, fmaf(wqk.y, x1, fmaf(wqk.z, x2, wqk.w * xt))));
+        if (i < n) { x0 = x1; x1 = x2; x2 = xt; }
+      }
+      sh.hx[cw][0][cc] = x0;
+      sh.hx[cw][1][cc] = x1;
+      sh.hx[cw][2][cc] = x2;
+      if (tid < KSL) {
+        float v0 = sh.hx[2][0][tid], v1 = sh.hx[2][1][tid], v2 = sh.hx[2][2][tid];
+        for (int i = 0; i < CC; ++i) {
+          const float xt = sh.yv[i][tid];
+          sh.yv[i][tid] = silu(fmaf(wv4.x, v0, fmaf(wv4.y, v1, fmaf(wv4.z, v2, wv4.w * xt))));
+          if (i < n) { v0 = v1; v1 = v2; v2 = xt; }
+        }
+        sh.hx[2][0][tid] = v0;
+        sh.hx[2][1][tid] = v1;
+        sh.hx[2][2][tid] = v2;
+      }
+      if (tid < KD) {
+        float run = 0.f;
+        for (int i = 0; i < CC; ++i) {
+          run += sh.g[i][tid];
+          sh.g[i][tid] = run;
+        }
+      }
+    }
+    __syncthreads();
+    // ---- 1 / norms of q and k per token: thread -> (q or k, token (t % 128) / 8), 16
+    //      channels (t % 8) + 8j, summed over the 8 lanes of the token
+    {
+      const float (*y)[KD] = cw ? sh.yk : sh.yq;
+      const int i = cc >> 3, c0 = cc & 7;
+      float s2 = 0.f;
+#pragma unroll
+      for (int j = 0; j < KD / 8; ++j) {
+        const float v = y[i][c0 + 8 * j];
+        s2 = fmaf(v, v, s2);
+      }
+      s2 += __shfl_xor(s2, 1);
+      s2 += __shfl_xor(s2, 2);
+      s2 += __shfl_xor(s2, 4);
+      if (c0 == 0) (cw ? sh.rk : sh.rq)[i] = rsqrtf(s2 + 1e-6f);
+    }
+    __syncthreads();
+    // ---- decayed operands: thread -> token t / 16, channels 8(t % 16) .. +7
+    {
+      const int i = tid >> 4, c0 = 8 * (tid & 15);
+      const float nq = sh.rq[i], nk = sh.rk[i];
+      bool bad = false;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = c0 + e;
+        const float G = sh.g[i][c], GL = sh.g[CC - 1][c];
+        const float q = sh.yq[i][c] * nq, k = sh.yk[i][c] * nk;
+        const float eg = expf(G);
+        sh.qt[i][c] = q * eg;
+        sh.kt[i][c] = k * eg;
+        sh.kh[i][c] = k * expf(-G);
+        sh.kb[i][c] = k * expf(GL - G);
+        if (i == CC - 1) {
+          sh.gl[c] = eg;
+          bad |= GL < G_SAFE;
+        }
+      }
+      if (bad) sh.unsafe = 1;
+    }
+    __syncthreads();
+    // ---- S0 products and the block coefficients on MFMA: waves 0 / 1 take k~ S0 for
+    //      columns 16w .. +15 (then U = v - k~ S0) and A / B; waves 2 / 3 keep q~ S0
+    f32x4_t r = {0.f, 0.f, 0.f, 0.f};
+    {
+      const int nt = wv & 1;
+      const float (*lhs)[CP] = wv < 2 ? sh.kt : sh.qt;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int s = 0; s < KD / 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(lhs[r16][4 * s + kq], sh.S[4 * s + kq][16 * nt + r16], acc, 0, 0, 0);
+      if (wv < 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sh.U[4 * kq + e][16 * nt + r16] = sh.yv[4 * kq + e][16 * nt + r16] - acc[e];
+        const float (*left)[CP] = wv == 0 ? sh.kt : sh.qt;
+        f32x4_t c2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int s = 0; s < KD / 4; ++s)
+          c2 = __builtin_amdgcn_mfma_f32_16x16x4f32(left[r16][4 * s + kq], sh.kh[r16][4 * s + kq], c2, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 4 * kq + e;
+          if (wv == 0) sh.A[row][r16] = r16 < row ? c2[e] : 0.f;
+          else sh.B[row][r16] = r16 <= row ? c2[e] : 0.f;
+        }
+      } else {
+        r = acc;
+      }
+    }
+    __syncthreads();
+    if (sh.unsafe) {
+      // term by term: thread -> (i, j) = (t / 16, t % 16), e^{G_i - G_j} <= 1 for j <= i
+      const int i = tid >> 4, j = tid & 15;
+      if (j <= i) {
+        const float nq = sh.rq[i], nki = sh.rk[i], nkj = sh.rk[j];
+        float sa = 0.f, sb = 0.f;
+        for (int c = 0; c < KD; ++c) {
+          const float d = expf(sh.g[i][c] - sh.g[j][c]);
+          const float kj = sh.yk[j][c] * nkj;
+          sa = fmaf(sh.yk[i][c] * nki * d, kj, sa);
+          sb = fmaf(sh.yq[i][c] * nq * d, kj, sb);
+        }
+        if (j < i) sh.A[i][j] = sa;
+        sh.B[i][j] = sb;
+      }
+      __syncthreads();
+    }
+    // ---- u by forward substitution: lanes 0 .. 31 of wave 0, one column each
+    if (tid < KSL) {
+#pragma unroll
+      for (int i = 0; i < CC; ++i) {
+        float acc = sh.U[i][tid];
+        for (int j = 0; j < i; ++j) acc = fmaf(-sh.A[i][j], sh.U[j][tid], acc);
+        sh.U[i][tid] = sh.beta[i] * acc;
+      }
+    }
+    __syncthreads();
+    // ---- outputs (waves 2 / 3): (q~ S0 + B u) / sqrt(128)
+    if (wv >= 2) {
+      const int nt = wv & 1;
+#pragma unroll
+      for (int s = 0; s < CC / 4; ++s)
+        r = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.B[r16][4 * s + kq], sh.U[4 * s + kq][16 * nt + r16], r, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 4 * kq + e;
+        if (row < n)
+          a.out[(((int64_t)b * T + t0 + row) * a.heads + h) * KD + KSL * sl + 16 * nt + r16] = r[e] * rs;
+      }
+    }
+    // ---- state update: S = Diag(e^{G_last}) S0 + k-bar^T u, tiles of 16 x 16, four per wave
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tile = 4 * wv + j, mt = tile >> 1, nt = tile & 1;
+      f32x4_t acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * mt + 4 * kq + e;
+        acc[e] = sh.S[row][16 * nt + r16] * sh.gl[row];
+      }
+#pragma unroll
+      for (int s = 0; s < CC / 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.kb[4 * s + kq][16 * mt + r16], sh.U[4 * s + kq][16 * nt + r16], acc,
+                                                  0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sh.S[16 * mt + 4 * kq + e][16 * nt + r16] = acc[e];
+    }
+  }
+  __syncthreads();
+  // ---- the state slice and the taps out (q and k taps by the head's first slice)
+  for (int i = tid; i < KD * KSL / 4; i += KT) {
+    const int row = i / (KSL / 4), c4 = i % (KSL / 4);
+    *(float4*)(Sg + (int64_t)row * KD + 4 * c4) =
+        make_float4(sh.S[row][4 * c4], sh.S[row][4 * c4 + 1], sh.S[row][4 * c4 + 2], sh.S[row][4 * c4 + 3]);
+  }
+  for (int i = tid; i < 3 * 3 * KD; i += KT) {
+    const int w = i / (3 * KD), m = (i / KD) % 3, c = i % KD;
+    if ((w < 2 && sl == 0) || (w == 2 && c < KSL))
+      a.conv_out[((int64_t)b * 3 + w) * 3 * HD + m * HD + (int64_t)h * KD + (w < 2 ? c : KSL * sl + c)] = sh.hx[w][m][c];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kda_chunk(const KdaChunkArgs& a, hipStream_t s) {
+  if (a.batch <= 0 || a.heads <= 0) return hipSuccess;
+  launch(K_KDA, kda_chunk_kernel, dim3(a.heads * KNS, a.batch), dim3(KT), s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_kda_decode(const KdaArgs& a, hipStream_t s) {
   if (a.batch <= 0 || a.heads <= 0) return hipSuccess;

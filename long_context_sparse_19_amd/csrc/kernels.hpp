@@ -8,7 +8,8 @@
 
 namespace ip {
 
-enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3 /* select */, K_ATTN = 4, K_COMBINE = 5, K_APPEND = 6, K_KDA = 7, K_LAST = 7 };
+enum KernelId { K_COMPRESS = 1, K_SCORE = 2, K_TOPK = 3 /* select */, K_ATTN = 4, K_COMBINE = 5, K_APPEND = 6, K_KDA = 7,
+                K_STEP = 8, K_LAST = 8 };
 
 // Takes (and disarms) the timing hook's events if one is armed for kernel `id`.
 bool hook_take(int id, hipEvent_t* start, hipEvent_t* stop);
@@ -143,6 +144,12 @@ struct AttnArgs {
   int n_split, blocks_per_split;
   int heads, dk, dv;
   int k_off32;                 // every K row lies within 4 GB of k (32-bit byte offsets)
+  // fused decode step only (else null): sel_ready[r - row0] is set to 1 by the
+  // workgroup that stores row r's ids in the same launch (cleared by the combine),
+  // and the query's own token row is read from k_new + b * k_new_stride
+  uint32_t* sel_ready;
+  const uint8_t* k_new;
+  int64_t k_new_stride;
 };
 // bf16 latent MQA: 64 heads, dk 576, dv 512
 constexpr int LAT_H = 64, LAT_DK = 576, LAT_DV = 512;
@@ -152,6 +159,21 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 constexpr int PIPE_MIN_BLOCKS = 128;
 hipError_t launch_attn_bf16_pipe(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t s);
+
+// The fused decode step: one launch whose first workgroups score, select (and
+// append) every row as launch_score_fp8_bf16 does with fuse set, and whose last
+// workgroups run the bf16 attention of each (row, split) once the row's ids are
+// published; then the combine.  score: one pass over all rows, fuse and
+// with_append set; attn: n_split > 1, blocks_per_split < PIPE_MIN_BLOCKS,
+// sel_ready and k_new set.  A waiting workgroup gives up after STEP_SPIN_LIMIT
+// polls (only possible if earlier workgroups of the launch never run).
+constexpr int STEP_SPIN_LIMIT = 1 << 22;
+struct StepArgs {
+  ScoreArgs score;
+  AttnArgs attn;
+};
+bool decode_step_supported(const StepArgs& a);
+hipError_t launch_decode_step(const StepArgs& a, hipStream_t s);
 
 // KDA decode step (the linear-attention half): 128 key and value channels per head
 constexpr int KDA_D = 128;
@@ -169,6 +191,24 @@ struct KdaArgs {
   float* out;                  // [batch, heads, 128]
 };
 hipError_t launch_kda_decode(const KdaArgs& a, hipStream_t s);
+// KDA over a chunk of n_tokens consecutive tokens per sequence (prefill): the same
+// recurrence as n_tokens decode steps.  x* [batch, n_tokens, heads * 128] bf16,
+// alpha [batch, n_tokens, heads, 128], beta [batch, n_tokens, heads], out
+// [batch, n_tokens, heads, 128]; conv and state as in KdaArgs.
+struct KdaChunkArgs {
+  int batch, heads, n_tokens;
+  const uint16_t* xq;
+  const uint16_t* xk;
+  const uint16_t* xv;
+  const float* alpha;
+  const float* beta;
+  const float* conv_w;
+  const float* conv_in;
+  float* conv_out;
+  float* state;
+  float* out;
+};
+hipError_t launch_kda_chunk(const KdaChunkArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
 }  // namespace ip

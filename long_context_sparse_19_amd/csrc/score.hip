@@ -18,265 +18,22 @@
 // workgroup counts itself in on a per-row counter once its scores are stored, and
 // the one that completes the count selects the row (select.hpp) and clears the
 // counter for the next call.
-#include "append.hpp"
-#include "select.hpp"
+#include "score_fp8.hpp"
 
 namespace ip {
 
 namespace {
 
+using scorek::row16_max;
 constexpr int NT = 256;                         // f32 kernel; prefill fp8 workgroups
-constexpr int TILES = 4;                        // 32-key tiles per wave
-constexpr int HI = 32, DI = 128;
+constexpr int TILES = scorek::TILES;
 
-struct QStage {
-  static constexpr int QROW = DI + 8;           // padded LDS row (272 bytes): conflict-free reads
-  uint16_t qs[2][HI * QROW];                    // double-buffered query rows
-  float gs[2][HI];
-};
-
-// the largest of the 16 values of this lane's 16-lane row (DPP within rows)
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_f<0xB1>(-INFINITY, x));      // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp_f<0x4E>(-INFINITY, x));      // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_f<0x141>(-INFINITY, x));     // row_half_mirror
-  x = fmaxf(x, dpp_f<0x140>(-INFINITY, x));     // row_mirror
-  return x;
-}
-
-template <int NWV, bool FUSE>
-constexpr size_t score_smem() {
-  return FUSE && sizeof(sel::Shared<NWV * 64>) > sizeof(QStage) ? sizeof(sel::Shared<NWV * 64>) : sizeof(QStage);
-}
-
-// RPW query rows share one key chunk held in registers (prefill, where consecutive
-// rows are tokens of one sequence); decode rows are separate sequences and use 1.
-// A workgroup of NWV waves covers NWV * 128 keys.  All key loads of a wave are
-// issued before the first MFMA: decode launches use 8 waves (1024 keys, 132 KB of
-// pooled rows in flight per workgroup) so that one workgroup per compute unit
-// covers the whole batch of the 128K-token decode workload at once.
 template <int RPW, int NWV, bool FUSE>
 __global__ __launch_bounds__(NWV * 64) void score_fp8_bf16_kernel(ScoreArgs a) {
-  static_assert(!FUSE || RPW == 1, "the fused selection handles one row per workgroup");
-  constexpr int NTW = NWV * 64;
-  constexpr int KEYS = NWV * TILES * 32;
-  static_assert(SCORE_TILE % KEYS == 0, "score rows pad to whole workgroup tiles");
-  constexpr int QROW = QStage::QROW;
   // the query stage, and (fused) the selection's state once scoring is done
-  __shared__ __align__(16) uint8_t smem[score_smem<NWV, FUSE>()];
+  __shared__ __align__(16) uint8_t smem[scorek::score_smem<NWV, FUSE>()];
   __shared__ int last_here;
-  QStage& st = *reinterpret_cast<QStage*>(smem);
-  auto& qs = st.qs;
-  auto& gs = st.gs;
-  if (a.with_append && (int)blockIdx.y >= a.n_rows) {
-    // the fused decode append, one sequence per workgroup of the extra grid rows:
-    // scoring reads pooled rows of blocks before the query's own block only, and
-    // the append writes the new token's rows and the pooled row of the block it
-    // completes (the query's own block)
-    const int b = ((int)blockIdx.y - a.n_rows) * (int)gridDim.x + (int)blockIdx.x;
-    if (b < a.append.batch) append_one<NTW>(a.append, b);
-    return;
-  }
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int kl = lane & 31, hh = lane >> 5;
-  const int kc0 = blockIdx.x * KEYS;
-  const int rbeg = a.row0 + blockIdx.y * RPW;
-  const int rend = min(rbeg + RPW, a.row0 + a.n_rows);
-
-  // query rows (8 KB) and gates go through LDS; row r+1's are loaded while row r
-  // is computed, and staged in the other buffer, so one barrier per row suffices
-  // and the load latency of a row is hidden behind the previous one.  Thread t
-  // (t < 256) holds elements 16t .. 16t+15 = head t/8, dims (t%8)*16 ..
-  const bool qt = threadIdx.x < 256;
-  u32x4_t qv0, qv1;
-  float gv = 0.f;
-  auto load_q = [&](int r) {
-    const u32x4_t* qg = (const u32x4_t*)((const uint16_t*)a.q + (int64_t)r * HI * DI);
-    if (qt) {
-      qv0 = qg[2 * threadIdx.x];
-      qv1 = qg[2 * threadIdx.x + 1];
-    }
-    if (threadIdx.x < HI) gv = a.gates[(int64_t)r * HI + threadIdx.x];
-  };
-  auto stage_q = [&](int buf) {
-    const int h = threadIdx.x >> 3, d = (threadIdx.x & 7) * 16;
-    if (qt) {
-      *(u32x4_t*)(qs[buf] + h * QROW + d) = qv0;
-      *(u32x4_t*)(qs[buf] + h * QROW + d + 8) = qv1;
-    }
-    if (threadIdx.x < HI) gs[buf][threadIdx.x] = gv;
-  };
-  // per-row sequence, position and pooled-row count, one row per lane, read once
-  // (per-row loads inside the loop would each wait for every load in flight)
-  int rb = 0, rp = 0, rn = 1;
-  if (lane < rend - rbeg) {
-    const int rr = rbeg + lane;
-    rb = a.q_seq ? a.q_seq[rr] : rr;
-    const int len = a.L.seq_lens[rb];
-    rp = a.q_pos ? a.q_pos[rr] : len - 1;
-    rn = (len + 3) >> 2;
-  }
-  load_q(rbeg);
-  stage_q(0);
-  if (rbeg + 1 < rend) load_q(rbeg + 1);
-
-  bf16x8_t kf[TILES][8];
-  float ksig[TILES];
-  float scv[TILES];                             // this lane's scores of the last row (all tiles)
-  float gmv[TILES];                             // and their group maxima
-  int cur_b = -1;
-
-  for (int r = rbeg, i = 0; r < rend; ++r, ++i) {
-    // row r's query is visible in buffer i&1, and every wave is done with buffer
-    // (i+1)&1 (read in row r-1); LDS-only barrier: loads in flight are not waited for
-    block_sync_lds();
-    const int b = __builtin_amdgcn_readlane(rb, i);
-    const int p = __builtin_amdgcn_readlane(rp, i);
-    const int nel = p >> 2;                    // eligible blocks j < b_q
-    const bool run = kc0 < nel;                // uniform over the workgroup
-    if (run && b != cur_b) {
-      cur_b = b;
-      // pooled rows that exist; keys past them are clamped to the last one (their
-      // scores are never written), so every load is unconditional and all of a
-      // wave's loads are in flight together
-      const int nrows = __builtin_amdgcn_readlane(rn, i);
-      u32x4_t raw[TILES][4];
-#pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        const int j = min(kc0 + (wv * TILES + t) * 32 + kl, nrows - 1);
-        const int64_t row = a.L.pool_row(b, j);
-        const u32x4_t* src = (const u32x4_t*)(a.keys + row * a.key_stride + hh * 64);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) raw[t][c] = src[c];
-        ksig[t] = a.key_scale[row];
-      }
-#pragma unroll
-      for (int t = 0; t < TILES; ++t)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          kf[t][2 * c] = fp8x8_to_bf16x8(raw[t][c][0], raw[t][c][1]);
-          kf[t][2 * c + 1] = fp8x8_to_bf16x8(raw[t][c][2], raw[t][c][3]);
-        }
-      // the scales land here too, so that no later use of them waits for the
-      // query prefetch issued after this point
-#pragma unroll
-      for (int t = 0; t < TILES; ++t) asm volatile("" ::"v"(ksig[t]));
-    }
-    const uint16_t* qb = qs[i & 1];
-    const float* gb = gs[i & 1];
-    // query fragment: head kl, dims hh*64 .. hh*64+63 (the same dims as the key half)
-    bf16x8_t qf[8];
-    // gates of the 16 heads this lane accumulates: rows (i/4)*8 + hh*4 + i%4
-    float g[16];
-    if (run) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) qf[c] = *(const bf16x8_t*)(qb + kl * QROW + hh * 64 + c * 8);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) g[e] = gb[(e >> 2) * 8 + hh * 4 + (e & 3)];
-    }
-    // stage row r+1 and fetch row r+2.  Staging waits for row r+1's loads, issued
-    // one row ago, and for whatever followed them (row r-1's score stores): both
-    // have had a row's time to finish.
-    if (r + 1 < rend) {
-      stage_q((i + 1) & 1);
-      if (r + 2 < rend) load_q(r + 2);
-    }
-    if (!run) continue;
-
-    float* srow = a.scores + (int64_t)(r - a.row0) * a.ld;
-    float* grow = a.gm + (int64_t)(r - a.row0) * a.gld;
-#pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      f32x16_t acc = {};
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[c], kf[t][c], acc, 0, 0, 0);
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) part = fmaf(g[e], fmaxf(acc[e], 0.f), part);
-      part += __shfl_xor(part, 32);
-      const int j = kc0 + (wv * TILES + t) * 32 + kl;
-      const float sc = j < nel ? part * ksig[t] : -INFINITY;
-      scv[t] = sc;
-      // the maximum of each group of 16 consecutive blocks: lanes kl 0..15 and
-      // 16..31 of the tile are 16-lane rows
-      const float gmax = row16_max(sc);
-      gmv[t] = gmax;
-      // fused: stored after the wave's list (see below), so that building the list
-      // does not wait for these stores
-      if (!FUSE && hh == 0 && j < nel) {
-        srow[j] = sc;
-        if ((kl & 15) == 0) grow[j >> 4] = gmax;
-      }
-    }
-  }
-  if constexpr (FUSE) {
-    // one row: select it once every workgroup that scored it has stored its part
-    const int r = rbeg;
-    const int p = __builtin_amdgcn_readlane(rp, 0);
-    const int nel = p >> 2;
-    const int need = min(a.top_k, nel + 1) - 1;
-    int32_t* out = a.out + (int64_t)r * a.top_k;
-    sel::Shared<NTW>& ss = *reinterpret_cast<sel::Shared<NTW>*>(smem);
-    const bool trivial = need == 0 || need >= nel;   // nothing to rank: the own block alone, or every block
-    const int n_run = (nel + KEYS - 1) / KEYS;
-    const int n_lists = n_run * NWV;
-    // rows long enough for about 2 winners per wave: every wave lists its best
-    // (see sel::wave_list) and the last workgroup merges the lists
-    const bool lists = !trivial && a.lists && n_lists * sel::LIST <= sel::C_CAP && n_lists <= NTW &&
-                       need <= 2 * n_lists;
-    uint64_t* lrow = lists ? a.lists + (int64_t)(r - a.row0) * a.max_lists * sel::LIST : nullptr;
-    uint2* mrow = lists ? a.lists_meta + (int64_t)(r - a.row0) * a.max_lists : nullptr;
-    if (kc0 < nel) {
-      const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hh = lane >> 5, kl = lane & 31;
-      if (lists) {
-        uint32_t k[2];
-        int id[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int t = 2 * hh + i;
-          id[i] = kc0 + (wv * TILES + t) * 32 + kl;
-          k[i] = id[i] < nel ? float_key(scv[t]) : 0u;
-        }
-        const int slot = blockIdx.x * NWV + wv;
-        sel::wave_list<4>(k, id, lrow + (int64_t)slot * sel::LIST, mrow + slot);
-      }
-      // the scores and group maxima (read by the exact fallback, and the caller's
-      // score output), after the list so that building it does not wait for them
-      float* srow = a.scores + (int64_t)(r - a.row0) * a.ld;
-      float* grow = a.gm + (int64_t)(r - a.row0) * a.gld;
-#pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        const int j = kc0 + (wv * TILES + t) * 32 + kl;
-        if (hh == 0 && j < nel) {
-          sel::st_agent(srow + j, scv[t]);
-          if ((kl & 15) == 0) sel::st_agent(grow + (j >> 4), gmv[t]);
-        }
-      }
-    }
-    if (trivial) {
-      if (blockIdx.x == 0) {
-        __syncthreads();
-        sel::select_row<NTW>(nullptr, nullptr, nel, nel, a.top_k, out, ss);
-      }
-      return;
-    }
-    if (kc0 >= nel) return;                      // this workgroup scored nothing
-    // every score, maximum and list entry of this workgroup is stored (acknowledged
-    // by memory) before it counts itself in: the stores are device-coherent, so the
-    // workgroup that completes the count reads them with device-coherent loads
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
-    if (threadIdx.x == 0) last_here = atomicAdd(a.count + (r - a.row0), 1) == n_run - 1;
-    __syncthreads();
-    if (!last_here) return;
-    if (threadIdx.x == 0) sel::st_agent(a.count + (r - a.row0), 0);   // clear for the next call
-    if (lists && sel::merge_lists<NTW>(lrow, mrow, n_lists, need, nel, a.top_k, out, ss)) return;
-    __syncthreads();
-    sel::select_row<NTW>(a.scores + (int64_t)(r - a.row0) * a.ld, a.gm + (int64_t)(r - a.row0) * a.gld, nel,
-                         nel, a.top_k, out, ss);
-  }
+  scorek::score_fp8_body<RPW, NWV, FUSE>(a, blockIdx.x, blockIdx.y, gridDim.x, smem, last_here, nullptr);
 }
 
 // float keys and queries (small geometries): one thread per key, queries in LDS.

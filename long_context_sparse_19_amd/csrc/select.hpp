@@ -29,7 +29,9 @@
 //
 // Scores and group maxima written by other workgroups of the same kernel are read
 // with device-coherent loads (they bypass this die's L2, which may not have seen
-// them); data written by an earlier kernel reads the same way.
+// them); data written by an earlier kernel reads the same way.  The selected ids
+// are stored device-coherently too, so that a consumer in the same launch (the
+// fused decode step's attention) can read them once the row is published.
 #pragma once
 #include "kernels.hpp"
 
@@ -319,7 +321,7 @@ __device__ __forceinline__ bool keep_best_regs(const uint32_t (&key)[E], const i
   const int off = wave_base(kept_w, sh, 0, all);
 #pragma unroll
   for (int i = 0; i < E; ++i)
-    if (k[i]) out[off + pos[i]] = cid[i];
+    if (k[i]) st_agent(out + off + pos[i], cid[i]);
   return true;
 }
 
@@ -406,11 +408,11 @@ __device__ __noinline__ void radix_row(const float* S, int nel, int need, int bq
     int off = done + x_scan(nk, 0, sh, par ^ 1, &kt, &unused);
 #pragma unroll
     for (int e = 0; e < RE; ++e)
-      if ((km >> e) & 1u) out[off++] = base + t0 + e;
+      if ((km >> e) & 1u) st_agent(out + off++, (int32_t)(base + t0 + e));
     done += kt;
     ties += tt;
   }
-  for (int i = need + threadIdx.x; i < top_k; i += NT) out[i] = i == need ? bq : -1;
+  for (int i = need + threadIdx.x; i < top_k; i += NT) st_agent(out + i, i == need ? bq : -1);
 }
 
 // One tile of the bound's source V: wave w holds V [t0 + w 64 VB, + 64 VB), lane l
@@ -479,7 +481,7 @@ __device__ __noinline__ void select_row(const float* S, const float* GM, int nel
   const int need = min(top_k, bq + 1) - 1;
   if (need == 0 || need >= nel) {
     // the own block alone, or every eligible block (need == nel)
-    for (int i = threadIdx.x; i < top_k; i += NT) out[i] = i < need ? i : (i == need ? bq : -1);
+    for (int i = threadIdx.x; i < top_k; i += NT) st_agent(out + i, i < need ? i : (i == need ? bq : -1));
     return;
   }
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -598,13 +600,13 @@ __device__ __noinline__ void select_row(const float* S, const float* GM, int nel
   if (M > need) {
     keep_best<NT>(M, need, out, sh);
   } else {
-    for (int i = threadIdx.x; i < need; i += NT) out[i] = sh.cid[i];
+    for (int i = threadIdx.x; i < need; i += NT) st_agent(out + i, sh.cid[i]);
   }
-  for (int i = need + threadIdx.x; i < top_k; i += NT) out[i] = i == need ? bq : -1;
+  for (int i = need + threadIdx.x; i < top_k; i += NT) st_agent(out + i, i == need ? bq : -1);
 }
 
 // ---------------------------------------------------------------- per-wave lists
-// A scoring wave of 128 consecutive blocks writes the blocks whose keys reach its
+// A scoring wave of 64 KPL consecutive blocks writes the blocks whose keys reach its
 // own threshold L (its 16th largest key, found bit by bit with ballots): at most
 // LIST entries (key | id << 32) in ascending id, with (count, L') where L' = L, or
 // L + 1 when ties at L did not all fit (the list then holds every key > L).  The
@@ -613,13 +615,22 @@ __device__ __noinline__ void select_row(const float* S, const float* GM, int nel
 // at least every L' -- which the merge checks.
 constexpr int LIST = 16;
 
-// The wave's list from its two keys per lane (key 0 = none): k[0] covers blocks
-// id0[0] (lanes 0..31) then id0[1] (lanes 32..63) ... see the caller; returns the
-// count; the entries go to `dst` [0, count) in the order (segment, lane).
-template <int NSEG>
-__device__ __forceinline__ void wave_list(const uint32_t (&k)[2], const int (&id)[2], uint64_t* dst, uint2* meta) {
+// number of lanes whose key k[i] passes `pred`, over the KPL keys of each lane
+template <int KPL, class P>
+__device__ __forceinline__ int wave_count(const uint32_t (&k)[KPL], P pred) {
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) c += __popcll(__ballot(pred(k[i])));
+  return c;
+}
+
+// The wave's list from its KPL keys per lane (key 0 = none).  Ids ascend over the
+// segments (half, i): lanes 0..31 hold the lower half, k[i] before k[i + 1].
+// The entries go to `dst` [0, count) in that order, (count, L') to `meta`.
+template <int KPL>
+__device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&id)[KPL], uint64_t* dst, uint2* meta) {
   const int lane = threadIdx.x & 63;
-  int valid = __popcll(__ballot(k[0] != 0)) + __popcll(__ballot(k[1] != 0));
+  const int valid = wave_count<KPL>(k, [](uint32_t x) { return x != 0u; });
   uint32_t T = 0;
   if (valid > LIST) {
     // the largest T with count(keys >= T) >= LIST.  T lies between the wave's
@@ -627,8 +638,14 @@ __device__ __forceinline__ void wave_list(const uint32_t (&k)[2], const int (&id
     // differing bit; the bits below are found two at a time (three trial counts per
     // step, independent of each other).  Stop once the count is exactly LIST (the
     // set is then the wave's LIST best).
-    const uint32_t kmx = wave_umax(max(k[0], k[1]));
-    const uint32_t kmn = wave_umin(min(k[0] ? k[0] : 0xFFFFFFFFu, k[1] ? k[1] : 0xFFFFFFFFu));
+    uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      mx = max(mx, k[i]);
+      mn = min(mn, k[i] ? k[i] : 0xFFFFFFFFu);
+    }
+    const uint32_t kmx = wave_umax(mx);
+    const uint32_t kmn = wave_umin(mn);
     const uint32_t diff = kmx ^ kmn;
     int b = diff ? 31 - __clz((int)diff) : -1;    // highest differing bit
     T = diff ? kmx & ~((2u << b) - 1u) : kmx;      // the shared prefix (b == 31: none)
@@ -636,35 +653,33 @@ __device__ __forceinline__ void wave_list(const uint32_t (&k)[2], const int (&id
 #pragma unroll 1
     for (; b >= 1; b -= 2) {
       const uint32_t t1 = T | (1u << (b - 1)), t2 = T | (2u << (b - 1)), t3 = T | (3u << (b - 1));
-      const int c1 = __popcll(__ballot(k[0] >= t1)) + __popcll(__ballot(k[1] >= t1));
-      const int c2 = __popcll(__ballot(k[0] >= t2)) + __popcll(__ballot(k[1] >= t2));
-      const int c3 = __popcll(__ballot(k[0] >= t3)) + __popcll(__ballot(k[1] >= t3));
+      const int c1 = wave_count<KPL>(k, [=](uint32_t x) { return x >= t1; });
+      const int c2 = wave_count<KPL>(k, [=](uint32_t x) { return x >= t2; });
+      const int c3 = wave_count<KPL>(k, [=](uint32_t x) { return x >= t3; });
       const int c = c3 >= LIST ? c3 : (c2 >= LIST ? c2 : c1);
       T = c3 >= LIST ? t3 : (c2 >= LIST ? t2 : (c1 >= LIST ? t1 : T));
       if (c == LIST) { b = -1; break; }
     }
     if (b == 0) {
       const uint32_t t1 = T | 1u;
-      if (__popcll(__ballot(k[0] >= t1)) + __popcll(__ballot(k[1] >= t1)) >= LIST) T = t1;
+      if (wave_count<KPL>(k, [=](uint32_t x) { return x >= t1; }) >= LIST) T = t1;
     }
   }
   // keys > T all fit; ties at T fill up to LIST in id order
-  const int gt = __popcll(__ballot(k[0] > T && k[0])) + __popcll(__ballot(k[1] > T && k[1]));
+  const int gt = wave_count<KPL>(k, [=](uint32_t x) { return x > T && x; });
   const int room = LIST - gt;
-  // id order: segment 0 = k[0] on lanes 0..31, 1 = k[1] on lanes 0..31,
-  // 2 = k[0] on lanes 32..63, 3 = k[1] on lanes 32..63
   int n = 0, ties = 0;
 #pragma unroll
-  for (int sgm = 0; sgm < 4; ++sgm) {
-    const bool mine = (lane >> 5) == (sgm >> 1);
-    const uint32_t kk = k[sgm & 1];
+  for (int sgm = 0; sgm < 2 * KPL; ++sgm) {
+    const bool mine = (lane >> 5) == sgm / KPL;
+    const uint32_t kk = k[sgm % KPL];
     const bool tie = mine && kk && kk == T && T;
     const uint64_t mt = __ballot(tie);
     const int trank = ties + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mt, 0u));
     const bool keep = mine && kk && (kk > T || (kk == T && (T == 0 || trank < room)));
     const uint64_t mk = __ballot(keep);
     const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-    if (keep && pos < LIST) st_agent(dst + pos, (uint64_t)kk | ((uint64_t)(uint32_t)id[sgm & 1] << 32));
+    if (keep && pos < LIST) st_agent(dst + pos, (uint64_t)kk | ((uint64_t)(uint32_t)id[sgm % KPL] << 32));
     n += __popcll(mk);
     ties += __popcll(mt);
   }
@@ -732,7 +747,7 @@ __device__ __noinline__ bool merge_lists(const uint64_t* lists, const uint2* met
   }
   if (total <= need) return false;
   if (!keep_best_regs<NT, E>(key, cid, need, out, sh, limit, kmin, kmax)) return false;
-  for (int i = need + threadIdx.x; i < top_k; i += NT) out[i] = i == need ? bq : -1;
+  for (int i = need + threadIdx.x; i < top_k; i += NT) st_agent(out + i, i == need ? bq : -1);
   return true;
 }
 

@@ -141,6 +141,11 @@ class FollowerWorkspaces:
         self.ws_attn = torch.empty(max(na, 16), dtype=torch.uint8, device=dev)
         self.out = torch.empty((d.n_q, d.q.shape[1], d.dv), dtype=d.q.dtype, device=dev)
         self.lse = torch.empty((d.n_q, d.q.shape[1]), dtype=torch.float32, device=dev)
+        # the whole decode step's workspace (indexer, attention, ready words), zero-filled
+        self.ws_step = None
+        if d.is_decode and d.keys is not None:
+            ns = _lib.indexpool_decode_step_workspace_bytes(d.seqs, d.top_k, d.q.shape[1], d.dv, qdt, keep_scores)
+            self.ws_step = torch.zeros(max(ns, 256), dtype=torch.uint8, device=dev)
 
 
 class Workspaces:
@@ -162,6 +167,11 @@ class Workspaces:
         self.ws_attn = torch.empty(max(na, 16), dtype=torch.uint8, device=dev)
         self.out = torch.empty((d.n_q, d.q.shape[1], d.dv), dtype=d.q.dtype, device=dev)
         self.lse = torch.empty((d.n_q, d.q.shape[1]), dtype=torch.float32, device=dev)
+        # the whole decode step's workspace (indexer, attention, ready words), zero-filled
+        self.ws_step = None
+        if d.is_decode and d.keys is not None:
+            ns = _lib.indexpool_decode_step_workspace_bytes(d.seqs, d.top_k, d.q.shape[1], d.dv, qdt, keep_scores)
+            self.ws_step = torch.zeros(max(ns, 256), dtype=torch.uint8, device=dev)
 
 
 def score_topk(d: DeviceInputs, ws: Workspaces, stream=None) -> None:
@@ -177,6 +187,14 @@ def decode_index(d: DeviceInputs, t: NewTokens, ws: Workspaces, stream=None) -> 
     _lib.indexpool_decode_index(d.seqs, t.kv_new, d.kv, t.key_new, d.keys, t.logit_new, d.logits, d.pooled,
                                 d.q_idx, d.gates, d.top_k, ws.sel, scores=ws.scores, ws=ws.ws_idx, v_new=t.v_new,
                                 v=d.v, stream=stream)
+
+
+def decode_step(d: DeviceInputs, t: NewTokens, ws: Workspaces, stream=None) -> None:
+    """decode_index(d, t, ws) then attention(d, ws), in one call (one launch plus the
+    split combine where the geometry allows)."""
+    _lib.indexpool_decode_step(d.seqs, t.kv_new, d.kv, t.key_new, d.keys, t.logit_new, d.logits, d.pooled,
+                               d.q_idx, d.gates, d.top_k, ws.sel, d.q, ws.out, d.scale, d.dv, lse=ws.lse,
+                               scores=ws.scores, ws=ws.ws_step, v_new=t.v_new, v=d.v, stream=stream)
 
 
 def attention(d: DeviceInputs, ws: Workspaces, sel: Optional[torch.Tensor] = None, stream=None) -> None:

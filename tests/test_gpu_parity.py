@@ -576,3 +576,84 @@ def test_decode_index_equals_append_then_score_topk(name):
                     [x for x in (d.kv.scale, d.keys.scale, d.pooled.scale) if x is not None])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- fused decode step
+STEP_CASES = {
+    # new tokens at every position of a block; short rows take the trivial selection
+    "decode_positions": (scaled_down(DECODE, 1024, batch=4), lambda L: L - np.arange(4)),
+    # rows long enough for the per-wave lists, two attention splits per row
+    "decode_lists": (scaled_down(DECODE, 4 * 30000 + 36, batch=3), lambda L: L - np.arange(3)),
+    "ragged_paged": (_RAGGED_SMALL, lambda L: L),
+    "decode_batch64": (scaled_down(DECODE, 4 * 600, batch=64), lambda L: L),
+    "decode_full": (DECODE, lambda L: L),
+    "max_ctx": (MAX_CTX, lambda L: L),
+    # geometries the one-launch step does not cover run the two calls
+    "fp8kv_positions": (scaled_down(DECODE_FP8KV, 1024, batch=4), lambda L: L - np.arange(4)),
+    "decode_batch128": (scaled_down(DECODE, 4 * 600, batch=128), lambda L: L),
+    "tiny_f32": (TINY, lambda L: L),
+}
+
+
+def _step_oracle_check(inp, d, ws, rows):
+    """The step's selection and attention against the oracle over the device's cache
+    state after the step (the append's own parity is checked elsewhere)."""
+    import dataclasses
+    lat = _bits(d.kv.data) if inp.latent is not None else None
+    inp2 = dataclasses.replace(inp, latent=lat) if lat is not None else inp
+    if inp.latent_scale is not None:
+        inp2 = dataclasses.replace(inp2, latent_scale=d.kv.scale.cpu().numpy())
+    if inp.k_cache is not None:
+        inp2 = dataclasses.replace(inp2, k_cache=d.kv.data.cpu().numpy(), v_cache=d.v.data.cpu().numpy())
+    if d.pooled.scale is not None:
+        vals = O.pooled_values(d.pooled.data.cpu().numpy(), d.pooled.scale.cpu().numpy().astype(np.float64))
+    else:
+        vals = d.pooled.data.cpu().numpy().astype(np.float64)
+    gsel = ws.sel.cpu().numpy()
+    o_ids = np.full((len(rows), d.top_k), -1, np.int32)
+    for n, r in enumerate(rows):
+        b, b_q = int(inp.q_seq[r]), int(inp.q_pos[r]) // 4
+        S = O.score(O._to_f64(inp.q_idx[r]), inp.gates[r], vals[O.pooled_rows(inp, b, np.arange(b_q))])
+        o_ids[n] = O.select(S, b_q, d.top_k)
+        P.check_selection(gsel[r], o_ids[n], S, b_q, d.top_k)
+    o_out, o_lse = O.attention_rows(inp2, o_ids, d.scale, d.dv, rows=rows)
+    kind = _kind(inp.w)
+    P.check_attention(_out_np(ws.out)[rows], o_out, kind)
+    P.check_lse(ws.lse.cpu().numpy()[rows], o_lse, kind)
+
+
+@pytest.mark.parametrize("name", list(STEP_CASES))
+def test_decode_step_equals_decode_index_then_attention(name):
+    """indexpool_decode_step gives the results of indexpool_decode_index followed by
+    sparse_attn_decode, bit for bit, on two calls in a row (the second checks that
+    the first left its ready words and counters cleared); and against the oracle."""
+    D = _dev()
+    w, lens = STEP_CASES[name]
+    inp = make_inputs(w)
+    inp.seq_lens = np.asarray(lens(inp.seq_lens), dtype=np.int32)
+    inp.q_pos = inp.seq_lens[inp.q_seq] - 1
+    log(f"[case] decode_step {name} B={w.batch} lens={inp.seq_lens[:4].tolist()} k={w.top_k}")
+    new = new_tokens(w, len(inp.seq_lens), seed=9)
+    res = {}
+    for mode in ("two_calls", "step"):
+        d = D.upload(inp)
+        D.compress(d)
+        ws = D.Workspaces(d, keep_scores=False)
+        t = D.NewTokens(new)
+        outs = []
+        for _ in range(2):
+            if mode == "step":
+                D.decode_step(d, t, ws)
+            else:
+                D.decode_index(d, t, ws)
+                D.attention(d, ws)
+            torch.cuda.synchronize()
+            outs.append([ws.sel.clone(), ws.out.clone(), ws.lse.clone()])
+        res[mode] = (outs, d, ws)
+    for call in range(2):
+        for a, b in zip(res["two_calls"][0][call], res["step"][0][call]):
+            assert torch.equal(a, b), f"call {call}: the step differs from the two calls"
+    _, d, ws = res["step"]
+    rows = np.unique(np.concatenate([np.arange(min(4, w.batch)), [w.batch - 1]]))
+    _step_oracle_check(inp, d, ws, rows)
+    log(f"  step == two calls (2 calls), oracle ok on rows {rows.tolist()}")
