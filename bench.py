@@ -127,12 +127,16 @@ def kernel_bytes(inp, w, ab, fused, step=False):
 
 def step_fused(w):
     """Whether indexpool_decode_step runs as one launch (plus the split combine) for
-    this workload: decode over fp8 indexer keys and a bf16 latent cache, with the
+    this workload: decode over fp8 indexer keys and a bf16 latent cache, rows short
+    enough for the selection's per-wave lists (fewer than 64 rows), with the
     attention split (the plan of sparse_attn_workspace_bytes) into splits of fewer
     than 128 blocks."""
     if not (w.mode == "decode" and w.idx_key_dtype == "fp8" and w.attn_dtype == "bf16" and not w.latent_fp8):
         return False
     n, k = w.batch, w.top_k
+    # the scoring's per-wave lists: 8 per 1024 blocks, at most 256 per row
+    if 8 * ((max(1, (w.seq_len - 1) // 4) + 1023) // 1024) > 256 or n >= 64:
+        return False
     nsub = (k + 15) // 16
     ns = max(1, min((128 + n - 1) // n, nsub, 64))
     bps = min((nsub + ns - 1) // ns, 32) * 16
@@ -384,7 +388,77 @@ def kda_main(args, kw):
                      "avg_ms": kt, "launches": K},
         "cpu_baseline": None if args.no_cpu_baseline else kda_cpu_baseline(kin, kw),
     }
-    print(json.dumps(line))
+    return line
+
+
+KDA_PREFILL_METRIC = "KDA prefill tokens/s (chunked gated delta rule, 64 heads x 128^2 fp32 state)"
+FP32_PEAK_TFLOPS = 157.3
+
+
+def kda_prefill_flops(kw):
+    """Algorithmic flops of a KDA prefill chunk: per (token, head) the recurrence's
+    three dense products with the 128 x 128 state (S'^T k, the rank-1 write, S^T q),
+    2 d^2 each."""
+    return 6 * kw.head_dim * kw.head_dim * kw.tokens * kw.heads * kw.batch
+
+
+def kda_prefill_main(args, kw):
+    """KDA prefill: every timed step runs the whole chunk (kda_prefill_chunk) on the
+    state in place."""
+    import numpy as np
+    import torch
+    from long_context_sparse_19_amd import _lib, device as D
+    from long_context_sparse_19_amd.inputs import kda_inputs
+    kin = kda_inputs(kw, kw.tokens)
+    d = D.KdaChunkDevice(kin)
+    torch.cuda.synchronize()
+    K = args.steps
+    for _ in range(args.warmup):
+        d.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        d.run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for e0, e1 in ev:
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    for i in range(K):
+        _lib.time_next_launch(_lib.K_KDA, *ev[i])
+        d.run()
+    torch.cuda.synchronize()
+    kt = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    fl = kda_prefill_flops(kw)
+    ach = fl / (kt * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import kda as Ko
+        from long_context_sparse_19_amd.inputs import bf16_bits_to_f32
+        n = min(kw.tokens, 256)
+        sw = lambda x: np.swapaxes(x[:n], 0, 1)
+        tc = time.perf_counter()
+        Ko.prefill_chunk(kin["state"], kin["conv_state"], sw(bf16_bits_to_f32(kin["xq"])), sw(bf16_bits_to_f32(kin["xk"])),
+                         sw(bf16_bits_to_f32(kin["xv"])), sw(kin["alpha"]), sw(kin["beta"]), kin["conv_w"])
+        dt = time.perf_counter() - tc
+        cpu = {"value": kw.batch * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "host_cores_available": len(os.sched_getaffinity(0)),
+               "sample": f"the first {n} tokens of the chunk, token by token (all {kw.heads} heads, float64), {dt:.1f} s"}
+    line = {
+        "metric": KDA_PREFILL_METRIC, "value": kw.batch * kw.tokens / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": kw.name, "batch": kw.batch, "tokens": kw.tokens, "heads": kw.heads,
+                   "head_dim": kw.head_dim, "state": "fp32", "launch": "eager", "parallelism": "single GPU"},
+        "algorithmic_flops_per_step": fl,
+        "kernels": {"kda_chunk": {"avg_ms": kt, "flops": fl, "TFLOPs": ach}},
+        "roofline": {"bound": "mfma", "kernel": "kda_chunk_kernel", "achieved": ach, "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": ach / FP32_PEAK_TFLOPS, "traffic": None, "avg_ms": kt, "launches": K},
+        "cpu_baseline": cpu,
+    }
+    return line
 
 
 def main():
@@ -410,7 +484,8 @@ def main():
         sys.exit(2)
 
     if args.workload in _KW:
-        kda_main(args, _KW[args.workload])
+        kw = _KW[args.workload]
+        print(json.dumps((kda_prefill_main if kw.tokens else kda_main)(args, kw)))
         return
 
     from long_context_sparse_19_amd.configs import WORKLOADS
@@ -424,6 +499,14 @@ def main():
             steps = max(3, min(args.steps, 10))
             r, _ = run_workload(WORKLOADS[name], steps, 2, 2 if name != "max_ctx" else 1, args.eager, with_cpu=False)
             extra[name] = r
+        # the KDA half of the hybrid layer: a decode step and a 4096-token prefill chunk
+        from long_context_sparse_19_amd.configs import KDA_WORKLOADS
+        for name, kw in KDA_WORKLOADS.items():
+            ka = argparse.Namespace(**{**vars(args), "steps": max(3, min(args.steps, 10)), "warmup": 2,
+                                       "no_cpu_baseline": True, "replicas": 0})
+            kl = (kda_prefill_main if kw.tokens else kda_main)(ka, kw)
+            extra[name] = {"workload": name, "ms_per_step": kl["ms_per_step"], "value": kl["value"], "unit": kl["unit"],
+                           "roofline": kl["roofline"], "kernels": kl["kernels"], "steps": kl["steps"]}
         line["configs"] = extra
     print(json.dumps(line))
 

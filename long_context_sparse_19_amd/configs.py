@@ -109,17 +109,21 @@ WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, MAX_CTX, RAGGED, DECODE_
 
 @dataclass(frozen=True)
 class KdaWorkload:
-    """A decode step of the linear-attention (KDA) half: 64 heads of width 128 (a
-    128 x 128 fp32 state per head), short convolution of width 4."""
+    """The linear-attention (KDA) half: 64 heads of width 128 (a 128 x 128 fp32 state
+    per head), short convolution of width 4.  tokens = 0: one decode step per
+    sequence; tokens > 0: a prefill chunk of that many tokens per sequence."""
     name: str
     batch: int
     heads: int = 64
     head_dim: int = 128
     seed: int = 7
+    tokens: int = 0
 
 
 KDA_DECODE = KdaWorkload("kda_decode", batch=8)
-KDA_WORKLOADS = {KDA_DECODE.name: KDA_DECODE}
+# a 4096-token prefill chunk of one sequence (the chunked form)
+KDA_PREFILL = KdaWorkload("kda_prefill", batch=1, tokens=4096, seed=8)
+KDA_WORKLOADS = {KDA_DECODE.name: KDA_DECODE, KDA_PREFILL.name: KDA_PREFILL}
 
 
 def scaled_down(w: Workload, seq_len: int, batch: Optional[int] = None,

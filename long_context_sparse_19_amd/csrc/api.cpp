@@ -636,9 +636,11 @@ ip_status indexpool_decode_step(const ip_seqs* seqs, const void* kv_new, const i
   if (ip_status st = attn_build(fn, seqs, B, nullptr, nullptr, q, q_dtype, n_heads, dk, dv, scale, kv, v, out_idx,
                                 top_k, out, lse, plan.attn_bytes ? ws_att : nullptr, plan.attn_bytes, a, kind))
     return st;
-  // one launch when the selection is fused into the scoring (FP8 keys, every row
-  // in one pass) and the attention is the split bf16 latent kernel
-  if (kind == ATTN_BF16 && pooled->dtype == IP_FP8_E4M3FN && plan.score.rows_per_pass >= B &&
+  // one launch when the selection is fused into the scoring (FP8 keys, every row in
+  // one pass, rows short enough for the per-wave lists: the merge of one workgroup
+  // of 4 waves is slower than the standalone scoring's 8-wave selection otherwise)
+  // and the attention is the split bf16 latent kernel
+  if (kind == ATTN_BF16 && pooled->dtype == IP_FP8_E4M3FN && plan.score.rows_per_pass >= B && plan.score.max_lists > 0 &&
       ((uintptr_t)kv_new & 15) == 0 && app.kv_row_bytes >= ip::LAT_DK * 2) {
     ip::StepArgs st;
     st.score = score_args(seqs, plan.score, 0, B, nullptr, nullptr, q_idx, idx_heads, idx_dim, gates, pooled, top_k,

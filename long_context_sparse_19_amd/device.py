@@ -237,3 +237,27 @@ class KdaDevice:
                              stream=stream)
         if alternate:
             self.parity = 1 - self.parity
+
+
+class KdaChunkDevice:
+    """Device copies of the inputs of one KDA prefill chunk of T tokens (from
+    inputs.kda_inputs with steps = T, token-major there, sequence-major here)."""
+
+    def __init__(self, kin: dict, device="cuda"):
+        tr = lambda x: np.ascontiguousarray(np.swapaxes(x, 0, 1))
+        self.xq = _dev(tr(kin["xq"]), device, torch.bfloat16)
+        self.xk = _dev(tr(kin["xk"]), device, torch.bfloat16)
+        self.xv = _dev(tr(kin["xv"]), device, torch.bfloat16)
+        self.alpha = _dev(tr(kin["alpha"]), device)
+        self.beta = _dev(tr(kin["beta"]), device)
+        self.conv_w = _dev(kin["conv_w"], device)
+        self.conv_in = _dev(kin["conv_state"], device)
+        self.conv_out = torch.empty_like(self.conv_in)
+        self.state = _dev(kin["state"], device)
+        B, T = self.xq.shape[0], self.xq.shape[1]
+        H, d = self.state.shape[1], self.state.shape[3]
+        self.out = torch.empty((B, T, H, d), dtype=torch.float32, device=device)
+
+    def run(self, stream=None) -> None:
+        _lib.kda_prefill_chunk(self.xq, self.xk, self.xv, self.alpha, self.beta, self.conv_w, self.conv_in,
+                               self.conv_out, self.state, self.out, stream=stream)

@@ -96,3 +96,18 @@ def decode_step(state, conv_state, xq, xk, xv, alpha, beta, conv_w):
         for h in range(H):
             S_out[b, h], o[b, h] = delta_step(state[b, h], q[h], k[h], v[h], alpha[b, h], float(beta[b, h]))
     return S_out, cs_out, o
+
+
+def prefill_chunk(state, conv_state, xq, xk, xv, alpha, beta, conv_w):
+    """The reference of the chunked (prefill) form: the recurrence of decode_step run
+    token by token over a chunk of T tokens.  xq, xk [B, T, H*dk], xv [B, T, H*dv]
+    (float values), alpha [B, T, H, dk], beta [B, T, H]; state and conv_state as for
+    decode_step.  Returns (state, conv state, o [B, T, H, dv])."""
+    S, cs = np.asarray(state, dtype=F64), np.asarray(conv_state, dtype=F64)
+    T = np.shape(xq)[1]
+    outs = []
+    for t in range(T):
+        S, cs, o = decode_step(S, cs, xq[:, t], xk[:, t], xv[:, t], alpha[:, t], beta[:, t], conv_w)
+        outs.append(o)
+    B, H, _, dv = S.shape
+    return S, cs, (np.stack(outs, axis=1) if outs else np.zeros((B, 0, H, dv)))

@@ -75,3 +75,84 @@ def test_kda_identity_gates_leave_the_state_unchanged():
     assert torch.equal(d.state, S0)
     _, _, outs = _oracle_steps(kin, 1)
     _close(d.out.cpu().numpy(), outs[0], "out")
+
+
+# ---------------------------------------------------------------- chunked (prefill) form
+def _f32(bits):
+    return bf16_bits_to_f32(bits)
+
+
+def _oracle_chunk(kin):
+    """oracle.kda.prefill_chunk on the token-major inputs of kda_inputs(kw, T)."""
+    sw = lambda x: np.swapaxes(x, 0, 1)
+    return K.prefill_chunk(kin["state"], kin["conv_state"], sw(_f32(kin["xq"])), sw(_f32(kin["xk"])),
+                           sw(_f32(kin["xv"])), sw(kin["alpha"]), sw(kin["beta"]), kin["conv_w"])
+
+
+def _check_chunk(d, S, cs, o, what):
+    _close(d.out.cpu().numpy(), o, f"{what}: out")
+    err = _close(d.state.cpu().numpy(), S, f"{what}: state")
+    # the taps only move bf16 inputs: exact
+    assert np.array_equal(d.conv_out.cpu().numpy(), cs.astype(np.float32)), f"{what}: conv taps"
+    return err
+
+
+@pytest.mark.parametrize("kw", [KdaWorkload("kda_chunk_ragged", batch=2, heads=3, seed=11, tokens=37),
+                                KdaWorkload("kda_chunk_one_block", batch=3, heads=2, seed=12, tokens=16),
+                                KdaWorkload("kda_chunk_two_tokens", batch=2, heads=2, seed=13, tokens=2),
+                                KdaWorkload("kda_chunk_prefill_4096", batch=1, heads=64, seed=8, tokens=4096)],
+                         ids=["ragged_37", "one_block", "two_tokens", "full_4096"])
+def test_kda_prefill_chunk_parity(kw):
+    """kda_prefill_chunk against the token-by-token recurrence of the oracle."""
+    from long_context_sparse_19_amd import device as D
+    log(f"[case] kda chunk {kw.name} B={kw.batch} H={kw.heads} T={kw.tokens}")
+    kin = kda_inputs(kw, kw.tokens)
+    d = D.KdaChunkDevice(kin)
+    d.run()
+    torch.cuda.synchronize()
+    S, cs, o = _oracle_chunk(kin)
+    err = _check_chunk(d, S, cs, o, kw.name)
+    log(f"  kda chunk ok (state max-abs {err:.2e})")
+
+
+def test_kda_prefill_chunk_extreme_decay():
+    """Gates small enough that the cumulative decay inside a 16-token block leaves
+    fp32's range: the block coefficients are summed term by term."""
+    from long_context_sparse_19_amd import device as D
+    kw = KdaWorkload("kda_chunk_extreme", batch=1, heads=2, seed=14, tokens=40)
+    kin = kda_inputs(kw, kw.tokens)
+    kin["alpha"][:, :, :, :5] = 1e-3          # e^(16 log 1e-3) ~ 1e-48 on channels 0..4
+    kin["alpha"][5:9, :, 1, 7] = 1e-30
+    d = D.KdaChunkDevice(kin)
+    d.run()
+    torch.cuda.synchronize()
+    S, cs, o = _oracle_chunk(kin)
+    _check_chunk(d, S, cs, o, kw.name)
+
+
+def test_kda_prefill_chunk_equals_decode_steps_and_empty_chunk():
+    """T decode steps on the device and one chunk of T tokens agree (to fp32
+    rounding); a chunk of 0 tokens copies the taps and keeps the state."""
+    from long_context_sparse_19_amd import device as D
+    kw = KdaWorkload("kda_chunk_vs_steps", batch=2, heads=4, seed=15, tokens=21)
+    kin = kda_inputs(kw, kw.tokens)
+    dc = D.KdaChunkDevice(kin)
+    dc.run()
+    ds = D.KdaDevice(kin)
+    outs = []
+    for t in range(kw.tokens):
+        ds.step(t)
+        outs.append(ds.out.clone())
+    torch.cuda.synchronize()
+    o_steps = torch.stack(outs, dim=1).cpu().numpy().astype(np.float64)
+    _close(dc.out.cpu().numpy(), o_steps, "chunk vs steps: out")
+    _close(dc.state.cpu().numpy(), ds.state.cpu().numpy().astype(np.float64), "chunk vs steps: state")
+    assert np.array_equal(dc.conv_out.cpu().numpy(), ds.conv_state.cpu().numpy())
+    kin0 = kda_inputs(KdaWorkload("kda_chunk_empty", batch=2, heads=2, seed=16, tokens=0), 1)
+    kin0 = {k: (v[:0] if k in ("xq", "xk", "xv", "alpha", "beta") else v) for k, v in kin0.items()}
+    d0 = D.KdaChunkDevice(kin0)
+    S0 = d0.state.clone()
+    d0.run()
+    torch.cuda.synchronize()
+    assert torch.equal(d0.state, S0)
+    assert torch.equal(d0.conv_out, d0.conv_in)

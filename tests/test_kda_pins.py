@@ -101,3 +101,27 @@ def test_decode_step_wiring_closed_form():
     yq, yk, yv = rng.standard_normal((3, B, H * d))
     S2, _, o2 = K.decode_step(np.zeros((B, H, d, d)), cs, yq, yk, yv, np.ones((B, H, d)), np.ones((B, H)), w2)
     np.testing.assert_allclose(S2[1, 2], np.outer(K.l2norm(K.silu(xk[1, 2 * d:])), K.silu(xv[1, 2 * d:])), atol=1e-14)
+
+
+def test_prefill_chunk_is_the_token_recurrence():
+    """prefill_chunk over T tokens is T decode steps in order (state, taps and every
+    output), and a chunk of no tokens changes nothing."""
+    rng = np.random.default_rng(5)
+    B, H, d, T = 2, 2, 8, 5
+    S0 = rng.standard_normal((B, H, d, d))
+    cs0 = rng.standard_normal((B, 3, 3, H * d))
+    xq, xk, xv = (rng.standard_normal((B, T, H * d)) for _ in range(3))
+    al = rng.uniform(0.5, 1.0, (B, T, H, d))
+    be = rng.uniform(0.0, 1.0, (B, T, H))
+    w = rng.standard_normal((3, H * d, 4))
+    S, cs, o = K.prefill_chunk(S0, cs0, xq, xk, xv, al, be, w)
+    S2, cs2 = S0, cs0
+    for t in range(T):
+        S2, cs2, ot = K.decode_step(S2, cs2, xq[:, t], xk[:, t], xv[:, t], al[:, t], be[:, t], w)
+        np.testing.assert_array_equal(o[:, t], ot)
+    np.testing.assert_array_equal(S, S2)
+    np.testing.assert_array_equal(cs, cs2)
+    S3, cs3, o3 = K.prefill_chunk(S0, cs0, xq[:, :0], xk[:, :0], xv[:, :0], al[:, :0], be[:, :0], w)
+    assert o3.shape == (B, 0, H, d)
+    np.testing.assert_array_equal(S3, S0)
+    np.testing.assert_array_equal(cs3, cs0)
