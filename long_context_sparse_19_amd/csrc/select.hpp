@@ -693,10 +693,11 @@ __device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&
 // the need-th largest key of the union, or the union holds too few entries.  The
 // entries go straight from memory into the registers of keep_best_regs' layout.
 // Called after a barrier that frees `sh` (whose contents are arbitrary).
-template <int NT>
-__device__ __noinline__ bool merge_lists(const uint64_t* lists, const uint2* meta, int n_lists, int need, int bq,
-                                         int top_k, int32_t* out, Shared<NT>& sh) {
-  constexpr int NW = Shared<NT>::NW, E = C_CAP / NT;
+template <int NT, int E>
+__device__ __noinline__ bool merge_lists_e(const uint64_t* lists, const uint2* meta, int n_lists, int need, int bq,
+                                           int top_k, int32_t* out, Shared<NT>& sh) {
+  constexpr int NW = Shared<NT>::NW;
+  static_assert(E * NT <= C_CAP, "candidates fit the exchange buffers");
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   const int M = n_lists * LIST;
   const int per = (M + NW - 1) / NW;
@@ -749,6 +750,17 @@ __device__ __noinline__ bool merge_lists(const uint64_t* lists, const uint2* met
   if (!keep_best_regs<NT, E>(key, cid, need, out, sh, limit, kmin, kmax)) return false;
   for (int i = need + threadIdx.x; i < top_k; i += NT) st_agent(out + i, i == need ? bq : -1);
   return true;
+}
+
+// merge_lists_e with as few entries per thread as the lists need (8 for up to 8 NT
+// entries: the 4-wave step's 128 lists of a 128K-token row)
+template <int NT>
+__device__ __forceinline__ bool merge_lists(const uint64_t* lists, const uint2* meta, int n_lists, int need, int bq,
+                                            int top_k, int32_t* out, Shared<NT>& sh) {
+  constexpr int EMAX = C_CAP / NT, ESMALL = EMAX > 8 ? 8 : EMAX;
+  if (EMAX > ESMALL && n_lists * LIST <= ESMALL * NT)
+    return merge_lists_e<NT, ESMALL>(lists, meta, n_lists, need, bq, top_k, out, sh);
+  return merge_lists_e<NT, EMAX>(lists, meta, n_lists, need, bq, top_k, out, sh);
 }
 
 }  // namespace sel
