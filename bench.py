@@ -153,7 +153,7 @@ def fuses_select(w):
 # the sources each kernel is built from (the HBM counters in profiles/ are tied to them)
 _KERNEL_SOURCES = {"attention": ("attn.hip", "attn_pipe.hip", "attn_common.hpp"), "combine": ("attn.hip", "attn_common.hpp"),
                    "step": ("attn.hip", "attn_common.hpp", "score_fp8.hpp", "select.hpp"),
-                   "score": ("score.hip", "score_fp8.hpp", "select.hpp"), "topk": ("select.hip", "select.hpp"), "compress": ("compress.hip",),
+                   "score": ("score.hip", "score_fp8.hpp", "select.hpp"), "topk": ("topk.hip", "select.hip", "select.hpp"), "compress": ("compress.hip",),
                    "append": ("compress.hip",), "kda": ("kda.hip",)}
 
 

@@ -397,13 +397,35 @@ static ip_status score_topk_impl(const char* fn, const ip_seqs* seqs, int32_t n_
     if (ip_status st = device_status(ip::launch_append(*append, stream), fn)) return st;
     append = nullptr;
   }
+  // rows that fit one register-resident chunk whose padding the score rows cover
+  // take the chunk select (no group maxima needed); others the whole-row select
+  const int chunk = ip::topk_chunk_size(std::max(1, plan.max_blocks));
+  const bool chunk_select = chunk > 0 && chunk <= plan.ld;
   for (int row0 = 0; row0 < n_q; row0 += plan.rows_per_pass) {
     const int nr = std::min(plan.rows_per_pass, n_q - row0);
-    const ip::ScoreArgs sa = score_args(seqs, plan, row0, nr, q_seq, q_pos, q_idx, n_heads, head_dim, gates, pooled,
-                                        top_k, out_idx, scores, ws, append);
+    ip::ScoreArgs sa = score_args(seqs, plan, row0, nr, q_seq, q_pos, q_idx, n_heads, head_dim, gates, pooled,
+                                  top_k, out_idx, scores, ws, append);
+    if (!sa.fuse && chunk_select) sa.gm = nullptr;
     ip_status st = device_status(fp8 ? ip::launch_score_fp8_bf16(sa, stream) : ip::launch_score_f32(sa, stream), fn);
     if (st) return st;
     if (sa.fuse) continue;
+    if (chunk_select) {
+      ip::TopkArgs ka{};
+      ka.L = sa.L;
+      ka.row0 = row0;
+      ka.n_rows = nr;
+      ka.q_seq = q_seq;
+      ka.q_pos = q_pos;
+      ka.scores = sa.scores;
+      ka.ld = plan.ld;
+      ka.top_k = top_k;
+      ka.out = out_idx;
+      ka.n_chunks = 1;
+      ka.chunk = chunk;
+      st = device_status(ip::launch_topk(ka, stream), fn);
+      if (st) return st;
+      continue;
+    }
     ip::SelectArgs ta;
     ta.L = sa.L;
     ta.row0 = row0;

@@ -86,7 +86,7 @@ struct ScoreArgs {
   const float* key_scale;      // [pooled rows] (fp8) or null
   float* scores;               // [n_rows, ld], row r - row0
   int64_t ld;                  // a multiple of 512
-  float* gm;                   // [n_rows, gld] maxima of groups of 16 consecutive scores
+  float* gm;                   // [n_rows, gld] maxima of groups of 16 consecutive scores (non-fused: or null)
   int64_t gld;                 // ld / 16
   int heads, dim;
   int max_blocks;              // key range covered by the grid
@@ -108,6 +108,31 @@ bool score_fuses_select(const ScoreArgs& a);
 constexpr int SCORE_TILE = 1024;    // score rows pad to whole tiles of the scoring workgroups
 
 // ------------------------------------------------------------ top-k selection
+// One workgroup per row chunk holds up to 48 x 512 scores in registers (topk.hip):
+// the faster select for rows of at most TOPK_SINGLE_MAX eligible blocks whose score
+// rows are padded to a whole chunk (prefill rows of a 73728-token chunk).  Only the
+// single-chunk form is launched (n_chunks == 1, cand_* and count unused).
+struct TopkArgs {
+  Layout L;
+  int row0, n_rows;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  const float* scores;         // [n_rows, ld]
+  int64_t ld;
+  int top_k;
+  int32_t* out;                // [n_q, top_k], row r
+  uint32_t* cand_key;          // unused (multi-chunk rows)
+  int32_t* cand_idx;
+  int n_chunks;                // 1
+  int chunk;                   // scores per chunk (topk_chunk_size)
+  int32_t* count;
+};
+constexpr int TOPK_MAX_CHUNK = 16384;   // scores per chunk workgroup (512 threads x 32)
+constexpr int TOPK_MERGE_CAP = 16384;
+constexpr int TOPK_SINGLE_MAX = 512 * 48;
+int topk_chunk_size(int max_blocks);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
 struct SelectArgs {
   Layout L;
   int row0, n_rows;

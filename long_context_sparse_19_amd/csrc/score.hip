@@ -65,7 +65,7 @@ __global__ __launch_bounds__(NT) void score_f32_kernel(ScoreArgs a) {
   }
   // groups of 16 consecutive blocks are 16-lane rows of the wave
   const float gmax = row16_max(s);
-  if ((threadIdx.x & 15) == 0 && j < nel) a.gm[(int64_t)(r - a.row0) * a.gld + (j >> 4)] = gmax;
+  if (a.gm && (threadIdx.x & 15) == 0 && j < nel) a.gm[(int64_t)(r - a.row0) * a.gld + (j >> 4)] = gmax;
 }
 
 }  // namespace

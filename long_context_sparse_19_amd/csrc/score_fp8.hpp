@@ -204,15 +204,18 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
       const int j = kc0 + (wv * TILES + t) * 32 + kl;
       const float sc = j < nel ? part * ksig[t] : -INFINITY;
       scv[t] = sc;
-      // the maximum of each group of 16 consecutive blocks: lanes kl 0..15 and
-      // 16..31 of the tile are 16-lane rows
-      const float gmax = row16_max(sc);
-      gmv[t] = gmax;
       // fused: stored after the wave's list (see below), so that building the list
       // does not wait for these stores
-      if (!FUSE && hh == 0 && j < nel) {
-        srow[j] = sc;
-        if ((kl & 15) == 0) grow[j >> 4] = gmax;
+      if constexpr (FUSE) {
+        // the maximum of each group of 16 consecutive blocks: lanes kl 0..15 and
+        // 16..31 of the tile are 16-lane rows
+        gmv[t] = row16_max(sc);
+      } else {
+        if (hh == 0 && j < nel) srow[j] = sc;
+        if (a.gm) {                              // only the whole-row select reads them
+          const float gmax = row16_max(sc);
+          if (hh == 0 && j < nel && (kl & 15) == 0) grow[j >> 4] = gmax;
+        }
       }
     }
   }

@@ -154,6 +154,9 @@ SMALL = {
     "ragged_multichunk": scaled_down(RAGGED, 4 * 40000, batch=4, min_blocks=100),
     "decode_short": scaled_down(DECODE, 300, batch=3),
     "prefill_tail": scaled_down(PREFILL, 3000, n_query=130),
+    # prefill rows longer than one register-resident chunk (24576 blocks): the
+    # whole-row select over the stored scores and group maxima
+    "prefill_long_rows": scaled_down(PREFILL, 4 * 30000 + 8, n_query=64),
     "prefill_from_zero": scaled_down(PREFILL, 64, n_query=64, top_k=6),
     # long selections take the pipelined attention kernel (32-token sub-tiles):
     # 200 blocks = 25 sub-tiles padded to 28, rows at blocks 192..255 (some padded
