@@ -1081,7 +1081,7 @@ hipError_t launch_decode_step(const StepArgs& a, hipStream_t s) {
   k.at = a.attn;
   k.gx = (a.score.max_blocks + KEYS - 1) / KEYS;
   k.n_score = k.gx * a.score.n_rows;
-  k.n_app = a.score.with_append ? k.gx * ((a.score.append.batch + k.gx - 1) / k.gx) : 0;
+  k.n_app = a.score.with_append ? a.score.append.batch : 0;   // one workgroup per sequence
   const int64_t grid = (int64_t)k.n_score + k.n_app + (int64_t)a.attn.n_rows * a.attn.n_split;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   launch(K_STEP, decode_step_kernel, dim3((unsigned)grid), dim3(NTA), s, k);

@@ -227,49 +227,69 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
   if (tid < KSL) wv4 = *(const float4*)(a.conv_w + (2 * HD + (int64_t)h * KD + KSL * sl + tid) * 4);
   const float rs = rsqrtf((float)KD);
 
-  for (int t0 = 0; t0 < T; t0 += CC) {
+  // the inputs of a block, fetched into registers one block ahead: x (zero past the
+  // chunk's end), alpha (1 past it), beta (0 past it)
+  const int fi = tid >> 4, fc0 = 8 * (tid & 15);           // q, k: token, channels
+  const int fiv = tid >> 2, fv0 = 8 * (tid & 3);           // v (threads < 64)
+  u32x4_t pxq, pxk, pxv;
+  float4 pal[2];
+  float pbeta = 0.f;
+  auto fetch = [&](int t0) {
     const int n = min(CC, T - t0);
-    __syncthreads();                             // the previous block is done with every buffer
-    // ---- the block's inputs: x (zero past n), log alpha (0 past n), beta (0 past n)
-    {
-      const int i = tid >> 4, c0 = 8 * (tid & 15);
-      u32x4_t xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
-      if (i < n) {
-        const int64_t off = ((int64_t)b * T + t0 + i) * HD + (int64_t)h * KD + c0;
-        xq = *(const u32x4_t*)(a.xq + off);
-        xk = *(const u32x4_t*)(a.xk + off);
-      }
+    pxq = u32x4_t{0u, 0u, 0u, 0u};
+    pxk = u32x4_t{0u, 0u, 0u, 0u};
+    pxv = u32x4_t{0u, 0u, 0u, 0u};
+    if (fi < n) {
+      const int64_t off = ((int64_t)b * T + t0 + fi) * HD + (int64_t)h * KD + fc0;
+      pxq = *(const u32x4_t*)(a.xq + off);
+      pxk = *(const u32x4_t*)(a.xk + off);
+    }
+    if (tid < CC * KSL / 8 && fiv < n)
+      pxv = *(const u32x4_t*)(a.xv + ((int64_t)b * T + t0 + fiv) * HD + (int64_t)h * KD + KSL * sl + fv0);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int idx = tid + KT * k, ia = idx >> 5, c4 = idx & 31;
+      pal[k] = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (ia < n) pal[k] = *(const float4*)(a.alpha + (((int64_t)b * T + t0 + ia) * a.heads + h) * KD + 4 * c4);
+    }
+    if (tid < CC) pbeta = tid < n ? a.beta[((int64_t)b * T + t0 + tid) * a.heads + h] : 0.f;
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sh.yq[fi][fc0 + 2 * e] = bf16_lo(pxq[e]);
+      sh.yq[fi][fc0 + 2 * e + 1] = bf16_hi(pxq[e]);
+      sh.yk[fi][fc0 + 2 * e] = bf16_lo(pxk[e]);
+      sh.yk[fi][fc0 + 2 * e + 1] = bf16_hi(pxk[e]);
+    }
+    if (tid < CC * KSL / 8) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sh.yq[i][c0 + 2 * e] = bf16_lo(xq[e]);
-        sh.yq[i][c0 + 2 * e + 1] = bf16_hi(xq[e]);
-        sh.yk[i][c0 + 2 * e] = bf16_lo(xk[e]);
-        sh.yk[i][c0 + 2 * e + 1] = bf16_hi(xk[e]);
+        sh.yv[fiv][fv0 + 2 * e] = bf16_lo(pxv[e]);
+        sh.yv[fiv][fv0 + 2 * e + 1] = bf16_hi(pxv[e]);
       }
-      if (tid < CC * KSL / 8) {
-        const int iv = tid >> 2, v0 = 8 * (tid & 3);
-        u32x4_t xv = {0u, 0u, 0u, 0u};
-        if (iv < n) xv = *(const u32x4_t*)(a.xv + ((int64_t)b * T + t0 + iv) * HD + (int64_t)h * KD + KSL * sl + v0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sh.yv[iv][v0 + 2 * e] = bf16_lo(xv[e]);
-          sh.yv[iv][v0 + 2 * e + 1] = bf16_hi(xv[e]);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int idx = tid + KT * k, ia = idx >> 5, c4 = idx & 31;
-        float4 al = make_float4(1.f, 1.f, 1.f, 1.f);
-        if (ia < n) al = *(const float4*)(a.alpha + (((int64_t)b * T + t0 + ia) * a.heads + h) * KD + 4 * c4);
-        sh.g[ia][4 * c4] = logf(al.x);
-        sh.g[ia][4 * c4 + 1] = logf(al.y);
-        sh.g[ia][4 * c4 + 2] = logf(al.z);
-        sh.g[ia][4 * c4 + 3] = logf(al.w);
-      }
-      if (tid < CC) sh.beta[tid] = tid < n ? a.beta[((int64_t)b * T + t0 + tid) * a.heads + h] : 0.f;
-      if (tid == 0) sh.unsafe = 0;
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int idx = tid + KT * k, ia = idx >> 5, c4 = idx & 31;
+      sh.g[ia][4 * c4] = logf(pal[k].x);
+      sh.g[ia][4 * c4 + 1] = logf(pal[k].y);
+      sh.g[ia][4 * c4 + 2] = logf(pal[k].z);
+      sh.g[ia][4 * c4 + 3] = logf(pal[k].w);
+    }
+    if (tid < CC) sh.beta[tid] = pbeta;
+    if (tid == 0) sh.unsafe = 0;
+  };
+  if (T > 0) fetch(0);
+
+  // LDS-only barriers inside the loop (block_sync_lds): the next block's loads stay
+  // in flight across them
+  for (int t0 = 0; t0 < T; t0 += CC) {
+    const int n = min(CC, T - t0);
+    block_sync_lds();                            // the previous block is done with every buffer
+    stage();
+    if (t0 + CC < T) fetch(t0 + CC);
+    block_sync_lds();
     // ---- short convolution + SiLU in place, taps sliding in registers (the taps after
     //      the block are the last 3 inputs up to token n-1); the running sum G
     {
@@ -302,7 +322,7 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
         }
       }
     }
-    __syncthreads();
+    block_sync_lds();
     // ---- 1 / norms of q and k per token: thread -> (q or k, token (t % 128) / 8), 16
     //      channels (t % 8) + 8j, summed over the 8 lanes of the token
     {
@@ -319,7 +339,7 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
       s2 += __shfl_xor(s2, 4);
       if (c0 == 0) (cw ? sh.rk : sh.rq)[i] = rsqrtf(s2 + 1e-6f);
     }
-    __syncthreads();
+    block_sync_lds();
     // ---- decayed operands: thread -> token t / 16, channels 8(t % 16) .. +7
     {
       const int i = tid >> 4, c0 = 8 * (tid & 15);
@@ -342,7 +362,7 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
       }
       if (bad) sh.unsafe = 1;
     }
-    __syncthreads();
+    block_sync_lds();
     // ---- S0 products and the block coefficients on MFMA: waves 0 / 1 take k~ S0 for
     //      columns 16w .. +15 (then U = v - k~ S0) and A / B; waves 2 / 3 keep q~ S0
     f32x4_t r = {0.f, 0.f, 0.f, 0.f};
@@ -371,7 +391,7 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
         r = acc;
       }
     }
-    __syncthreads();
+    block_sync_lds();
     if (sh.unsafe) {
       // term by term: thread -> (i, j) = (t / 16, t % 16), e^{G_i - G_j} <= 1 for j <= i
       const int i = tid >> 4, j = tid & 15;
@@ -387,18 +407,22 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
         if (j < i) sh.A[i][j] = sa;
         sh.B[i][j] = sb;
       }
-      __syncthreads();
+      block_sync_lds();
     }
     // ---- u by forward substitution: lanes 0 .. 31 of wave 0, one column each
     if (tid < KSL) {
+      float u[CC];
 #pragma unroll
       for (int i = 0; i < CC; ++i) {
         float acc = sh.U[i][tid];
-        for (int j = 0; j < i; ++j) acc = fmaf(-sh.A[i][j], sh.U[j][tid], acc);
-        sh.U[i][tid] = sh.beta[i] * acc;
+#pragma unroll
+        for (int j = 0; j < i; ++j) acc = fmaf(-sh.A[i][j], u[j], acc);
+        u[i] = sh.beta[i] * acc;
       }
+#pragma unroll
+      for (int i = 0; i < CC; ++i) sh.U[i][tid] = u[i];
     }
-    __syncthreads();
+    block_sync_lds();
     // ---- outputs (waves 2 / 3): (q~ S0 + B u) / sqrt(128)
     if (wv >= 2) {
       const int nt = wv & 1;
@@ -430,7 +454,7 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
       for (int e = 0; e < 4; ++e) sh.S[16 * mt + 4 * kq + e][16 * nt + r16] = acc[e];
     }
   }
-  __syncthreads();
+  block_sync_lds();
   // ---- the state slice and the taps out (q and k taps by the head's first slice)
   for (int i = tid; i < KD * KSL / 4; i += KT) {
     const int row = i / (KSL / 4), c4 = i % (KSL / 4);
