@@ -91,7 +91,7 @@ struct ScorePlan {
   int max_blocks;      // eligible blocks bound
   int rows_per_pass;   // query rows per pass
   int max_lists;       // per-wave candidate lists per row (0: rows too long for them)
-  size_t count_bytes, gm_bytes, list_bytes, score_bytes, total;
+  size_t count_bytes, ack_bytes, gm_bytes, list_bytes, score_bytes, total;
 };
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -114,8 +114,9 @@ ScorePlan score_plan(const ip_seqs* s, int n_q, bool scores_given) {
   const int waves = 8 * (int)((std::max(1, p.max_blocks) + 1023) / 1024);
   p.max_lists = waves <= 256 && n_q < 64 ? waves : 0;
   p.list_bytes = align256((size_t)p.rows_per_pass * p.max_lists * (16 * 8 + 8));
+  p.ack_bytes = p.max_lists ? align256((size_t)p.rows_per_pass * 12) : 0;
   p.score_bytes = scores_given ? 0 : align256((size_t)p.rows_per_pass * p.ld * 4);
-  p.total = p.count_bytes + p.gm_bytes + p.list_bytes + p.score_bytes;
+  p.total = p.count_bytes + p.ack_bytes + p.gm_bytes + p.list_bytes + p.score_bytes;
   return p;
 }
 
@@ -342,8 +343,9 @@ static ip::ScoreArgs score_args(const ip_seqs* seqs, const ScorePlan& plan, int 
                                 const float* gates, const ip_cache* pooled, int32_t top_k, int32_t* out_idx,
                                 float* scores, void* ws, const ip::AppendArgs* append) {
   int32_t* count = (int32_t*)ws;
-  float* gm = (float*)((char*)ws + plan.count_bytes);
-  char* lists = (char*)ws + plan.count_bytes + plan.gm_bytes;
+  uint32_t* ack = plan.ack_bytes ? (uint32_t*)((char*)ws + plan.count_bytes) : nullptr;
+  float* gm = (float*)((char*)ws + plan.count_bytes + plan.ack_bytes);
+  char* lists = (char*)ws + plan.count_bytes + plan.ack_bytes + plan.gm_bytes;
   float* score_buf = scores ? scores : (float*)(lists + plan.list_bytes);
   ip::ScoreArgs sa;
   sa.L = layout_of(seqs);
@@ -367,6 +369,8 @@ static ip::ScoreArgs score_args(const ip_seqs* seqs, const ScorePlan& plan, int 
   sa.top_k = top_k;
   sa.out = out_idx;
   sa.count = count;
+  sa.ack = ack;
+  sa.scores_own = scores == nullptr;
   sa.max_lists = plan.max_lists;
   sa.lists = plan.max_lists ? (uint64_t*)lists : nullptr;
   sa.lists_meta = plan.max_lists ? (uint2*)(lists + (size_t)plan.rows_per_pass * plan.max_lists * 16 * 8) : nullptr;

@@ -94,6 +94,8 @@ struct ScoreArgs {
   int top_k;                   // fused selection: ids out
   int32_t* out;                // [n_q, top_k], row r
   int32_t* count;              // [n_rows] per-row counters, zero on entry and on exit
+  uint32_t* ack;               // with lists: [n_rows][3] per row (parity, two counters), zero-filled once
+  int scores_own;              // scores is the workspace (rows may be written past b_q)
   uint64_t* lists;             // fused: [n_rows, max_lists, 16] per-wave candidate lists, or null
   uint2* lists_meta;           // [n_rows, max_lists] (count, threshold) of each list
   int max_lists;               // waves per row covered by the grid

@@ -12,6 +12,16 @@ namespace ip {
 namespace scorek {
 
 constexpr int TILES = 4;                        // 32-key tiles per wave (default)
+constexpr int SCORE_SPIN_LIMIT = 1 << 22;       // bound on the fallback's wait for score acknowledgements
+
+// Waits until at most N of this wave's vector memory operations are outstanding
+// (they complete in issue order).  vmcnt is bits 0..3 and 14..15 of the immediate;
+// expcnt and lgkmcnt stay at their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 constexpr int HI = 32, DI = 128;
 
 struct QStage {
@@ -236,6 +246,20 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
                        need <= TILES / 2 * n_lists;
     uint64_t* lrow = lists ? a.lists + (int64_t)(r - a.row0) * a.max_lists * sel::LIST : nullptr;
     uint2* mrow = lists ? a.lists_meta + (int64_t)(r - a.row0) * a.max_lists : nullptr;
+    // With lists and the scores in the workspace, a workgroup counts itself in once
+    // its lists are acknowledged, without waiting for its score stores: the scores are
+    // read only by the exact fallback, which first waits until every workgroup of the
+    // row has counted its acknowledged scores into the counter of the row's current
+    // parity (ack[0] = parity, ack[1 + parity] = the count; the row's selecting
+    // workgroup clears the other counter and flips the parity for the next call,
+    // after every workgroup of this call has read it).
+    const bool defer = lists && a.ack && a.scores_own;
+    uint32_t* ack = defer ? a.ack + (int64_t)(r - a.row0) * 3 : nullptr;
+    // the parity, read (device-coherently) before the lists are stored; it has landed
+    // by the time the count moves, and is first used after that
+    uint32_t par_v = 0;
+    if (defer && kc0 < nel)
+      par_v = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(sel::dev_rsrc(ack), 0u, 0, 16 /* sc1 */);
     if (kc0 < nel) {
       const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hh = lane >> 5, kl = lane & 31;
       if (lists) {
@@ -253,14 +277,31 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
       }
       // the scores and group maxima (read by the exact fallback, and the caller's
       // score output), after the list so that building it does not wait for them
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       float* srow = a.scores + (int64_t)(r - a.row0) * a.ld;
       float* grow = a.gm + (int64_t)(r - a.row0) * a.gld;
+      if (defer) {
+        // exactly 2 TILES stores per wave, after the lists (every lane writes: the two
+        // halves hold the same score, a group's 16 lanes the same maximum, and rows of
+        // the workspace are padded to whole tiles), so that waiting for all but the
+        // last 2 TILES of the wave's memory operations waits for its lists
 #pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        const int j = kc0 + (wv * TILES + t) * 32 + kl;
-        if (hh == 0 && j < nel) {
+        for (int t = 0; t < TILES; ++t) {
+          const int j = kc0 + (wv * TILES + t) * 32 + kl;
           sel::st_agent(srow + j, scv[t]);
-          if ((kl & 15) == 0) sel::st_agent(grow + (j >> 4), gmv[t]);
+          sel::st_agent(grow + (j >> 4), gmv[t]);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_vm<2 * TILES>();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+          const int j = kc0 + (wv * TILES + t) * 32 + kl;
+          if (hh == 0 && j < nel) {
+            sel::st_agent(srow + j, scv[t]);
+            if ((kl & 15) == 0) sel::st_agent(grow + (j >> 4), gmv[t]);
+          }
         }
       }
     }
@@ -271,6 +312,14 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
       __syncthreads();
       if (threadIdx.x == 0) sel::st_agent(sel_ready + (r - a.row0), 1u);
     };
+    // this workgroup's scores are acknowledged: count them in (deferred mode)
+    uint32_t par = 0;
+    auto count_scores = [&]() {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      par = __builtin_amdgcn_readfirstlane(par_v);
+      if (threadIdx.x == 0) atomicAdd(ack + 1 + par, 1u);
+    };
     if (trivial) {
       if (bx == 0) {
         __syncthreads();
@@ -280,21 +329,42 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
       return;
     }
     if (kc0 >= nel) return;                      // this workgroup scored nothing
-    // every score, maximum and list entry of this workgroup is stored (acknowledged
-    // by memory) before it counts itself in: the stores are device-coherent, so the
-    // workgroup that completes the count reads them with device-coherent loads
+    // every list entry (and, unless deferred, every score and maximum) of this
+    // workgroup is stored (acknowledged by memory) before it counts itself in: the
+    // stores are device-coherent, so the workgroup that completes the count reads
+    // them with device-coherent loads
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
+    if (!defer) __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
     if (threadIdx.x == 0) last_here = atomicAdd(a.count + (r - a.row0), 1) == n_run - 1;
     __syncthreads();
-    if (!last_here) return;
+    if (!last_here) {
+      if (defer) count_scores();
+      return;
+    }
     if (threadIdx.x == 0) sel::st_agent(a.count + (r - a.row0), 0);   // clear for the next call
     if (!(lists && sel::merge_lists<NTW>(lrow, mrow, n_lists, need, nel, a.top_k, out, ss))) {
+      if (defer) {
+        // the fallback reads every score of the row: wait (bounded) until every
+        // workgroup has counted its acknowledged scores in
+        count_scores();
+        if (threadIdx.x == 0)
+          for (int n = 0; sel::ld_agent(ack + 1 + par) < (uint32_t)n_run && n < SCORE_SPIN_LIMIT; ++n)
+            __builtin_amdgcn_s_sleep(1);
+        __syncthreads();
+      }
       __syncthreads();
       sel::select_row<NTW>(a.scores + (int64_t)(r - a.row0) * a.ld, a.gm + (int64_t)(r - a.row0) * a.gld, nel,
                            nel, a.top_k, out, ss);
+    } else if (defer) {
+      count_scores();
+    }
+    if (defer && threadIdx.x == 0) {
+      // every workgroup of this call has read the parity (it counted itself in
+      // before the row's count completed): clear the other counter, flip
+      sel::st_agent(ack + 2 - par, 0u);
+      sel::st_agent(ack, 1u - par);
     }
     publish();
   }

@@ -210,15 +210,16 @@ def test_noalloc_rejects_bad_arguments_and_oversized_calls(L):
 def test_workspace_sizes_are_consistent(L):
     s = seqs(batch=8, max_seq_len=131072, seq_stride=131072)
     n = L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 0)
-    # per row: one counter (the block padded to 256 bytes), the maxima of groups of
-    # 16 scores, the 16-entry candidate lists (8 bytes each) and their (count,
-    # threshold) of the 256 waves of 128 blocks, and the scores, each row padded to
-    # whole scoring tiles of 1024
+    # per row: one counter (the block padded to 256 bytes), three words of the
+    # score-acknowledgement count (with lists; padded to 256 bytes), the maxima of
+    # groups of 16 scores, the 16-entry candidate lists (8 bytes each) and their
+    # (count, threshold) of the 256 waves of 128 blocks, and the scores, each row
+    # padded to whole scoring tiles of 1024
     ld = L.LIB.index_scores_ld(131072)
     assert ld == 32768
     lists = 8 * 256 * (16 * 8 + 8)
-    assert n == 256 + 8 * (ld // 16) * 4 + lists + 8 * ld * 4
-    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 1) == 256 + 8 * (ld // 16) * 4 + lists
+    assert n == 256 + 256 + 8 * (ld // 16) * 4 + lists + 8 * ld * 4
+    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s), 8, 512, 1) == 512 + 8 * (ld // 16) * 4 + lists
     # 73728 tokens -> 18431 eligible blocks -> 18 tiles of 1024; a prefill chunk of
     # 8192 rows keeps no lists
     assert L.LIB.index_scores_ld(73728) == 18432
