@@ -177,8 +177,11 @@ ip_status indexpool_append(const ip_seqs* seqs, const void* kv_new, const ip_cac
  *           and no score workspace is used
  *  ws       device workspace of ws_bytes >= index_score_topk_workspace_bytes(...),
  *           256-byte aligned, zero-filled before its first use; each call leaves
- *           its per-row counters at zero again, so a workspace serves any number
- *           of later calls (one call at a time) without being cleared again
+ *           its per-row synchronisation words (counters, and a parity word that
+ *           alternates from call to call) in the state the next call expects, so a
+ *           workspace serves any number of later calls (one call at a time)
+ *           without being cleared again; the caller must not modify it between
+ *           calls
  * Contract: 0 <= p < seq_lens[b]; blocks j < b_q were pooled.
  * ------------------------------------------------------------------------------- */
 int64_t index_scores_ld(int32_t max_seq_len);   /* >= max_seq_len/4, rounded up to whole top-k chunks */
@@ -298,7 +301,8 @@ ip_status sparse_attn_prefill(const ip_seqs* seqs, int32_t n_q, const int32_t* q
  * calls.
  *  ws  device workspace of ws_bytes >= indexpool_decode_step_workspace_bytes(seqs,
  *      top_k, n_heads, dv, q_dtype, scores != NULL), 256-byte aligned, zero-filled
- *      before its first use (the call leaves its counters and ready words at zero).
+ *      before its first use and not modified between calls (as for index_score_topk;
+ *      the ready words return to zero in every call).
  * Errors: those of the two calls.  Calls sharing a workspace must not overlap.
  * ------------------------------------------------------------------------------- */
 size_t indexpool_decode_step_workspace_bytes(const ip_seqs* seqs, int32_t top_k, int32_t n_heads,
