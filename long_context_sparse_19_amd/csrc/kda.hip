@@ -165,8 +165,9 @@ __global__ __launch_bounds__(KT) void kda_decode_kernel(KdaArgs a) {
 // The products with S0, the outputs and the state update are dense contractions
 // on fp32 MFMA (v_mfma_f32_16x16x4_f32).  A and B are (k e^G)(k e^-G)^T and
 // (q e^G)(k e^-G)^T -- unless some e^-G of the block would leave fp32's range (a
-// cumulative decay below e^-80 inside 16 tokens), in which case they are summed
-// term by term with e^{G_i - G_j} <= 1.  One workgroup per (head, 32-column slice,
+// cumulative decay below 2^-115 inside 16 tokens), in which case they are summed
+// term by term with e^{G_i - G_j} <= 1.  G is kept in base 2 (running sums of
+// log2 alpha from v_log_f32, powers from v_exp_f32).  One workgroup per (head, 32-column slice,
 // sequence), as in the decode step; the blocks of a sequence run in order inside it,
 // the state slice staying in LDS.  Tokens past the end of the last block enter with
 // zero input, alpha = 1 and beta = 0, which leaves the state and the taps unchanged.
@@ -174,7 +175,7 @@ constexpr int CC = 16;               // tokens per block
 constexpr int CP = KD + 2;           // row of q~, k~, k^ (read [token][channel] by 16 x 4 lanes)
 constexpr int KBP = KD + 16;         // row of k-bar (read [token][channel] by 4 x 16 lanes)
 constexpr int SP = KSL + 16;         // row of the state slice and of u
-constexpr float G_SAFE = -80.f;
+constexpr float G_SAFE = -115.f;          // log2 of the decay: 2^115 stays inside fp32
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -182,7 +183,7 @@ struct KdaChunkShared {
   float hx[3][3][KD];                // conv taps x_{t-3 .. t-1}: q, k (128 channels), v (first 32)
   float yq[CC][KD], yk[CC][KD];      // raw inputs, then conv + SiLU
   float yv[CC][KSL];
-  float g[CC][KD];                   // log alpha, then its running sum G
+  float g[CC][KD];                   // log2 alpha, then its running sum (G in base 2)
   float qt[CC][CP], kt[CC][CP], kh[CC][CP];
   float kb[CC][KBP];
   float S[KD][SP];
@@ -272,10 +273,10 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int idx = tid + KT * k, ia = idx >> 5, c4 = idx & 31;
-      sh.g[ia][4 * c4] = logf(pal[k].x);
-      sh.g[ia][4 * c4 + 1] = logf(pal[k].y);
-      sh.g[ia][4 * c4 + 2] = logf(pal[k].z);
-      sh.g[ia][4 * c4 + 3] = logf(pal[k].w);
+      sh.g[ia][4 * c4] = __builtin_amdgcn_logf(pal[k].x);
+      sh.g[ia][4 * c4 + 1] = __builtin_amdgcn_logf(pal[k].y);
+      sh.g[ia][4 * c4 + 2] = __builtin_amdgcn_logf(pal[k].z);
+      sh.g[ia][4 * c4 + 3] = __builtin_amdgcn_logf(pal[k].w);
     }
     if (tid < CC) sh.beta[tid] = pbeta;
     if (tid == 0) sh.unsafe = 0;
@@ -350,11 +351,11 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
         const int c = c0 + e;
         const float G = sh.g[i][c], GL = sh.g[CC - 1][c];
         const float q = sh.yq[i][c] * nq, k = sh.yk[i][c] * nk;
-        const float eg = expf(G);
+        const float eg = __builtin_amdgcn_exp2f(G);
         sh.qt[i][c] = q * eg;
         sh.kt[i][c] = k * eg;
-        sh.kh[i][c] = k * expf(-G);
-        sh.kb[i][c] = k * expf(GL - G);
+        sh.kh[i][c] = k * __builtin_amdgcn_exp2f(-G);
+        sh.kb[i][c] = k * __builtin_amdgcn_exp2f(GL - G);
         if (i == CC - 1) {
           sh.gl[c] = eg;
           bad |= GL < G_SAFE;
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
         const float nq = sh.rq[i], nki = sh.rk[i], nkj = sh.rk[j];
         float sa = 0.f, sb = 0.f;
         for (int c = 0; c < KD; ++c) {
-          const float d = expf(sh.g[i][c] - sh.g[j][c]);
+          const float d = __builtin_amdgcn_exp2f(sh.g[i][c] - sh.g[j][c]);
           const float kj = sh.yk[j][c] * nkj;
           sa = fmaf(sh.yk[i][c] * nki * d, kj, sa);
           sb = fmaf(sh.yq[i][c] * nq * d, kj, sb);
