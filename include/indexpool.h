@@ -294,15 +294,21 @@ ip_status sparse_attn_prefill(const ip_seqs* seqs, int32_t n_q, const int32_t* q
  * The results are those of the two calls in order: out_idx (and scores when
  * given) bit for bit, out and lse to the attention's rounding.  With FP8 indexer
  * keys and the split BF16 latent attention (decode batches of up to 64 rows) the
- * step is one launch plus the split combine: each row's attention workgroups
- * start while rows are still being selected, fetch their query, and wait for the
- * row's ids (published device-coherently by the workgroup that selects the row);
- * the query's own new token is read from kv_new.  Other geometries run the two
- * calls.
+ * step is one launch plus the split combine: the scoring workgroups store each
+ * wave's best blocks (a per-wave candidate list), and each row's attention
+ * workgroups, which start as scoring workgroups finish, fetch their query, merge
+ * the row's lists themselves as soon as every list is stored, and attend over
+ * their share of the ids (rows whose lists cannot decide the selection take the
+ * exact select over the row's scores, published device-coherently by one of
+ * them; rows too short or too long for lists wait for the ids published by their
+ * last scoring workgroup); the query's own new token is read from kv_new.  Other
+ * geometries run the two calls.
  *  ws  device workspace of ws_bytes >= indexpool_decode_step_workspace_bytes(seqs,
  *      top_k, n_heads, dv, q_dtype, scores != NULL), 256-byte aligned, zero-filled
- *      before its first use and not modified between calls (as for index_score_topk;
- *      the ready words return to zero in every call).
+ *      before its first use and not modified between calls (as for index_score_topk);
+ *      each call returns its ready words, counters and candidate lists to zero.
+ *      The layout depends on seqs->batch, seqs->max_seq_len, top_k, n_heads, dv and
+ *      q_dtype: zero-fill it again before a call that changes them.
  * Errors: those of the two calls.  Calls sharing a workspace must not overlap.
  * ------------------------------------------------------------------------------- */
 size_t indexpool_decode_step_workspace_bytes(const ip_seqs* seqs, int32_t top_k, int32_t n_heads,

@@ -347,7 +347,7 @@ static ip::ScoreArgs score_args(const ip_seqs* seqs, const ScorePlan& plan, int 
   float* gm = (float*)((char*)ws + plan.count_bytes + plan.ack_bytes);
   char* lists = (char*)ws + plan.count_bytes + plan.ack_bytes + plan.gm_bytes;
   float* score_buf = scores ? scores : (float*)(lists + plan.list_bytes);
-  ip::ScoreArgs sa;
+  ip::ScoreArgs sa{};
   sa.L = layout_of(seqs);
   sa.row0 = row0;
   sa.n_rows = nr;
@@ -604,11 +604,13 @@ ip_status sparse_attn_prefill(const ip_seqs* seqs, int32_t n_q, const int32_t* q
 }
 
 // ------------------------------------------------------------------ fused decode step
-// workspace: the indexer's, the attention's, then one ready word per sequence
+// workspace: the indexer's, the attention's, then per sequence a ready word and a
+// count of acknowledged scoring workgroups, then the one-launch step's own per-wave
+// lists (zero between calls)
 struct StepPlan {
   ScorePlan score;
   AttnPlan attn;
-  size_t idx_bytes, attn_bytes, ready_bytes, total;
+  size_t idx_bytes, attn_bytes, ready_bytes, list_bytes, total;
 };
 
 static StepPlan step_plan(const ip_seqs* seqs, int32_t top_k, int32_t n_heads, int32_t dv, int32_t q_dtype,
@@ -618,8 +620,9 @@ static StepPlan step_plan(const ip_seqs* seqs, int32_t top_k, int32_t n_heads, i
   p.attn = attn_plan(seqs->batch, n_heads, dv, top_k, q_dtype);
   p.idx_bytes = align256(p.score.total);
   p.attn_bytes = align256(p.attn.bytes);
-  p.ready_bytes = align256((size_t)seqs->batch * 4);
-  p.total = p.idx_bytes + p.attn_bytes + p.ready_bytes;
+  p.ready_bytes = align256((size_t)seqs->batch * 8);
+  p.list_bytes = align256((size_t)seqs->batch * p.score.max_lists * (16 * 8 + 8));
+  p.total = p.idx_bytes + p.attn_bytes + p.ready_bytes + p.list_bytes;
   return p;
 }
 
@@ -657,6 +660,8 @@ ip_status indexpool_decode_step(const ip_seqs* seqs, const void* kv_new, const i
   char* ws_idx = (char*)ws;
   char* ws_att = ws_idx + plan.idx_bytes;
   uint32_t* ready = (uint32_t*)(ws_att + plan.attn_bytes);
+  uint32_t* acked = ready + B;
+  char* step_lists = (char*)ready + plan.ready_bytes;
   ip::AttnArgs a;
   AttnKind kind;
   if (ip_status st = attn_build(fn, seqs, B, nullptr, nullptr, q, q_dtype, n_heads, dk, dv, scale, kv, v, out_idx,
@@ -671,10 +676,23 @@ ip_status indexpool_decode_step(const ip_seqs* seqs, const void* kv_new, const i
     ip::StepArgs st;
     st.score = score_args(seqs, plan.score, 0, B, nullptr, nullptr, q_idx, idx_heads, idx_dim, gates, pooled, top_k,
                           out_idx, scores, ws_idx, &app);
+    // the step's own lists (zero between calls: the combine clears them)
+    st.score.lists = (uint64_t*)step_lists;
+    st.score.lists_meta = (uint2*)(step_lists + (size_t)B * plan.score.max_lists * 16 * 8);
+    st.score.step_acked = acked;
     st.attn = a;
     st.attn.sel_ready = ready;
     st.attn.k_new = (const uint8_t*)kv_new;
     st.attn.k_new_stride = app.kv_row_bytes;
+    st.attn.step_lists = st.score.lists;
+    st.attn.step_meta = st.score.lists_meta;
+    st.attn.step_max_lists = st.score.max_lists;
+    st.attn.step_scores = st.score.scores;
+    st.attn.step_ld = st.score.ld;
+    st.attn.step_gm = st.score.gm;
+    st.attn.step_gld = st.score.gld;
+    st.attn.step_acked = acked;
+    st.attn.sel_out = out_idx;
     if (ip::decode_step_supported(st)) return device_status(ip::launch_decode_step(st, stream), fn);
   }
   // otherwise: the indexer call (with the append), then the attention

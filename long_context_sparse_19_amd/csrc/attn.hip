@@ -166,12 +166,72 @@ __device__ __forceinline__ void load_column(const SubtileSrc& src, uint8_t* buf,
 }
 
 
+// The fused decode step's scoring role: 4 waves of 8 tiles (1024 keys per
+// workgroup, as the standalone fused scoring's 8 waves of 4 tiles), the register
+// budget of one wave per SIMD that the attention role needs anyway.
+constexpr int STEP_NWV = 4, STEP_TILES = 8;
+static_assert(sizeof(sel::Shared<NTA>) <= KVBUF, "the selection state fits a sub-tile buffer");
+static_assert(MAX_BLOCKS_PER_SPLIT * 4 <= LAT_H * PROW, "a split's ids fit the P buffer");
+
+// The fused decode step: the ids of positions [sb0, send) of row rl's selection
+// into lid (LDS), and for the rows selected here into the row of sel_out.
+//  - Trivial rows (the query's own block alone, or every block): the ids directly.
+//  - List rows: the row's per-wave lists, merged as soon as every list is stored
+//    (see sel::merge_lists_e).  When the lists cannot decide the row, split 0 runs
+//    the exact select over the row's scores once every scoring workgroup has counted
+//    its scores in, and publishes the ids; the other splits wait for them.
+//  - Other rows: the ids published by the row's last scoring workgroup.
+// ss (the first sub-tile buffer) holds the selection state; it is free again on
+// return.  Waits only on workgroups that started earlier, bounded as the others.
+__device__ __forceinline__ void step_select(const AttnArgs& a, const RowCtx& c, int rl, int split, int sb0,
+                                            int send, int32_t* lid, uint8_t* kv0) {
+  sel::Shared<NTA>& ss = *reinterpret_cast<sel::Shared<NTA>*>(kv0);
+  const int nel = c.p >> 2;                      // eligible blocks j < b_q
+  const int need = min(a.top_k, nel + 1) - 1;
+  const int n = send - sb0;
+  int32_t* row_out = a.sel_out + (int64_t)(a.row0 + rl) * a.top_k;
+  bool local = true;
+  if (need == 0 || need >= nel) {
+    for (int i = threadIdx.x; i < n; i += NTA) {
+      const int pos = sb0 + i;
+      lid[i] = pos < need ? pos : (pos == need ? nel : -1);
+    }
+  } else {
+    const int n_lists = scorek::fused_list_count<STEP_NWV, STEP_TILES>(nel, need, a.step_lists != nullptr);
+    local = n_lists > 0 &&
+            sel::merge_lists_slice<NTA>(a.step_lists + (int64_t)rl * a.step_max_lists * sel::LIST,
+                                        a.step_meta + (int64_t)rl * a.step_max_lists, n_lists, need, nel, a.top_k,
+                                        sel::SliceOut{lid, sb0, send}, ss);
+    if (!local && n_lists > 0 && split == 0) {
+      constexpr int KEYS = STEP_NWV * STEP_TILES * 32;
+      const uint32_t n_run = (uint32_t)((nel + KEYS - 1) / KEYS);
+      if (threadIdx.x == 0)
+        for (int k = 0; sel::ld_agent(a.step_acked + rl) < n_run && k < STEP_SPIN_LIMIT; ++k)
+          __builtin_amdgcn_s_sleep(1);
+      __syncthreads();
+      sel::select_row<NTA>(a.step_scores + (int64_t)rl * a.step_ld, a.step_gm + (int64_t)rl * a.step_gld, nel, nel,
+                           a.top_k, row_out, ss);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) sel::st_agent(a.sel_ready + rl, 1u);
+    }
+  }
+  if (!local) {
+    if (threadIdx.x == 0)
+      for (int k = 0; sel::ld_agent(a.sel_ready + rl) == 0u && k < STEP_SPIN_LIMIT; ++k) __builtin_amdgcn_s_sleep(1);
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += NTA) lid[i] = sel_id<true>(c, sb0 + i);
+  }
+  __syncthreads();                               // lid complete, ss free
+  if (local)
+    for (int i = threadIdx.x; i < n; i += NTA) row_out[sb0 + i] = lid[i];
+}
+
 // The body of the bf16 kernel for workgroup `bid` (4 waves, threads 0..255), over
-// the LDS objects of the calling kernel.  STEP (the fused decode step): the row's
-// selection is produced by another workgroup of the same launch, which sets
-// a.sel_ready[row] once its ids are stored; the query is fetched first, then the
-// workgroup waits for that word and reads the ids device-coherently, and the
-// query's own token row comes from a.k_new.
+// the LDS objects of the calling kernel.  STEP (the fused decode step): the query
+// is fetched first, then the row's ids come from step_select (selected here, or
+// published by another workgroup of the same launch), and the query's own token
+// row comes from a.k_new.
 template <bool STEP>
 __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const int bid, AttnShared& sh, uint8_t* pmat,
                                                uint8_t* kv0, uint8_t* kv1) {
@@ -199,14 +259,24 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const int bid,
   BlockIds ids;
   // ids of this lane's source blocks for sub-tiles 0 and 1 (rows 8(2w + h) + l/8)
   int pid[2][2];
+  // STEP: the split's ids in LDS (the P buffer, first written in step 0)
+  int32_t* const lid = reinterpret_cast<int32_t*>(pmat);
   auto load_ids = [&]() {
-    ids = fetch_blocks<STEP>(c, sb0, send);
+    if constexpr (STEP) {
+#pragma unroll
+      for (int k = 0; k < MAX_BLOCKS_PER_SPLIT / NTA; ++k) {
+        const int i = (int)threadIdx.x + k * NTA;
+        ids.blk[k] = sb0 + i < send ? lid[i] : -1;
+      }
+    } else {
+      ids = fetch_blocks<false>(c, sb0, send);
+    }
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int bi = sb0 + 16 * n + ((8 * (2 * wv + h) + (lane >> 3)) >> 2);
-        pid[n][h] = bi < send ? sel_id<STEP>(c, bi) : -1;
+        pid[n][h] = bi < send ? (STEP ? lid[bi - sb0] : sel_id<false>(c, bi)) : -1;
       }
   };
   if constexpr (!STEP) load_ids();
@@ -224,14 +294,8 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const int bid,
     for (int k = 0; k < KV_LOADS; ++k) load_column(qsrc, kv1, k);
   }
   if constexpr (STEP) {
-    // wait (bounded) until the row's ids are published; a load of the word waits
-    // for the query loads above as well, which by then have long landed
     __builtin_amdgcn_sched_barrier(0);
-    if (threadIdx.x == 0) {
-      const uint32_t* f = a.sel_ready + rl;
-      for (int n = 0; sel::ld_agent(f) == 0u && n < STEP_SPIN_LIMIT; ++n) __builtin_amdgcn_s_sleep(1);
-    }
-    block_sync_lds();
+    step_select(a, c, rl, split, sb0, send, lid, kv0);
     load_ids();
   }
   // every query DMA is issued before anything consumes the ids
@@ -467,10 +531,9 @@ __global__ __launch_bounds__(NTA, 1) void attn_bf16_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ fused decode step
-// One launch for the decode step: workgroups [0, n_score) score and select (one
-// row each; the row's last scoring workgroup selects it and publishes the ids),
-// [n_score, n_score + n_app) append the new tokens, and the rest run the attention
-// of one (row, split) each.  Workgroups start in
+// One launch for the decode step: workgroups [0, n_score) score (and list) the
+// rows, [n_score, n_score + n_app) append the new tokens, and the rest run the
+// attention of one (row, split) each, selecting the row's ids first (step_select).  Workgroups start in
 // index order, so every attention workgroup waits only on workgroups that have
 // started before it and never wait themselves: the wait ends.  The attention
 // workgroups take their compute units as the scoring ones finish and fetch their
@@ -481,10 +544,6 @@ struct StepKArgs {
   AttnArgs at;
   int gx, n_score, n_app;
 };
-// The scoring role: 4 waves of 8 tiles (1024 keys per workgroup, as the standalone
-// fused scoring's 8 waves of 4 tiles), the register budget of one wave per SIMD
-// that the attention role needs anyway.
-constexpr int STEP_NWV = 4, STEP_TILES = 8;
 static_assert(scorek::score_smem<STEP_NWV, true>() <= KVBUF, "the scoring state fits a sub-tile buffer");
 
 __global__ __launch_bounds__(NTA, 1) void decode_step_kernel(StepKArgs A) {
@@ -921,9 +980,19 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     for (int u = 0; u < 4; ++u) add(__shfl(wgt, s + u), v[u]);
   }
   for (; s < S; ++s) add(__shfl(wgt, s), *(const uint2*)(base + (int64_t)s * LAT_H * LAT_DV));
-  // the fused step's ready word of the row, for the next launch (every reader of it
-  // belongs to the step launch, which has ended)
-  if (a.sel_ready && blockIdx.x == 0 && threadIdx.x == 0) a.sel_ready[rl] = 0u;
+  // the fused step's words and lists of the row return to zero for the next launch
+  // (every reader of them belongs to the step launch, which has ended)
+  if (a.sel_ready && blockIdx.x == 0 && threadIdx.x == 0) {
+    a.sel_ready[rl] = 0u;
+    a.step_acked[rl] = 0u;
+  }
+  if (a.step_lists) {
+    const int g = blockIdx.x * 256 + threadIdx.x, G = gridDim.x * 256;
+    u32x4_t* l16 = (u32x4_t*)(a.step_lists + (int64_t)rl * a.step_max_lists * sel::LIST);
+    for (int i = g; i < a.step_max_lists * sel::LIST / 2; i += G) l16[i] = u32x4_t{0u, 0u, 0u, 0u};
+    uint2* m = a.step_meta + (int64_t)rl * a.step_max_lists;
+    for (int i = g; i < a.step_max_lists; i += G) m[i] = make_uint2(0u, 0u);
+  }
   const float inv = 1.f / L;
   uint16_t* out = (uint16_t*)a.out + ((int64_t)r * LAT_H + head) * LAT_DV + t * 4;
   *(uint2*)out = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
@@ -1070,7 +1139,10 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
 bool decode_step_supported(const StepArgs& a) {
   return a.score.fuse && a.score.row0 == 0 && a.attn.row0 == 0 && a.attn.n_rows == a.score.n_rows &&
          a.attn.n_split > 1 && a.attn.blocks_per_split < PIPE_MIN_BLOCKS && a.attn.sel_ready && a.attn.k_new &&
-         !a.attn.k_scale && a.score.max_blocks > 0;
+         !a.attn.k_scale && a.score.max_blocks > 0 && a.score.step_acked && a.attn.step_acked == a.score.step_acked &&
+         a.attn.step_lists == a.score.lists && a.attn.step_meta == a.score.lists_meta &&
+         a.attn.step_max_lists == a.score.max_lists && a.attn.sel_out && a.attn.sel_out == a.score.out &&
+         a.attn.n_split * a.attn.blocks_per_split >= a.attn.top_k;
 }
 
 hipError_t launch_decode_step(const StepArgs& a, hipStream_t s) {

@@ -39,6 +39,20 @@ __device__ __forceinline__ float row16_max(float x) {
   return x;
 }
 
+// The number of per-wave lists the fused selection ranks row r from (nel eligible
+// blocks, need = k' - 1), or 0: the row is trivial (its own block alone, or every
+// block), or too short or too long for lists (it selects from its scores).
+template <int NWV, int TILES>
+__device__ __forceinline__ int fused_list_count(int nel, int need, bool have_lists) {
+  constexpr int NTW = NWV * 64, KEYS = NWV * TILES * 32;
+  const bool trivial = need == 0 || need >= nel;
+  const int n_lists = (nel + KEYS - 1) / KEYS * NWV;
+  // rows long enough for about 2 winners per wave
+  const bool ok = !trivial && have_lists && n_lists * sel::LIST <= sel::C_CAP && n_lists <= NTW &&
+                  need <= TILES / 2 * n_lists;
+  return ok ? n_lists : 0;
+}
+
 template <int NWV, bool FUSE>
 constexpr size_t score_smem() {
   return FUSE && sizeof(sel::Shared<NWV * 64>) > sizeof(QStage) ? sizeof(sel::Shared<NWV * 64>) : sizeof(QStage);
@@ -242,8 +256,12 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
     const int n_lists = n_run * NWV;
     // rows long enough for about 2 winners per wave: every wave lists its best
     // (see sel::wave_list) and the last workgroup merges the lists
-    const bool lists = !trivial && a.lists && n_lists * sel::LIST <= sel::C_CAP && n_lists <= NTW &&
-                       need <= TILES / 2 * n_lists;
+    const bool lists = fused_list_count<NWV, TILES>(nel, need, a.lists != nullptr) > 0;
+    // the fused decode step: the attention workgroups of a list row merge its lists
+    // themselves, those of a trivial row write its ids directly; the scoring
+    // workgroups of those rows store their lists and scores and count themselves in
+    // (the scores feed an exact fallback once every workgroup is counted)
+    const bool step = a.step_acked != nullptr;
     uint64_t* lrow = lists ? a.lists + (int64_t)(r - a.row0) * a.max_lists * sel::LIST : nullptr;
     uint2* mrow = lists ? a.lists_meta + (int64_t)(r - a.row0) * a.max_lists : nullptr;
     // With lists and the scores in the workspace, a workgroup counts itself in once
@@ -253,7 +271,7 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
     // parity (ack[0] = parity, ack[1 + parity] = the count; the row's selecting
     // workgroup clears the other counter and flips the parity for the next call,
     // after every workgroup of this call has read it).
-    const bool defer = lists && a.ack && a.scores_own;
+    const bool defer = !step && lists && a.ack && a.scores_own;
     uint32_t* ack = defer ? a.ack + (int64_t)(r - a.row0) * 3 : nullptr;
     // the parity, read (device-coherently) before the lists are stored; it has landed
     // by the time the count moves, and is first used after that
@@ -270,7 +288,11 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
         for (int i = 0; i < KPL; ++i) {
           const int t = KPL * hh + i;
           id[i] = kc0 + (wv * TILES + t) * 32 + kl;
-          k[i] = id[i] < nel ? float_key(scv[t]) : 0u;
+          // scv read at indices known at compile time and blended by half (a
+          // lane-dependent index would put the array in scratch or select chains)
+          const uint32_t hm = 0u - (uint32_t)hh;
+          const float sc = __uint_as_float((__float_as_uint(scv[i]) & ~hm) | (__float_as_uint(scv[KPL + i]) & hm));
+          k[i] = id[i] < nel ? float_key(sc) : 0u;
         }
         const int slot = bx * NWV + wv;
         sel::wave_list<KPL>(k, id, lrow + (int64_t)slot * sel::LIST, mrow + slot);
@@ -280,20 +302,23 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       float* srow = a.scores + (int64_t)(r - a.row0) * a.ld;
       float* grow = a.gm + (int64_t)(r - a.row0) * a.gld;
-      if (defer) {
-        // exactly 2 TILES stores per wave, after the lists (every lane writes: the two
-        // halves hold the same score, a group's 16 lanes the same maximum, and rows of
-        // the workspace are padded to whole tiles), so that waiting for all but the
-        // last 2 TILES of the wave's memory operations waits for its lists
+      if (defer || (step && a.scores_own)) {
+        // every lane writes (the two halves hold the same score, a group's 16 lanes
+        // the same maximum, and rows of the workspace are padded to whole tiles):
+        // unconditional stores stay in flight together.  Deferred: exactly 2 TILES
+        // stores per wave, after the lists, so that waiting for all but the last
+        // 2 TILES of the wave's memory operations waits for its lists
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
           const int j = kc0 + (wv * TILES + t) * 32 + kl;
           sel::st_agent(srow + j, scv[t]);
           sel::st_agent(grow + (j >> 4), gmv[t]);
         }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        wait_vm<2 * TILES>();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (defer) {
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          wait_vm<2 * TILES>();
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        }
       } else {
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
@@ -304,6 +329,13 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
           }
         }
       }
+    }
+    if (step && (trivial || lists)) {
+      if (trivial || kc0 >= nel) return;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) atomicAdd(a.step_acked + (r - a.row0), 1u);
+      return;
     }
     // the row's ids are stored (device-coherent stores): publish them
     auto publish = [&]() {

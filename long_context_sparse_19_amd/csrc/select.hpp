@@ -277,16 +277,41 @@ __device__ __forceinline__ int wave_base(int wave_total, Shared<NT>& sh, int p, 
   return before;
 }
 
+// Where a selection puts the row's ids (positions 0 .. top_k - 1): the kept ids in
+// ascending id order, then the query's own block at position need, then -1.
+// RowOut: every position, device-coherent stores to the row of `out`.  SliceOut:
+// positions [lo, hi) only, into LDS (lds[pos - lo]), for a workgroup that consumes
+// one slice of the row itself.
+struct RowOut {
+  int32_t* out;
+  __device__ __forceinline__ void put(int pos, int32_t id) const { st_agent(out + pos, id); }
+  template <int NT>
+  __device__ __forceinline__ void tail(int need, int bq, int top_k) const {
+    for (int i = need + threadIdx.x; i < top_k; i += NT) st_agent(out + i, i == need ? bq : -1);
+  }
+};
+struct SliceOut {
+  int32_t* lds;
+  int lo, hi;                                    // hi <= top_k
+  __device__ __forceinline__ void put(int pos, int32_t id) const {
+    if (pos >= lo && pos < hi) lds[pos - lo] = id;
+  }
+  template <int NT>
+  __device__ __forceinline__ void tail(int need, int bq, int top_k) const {
+    for (int i = max(need, lo) + threadIdx.x; i < hi; i += NT) lds[i - lo] = i == need ? bq : -1;
+  }
+};
+
 // Keeps the need best (ties to the lower id) of a flat candidate list held in
 // registers: wave w holds entries [w per, (w+1) per), lane l of round i entry
 // w per + 64 i + l (key 0 = an empty slot; more than need entries in all), and
-// writes their ids to out[0, need) in list (ascending id) order.  Writes nothing
+// puts their ids at positions [0, need) of `out` in list (ascending id) order.  Writes nothing
 // and returns false when `limit` exceeds the lower end of the interval found for
 // the need-th key (the caller's lists may then miss a winner); `limit` 0 never
 // does.  kmax != 0: [kmin, kmax] is the keys' range.  Enters after a barrier.
-template <int NT, int E>
+template <int NT, int E, class O>
 __device__ __forceinline__ bool keep_best_regs(const uint32_t (&key)[E], const int32_t (&cid)[E], int need,
-                                               int32_t* out, Shared<NT>& sh, uint32_t limit, uint32_t kmin,
+                                               const O& out, Shared<NT>& sh, uint32_t limit, uint32_t kmin,
                                                uint32_t kmax) {
   uint32_t base;
   uint64_t width;
@@ -321,7 +346,7 @@ __device__ __forceinline__ bool keep_best_regs(const uint32_t (&key)[E], const i
   const int off = wave_base(kept_w, sh, 0, all);
 #pragma unroll
   for (int i = 0; i < E; ++i)
-    if (k[i]) st_agent(out + off + pos[i], cid[i]);
+    if (k[i]) out.put(off + pos[i], cid[i]);
   return true;
 }
 
@@ -340,7 +365,7 @@ __device__ __noinline__ bool keep_best(int M, int need, int32_t* out, Shared<NT>
     key[i] = at < hi ? sh.ckey[at] : 0u;          // key 0: no entry (no score maps to it)
     cid[i] = at < hi ? sh.cid[at] : 0;
   }
-  return keep_best_regs<NT, E>(key, cid, need, out, sh, limit, 0u, 0u);
+  return keep_best_regs<NT, E>(key, cid, need, RowOut{out}, sh, limit, 0u, 0u);
 }
 
 // Radix select over the order-preserving keys of the whole row (any score
@@ -614,6 +639,8 @@ __device__ __noinline__ void select_row(const float* S, const float* GM, int nel
 // so it holds the row's winners whenever the need-th largest key of the union is
 // at least every L' -- which the merge checks.
 constexpr int LIST = 16;
+constexpr uint32_t LIST_WRITTEN = 0x100;   // set in every stored count word (a zeroed word: not yet stored)
+constexpr int LIST_POLL_LIMIT = 1 << 16;   // bound on the rounds of a merge that polls its lists
 
 // number of lanes whose key k[i] passes `pred`, over the KPL keys of each lane
 template <int KPL, class P>
@@ -622,6 +649,28 @@ __device__ __forceinline__ int wave_count(const uint32_t (&k)[KPL], P pred) {
 #pragma unroll
   for (int i = 0; i < KPL; ++i) c += __popcll(__ballot(pred(k[i])));
   return c;
+}
+
+// wave_count for three thresholds at once: every ballot is taken before the first
+// population count, so the compares issue back to back instead of each waiting for
+// the scalar count of the one before
+template <int KPL>
+__device__ __forceinline__ void wave_count3(const uint32_t (&k)[KPL], uint32_t t1, uint32_t t2, uint32_t t3, int& c1,
+                                            int& c2, int& c3) {
+  uint64_t m1[KPL], m2[KPL], m3[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    m1[i] = __ballot(k[i] >= t1);
+    m2[i] = __ballot(k[i] >= t2);
+    m3[i] = __ballot(k[i] >= t3);
+  }
+  c1 = c2 = c3 = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    c1 += __popcll(m1[i]);
+    c2 += __popcll(m2[i]);
+    c3 += __popcll(m3[i]);
+  }
 }
 
 // The wave's list from its KPL keys per lane (key 0 = none).  Ids ascend over the
@@ -653,9 +702,8 @@ __device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&
 #pragma unroll 1
     for (; b >= 1; b -= 2) {
       const uint32_t t1 = T | (1u << (b - 1)), t2 = T | (2u << (b - 1)), t3 = T | (3u << (b - 1));
-      const int c1 = wave_count<KPL>(k, [=](uint32_t x) { return x >= t1; });
-      const int c2 = wave_count<KPL>(k, [=](uint32_t x) { return x >= t2; });
-      const int c3 = wave_count<KPL>(k, [=](uint32_t x) { return x >= t3; });
+      int c1, c2, c3;
+      wave_count3<KPL>(k, t1, t2, t3, c1, c2, c3);
       const int c = c3 >= LIST ? c3 : (c2 >= LIST ? c2 : c1);
       T = c3 >= LIST ? t3 : (c2 >= LIST ? t2 : (c1 >= LIST ? t1 : T));
       if (c == LIST) { b = -1; break; }
@@ -668,24 +716,42 @@ __device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&
   // keys > T all fit; ties at T fill up to LIST in id order
   const int gt = wave_count<KPL>(k, [=](uint32_t x) { return x > T && x; });
   const int room = LIST - gt;
-  int n = 0, ties = 0;
+  // segment by segment in list order; the ballots of all segments are taken first
+  // (independent of each other), then the running counts
+  constexpr int NS = 2 * KPL;
+  auto mbcnt = [](uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  };
+  uint64_t mt[NS];
 #pragma unroll
-  for (int sgm = 0; sgm < 2 * KPL; ++sgm) {
+  for (int sgm = 0; sgm < NS; ++sgm) {
     const bool mine = (lane >> 5) == sgm / KPL;
     const uint32_t kk = k[sgm % KPL];
-    const bool tie = mine && kk && kk == T && T;
-    const uint64_t mt = __ballot(tie);
-    const int trank = ties + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mt, 0u));
-    const bool keep = mine && kk && (kk > T || (kk == T && (T == 0 || trank < room)));
-    const uint64_t mk = __ballot(keep);
-    const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-    if (keep && pos < LIST) st_agent(dst + pos, (uint64_t)kk | ((uint64_t)(uint32_t)id[sgm % KPL] << 32));
-    n += __popcll(mk);
-    ties += __popcll(mt);
+    mt[sgm] = __ballot(mine && kk && kk == T && T);
+  }
+  uint64_t mk[NS];
+  bool kp[NS];
+  int ties = 0;
+#pragma unroll
+  for (int sgm = 0; sgm < NS; ++sgm) {
+    const bool mine = (lane >> 5) == sgm / KPL;
+    const uint32_t kk = k[sgm % KPL];
+    const int trank = ties + mbcnt(mt[sgm]);
+    kp[sgm] = mine && kk && (kk > T || (kk == T && (T == 0 || trank < room)));
+    mk[sgm] = __ballot(kp[sgm]);
+    ties += __popcll(mt[sgm]);
+  }
+  int n = 0;
+#pragma unroll
+  for (int sgm = 0; sgm < NS; ++sgm) {
+    const int pos = n + mbcnt(mk[sgm]);
+    if (kp[sgm] && pos < LIST)
+      st_agent(dst + pos, (uint64_t)k[sgm % KPL] | ((uint64_t)(uint32_t)id[sgm % KPL] << 32));
+    n += __popcll(mk[sgm]);
   }
   // L' = T, or T + 1 when some ties at T were left out
   const uint32_t Lp = (T && ties > room) ? T + 1 : T;
-  if (lane == 0) st_agent((uint64_t*)meta, (uint64_t)(uint32_t)min(n, LIST) | ((uint64_t)Lp << 32));
+  if (lane == 0) st_agent((uint64_t*)meta, (uint64_t)((uint32_t)min(n, LIST) | LIST_WRITTEN) | ((uint64_t)Lp << 32));
 }
 
 // The last workgroup of a row merges its n_lists wave lists (n_lists * LIST <=
@@ -693,9 +759,15 @@ __device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&
 // the need-th largest key of the union, or the union holds too few entries.  The
 // entries go straight from memory into the registers of keep_best_regs' layout.
 // Called after a barrier that frees `sh` (whose contents are arbitrary).
-template <int NT, int E>
+// POLL: the lists are being stored by other workgroups of the same launch and every
+// list word was zero before it (the fused decode step, whose attention workgroups
+// merge their row's lists themselves).  The loads repeat, bounded by
+// LIST_POLL_LIMIT rounds (false when it runs out), until every count word carries
+// LIST_WRITTEN and every counted entry is nonzero: an entry is one 8-byte store and
+// no key is 0, so a nonzero entry is this launch's key and id.
+template <int NT, int E, bool POLL, class O>
 __device__ __noinline__ bool merge_lists_e(const uint64_t* lists, const uint2* meta, int n_lists, int need, int bq,
-                                           int top_k, int32_t* out, Shared<NT>& sh) {
+                                           int top_k, const O& out, Shared<NT>& sh) {
   constexpr int NW = Shared<NT>::NW;
   static_assert(E * NT <= C_CAP, "candidates fit the exchange buffers");
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
@@ -705,8 +777,9 @@ __device__ __noinline__ bool merge_lists_e(const uint64_t* lists, const uint2* m
   const __amdgpu_buffer_rsrc_t rl = dev_rsrc(lists), rm = dev_rsrc(meta);
   uint32_t key[E];
   int32_t cid[E];
-  uint32_t cnt = 0, kmn = 0xFFFFFFFFu, kmx = 0u, lmax = 0u;
-  {
+  uint32_t cnt, kmn, kmx, lmax;
+#pragma unroll 1
+  for (int round = 0;; ++round) {
     u32x2_t ev[E], mv[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
@@ -714,16 +787,35 @@ __device__ __noinline__ bool merge_lists_e(const uint64_t* lists, const uint2* m
       ev[i] = at < hi ? __builtin_amdgcn_raw_buffer_load_b64(rl, (uint32_t)at * 8u, 0, 16 /* sc1 */) : u32x2_t{};
       mv[i] = at < hi ? __builtin_amdgcn_raw_buffer_load_b64(rm, (uint32_t)(at / LIST) * 8u, 0, 16) : u32x2_t{};
     }
+    bool ok = true;
+    cnt = 0;
+    kmn = 0xFFFFFFFFu;
+    kmx = 0u;
+    lmax = 0u;
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const int at = lo + 64 * i + lane;
-      const bool on = at < hi && (at % LIST) < (int)mv[i][0];
+      const bool on = at < hi && (at % LIST) < (int)(mv[i][0] & 0xFFu);
       key[i] = on ? ev[i][0] : 0u;
       cid[i] = (int32_t)ev[i][1];
       cnt += on;
       if (on) { kmn = min(kmn, key[i]); kmx = max(kmx, key[i]); }
       if (at < hi) lmax = max(lmax, mv[i][1]);
+      if (POLL && at < hi) ok = ok && (mv[i][0] & LIST_WRITTEN) && (!on || ev[i][0] != 0u);
     }
+    if constexpr (!POLL) break;
+    // every entry of the workgroup complete?  (slots alternate between rounds; the
+    // exchange below uses the other sets)
+    int* slot = (round & 1) ? sh.xj[0] : sh.xi[0];
+    const bool wave_ok = __ballot(!ok) == 0ull;   // every lane's (outside the lane-0 branch)
+    if (lane == 0) slot[wv] = wave_ok;
+    __syncthreads();
+    bool all = true;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) all = all && slot[w];
+    if (all) break;
+    if (round >= LIST_POLL_LIMIT) return false;
+    __builtin_amdgcn_s_sleep(1);
   }
   for (int i = t; i < NBINS; i += NT) sh.hist[i] = 0;   // visible after the next barrier
   // one exchange: entries, the largest L', and the keys' range
@@ -748,19 +840,32 @@ __device__ __noinline__ bool merge_lists_e(const uint64_t* lists, const uint2* m
   }
   if (total <= need) return false;
   if (!keep_best_regs<NT, E>(key, cid, need, out, sh, limit, kmin, kmax)) return false;
-  for (int i = need + threadIdx.x; i < top_k; i += NT) st_agent(out + i, i == need ? bq : -1);
+  out.template tail<NT>(need, bq, top_k);
   return true;
 }
 
 // merge_lists_e with as few entries per thread as the lists need (8 for up to 8 NT
 // entries: the 4-wave step's 128 lists of a 128K-token row)
+template <int NT, bool POLL = false, class O>
+__device__ __forceinline__ bool merge_lists_o(const uint64_t* lists, const uint2* meta, int n_lists, int need,
+                                              int bq, int top_k, const O& out, Shared<NT>& sh) {
+  constexpr int EMAX = C_CAP / NT, ESMALL = EMAX > 8 ? 8 : EMAX;
+  if (EMAX > ESMALL && n_lists * LIST <= ESMALL * NT)
+    return merge_lists_e<NT, ESMALL, POLL>(lists, meta, n_lists, need, bq, top_k, out, sh);
+  return merge_lists_e<NT, EMAX, POLL>(lists, meta, n_lists, need, bq, top_k, out, sh);
+}
+// the row's ids to out[0, top_k)
 template <int NT>
 __device__ __forceinline__ bool merge_lists(const uint64_t* lists, const uint2* meta, int n_lists, int need, int bq,
                                             int top_k, int32_t* out, Shared<NT>& sh) {
-  constexpr int EMAX = C_CAP / NT, ESMALL = EMAX > 8 ? 8 : EMAX;
-  if (EMAX > ESMALL && n_lists * LIST <= ESMALL * NT)
-    return merge_lists_e<NT, ESMALL>(lists, meta, n_lists, need, bq, top_k, out, sh);
-  return merge_lists_e<NT, EMAX>(lists, meta, n_lists, need, bq, top_k, out, sh);
+  return merge_lists_o<NT>(lists, meta, n_lists, need, bq, top_k, RowOut{out}, sh);
+}
+// positions [o.lo, o.hi) of the row into LDS, polling lists that other workgroups of
+// the launch are storing (see merge_lists_e)
+template <int NT>
+__device__ __forceinline__ bool merge_lists_slice(const uint64_t* lists, const uint2* meta, int n_lists, int need,
+                                                  int bq, int top_k, const SliceOut& o, Shared<NT>& sh) {
+  return merge_lists_o<NT, true>(lists, meta, n_lists, need, bq, top_k, o, sh);
 }
 
 }  // namespace sel

@@ -591,11 +591,22 @@ STEP_CASES = {
     "decode_batch64": (scaled_down(DECODE, 4 * 600, batch=64), lambda L: L),
     "decode_full": (DECODE, lambda L: L),
     "max_ctx": (MAX_CTX, lambda L: L),
+    # rows the attention workgroups select from the per-wave lists (9 scoring
+    # workgroups per row, the last one ragged), four attention splits per row
+    "lists_small": (scaled_down(DECODE, 4 * 8209, batch=3, top_k=64), lambda L: L - np.array([0, 5, 9])),
+    # the same with row 0's first 200 blocks boosted (STEP_BOOST): 46 of its 63
+    # winners lie in the first wave's 256 blocks, more than a list holds, so the
+    # row takes the exact select over its scores; rows 1 and 2 keep their lists
+    "lists_fallback": (scaled_down(DECODE, 4 * 8209, batch=3, top_k=64), lambda L: L - np.array([0, 5, 9])),
     # geometries the one-launch step does not cover run the two calls
     "fp8kv_positions": (scaled_down(DECODE_FP8KV, 1024, batch=4), lambda L: L - np.arange(4)),
     "decode_batch128": (scaled_down(DECODE, 4 * 600, batch=128), lambda L: L),
     "tiny_f32": (TINY, lambda L: L),
 }
+
+
+# case -> (sequence, blocks [0, n), factor): pooled scales multiplied after pooling
+STEP_BOOST = {"lists_fallback": (0, 200, 8.0)}
 
 
 def _step_oracle_check(inp, d, ws, rows):
@@ -623,13 +634,16 @@ def _step_oracle_check(inp, d, ws, rows):
     kind = _kind(inp.w)
     P.check_attention(_out_np(ws.out)[rows], o_out, kind)
     P.check_lse(ws.lse.cpu().numpy()[rows], o_lse, kind)
+    return o_ids
 
 
 @pytest.mark.parametrize("name", list(STEP_CASES))
 def test_decode_step_equals_decode_index_then_attention(name):
     """indexpool_decode_step gives the results of indexpool_decode_index followed by
     sparse_attn_decode, bit for bit, on two calls in a row (the second checks that
-    the first left its ready words and counters cleared); and against the oracle."""
+    the first left its ready words, counters and lists cleared: the second call's
+    indexer queries differ, so stale lists would select the first call's blocks);
+    and against the oracle."""
     D = _dev()
     w, lens = STEP_CASES[name]
     inp = make_inputs(w)
@@ -641,10 +655,16 @@ def test_decode_step_equals_decode_index_then_attention(name):
     for mode in ("two_calls", "step"):
         d = D.upload(inp)
         D.compress(d)
+        if name in STEP_BOOST:
+            b0, nb, f = STEP_BOOST[name]
+            rows_b = torch.as_tensor(O.pooled_rows(inp, b0, np.arange(nb)), device=d.pooled.scale.device)
+            d.pooled.scale[rows_b] *= f
         ws = D.Workspaces(d, keep_scores=False)
         t = D.NewTokens(new)
         outs = []
-        for _ in range(2):
+        for call in range(2):
+            if call == 1:
+                d.q_idx.copy_(torch.roll(d.q_idx, 1, dims=-1))
             if mode == "step":
                 D.decode_step(d, t, ws)
             else:
@@ -657,6 +677,10 @@ def test_decode_step_equals_decode_index_then_attention(name):
         for a, b in zip(res["two_calls"][0][call], res["step"][0][call]):
             assert torch.equal(a, b), f"call {call}: the step differs from the two calls"
     _, d, ws = res["step"]
+    inp.q_idx = np.roll(inp.q_idx, 1, axis=-1)
     rows = np.unique(np.concatenate([np.arange(min(4, w.batch)), [w.batch - 1]]))
-    _step_oracle_check(inp, d, ws, rows)
+    o_ids = _step_oracle_check(inp, d, ws, rows)
+    if name in STEP_BOOST:
+        # the case does what it is for: row 0's winners overflow the first wave's list
+        assert rows[0] == 0 and int(((o_ids[0] >= 0) & (o_ids[0] < 256)).sum()) > 16
     log(f"  step == two calls (2 calls), oracle ok on rows {rows.tolist()}")
