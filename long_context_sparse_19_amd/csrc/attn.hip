@@ -176,15 +176,15 @@ static_assert(MAX_BLOCKS_PER_SPLIT * 4 <= LAT_H * PROW, "a split's ids fit the P
 // The fused decode step: the ids of positions [sb0, send) of row rl's selection
 // into lid (LDS), and for the rows selected here into the row of sel_out.
 //  - Trivial rows (the query's own block alone, or every block): the ids directly.
-//  - List rows: the row's per-wave lists, merged as soon as every list is stored
-//    (see sel::merge_lists_e).  When the lists cannot decide the row, split 0 runs
+//  - List rows: the row's per-wave lists (whose loads sl started), merged as soon
+//    as every list is stored (see sel::StepLists).  When the lists cannot decide the row, split 0 runs
 //    the exact select over the row's scores once every scoring workgroup has counted
 //    its scores in, and publishes the ids; the other splits wait for them.
 //  - Other rows: the ids published by the row's last scoring workgroup.
 // ss (the first sub-tile buffer) holds the selection state; it is free again on
 // return.  Waits only on workgroups that started earlier, bounded as the others.
 __device__ __forceinline__ void step_select(const AttnArgs& a, const RowCtx& c, int rl, int split, int sb0,
-                                            int send, int32_t* lid, uint8_t* kv0) {
+                                            int send, int32_t* lid, uint8_t* kv0, sel::StepLists<NTA, 8>& sl) {
   sel::Shared<NTA>& ss = *reinterpret_cast<sel::Shared<NTA>*>(kv0);
   const int nel = c.p >> 2;                      // eligible blocks j < b_q
   const int need = min(a.top_k, nel + 1) - 1;
@@ -198,10 +198,7 @@ __device__ __forceinline__ void step_select(const AttnArgs& a, const RowCtx& c, 
     }
   } else {
     const int n_lists = scorek::fused_list_count<STEP_NWV, STEP_TILES>(nel, need, a.step_lists != nullptr);
-    local = n_lists > 0 &&
-            sel::merge_lists_slice<NTA>(a.step_lists + (int64_t)rl * a.step_max_lists * sel::LIST,
-                                        a.step_meta + (int64_t)rl * a.step_max_lists, n_lists, need, nel, a.top_k,
-                                        sel::SliceOut{lid, sb0, send}, ss);
+    local = n_lists > 0 && sl.merge(n_lists, need, nel, a.top_k, sel::SliceOut{lid, sb0, send}, ss);
     if (!local && n_lists > 0 && split == 0) {
       constexpr int KEYS = STEP_NWV * STEP_TILES * 32;
       const uint32_t n_run = (uint32_t)((nel + KEYS - 1) / KEYS);
@@ -248,8 +245,12 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const int bid,
   const int send = min(a.top_k, sb0 + a.blocks_per_split);
   const int nsub = (send - sb0 + 15) >> 4;
   const int hs = 32 * hb + l32;                  // head of this lane in the S^T layout
-  NewRow nr{~0u, nullptr};
-  if constexpr (STEP) nr = NewRow{(uint32_t)a.L.tok_row(c.b, c.p), a.k_new + (int64_t)c.b * a.k_new_stride};
+  // STEP: the first loads of the row's lists go out before anything else, while the
+  // row's length is still on its way
+  sel::StepLists<NTA, 8> sl;
+  if constexpr (STEP)
+    sl.start(a.step_lists + (int64_t)rl * a.step_max_lists * sel::LIST, a.step_meta + (int64_t)rl * a.step_max_lists,
+             a.step_lists_n);
 
   // prologue: the selection ids (block-table entries and this lane's rows of
   // sub-tiles 0 and 1); the query row into kv1; sub-tile 0; q into registers; then
@@ -293,9 +294,11 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const int bid,
 #pragma unroll
     for (int k = 0; k < KV_LOADS; ++k) load_column(qsrc, kv1, k);
   }
+  NewRow nr{~0u, nullptr};
   if constexpr (STEP) {
+    nr = NewRow{(uint32_t)a.L.tok_row(c.b, c.p), a.k_new + (int64_t)c.b * a.k_new_stride};
     __builtin_amdgcn_sched_barrier(0);
-    step_select(a, c, rl, split, sb0, send, lid, kv0);
+    step_select(a, c, rl, split, sb0, send, lid, kv0, sl);
     load_ids();
   }
   // every query DMA is issued before anything consumes the ids
@@ -1154,6 +1157,9 @@ hipError_t launch_decode_step(const StepArgs& a, hipStream_t s) {
   k.gx = (a.score.max_blocks + KEYS - 1) / KEYS;
   k.n_score = k.gx * a.score.n_rows;
   k.n_app = a.score.with_append ? a.score.append.batch : 0;   // one workgroup per sequence
+  k.at.step_lists_n = STEP_NWV * k.gx;                         // lists of the longest row
+  if (k.at.step_lists_n * sel::LIST > 8 * NTA || k.at.step_lists_n > a.attn.step_max_lists)
+    return hipErrorInvalidValue;
   const int64_t grid = (int64_t)k.n_score + k.n_app + (int64_t)a.attn.n_rows * a.attn.n_split;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   launch(K_STEP, decode_step_kernel, dim3((unsigned)grid), dim3(NTA), s, k);

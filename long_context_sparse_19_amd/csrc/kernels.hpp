@@ -187,7 +187,8 @@ struct AttnArgs {
   // (for the exact fallback), and the row's ids written to sel_out (= sel)
   uint64_t* step_lists;
   uint2* step_meta;
-  int step_max_lists;
+  int step_max_lists;          // lists per row in step_lists / step_meta
+  int step_lists_n;            // lists of the longest row (<= step_max_lists, * 16 <= 8 * 256)
   const float* step_scores;
   int64_t step_ld;
   const float* step_gm;

@@ -754,71 +754,51 @@ __device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&
   if (lane == 0) st_agent((uint64_t*)meta, (uint64_t)((uint32_t)min(n, LIST) | LIST_WRITTEN) | ((uint64_t)Lp << 32));
 }
 
-// The last workgroup of a row merges its n_lists wave lists (n_lists * LIST <=
-// C_CAP, n_lists <= NT): returns false (nothing written) when a list's L' exceeds
-// the need-th largest key of the union, or the union holds too few entries.  The
-// entries go straight from memory into the registers of keep_best_regs' layout.
-// Called after a barrier that frees `sh` (whose contents are arbitrary).
-// POLL: the lists are being stored by other workgroups of the same launch and every
-// list word was zero before it (the fused decode step, whose attention workgroups
-// merge their row's lists themselves).  The loads repeat, bounded by
-// LIST_POLL_LIMIT rounds (false when it runs out), until every count word carries
-// LIST_WRITTEN and every counted entry is nonzero: an entry is one 8-byte store and
-// no key is 0, so a nonzero entry is this launch's key and id.
-template <int NT, int E, bool POLL, class O>
-__device__ __noinline__ bool merge_lists_e(const uint64_t* lists, const uint2* meta, int n_lists, int need, int bq,
-                                           int top_k, const O& out, Shared<NT>& sh) {
-  constexpr int NW = Shared<NT>::NW;
-  static_assert(E * NT <= C_CAP, "candidates fit the exchange buffers");
-  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
-  const int M = n_lists * LIST;
-  const int per = (M + NW - 1) / NW;
-  const int lo = wv * per, hi = min(M, lo + per);
-  const __amdgpu_buffer_rsrc_t rl = dev_rsrc(lists), rm = dev_rsrc(meta);
-  uint32_t key[E];
-  int32_t cid[E];
-  uint32_t cnt, kmn, kmx, lmax;
-#pragma unroll 1
-  for (int round = 0;; ++round) {
-    u32x2_t ev[E], mv[E];
+// A merge's candidates in the registers of keep_best_regs' layout, from loaded list
+// words: slot at = lo + 64 i + lane holds entry ev[i] of list at / LIST, whose count
+// word is mv[i]; the wave's slots end at m (slots at >= m hold no entry).  ok (checked by the fused decode step,
+// whose lists are being stored while it loads them, and were zero before its
+// launch): every list below m is stored (its count word carries LIST_WRITTEN) and so
+// is every counted entry (nonzero: an entry is one 8-byte store and no key is 0).
+template <int E>
+__device__ __forceinline__ void list_cands(const u32x2_t (&ev)[E], const u32x2_t (&mv)[E], int lo, int m,
+                                           uint32_t (&key)[E], int32_t (&cid)[E], uint32_t& cnt, uint32_t& kmn,
+                                           uint32_t& kmx, uint32_t& lmax, bool& ok) {
+  const int lane = threadIdx.x & 63;
+  ok = true;
+  cnt = 0;
+  kmn = 0xFFFFFFFFu;
+  kmx = 0u;
+  lmax = 0u;
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const int at = lo + 64 * i + lane;
-      ev[i] = at < hi ? __builtin_amdgcn_raw_buffer_load_b64(rl, (uint32_t)at * 8u, 0, 16 /* sc1 */) : u32x2_t{};
-      mv[i] = at < hi ? __builtin_amdgcn_raw_buffer_load_b64(rm, (uint32_t)(at / LIST) * 8u, 0, 16) : u32x2_t{};
+  for (int i = 0; i < E; ++i) {
+    const int at = lo + 64 * i + lane;
+    const bool in = at < m;
+    const bool on = in && (at % LIST) < (int)(mv[i][0] & 0xFFu);
+    key[i] = on ? ev[i][0] : 0u;
+    cid[i] = (int32_t)ev[i][1];
+    cnt += on;
+    if (on) { kmn = min(kmn, key[i]); kmx = max(kmx, key[i]); }
+    if (in) {
+      lmax = max(lmax, mv[i][1]);
+      ok = ok && (mv[i][0] & LIST_WRITTEN) && (!on || ev[i][0] != 0u);
     }
-    bool ok = true;
-    cnt = 0;
-    kmn = 0xFFFFFFFFu;
-    kmx = 0u;
-    lmax = 0u;
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const int at = lo + 64 * i + lane;
-      const bool on = at < hi && (at % LIST) < (int)(mv[i][0] & 0xFFu);
-      key[i] = on ? ev[i][0] : 0u;
-      cid[i] = (int32_t)ev[i][1];
-      cnt += on;
-      if (on) { kmn = min(kmn, key[i]); kmx = max(kmx, key[i]); }
-      if (at < hi) lmax = max(lmax, mv[i][1]);
-      if (POLL && at < hi) ok = ok && (mv[i][0] & LIST_WRITTEN) && (!on || ev[i][0] != 0u);
-    }
-    if constexpr (!POLL) break;
-    // every entry of the workgroup complete?  (slots alternate between rounds; the
-    // exchange below uses the other sets)
-    int* slot = (round & 1) ? sh.xj[0] : sh.xi[0];
-    const bool wave_ok = __ballot(!ok) == 0ull;   // every lane's (outside the lane-0 branch)
-    if (lane == 0) slot[wv] = wave_ok;
-    __syncthreads();
-    bool all = true;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) all = all && slot[w];
-    if (all) break;
-    if (round >= LIST_POLL_LIMIT) return false;
-    __builtin_amdgcn_s_sleep(1);
   }
+}
+
+// The merge once the candidates are in registers: one exchange (entries, the
+// largest L', the keys' range), then the exact select of the need best.  False
+// (nothing written) when a list's L' exceeds the need-th largest key of the union,
+// or the union holds too few entries.  Enters after a barrier that frees `sh`
+// (whose contents are arbitrary), and uses no slot of set 0 of sh.xi / sh.xj before
+// its first barrier.
+template <int NT, int E, class O>
+__device__ __forceinline__ bool merge_cands(const uint32_t (&key)[E], const int32_t (&cid)[E], uint32_t cnt,
+                                            uint32_t kmn, uint32_t kmx, uint32_t lmax, int need, int bq, int top_k,
+                                            const O& out, Shared<NT>& sh) {
+  constexpr int NW = Shared<NT>::NW;
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   for (int i = t; i < NBINS; i += NT) sh.hist[i] = 0;   // visible after the next barrier
-  // one exchange: entries, the largest L', and the keys' range
   const int tot = wave_sum((int)cnt);
   lmax = wave_umax(lmax);
   const uint32_t mn = wave_umin(kmn), mx = wave_umax(kmx);
@@ -844,29 +824,108 @@ __device__ __noinline__ bool merge_lists_e(const uint64_t* lists, const uint2* m
   return true;
 }
 
-// merge_lists_e with as few entries per thread as the lists need (8 for up to 8 NT
-// entries: the 4-wave step's 128 lists of a 128K-token row)
-template <int NT, bool POLL = false, class O>
-__device__ __forceinline__ bool merge_lists_o(const uint64_t* lists, const uint2* meta, int n_lists, int need,
-                                              int bq, int top_k, const O& out, Shared<NT>& sh) {
-  constexpr int EMAX = C_CAP / NT, ESMALL = EMAX > 8 ? 8 : EMAX;
-  if (EMAX > ESMALL && n_lists * LIST <= ESMALL * NT)
-    return merge_lists_e<NT, ESMALL, POLL>(lists, meta, n_lists, need, bq, top_k, out, sh);
-  return merge_lists_e<NT, EMAX, POLL>(lists, meta, n_lists, need, bq, top_k, out, sh);
+// The last workgroup of a row merges its n_lists wave lists (n_lists * LIST <=
+// E NT <= C_CAP, n_lists <= NT): the entries go straight from memory into
+// registers (device-coherent loads), then merge_cands.  Called after a barrier that
+// frees `sh`.
+template <int NT, int E, class O>
+__device__ __noinline__ bool merge_lists_e(const uint64_t* lists, const uint2* meta, int n_lists, int need, int bq,
+                                           int top_k, const O& out, Shared<NT>& sh) {
+  constexpr int NW = Shared<NT>::NW;
+  static_assert(E * NT <= C_CAP, "candidates fit the exchange buffers");
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int M = n_lists * LIST;
+  const int per = (M + NW - 1) / NW;
+  const int lo = wv * per, hi = min(M, lo + per);
+  const __amdgpu_buffer_rsrc_t rl = dev_rsrc(lists), rm = dev_rsrc(meta);
+  u32x2_t ev[E], mv[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int at = lo + 64 * i + lane;
+    ev[i] = at < hi ? __builtin_amdgcn_raw_buffer_load_b64(rl, (uint32_t)at * 8u, 0, 16 /* sc1 */) : u32x2_t{};
+    mv[i] = at < hi ? __builtin_amdgcn_raw_buffer_load_b64(rm, (uint32_t)(at / LIST) * 8u, 0, 16) : u32x2_t{};
+  }
+  uint32_t key[E];
+  int32_t cid[E];
+  uint32_t cnt, kmn, kmx, lmax;
+  bool ok;
+  list_cands<E>(ev, mv, lo, hi, key, cid, cnt, kmn, kmx, lmax, ok);
+  return merge_cands<NT, E>(key, cid, cnt, kmn, kmx, lmax, need, bq, top_k, out, sh);
 }
-// the row's ids to out[0, top_k)
+
+// merge_lists_e with as few entries per thread as the lists need (8 for up to 8 NT
+// entries: the 4-wave step's 128 lists of a 128K-token row); the row's ids to
+// out[0, top_k)
 template <int NT>
 __device__ __forceinline__ bool merge_lists(const uint64_t* lists, const uint2* meta, int n_lists, int need, int bq,
                                             int top_k, int32_t* out, Shared<NT>& sh) {
-  return merge_lists_o<NT>(lists, meta, n_lists, need, bq, top_k, RowOut{out}, sh);
+  constexpr int EMAX = C_CAP / NT, ESMALL = EMAX > 8 ? 8 : EMAX;
+  if (EMAX > ESMALL && n_lists * LIST <= ESMALL * NT)
+    return merge_lists_e<NT, ESMALL>(lists, meta, n_lists, need, bq, top_k, RowOut{out}, sh);
+  return merge_lists_e<NT, EMAX>(lists, meta, n_lists, need, bq, top_k, RowOut{out}, sh);
 }
-// positions [o.lo, o.hi) of the row into LDS, polling lists that other workgroups of
-// the launch are storing (see merge_lists_e)
-template <int NT>
-__device__ __forceinline__ bool merge_lists_slice(const uint64_t* lists, const uint2* meta, int n_lists, int need,
-                                                  int bq, int top_k, const SliceOut& o, Shared<NT>& sh) {
-  return merge_lists_o<NT, true>(lists, meta, n_lists, need, bq, top_k, o, sh);
-}
+
+// The fused decode step's merge of one row's lists, by a workgroup that consumes
+// the ids itself, while other workgroups of the launch are still storing the lists
+// (which were zero before the launch).  start() issues the loads of every slot of
+// the m_lists lists the row may have (m_lists * LIST <= E NT) before the row's
+// length is known; merge() takes the row's n_lists <= m_lists lists, loads again
+// (bounded by LIST_POLL_LIMIT rounds, false when it runs out) until all of them
+// are stored, and merges them (merge_cands).
+template <int NT, int E>
+struct StepLists {
+  static constexpr int NW = NT / 64;
+  __amdgpu_buffer_rsrc_t rl, rm;
+  int lo, hi;
+  u32x2_t ev[E], mv[E];
+  __device__ __forceinline__ void load() {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int at = lo + 64 * i + lane;
+      ev[i] = at < hi ? __builtin_amdgcn_raw_buffer_load_b64(rl, (uint32_t)at * 8u, 0, 16 /* sc1 */) : u32x2_t{};
+      mv[i] = at < hi ? __builtin_amdgcn_raw_buffer_load_b64(rm, (uint32_t)(at / LIST) * 8u, 0, 16) : u32x2_t{};
+    }
+  }
+  __device__ __forceinline__ void start(const uint64_t* lists, const uint2* meta, int m_lists) {
+    const int wv = threadIdx.x >> 6;
+    const int m = m_lists * LIST;
+    const int per = (m + NW - 1) / NW;
+    rl = dev_rsrc(lists);
+    rm = dev_rsrc(meta);
+    lo = wv * per;
+    hi = min(m, lo + per);
+    load();
+  }
+  template <class O>
+  __device__ __forceinline__ bool merge(int n_lists, int need, int bq, int top_k, const O& out, Shared<NT>& sh) {
+    static_assert(E * NT <= C_CAP, "candidates fit the exchange buffers");
+    const int wv = threadIdx.x >> 6;
+    const int M = n_lists * LIST;
+    uint32_t key[E];
+    int32_t cid[E];
+    uint32_t cnt, kmn, kmx, lmax;
+#pragma unroll 1
+    for (int round = 0;; ++round) {
+      bool ok;
+      list_cands<E>(ev, mv, lo, min(M, hi), key, cid, cnt, kmn, kmx, lmax, ok);
+      // every slot of the workgroup stored?  (slots alternate between rounds;
+      // merge_cands uses the other sets before its first barrier)
+      int* slot = (round & 1) ? sh.xj[0] : sh.xi[0];
+      const bool wave_ok = __ballot(!ok) == 0ull;   // every lane's (outside the lane-0 branch)
+      if ((threadIdx.x & 63) == 0) slot[wv] = wave_ok;
+      __syncthreads();
+      bool all = true;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) all = all && slot[w];
+      if (all) break;
+      if (round >= LIST_POLL_LIMIT) return false;
+      __builtin_amdgcn_s_sleep(1);
+      load();
+    }
+    return merge_cands<NT, E>(key, cid, cnt, kmn, kmx, lmax, need, bq, top_k, out, sh);
+  }
+};
 
 }  // namespace sel
 }  // namespace ip
