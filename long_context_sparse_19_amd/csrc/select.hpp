@@ -144,6 +144,13 @@ __device__ __forceinline__ void x_uminmax(uint32_t& mn, uint32_t& mx, Shared<NT>
   mx = b;
 }
 
+// wave_excl of a flag (x in {0, 1}): one ballot instead of a scan
+__device__ __forceinline__ int wave_excl_bit(bool x, int& total) {
+  const uint64_t m = __ballot(x);
+  total = __popcll(m);
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // exclusive prefix of x over the lanes, and the wave total
 __device__ __forceinline__ int wave_excl(int x, int& total) {
   const int incl = wave_incl_scan(x);
@@ -328,7 +335,7 @@ __device__ __forceinline__ bool keep_best_regs(const uint32_t (&key)[E], const i
   for (int i = 0; i < E; ++i) {
     const bool in = key[i] && key[i] >= base && (uint64_t)key[i] < top;
     int t;
-    pos[i] = tie_w + wave_excl(in, t);
+    pos[i] = tie_w + wave_excl_bit(in, t);
     tie_w += t;
   }
   int all;
@@ -340,7 +347,7 @@ __device__ __forceinline__ bool keep_best_regs(const uint32_t (&key)[E], const i
     const bool in = key[i] && key[i] >= base && (uint64_t)key[i] < top;
     k[i] = (uint64_t)key[i] >= top || (in && (whole || tie0 + pos[i] < rem));
     int t;
-    pos[i] = kept_w + wave_excl(k[i], t);         // now: this entry's place among the wave's kept
+    pos[i] = kept_w + wave_excl_bit(k[i], t);     // now: this entry's place among the wave's kept
     kept_w += t;
   }
   const int off = wave_base(kept_w, sh, 0, all);
