@@ -42,7 +42,8 @@ struct KdaShared {
   float nrm[2][2];                   // per-wave sums of q^2, k^2 (waves 0 and 1)
 };
 
-__device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+// x sigmoid(x), the reciprocal from the hardware (v_rcp_f32, 1 ulp)
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 // sum over the 8 row groups of a wave (lanes l, l ^ 8, l ^ 16, ... hold one column set)
 __device__ __forceinline__ float4 wave_rows_sum(float4 v) {
@@ -182,17 +183,26 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 struct KdaChunkShared {
   float hx[3][3][KD];                // conv taps x_{t-3 .. t-1}: q, k (128 channels), v (first 32)
   float yq[CC][KD], yk[CC][KD];      // raw inputs, then conv + SiLU
-  float yv[CC][KSL];
+  float yv[CC][KSL];                 // raw v inputs
   float g[CC][KD];                   // log2 alpha, then its running sum (G in base 2)
   float qt[CC][CP], kt[CC][CP], kh[CC][CP];
   float kb[CC][KBP];
   float S[KD][SP];
-  float A[CC][CC + 1], B[CC][CC + 1];
-  float U[CC][SP];                   // v - S0^T k~, then u
+  float A[2][CC][CC + 1], B[2][CC][CC + 1];   // halves over channels 0..63, 64..127
+  float U[CC][SP];                   // conv + SiLU of v, then v - S0^T k~, then u
   float gl[KD];                      // e^{G_last}
   float beta[CC], rq[CC], rk[CC];
   int unsafe;
 };
+
+// x[k] of a register array for a k known only at run time (compares, no indexing)
+template <int N>
+__device__ __forceinline__ float pick_tap(const float (&x)[N], int k) {
+  float v = x[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) v = i == k ? x[i] : v;
+  return v;
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -224,8 +234,7 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
   // the slice's v channel t
   const int cw = tid >> 7, cc = tid & (KD - 1);
   const float4 wqk = *(const float4*)(a.conv_w + ((int64_t)cw * HD + (int64_t)h * KD + cc) * 4);
-  float4 wv4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (tid < KSL) wv4 = *(const float4*)(a.conv_w + (2 * HD + (int64_t)h * KD + KSL * sl + tid) * 4);
+  const float4 wv4c = *(const float4*)(a.conv_w + (2 * HD + (int64_t)h * KD + KSL * sl + (tid & (KSL - 1))) * 4);
   const float rs = rsqrtf((float)KD);
 
   // the inputs of a block, fetched into registers one block ahead: x (zero past the
@@ -255,28 +264,20 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
     }
     if (tid < CC) pbeta = tid < n ? a.beta[((int64_t)b * T + t0 + tid) * a.heads + h] : 0.f;
   };
+  // 16-byte LDS stores (8 channels of a token per thread, 4 log2 alpha per store)
+  auto widen8 = [](const u32x4_t& x, float* dst) {
+    *(float4*)dst = make_float4(bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1]));
+    *(float4*)(dst + 4) = make_float4(bf16_lo(x[2]), bf16_hi(x[2]), bf16_lo(x[3]), bf16_hi(x[3]));
+  };
   auto stage = [&]() {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sh.yq[fi][fc0 + 2 * e] = bf16_lo(pxq[e]);
-      sh.yq[fi][fc0 + 2 * e + 1] = bf16_hi(pxq[e]);
-      sh.yk[fi][fc0 + 2 * e] = bf16_lo(pxk[e]);
-      sh.yk[fi][fc0 + 2 * e + 1] = bf16_hi(pxk[e]);
-    }
-    if (tid < CC * KSL / 8) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sh.yv[fiv][fv0 + 2 * e] = bf16_lo(pxv[e]);
-        sh.yv[fiv][fv0 + 2 * e + 1] = bf16_hi(pxv[e]);
-      }
-    }
+    widen8(pxq, &sh.yq[fi][fc0]);
+    widen8(pxk, &sh.yk[fi][fc0]);
+    if (tid < CC * KSL / 8) widen8(pxv, &sh.yv[fiv][fv0]);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int idx = tid + KT * k, ia = idx >> 5, c4 = idx & 31;
-      sh.g[ia][4 * c4] = __builtin_amdgcn_logf(pal[k].x);
-      sh.g[ia][4 * c4 + 1] = __builtin_amdgcn_logf(pal[k].y);
-      sh.g[ia][4 * c4 + 2] = __builtin_amdgcn_logf(pal[k].z);
-      sh.g[ia][4 * c4 + 3] = __builtin_amdgcn_logf(pal[k].w);
+      *(float4*)&sh.g[ia][4 * c4] = make_float4(__builtin_amdgcn_logf(pal[k].x), __builtin_amdgcn_logf(pal[k].y),
+                                                __builtin_amdgcn_logf(pal[k].z), __builtin_amdgcn_logf(pal[k].w));
     }
     if (tid < CC) sh.beta[tid] = pbeta;
     if (tid == 0) sh.unsafe = 0;
@@ -294,33 +295,48 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
     // ---- short convolution + SiLU in place, taps sliding in registers (the taps after
     //      the block are the last 3 inputs up to token n-1); the running sum G
     {
+      // every output of the block is independent of the others (the taps are inputs):
+      // the 16 tokens of a channel are read, convolved and written unrolled
       float (*y)[KD] = cw ? sh.yk : sh.yq;
-      float x0 = sh.hx[cw][0][cc], x1 = sh.hx[cw][1][cc], x2 = sh.hx[cw][2][cc];
-      for (int i = 0; i < CC; ++i) {
-        const float xt = y[i][cc];
-        y[i][cc] = silu(fmaf(wqk.x, x0, fmaf(wqk.y, x1, fmaf(wqk.z, x2, wqk.w * xt))));
-        if (i < n) { x0 = x1; x1 = x2; x2 = xt; }
+      {
+        float x[CC + 3];
+        x[0] = sh.hx[cw][0][cc];
+        x[1] = sh.hx[cw][1][cc];
+        x[2] = sh.hx[cw][2][cc];
+#pragma unroll
+        for (int i = 0; i < CC; ++i) x[i + 3] = y[i][cc];
+#pragma unroll
+        for (int i = 0; i < CC; ++i)
+          y[i][cc] = silu(fmaf(wqk.x, x[i], fmaf(wqk.y, x[i + 1], fmaf(wqk.z, x[i + 2], wqk.w * x[i + 3]))));
+        // the taps after the block: inputs n-3 .. n-1 (n = tokens of the block)
+        sh.hx[cw][0][cc] = pick_tap(x, n);
+        sh.hx[cw][1][cc] = pick_tap(x, n + 1);
+        sh.hx[cw][2][cc] = pick_tap(x, n + 2);
       }
-      sh.hx[cw][0][cc] = x0;
-      sh.hx[cw][1][cc] = x1;
-      sh.hx[cw][2][cc] = x2;
-      if (tid < KSL) {
-        float v0 = sh.hx[2][0][tid], v1 = sh.hx[2][1][tid], v2 = sh.hx[2][2][tid];
-        for (int i = 0; i < CC; ++i) {
-          const float xt = sh.yv[i][tid];
-          sh.yv[i][tid] = silu(fmaf(wv4.x, v0, fmaf(wv4.y, v1, fmaf(wv4.z, v2, wv4.w * xt))));
-          if (i < n) { v0 = v1; v1 = v2; v2 = xt; }
+      // the slice's v channels: thread -> channel t % 32, tokens 2 (t / 32) and the next,
+      // into U (yv keeps the raw inputs; their taps move on in the next phase)
+      {
+        const int c = tid & (KSL - 1), i0 = 2 * (tid >> 5);
+        float x[5];
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+          const int j = i0 - 3 + m;                  // input token (negative: a tap)
+          const float in = sh.yv[max(j, 0)][c], tap = sh.hx[2][min(j + 3, 2)][c];
+          x[m] = j >= 0 ? in : tap;
         }
-        sh.hx[2][0][tid] = v0;
-        sh.hx[2][1][tid] = v1;
-        sh.hx[2][2][tid] = v2;
+        const float4 w = wv4c;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          sh.U[i0 + m][c] = silu(fmaf(w.x, x[m], fmaf(w.y, x[m + 1], fmaf(w.z, x[m + 2], w.w * x[m + 3]))));
       }
       if (tid < KD) {
-        float run = 0.f;
-        for (int i = 0; i < CC; ++i) {
-          run += sh.g[i][tid];
-          sh.g[i][tid] = run;
-        }
+        float gv[CC];
+#pragma unroll
+        for (int i = 0; i < CC; ++i) gv[i] = sh.g[i][tid];
+#pragma unroll
+        for (int i = 1; i < CC; ++i) gv[i] += gv[i - 1];
+#pragma unroll
+        for (int i = 0; i < CC; ++i) sh.g[i][tid] = gv[i];
       }
     }
     block_sync_lds();
@@ -339,6 +355,18 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
       s2 += __shfl_xor(s2, 2);
       s2 += __shfl_xor(s2, 4);
       if (c0 == 0) (cw ? sh.rk : sh.rq)[i] = rsqrtf(s2 + 1e-6f);
+      // the v taps after the block (every read of the old taps is done)
+      if (tid < KSL) {
+        float x[CC + 3];
+        x[0] = sh.hx[2][0][tid];
+        x[1] = sh.hx[2][1][tid];
+        x[2] = sh.hx[2][2][tid];
+#pragma unroll
+        for (int j = 0; j < CC; ++j) x[j + 3] = sh.yv[j][tid];
+        sh.hx[2][0][tid] = pick_tap(x, n);
+        sh.hx[2][1][tid] = pick_tap(x, n + 1);
+        sh.hx[2][2][tid] = pick_tap(x, n + 2);
+      }
     }
     block_sync_lds();
     // ---- decayed operands: thread -> token t / 16, channels 8(t % 16) .. +7
@@ -365,7 +393,8 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
     }
     block_sync_lds();
     // ---- S0 products and the block coefficients on MFMA: waves 0 / 1 take k~ S0 for
-    //      columns 16w .. +15 (then U = v - k~ S0) and A / B; waves 2 / 3 keep q~ S0
+    //      columns 16w .. +15 (then U = v - k~ S0), waves 2 / 3 keep q~ S0; then each
+    //      wave one half (64 channels) of A (waves 0 / 1) or B (waves 2 / 3)
     f32x4_t r = {0.f, 0.f, 0.f, 0.f};
     {
       const int nt = wv & 1;
@@ -376,20 +405,20 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(lhs[r16][4 * s + kq], sh.S[4 * s + kq][16 * nt + r16], acc, 0, 0, 0);
       if (wv < 2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sh.U[4 * kq + e][16 * nt + r16] = sh.yv[4 * kq + e][16 * nt + r16] - acc[e];
-        const float (*left)[CP] = wv == 0 ? sh.kt : sh.qt;
-        f32x4_t c2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int s = 0; s < KD / 4; ++s)
-          c2 = __builtin_amdgcn_mfma_f32_16x16x4f32(left[r16][4 * s + kq], sh.kh[r16][4 * s + kq], c2, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 4 * kq + e;
-          if (wv == 0) sh.A[row][r16] = r16 < row ? c2[e] : 0.f;
-          else sh.B[row][r16] = r16 <= row ? c2[e] : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) sh.U[4 * kq + e][16 * nt + r16] -= acc[e];
       } else {
         r = acc;
+      }
+      const int k0 = 64 * nt;
+      f32x4_t c2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int s = 0; s < KD / 8; ++s)
+        c2 = __builtin_amdgcn_mfma_f32_16x16x4f32(lhs[r16][k0 + 4 * s + kq], sh.kh[r16][k0 + 4 * s + kq], c2, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 4 * kq + e;
+        if (wv < 2) sh.A[nt][row][r16] = r16 < row ? c2[e] : 0.f;
+        else sh.B[nt][row][r16] = r16 <= row ? c2[e] : 0.f;
       }
     }
     block_sync_lds();
@@ -405,11 +434,18 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
           sa = fmaf(sh.yk[i][c] * nki * d, kj, sa);
           sb = fmaf(sh.yq[i][c] * nq * d, kj, sb);
         }
-        if (j < i) sh.A[i][j] = sa;
-        sh.B[i][j] = sb;
+        if (j < i) {
+          sh.A[0][i][j] = sa;
+          sh.A[1][i][j] = 0.f;
+        }
+        sh.B[0][i][j] = sb;
+        sh.B[1][i][j] = 0.f;
       }
       block_sync_lds();
     }
+    // A as one matrix (its two channel halves summed, one entry per thread)
+    sh.A[0][tid >> 4][tid & 15] += sh.A[1][tid >> 4][tid & 15];
+    block_sync_lds();
     // ---- u by forward substitution: lanes 0 .. 31 of wave 0, one column each
     if (tid < KSL) {
       float u[CC];
@@ -417,7 +453,7 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
       for (int i = 0; i < CC; ++i) {
         float acc = sh.U[i][tid];
 #pragma unroll
-        for (int j = 0; j < i; ++j) acc = fmaf(-sh.A[i][j], u[j], acc);
+        for (int j = 0; j < i; ++j) acc = fmaf(-sh.A[0][i][j], u[j], acc);
         u[i] = sh.beta[i] * acc;
       }
 #pragma unroll
@@ -428,8 +464,11 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
     if (wv >= 2) {
       const int nt = wv & 1;
 #pragma unroll
-      for (int s = 0; s < CC / 4; ++s)
-        r = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.B[r16][4 * s + kq], sh.U[4 * s + kq][16 * nt + r16], r, 0, 0, 0);
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int s = 0; s < CC / 4; ++s)
+          r = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.B[hb][r16][4 * s + kq], sh.U[4 * s + kq][16 * nt + r16], r, 0, 0,
+                                                   0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 4 * kq + e;
