@@ -180,7 +180,7 @@ constexpr float G_SAFE = -115.f;          // log2 of the decay: 2^115 stays insi
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-struct KdaChunkShared {
+struct __align__(16) KdaChunkShared {
   float hx[3][3][KD];                // conv taps x_{t-3 .. t-1}: q, k (128 channels), v (first 32)
   float yq[CC][KD], yk[CC][KD];      // raw inputs, then conv + SiLU
   float yv[CC][KSL];                 // raw v inputs
@@ -341,15 +341,19 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
     }
     block_sync_lds();
     // ---- 1 / norms of q and k per token: thread -> (q or k, token (t % 128) / 8), 16
-    //      channels (t % 8) + 8j, summed over the 8 lanes of the token
+    //      channels 16 (t % 8) .. +15 (four 16-byte reads), summed over the 8 lanes of the
+    //      token
     {
       const float (*y)[KD] = cw ? sh.yk : sh.yq;
       const int i = cc >> 3, c0 = cc & 7;
       float s2 = 0.f;
 #pragma unroll
-      for (int j = 0; j < KD / 8; ++j) {
-        const float v = y[i][c0 + 8 * j];
-        s2 = fmaf(v, v, s2);
+      for (int j = 0; j < 4; ++j) {
+        const float4 v = *(const float4*)&y[i][16 * c0 + 4 * j];
+        s2 = fmaf(v.x, v.x, s2);
+        s2 = fmaf(v.y, v.y, s2);
+        s2 = fmaf(v.z, v.z, s2);
+        s2 = fmaf(v.w, v.w, s2);
       }
       s2 += __shfl_xor(s2, 1);
       s2 += __shfl_xor(s2, 2);
@@ -370,26 +374,44 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
     }
     block_sync_lds();
     // ---- decayed operands: thread -> token t / 16, channels 8(t % 16) .. +7
+    //      (all reads issued together, 8- and 16-byte LDS accesses)
     {
       const int i = tid >> 4, c0 = 8 * (tid & 15);
       const float nq = sh.rq[i], nk = sh.rk[i];
+      float G[8], GL[8], q[8], k[8];
+      auto ld8 = [](const float* p, float (&d)[8]) {
+        const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+        d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w; d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
+      };
+      ld8(&sh.g[i][c0], G);
+      ld8(&sh.g[CC - 1][c0], GL);
+      ld8(&sh.yq[i][c0], q);
+      ld8(&sh.yk[i][c0], k);
+      float qt[8], kt[8], kh[8], kb[8], eg[8];
       bool bad = false;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int c = c0 + e;
-        const float G = sh.g[i][c], GL = sh.g[CC - 1][c];
-        const float q = sh.yq[i][c] * nq, k = sh.yk[i][c] * nk;
-        const float eg = __builtin_amdgcn_exp2f(G);
-        sh.qt[i][c] = q * eg;
-        sh.kt[i][c] = k * eg;
-        sh.kh[i][c] = k * __builtin_amdgcn_exp2f(-G);
-        sh.kb[i][c] = k * __builtin_amdgcn_exp2f(GL - G);
-        if (i == CC - 1) {
-          sh.gl[c] = eg;
-          bad |= GL < G_SAFE;
-        }
+        const float qq = q[e] * nq, kk = k[e] * nk;
+        eg[e] = __builtin_amdgcn_exp2f(G[e]);
+        qt[e] = qq * eg[e];
+        kt[e] = kk * eg[e];
+        kh[e] = kk * __builtin_amdgcn_exp2f(-G[e]);
+        kb[e] = kk * __builtin_amdgcn_exp2f(GL[e] - G[e]);
+        bad |= GL[e] < G_SAFE;
       }
-      if (bad) sh.unsafe = 1;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {             // rows of CP floats: 8-byte aligned
+        *(float2*)&sh.qt[i][c0 + e] = make_float2(qt[e], qt[e + 1]);
+        *(float2*)&sh.kt[i][c0 + e] = make_float2(kt[e], kt[e + 1]);
+        *(float2*)&sh.kh[i][c0 + e] = make_float2(kh[e], kh[e + 1]);
+      }
+      *(float4*)&sh.kb[i][c0] = make_float4(kb[0], kb[1], kb[2], kb[3]);
+      *(float4*)&sh.kb[i][c0 + 4] = make_float4(kb[4], kb[5], kb[6], kb[7]);
+      if (i == CC - 1) {
+        *(float4*)&sh.gl[c0] = make_float4(eg[0], eg[1], eg[2], eg[3]);
+        *(float4*)&sh.gl[c0 + 4] = make_float4(eg[4], eg[5], eg[6], eg[7]);
+        if (bad) sh.unsafe = 1;
+      }
     }
     block_sync_lds();
     // ---- S0 products and the block coefficients on MFMA: waves 0 / 1 take k~ S0 for
