@@ -173,9 +173,10 @@ __global__ __launch_bounds__(KT) void kda_decode_kernel(KdaArgs a) {
 // the state slice staying in LDS.  Tokens past the end of the last block enter with
 // zero input, alpha = 1 and beta = 0, which leaves the state and the taps unchanged.
 constexpr int CC = 16;               // tokens per block
-constexpr int CP = KD + 2;           // row of q~, k~, k^ (read [token][channel] by 16 x 4 lanes)
+constexpr int CP = KD + 4;           // row of q~, k~, k^ (16-byte reads of 4 channels by 16 x 4 lanes)
 constexpr int KBP = KD + 16;         // row of k-bar (read [token][channel] by 4 x 16 lanes)
-constexpr int SP = KSL + 16;         // row of the state slice and of u
+constexpr int SP = KSL + 16;         // row of u
+constexpr int STP = KD + 4;          // row of the transposed state slice: column c of S holds S[.][c]
 constexpr float G_SAFE = -115.f;          // log2 of the decay: 2^115 stays inside fp32
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -187,8 +188,8 @@ struct __align__(16) KdaChunkShared {
   float g[CC][KD];                   // log2 alpha, then its running sum (G in base 2)
   float qt[CC][CP], kt[CC][CP], kh[CC][CP];
   float kb[CC][KBP];
-  float S[KD][SP];
-  float A[2][CC][CC + 1], B[2][CC][CC + 1];   // halves over channels 0..63, 64..127
+  float St[KSL][STP];                // the state slice, transposed: St[c][k] = S[k][c]
+  float A[2][CC][CC], B[2][CC][CC];  // halves over channels 0..63, 64..127
   float U[CC][SP];                   // conv + SiLU of v, then v - S0^T k~, then u
   float gl[KD];                      // e^{G_last}
   float beta[CC], rq[CC], rk[CC];
@@ -220,10 +221,10 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
   for (int i = tid; i < KD * KSL / 4; i += KT) {
     const int row = i / (KSL / 4), c4 = i % (KSL / 4);
     const float4 v = *(const float4*)(Sg + (int64_t)row * KD + 4 * c4);
-    sh.S[row][4 * c4] = v.x;
-    sh.S[row][4 * c4 + 1] = v.y;
-    sh.S[row][4 * c4 + 2] = v.z;
-    sh.S[row][4 * c4 + 3] = v.w;
+    sh.St[4 * c4][row] = v.x;
+    sh.St[4 * c4 + 1][row] = v.y;
+    sh.St[4 * c4 + 2][row] = v.z;
+    sh.St[4 * c4 + 3][row] = v.w;
   }
   for (int i = tid; i < 3 * 3 * KD; i += KT) {
     const int w = i / (3 * KD), m = (i / KD) % 3, c = i % KD;
@@ -400,10 +401,10 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
         bad |= GL[e] < G_SAFE;
       }
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {             // rows of CP floats: 8-byte aligned
-        *(float2*)&sh.qt[i][c0 + e] = make_float2(qt[e], qt[e + 1]);
-        *(float2*)&sh.kt[i][c0 + e] = make_float2(kt[e], kt[e + 1]);
-        *(float2*)&sh.kh[i][c0 + e] = make_float2(kh[e], kh[e + 1]);
+      for (int e = 0; e < 8; e += 4) {
+        *(float4*)&sh.qt[i][c0 + e] = make_float4(qt[e], qt[e + 1], qt[e + 2], qt[e + 3]);
+        *(float4*)&sh.kt[i][c0 + e] = make_float4(kt[e], kt[e + 1], kt[e + 2], kt[e + 3]);
+        *(float4*)&sh.kh[i][c0 + e] = make_float4(kh[e], kh[e + 1], kh[e + 2], kh[e + 3]);
       }
       *(float4*)&sh.kb[i][c0] = make_float4(kb[0], kb[1], kb[2], kb[3]);
       *(float4*)&sh.kb[i][c0 + 4] = make_float4(kb[4], kb[5], kb[6], kb[7]);
@@ -421,10 +422,16 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
     {
       const int nt = wv & 1;
       const float (*lhs)[CP] = wv < 2 ? sh.kt : sh.qt;
+      // the sum over channels runs in the order k = 32 kq + s (lane kq's channels
+      // contiguous): one 16-byte read of each operand per four MFMAs
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int s = 0; s < KD / 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(lhs[r16][4 * s + kq], sh.S[4 * s + kq][16 * nt + r16], acc, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < KD / 16; ++j) {
+        const f32x4_t la = *(const f32x4_t*)&lhs[r16][32 * kq + 4 * j];
+        const f32x4_t lb = *(const f32x4_t*)&sh.St[16 * nt + r16][32 * kq + 4 * j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(la[e], lb[e], acc, 0, 0, 0);
+      }
       if (wv < 2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sh.U[4 * kq + e][16 * nt + r16] -= acc[e];
@@ -433,9 +440,13 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
       }
       const int k0 = 64 * nt;
       f32x4_t c2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int s = 0; s < KD / 8; ++s)
-        c2 = __builtin_amdgcn_mfma_f32_16x16x4f32(lhs[r16][k0 + 4 * s + kq], sh.kh[r16][k0 + 4 * s + kq], c2, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < KD / 32; ++j) {
+        const f32x4_t la = *(const f32x4_t*)&lhs[r16][k0 + 16 * kq + 4 * j];
+        const f32x4_t lb = *(const f32x4_t*)&sh.kh[r16][k0 + 16 * kq + 4 * j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c2 = __builtin_amdgcn_mfma_f32_16x16x4f32(la[e], lb[e], c2, 0, 0, 0);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 4 * kq + e;
@@ -502,18 +513,14 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tile = 4 * wv + j, mt = tile >> 1, nt = tile & 1;
-      f32x4_t acc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * mt + 4 * kq + e;
-        acc[e] = sh.S[row][16 * nt + r16] * sh.gl[row];
-      }
+      // rows 16 mt + 4 kq .. +3 of column 16 nt + r16: one 16-byte piece of St
+      f32x4_t* sp = (f32x4_t*)&sh.St[16 * nt + r16][16 * mt + 4 * kq];
+      f32x4_t acc = *sp * *(const f32x4_t*)&sh.gl[16 * mt + 4 * kq];
 #pragma unroll
       for (int s = 0; s < CC / 4; ++s)
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.kb[4 * s + kq][16 * mt + r16], sh.U[4 * s + kq][16 * nt + r16], acc,
                                                   0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sh.S[16 * mt + 4 * kq + e][16 * nt + r16] = acc[e];
+      *sp = acc;
     }
   }
   block_sync_lds();
@@ -521,7 +528,7 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
   for (int i = tid; i < KD * KSL / 4; i += KT) {
     const int row = i / (KSL / 4), c4 = i % (KSL / 4);
     *(float4*)(Sg + (int64_t)row * KD + 4 * c4) =
-        make_float4(sh.S[row][4 * c4], sh.S[row][4 * c4 + 1], sh.S[row][4 * c4 + 2], sh.S[row][4 * c4 + 3]);
+        make_float4(sh.St[4 * c4][row], sh.St[4 * c4 + 1][row], sh.St[4 * c4 + 2][row], sh.St[4 * c4 + 3][row]);
   }
   for (int i = tid; i < 3 * 3 * KD; i += KT) {
     const int w = i / (3 * KD), m = (i / KD) % 3, c = i % KD;
