@@ -341,44 +341,11 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
       }
     }
     block_sync_lds();
-    // ---- 1 / norms of q and k per token: thread -> (q or k, token (t % 128) / 8), 16
-    //      channels 16 (t % 8) .. +15 (four 16-byte reads), summed over the 8 lanes of the
-    //      token
-    {
-      const float (*y)[KD] = cw ? sh.yk : sh.yq;
-      const int i = cc >> 3, c0 = cc & 7;
-      float s2 = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 v = *(const float4*)&y[i][16 * c0 + 4 * j];
-        s2 = fmaf(v.x, v.x, s2);
-        s2 = fmaf(v.y, v.y, s2);
-        s2 = fmaf(v.z, v.z, s2);
-        s2 = fmaf(v.w, v.w, s2);
-      }
-      s2 += __shfl_xor(s2, 1);
-      s2 += __shfl_xor(s2, 2);
-      s2 += __shfl_xor(s2, 4);
-      if (c0 == 0) (cw ? sh.rk : sh.rq)[i] = rsqrtf(s2 + 1e-6f);
-      // the v taps after the block (every read of the old taps is done)
-      if (tid < KSL) {
-        float x[CC + 3];
-        x[0] = sh.hx[2][0][tid];
-        x[1] = sh.hx[2][1][tid];
-        x[2] = sh.hx[2][2][tid];
-#pragma unroll
-        for (int j = 0; j < CC; ++j) x[j + 3] = sh.yv[j][tid];
-        sh.hx[2][0][tid] = pick_tap(x, n);
-        sh.hx[2][1][tid] = pick_tap(x, n + 1);
-        sh.hx[2][2][tid] = pick_tap(x, n + 2);
-      }
-    }
-    block_sync_lds();
-    // ---- decayed operands: thread -> token t / 16, channels 8(t % 16) .. +7
-    //      (all reads issued together, 8- and 16-byte LDS accesses)
+    // ---- 1 / norms of q and k and the decayed operands: thread -> token t / 16,
+    //      channels 8(t % 16) .. +7 (all reads issued together, 16-byte LDS accesses);
+    //      the 16 lanes of a token sum its squares
     {
       const int i = tid >> 4, c0 = 8 * (tid & 15);
-      const float nq = sh.rq[i], nk = sh.rk[i];
       float G[8], GL[8], q[8], k[8];
       auto ld8 = [](const float* p, float (&d)[8]) {
         const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
@@ -388,6 +355,22 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
       ld8(&sh.g[CC - 1][c0], GL);
       ld8(&sh.yq[i][c0], q);
       ld8(&sh.yk[i][c0], k);
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sq = fmaf(q[e], q[e], sq);
+        sk = fmaf(k[e], k[e], sk);
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        sq += __shfl_xor(sq, m);
+        sk += __shfl_xor(sk, m);
+      }
+      const float nq = rsqrtf(sq + 1e-6f), nk = rsqrtf(sk + 1e-6f);
+      if ((tid & 15) == 0) {
+        sh.rq[i] = nq;                           // for the term-by-term coefficients
+        sh.rk[i] = nk;
+      }
       float qt[8], kt[8], kh[8], kb[8], eg[8];
       bool bad = false;
 #pragma unroll
@@ -412,6 +395,18 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
         *(float4*)&sh.gl[c0] = make_float4(eg[0], eg[1], eg[2], eg[3]);
         *(float4*)&sh.gl[c0 + 4] = make_float4(eg[4], eg[5], eg[6], eg[7]);
         if (bad) sh.unsafe = 1;
+      }
+      // the v taps after the block (every read of the old taps is done)
+      if (tid < KSL) {
+        float x[CC + 3];
+        x[0] = sh.hx[2][0][tid];
+        x[1] = sh.hx[2][1][tid];
+        x[2] = sh.hx[2][2][tid];
+#pragma unroll
+        for (int j = 0; j < CC; ++j) x[j + 3] = sh.yv[j][tid];
+        sh.hx[2][0][tid] = pick_tap(x, n);
+        sh.hx[2][1][tid] = pick_tap(x, n + 1);
+        sh.hx[2][2][tid] = pick_tap(x, n + 2);
       }
     }
     block_sync_lds();
@@ -479,15 +474,28 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
     // A as one matrix (its two channel halves summed, one entry per thread)
     sh.A[0][tid >> 4][tid & 15] += sh.A[1][tid >> 4][tid & 15];
     block_sync_lds();
-    // ---- u by forward substitution: lanes 0 .. 31 of wave 0, one column each
+    // ---- u by forward substitution: lanes 0 .. 31 of wave 0, one column each.  Each
+    //      u_j goes into every later row's running sum at once (the same terms in the
+    //      same order per row), so the dependent path is one fma and one multiply a row
     if (tid < KSL) {
-      float u[CC];
+      float p[CC], u[CC];
+      float4 ar[CC][CC / 4];                    // A's rows, 16-byte reads (lower triangle used)
 #pragma unroll
       for (int i = 0; i < CC; ++i) {
-        float acc = sh.U[i][tid];
+        p[i] = sh.U[i][tid];
 #pragma unroll
-        for (int j = 0; j < i; ++j) acc = fmaf(-sh.A[0][i][j], u[j], acc);
-        u[i] = sh.beta[i] * acc;
+        for (int q = 0; q < CC / 4; ++q)
+          if (4 * q < i) ar[i][q] = *(const float4*)&sh.A[0][i][4 * q];
+      }
+      auto aij = [&](int i, int j) {
+        const float4 v = ar[i][j >> 2];
+        return (j & 3) == 0 ? v.x : ((j & 3) == 1 ? v.y : ((j & 3) == 2 ? v.z : v.w));
+      };
+#pragma unroll
+      for (int j = 0; j < CC; ++j) {
+        u[j] = sh.beta[j] * p[j];
+#pragma unroll
+        for (int i = j + 1; i < CC; ++i) p[i] = fmaf(-aij(i, j), u[j], p[i]);
       }
 #pragma unroll
       for (int i = 0; i < CC; ++i) sh.U[i][tid] = u[i];
