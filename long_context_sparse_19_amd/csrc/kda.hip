@@ -283,16 +283,24 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
     if (tid < CC) sh.beta[tid] = pbeta;
     if (tid == 0) sh.unsafe = 0;
   };
-  if (T > 0) fetch(0);
+  // block 0's inputs staged, block 1's in flight; a block's inputs are staged during
+  // the previous block's substitution (by the threads it leaves idle) and just after it
+  if (T > 0) {
+    fetch(0);
+    stage();
+    if (CC < T) fetch(CC);
+  }
 
   // LDS-only barriers inside the loop (block_sync_lds): the next block's loads stay
   // in flight across them
   for (int t0 = 0; t0 < T; t0 += CC) {
     const int n = min(CC, T - t0);
-    block_sync_lds();                            // the previous block is done with every buffer
-    stage();
-    if (t0 + CC < T) fetch(t0 + CC);
-    block_sync_lds();
+    const bool more = t0 + CC < T;               // a next block to stage
+    auto stage_next = [&]() {
+      stage();
+      if (t0 + 2 * CC < T) fetch(t0 + 2 * CC);
+    };
+    block_sync_lds();                            // the block's inputs are staged
     // ---- short convolution + SiLU in place, taps sliding in registers (the taps after
     //      the block are the last 3 inputs up to token n-1); the running sum G
     {
@@ -499,8 +507,11 @@ __global__ __launch_bounds__(KT) void kda_chunk_kernel(KdaChunkArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < CC; ++i) sh.U[i][tid] = u[i];
+    } else if (more) {
+      stage_next();                              // nothing below reads the staged buffers
     }
     block_sync_lds();
+    if (tid < KSL && more) stage_next();
     // ---- outputs (waves 2 / 3): (q~ S0 + B u) / sqrt(128)
     if (wv >= 2) {
       const int nt = wv & 1;
