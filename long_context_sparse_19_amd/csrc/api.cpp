@@ -604,9 +604,8 @@ ip_status sparse_attn_prefill(const ip_seqs* seqs, int32_t n_q, const int32_t* q
 }
 
 // ------------------------------------------------------------------ fused decode step
-// workspace: the indexer's, the attention's, then per sequence a ready word and a
-// count of acknowledged scoring workgroups, then the one-launch step's own per-wave
-// lists (zero between calls)
+// workspace: the indexer's, the attention's, then per sequence a ready word, then the
+// one-launch step's own per-wave lists (zero between calls)
 struct StepPlan {
   ScorePlan score;
   AttnPlan attn;
@@ -620,7 +619,7 @@ static StepPlan step_plan(const ip_seqs* seqs, int32_t top_k, int32_t n_heads, i
   p.attn = attn_plan(seqs->batch, n_heads, dv, top_k, q_dtype);
   p.idx_bytes = align256(p.score.total);
   p.attn_bytes = align256(p.attn.bytes);
-  p.ready_bytes = align256((size_t)seqs->batch * 8);
+  p.ready_bytes = align256((size_t)seqs->batch * 4);
   p.list_bytes = align256((size_t)seqs->batch * p.score.max_lists * (16 * 8 + 8));
   p.total = p.idx_bytes + p.attn_bytes + p.ready_bytes + p.list_bytes;
   return p;
@@ -660,7 +659,6 @@ ip_status indexpool_decode_step(const ip_seqs* seqs, const void* kv_new, const i
   char* ws_idx = (char*)ws;
   char* ws_att = ws_idx + plan.idx_bytes;
   uint32_t* ready = (uint32_t*)(ws_att + plan.attn_bytes);
-  uint32_t* acked = ready + B;
   char* step_lists = (char*)ready + plan.ready_bytes;
   ip::AttnArgs a;
   AttnKind kind;
@@ -679,7 +677,7 @@ ip_status indexpool_decode_step(const ip_seqs* seqs, const void* kv_new, const i
     // the step's own lists (zero between calls: the combine clears them)
     st.score.lists = (uint64_t*)step_lists;
     st.score.lists_meta = (uint2*)(step_lists + (size_t)B * plan.score.max_lists * 16 * 8);
-    st.score.step_acked = acked;
+    st.score.step = 1;
     st.attn = a;
     st.attn.sel_ready = ready;
     st.attn.k_new = (const uint8_t*)kv_new;
@@ -691,7 +689,6 @@ ip_status indexpool_decode_step(const ip_seqs* seqs, const void* kv_new, const i
     st.attn.step_ld = st.score.ld;
     st.attn.step_gm = st.score.gm;
     st.attn.step_gld = st.score.gld;
-    st.attn.step_acked = acked;
     st.attn.sel_out = out_idx;
     if (ip::decode_step_supported(st)) return device_status(ip::launch_decode_step(st, stream), fn);
   }

@@ -200,11 +200,8 @@ __device__ __forceinline__ void step_select(const AttnArgs& a, const RowCtx& c, 
     const int n_lists = scorek::fused_list_count<STEP_NWV, STEP_TILES>(nel, need, a.step_lists != nullptr);
     local = n_lists > 0 && sl.merge(n_lists, need, nel, a.top_k, sel::SliceOut{lid, sb0, send}, ss);
     if (!local && n_lists > 0 && split == 0) {
-      constexpr int KEYS = STEP_NWV * STEP_TILES * 32;
-      const uint32_t n_run = (uint32_t)((nel + KEYS - 1) / KEYS);
-      if (threadIdx.x == 0)
-        for (int k = 0; sel::ld_agent(a.step_acked + rl) < n_run && k < STEP_SPIN_LIMIT; ++k)
-          __builtin_amdgcn_s_sleep(1);
+      // the merge saw every list of the row stored, and a scoring wave stores its list
+      // only once its scores are acknowledged: every score of the row is in memory
       __syncthreads();
       sel::select_row<NTA>(a.step_scores + (int64_t)rl * a.step_ld, a.step_gm + (int64_t)rl * a.step_gld, nel, nel,
                            a.top_k, row_out, ss);
@@ -956,8 +953,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int64_t pi0 = (int64_t)rl * S;
   float ms = -INFINITY, ls = 0.f;
   if (lane < S) {
-    ms = a.part_ml[((pi0 + lane) * LAT_H + head) * 2];
-    ls = a.part_ml[((pi0 + lane) * LAT_H + head) * 2 + 1];
+    const float2 ml = *(const float2*)&a.part_ml[((pi0 + lane) * LAT_H + head) * 2];
+    ms = ml.x;
+    ls = ml.y;
+  }
+  const uint16_t* base = a.part_o + (pi0 * LAT_H + head) * LAT_DV + t * 4;
+  // up to CMB_REG splits: every partial load is issued at once, beside the weights'
+  constexpr int CMB_REG = 16;
+  uint2 v[CMB_REG];
+  if (S <= CMB_REG) {
+#pragma unroll
+    for (int u = 0; u < CMB_REG; ++u)
+      v[u] = u < S ? *(const uint2*)(base + (int64_t)u * LAT_H * LAT_DV) : make_uint2(0u, 0u);
   }
   float m = ms;
 #pragma unroll
@@ -967,27 +974,31 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const uint16_t* base = a.part_o + (pi0 * LAT_H + head) * LAT_DV + t * 4;
   auto add = [&](float wu, uint2 v) {
     acc.x = fmaf(wu, __uint_as_float(v.x << 16), acc.x);
     acc.y = fmaf(wu, __uint_as_float(v.x & 0xFFFF0000u), acc.y);
     acc.z = fmaf(wu, __uint_as_float(v.y << 16), acc.z);
     acc.w = fmaf(wu, __uint_as_float(v.y & 0xFFFF0000u), acc.w);
   };
-  int s = 0;
-  for (; s + 4 <= S; s += 4) {
-    uint2 v[4];
+  if (S <= CMB_REG) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *(const uint2*)(base + (int64_t)(s + u) * LAT_H * LAT_DV);
+    for (int u = 0; u < CMB_REG; ++u)
+      if (u < S) add(__shfl(wgt, u), v[u]);
+  } else {
+    int s = 0;
+    for (; s + 4 <= S; s += 4) {
+      uint2 w[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) add(__shfl(wgt, s + u), v[u]);
+      for (int u = 0; u < 4; ++u) w[u] = *(const uint2*)(base + (int64_t)(s + u) * LAT_H * LAT_DV);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add(__shfl(wgt, s + u), w[u]);
+    }
+    for (; s < S; ++s) add(__shfl(wgt, s), *(const uint2*)(base + (int64_t)s * LAT_H * LAT_DV));
   }
-  for (; s < S; ++s) add(__shfl(wgt, s), *(const uint2*)(base + (int64_t)s * LAT_H * LAT_DV));
   // the fused step's words and lists of the row return to zero for the next launch
   // (every reader of them belongs to the step launch, which has ended)
   if (a.sel_ready && blockIdx.x == 0 && threadIdx.x == 0) {
     a.sel_ready[rl] = 0u;
-    a.step_acked[rl] = 0u;
   }
   if (a.step_lists) {
     const int g = blockIdx.x * 256 + threadIdx.x, G = gridDim.x * 256;
@@ -1142,7 +1153,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
 bool decode_step_supported(const StepArgs& a) {
   return a.score.fuse && a.score.row0 == 0 && a.attn.row0 == 0 && a.attn.n_rows == a.score.n_rows &&
          a.attn.n_split > 1 && a.attn.blocks_per_split < PIPE_MIN_BLOCKS && a.attn.sel_ready && a.attn.k_new &&
-         !a.attn.k_scale && a.score.max_blocks > 0 && a.score.step_acked && a.attn.step_acked == a.score.step_acked &&
+         !a.attn.k_scale && a.score.max_blocks > 0 && a.score.step &&
          a.attn.step_lists == a.score.lists && a.attn.step_meta == a.score.lists_meta &&
          a.attn.step_max_lists == a.score.max_lists && a.attn.sel_out && a.attn.sel_out == a.score.out &&
          a.attn.n_split * a.attn.blocks_per_split >= a.attn.top_k;

@@ -101,11 +101,11 @@ struct ScoreArgs {
   int max_lists;               // waves per row covered by the grid
   int with_append;             // decode: extra grid rows of workgroups run `append`,
   AppendArgs append;           // one sequence each (see append.hpp)
-  // the fused decode step only (else null): the attention workgroups select the rows
-  // that use lists (and the trivial rows) themselves; step_acked[r - row0] counts the
-  // scoring workgroups of row r whose scores are acknowledged (zero on entry, cleared
-  // by the combine), and the lists are zero on entry (cleared by the combine)
-  uint32_t* step_acked;
+  // the fused decode step only (else 0): the attention workgroups select the rows
+  // that use lists (and the trivial rows) themselves.  A wave of a list row stores its
+  // scores, then (once they are acknowledged) its list; the lists are zero on entry
+  // (cleared by the combine)
+  int step;
 };
 hipError_t launch_score_fp8_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s);
@@ -182,7 +182,7 @@ struct AttnArgs {
   uint32_t* sel_ready;
   const uint8_t* k_new;
   int64_t k_new_stride;
-  // the fused decode step's selection of the list rows (see ScoreArgs::step_acked),
+  // the fused decode step's selection of the list rows (see ScoreArgs::step),
   // done by the attention workgroups: the row's lists, its scores and group maxima
   // (for the exact fallback), and the row's ids written to sel_out (= sel)
   uint64_t* step_lists;
@@ -193,7 +193,6 @@ struct AttnArgs {
   int64_t step_ld;
   const float* step_gm;
   int64_t step_gld;
-  uint32_t* step_acked;
   int32_t* sel_out;
 };
 // bf16 latent MQA: 64 heads, dk 576, dv 512

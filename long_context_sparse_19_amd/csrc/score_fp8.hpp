@@ -259,9 +259,8 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
     const bool lists = fused_list_count<NWV, TILES>(nel, need, a.lists != nullptr) > 0;
     // the fused decode step: the attention workgroups of a list row merge its lists
     // themselves, those of a trivial row write its ids directly; the scoring
-    // workgroups of those rows store their lists and scores and count themselves in
-    // (the scores feed an exact fallback once every workgroup is counted)
-    const bool step = a.step_acked != nullptr;
+    // workgroups of those rows store their scores and lists and end
+    const bool step = a.step != 0;
     uint64_t* lrow = lists ? a.lists + (int64_t)(r - a.row0) * a.max_lists * sel::LIST : nullptr;
     uint2* mrow = lists ? a.lists_meta + (int64_t)(r - a.row0) * a.max_lists : nullptr;
     // With lists and the scores in the workspace, a workgroup counts itself in once
@@ -280,6 +279,47 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
       par_v = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(sel::dev_rsrc(ack), 0u, 0, 16 /* sc1 */);
     if (kc0 < nel) {
       const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hh = lane >> 5, kl = lane & 31;
+      // the scores and group maxima (read by the exact fallback, and the caller's
+      // score output)
+      auto store_scores = [&]() {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        float* srow = a.scores + (int64_t)(r - a.row0) * a.ld;
+        float* grow = a.gm + (int64_t)(r - a.row0) * a.gld;
+        if (defer || (step && a.scores_own)) {
+          // every lane writes (the two halves hold the same score, a group's 16 lanes
+          // the same maximum, and rows of the workspace are padded to whole tiles):
+          // unconditional stores stay in flight together.  Deferred: exactly 2 TILES
+          // stores per wave, after the lists, so that waiting for all but the last
+          // 2 TILES of the wave's memory operations waits for its lists
+#pragma unroll
+          for (int t = 0; t < TILES; ++t) {
+            const int j = kc0 + (wv * TILES + t) * 32 + kl;
+            sel::st_agent(srow + j, scv[t]);
+            sel::st_agent(grow + (j >> 4), gmv[t]);
+          }
+          if (defer) {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            wait_vm<2 * TILES>();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < TILES; ++t) {
+            const int j = kc0 + (wv * TILES + t) * 32 + kl;
+            if (hh == 0 && j < nel) {
+              sel::st_agent(srow + j, scv[t]);
+              if ((kl & 15) == 0) sel::st_agent(grow + (j >> 4), gmv[t]);
+            }
+          }
+        }
+      };
+      // the fused decode step: a wave stores its scores first and its list only once
+      // they are acknowledged, so a row whose lists are all stored has all its scores
+      // stored as well (the attention workgroups check every list before they merge,
+      // and the exact fallback reads the scores after that).  Otherwise the scores go
+      // after the list, so that building it does not wait for them.
+      const bool scores_first = step && lists;
+      if (scores_first) store_scores();
       if (lists) {
         constexpr int KPL = TILES / 2;           // keys per lane: half hh holds tiles KPL hh ..
         uint32_t k[KPL];
@@ -295,48 +335,11 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
           k[i] = id[i] < nel ? float_key(sc) : 0u;
         }
         const int slot = bx * NWV + wv;
-        sel::wave_list<KPL>(k, id, lrow + (int64_t)slot * sel::LIST, mrow + slot);
+        sel::wave_list<KPL>(k, id, lrow + (int64_t)slot * sel::LIST, mrow + slot, scores_first);
       }
-      // the scores and group maxima (read by the exact fallback, and the caller's
-      // score output), after the list so that building it does not wait for them
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      float* srow = a.scores + (int64_t)(r - a.row0) * a.ld;
-      float* grow = a.gm + (int64_t)(r - a.row0) * a.gld;
-      if (defer || (step && a.scores_own)) {
-        // every lane writes (the two halves hold the same score, a group's 16 lanes
-        // the same maximum, and rows of the workspace are padded to whole tiles):
-        // unconditional stores stay in flight together.  Deferred: exactly 2 TILES
-        // stores per wave, after the lists, so that waiting for all but the last
-        // 2 TILES of the wave's memory operations waits for its lists
-#pragma unroll
-        for (int t = 0; t < TILES; ++t) {
-          const int j = kc0 + (wv * TILES + t) * 32 + kl;
-          sel::st_agent(srow + j, scv[t]);
-          sel::st_agent(grow + (j >> 4), gmv[t]);
-        }
-        if (defer) {
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-          wait_vm<2 * TILES>();
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        }
-      } else {
-#pragma unroll
-        for (int t = 0; t < TILES; ++t) {
-          const int j = kc0 + (wv * TILES + t) * 32 + kl;
-          if (hh == 0 && j < nel) {
-            sel::st_agent(srow + j, scv[t]);
-            if ((kl & 15) == 0) sel::st_agent(grow + (j >> 4), gmv[t]);
-          }
-        }
-      }
+      if (!scores_first) store_scores();
     }
-    if (step && (trivial || lists)) {
-      if (trivial || kc0 >= nel) return;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (threadIdx.x == 0) atomicAdd(a.step_acked + (r - a.row0), 1u);
-      return;
-    }
+    if (step && (trivial || lists)) return;
     // the row's ids are stored (device-coherent stores): publish them
     auto publish = [&]() {
       if (!sel_ready) return;

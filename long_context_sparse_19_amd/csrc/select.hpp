@@ -683,8 +683,11 @@ __device__ __forceinline__ void wave_count3(const uint32_t (&k)[KPL], uint32_t t
 // The wave's list from its KPL keys per lane (key 0 = none).  Ids ascend over the
 // segments (half, i): lanes 0..31 hold the lower half, k[i] before k[i + 1].
 // The entries go to `dst` [0, count) in that order, (count, L') to `meta`.
+// after_prior: the list's stores wait until every earlier memory operation of the
+// wave is acknowledged (a reader that sees the list stored sees those too).
 template <int KPL>
-__device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&id)[KPL], uint64_t* dst, uint2* meta) {
+__device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&id)[KPL], uint64_t* dst, uint2* meta,
+                                          bool after_prior = false) {
   const int lane = threadIdx.x & 63;
   const int valid = wave_count<KPL>(k, [](uint32_t x) { return x != 0u; });
   uint32_t T = 0;
@@ -747,6 +750,11 @@ __device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&
     kp[sgm] = mine && kk && (kk > T || (kk == T && (T == 0 || trank < room)));
     mk[sgm] = __ballot(kp[sgm]);
     ties += __popcll(mt[sgm]);
+  }
+  if (after_prior) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
   int n = 0;
 #pragma unroll
