@@ -688,24 +688,29 @@ __device__ __forceinline__ void wave_count3(const uint32_t (&k)[KPL], uint32_t t
 template <int KPL>
 __device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&id)[KPL], uint64_t* dst, uint2* meta,
                                           bool after_prior = false) {
+  static_assert(LIST == 16, "one lower bound per group of 4 lanes");
   const int lane = threadIdx.x & 63;
   const int valid = wave_count<KPL>(k, [](uint32_t x) { return x != 0u; });
   uint32_t T = 0;
   if (valid > LIST) {
-    // the largest T with count(keys >= T) >= LIST.  T lies between the wave's
-    // smallest and largest keys, so it shares the bits above their highest
-    // differing bit; the bits below are found two at a time (three trial counts per
-    // step, independent of each other).  Stop once the count is exactly LIST (the
-    // set is then the wave's LIST best).
+    // the largest T with count(keys >= T) >= LIST.  T is at most the wave's largest
+    // key and at least lb: the smallest key (every valid key counts, and there are
+    // more than LIST), and the smallest of the 16 four-lane groups' largest keys
+    // (each group holds one key >= it).  So T shares the bits of the two above
+    // their highest differing bit; the bits below are found two at a time (three
+    // trial counts per step, independent of each other).  Stop once the count is
+    // exactly LIST (the set is then the wave's LIST best).
     uint32_t mx = 0u, mn = 0xFFFFFFFFu;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
       mx = max(mx, k[i]);
       mn = min(mn, k[i] ? k[i] : 0xFFFFFFFFu);
     }
+    mx = max(mx, (uint32_t)dpp_i<0xB1>(0, (int)mx));       // the group of 4 lanes
+    mx = max(mx, (uint32_t)dpp_i<0x4E>(0, (int)mx));
     const uint32_t kmx = wave_umax(mx);
-    const uint32_t kmn = wave_umin(mn);
-    const uint32_t diff = kmx ^ kmn;
+    const uint32_t lb = max(wave_umin(mn), wave_umin(mx));
+    const uint32_t diff = kmx ^ lb;
     int b = diff ? 31 - __clz((int)diff) : -1;    // highest differing bit
     T = diff ? kmx & ~((2u << b) - 1u) : kmx;      // the shared prefix (b == 31: none)
     if (b == 31) T = 0;
@@ -723,33 +728,57 @@ __device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&
       if (wave_count<KPL>(k, [=](uint32_t x) { return x >= t1; }) >= LIST) T = t1;
     }
   }
-  // keys > T all fit; ties at T fill up to LIST in id order
-  const int gt = wave_count<KPL>(k, [=](uint32_t x) { return x > T && x; });
-  const int room = LIST - gt;
-  // segment by segment in list order; the ballots of all segments are taken first
-  // (independent of each other), then the running counts
+  // keys >= T: all kept when they fit (T = 0: every valid key), else the keys > T
+  // and the ties at T up to LIST in id order; segment by segment in list order
   constexpr int NS = 2 * KPL;
   auto mbcnt = [](uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
   };
-  uint64_t mt[NS];
-#pragma unroll
-  for (int sgm = 0; sgm < NS; ++sgm) {
-    const bool mine = (lane >> 5) == sgm / KPL;
-    const uint32_t kk = k[sgm % KPL];
-    mt[sgm] = __ballot(mine && kk && kk == T && T);
-  }
   uint64_t mk[NS];
   bool kp[NS];
-  int ties = 0;
+  uint32_t Lp = T;                               // L' = T, or T + 1 when some ties at T were left out
+  int ge_c[KPL];
+  {
+    uint64_t mg[KPL];
 #pragma unroll
-  for (int sgm = 0; sgm < NS; ++sgm) {
-    const bool mine = (lane >> 5) == sgm / KPL;
-    const uint32_t kk = k[sgm % KPL];
-    const int trank = ties + mbcnt(mt[sgm]);
-    kp[sgm] = mine && kk && (kk > T || (kk == T && (T == 0 || trank < room)));
-    mk[sgm] = __ballot(kp[sgm]);
-    ties += __popcll(mt[sgm]);
+    for (int i = 0; i < KPL; ++i) mg[i] = __ballot(k[i] && k[i] >= T);
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) ge_c[i] = __popcll(mg[i]);
+  }
+  int ge = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) ge += ge_c[i];
+  if (ge <= LIST) {
+    // the ballots of all segments are independent
+#pragma unroll
+    for (int sgm = 0; sgm < NS; ++sgm) {
+      const uint32_t kk = k[sgm % KPL];
+      kp[sgm] = (lane >> 5) == sgm / KPL && kk && kk >= T;
+      mk[sgm] = __ballot(kp[sgm]);
+    }
+  } else {
+    const int gt = wave_count<KPL>(k, [=](uint32_t x) { return x > T && x; });
+    const int room = LIST - gt;
+    // the tie ballots of all segments first (independent of each other), then the
+    // running counts
+    uint64_t mt[NS];
+#pragma unroll
+    for (int sgm = 0; sgm < NS; ++sgm) {
+      const bool mine = (lane >> 5) == sgm / KPL;
+      const uint32_t kk = k[sgm % KPL];
+      mt[sgm] = __ballot(mine && kk && kk == T && T);
+    }
+    int ties = 0;
+#pragma unroll
+    for (int sgm = 0; sgm < NS; ++sgm) {
+      const bool mine = (lane >> 5) == sgm / KPL;
+      const uint32_t kk = k[sgm % KPL];
+      const int trank = ties + mbcnt(mt[sgm]);
+      kp[sgm] = mine && kk && (kk > T || (kk == T && (T == 0 || trank < room)));
+      mk[sgm] = __ballot(kp[sgm]);
+      ties += __popcll(mt[sgm]);
+    }
+    if (T && ties > room) Lp = T + 1;
   }
   if (after_prior) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -764,8 +793,6 @@ __device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&
       st_agent(dst + pos, (uint64_t)k[sgm % KPL] | ((uint64_t)(uint32_t)id[sgm % KPL] << 32));
     n += __popcll(mk[sgm]);
   }
-  // L' = T, or T + 1 when some ties at T were left out
-  const uint32_t Lp = (T && ties > room) ? T + 1 : T;
   if (lane == 0) st_agent((uint64_t*)meta, (uint64_t)((uint32_t)min(n, LIST) | LIST_WRITTEN) | ((uint64_t)Lp << 32));
 }
 

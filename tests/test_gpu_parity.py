@@ -598,6 +598,12 @@ STEP_CASES = {
     # winners lie in the first wave's 256 blocks, more than a list holds, so the
     # row takes the exact select over its scores; rows 1 and 2 keep their lists
     "lists_fallback": (scaled_down(DECODE, 4 * 8209, batch=3, top_k=64), lambda L: L - np.array([0, 5, 9])),
+    # the same with block j taking block j % period's pooled key (STEP_PERIOD): with
+    # period 700 a wave's 256 keys are distinct but every score repeats across the
+    # row, so the merge breaks ties by id; with period 7 a wave's keys tie at its
+    # threshold (its list keeps the lowest ids) and the merge takes the exact select
+    "lists_repeated": (scaled_down(DECODE, 4 * 8209, batch=3, top_k=64), lambda L: L - np.array([0, 5, 9])),
+    "lists_ties": (scaled_down(DECODE, 4 * 8209, batch=3, top_k=64), lambda L: L - np.array([0, 5, 9])),
     # geometries the one-launch step does not cover run the two calls
     "fp8kv_positions": (scaled_down(DECODE_FP8KV, 1024, batch=4), lambda L: L - np.arange(4)),
     "decode_batch128": (scaled_down(DECODE, 4 * 600, batch=128), lambda L: L),
@@ -607,6 +613,8 @@ STEP_CASES = {
 
 # case -> (sequence, blocks [0, n), factor): pooled scales multiplied after pooling
 STEP_BOOST = {"lists_fallback": (0, 200, 8.0)}
+# case -> period: block j of every sequence takes the pooled key of block j % period
+STEP_PERIOD = {"lists_repeated": 700, "lists_ties": 7}
 
 
 def _step_oracle_check(inp, d, ws, rows):
@@ -659,6 +667,14 @@ def test_decode_step_equals_decode_index_then_attention(name):
             b0, nb, f = STEP_BOOST[name]
             rows_b = torch.as_tensor(O.pooled_rows(inp, b0, np.arange(nb)), device=d.pooled.scale.device)
             d.pooled.scale[rows_b] *= f
+        if name in STEP_PERIOD:
+            for b in range(w.batch):
+                nb = int(inp.seq_lens[b]) // 4
+                dst = torch.as_tensor(O.pooled_rows(inp, b, np.arange(nb)), device=d.pooled.data.device)
+                src = torch.as_tensor(O.pooled_rows(inp, b, np.arange(nb) % STEP_PERIOD[name]),
+                                      device=d.pooled.data.device)
+                d.pooled.data[dst] = d.pooled.data[src]
+                d.pooled.scale[dst] = d.pooled.scale[src]
         ws = D.Workspaces(d, keep_scores=False)
         t = D.NewTokens(new)
         outs = []
@@ -683,4 +699,8 @@ def test_decode_step_equals_decode_index_then_attention(name):
     if name in STEP_BOOST:
         # the case does what it is for: row 0's winners overflow the first wave's list
         assert rows[0] == 0 and int(((o_ids[0] >= 0) & (o_ids[0] < 256)).sum()) > 16
+    if name in STEP_PERIOD:
+        # the case does what it is for: equal scores among the winners (the kept ids
+        # of a repeated score are its lowest)
+        assert len(np.unique(o_ids[0][o_ids[0] >= 0] % STEP_PERIOD[name])) < d.top_k - 1
     log(f"  step == two calls (2 calls), oracle ok on rows {rows.tolist()}")
