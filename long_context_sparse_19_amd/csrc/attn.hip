@@ -234,8 +234,10 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const int bid,
   const int l32 = lane & 31, lh = lane >> 5;
   const int hb = wv & 1, th = wv >> 1;           // S^T tile: heads 32hb .., tokens 32th ..
   if (bid >= a.n_rows * a.n_split) return;
-  const int split = bid % a.n_split;
-  const int rl = bid / a.n_split;
+  // STEP: rows fastest, so that the splits of a row share a die (workgroups go to
+  // the dies round robin) and split 0 of every row comes first
+  const int split = STEP ? bid / a.n_rows : bid % a.n_split;
+  const int rl = STEP ? bid % a.n_rows : bid / a.n_split;
   const int r = a.row0 + rl;
   const RowCtx c = row_ctx(a, r);
   const int sb0 = split * a.blocks_per_split;
@@ -945,8 +947,9 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
 // computed once per wave (lane s holds split s) and broadcast.
 constexpr int MAX_SPLIT = 64;
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int head = blockIdx.x * 2 + (threadIdx.x >> 7);
-  const int rl = blockIdx.y;
+  // rows fastest (a row's workgroups share a die, as the fused step's attention)
+  const int head = (int)(blockIdx.x / a.n_rows) * 2 + (threadIdx.x >> 7);
+  const int rl = (int)(blockIdx.x % a.n_rows);
   const int r = a.row0 + rl;
   const int t = threadIdx.x & 127, lane = threadIdx.x & 63;
   const int S = a.n_split;
@@ -997,11 +1000,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   }
   // the fused step's words and lists of the row return to zero for the next launch
   // (every reader of them belongs to the step launch, which has ended)
-  if (a.sel_ready && blockIdx.x == 0 && threadIdx.x == 0) {
+  if (a.sel_ready && blockIdx.x < (unsigned)a.n_rows && threadIdx.x == 0) {
     a.sel_ready[rl] = 0u;
   }
   if (a.step_lists) {
-    const int g = blockIdx.x * 256 + threadIdx.x, G = gridDim.x * 256;
+    const int g = (int)(blockIdx.x / a.n_rows) * 256 + threadIdx.x, G = LAT_H / 2 * 256;
     u32x4_t* l16 = (u32x4_t*)(a.step_lists + (int64_t)rl * a.step_max_lists * sel::LIST);
     for (int i = g; i < a.step_max_lists * sel::LIST / 2; i += G) l16[i] = u32x4_t{0u, 0u, 0u, 0u};
     uint2* m = a.step_meta + (int64_t)rl * a.step_max_lists;
@@ -1146,7 +1149,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  launch(K_COMBINE, attn_combine_kernel, dim3(LAT_H / 2, a.n_rows), dim3(256), s, a);
+  launch(K_COMBINE, attn_combine_kernel, dim3(LAT_H / 2 * a.n_rows), dim3(256), s, a);
   return hipGetLastError();
 }
 
@@ -1176,7 +1179,7 @@ hipError_t launch_decode_step(const StepArgs& a, hipStream_t s) {
   launch(K_STEP, decode_step_kernel, dim3((unsigned)grid), dim3(NTA), s, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  launch(K_COMBINE, attn_combine_kernel, dim3(LAT_H / 2, a.attn.n_rows), dim3(256), s, a.attn);
+  launch(K_COMBINE, attn_combine_kernel, dim3(LAT_H / 2 * a.attn.n_rows), dim3(256), s, a.attn);
   return hipGetLastError();
 }
 
@@ -1185,7 +1188,7 @@ hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t s) {
   launch(K_ATTN, attn_fp8_kernel, dim3((unsigned)((int64_t)a.n_rows * a.n_split)), dim3(NTA), s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  launch(K_COMBINE, attn_combine_kernel, dim3(LAT_H / 2, a.n_rows), dim3(256), s, a);
+  launch(K_COMBINE, attn_combine_kernel, dim3(LAT_H / 2 * a.n_rows), dim3(256), s, a);
   return hipGetLastError();
 }
 
