@@ -151,8 +151,10 @@ def fuses_select(w):
 
 
 # the sources each kernel is built from (the HBM counters in profiles/ are tied to them)
-_KERNEL_SOURCES = {"attention": ("attn.hip", "attn_pipe.hip", "attn_common.hpp"), "combine": ("attn.hip", "attn_common.hpp"),
-                   "step": ("attn.hip", "attn_common.hpp", "score_fp8.hpp", "select.hpp"),
+_KERNEL_SOURCES = {"attention": ("attn.hip", "attn_bf16.hpp", "attn_pipe.hip", "attn_common.hpp"),
+                   "combine": ("attn.hip", "attn_bf16.hpp", "attn_common.hpp"),
+                   "step": ("attn.hip", "attn_bf16.hpp", "attn_step_h32.hip", "attn_common.hpp", "score_fp8.hpp",
+                            "select.hpp"),
                    "score": ("score.hip", "score_fp8.hpp", "select.hpp"), "topk": ("topk.hip", "select.hip", "select.hpp"), "compress": ("compress.hip",),
                    "append": ("compress.hip",), "kda": ("kda.hip",)}
 

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libindexpool.so")
-SOURCES = ["compress.hip", "score.hip", "select.hip", "topk.hip", "attn.hip", "attn_pipe.hip", "kda.hip", "api.cpp"]
+SOURCES = ["compress.hip", "score.hip", "select.hip", "topk.hip", "attn.hip", "attn_step_h32.hip", "attn_pipe.hip", "kda.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -218,6 +218,16 @@ struct StepArgs {
 };
 bool decode_step_supported(const StepArgs& a);
 hipError_t launch_decode_step(const StepArgs& a, hipStream_t s);
+// The step kernel's arguments: the scoring and attention arguments, the scoring
+// grid's width (workgroups per row), and the numbers of scoring and append
+// workgroups before the attention ones.
+struct StepKArgs {
+  ScoreArgs s;
+  AttnArgs at;
+  int gx, n_score, n_app;
+};
+// the step kernel with 32-head attention units, over `grid` workgroups
+hipError_t launch_decode_step_h32(const StepKArgs& k, unsigned grid, hipStream_t s);
 
 // KDA decode step (the linear-attention half): 128 key and value channels per head
 constexpr int KDA_D = 128;
