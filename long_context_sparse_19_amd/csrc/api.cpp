@@ -91,6 +91,7 @@ struct ScorePlan {
   int max_blocks;      // eligible blocks bound
   int rows_per_pass;   // query rows per pass
   int max_lists;       // per-wave candidate lists per row (0: rows too long for them)
+  int wg_lists;        // else per-workgroup lists per row (1M-token rows), or 0
   size_t count_bytes, ack_bytes, gm_bytes, list_bytes, score_bytes, total;
 };
 
@@ -113,7 +114,9 @@ ScorePlan score_plan(const ip_seqs* s, int n_q, bool scores_given) {
   // of a row, when a row has at most 256 of them (the selection merges them in LDS)
   const int waves = 8 * (int)((std::max(1, p.max_blocks) + 1023) / 1024);
   p.max_lists = waves <= 256 && n_q < 64 ? waves : 0;
-  p.list_bytes = align256((size_t)p.rows_per_pass * p.max_lists * (16 * 8 + 8));
+  // longer decode rows: one 16-entry list per 8-wave workgroup, up to 256 of them
+  p.wg_lists = !p.max_lists && n_q < 64 && waves / 8 <= 256 ? waves / 8 : 0;
+  p.list_bytes = align256((size_t)p.rows_per_pass * (p.max_lists + p.wg_lists) * (16 * 8 + 8));
   p.ack_bytes = p.max_lists ? align256((size_t)p.rows_per_pass * 12) : 0;
   p.score_bytes = scores_given ? 0 : align256((size_t)p.rows_per_pass * p.ld * 4);
   p.total = p.count_bytes + p.ack_bytes + p.gm_bytes + p.list_bytes + p.score_bytes;
@@ -372,8 +375,10 @@ static ip::ScoreArgs score_args(const ip_seqs* seqs, const ScorePlan& plan, int 
   sa.ack = ack;
   sa.scores_own = scores == nullptr;
   sa.max_lists = plan.max_lists;
-  sa.lists = plan.max_lists ? (uint64_t*)lists : nullptr;
-  sa.lists_meta = plan.max_lists ? (uint2*)(lists + (size_t)plan.rows_per_pass * plan.max_lists * 16 * 8) : nullptr;
+  sa.wg_lists = plan.wg_lists;
+  const int lpr = plan.max_lists + plan.wg_lists;   // one of the two is 0
+  sa.lists = lpr ? (uint64_t*)lists : nullptr;
+  sa.lists_meta = lpr ? (uint2*)(lists + (size_t)plan.rows_per_pass * lpr * 16 * 8) : nullptr;
   sa.with_append = append && row0 == 0;
   if (sa.with_append) sa.append = *append;
   sa.fuse = 0;

@@ -99,6 +99,8 @@ struct ScoreArgs {
   uint64_t* lists;             // fused: [n_rows, max_lists, 16] per-wave candidate lists, or null
   uint2* lists_meta;           // [n_rows, max_lists] (count, threshold) of each list
   int max_lists;               // waves per row covered by the grid
+  int wg_lists;                // rows too long for per-wave lists (max_lists 0): one list per
+                               // workgroup in lists / lists_meta, this many per row, or 0
   int with_append;             // decode: extra grid rows of workgroups run `append`,
   AppendArgs append;           // one sequence each (see append.hpp)
   // the fused decode step only (else 0): the attention workgroups select the rows

@@ -256,13 +256,19 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
     const int n_lists = n_run * NWV;
     // rows long enough for about 2 winners per wave: every wave lists its best
     // (see sel::wave_list) and the last workgroup merges the lists
-    const bool lists = fused_list_count<NWV, TILES>(nel, need, a.lists != nullptr) > 0;
+    const bool lists = fused_list_count<NWV, TILES>(nel, need, a.lists != nullptr && a.max_lists > 0) > 0;
     // the fused decode step: the attention workgroups of a list row merge its lists
     // themselves, those of a trivial row write its ids directly; the scoring
     // workgroups of those rows store their scores and lists and end
     const bool step = a.step != 0;
-    uint64_t* lrow = lists ? a.lists + (int64_t)(r - a.row0) * a.max_lists * sel::LIST : nullptr;
-    uint2* mrow = lists ? a.lists_meta + (int64_t)(r - a.row0) * a.max_lists : nullptr;
+    // rows too long for per-wave lists (a 1M-token row has 2048 waves): the waves'
+    // lists of a workgroup are reduced to one list of its 16 best (sel::wave_list
+    // over their union), and the last workgroup merges one list per workgroup
+    const bool wgl = FUSE && NWV == 8 && TILES == 4 && !step && !lists && !trivial && a.lists != nullptr && a.wg_lists >= n_run &&
+                     n_run * sel::LIST <= sel::C_CAP && n_run <= NTW && need <= sel::LIST / 2 * n_run;
+    const int lpr = lists ? a.max_lists : a.wg_lists;   // lists per row in the workspace
+    uint64_t* lrow = (lists || wgl) ? a.lists + (int64_t)(r - a.row0) * lpr * sel::LIST : nullptr;
+    uint2* mrow = (lists || wgl) ? a.lists_meta + (int64_t)(r - a.row0) * lpr : nullptr;
     // With lists and the scores in the workspace, a workgroup counts itself in once
     // its lists are acknowledged, without waiting for its score stores: the scores are
     // read only by the exact fallback, which first waits until every workgroup of the
@@ -337,6 +343,43 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
         const int slot = bx * NWV + wv;
         sel::wave_list<KPL>(k, id, lrow + (int64_t)slot * sel::LIST, mrow + slot, scores_first);
       }
+      if constexpr (NWV == 8 && TILES == 4) if (wgl) {
+        constexpr int KPL = TILES / 2;
+        uint32_t k[KPL];
+        int id[KPL];
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+          const int t = KPL * hh + i;
+          id[i] = kc0 + (wv * TILES + t) * 32 + kl;
+          const uint32_t hm = 0u - (uint32_t)hh;
+          const float sc = __uint_as_float((__float_as_uint(scv[i]) & ~hm) | (__float_as_uint(scv[KPL + i]) & hm));
+          k[i] = id[i] < nel ? float_key(sc) : 0u;
+        }
+        // the wave's list into LDS (past the query stage, which other waves may
+        // still read), then wave 0 lists the union of the NWV lists: entry u = 16w + p
+        // (ascending ids) sits in segment u / 32 of wave_list's order, half u / 64
+        static_assert(NWV * sel::LIST == 2 * 64 && KPL == 2, "the waves' lists fill two keys per lane");
+        sel::wave_list<KPL, true>(k, id, ss.wl + wv * sel::LIST, ss.wm + wv);
+        __syncthreads();
+        if (wv == 0) {
+          uint32_t uk[2];
+          int ui[2];
+          uint32_t lpm = 0u;
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int u = 64 * (lane >> 5) + 32 * i + (lane & 31);
+            const int w = u / sel::LIST, p = u % sel::LIST;
+            const uint2 m = ss.wm[w];
+            const uint64_t e = ss.wl[u];
+            const bool on = p < (int)(m.x & 0xFFu);
+            uk[i] = on ? (uint32_t)e : 0u;
+            ui[i] = on ? (int)(e >> 32) : 0;
+          }
+#pragma unroll
+          for (int w = 0; w < NWV; ++w) lpm = max(lpm, ss.wm[w].y);
+          sel::wave_list<2>(uk, ui, lrow + (int64_t)bx * sel::LIST, mrow + bx, false, lpm);
+        }
+      }
       if (!scores_first) store_scores();
     }
     if (step && (trivial || lists)) return;
@@ -379,7 +422,7 @@ __device__ __forceinline__ void score_fp8_body(const ScoreArgs& a, const int bx,
       return;
     }
     if (threadIdx.x == 0) sel::st_agent(a.count + (r - a.row0), 0);   // clear for the next call
-    if (!(lists && sel::merge_lists<NTW>(lrow, mrow, n_lists, need, nel, a.top_k, out, ss))) {
+    if (!((lists || wgl) && sel::merge_lists<NTW>(lrow, mrow, wgl ? n_run : n_lists, need, nel, a.top_k, out, ss))) {
       if (defer) {
         // the fallback reads every score of the row: wait (bounded) until every
         // workgroup has counted its acknowledged scores in

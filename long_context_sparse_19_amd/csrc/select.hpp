@@ -60,6 +60,8 @@ struct Shared {
   int cg[CG_CAP];                  // candidate groups, ascending
   uint32_t ckey[C_CAP + 64];       // candidates (order-preserving key, id), ascending id;
   int32_t cid[C_CAP + 64];         // + one spare entry per lane
+  uint64_t wl[NW * 16];            // the waves' lists of a workgroup list (see wave_list)
+  uint2 wm[NW];
 };
 
 // digit l of a key: bits 31..21, 20..10, 9..0
@@ -682,12 +684,14 @@ __device__ __forceinline__ void wave_count3(const uint32_t (&k)[KPL], uint32_t t
 
 // The wave's list from its KPL keys per lane (key 0 = none).  Ids ascend over the
 // segments (half, i): lanes 0..31 hold the lower half, k[i] before k[i + 1].
-// The entries go to `dst` [0, count) in that order, (count, L') to `meta`.
-// after_prior: the list's stores wait until every earlier memory operation of the
-// wave is acknowledged (a reader that sees the list stored sees those too).
-template <int KPL>
+// The entries go to `dst` [0, count) in that order, (count, L') to `meta`, with
+// L' raised to lp_floor when that is larger (a list of lists: every key above the
+// lower lists' L' is in them).  after_prior: the list's stores wait until every
+// earlier memory operation of the wave is acknowledged (a reader that sees the list
+// stored sees those too).  LDS_DST: dst and meta are in LDS (plain stores).
+template <int KPL, bool LDS_DST = false>
 __device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&id)[KPL], uint64_t* dst, uint2* meta,
-                                          bool after_prior = false) {
+                                          bool after_prior = false, uint32_t lp_floor = 0u) {
   static_assert(LIST == 16, "one lower bound per group of 4 lanes");
   const int lane = threadIdx.x & 63;
   const int valid = wave_count<KPL>(k, [](uint32_t x) { return x != 0u; });
@@ -785,15 +789,27 @@ __device__ __forceinline__ void wave_list(const uint32_t (&k)[KPL], const int (&
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
+  Lp = max(Lp, lp_floor);
   int n = 0;
 #pragma unroll
   for (int sgm = 0; sgm < NS; ++sgm) {
     const int pos = n + mbcnt(mk[sgm]);
-    if (kp[sgm] && pos < LIST)
-      st_agent(dst + pos, (uint64_t)k[sgm % KPL] | ((uint64_t)(uint32_t)id[sgm % KPL] << 32));
+    if (kp[sgm] && pos < LIST) {
+      const uint64_t e = (uint64_t)k[sgm % KPL] | ((uint64_t)(uint32_t)id[sgm % KPL] << 32);
+      if constexpr (LDS_DST)
+        dst[pos] = e;
+      else
+        st_agent(dst + pos, e);
+    }
     n += __popcll(mk[sgm]);
   }
-  if (lane == 0) st_agent((uint64_t*)meta, (uint64_t)((uint32_t)min(n, LIST) | LIST_WRITTEN) | ((uint64_t)Lp << 32));
+  const uint64_t mw = (uint64_t)((uint32_t)min(n, LIST) | LIST_WRITTEN) | ((uint64_t)Lp << 32);
+  if (lane == 0) {
+    if constexpr (LDS_DST)
+      *(uint64_t*)meta = mw;
+    else
+      st_agent((uint64_t*)meta, mw);
+  }
 }
 
 // A merge's candidates in the registers of keep_best_regs' layout, from loaded list

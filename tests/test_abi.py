@@ -225,11 +225,13 @@ def test_workspace_sizes_are_consistent(L):
     assert L.LIB.index_scores_ld(73728) == 18432
     s2 = seqs(batch=1, max_seq_len=73728, seq_stride=73728)
     assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s2), 8192, 512, 1) == 8192 * 4 + 8192 * 1152 * 4
-    # 1M tokens: 262143 blocks -> 256 tiles, 2048 waves: too many for lists
+    # 1M tokens: 262143 blocks -> 256 tiles, 2048 waves: too many for per-wave lists,
+    # one 16-entry list (+ its count word) per 8-wave workgroup instead
     s1 = seqs(batch=1, max_seq_len=1 << 20, seq_stride=1 << 20)
     ld1 = L.LIB.index_scores_ld(1 << 20)
     assert ld1 == 262144
-    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s1), 1, 512, 0) == 256 + 16384 * 4 + ld1 * 4
+    assert L.LIB.index_score_topk_workspace_bytes(ctypes.byref(s1), 1, 512, 0) == \
+        256 + 16384 * 4 + 256 * (16 * 8 + 8) + ld1 * 4
     # 1025 blocks -> 2 tiles
     assert L.LIB.index_scores_ld(4 * 1026) == 2048
     assert L.LIB.sparse_attn_workspace_bytes(8192, 64, 512, 512, L.IP_BF16) == 0      # prefill: no split

@@ -423,6 +423,57 @@ def test_full_size_decode(w):
     full_case(w, keep_scores=False)
 
 
+# rows of more than 256 scoring waves (two sequences of 280000 and 268000 tokens:
+# 69 and 66 scoring workgroups) select through one list per scoring workgroup
+LONG_ROWS = scaled_down(MAX_CTX, 4 * 70000, batch=2)
+
+
+@pytest.mark.parametrize("case", ["plain", "overflow", "ties"])
+def test_long_rows_select_through_workgroup_lists(case):
+    """Decode rows too long for per-wave lists: each scoring workgroup reduces its
+    waves' lists to one list of its 16 best, and the row's last workgroup merges
+    those.  'overflow': the first 200 blocks of sequence 0 are boosted (pooled scale
+    x8), so their workgroup holds more than 16 winners and the merge must fall back
+    to the exact select; 'ties': block j takes block j % 7's pooled key, so every
+    score repeats and the lists keep the lowest ids of a tie.  Checked against the
+    oracle's selection over the device's pooled keys."""
+    D = _dev()
+    w = LONG_ROWS
+    inp = make_inputs(w, with_attention=False)
+    inp.seq_lens = np.asarray(inp.seq_lens - np.array([0, 4 * 3000]), dtype=np.int32)
+    inp.q_pos = inp.seq_lens[inp.q_seq] - 1
+    log(f"[case] long rows {case} lens={inp.seq_lens.tolist()} k={w.top_k}")
+    d = D.upload(inp)
+    D.compress(d)
+    if case == "overflow":
+        rows_b = torch.as_tensor(O.pooled_rows(inp, 0, np.arange(200)), device=d.pooled.scale.device)
+        d.pooled.scale[rows_b] *= 8.0
+    if case == "ties":
+        for b in range(w.batch):
+            nb = int(inp.seq_lens[b]) // 4
+            dst = torch.as_tensor(O.pooled_rows(inp, b, np.arange(nb)), device=d.pooled.data.device)
+            src = torch.as_tensor(O.pooled_rows(inp, b, np.arange(nb) % 7), device=d.pooled.data.device)
+            d.pooled.data[dst] = d.pooled.data[src]
+            d.pooled.scale[dst] = d.pooled.scale[src]
+    ws = D.Workspaces(d, keep_scores=False)
+    D.score_topk(d, ws)
+    torch.cuda.synchronize()
+    gsel = ws.sel.cpu().numpy()
+    vals = O.pooled_values(d.pooled.data.cpu().numpy(), d.pooled.scale.cpu().numpy().astype(np.float64))
+    for r in range(w.batch):
+        b, b_q = int(inp.q_seq[r]), int(inp.q_pos[r]) // 4
+        S = O.score(O._to_f64(inp.q_idx[r]), inp.gates[r], vals[O.pooled_rows(inp, b, np.arange(b_q))])
+        o_ids = O.select(S, b_q, w.top_k)
+        P.check_selection(gsel[r], o_ids, S, b_q, w.top_k)
+        if case == "overflow" and r == 0:
+            # the case does what it is for: the first workgroup's 1024 blocks hold
+            # more winners than its list
+            assert int(((o_ids >= 0) & (o_ids < 1024)).sum()) > 16
+        if case == "ties" and r == 0:
+            assert len(np.unique(o_ids[o_ids >= 0] % 7)) < w.top_k - 1
+    log(f"  selection ok on {w.batch} rows")
+
+
 def _prefill_selection_all_rows(inp, vals, gsel, top_k, chunk=128):
     """The oracle's selection for every prefill row (one sequence: the rows share
     its key prefix, so scores come from score_many over row chunks), checked row by
