@@ -15,10 +15,11 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Memory: every pointer named "device" is device memory owned by the caller.
- *    The library allocates nothing.  Its only state between calls is per host
- *    thread: the text behind ip_last_error() and the benchmarking hook armed by
+ *    The library allocates nothing.  Its only state between calls: per host
+ *    thread, the text behind ip_last_error() and the benchmarking hook armed by
  *    ip_time_next_launch() (see the end of this header), which no compute call
- *    needs.
+ *    needs; per GPU, the static workspace of index_score_topk_noalloc and its
+ *    device address, set up by that call's first use on the GPU.
  *  - Streams: every call only enqueues work on `stream` (0 = the null stream) and
  *    never synchronises the host.  Outputs are ready when the stream reaches them.
  *  - Errors: arguments the host can check (null pointers, unsupported dtypes or
