@@ -400,6 +400,17 @@ const char* ip_last_error(void);
  * outside stream capture.  Not needed for normal use. */
 ip_status ip_time_next_launch(int32_t kernel_id, hipEvent_t start, hipEvent_t stop);
 
+/* Diagnostics: copies the phase stamps of the last fused decode step (up to `bytes`
+ * bytes of a [5120][8] uint64 array: rows 0..4095 the step's workgroups by index,
+ * rows 4096.. the combine's; slots 0 start, 1 scoring done and its stores
+ * acknowledged, 2 ids ready, 3 sub-tile 0 landed, 4 sub-tiles done, 5 end (for the
+ * combine: 0 start, 1 end); values of a 100 MHz clock shared by all compute units,
+ * 0 where a workgroup recorded nothing) to host memory `host`.  Only a library built
+ * with IP_PHASE_STAMPS records them (`python -m long_context_sparse_19_amd.build
+ * --stamps`, a library of its own); otherwise IP_EUNSUPPORTED.  Synchronises with
+ * the device.  Not needed for normal use. */
+ip_status ip_phase_stamps(void* host, size_t bytes);
+
 /* Library version, e.g. "0.1.0". */
 const char* ip_version(void);
 

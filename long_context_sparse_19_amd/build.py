@@ -14,6 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libindexpool.so")
+STAMPS_LIB = os.path.join(PKG, "libindexpool_stamps.so")
 SOURCES = ["compress.hip", "score.hip", "select.hip", "topk.hip", "attn.hip", "attn_step_h32.hip", "attn_pipe.hip", "kda.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -30,9 +31,10 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, stamps: bool = False) -> str:
+    bdir = BUILD + ("_stamps" if stamps else "")
+    obj = os.path.join(bdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *(["-DIP_PHASE_STAMPS"] if stamps else []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,21 +43,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, stamps: bool = False) -> str:
+    """The library; stamps: the diagnostics library that records the decode step's
+    phase stamps (ip_phase_stamps), built beside it as libindexpool_stamps.so."""
+    os.makedirs(BUILD + ("_stamps" if stamps else ""), exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, stamps), SOURCES))
+    lib = STAMPS_LIB if stamps else LIB
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, stamps="--stamps" in sys.argv[1:])
     sys.exit(0)

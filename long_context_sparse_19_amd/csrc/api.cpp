@@ -164,6 +164,13 @@ extern "C" {
 const char* ip_last_error(void) { return g_err.c_str(); }
 const char* ip_version(void) { return "0.1.0"; }
 
+ip_status ip_phase_stamps(void* host, size_t bytes) {
+  if (!host) return fail(IP_EINVAL, "ip_phase_stamps: host is NULL");
+  if (!ip::phase_stamps(host, bytes))
+    return fail(IP_EUNSUPPORTED, "ip_phase_stamps: the library was built without IP_PHASE_STAMPS");
+  return IP_OK;
+}
+
 ip_status ip_time_next_launch(int32_t kernel_id, hipEvent_t start, hipEvent_t stop) {
   if (kernel_id == 0 && !start && !stop) {
     for (auto& h : g_hook) h = Hook{};

@@ -38,12 +38,21 @@ __global__ __launch_bounds__(NTA, 1) void decode_step_kernel(StepKArgs A) {
   __shared__ __align__(16) uint8_t kv1[KVBUF];
   __shared__ int last_here;
   const int L = blockIdx.x;
+  IP_STAMP(L, ST_START);
   if (L < A.n_score + A.n_app) {
     scorek::score_fp8_body<1, STEP_NWV, true, STEP_TILES>(A.s, L % A.gx, L / A.gx, A.gx, kv0, last_here,
                                                            A.at.sel_ready);
+#ifdef IP_PHASE_STAMPS
+    __builtin_amdgcn_s_waitcnt(0);               // its stores acknowledged
+#endif
+    IP_STAMP(L, ST_SCORED);
     return;
   }
   attn_bf16_body<true>(A.at, L - A.n_score - A.n_app, sh, pmat, kv0, kv1);
+#ifdef IP_PHASE_STAMPS
+  __builtin_amdgcn_s_waitcnt(0);                 // its partials acknowledged
+#endif
+  IP_STAMP(L, ST_END);
 }
 
 // ------------------------------------------------------------------ fp8 latent tier
@@ -431,6 +440,7 @@ __global__ __launch_bounds__(NTA, 1) void attn_fp8_kernel(AttnArgs a) {
 constexpr int MAX_SPLIT = 64;
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   // rows fastest (a row's workgroups share a die, as the fused step's attention)
+  IP_STAMP(STAMP_STEP_ROWS + (int)blockIdx.x, ST_C_START);
   const int head = (int)(blockIdx.x / a.n_rows) * 2 + (threadIdx.x >> 7);
   const int rl = (int)(blockIdx.x % a.n_rows);
   const int r = a.row0 + rl;
@@ -497,6 +507,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   uint16_t* out = (uint16_t*)a.out + ((int64_t)r * LAT_H + head) * LAT_DV + t * 4;
   *(uint2*)out = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
   if (a.lse && t == 0) a.lse[(int64_t)r * LAT_H + head] = (m + log2f(L)) * LN2;
+#ifdef IP_PHASE_STAMPS
+  __builtin_amdgcn_s_waitcnt(0);
+#endif
+  IP_STAMP(STAMP_STEP_ROWS + (int)blockIdx.x, ST_C_END);
 }
 
 // ------------------------------------------------------------------ f32 path
@@ -619,6 +633,18 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(AttnArgs a) {
 }
 
 }  // namespace
+
+// the phase stamps of the last decode step (a library built with IP_PHASE_STAMPS)
+bool phase_stamps(void* host, size_t bytes) {
+#ifdef IP_PHASE_STAMPS
+  if (bytes > sizeof(ip_phase_stamp_rows)) bytes = sizeof(ip_phase_stamp_rows);
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(ip_phase_stamp_rows), bytes, 0, hipMemcpyDeviceToHost) == hipSuccess;
+#else
+  (void)host;
+  (void)bytes;
+  return false;
+#endif
+}
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;

@@ -30,6 +30,7 @@
 #pragma once
 #include "attn_common.hpp"
 #include "score_fp8.hpp"
+#include "stamps.hpp"
 
 namespace ip {
 
@@ -304,6 +305,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const int bid,
     nr = NewRow{(uint32_t)a.L.tok_row(c.b, c.p), a.k_new + (int64_t)c.b * a.k_new_stride};
     __builtin_amdgcn_sched_barrier(0);
     step_select(a, c, rl, split, sb0, send, lid, kv0, sl);
+    IP_STAMP((int)blockIdx.x, ST_IDS);
     load_ids();
   }
   // every query DMA is issued before anything consumes the ids
@@ -350,6 +352,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const int bid,
   for (int k = 0; k < KV_LOADS; ++k) load_column(src[1], kv1, k);
   wait_vm<KV_LOADS>();                           // sub-tile 0 landed (this wave's part)
   block_sync_lds();
+  if constexpr (STEP) IP_STAMP((int)blockIdx.x, ST_SUB0);
   const float cs = a.scale * LOG2E;
 
   // O^T tiles [32 dims, 32 heads]: o[i][db][k] = head 32i + l32, dim 128wv + 32db +
@@ -489,6 +492,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const int bid,
     step(n, kv0, kv1);
     if (n + 1 < nsub) step(n + 1, kv1, kv0);
   }
+  if constexpr (STEP) IP_STAMP((int)blockIdx.x, ST_SUBS);
 
   // ---- epilogue: l of each head = sum of its two token halves
   if (lh == 0) lds_st(&sh.lpart[th][hs], l_half);

@@ -230,6 +230,9 @@ struct StepKArgs {
 };
 // the step kernel with 32-head attention units, over `grid` workgroups
 hipError_t launch_decode_step_h32(const StepKArgs& k, unsigned grid, hipStream_t s);
+// Copies the phase stamps of the last decode step (ip_phase_stamps); false unless
+// the library was built with IP_PHASE_STAMPS.
+bool phase_stamps(void* host, size_t bytes);
 
 // KDA decode step (the linear-attention half): 128 key and value channels per head
 constexpr int KDA_D = 128;
