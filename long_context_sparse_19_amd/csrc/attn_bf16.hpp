@@ -528,9 +528,13 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const int bid,
   block_sync_lds();
   uint16_t* dst = final_out ? (uint16_t*)a.out + (int64_t)r * LAT_H * LAT_DV : a.part_o + pi * LAT_H * LAT_DV;
 #pragma unroll
+  // non-temporal stores: the rows stream out of the die's L2 as they are written
+  // (a launch's end writes back what its workgroups left dirty there, and the
+  // combine waits for that)
   for (int k = 0; k < LAT_H / NWA; ++k) {
     const int h = wv + NWA * k;
-    *(u32x4_t*)(dst + h * LAT_DV + lane * 8) = *(const u32x4_t*)(kv0 + h * OPITCH + lane * 16);
+    __builtin_nontemporal_store(*(const u32x4_t*)(kv0 + h * OPITCH + lane * 16),
+                                (u32x4_t*)(dst + h * LAT_DV + lane * 8));
   }
 }
 
@@ -834,7 +838,8 @@ __device__ __forceinline__ void attn_bf16_h32_body(const AttnArgs& a, const int 
 #pragma unroll
   for (int k = 0; k < 32 / NWA; ++k) {
     const int h = wv + NWA * k;
-    *(u32x4_t*)(dst + (H0 + h) * LAT_DV + lane * 8) = *(const u32x4_t*)(kv0 + h * OPITCH + lane * 16);
+    __builtin_nontemporal_store(*(const u32x4_t*)(kv0 + h * OPITCH + lane * 16),
+                                (u32x4_t*)(dst + (H0 + h) * LAT_DV + lane * 8));   // streamed, as above
   }
 }
 
