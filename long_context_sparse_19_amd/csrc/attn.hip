@@ -492,20 +492,22 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     for (; s < S; ++s) add(__shfl(wgt, s), *(const uint2*)(base + (int64_t)s * LAT_H * LAT_DV));
   }
   // the fused step's words and lists of the row return to zero for the next launch
-  // (every reader of them belongs to the step launch, which has ended)
+  // (every reader of them belongs to the step launch, which has ended); this
+  // kernel's stores are non-temporal, so little is left to write back at its end
   if (a.sel_ready && blockIdx.x < (unsigned)a.n_rows && threadIdx.x == 0) {
     a.sel_ready[rl] = 0u;
   }
   if (a.step_lists) {
     const int g = (int)(blockIdx.x / a.n_rows) * 256 + threadIdx.x, G = LAT_H / 2 * 256;
     u32x4_t* l16 = (u32x4_t*)(a.step_lists + (int64_t)rl * a.step_max_lists * sel::LIST);
-    for (int i = g; i < a.step_max_lists * sel::LIST / 2; i += G) l16[i] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = g; i < a.step_max_lists * sel::LIST / 2; i += G) __builtin_nontemporal_store(u32x4_t{0u, 0u, 0u, 0u}, l16 + i);
     uint2* m = a.step_meta + (int64_t)rl * a.step_max_lists;
-    for (int i = g; i < a.step_max_lists; i += G) m[i] = make_uint2(0u, 0u);
+    for (int i = g; i < a.step_max_lists; i += G) __builtin_nontemporal_store((uint64_t)0, (uint64_t*)(m + i));
   }
   const float inv = 1.f / L;
   uint16_t* out = (uint16_t*)a.out + ((int64_t)r * LAT_H + head) * LAT_DV + t * 4;
-  *(uint2*)out = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+  __builtin_nontemporal_store((uint64_t)pack_bf16x2(acc.x * inv, acc.y * inv) |
+                                  ((uint64_t)pack_bf16x2(acc.z * inv, acc.w * inv) << 32), (uint64_t*)out);
   if (a.lse && t == 0) a.lse[(int64_t)r * LAT_H + head] = (m + log2f(L)) * LN2;
 #ifdef IP_PHASE_STAMPS
   __builtin_amdgcn_s_waitcnt(0);

@@ -225,7 +225,7 @@ __device__ __forceinline__ void step_select(const AttnArgs& a, const RowCtx& c, 
   }
   __syncthreads();                               // lid complete, ss free
   if (local)
-    for (int i = threadIdx.x; i < n; i += NTA) row_out[sb0 + i] = lid[i];
+    for (int i = threadIdx.x; i < n; i += NTA) __builtin_nontemporal_store(lid[i], row_out + sb0 + i);
 }
 
 // The body of the bf16 kernel for workgroup `bid` (4 waves, threads 0..255), over
