@@ -141,7 +141,8 @@ __global__ __launch_bounds__(KT) void kda_decode_kernel(KdaArgs a) {
     const float ki = sh.k[i] * rk, qi = sh.q[i] * rq;
     s[p] = make_float4(fmaf(ki, d.x, s[p].x), fmaf(ki, d.y, s[p].y), fmaf(ki, d.z, s[p].z), fmaf(ki, d.w, s[p].w));
     o = make_float4(fmaf(qi, s[p].x, o.x), fmaf(qi, s[p].y, o.y), fmaf(qi, s[p].z, o.z), fmaf(qi, s[p].w, o.w));
-    *(float4*)(S + i * KD) = s[p];
+    // streamed: the state leaves the die's L2 as it is written, not at the launch's end
+    __builtin_nontemporal_store(f32x4_t{s[p].x, s[p].y, s[p].z, s[p].w}, (f32x4_t*)(S + i * KD));
   }
   __syncthreads();                   // every wave has read red[] (u) before it is rewritten
   o = column_sums(o, sh);
