@@ -836,10 +836,12 @@ __device__ __forceinline__ void attn_bf16_h32_body(const AttnArgs& a, const int 
   block_sync_lds();
   uint16_t* dst = final_out ? (uint16_t*)a.out + (int64_t)r * LAT_H * LAT_DV : a.part_o + pi * LAT_H * LAT_DV;
 #pragma unroll
+  // plain stores: a launch of few units leaves little to write back at its end,
+  // and the combine then reads the partials from the last-level cache (streamed,
+  // the 1M-token row's combine measured 7.3 against 5.3 us)
   for (int k = 0; k < 32 / NWA; ++k) {
     const int h = wv + NWA * k;
-    __builtin_nontemporal_store(*(const u32x4_t*)(kv0 + h * OPITCH + lane * 16),
-                                (u32x4_t*)(dst + (H0 + h) * LAT_DV + lane * 8));   // streamed, as above
+    *(u32x4_t*)(dst + (H0 + h) * LAT_DV + lane * 8) = *(const u32x4_t*)(kv0 + h * OPITCH + lane * 16);
   }
 }
 
