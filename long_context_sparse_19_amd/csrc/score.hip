@@ -33,7 +33,20 @@ __global__ __launch_bounds__(NWV * 64) void score_fp8_bf16_kernel(ScoreArgs a) {
   // the query stage, and (fused) the selection's state once scoring is done
   __shared__ __align__(16) uint8_t smem[scorek::score_smem<NWV, FUSE>()];
   __shared__ int last_here;
-  scorek::score_fp8_body<RPW, NWV, FUSE>(a, blockIdx.x, blockIdx.y, gridDim.x, smem, last_here, nullptr);
+  // fused (decode rows): the scoring workgroups take their (key chunk, row) rows
+  // fastest in dispatch order, so the first chunks of every row go before the later
+  // chunks of the long rows, and the append workgroups come last.  Consecutive
+  // workgroups go to the dies in turn, so every die keeps an even share of the
+  // scoring (a one-row grid is unchanged).
+  if constexpr (FUSE) {
+    const int gx = (int)gridDim.x, nr = a.n_rows;
+    const int L = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+    const int A = L - nr * gx;                   // >= 0: an append workgroup
+    const int bx = A < 0 ? L / nr : A % gx;
+    const int by = A < 0 ? L % nr : nr + A / gx;
+    scorek::score_fp8_body<RPW, NWV, FUSE>(a, bx, by, gx, smem, last_here, nullptr);
+  } else
+    scorek::score_fp8_body<RPW, NWV, FUSE>(a, blockIdx.x, blockIdx.y, gridDim.x, smem, last_here, nullptr);
 }
 
 // float keys and queries (small geometries): one thread per key, queries in LDS.
