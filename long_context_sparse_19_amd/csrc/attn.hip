@@ -652,8 +652,8 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   // (row, split) units, or (row, split, head half) units of the 32-head body
   const dim3 grid((unsigned)((use_h32(a) ? 2 : 1) * (int64_t)a.n_rows * a.n_split));
-  // long splits over a cache addressable with 32-bit offsets: the pipelined kernel
-  if (a.blocks_per_split >= PIPE_MIN_BLOCKS && a.k_off32) {
+  // long splits: the pipelined kernel
+  if (a.blocks_per_split >= PIPE_MIN_BLOCKS) {
     const hipError_t e = launch_attn_bf16_pipe(a, s);
     if (e != hipSuccess) return e;
   } else {

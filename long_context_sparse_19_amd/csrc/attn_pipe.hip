@@ -59,21 +59,41 @@ __device__ __forceinline__ int kvp_off(int t, int ch) {
   return (ch >> 3) * SEGP + t * 128 + 16 * ((ch & 7) ^ kv_swz(t));
 }
 
-// The sub-tiles arrive by buffer loads to LDS (buffer_load_dwordx4 ... lds) with
-// 32-bit byte offsets from the cache base.  (The global_load_lds form used above
-// counts, for the compiler, as an access that may touch LDS through the flat
-// path; while one is in flight it waits for all outstanding LDS reads wherever it
-// needs one, so the K fragments read ahead would be waited for together.)
+// The sub-tiles arrive by loads to LDS.  A cache whose rows all lie within 4 GB of
+// its base (OFF32) is read by buffer loads (buffer_load_dwordx4 ... lds) with 32-bit
+// byte offsets; a paged cache, whose extent the host cannot bound, by
+// global_load_lds from base + a 64-bit offset.  (The global form counts, for the
+// compiler, as an access that may touch LDS through the flat path; while one is in
+// flight it waits for all outstanding LDS reads wherever it needs one, so the K
+// fragments read ahead are waited for together: slower on long contiguous splits,
+// still far ahead of the one-sub-tile-in-flight kernel on gather-bound paged rows.)
 // Lane l of O-wave p loads, of sub-tile m, row t = 8p + l/8 (block 2p + l/32),
 // chunk slot l%8; instruction g fills rows 8p .. +7 of segment g, adding 128g
-// through the scalar offset.  The two block-table entries come from one 8-byte
-// LDS read.
-__device__ __forceinline__ uint32_t pipe_src(const AttnArgs& a, const uint32_t* brow, int m, int p) {
+// through the scalar offset (or the address).  The two block-table entries come
+// from one 8-byte LDS read.
+// row_off: the byte offset from the cache base of this lane's 16 bytes of row t
+// (entry e), 32-bit when OFF32.
+template <bool OFF32>
+struct PipeOff {
+  using type = uint64_t;
+};
+template <>
+struct PipeOff<true> {
+  using type = uint32_t;
+};
+template <bool OFF32>
+__device__ __forceinline__ typename PipeOff<OFF32>::type row_off(const AttnArgs& a, uint32_t e, int t) {
+  const int lane = threadIdx.x & 63;
+  using T = typename PipeOff<OFF32>::type;
+  return (T)((e & ROW_BITS) + (t & 3)) * (T)a.k_stride + 16 * ((lane & 7) ^ kv_swz(t));
+}
+template <bool OFF32>
+__device__ __forceinline__ typename PipeOff<OFF32>::type pipe_src(const AttnArgs& a, const uint32_t* brow, int m,
+                                                                  int p) {
   const int lane = threadIdx.x & 63;
   const uint2 e2 = lds_ld((const uint2*)&brow[8 * m + 2 * p]);
   const uint32_t e = (lane >> 5) ? e2.y : e2.x;
-  const int t = 8 * p + (lane >> 3);
-  return ((e & ROW_BITS) + (t & 3)) * (uint32_t)a.k_stride + 16 * ((lane & 7) ^ kv_swz(t));
+  return row_off<OFF32>(a, e, 8 * p + (lane >> 3));
 }
 
 // a buffer resource over [base, base + 4 GB) (raw, no stride)
@@ -88,6 +108,19 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t vo
 __device__ __forceinline__ void pipe_load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint8_t* buf, int g, int p) {
   lds_dma16(rs, voff, 128 * g, buf + g * SEGP + p * 1024);
 }
+__device__ __forceinline__ void pipe_load(__amdgpu_buffer_rsrc_t, uint64_t off, const uint8_t* k, uint8_t* buf, int g,
+                                          int p) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(k + off + 128 * g),
+                                   (void __attribute__((address_space(3)))*)(buf + g * SEGP + p * 1024), 16, 0, 0);
+}
+template <bool OFF32>
+__device__ __forceinline__ void pipe_load_t(__amdgpu_buffer_rsrc_t rs, typename PipeOff<OFF32>::type off,
+                                            const uint8_t* k, uint8_t* buf, int g, int p) {
+  if constexpr (OFF32)
+    pipe_load(rs, off, buf, g, p);
+  else
+    pipe_load(rs, off, k, buf, g, p);
+}
 
 // 8-byte LDS store of (lo, hi) at base + off, as one integer store whose offset the
 // compiler cannot relate to that of another store: two stores from one base are
@@ -98,6 +131,7 @@ __device__ __forceinline__ void lds_st8(uint8_t* base, int off, uint32_t lo, uin
   lds_st((uint64_t*)(base + off), (uint64_t)lo | ((uint64_t)hi << 32));
 }
 
+template <bool OFF32>
 __global__ __launch_bounds__(NTW, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
   __shared__ PipeShared sh;
   __shared__ __align__(16) uint8_t pb0[PBUF];    // P[head][token] bf16, even sub-tiles
@@ -152,9 +186,9 @@ __global__ __launch_bounds__(NTW, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int t = 8 * pw + (lane >> 3);
-      const uint32_t so = ((ent[1 + n] & ROW_BITS) + (t & 3)) * (uint32_t)a.k_stride + 16 * ((lane & 7) ^ kv_swz(t));
+      const auto so = row_off<OFF32>(a, ent[1 + n], t);
 #pragma unroll
-      for (int g = 0; g < NSEG; ++g) pipe_load(krs, so, n ? kb1 : kb0, g, pw);
+      for (int g = 0; g < NSEG; ++g) pipe_load_t<OFF32>(krs, so, a.k, n ? kb1 : kb0, g, pw);
     }
   }
   wait_vm<0>();                                  // the query (and, O-waves, sub-tiles 0 and 1)
@@ -390,9 +424,9 @@ __global__ __launch_bounds__(NTW, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
     // step n: stream sub-tile n+2 (clamped to the last) into `db`, add sub-tile
     // n-1 (`ob`, P from `pr`); past the barrier sub-tile n+1 has landed
     auto ostep = [&](const int n, const uint8_t* ob, const uint8_t* pr, uint8_t* db) __attribute__((always_inline)) {
-      const uint32_t so = pipe_src(a, sh.brow, min(n + 2, nsub - 1), pw);
+      const auto so = pipe_src<OFF32>(a, sh.brow, min(n + 2, nsub - 1), pw);
 #pragma unroll
-      for (int g = 0; g < NSEG; ++g) pipe_load(krs, so, db, g, pw);
+      for (int g = 0; g < NSEG; ++g) pipe_load_t<OFF32>(krs, so, a.k, db, g, pw);
       if (n > 0) ojob(n - 1, ob, pr);
       wait_vm<PL_LOADS>();
       block_sync_lds();
@@ -434,7 +468,11 @@ __global__ __launch_bounds__(NTW, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
 
 hipError_t launch_attn_bf16_pipe(const AttnArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  launch(K_ATTN, attn_bf16_pipe_kernel, dim3((unsigned)((int64_t)a.n_rows * a.n_split)), dim3(NTW), s, a);
+  const dim3 grid((unsigned)((int64_t)a.n_rows * a.n_split));
+  if (a.k_off32)
+    launch(K_ATTN, attn_bf16_pipe_kernel<true>, grid, dim3(NTW), s, a);
+  else
+    launch(K_ATTN, attn_bf16_pipe_kernel<false>, grid, dim3(NTW), s, a);
   return hipGetLastError();
 }
 

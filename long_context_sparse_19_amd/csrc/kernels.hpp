@@ -201,7 +201,7 @@ struct AttnArgs {
 constexpr int LAT_H = 64, LAT_DK = 576, LAT_DV = 512;
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 // the pipelined bf16 kernel alone (no combine); launch_attn_bf16 picks it for splits
-// of at least PIPE_MIN_BLOCKS blocks when every K row lies within 4 GB of k
+// of at least PIPE_MIN_BLOCKS blocks (32-bit offsets when k_off32, else 64-bit)
 constexpr int PIPE_MIN_BLOCKS = 128;
 hipError_t launch_attn_bf16_pipe(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t s);
