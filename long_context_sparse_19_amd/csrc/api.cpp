@@ -37,6 +37,7 @@ constexpr size_t kScoreBudget = size_t(256) << 20;  // score workspace per row c
 #ifndef IP_ATTN_WG
 #define IP_ATTN_WG 128
 #endif
+constexpr int kComputeUnits = 256;                     // gfx950: 8 dies x 32
 constexpr int kAttnWorkgroups = IP_ATTN_WG;               // split decode attention up to this many workgroups
 
 ip_status check_seqs(const ip_seqs* s, const char* fn) {
@@ -141,6 +142,13 @@ AttnPlan attn_plan(int n_q, int n_heads, int dv, int top_k, int q_dtype) {
     const int sub_per = std::min((nsub + ns - 1) / ns, 32);   // <= 512 blocks per split
     p.blocks_per_split = sub_per * 16;
     p.n_split = (top_k + p.blocks_per_split - 1) / p.blocks_per_split;
+    // long splits run one pipelined workgroup per compute unit: halve them while a
+    // launch has fewer units than the chip has compute units and the halves stay
+    // long enough for the pipelined kernel
+    while ((int64_t)p.n_split * n_q < kComputeUnits && p.blocks_per_split >= 2 * ip::PIPE_MIN_BLOCKS) {
+      p.blocks_per_split /= 2;
+      p.n_split = (top_k + p.blocks_per_split - 1) / p.blocks_per_split;
+    }
   }
   // bf16 partial O, then fp32 (m, l) pairs
   p.bytes = p.n_split > 1 ? (size_t)n_q * p.n_split * n_heads * ((size_t)dv * 2 + 8) : 0;

@@ -165,6 +165,9 @@ SMALL = {
     "prefill_split_k700": scaled_down(PREFILL, 3200, n_query=128, top_k=700),
     "decode_batch128": scaled_down(DECODE, 4 * 600, batch=128),
     "ragged_paged": scaled_down(RAGGED, 8192, batch=5, min_blocks=50),
+    # 32 paged rows of 20..700 blocks, top-512: four 128-block splits through the
+    # pipelined kernel's 64-bit-address form, the later splits of short rows all padding
+    "ragged_paged_pipe": scaled_down(RAGGED, 4 * 700, batch=32, min_blocks=20),
     "k1": scaled_down(DECODE, 1024, batch=2, top_k=1),
     "k_exceeds": scaled_down(DECODE, 256, batch=2, top_k=100),
     "tiny_prefill_f32": TINY.with_(mode="prefill", n_query=40, seq_len=512, top_k=16),
